@@ -1,0 +1,98 @@
+"""Algorithmic work of each hot-path stage and MI355X peak figures.
+
+"Algorithmic" bytes are what the method must move at least once: weights
+streamed once per call, storage-type inputs read once, outputs written once,
+context K/V read once per layer.  No padding, re-reads or split-K partials are
+counted; those are implementation overheads the roofline fraction exposes.
+
+The per-stage formulas follow the pages' cost discussion: the context feature
+is computed once and reused ("DFlash: Block Diffusion for Flash Speculative
+Decoding 논문 정리", section "KV Injection 메커니즘", memory table), and one
+drafting pass costs one forward whatever the block size (same page, section
+"Preliminaries", eq. (3)).
+"""
+from __future__ import annotations
+
+# MI355X (gfx950) published peaks
+HBM_PEAK_GBS = 8000.0            # HBM3E, GB/s
+MFMA_BF16_TFLOPS = 2500.0        # dense bf16 MFMA
+FP32_VECTOR_TFLOPS = 157.3
+N_CU = 256
+CLOCK_GHZ = 2.4
+
+
+def elem_bytes(dtype: str) -> int:
+    return {"bf16": 2, "f32": 4}[dtype]
+
+
+# ---------------------------------------------------------------- (a) fusion
+def fuse_bytes(T: int, D: int, n_tgt: int = 5, es: int = 2) -> int:
+    """n_tgt source states [T, D] + W_c [D, n_tgt*D] + H_t [T, D], storage type."""
+    return (n_tgt * T * D + n_tgt * D * D + T * D) * es
+
+
+def fuse_flops(T: int, D: int, n_tgt: int = 5) -> int:
+    return 2 * T * n_tgt * D * D
+
+
+def w_c_bytes(D: int, n_tgt: int = 5, es: int = 2) -> int:
+    return n_tgt * D * D * es
+
+
+def fusion_input_bytes(T: int, D: int, n_tgt: int = 5, es: int = 2) -> int:
+    return n_tgt * T * D * es
+
+
+def fusion_output_bytes(T: int, D: int, es: int = 2) -> int:
+    return T * D * es
+
+
+# ------------------------------------------------------------- (b) injection
+def inject_bytes(T: int, D: int, L: int, Hkv: int, d: int, es: int = 2) -> int:
+    """H_t [T, D] + every layer's W_K, W_V + the K/V rows written to the cache."""
+    kv = 2 * L * Hkv * d
+    return (T * D + kv * D + T * kv) * es
+
+
+def inject_flops(T: int, D: int, L: int, Hkv: int, d: int) -> int:
+    return 2 * T * D * 2 * L * Hkv * d
+
+
+# ----------------------------------------------------------- (c) draft forward
+def layer_weight_elems(D: int, Hq: int, Hkv: int, d: int, F: int) -> int:
+    return (Hq + 2 * Hkv) * d * D + D * Hq * d + 2 * F * D + D * F + 2 * D
+
+
+def draft_forward_bytes(D, L, Hq, Hkv, d, F, V, B, gamma, ctx_lens, es=2) -> int:
+    """All drafter weights once, the LM head once, each layer's context + block K/V
+    once, and the fp32 activations in/out (block embedding rows and h_final)."""
+    w = L * layer_weight_elems(D, Hq, Hkv, d, F) + D
+    kv = L * sum(n + gamma for n in ctx_lens) * 2 * Hkv * d
+    lm = V * D
+    act = B * gamma * D * 4 * 2
+    return (w + kv + lm) * es + act
+
+
+def draft_forward_flops(D, L, Hq, Hkv, d, F, V, B, gamma, ctx_lens) -> int:
+    M = B * gamma
+    proj = 2 * M * L * ((Hq + 2 * Hkv) * d * D + D * Hq * d + 2 * F * D + D * F)
+    att = L * sum(4 * Hq * gamma * (n + gamma) * d for n in ctx_lens)
+    lm = 2 * B * (gamma - 1) * V * D
+    return proj + att + lm
+
+
+def lm_head_bytes(V: int, D: int, rows: int, es: int = 2) -> int:
+    """LM-head GEMM + argmax: the [V, D] table once, fp32 rows in, ids out."""
+    return V * D * es + rows * D * 4 + rows * 4
+
+
+def lm_head_flops(V: int, D: int, rows: int) -> int:
+    return 2 * rows * V * D
+
+
+def attention_bytes(L: int, Hkv: int, d: int, gamma: int, ctx_lens, es: int = 2) -> int:
+    return L * sum(n + gamma for n in ctx_lens) * 2 * Hkv * d * es
+
+
+def accept_bytes(B: int, n: int) -> int:
+    return B * (2 * n + 1) * 4 + B * 8

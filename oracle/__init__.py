@@ -1,0 +1,11 @@
+"""CPU oracle for the DFlash drafter hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library.
+"""
+from .dflash_oracle import (  # noqa: F401
+    OracleCache, accept, attention, draft_forward, fuse_context, inject_kv,
+    lm_head_argmax, rmsnorm, silu, store, to_bf16,
+)

@@ -1,0 +1,250 @@
+"""Plain, slow CPU oracle of the DFlash drafter hot path (float64 numpy).
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
+cpu_baseline leg may import this module.  It shares no code with the HIP path.
+
+Every function writes a definition out in the order the pages state it, with a
+numpy matmul as the only library primitive.  Storage tensors (the fused context
+feature H_t and every key/value row that lands in the drafter's KV cache) are
+rounded once to the workload's storage type ("bf16": round to nearest even;
+"f32": IEEE single); everything else stays float64.
+
+Sources (page titles as published):
+  [JP]  "DFlash: Block Diffusion for Flash Speculative Decoding 논문 정리"
+        (juhoplayground)
+  [GL]  "DFlash 블록 확산 디코딩: 투기적 디코딩의 드래프트 비용을 상수로 만드는 법"
+        (gillilab)
+  [MG]  "ICML'26 | DFlash：用 Diffusion 模型干掉 AR Drafter，投机解码提速 6×"
+        (marsggbo)
+
+Readings taken where the pages are silent (each is also listed in the design
+notes): pre-norm residual drafter layers with a final RMSNorm before the shared
+LM head; no positional encoding, no bias; GQA with contiguous head groups and a
+1/sqrt(d) softmax scale; the block is gamma query rows (anchor at row 0, mask
+tokens after it) whose own K/V rows are stored in the cache like context rows.
+
+Parity pins live in tests/test_oracle_pins.py; every function below is pinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# storage rounding
+# ---------------------------------------------------------------------------
+def to_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (8 significant bits, ties to
+    even) and return them as float64."""
+    x = np.asarray(x, dtype=F64)
+    m, e = np.frexp(x)                   # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def store(x, storage: str) -> np.ndarray:
+    """Value of ``x`` after it is written to a tensor of the storage type."""
+    if storage == "bf16":
+        return to_bf16(x)
+    if storage == "f32":
+        return np.asarray(x, dtype=np.float32).astype(F64)
+    raise ValueError(storage)
+
+
+# ---------------------------------------------------------------------------
+# elementwise pieces
+# ---------------------------------------------------------------------------
+def rmsnorm(x, g, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: g * x / sqrt(mean(x^2) + eps)
+    ([MG] section 3.1 applies it to the fused projection)."""
+    x = np.asarray(x, dtype=F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return np.asarray(g, dtype=F64) * (x / np.sqrt(ms + eps))
+
+
+def silu(x) -> np.ndarray:
+    """SiLU(x) = x / (1 + exp(-x)), the gate of the SwiGLU FFN."""
+    x = np.asarray(x, dtype=F64)
+    return x / (1.0 + np.exp(-x))
+
+
+# ---------------------------------------------------------------------------
+# (a) context fusion
+# ---------------------------------------------------------------------------
+def fuse_context(h_tgt, w_c, g_c, eps: float, storage: str) -> np.ndarray:
+    """H_t = RMSNorm(W_c [H(l1); ...; H(l5)]).
+
+    [JP] section "KV Injection 메커니즘" (the fusion equation): the tapped target
+    states are concatenated along the feature axis, shallowest first, projected
+    by the bias-free W_c (D x 5D) and RMS-normalised; [MG] section 3.1 describes
+    the same extractor as a bias-free 5D-to-D linear map followed by RMSNorm.
+    h_tgt: list of [T, D]; w_c: [D, n*D] laid out [out, in]; returns [T, D].
+    """
+    x = np.concatenate([np.asarray(h, dtype=F64) for h in h_tgt], axis=1)
+    u = x @ np.asarray(w_c, dtype=F64).T
+    return store(rmsnorm(u, g_c, eps), storage)
+
+
+# ---------------------------------------------------------------------------
+# (b) KV injection
+# ---------------------------------------------------------------------------
+def split_qkv(w_qkv, Hq: int, Hkv: int, d: int):
+    """Rows of a packed [Q; K; V] projection matrix."""
+    w = np.asarray(w_qkv)
+    return w[: Hq * d], w[Hq * d:(Hq + Hkv) * d], w[(Hq + Hkv) * d:(Hq + 2 * Hkv) * d]
+
+
+def inject_kv(H_t, w_qkv, Hq: int, Hkv: int, d: int, storage: str):
+    """Context key/value rows of one drafter layer: K = W_K H_t, V = W_V H_t.
+
+    [JP] section "KV Injection 메커니즘": the target feature enters every layer
+    only through that layer's K and V projections (no Q, O, FFN or norm);
+    [MG] section 3.2 projects the context feature with the layer's own key and
+    value maps.  Returns ([T, Hkv, d], [T, Hkv, d]).
+    """
+    _, wk, wv = split_qkv(w_qkv, Hq, Hkv, d)
+    h = np.asarray(H_t, dtype=F64)
+    k = store(h @ np.asarray(wk, dtype=F64).T, storage)
+    v = store(h @ np.asarray(wv, dtype=F64).T, storage)
+    T = h.shape[0]
+    return k.reshape(T, Hkv, d), v.reshape(T, Hkv, d)
+
+
+class OracleCache:
+    """The drafter's per-layer KV cache of injected context rows.
+
+    [JP] section "방법론 / 추론 구조" and [GL] section "KV 주입": the injected K/V
+    are kept in the drafter's KV cache and reused across drafting iterations.
+    k[l][b] / v[l][b] are [len_b, Hkv, d] float64 arrays.
+    """
+
+    def __init__(self, L: int, B: int, Hkv: int, d: int):
+        self.k = [[np.zeros((0, Hkv, d)) for _ in range(B)] for _ in range(L)]
+        self.v = [[np.zeros((0, Hkv, d)) for _ in range(B)] for _ in range(L)]
+
+    def lens(self):
+        return [self.k[0][b].shape[0] for b in range(len(self.k[0]))]
+
+    def append(self, l: int, b: int, k, v):
+        self.k[l][b] = np.concatenate([self.k[l][b], k], axis=0)
+        self.v[l][b] = np.concatenate([self.v[l][b], v], axis=0)
+
+
+# ---------------------------------------------------------------------------
+# (c) draft forward
+# ---------------------------------------------------------------------------
+def attention(q, k, v) -> np.ndarray:
+    """Softmax attention of every query row over every key row, no mask.
+
+    [JP] "KV Injection 메커니즘": queries come from the draft block only, keys and
+    values are [context ; block] joined along the sequence; [MG] section 3.2:
+    scaled dot-product attention over that join, bidirectional inside the block.
+    q: [R, Hq, d]; k, v: [n, Hkv, d].  Query head h reads KV head h // (Hq/Hkv).
+    Returns [R, Hq, d].
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    R, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.empty((R, Hq, d))
+    for h in range(Hq):
+        j = h // G
+        s = (q[:, h, :] @ k[:, j, :].T) / np.sqrt(d)          # [R, n]
+        s = s - np.max(s, axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / np.sum(p, axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, j, :]
+    return out
+
+
+def draft_forward(dims, layers, g_final, cache: OracleCache, gamma: int,
+                  embed=None, tokens=None, override=None, storage: str = "bf16"):
+    """One forward pass of the drafter over a block of ``gamma`` rows per sequence.
+
+    [JP] "추론 구조": the block (the clean anchor from the last verify, then mask
+    tokens; "학습 방법" puts the anchor at block position 0) is decoded in a single
+    forward pass with bidirectional attention; "KV Injection 메커니즘": in layer i,
+    Q = W_Q H_d and K, V = [W_K H_t ; W_K H_d] / [W_V H_t ; W_V H_d].
+    [MG] section 3.3 runs the embedded block through every layer with the
+    injected context.  Each layer is read as a pre-norm residual block:
+        a = RMSNorm(h; g_attn); h += Attn(a) W_O^T
+        f = RMSNorm(h; g_ffn);  h += (SiLU(f W_gate^T) * (f W_up^T)) W_down^T
+    and a final RMSNorm(h; g_final) feeds the shared LM head.
+
+    dims: object with D, Hq, Hkv, d, F, eps.  layers: list of dicts with w_qkv,
+    w_o, w_gateup ([gate; up] rows), w_down, g_attn, g_ffn.  The block rows come
+    from embed[tokens] ([B, gamma] ids) or from ``override`` ([B, gamma, D]).
+    Returns (h_final [B, gamma, D] float64, block K/V per layer).
+    """
+    D, Hq, Hkv, d, F, eps = dims.D, dims.Hq, dims.Hkv, dims.d, dims.F, dims.eps
+    if override is not None:
+        h = np.asarray(override, dtype=F64).copy()
+    else:
+        h = np.asarray(embed)[np.asarray(tokens)].astype(F64)
+    B = h.shape[0]
+    assert h.shape == (B, gamma, D)
+    block_kv = []
+    for l, w in enumerate(layers):
+        a = rmsnorm(h, w["g_attn"], eps)                                  # [B, g, D]
+        qkv = a @ np.asarray(w["w_qkv"], dtype=F64).T                     # [B, g, (Hq+2Hkv)d]
+        q = qkv[..., : Hq * d].reshape(B, gamma, Hq, d)
+        kb = store(qkv[..., Hq * d:(Hq + Hkv) * d], storage).reshape(B, gamma, Hkv, d)
+        vb = store(qkv[..., (Hq + Hkv) * d:], storage).reshape(B, gamma, Hkv, d)
+        block_kv.append((kb, vb))
+        o = np.empty((B, gamma, Hq * d))
+        for b in range(B):
+            keys = np.concatenate([cache.k[l][b], kb[b]], axis=0)
+            vals = np.concatenate([cache.v[l][b], vb[b]], axis=0)
+            o[b] = attention(q[b], keys, vals).reshape(gamma, Hq * d)
+        h = h + o @ np.asarray(w["w_o"], dtype=F64).T
+        f = rmsnorm(h, w["g_ffn"], eps)
+        gu = f @ np.asarray(w["w_gateup"], dtype=F64).T
+        s = silu(gu[..., :F]) * gu[..., F:]
+        h = h + s @ np.asarray(w["w_down"], dtype=F64).T
+    return rmsnorm(h, g_final, eps), block_kv
+
+
+# ---------------------------------------------------------------------------
+# (d) LM head, argmax and greedy acceptance
+# ---------------------------------------------------------------------------
+def lm_head_argmax(h_final, lm_head):
+    """Logits of the mask rows and their argmax.
+
+    [MG] section 3.3: the LM head is applied to the block rows after the anchor
+    (the anchor's own output is not a draft), and each draft token is the argmax; [JP] "학습 방법": the LM head is the target's,
+    shared and frozen.  Ties go to the lowest token id.
+    Returns (draft [B, gamma-1] int32, top-2 gap [B, gamma-1], logits [B, gamma-1, V]).
+    """
+    z = np.asarray(h_final, dtype=F64)[:, 1:, :]
+    logits = z @ np.asarray(lm_head, dtype=F64).T
+    draft = np.argmax(logits, axis=-1).astype(np.int32)     # first maximum
+    top2 = -np.partition(-logits, 1, axis=-1)[..., :2]
+    gap = top2[..., 0] - top2[..., 1]
+    return draft, gap, logits
+
+
+def accept(draft, target):
+    """Greedy acceptance length and the next anchor.
+
+    [JP] "Preliminaries": tau counts the accepted drafts plus the target's bonus
+    token, 1 <= tau <= (drafts) + 1; [GL] "투기적 디코딩에 확산 모델을 끼워 넣다":
+    accepted tokens are kept and the ones after the first rejection dropped.
+    draft: [B, n]; target: [B, n+1] (the target's token at each draft position,
+    then the bonus).  tau = (length of the matching prefix) + 1 and the next
+    anchor is the target's token right after that prefix.
+    """
+    draft = np.asarray(draft)
+    target = np.asarray(target)
+    B, n = draft.shape
+    tau = np.zeros(B, dtype=np.int32)
+    nxt = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        m = 0
+        while m < n and int(draft[b, m]) == int(target[b, m]):
+            m += 1
+        tau[b] = m + 1
+        nxt[b] = target[b, m]
+    return tau, nxt

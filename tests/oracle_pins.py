@@ -1,0 +1,470 @@
+"""Pins that tie the CPU oracle to what the pages and the mathematics fix.
+
+Each pin takes the oracle module ``o`` so that the mutation tests can hand in a
+copy with a planted mistake and check that some pin catches it.  No pin
+re-types the oracle's formula: each one uses a closed form, an invariant, a
+brute-force loop over tiny inputs, or an independent library routine (PyTorch
+CPU) for a special case.
+"""
+from __future__ import annotations
+
+import math
+from types import SimpleNamespace
+
+import numpy as np
+import torch
+
+F64 = np.float64
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def dims(D=16, Hq=4, Hkv=2, d=8, F=24, eps=1e-6):
+    return SimpleNamespace(D=D, Hq=Hq, Hkv=Hkv, d=d, F=F, eps=eps)
+
+
+def rand_layers(rng, dm, L, std=0.3, gain_std=0.2):
+    D, Hq, Hkv, d, F = dm.D, dm.Hq, dm.Hkv, dm.d, dm.F
+    out = []
+    for _ in range(L):
+        out.append(dict(
+            w_qkv=rng.normal(0, std, ((Hq + 2 * Hkv) * d, D)),
+            w_o=rng.normal(0, std, (D, Hq * d)),
+            w_gateup=rng.normal(0, std, (2 * F, D)),
+            w_down=rng.normal(0, std, (D, F)),
+            g_attn=1 + rng.normal(0, gain_std, D),
+            g_ffn=1 + rng.normal(0, gain_std, D),
+        ))
+    return out
+
+
+def cache_with(o, L, B, Hkv, d, lens, rng):
+    c = o.OracleCache(L, B, Hkv, d)
+    for l in range(L):
+        for b in range(B):
+            c.append(l, b, rng.normal(0, 1, (lens[b], Hkv, d)), rng.normal(0, 1, (lens[b], Hkv, d)))
+    return c
+
+
+# ---------------------------------------------------------------------------
+# storage rounding
+# ---------------------------------------------------------------------------
+def pin_bf16_values(o):
+    # Hand-worked values: bf16 keeps 8 significant bits; ties go to the even mantissa.
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8 + 2 ** -20), 3.0, 0.0,
+                  2 ** -130 * 3, 65504.0])
+    want = np.array([1.0, 1.0, 1 + 2 ** -6, -(1 + 2 ** -7), 3.0, 0.0, 2 ** -130 * 3, 65536.0])
+    got = o.to_bf16(x)
+    assert np.array_equal(got, want), (got, want)
+
+
+def pin_bf16_vs_torch(o):
+    # Special case reducing to a library routine: fp32 -> bf16 conversion in torch.
+    x = _rng(1).normal(0, 3, 4096).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(o.to_bf16(x.astype(F64)), ref)
+    assert np.array_equal(o.store(x.astype(F64), "f32"), x.astype(F64))
+
+
+# ---------------------------------------------------------------------------
+# elementwise
+# ---------------------------------------------------------------------------
+def pin_rmsnorm_torch(o):
+    rng = _rng(2)
+    x = rng.normal(0, 2, (5, 32))
+    g = 1 + rng.normal(0, 0.3, 32)
+    m = torch.nn.RMSNorm(32, eps=1e-6, dtype=torch.float64)
+    with torch.no_grad():
+        m.weight.copy_(torch.from_numpy(g))
+        ref = m(torch.from_numpy(x)).numpy()
+    assert np.allclose(o.rmsnorm(x, g, 1e-6), ref, rtol=1e-13, atol=1e-13)
+
+
+def pin_rmsnorm_invariant(o):
+    # mean((y/g)^2) = ms / (ms + eps) exactly in real arithmetic.
+    rng = _rng(3)
+    x = rng.normal(0, 0.01, (7, 64))         # small ms so eps matters
+    g = 1 + rng.normal(0, 0.3, 64)
+    eps = 1e-4
+    y = o.rmsnorm(x, g, eps)
+    ms = np.mean(x * x, axis=1)
+    assert np.allclose(np.mean((y / g) ** 2, axis=1), ms / (ms + eps), rtol=1e-12)
+
+
+def pin_silu(o):
+    x = np.linspace(-12, 12, 241)
+    ref = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    assert np.allclose(o.silu(x), ref, rtol=1e-14, atol=1e-15)
+    assert o.silu(np.array([0.0]))[0] == 0.0
+
+
+# ---------------------------------------------------------------------------
+# (a) fusion
+# ---------------------------------------------------------------------------
+def pin_fuse_selector(o):
+    # W_c = [0 .. I .. 0] with the identity in block k: H_t = RMSNorm(H(l_k)).
+    rng = _rng(4)
+    T, D, n = 6, 16, 5
+    hs = [rng.normal(0, 1 + k, (T, D)) for k in range(n)]
+    g = 1 + rng.normal(0, 0.2, D)
+    for k in range(n):
+        w = np.zeros((D, n * D))
+        w[:, k * D:(k + 1) * D] = np.eye(D)
+        got = o.fuse_context(hs, w, g, 1e-6, "f32")
+        ms = np.mean(hs[k] ** 2, axis=1, keepdims=True)
+        want = (g * hs[k] / np.sqrt(ms + 1e-6)).astype(np.float32).astype(F64)
+        assert np.allclose(got, want, rtol=1e-6, atol=1e-7), k
+
+
+def pin_fuse_torch_linear(o):
+    # Library routine: torch Linear(5D -> D, no bias) then RMSNorm, on tiny shapes.
+    rng = _rng(5)
+    T, D, n = 9, 16, 5
+    hs = [rng.normal(0, 1, (T, D)) for _ in range(n)]
+    w = rng.normal(0, 0.1, (D, n * D))
+    g = 1 + rng.normal(0, 0.2, D)
+    lin = torch.nn.Linear(n * D, D, bias=False, dtype=torch.float64)
+    nrm = torch.nn.RMSNorm(D, eps=1e-6, dtype=torch.float64)
+    with torch.no_grad():
+        lin.weight.copy_(torch.from_numpy(w))
+        nrm.weight.copy_(torch.from_numpy(g))
+        ref = nrm(lin(torch.cat([torch.from_numpy(h) for h in hs], dim=-1))).numpy()
+    got = o.fuse_context(hs, w, g, 1e-6, "bf16")
+    # bf16 storage: within half an ulp (2^-9 relative) of the exact value
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+    assert np.array_equal(got, o.to_bf16(got))
+
+
+# ---------------------------------------------------------------------------
+# (b) injection
+# ---------------------------------------------------------------------------
+def pin_inject_identity(o):
+    # D = Hkv*d, W_K = I and W_V = 2I: cache K rows equal H_t, V rows 2*H_t, and
+    # the W_Q rows (NaN here) are never used.
+    Hkv, d = 2, 8
+    D = Hkv * d
+    T = 5
+    H = np.arange(T * D, dtype=F64).reshape(T, D) / 7.0     # position-coded rows
+    want_k = H.astype(np.float32).astype(F64)
+    want_v = (2 * H).astype(np.float32).astype(F64)
+    for Hq in (Hkv, 2 * Hkv):
+        w = np.concatenate([np.full((Hq * d, D), np.nan), np.eye(D), 2 * np.eye(D)], axis=0)
+        k, v = o.inject_kv(H, w, Hq, Hkv, d, "f32")
+        assert k.shape == (T, Hkv, d) and v.shape == (T, Hkv, d)
+        assert np.array_equal(k.reshape(T, D), want_k)
+        assert np.array_equal(v.reshape(T, D), want_v)
+        # head-major split: head j of row t holds H[t, j*d:(j+1)*d]
+        assert np.array_equal(k[3, 1], want_k[3, d:2 * d])
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+def _brute_attention(q, k, v):
+    # Pure-Python loops, float64.
+    R, Hq, d = q.shape
+    n, Hkv, _ = k.shape
+    G = Hq // Hkv
+    out = np.zeros((R, Hq, d))
+    for r in range(R):
+        for h in range(Hq):
+            j = h // G
+            s = [sum(q[r, h, c] * k[t, j, c] for c in range(d)) / math.sqrt(d) for t in range(n)]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = sum(e)
+            for c in range(d):
+                out[r, h, c] = sum(e[t] * v[t, j, c] for t in range(n)) / z
+    return out
+
+
+def pin_attention_bruteforce(o):
+    rng = _rng(7)
+    for (R, Hq, Hkv, d, n) in [(3, 4, 2, 4, 6), (4, 2, 2, 3, 1), (2, 6, 3, 5, 8)]:
+        q = rng.normal(0, 1, (R, Hq, d))
+        k = rng.normal(0, 1, (n, Hkv, d))
+        v = rng.normal(0, 1, (n, Hkv, d))
+        assert np.allclose(o.attention(q, k, v), _brute_attention(q, k, v), rtol=1e-12, atol=1e-12)
+
+
+def pin_attention_closed_forms(o):
+    rng = _rng(8)
+    R, Hq, Hkv, d, n = 4, 4, 2, 8, 9
+    q = rng.normal(0, 1, (R, Hq, d))
+    k = rng.normal(0, 1, (n, Hkv, d))
+    # equal value rows -> output equals that row
+    vrow = rng.normal(0, 1, (Hkv, d))
+    v = np.broadcast_to(vrow, (n, Hkv, d)).copy()
+    out = o.attention(q, k, v)
+    for h in range(Hq):
+        assert np.allclose(out[:, h], vrow[h // (Hq // Hkv)], atol=1e-12)
+    # Q = 0 -> mean of the value rows
+    v = rng.normal(0, 1, (n, Hkv, d))
+    out = o.attention(np.zeros_like(q), k, v)
+    for h in range(Hq):
+        assert np.allclose(out[:, h], v[:, h // (Hq // Hkv)].mean(axis=0), atol=1e-12)
+    # single key -> its value row
+    out = o.attention(q, k[:1], v[:1])
+    for h in range(Hq):
+        assert np.allclose(out[:, h], v[0, h // (Hq // Hkv)], atol=1e-12)
+
+
+def pin_attention_sdpa(o):
+    # Library routine: torch SDPA with grouped KV heads (expanded per group).
+    rng = _rng(9)
+    R, Hq, Hkv, d, n = 5, 8, 2, 16, 11
+    q = rng.normal(0, 1, (R, Hq, d))
+    k = rng.normal(0, 1, (n, Hkv, d))
+    v = rng.normal(0, 1, (n, Hkv, d))
+    G = Hq // Hkv
+    tq = torch.from_numpy(q).permute(1, 0, 2)                              # [Hq, R, d]
+    tk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, dim=0)  # [Hq, n, d]
+    tv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).permute(1, 0, 2).numpy()
+    assert np.allclose(o.attention(q, k, v), ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_attention_permutations(o):
+    rng = _rng(10)
+    R, Hq, Hkv, d, n = 6, 4, 1, 8, 12
+    q = rng.normal(0, 1, (R, Hq, d))
+    k = rng.normal(0, 1, (n, Hkv, d))
+    v = rng.normal(0, 1, (n, Hkv, d))
+    base = o.attention(q, k, v)
+    p = rng.permutation(n)
+    assert np.allclose(o.attention(q, k[p], v[p]), base, atol=1e-12)
+    pr = rng.permutation(R)
+    assert np.allclose(o.attention(q[pr], k, v), base[pr], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# draft forward
+# ---------------------------------------------------------------------------
+def _torch_layer_forward(dm, layers, g_final, ctx_k, ctx_v, h0):
+    """Library-routine composition (float64 CPU): RMSNorm modules, SDPA over the
+    joined [context; block] keys with grouped heads, SiLU; one sequence, f32 storage
+    of the block K/V is emulated by float32 round trips."""
+    D, Hq, Hkv, d, F, eps = dm.D, dm.Hq, dm.Hkv, dm.d, dm.F, dm.eps
+    G = Hq // Hkv
+    h = torch.from_numpy(h0.copy())
+    g_ = h.shape[0]
+
+    def norm(x, g):
+        m = torch.nn.RMSNorm(D, eps=eps, dtype=torch.float64)
+        with torch.no_grad():
+            m.weight.copy_(torch.from_numpy(np.asarray(g, dtype=F64)))
+            return m(x)
+
+    with torch.no_grad():
+        for l, w in enumerate(layers):
+            a = norm(h, w["g_attn"])
+            wq = torch.from_numpy(w["w_qkv"][: Hq * d])
+            wk = torch.from_numpy(w["w_qkv"][Hq * d:(Hq + Hkv) * d])
+            wv = torch.from_numpy(w["w_qkv"][(Hq + Hkv) * d:])
+            q = torch.nn.functional.linear(a, wq).reshape(g_, Hq, d).permute(1, 0, 2)
+            kb = torch.nn.functional.linear(a, wk).float().double().reshape(g_, Hkv, d)
+            vb = torch.nn.functional.linear(a, wv).float().double().reshape(g_, Hkv, d)
+            K = torch.cat([torch.from_numpy(ctx_k[l]), kb], 0).permute(1, 0, 2).repeat_interleave(G, 0)
+            Vv = torch.cat([torch.from_numpy(ctx_v[l]), vb], 0).permute(1, 0, 2).repeat_interleave(G, 0)
+            att = torch.nn.functional.scaled_dot_product_attention(q, K, Vv)      # [Hq, g, d]
+            att = att.permute(1, 0, 2).reshape(g_, Hq * d)
+            h = h + torch.nn.functional.linear(att, torch.from_numpy(w["w_o"]))
+            f = norm(h, w["g_ffn"])
+            gu = torch.nn.functional.linear(f, torch.from_numpy(w["w_gateup"]))
+            s = torch.nn.functional.silu(gu[:, :F]) * gu[:, F:]
+            h = h + torch.nn.functional.linear(s, torch.from_numpy(w["w_down"]))
+        return norm(h, g_final).numpy()
+
+
+def pin_draft_torch_composition(o):
+    rng = _rng(11)
+    dm = dims()
+    L, B, gamma = 2, 2, 5
+    layers = rand_layers(rng, dm, L)
+    gf = 1 + rng.normal(0, 0.2, dm.D)
+    lens = [7, 0]
+    cache = cache_with(o, L, B, dm.Hkv, dm.d, lens, rng)
+    h0 = rng.normal(0, 1, (B, gamma, dm.D))
+    got, _ = o.draft_forward(dm, layers, gf, cache, gamma, override=h0, storage="f32")
+    for b in range(B):
+        ref = _torch_layer_forward(dm, layers, gf, [cache.k[l][b] for l in range(L)],
+                                   [cache.v[l][b] for l in range(L)], h0[b])
+        assert np.allclose(got[b], ref, rtol=1e-9, atol=1e-9), b
+
+
+def pin_draft_zero_branches(o):
+    # W_O = 0 and W_down = 0: the residual stream passes through unchanged, so
+    # h_final = RMSNorm(embedding; g_final) and logits = E . that, in closed form.
+    rng = _rng(12)
+    dm = dims()
+    L, B, gamma, V = 3, 2, 4, 40
+    layers = rand_layers(rng, dm, L)
+    for w in layers:
+        w["w_o"][:] = 0
+        w["w_down"][:] = 0
+    gf = 1 + rng.normal(0, 0.2, dm.D)
+    E = rng.normal(0, 1, (V, dm.D))
+    tok = rng.integers(0, V, (B, gamma))
+    cache = cache_with(o, L, B, dm.Hkv, dm.d, [3, 5], rng)
+    got, _ = o.draft_forward(dm, layers, gf, cache, gamma, embed=E, tokens=tok, storage="f32")
+    h0 = E[tok]
+    want = gf * h0 / np.sqrt(np.mean(h0 ** 2, axis=-1, keepdims=True) + dm.eps)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+    d, _, logits = o.lm_head_argmax(got, E)
+    assert np.allclose(logits, np.einsum("bgd,vd->bgv", want[:, 1:], E), rtol=1e-12, atol=1e-10)
+
+
+def pin_draft_visibility(o):
+    # Every block query sees every context row and every block row (no mask):
+    # perturbing any one of them changes every query's output.
+    rng = _rng(13)
+    dm = dims()
+    L, B, gamma = 1, 1, 4
+    layers = rand_layers(rng, dm, L)
+    gf = np.ones(dm.D)
+    n = 6
+    cache = cache_with(o, L, B, dm.Hkv, dm.d, [n], rng)
+    h0 = rng.normal(0, 1, (B, gamma, dm.D))
+    base, _ = o.draft_forward(dm, layers, gf, cache, gamma, override=h0, storage="f32")
+    for t in (0, n // 2, n - 1):
+        c2 = o.OracleCache(L, B, dm.Hkv, dm.d)
+        k = cache.k[0][0].copy()
+        v = cache.v[0][0].copy()
+        k[t] += 0.5
+        v[t] -= 0.5
+        c2.append(0, 0, k, v)
+        out, _ = o.draft_forward(dm, layers, gf, c2, gamma, override=h0, storage="f32")
+        assert np.all(np.max(np.abs(out - base), axis=-1) > 1e-6), t
+    for i in range(gamma):
+        h1 = h0.copy()
+        h1[0, i] += 0.5
+        out, _ = o.draft_forward(dm, layers, gf, cache, gamma, override=h1, storage="f32")
+        others = [r for r in range(gamma) if r != i]
+        assert np.all(np.max(np.abs(out[0, others] - base[0, others]), axis=-1) > 1e-6), i
+
+
+def pin_draft_permutations(o):
+    rng = _rng(14)
+    dm = dims()
+    L, B, gamma = 2, 1, 6
+    layers = rand_layers(rng, dm, L)
+    gf = np.ones(dm.D)
+    n = 9
+    cache = cache_with(o, L, B, dm.Hkv, dm.d, [n], rng)
+    h0 = rng.normal(0, 1, (B, gamma, dm.D))
+    base, _ = o.draft_forward(dm, layers, gf, cache, gamma, override=h0, storage="f32")
+    # permuting block rows permutes outputs (no positional encoding)
+    p = rng.permutation(gamma)
+    out, _ = o.draft_forward(dm, layers, gf, cache, gamma, override=h0[:, p], storage="f32")
+    assert np.allclose(out, base[:, p], rtol=1e-12, atol=1e-12)
+    # permuting context rows leaves outputs unchanged
+    pc = rng.permutation(n)
+    c2 = o.OracleCache(L, B, dm.Hkv, dm.d)
+    for l in range(L):
+        c2.append(l, 0, cache.k[l][0][pc], cache.v[l][0][pc])
+    out, _ = o.draft_forward(dm, layers, gf, c2, gamma, override=h0, storage="f32")
+    assert np.allclose(out, base, rtol=1e-12, atol=1e-12)
+
+
+def pin_draft_block_kv_storage(o):
+    # The block's own K/V rows are rounded like cache rows: with bf16 storage
+    # every returned block key is bf16-exact, and it differs from f32 storage.
+    rng = _rng(15)
+    dm = dims()
+    layers = rand_layers(rng, dm, 1)
+    cache = cache_with(o, 1, 1, dm.Hkv, dm.d, [4], rng)
+    h0 = rng.normal(0, 1, (1, 3, dm.D))
+    a, kv_a = o.draft_forward(dm, layers, np.ones(dm.D), cache, 3, override=h0, storage="bf16")
+    b, kv_b = o.draft_forward(dm, layers, np.ones(dm.D), cache, 3, override=h0, storage="f32")
+    kb = kv_a[0][0]
+    assert np.array_equal(kb, o.to_bf16(kb))
+    assert not np.array_equal(kv_a[0][0], kv_b[0][0])
+
+
+# ---------------------------------------------------------------------------
+# argmax / accept
+# ---------------------------------------------------------------------------
+def pin_argmax_planted(o):
+    # Orthonormal block rows z_r = e_r and a planted LM-head row E[v_r] = 5 e_r:
+    # the planted token has logit 5, every other logit is small.
+    rng = _rng(16)
+    B, g, D, V = 2, 5, 12, 50
+    rows = B * (g - 1)
+    z = np.zeros((B, g, D))
+    E = rng.normal(0, 0.1, (V, D))
+    planted = rng.choice(V, size=rows, replace=False)
+    r = 0
+    for b in range(B):
+        z[b, 0, D - 1] = 1.0
+        for i in range(1, g):
+            z[b, i, r] = 1.0
+            E[planted[r], r] = 5.0
+            r += 1
+    d, gap, logits = o.lm_head_argmax(z, E)
+    assert np.array_equal(d.reshape(-1), planted)
+    assert np.all(gap > 3.0)
+    # the anchor row (row 0) is not drafted even if it has the largest logit
+    z2 = z.copy()
+    z2[:, 0] = 100.0
+    d2, _, l2 = o.lm_head_argmax(z2, E)
+    assert l2.shape == (B, g - 1, V) and np.array_equal(d2, d)
+
+
+def pin_argmax_ties(o):
+    z = np.zeros((1, 3, 4))
+    z[0, 1] = [1, 0, 0, 0]
+    z[0, 2] = [0, 1, 0, 0]
+    E = np.zeros((6, 4))
+    E[2, 0] = 1.0
+    E[4, 0] = 1.0          # tie with token 2 -> lowest id wins
+    E[5, 1] = 3.0
+    E[1, 1] = 2.0
+    d, gap, _ = o.lm_head_argmax(z, E)
+    assert list(d[0]) == [2, 5]
+    assert gap[0, 0] == 0.0 and gap[0, 1] == 1.0
+
+
+def pin_accept_cases(o):
+    n = 6
+    d = np.array([[1, 2, 3, 4, 5, 6]] * 5)
+    t = np.array([
+        [1, 2, 3, 4, 5, 6, 7],      # all match -> tau = n+1, next = bonus
+        [9, 2, 3, 4, 5, 6, 7],      # mismatch at 0 -> tau 1
+        [1, 2, 9, 4, 5, 6, 7],      # mismatch at 2 -> tau 3 (later matches ignored)
+        [1, 2, 3, 4, 5, 9, 7],      # mismatch at n-1 -> tau n
+        [1, 9, 9, 9, 9, 9, 9],
+    ])
+    tau, nxt = o.accept(d, t)
+    assert list(tau) == [7, 1, 3, 6, 2]
+    assert list(nxt) == [7, 9, 9, 9, 9]
+    assert np.all((tau >= 1) & (tau <= n + 1))
+
+
+def expected_tau(p) -> float:
+    """E[tau] = sum_{k=0..n} prod_{j<k} p_j for independent per-position matches."""
+    tot, pr = 0.0, 1.0
+    for k in range(len(p) + 1):
+        tot += pr
+        if k < len(p):
+            pr *= p[k]
+    return tot
+
+
+def pin_accept_expectation(o):
+    # Monte Carlo over seeded blocks against the closed form (3 sigma).
+    rng = _rng(17)
+    for p in (np.full(15, 0.8), 0.9 - 0.4 * np.arange(15) / 14):
+        N, n = 20000, len(p)
+        d = rng.integers(0, 1000, (N, n))
+        match = rng.random((N, n)) < p
+        t = np.where(match, d, (d + rng.integers(1, 1000, (N, n))) % 1000)
+        t = np.concatenate([t, rng.integers(0, 1000, (N, 1))], axis=1)
+        tau, _ = o.accept(d, t)
+        mu = expected_tau(p)
+        sd = tau.std() / math.sqrt(N)
+        assert abs(tau.mean() - mu) < 3.5 * sd + 1e-9, (tau.mean(), mu)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,52 @@
+"""Seeded input generators: determinism, storage exactness and workload shapes."""
+import numpy as np
+
+from dflash_inputs import CONFIGS, Inputs, bf16_round_f32, build_target_np, shrink
+from dflash_inputs.gen import CHUNK
+
+
+def test_seeded_and_storage_exact():
+    cfg = shrink(CONFIGS[2], D=256, F=512, V=1000, L=2, ctx=(40,))
+    a, b = Inputs(cfg), Inputs(cfg)
+    assert np.array_equal(a.w_qkv(1), b.w_qkv(1))
+    assert not np.array_equal(a.w_qkv(0), a.w_qkv(1))
+    w = a.w_c()
+    assert w.dtype == np.float32 and w.shape == (256, 1280)
+    assert np.array_equal(w, bf16_round_f32(w.copy()))         # bf16-exact values
+    assert abs(w.std() - 0.02) < 0.002
+    h = a.ctx_states()
+    assert len(h) == 5 and h[0].shape == (40, 256) and abs(h[0].std() - 1) < 0.1
+    f32 = Inputs(CONFIGS[1]).w_c()
+    assert not np.array_equal(f32, bf16_round_f32(f32.copy()))  # fp32 workload keeps fp32
+
+
+def test_chunked_generation_is_chunk_local():
+    cfg = shrink(CONFIGS[2], D=2048, V=4096, ctx=(8,))
+    e = Inputs(cfg).embed()              # 8M elements -> 2 chunks
+    assert e.size > CHUNK
+    e2 = Inputs(cfg).embed()
+    assert np.array_equal(e[:16], e2[:16]) and np.array_equal(e[-16:], e2[-16:])
+
+
+def test_workload_shapes():
+    c4 = CONFIGS[4]
+    assert c4.B == 16 and len(c4.ctx) == 16
+    assert all(1024 <= n <= 4096 for n in c4.ctx)
+    assert CONFIGS[5].gammas == (8, 16, 32)
+    p = CONFIGS[5].match_probs(16)
+    assert np.isclose(p[0], 0.9) and np.isclose(p[-1], 0.5)
+    assert np.allclose(CONFIGS[2].match_probs(16), 0.8)
+
+
+def test_block_tokens_and_targets():
+    cfg = CONFIGS[4]
+    inp = Inputs(cfg)
+    t = inp.block_tokens(16)
+    assert t.shape == (16, 16) and np.all(t[:, 1:] == cfg.V - 1)
+    assert np.all(t[:, 0] < cfg.V - 1)
+    match, r, bonus = inp.verify_draws(0, 16)
+    d = np.random.default_rng(0).integers(0, cfg.V, (16, 15))
+    tgt = build_target_np(d, match, r, bonus, cfg.V)
+    assert tgt.shape == (16, 16)
+    assert np.array_equal(tgt[:, :15] == d, match)
+    assert np.all((tgt >= 0) & (tgt < cfg.V))

@@ -1,0 +1,77 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+at least one pin catches each of them: evidence that the pins constrain every
+part of the oracle, not just the parts that happened to be exercised."""
+import inspect
+import types
+
+import pytest
+
+from oracle import dflash_oracle
+from tests.oracle_pins import ALL_PINS
+
+SRC = inspect.getsource(dflash_oracle)
+
+# (name, text in the oracle, replacement)
+MUTANTS = [
+    ("bf16_truncates", "np.rint(m * 256.0)", "np.trunc(m * 256.0)"),
+    ("bf16_ties_away", "np.rint(m * 256.0)", "np.sign(m) * np.floor(np.abs(m) * 256.0 + 0.5)"),
+    ("rms_no_eps", "np.sqrt(ms + eps)", "np.sqrt(ms)"),
+    ("rms_sum_not_mean", "ms = np.mean(x * x, axis=-1, keepdims=True)",
+     "ms = np.sum(x * x, axis=-1, keepdims=True)"),
+    ("rms_no_gain", "return np.asarray(g, dtype=F64) * (x / np.sqrt(ms + eps))",
+     "return (x / np.sqrt(ms + eps))"),
+    ("silu_is_sigmoid", "return x / (1.0 + np.exp(-x))", "return 1.0 / (1.0 + np.exp(-x))"),
+    ("fuse_reversed_sources", "for h in h_tgt], axis=1)", "for h in h_tgt[::-1]], axis=1)"),
+    ("fuse_no_norm", "return store(rmsnorm(u, g_c, eps), storage)", "return store(u, storage)"),
+    ("inject_k_v_swapped", "_, wk, wv = split_qkv(w_qkv, Hq, Hkv, d)",
+     "_, wv, wk = split_qkv(w_qkv, Hq, Hkv, d)"),
+    ("inject_uses_wq", "_, wk, wv = split_qkv(w_qkv, Hq, Hkv, d)",
+     "wk, _, wv = split_qkv(w_qkv, Hq, Hkv, d)"),
+    ("attn_head_map_mod", "j = h // G", "j = h % Hkv"),
+    ("attn_no_scale", "/ np.sqrt(d)          # [R, n]", "# [R, n]"),
+    ("attn_causal", "s = s - np.max(s, axis=1, keepdims=True)",
+     "s = s + np.triu(np.full(s.shape, -1e30), 1 + s.shape[1] - s.shape[0]); "
+     "s = s - np.max(s, axis=1, keepdims=True)"),
+    ("attn_no_normalise", "p = p / np.sum(p, axis=1, keepdims=True)", "p = p"),
+    ("draft_block_kv_unrounded",
+     "kb = store(qkv[..., Hq * d:(Hq + Hkv) * d], storage)", "kb = (qkv[..., Hq * d:(Hq + Hkv) * d])"),
+    ("draft_context_ignored",
+     "keys = np.concatenate([cache.k[l][b], kb[b]], axis=0)\n"
+     "            vals = np.concatenate([cache.v[l][b], vb[b]], axis=0)",
+     "keys = kb[b]\n            vals = vb[b]"),
+    ("draft_no_attn_residual", "h = h + o @ np.asarray(w[\"w_o\"], dtype=F64).T",
+     "h = o @ np.asarray(w[\"w_o\"], dtype=F64).T"),
+    ("draft_gains_swapped", "a = rmsnorm(h, w[\"g_attn\"], eps)", "a = rmsnorm(h, w[\"g_ffn\"], eps)"),
+    ("draft_gate_up_swapped", "s = silu(gu[..., :F]) * gu[..., F:]", "s = silu(gu[..., F:]) * gu[..., :F]"),
+    ("draft_no_final_norm", "return rmsnorm(h, g_final, eps), block_kv", "return h, block_kv"),
+    ("draft_ffn_on_unnormed", "gu = f @ np.asarray(w[\"w_gateup\"], dtype=F64).T",
+     "gu = h @ np.asarray(w[\"w_gateup\"], dtype=F64).T"),
+    ("lm_includes_anchor", "z = np.asarray(h_final, dtype=F64)[:, 1:, :]",
+     "z = np.asarray(h_final, dtype=F64)[:, :-1, :]"),
+    ("argmax_last_tie", "draft = np.argmax(logits, axis=-1).astype(np.int32)",
+     "draft = (logits.shape[-1] - 1 - np.argmax(logits[..., ::-1], axis=-1)).astype(np.int32)"),
+    ("accept_no_bonus", "tau[b] = m + 1", "tau[b] = m"),
+    ("accept_counts_all_matches", "while m < n and int(draft[b, m]) == int(target[b, m]):\n            m += 1",
+     "m = int(np.sum(draft[b] == target[b, :n]))"),
+    ("accept_next_is_draft", "nxt[b] = target[b, m]", "nxt[b] = draft[b, min(m, n - 1)]"),
+]
+
+
+def _mutant_module(old, new):
+    assert SRC.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = SRC.replace(old, new, 1)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    mod = _mutant_module(old, new)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} survived every pin"
