@@ -1,0 +1,128 @@
+"""ctypes binding of libdflash (include/dflash.h): argument marshalling only.
+
+Every function takes raw device pointers (ints), sizes and a HIP stream handle,
+and raises DFlashError on a non-OK status.  The library must have been built
+(``__graft_entry__.build()``); loading fails loudly otherwise: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+ARGMAX, ACCEPT = 1, 2
+MAX_BATCH, MAX_TGT_LAYERS, MIN_GAMMA, MAX_GAMMA = 64, 8, 2, 33
+
+EXPORTED = ("dflash_version", "dflash_last_error", "dflash_workspace_size", "dflash_fuse_context",
+            "dflash_inject_kv", "dflash_draft_forward", "dflash_argmax_accept")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("D", c_int32), ("L", c_int32), ("Hq", c_int32), ("Hkv", c_int32),
+                ("head_dim", c_int32), ("F", c_int32), ("V", c_int32), ("n_tgt_layers", c_int32),
+                ("mask_id", c_int32), ("rms_eps", c_float), ("dtype", c_int32), ("cache_dtype", c_int32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("w_c", "g_c", "w_qkv", "w_o", "w_gateup", "w_down",
+                                        "g_attn", "g_ffn", "g_final", "embed", "lm_head")]
+
+
+class KVCache(ctypes.Structure):
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("B", c_int32), ("cap", c_int32),
+                ("len", POINTER(c_int32))]
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"dflash status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load libdflash.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.dflash_version.restype = c_char_p
+    lib.dflash_version.argtypes = []
+    lib.dflash_last_error.restype = c_char_p
+    lib.dflash_last_error.argtypes = []
+    lib.dflash_workspace_size.restype = c_int32
+    lib.dflash_workspace_size.argtypes = [POINTER(Dims), c_int32, c_int32, c_int32, POINTER(c_size_t)]
+    lib.dflash_fuse_context.restype = c_int32
+    lib.dflash_fuse_context.argtypes = [POINTER(Dims), POINTER(Weights), POINTER(c_void_p), c_int64, c_int32,
+                                        c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dflash_inject_kv.restype = c_int32
+    lib.dflash_inject_kv.argtypes = [POINTER(Dims), POINTER(Weights), c_void_p, POINTER(c_int32),
+                                     POINTER(KVCache), c_void_p, c_size_t, c_void_p]
+    lib.dflash_draft_forward.restype = c_int32
+    lib.dflash_draft_forward.argtypes = [POINTER(Dims), POINTER(Weights), POINTER(KVCache), c_void_p, c_void_p,
+                                         c_int32, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dflash_argmax_accept.restype = c_int32
+    lib.dflash_argmax_accept.argtypes = [POINTER(Dims), POINTER(Weights), c_uint32, c_void_p, c_int32, c_int32,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_size_t, c_void_p]
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load().dflash_version().decode()
+
+
+def last_error() -> str:
+    return load().dflash_last_error().decode()
+
+
+def _check(st: int):
+    if st != OK:
+        raise DFlashError(st, last_error())
+
+
+def _p(x):
+    return None if x is None or x == 0 else c_void_p(int(x))
+
+
+def workspace_size(dims: Dims, B: int, gamma: int, max_rows: int) -> int:
+    out = c_size_t(0)
+    _check(load().dflash_workspace_size(ctypes.byref(dims), B, gamma, max_rows, ctypes.byref(out)))
+    return out.value
+
+
+def fuse_context(dims: Dims, w: Weights, h_tgt, ld: int, T: int, H_t, ws, ws_bytes: int, stream=0):
+    arr = (c_void_p * max(1, len(h_tgt)))(*[int(p) for p in h_tgt])
+    _check(load().dflash_fuse_context(ctypes.byref(dims), ctypes.byref(w), arr, ld, T, _p(H_t), _p(ws),
+                                      ws_bytes, _p(stream)))
+
+
+def inject_kv(dims: Dims, w: Weights, H_t, rows_per_seq, cache: KVCache, ws, ws_bytes: int, stream=0):
+    rows = (c_int32 * max(1, len(rows_per_seq)))(*rows_per_seq)
+    _check(load().dflash_inject_kv(ctypes.byref(dims), ctypes.byref(w), _p(H_t), rows, ctypes.byref(cache),
+                                   _p(ws), ws_bytes, _p(stream)))
+
+
+def draft_forward(dims: Dims, w: Weights, cache: KVCache, block_tokens, embed_override, gamma: int, h_final,
+                  ws, ws_bytes: int, stream=0):
+    _check(load().dflash_draft_forward(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(cache),
+                                       _p(block_tokens), _p(embed_override), gamma, _p(h_final), _p(ws),
+                                       ws_bytes, _p(stream)))
+
+
+def argmax_accept(dims: Dims, w: Weights, flags: int, h_final, B: int, gamma: int, draft, target, tau,
+                  next_anchor, logits_dbg, top2_gap, ws, ws_bytes: int, stream=0):
+    _check(load().dflash_argmax_accept(ctypes.byref(dims), ctypes.byref(w) if w is not None else None, flags,
+                                       _p(h_final), B, gamma, _p(draft), _p(target), _p(tau), _p(next_anchor),
+                                       _p(logits_dbg), _p(top2_gap), _p(ws), ws_bytes, _p(stream)))

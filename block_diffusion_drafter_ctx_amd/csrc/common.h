@@ -1,0 +1,123 @@
+// Device-side helpers shared by the gfx950 kernels of the DFlash drafter path:
+// bf16 storage conversions, the 16x16x32 bf16 MFMA wrapper, fp32 -> (hi, lo)
+// bf16 splitting and wave-level reductions.  gfx950 only (64-wide waves).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 storage
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Storage-type traits: bf16 is held as uint16_t bit patterns.
+template <typename T> struct Store;
+template <> struct Store<uint16_t> {
+  static __device__ __forceinline__ float ld(const uint16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void st(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+template <> struct Store<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+
+// Pack 8 floats as bf16 (hi) and the bf16 of the remainder (lo): x ~= hi + lo
+// with |x - hi - lo| <= 2^-16 |x| (so an MFMA pair on (hi, lo) keeps ~16
+// significant bits of an fp32 activation against exact bf16 weights).
+__device__ __forceinline__ void split8(const float* x, uint4& hi, uint4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint16_t hb = f32_to_bf16(x[i]);
+    h[i] = hb;
+    l[i] = f32_to_bf16(x[i] - bf16_to_f32(hb));
+  }
+  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+}
+
+// D += A (16 rows x 32 k) * B (32 k x 16 cols).  Lane l supplies A row (l % 16)
+// and B column (l % 16), k-slots 8*(l/16)..+7 of each; D lane l holds rows
+// 4*(l/16)+r, column l%16 (r = 0..3).  The k-slot -> k map only has to agree
+// between A and B.
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Sum over a workgroup of up to 1024 threads; `red` holds >= 16 floats of LDS.
+// Every thread returns the total.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];   // fixed order: deterministic
+  return t;
+}
+
+// Top-2 candidate (value, index) with "larger value, then lower index" order.
+struct Top2 {
+  float v1;
+  int i1;
+  float v2;
+};
+
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
+  Top2 r;
+  if (better(b.v1, b.i1, a.v1, a.i1)) {
+    r.v1 = b.v1; r.i1 = b.i1; r.v2 = fmaxf(a.v1, b.v2);
+  } else {
+    r.v1 = a.v1; r.i1 = a.i1; r.v2 = fmaxf(a.v2, b.v1);
+  }
+  return r;
+}
+
+__device__ __forceinline__ Top2 top2_push(Top2 a, float v, int i) {
+  Top2 b{v, i, -INFINITY};
+  return top2_merge(a, b);
+}
+
+__device__ __forceinline__ Top2 top2_shfl_xor(Top2 a, int m) {
+  Top2 b;
+  b.v1 = __shfl_xor(a.v1, m, kWave);
+  b.i1 = __shfl_xor(a.i1, m, kWave);
+  b.v2 = __shfl_xor(a.v2, m, kWave);
+  return b;
+}
+
+}  // namespace dflash

@@ -1,0 +1,582 @@
+// C-ABI entry points of libdflash: argument validation, workspace planning and
+// the launch sequence of each hot-path stage.  Everything that can be checked
+// on the host is checked before the first HIP call, so a rejected call enqueues
+// nothing and touches no output.
+#include "../../include/dflash.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "launch.h"
+
+using namespace dflash;
+
+namespace {
+
+thread_local std::string g_err;
+
+dflash_status fail(dflash_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dflash_status ok() {
+  g_err.clear();
+  return DFLASH_OK;
+}
+
+#define DF_REQUIRE(cond, st, ...)           \
+  do {                                      \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define DF_HIP(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(DFLASH_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+constexpr int kRowBlock = 4096;   // rows per fuse / inject GEMM pass
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(const dflash_dims* d) { return d->dtype == DFLASH_BF16 ? 2 : 4; }          // weight type
+size_t csize(const dflash_dims* d) { return d->cache_dtype == DFLASH_BF16 ? 2 : 4; }    // cache type
+
+dflash_status check_dims(const dflash_dims* d) {
+  DF_REQUIRE(d != nullptr, DFLASH_ERR_INVALID_ARG, "dims is NULL");
+  DF_REQUIRE(d->dtype == DFLASH_F32 || d->dtype == DFLASH_BF16, DFLASH_ERR_INVALID_ARG,
+             "dtype %d is neither DFLASH_F32 nor DFLASH_BF16", d->dtype);
+  DF_REQUIRE(d->cache_dtype == DFLASH_F32 || d->cache_dtype == DFLASH_BF16, DFLASH_ERR_INVALID_ARG,
+             "cache_dtype %d is neither DFLASH_F32 nor DFLASH_BF16", d->cache_dtype);
+  DF_REQUIRE(!(d->dtype == DFLASH_F32 && d->cache_dtype == DFLASH_BF16), DFLASH_ERR_INVALID_ARG,
+             "fp32 weights need an fp32 cache (cache_dtype DFLASH_F32)");
+  DF_REQUIRE(d->D >= 64 && d->D % 64 == 0 && d->D <= 16384, DFLASH_ERR_INVALID_ARG,
+             "D=%d must be a multiple of 64 in [64, 16384]", d->D);
+  DF_REQUIRE(d->F >= 64 && d->F % 64 == 0, DFLASH_ERR_INVALID_ARG, "F=%d must be a positive multiple of 64", d->F);
+  DF_REQUIRE(d->L >= 1, DFLASH_ERR_INVALID_ARG, "L=%d must be >= 1", d->L);
+  DF_REQUIRE(d->head_dim == 64 || d->head_dim == 128, DFLASH_ERR_INVALID_ARG, "head_dim=%d must be 64 or 128",
+             d->head_dim);
+  DF_REQUIRE(d->Hq >= 1 && d->Hkv >= 1 && d->Hq % d->Hkv == 0, DFLASH_ERR_INVALID_ARG,
+             "Hq=%d must be a positive multiple of Hkv=%d", d->Hq, d->Hkv);
+  DF_REQUIRE(d->n_tgt_layers >= 1 && d->n_tgt_layers <= DFLASH_MAX_TGT_LAYERS, DFLASH_ERR_INVALID_ARG,
+             "n_tgt_layers=%d must be in [1, %d]", d->n_tgt_layers, DFLASH_MAX_TGT_LAYERS);
+  DF_REQUIRE(d->V >= 2, DFLASH_ERR_INVALID_ARG, "V=%d must be >= 2", d->V);
+  DF_REQUIRE(d->mask_id >= 0 && d->mask_id < d->V, DFLASH_ERR_INVALID_ARG, "mask_id=%d outside [0, V)", d->mask_id);
+  DF_REQUIRE(std::isfinite(d->rms_eps) && d->rms_eps > 0.f, DFLASH_ERR_INVALID_ARG, "rms_eps must be > 0");
+  const int64_t kvcols = static_cast<int64_t>(2) * d->L * d->Hkv * d->head_dim;
+  DF_REQUIRE(kvcols < INT_MAX && static_cast<int64_t>(d->Hq + 2 * d->Hkv) * d->head_dim < INT_MAX,
+             DFLASH_ERR_INVALID_ARG, "head counts too large");
+  return DFLASH_OK;
+}
+
+dflash_status check_gamma(int gamma) {
+  DF_REQUIRE(gamma >= DFLASH_MIN_GAMMA && gamma <= DFLASH_MAX_GAMMA, DFLASH_ERR_INVALID_ARG,
+             "gamma=%d outside [%d, %d]", gamma, DFLASH_MIN_GAMMA, DFLASH_MAX_GAMMA);
+  return DFLASH_OK;
+}
+
+dflash_status check_cache(const dflash_kv_cache* c) {
+  DF_REQUIRE(c != nullptr, DFLASH_ERR_INVALID_ARG, "cache is NULL");
+  DF_REQUIRE(c->B >= 1 && c->B <= DFLASH_MAX_BATCH, DFLASH_ERR_INVALID_ARG, "cache->B=%d outside [1, %d]", c->B,
+             DFLASH_MAX_BATCH);
+  DF_REQUIRE(c->k != nullptr && c->v != nullptr && c->len != nullptr, DFLASH_ERR_INVALID_ARG,
+             "cache k, v and len must be non-NULL");
+  DF_REQUIRE(aligned16(c->k) && aligned16(c->v), DFLASH_ERR_INVALID_ARG, "cache k/v must be 16-byte aligned");
+  DF_REQUIRE(c->cap >= 8 && c->cap % 8 == 0, DFLASH_ERR_INVALID_ARG, "cache->cap=%d must be a positive multiple of 8",
+             c->cap);
+  for (int b = 0; b < c->B; ++b)
+    DF_REQUIRE(c->len[b] >= 0 && c->len[b] <= c->cap, DFLASH_ERR_INVALID_ARG, "cache->len[%d]=%d outside [0, cap]",
+               b, c->len[b]);
+  return DFLASH_OK;
+}
+
+dflash_status check_ptr(const void* p, const char* name) {
+  DF_REQUIRE(p != nullptr, DFLASH_ERR_INVALID_ARG, "%s is NULL", name);
+  DF_REQUIRE(aligned16(p), DFLASH_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  return DFLASH_OK;
+}
+
+dflash_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return DFLASH_OK;
+  DF_REQUIRE(ws != nullptr, DFLASH_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  DF_REQUIRE(ws_bytes >= need, DFLASH_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  DF_REQUIRE((reinterpret_cast<uintptr_t>(ws) % kAlign) == 0, DFLASH_ERR_WORKSPACE,
+             "workspace must be %zu-byte aligned", kAlign);
+  return DFLASH_OK;
+}
+
+// gfx950 check, once per device.
+dflash_status check_device() {
+  static std::mutex mu;
+  static int state[64] = {0};   // 0 unknown, 1 ok, -1 unsupported
+  int dev = 0;
+  DF_HIP(hipGetDevice(&dev));
+  DF_REQUIRE(dev >= 0 && dev < 64, DFLASH_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    DF_HIP(hipGetDeviceProperties(&prop, dev));
+    state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (state[dev] < 0) return fail(DFLASH_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  }
+  DF_REQUIRE(state[dev] == 1, DFLASH_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return DFLASH_OK;
+}
+
+// ----------------------------------------------------------- workspace plans
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+size_t gemm_part_floats(const dflash_dims* d, int M, int N, int K, bool single) {
+  if (M <= 0) return 0;
+  if (d->dtype == DFLASH_F32) return static_cast<size_t>(M) * N;
+  return plan_gemm_mfma(M, N, K, single).part_floats;
+}
+
+// fuse: partials of one row-block pass
+size_t fuse_ws(const dflash_dims* d, int max_rows) {
+  size_t best = 0;
+  const int hi = max_rows < kRowBlock ? max_rows : kRowBlock;
+  for (int M = 1; M <= hi; ++M) {
+    const size_t f = gemm_part_floats(d, M, d->D, d->n_tgt_layers * d->D, false);
+    if (f > best) best = f;
+  }
+  return best ? align_up(best * 4) : 0;
+}
+
+size_t inject_ws(const dflash_dims* d, int max_rows) {
+  size_t best = 0;
+  const int N = 2 * d->L * d->Hkv * d->head_dim;
+  const int hi = max_rows < kRowBlock ? max_rows : kRowBlock;
+  for (int M = 1; M <= hi; ++M) {
+    const size_t f = gemm_part_floats(d, M, N, d->D, false);
+    if (f > best) best = f;
+  }
+  return best ? align_up(best * 4) : 0;
+}
+
+struct DraftWs {
+  size_t h, a, q, o, s, part, att_o, att_ml, total;
+};
+
+DraftWs draft_ws(const dflash_dims* d, int B, int gamma) {
+  const int M = B * gamma;
+  const int hd = d->Hq * d->head_dim;
+  const int nqkv = (d->Hq + 2 * d->Hkv) * d->head_dim;
+  size_t part = 0;
+  auto upd = [&](int N, int K) {
+    const size_t f = gemm_part_floats(d, M, N, K, false);
+    if (f > part) part = f;
+  };
+  upd(nqkv, d->D);
+  upd(d->D, hd);
+  upd(2 * d->F, d->D);
+  upd(d->D, d->F);
+  const int R = (d->Hq / d->Hkv) * gamma;
+  const size_t att = d->dtype == DFLASH_BF16 ? attention_part_bound(B, d->Hkv, R, d->head_dim) : 0;
+  const size_t rpad_rows = att / (d->head_dim + 2);
+  DraftWs w{};
+  Carve c;
+  w.h = c.take(static_cast<size_t>(M) * d->D * 4);
+  w.a = c.take(static_cast<size_t>(M) * d->D * 4);
+  w.q = c.take(static_cast<size_t>(M) * hd * 4);
+  w.o = c.take(static_cast<size_t>(M) * hd * 4);
+  w.s = c.take(static_cast<size_t>(M) * d->F * 4);
+  w.part = c.take(part * 4);
+  w.att_o = c.take(rpad_rows * d->head_dim * 4);
+  w.att_ml = c.take(rpad_rows * 2 * 4);
+  w.total = c.off;
+  return w;
+}
+
+size_t argmax_ws(const dflash_dims* d, int B, int gamma) {
+  const int M = B * (gamma - 1);
+  if (d->dtype == DFLASH_F32) return align_up(static_cast<size_t>(M) * d->V * 4);
+  const GemmPlan p = plan_gemm_mfma(M, d->V, d->D, true);
+  return align_up(static_cast<size_t>(p.ntiles) * M * 3 * 4);
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_version(void) { return "dflash-mi355x 0.1.0 (gfx950)"; }
+
+const char* dflash_last_error(void) { return g_err.c_str(); }
+
+dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t gamma, int32_t max_rows,
+                                    size_t* bytes) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_gamma(gamma)) != DFLASH_OK) return st;
+  DF_REQUIRE(B >= 1 && B <= DFLASH_MAX_BATCH, DFLASH_ERR_INVALID_ARG, "B=%d outside [1, %d]", B, DFLASH_MAX_BATCH);
+  DF_REQUIRE(max_rows >= 0, DFLASH_ERR_INVALID_ARG, "max_rows=%d < 0", max_rows);
+  DF_REQUIRE(bytes != nullptr, DFLASH_ERR_INVALID_ARG, "bytes is NULL");
+  size_t need = draft_ws(dims, B, gamma).total;
+  const size_t f = fuse_ws(dims, max_rows), i = inject_ws(dims, max_rows), a = argmax_ws(dims, B, gamma);
+  if (f > need) need = f;
+  if (i > need) need = i;
+  if (a > need) need = a;
+  *bytes = need;
+  return ok();
+}
+
+dflash_status dflash_fuse_context(const dflash_dims* dims, const dflash_weights* w, const void* const* h_tgt,
+                                  int64_t ld, int32_t T, void* H_t, void* ws, size_t ws_bytes, void* stream) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
+  DF_REQUIRE(T >= 0, DFLASH_ERR_INVALID_ARG, "T=%d < 0", T);
+  if (T == 0) return ok();
+  if ((st = check_ptr(w->w_c, "w_c")) != DFLASH_OK) return st;
+  if ((st = check_ptr(w->g_c, "g_c")) != DFLASH_OK) return st;
+  if ((st = check_ptr(H_t, "H_t")) != DFLASH_OK) return st;
+  DF_REQUIRE(h_tgt != nullptr, DFLASH_ERR_INVALID_ARG, "h_tgt is NULL");
+  DF_REQUIRE(ld >= dims->D && (ld * static_cast<int64_t>(esize(dims))) % 16 == 0, DFLASH_ERR_INVALID_ARG,
+             "ld=%lld must be >= D and keep rows 16-byte aligned", static_cast<long long>(ld));
+  for (int k = 0; k < dims->n_tgt_layers; ++k)
+    if ((st = check_ptr(h_tgt[k], "h_tgt[k]")) != DFLASH_OK) return st;
+  const size_t need = fuse_ws(dims, T);
+  if ((st = check_ws(ws, ws_bytes, need)) != DFLASH_OK) return st;
+  if ((st = check_device()) != DFLASH_OK) return st;
+
+  const bool bf = dims->dtype == DFLASH_BF16, cbf = dims->cache_dtype == DFLASH_BF16;
+  const int D = dims->D, K = dims->n_tgt_layers * D;
+  const size_t es = esize(dims), cs = csize(dims);
+  float* part = static_cast<float*>(ws);
+  hipStream_t s = as_stream(stream);
+  for (int r0 = 0; r0 < T; r0 += kRowBlock) {
+    const int M = T - r0 < kRowBlock ? T - r0 : kRowBlock;
+    GemmArgs g{};
+    for (int k = 0; k < dims->n_tgt_layers; ++k)
+      g.a_src[k] = static_cast<const char*>(h_tgt[k]) + static_cast<int64_t>(r0) * ld * es;
+    for (int k = dims->n_tgt_layers; k < kMaxSrc; ++k) g.a_src[k] = g.a_src[0];
+    g.a_cols = D;
+    g.a_rg = INT_MAX;
+    g.a_ld = ld;
+    g.a_gs = 0;
+    g.w = w->w_c;
+    g.w_ld = K;
+    g.w_rg = INT_MAX;
+    g.w_gs = 0;
+    g.w_off = 0;
+    g.M = M;
+    g.N = D;
+    g.K = K;
+    g.part = part;
+    int S = 1;
+    if (bf) {
+      const GemmPlan p = plan_gemm_mfma(M, D, K, false);
+      S = p.S;
+      DF_HIP(launch_gemm_mfma(g, A_BF16, p, false, s));
+    } else {
+      DF_HIP(launch_gemm_f32(g, s));
+    }
+    DF_HIP(launch_ctx_norm(part, S, M, D, w->g_c, dims->rms_eps,
+                           static_cast<char*>(H_t) + static_cast<int64_t>(r0) * D * cs, bf, cbf, s));
+  }
+  return ok();
+}
+
+dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w, const void* H_t,
+                               const int32_t* rows_per_seq, dflash_kv_cache* cache, void* ws, size_t ws_bytes,
+                               void* stream) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
+  if ((st = check_cache(cache)) != DFLASH_OK) return st;
+  DF_REQUIRE(rows_per_seq != nullptr, DFLASH_ERR_INVALID_ARG, "rows_per_seq is NULL");
+  int64_t total = 0;
+  for (int b = 0; b < cache->B; ++b) {
+    DF_REQUIRE(rows_per_seq[b] >= 0, DFLASH_ERR_INVALID_ARG, "rows_per_seq[%d]=%d < 0", b, rows_per_seq[b]);
+    DF_REQUIRE(static_cast<int64_t>(cache->len[b]) + rows_per_seq[b] <= cache->cap, DFLASH_ERR_CAPACITY,
+               "sequence %d: len %d + %d rows exceeds cap %d", b, cache->len[b], rows_per_seq[b], cache->cap);
+    total += rows_per_seq[b];
+  }
+  DF_REQUIRE(total < INT_MAX, DFLASH_ERR_INVALID_ARG, "too many rows");
+  if (total == 0) return ok();
+  if ((st = check_ptr(w->w_qkv, "w_qkv")) != DFLASH_OK) return st;
+  if ((st = check_ptr(H_t, "H_t")) != DFLASH_OK) return st;
+  const size_t need = inject_ws(dims, static_cast<int>(total));
+  if ((st = check_ws(ws, ws_bytes, need)) != DFLASH_OK) return st;
+  if ((st = check_device()) != DFLASH_OK) return st;
+
+  const bool bf = dims->dtype == DFLASH_BF16, cbf = dims->cache_dtype == DFLASH_BF16;
+  const int D = dims->D, d = dims->head_dim, Hkv = dims->Hkv;
+  const int N = 2 * dims->L * Hkv * d;
+  const size_t cs = csize(dims);
+  float* part = static_cast<float*>(ws);
+  hipStream_t s = as_stream(stream);
+  int row_off[kMaxSeq + 1];
+  row_off[0] = 0;
+  for (int b = 0; b < cache->B; ++b) row_off[b + 1] = row_off[b] + rows_per_seq[b];
+  const int T = static_cast<int>(total);
+  for (int r0 = 0; r0 < T; r0 += kRowBlock) {
+    const int M = T - r0 < kRowBlock ? T - r0 : kRowBlock;
+    GemmArgs g{};
+    for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = static_cast<const char*>(H_t) + static_cast<int64_t>(r0) * D * cs;
+    g.a_cols = D;
+    g.a_rg = INT_MAX;
+    g.a_ld = D;
+    g.a_gs = 0;
+    g.w = w->w_qkv;
+    g.w_ld = D;
+    g.w_rg = 2 * Hkv * d;
+    g.w_gs = static_cast<int64_t>(dims->Hq + 2 * Hkv) * d;
+    g.w_off = static_cast<int64_t>(dims->Hq) * d;
+    g.M = M;
+    g.N = N;
+    g.K = D;
+    g.part = part;
+    int S = 1;
+    if (bf) {
+      const GemmPlan p = plan_gemm_mfma(M, N, D, false);
+      S = p.S;
+      // an fp32 H_t is split hi + lo against the bf16 weights like any fp32 activation
+      DF_HIP(launch_gemm_mfma(g, cbf ? A_BF16 : A_F32_SPLIT, p, false, s));
+    } else {
+      DF_HIP(launch_gemm_f32(g, s));
+    }
+    ScatterArgs sa{};
+    sa.part = part;
+    sa.S = S;
+    sa.M = M;
+    sa.N = N;
+    sa.nq = 0;
+    sa.q_out = nullptr;
+    sa.kc = cache->k;
+    sa.vc = cache->v;
+    sa.layer0 = 0;
+    sa.B = cache->B;
+    sa.Hkv = Hkv;
+    sa.d = d;
+    sa.cap = cache->cap;
+    sa.rows.B = cache->B;
+    for (int b = 0; b < cache->B; ++b) {
+      const int lo = row_off[b] - r0, hi = row_off[b + 1] - r0;
+      sa.rows.row_off[b] = lo < 0 ? 0 : (lo > M ? M : lo);
+      sa.rows.pos0[b] = cache->len[b] + (r0 > row_off[b] ? r0 - row_off[b] : 0);
+      (void)hi;
+    }
+    sa.rows.row_off[cache->B] = M;
+    DF_HIP(launch_scatter_kv(sa, cbf, s));
+  }
+  for (int b = 0; b < cache->B; ++b) cache->len[b] += rows_per_seq[b];
+  return ok();
+}
+
+dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights* w, const dflash_kv_cache* cache,
+                                   const int32_t* block_tokens, const float* embed_override, int32_t gamma,
+                                   float* h_final, void* ws, size_t ws_bytes, void* stream) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_gamma(gamma)) != DFLASH_OK) return st;
+  DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
+  if ((st = check_cache(cache)) != DFLASH_OK) return st;
+  for (int b = 0; b < cache->B; ++b)
+    DF_REQUIRE(static_cast<int64_t>(cache->len[b]) + gamma <= cache->cap, DFLASH_ERR_CAPACITY,
+               "sequence %d: len %d + gamma %d exceeds cap %d", b, cache->len[b], gamma, cache->cap);
+  const char* names[] = {"w_qkv", "w_o", "w_gateup", "w_down", "g_attn", "g_ffn", "g_final"};
+  const void* ptrs[] = {w->w_qkv, w->w_o, w->w_gateup, w->w_down, w->g_attn, w->g_ffn, w->g_final};
+  for (int i = 0; i < 7; ++i)
+    if ((st = check_ptr(ptrs[i], names[i])) != DFLASH_OK) return st;
+  if (embed_override != nullptr) {
+    if ((st = check_ptr(embed_override, "embed_override")) != DFLASH_OK) return st;
+  } else {
+    if ((st = check_ptr(w->embed, "embed")) != DFLASH_OK) return st;
+    DF_REQUIRE(block_tokens != nullptr, DFLASH_ERR_INVALID_ARG, "block_tokens is NULL (and no embed_override)");
+  }
+  if ((st = check_ptr(h_final, "h_final")) != DFLASH_OK) return st;
+  const int B = cache->B;
+  const DraftWs lay = draft_ws(dims, B, gamma);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != DFLASH_OK) return st;
+  if ((st = check_device()) != DFLASH_OK) return st;
+
+  const bool bf = dims->dtype == DFLASH_BF16, cbf = dims->cache_dtype == DFLASH_BF16;
+  const int D = dims->D, d = dims->head_dim, Hq = dims->Hq, Hkv = dims->Hkv, F = dims->F, L = dims->L;
+  const int M = B * gamma, hd = Hq * d, nqkv = (Hq + 2 * Hkv) * d;
+  const size_t es = esize(dims), cs = csize(dims);
+  char* base = static_cast<char*>(ws);
+  float* h = reinterpret_cast<float*>(base + lay.h);
+  float* a = reinterpret_cast<float*>(base + lay.a);
+  float* q = reinterpret_cast<float*>(base + lay.q);
+  float* o = reinterpret_cast<float*>(base + lay.o);
+  float* sw = reinterpret_cast<float*>(base + lay.s);
+  float* part = reinterpret_cast<float*>(base + lay.part);
+  hipStream_t s = as_stream(stream);
+  auto wp = [&](const void* p, int64_t elems) { return static_cast<const char*>(p) + elems * es; };
+
+  // GEMM on fp32 activations (rows = block rows), returns the split count.
+  auto gemm = [&](const float* A, int K, const void* W, int N, int* S) -> hipError_t {
+    GemmArgs g{};
+    for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = A;
+    g.a_cols = K;
+    g.a_rg = INT_MAX;
+    g.a_ld = K;
+    g.a_gs = 0;
+    g.w = W;
+    g.w_ld = K;
+    g.w_rg = INT_MAX;
+    g.w_gs = 0;
+    g.w_off = 0;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.part = part;
+    if (!bf) {
+      *S = 1;
+      return launch_gemm_f32(g, s);
+    }
+    const GemmPlan p = plan_gemm_mfma(M, N, K, false);
+    *S = p.S;
+    return launch_gemm_mfma(g, A_F32_SPLIT, p, false, s);
+  };
+
+  int32_t nkeys[kMaxSeq];
+  for (int b = 0; b < B; ++b) nkeys[b] = cache->len[b] + gamma;
+  const int R = (Hq / Hkv) * gamma;
+  const AttnPlan ap = bf ? plan_attention(B, nkeys, Hkv, R, d) : AttnPlan{};
+  const size_t layer_elems = static_cast<size_t>(B) * Hkv * cache->cap * d;
+
+  DF_HIP(launch_embed_norm(block_tokens, embed_override, w->embed, dims->V, M, D, w->g_attn, dims->rms_eps, h, a, bf, s));
+  for (int l = 0; l < L; ++l) {
+    int S = 1;
+    DF_HIP(gemm(a, D, wp(w->w_qkv, static_cast<int64_t>(l) * nqkv * D), nqkv, &S));
+    ScatterArgs sa{};
+    sa.part = part;
+    sa.S = S;
+    sa.M = M;
+    sa.N = nqkv;
+    sa.nq = hd;
+    sa.q_out = q;
+    sa.kc = cache->k;
+    sa.vc = cache->v;
+    sa.layer0 = l;
+    sa.B = B;
+    sa.Hkv = Hkv;
+    sa.d = d;
+    sa.cap = cache->cap;
+    sa.rows.B = B;
+    for (int b = 0; b < B; ++b) {
+      sa.rows.row_off[b] = b * gamma;
+      sa.rows.pos0[b] = cache->len[b];
+    }
+    sa.rows.row_off[B] = M;
+    DF_HIP(launch_scatter_kv(sa, cbf, s));
+
+    AttnArgs at{};
+    at.q = q;
+    at.kc = static_cast<const char*>(cache->k) + l * layer_elems * cs;
+    at.vc = static_cast<const char*>(cache->v) + l * layer_elems * cs;
+    at.part_o = reinterpret_cast<float*>(base + lay.att_o);
+    at.part_ml = reinterpret_cast<float*>(base + lay.att_ml);
+    at.o_out = o;
+    at.B = B;
+    at.gamma = gamma;
+    at.Hq = Hq;
+    at.Hkv = Hkv;
+    at.d = d;
+    at.cap = cache->cap;
+    at.R = R;
+    at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
+    for (int b = 0; b < B; ++b) at.nkeys[b] = nkeys[b];
+    DF_HIP(launch_attention(at, ap, bf, cbf, s));
+
+    DF_HIP(gemm(o, hd, wp(w->w_o, static_cast<int64_t>(l) * D * hd), D, &S));
+    DF_HIP(launch_residual_norm(part, S, M, D, h, wp(w->g_ffn, static_cast<int64_t>(l) * D), dims->rms_eps, a, bf, s));
+    DF_HIP(gemm(a, D, wp(w->w_gateup, static_cast<int64_t>(l) * 2 * F * D), 2 * F, &S));
+    DF_HIP(launch_swiglu(part, S, M, F, sw, s));
+    DF_HIP(gemm(sw, F, wp(w->w_down, static_cast<int64_t>(l) * D * F), D, &S));
+    const bool last = l + 1 == L;
+    DF_HIP(launch_residual_norm(part, S, M, D, h,
+                                last ? w->g_final : wp(w->g_attn, static_cast<int64_t>(l + 1) * D),
+                                dims->rms_eps, last ? h_final : a, bf, s));
+  }
+  return ok();
+}
+
+dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights* w, uint32_t flags,
+                                   const float* h_final, int32_t B, int32_t gamma, int32_t* draft,
+                                   const int32_t* target, int32_t* tau, int32_t* next_anchor, float* logits_dbg,
+                                   float* top2_gap, void* ws, size_t ws_bytes, void* stream) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_gamma(gamma)) != DFLASH_OK) return st;
+  DF_REQUIRE(flags != 0 && (flags & ~(DFLASH_ARGMAX | DFLASH_ACCEPT)) == 0, DFLASH_ERR_INVALID_ARG,
+             "flags=0x%x must be a non-empty subset of ARGMAX|ACCEPT", flags);
+  DF_REQUIRE(B >= 1 && B <= DFLASH_MAX_BATCH, DFLASH_ERR_INVALID_ARG, "B=%d outside [1, %d]", B, DFLASH_MAX_BATCH);
+  DF_REQUIRE(draft != nullptr, DFLASH_ERR_INVALID_ARG, "draft is NULL");
+  size_t need = 0;
+  if (flags & DFLASH_ARGMAX) {
+    DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
+    if ((st = check_ptr(w->lm_head, "lm_head")) != DFLASH_OK) return st;
+    if ((st = check_ptr(h_final, "h_final")) != DFLASH_OK) return st;
+    if (logits_dbg != nullptr && (st = check_ptr(logits_dbg, "logits_dbg")) != DFLASH_OK) return st;
+    need = argmax_ws(dims, B, gamma);
+  }
+  if (flags & DFLASH_ACCEPT) {
+    DF_REQUIRE(target != nullptr && tau != nullptr && next_anchor != nullptr, DFLASH_ERR_INVALID_ARG,
+               "target, tau and next_anchor must be non-NULL for ACCEPT");
+  }
+  if ((st = check_ws(ws, ws_bytes, need)) != DFLASH_OK) return st;
+  if ((st = check_device()) != DFLASH_OK) return st;
+
+  hipStream_t s = as_stream(stream);
+  const int n = gamma - 1, Mr = B * n, D = dims->D;
+  if (flags & DFLASH_ARGMAX) {
+    GemmArgs g{};
+    for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = h_final + D;   // block row 1 of sequence 0
+    g.a_cols = D;
+    g.a_rg = n;
+    g.a_gs = static_cast<int64_t>(gamma) * D;
+    g.a_ld = D;
+    g.w = w->lm_head;
+    g.w_ld = D;
+    g.w_rg = INT_MAX;
+    g.w_gs = 0;
+    g.w_off = 0;
+    g.M = Mr;
+    g.N = dims->V;
+    g.K = D;
+    if (dims->dtype == DFLASH_BF16) {
+      const GemmPlan p = plan_gemm_mfma(Mr, dims->V, D, true);
+      g.top2 = static_cast<float*>(ws);
+      g.logits = logits_dbg;
+      DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, true, s));
+      DF_HIP(launch_argmax_final(g.top2, p.ntiles, Mr, draft, top2_gap, s));
+    } else {
+      float* lg = logits_dbg != nullptr ? logits_dbg : static_cast<float*>(ws);
+      g.part = lg;
+      DF_HIP(launch_gemm_f32(g, s));
+      DF_HIP(launch_argmax_rows(lg, Mr, dims->V, draft, top2_gap, s));
+    }
+  }
+  if (flags & DFLASH_ACCEPT) DF_HIP(launch_accept(draft, target, B, n, tau, next_anchor, s));
+  return ok();
+}
+
+}  // extern "C"

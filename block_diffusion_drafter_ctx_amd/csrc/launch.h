@@ -1,0 +1,130 @@
+// Host-side launchers of the gfx950 kernels (internal to libdflash).  Each
+// launcher enqueues on `st` and returns hipGetLastError() of its launches; the
+// argument structs are passed to the kernels by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dflash {
+
+constexpr int kMaxSrc = 8;
+constexpr int kMaxSeq = 64;
+
+// ------------------------------------------------------------------- GEMMs
+// C[m][n] = sum_k A[m][k] * W[n][k] over a K range, written as split-K partials
+// part[s][m][n] (fp32), or reduced in-kernel to per-tile top-2 for the LM head.
+//   A row m, column k: src[k / a_cols] + (m / a_rg) * a_gs + (m % a_rg) * a_ld + k % a_cols
+//   W row n: w + ((n / w_rg) * w_gs + w_off + n % w_rg) * w_ld
+struct GemmArgs {
+  const void* a_src[kMaxSrc];
+  int32_t a_cols;
+  int32_t a_rg;
+  int64_t a_ld, a_gs;
+  const void* w;
+  int64_t w_ld, w_gs, w_off;
+  int32_t w_rg;
+  int32_t M, N, K;
+  int32_t chunks_per_split;   // in 128-element K chunks (MFMA path)
+  float* part;                // [S][M][N]
+  float* top2;                // [ntiles][M][3] (LM head)
+  float* logits;              // nullable [M][N] (LM head)
+};
+
+enum GemmAKind { A_BF16 = 0, A_F32_SPLIT = 1 };  // exact bf16 A, or fp32 A split hi/lo
+
+struct GemmPlan {
+  int MT = 16, mtiles = 1, ntiles = 1, nchunks = 1, cps = 1, S = 1;
+  size_t part_floats = 0;
+};
+
+constexpr int kGemmTileN = 128;   // weight rows per workgroup (MFMA path)
+constexpr int kGemmKC = 128;      // K elements per pipeline chunk
+
+GemmPlan plan_gemm_mfma(int M, int N, int K, bool force_single_split);
+hipError_t launch_gemm_mfma(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, bool top2_epilogue,
+                            hipStream_t st);
+
+// fp32 storage path: plain FMA GEMM, single split; writes part[0][m][n].
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
+
+// ------------------------------------------------------------ epilogues
+// Per-sequence row table: rows [row_off[b], row_off[b+1]) of a GEMM output belong
+// to sequence b and land at cache rows pos0[b] + (row - row_off[b]).
+struct SeqRows {
+  int32_t B;
+  int32_t row_off[kMaxSeq + 1];
+  int32_t pos0[kMaxSeq];
+};
+
+struct ScatterArgs {
+  const float* part;   // [S][M][N]
+  int32_t S, M, N;
+  int32_t nq;          // columns [0, nq) are query columns -> q_out[m][n]
+  float* q_out;
+  void* kc;            // cache K base of layer `layer0`: [L][B][Hkv][cap][d]
+  void* vc;            // cache V base: [L][B][Hkv][d][cap]
+  int32_t layer0, B, Hkv, d, cap;
+  SeqRows rows;
+};
+
+hipError_t launch_scatter_kv(const ScatterArgs& a, bool bf16_cache, hipStream_t st);
+
+// H_t[t] = store(g * u / sqrt(mean(u^2)+eps)), u = sum_s part[s][t]; g in the weight type,
+// H_t in the cache type
+hipError_t launch_ctx_norm(const float* part, int S, int T, int D, const void* g, float eps,
+                           void* out, bool bf16_weights, bool bf16_cache, hipStream_t st);
+
+// h[m] += sum_s part[s][m]; a[m] = g * h / sqrt(mean(h^2)+eps)   (part may be null)
+hipError_t launch_residual_norm(const float* part, int S, int M, int D, float* h, const void* g,
+                                float eps, float* a_out, bool bf16, hipStream_t st);
+
+// s[m][f] = silu(sum_s part[s][m][f]) * sum_s part[s][m][F+f]
+hipError_t launch_swiglu(const float* part, int S, int M, int F, float* s_out, hipStream_t st);
+
+// h[m] = embed[tok[m]] or override[m]; a[m] = RMSNorm(h[m]; g)   (ids clamped to [0, V))
+hipError_t launch_embed_norm(const int32_t* tok, const float* ov, const void* embed, int V, int M, int D,
+                             const void* g, float eps, float* h, float* a, bool bf16, hipStream_t st);
+
+// top-2 partials [ntiles][M] -> draft[m], gap[m]
+hipError_t launch_argmax_final(const float* top2, int ntiles, int M, int32_t* draft, float* gap,
+                               hipStream_t st);
+// rows of logits [M][V] -> draft[m], gap[m]
+hipError_t launch_argmax_rows(const float* logits, int M, int V, int32_t* draft, float* gap,
+                              hipStream_t st);
+
+hipError_t launch_accept(const int32_t* draft, const int32_t* target, int B, int n, int32_t* tau,
+                         int32_t* next_anchor, hipStream_t st);
+
+// ------------------------------------------------------------ attention
+struct AttnArgs {
+  const float* q;        // [B*gamma][Hq*d]
+  const void* kc;        // layer base [B][Hkv][cap][d]
+  const void* vc;        // layer base [B][Hkv][d][cap]
+  float* part_o;         // [items][Rpad][d]
+  float* part_ml;        // [items][Rpad][2]
+  float* o_out;          // [B*gamma][Hq*d]
+  int32_t B, gamma, Hq, Hkv, d, cap;
+  int32_t R, Rpad;       // query rows per (b, kv head) = G*gamma, padded to 16
+  int32_t split_keys;    // keys per work item (multiple of 32)
+  int32_t items;
+  float scale_log2;      // log2(e) / sqrt(d)
+  int32_t nkeys[kMaxSeq];     // len_b + gamma
+  int32_t nsplit[kMaxSeq];
+  int32_t item_off[kMaxSeq + 1];
+};
+
+struct AttnPlan {
+  int split_keys = 32, items = 0, Rpad = 16, row_groups = 1;
+  int nsplit[kMaxSeq] = {0};
+  int item_off[kMaxSeq + 1] = {0};
+  size_t part_floats = 0;
+};
+
+AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d);
+size_t attention_part_bound(int B, int Hkv, int R, int d);
+hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, bool bf16_weights, bool bf16_cache,
+                            hipStream_t st);
+
+}  // namespace dflash

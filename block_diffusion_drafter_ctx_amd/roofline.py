@@ -26,9 +26,11 @@ def elem_bytes(dtype: str) -> int:
 
 
 # ---------------------------------------------------------------- (a) fusion
-def fuse_bytes(T: int, D: int, n_tgt: int = 5, es: int = 2) -> int:
-    """n_tgt source states [T, D] + W_c [D, n_tgt*D] + H_t [T, D], storage type."""
-    return (n_tgt * T * D + n_tgt * D * D + T * D) * es
+def fuse_bytes(T: int, D: int, n_tgt: int = 5, es: int = 2, cs: int = None) -> int:
+    """n_tgt source states [T, D] + W_c [D, n_tgt*D] (weight type, es bytes) +
+    H_t [T, D] (cache type, cs bytes)."""
+    cs = es if cs is None else cs
+    return (n_tgt * T * D + n_tgt * D * D) * es + T * D * cs
 
 
 def fuse_flops(T: int, D: int, n_tgt: int = 5) -> int:
@@ -48,10 +50,12 @@ def fusion_output_bytes(T: int, D: int, es: int = 2) -> int:
 
 
 # ------------------------------------------------------------- (b) injection
-def inject_bytes(T: int, D: int, L: int, Hkv: int, d: int, es: int = 2) -> int:
-    """H_t [T, D] + every layer's W_K, W_V + the K/V rows written to the cache."""
+def inject_bytes(T: int, D: int, L: int, Hkv: int, d: int, es: int = 2, cs: int = None) -> int:
+    """H_t [T, D] and the K/V rows written to the cache (cache type, cs bytes) +
+    every layer's W_K, W_V (weight type, es bytes)."""
+    cs = es if cs is None else cs
     kv = 2 * L * Hkv * d
-    return (T * D + kv * D + T * kv) * es
+    return kv * D * es + (T * D + T * kv) * cs
 
 
 def inject_flops(T: int, D: int, L: int, Hkv: int, d: int) -> int:
@@ -63,14 +67,16 @@ def layer_weight_elems(D: int, Hq: int, Hkv: int, d: int, F: int) -> int:
     return (Hq + 2 * Hkv) * d * D + D * Hq * d + 2 * F * D + D * F + 2 * D
 
 
-def draft_forward_bytes(D, L, Hq, Hkv, d, F, V, B, gamma, ctx_lens, es=2) -> int:
-    """All drafter weights once, the LM head once, each layer's context + block K/V
-    once, and the fp32 activations in/out (block embedding rows and h_final)."""
+def draft_forward_bytes(D, L, Hq, Hkv, d, F, V, B, gamma, ctx_lens, es=2, cs=None) -> int:
+    """All drafter weights once and the LM head once (weight type), each layer's
+    context + block K/V once (cache type), and the fp32 activations in/out (block
+    embedding rows and h_final)."""
+    cs = es if cs is None else cs
     w = L * layer_weight_elems(D, Hq, Hkv, d, F) + D
     kv = L * sum(n + gamma for n in ctx_lens) * 2 * Hkv * d
     lm = V * D
     act = B * gamma * D * 4 * 2
-    return (w + kv + lm) * es + act
+    return (w + lm) * es + kv * cs + act
 
 
 def draft_forward_flops(D, L, Hq, Hkv, d, F, V, B, gamma, ctx_lens) -> int:

@@ -1,0 +1,131 @@
+"""PyTorch plumbing around the C ABI: device weights, KV cache and workspace.
+
+PyTorch only allocates device memory and provides the stream; every step of the
+hot path runs in libdflash's HIP kernels through ``binding``.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dims_of(cfg) -> B.Dims:
+    return B.Dims(D=cfg.D, L=cfg.L, Hq=cfg.Hq, Hkv=cfg.Hkv, head_dim=cfg.d, F=cfg.F, V=cfg.V,
+                  n_tgt_layers=cfg.n_tgt, mask_id=cfg.V - 1, rms_eps=cfg.eps,
+                  dtype=B.BF16 if cfg.dtype == "bf16" else B.F32,
+                  cache_dtype=B.BF16 if cfg.cache_dtype == "bf16" else B.F32)
+
+
+def torch_dtype(cfg):
+    """Weight / target-state type."""
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def cache_torch_dtype(cfg):
+    """Type of H_t and the KV cache."""
+    return torch.bfloat16 if cfg.cache_dtype == "bf16" else torch.float32
+
+
+def upload(arr: np.ndarray, cfg, device="cuda") -> torch.Tensor:
+    """fp32 numpy (values exact in the storage type) -> device tensor of the storage type."""
+    t = torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    return t.to(torch_dtype(cfg)) if cfg.dtype == "bf16" else t
+
+
+class DeviceCache:
+    """KV cache [L][B][Hkv][cap][d] (keys) and [L][B][Hkv][d][cap] (values) plus host lens."""
+
+    def __init__(self, cfg, B_: int, cap: int, device="cuda"):
+        dt = cache_torch_dtype(cfg)
+        self.k = torch.zeros(cfg.L, B_, cfg.Hkv, cap, cfg.d, dtype=dt, device=device)
+        self.v = torch.zeros(cfg.L, B_, cfg.Hkv, cfg.d, cap, dtype=dt, device=device)
+        self.lens = (ctypes.c_int32 * B_)()
+        self.B, self.cap = B_, cap
+        self.struct = B.KVCache(k=self.k.data_ptr(), v=self.v.data_ptr(), B=B_, cap=cap,
+                                len=ctypes.cast(self.lens, ctypes.POINTER(ctypes.c_int32)))
+
+    def len_list(self):
+        return [int(self.lens[b]) for b in range(self.B)]
+
+    def set_lens(self, lens):
+        for b, n in enumerate(lens):
+            self.lens[b] = int(n)
+
+
+class DeviceDrafter:
+    """Weights of one drafter on the device, and thin wrappers over the four calls."""
+
+    def __init__(self, cfg, inputs, device="cuda", with_fusion=True):
+        self.cfg, self.device = cfg, device
+        self.dims = dims_of(cfg)
+        L = cfg.L
+        up = lambda a: upload(a, cfg, device)  # noqa: E731
+        self.w_c = up(inputs.w_c()) if with_fusion else None
+        self.g_c = up(inputs.g_c())
+        dt = torch_dtype(cfg)
+        self.w_qkv = torch.empty(L, (cfg.Hq + 2 * cfg.Hkv) * cfg.d, cfg.D, dtype=dt, device=device)
+        self.w_o = torch.empty(L, cfg.D, cfg.Hq * cfg.d, dtype=dt, device=device)
+        self.w_gateup = torch.empty(L, 2 * cfg.F, cfg.D, dtype=dt, device=device)
+        self.w_down = torch.empty(L, cfg.D, cfg.F, dtype=dt, device=device)
+        self.g_attn = torch.empty(L, cfg.D, dtype=dt, device=device)
+        self.g_ffn = torch.empty(L, cfg.D, dtype=dt, device=device)
+        for l in range(L):
+            self.w_qkv[l].copy_(up(inputs.w_qkv(l)))
+            self.w_o[l].copy_(up(inputs.w_o(l)))
+            self.w_gateup[l].copy_(up(inputs.w_gateup(l)))
+            self.w_down[l].copy_(up(inputs.w_down(l)))
+            self.g_attn[l].copy_(up(inputs.g_attn(l)))
+            self.g_ffn[l].copy_(up(inputs.g_ffn(l)))
+        self.g_final = up(inputs.g_final())
+        self.embed = up(inputs.embed())
+        ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+        self.weights = B.Weights(w_c=ptr(self.w_c), g_c=ptr(self.g_c), w_qkv=ptr(self.w_qkv), w_o=ptr(self.w_o),
+                                 w_gateup=ptr(self.w_gateup), w_down=ptr(self.w_down), g_attn=ptr(self.g_attn),
+                                 g_ffn=ptr(self.g_ffn), g_final=ptr(self.g_final), embed=ptr(self.embed),
+                                 lm_head=ptr(self.embed))
+        self.ws = None
+        self.ws_bytes = 0
+
+    # ---- memory
+    def cache(self, B_: int, cap: int) -> DeviceCache:
+        return DeviceCache(self.cfg, B_, cap, self.device)
+
+    def ensure_workspace(self, B_: int, gamma: int, max_rows: int):
+        need = B.workspace_size(self.dims, B_, gamma, max_rows)
+        if need > self.ws_bytes:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self.ws_bytes = need
+        return self.ws
+
+    def context_buffer(self, T: int) -> torch.Tensor:
+        """An H_t buffer [T, D] of the cache type."""
+        return torch.empty(max(T, 1), self.cfg.D, dtype=cache_torch_dtype(self.cfg), device=self.device)
+
+    # ---- the four calls
+    def fuse(self, h_tgt, T: int, H_t: torch.Tensor):
+        ld = h_tgt[0].stride(0)
+        B.fuse_context(self.dims, self.weights, [h.data_ptr() for h in h_tgt], ld, T, H_t.data_ptr(),
+                       self.ws.data_ptr() if self.ws is not None else 0, self.ws_bytes, _stream())
+
+    def inject(self, H_t: torch.Tensor, rows_per_seq, cache: DeviceCache):
+        B.inject_kv(self.dims, self.weights, H_t.data_ptr(), list(rows_per_seq), cache.struct,
+                    self.ws.data_ptr() if self.ws is not None else 0, self.ws_bytes, _stream())
+
+    def draft(self, cache: DeviceCache, tokens, override, gamma: int, h_final: torch.Tensor):
+        B.draft_forward(self.dims, self.weights, cache.struct, 0 if tokens is None else tokens.data_ptr(),
+                        0 if override is None else override.data_ptr(), gamma, h_final.data_ptr(),
+                        self.ws.data_ptr(), self.ws_bytes, _stream())
+
+    def argmax_accept(self, flags, h_final, B_, gamma, draft, target=None, tau=None, nxt=None, logits=None,
+                      gap=None):
+        p = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+        B.argmax_accept(self.dims, self.weights, flags, p(h_final), B_, gamma, p(draft), p(target), p(tau),
+                        p(nxt), p(logits), p(gap), p(self.ws), self.ws_bytes, _stream())

@@ -22,7 +22,7 @@ BASE_SEED = 20261202
 class Config:
     name: str
     cid: int                 # seed namespace for this workload
-    dtype: str               # "f32" or "bf16": storage type of weights, inputs, H_t, KV
+    dtype: str               # "f32" or "bf16": weights and target states
     D: int
     L: int
     Hq: int
@@ -40,6 +40,7 @@ class Config:
     match: str = "const"     # "const": p=0.8 per position; "linear": 0.9 -> 0.5
     w_std: float = 0.02
     gain_std: float = 0.0    # 0: unit gains (benchmark); >0: 1 + N(0, gain_std)
+    cache_dtype: str = "f32"  # H_t and the KV cache: "f32" (default) or "bf16"
 
     @property
     def G(self) -> int:

@@ -1,0 +1,204 @@
+/*
+ * dflash.h - C ABI of the MI355X (gfx950) DFlash drafter hot path.
+ *
+ * Four calls cover the data-parallel path of a block-diffusion drafter with
+ * target-context KV injection:
+ *   dflash_fuse_context   (a) H_t = RMSNorm(W_c [H(l1); ...; H(l5)])
+ *   dflash_inject_kv      (b) K/V = W_K H_t, W_V H_t for every drafter layer,
+ *                             appended to that layer's KV cache
+ *   dflash_draft_forward  (c) one forward over a gamma-row block (anchor + mask
+ *                             rows), bidirectional over [context ; block]
+ *   dflash_argmax_accept  (d) LM-head argmax of the mask rows and greedy
+ *                             acceptance length against the target's tokens
+ *
+ * Sources (page titles as published):
+ *   [JP] "DFlash: Block Diffusion for Flash Speculative Decoding 논문 정리"
+ *   [GL] "DFlash 블록 확산 디코딩: 투기적 디코딩의 드래프트 비용을 상수로 만드는 법"
+ *   [MG] "ICML'26 | DFlash：用 Diffusion 模型干掉 AR Drafter，投机解码提速 6×"
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers unless marked "host".  The caller
+ *     allocates and owns every buffer (weights, cache, workspace, outputs); the
+ *     library never allocates device memory and keeps no state between calls
+ *     except a per-thread error string and a per-device architecture check.
+ *   - Matrices are row-major and laid out [out, in] (a linear map y = W x stores
+ *     W as [rows = outputs][cols = inputs]).
+ *   - "weight type" is dims->dtype (DFLASH_BF16 or DFLASH_F32): weights and the
+ *     tapped target states use it.  "cache type" is dims->cache_dtype: the fused
+ *     context feature H_t and the KV cache use it (with bf16 weights it may be
+ *     bf16, halving cache traffic, or f32, which keeps the drafter's output within
+ *     ~1e-5 of an exact evaluation; with f32 weights it must be f32).  The
+ *     residual stream, h_final and logits are always float32.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and the
+ *     call returns without synchronising the host.
+ *   - Errors: arguments, shapes, capacities and workspace size are checked on the
+ *     host before anything is enqueued; on any error the call returns a negative
+ *     status, enqueues nothing and leaves every output untouched (a HIP launch
+ *     failure, DFLASH_ERR_HIP, is the only error raised after enqueueing began).
+ *     dflash_last_error() returns the message.  No C++ exception crosses the ABI.
+ *   - Calls on one stream are ordered; calls that write the same cache or
+ *     workspace from different streams race.
+ */
+#ifndef DFLASH_H_
+#define DFLASH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_MAX_BATCH 64      /* sequences per call */
+#define DFLASH_MAX_TGT_LAYERS 8  /* tapped target layers fused by W_c */
+#define DFLASH_MIN_GAMMA 2
+#define DFLASH_MAX_GAMMA 33      /* 1 anchor + 32 mask rows */
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_ERR_INVALID_ARG = -1,  /* null pointer, bad shape or flag */
+  DFLASH_ERR_UNSUPPORTED = -2,  /* device is not gfx950, or a shape outside the kernels' range */
+  DFLASH_ERR_CAPACITY = -3,     /* KV cache rows would exceed cap */
+  DFLASH_ERR_WORKSPACE = -4,    /* workspace missing or smaller than required */
+  DFLASH_ERR_HIP = -5           /* a HIP runtime call or kernel launch failed */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Drafter shape.  Hq query heads share Hkv KV heads in contiguous groups of
+ * G = Hq / Hkv (query head h reads KV head h / G).  Constraints checked by every
+ * call: D % 64 == 0, F % 64 == 0, head_dim in {64, 128}, Hq % Hkv == 0,
+ * 1 <= n_tgt_layers <= 8, 0 <= mask_id < V, V >= 2, rms_eps > 0, L >= 1,
+ * dtype and cache_dtype in {DFLASH_F32, DFLASH_BF16}, and cache_dtype ==
+ * DFLASH_F32 when dtype == DFLASH_F32. */
+typedef struct {
+  int32_t D;            /* hidden size of target and drafter */
+  int32_t L;            /* drafter layers */
+  int32_t Hq, Hkv;      /* query / key-value heads */
+  int32_t head_dim;     /* d */
+  int32_t F;            /* SwiGLU hidden size */
+  int32_t V;            /* vocabulary of the shared embedding / LM head */
+  int32_t n_tgt_layers; /* tapped target layers (5 in the pages) */
+  int32_t mask_id;      /* token id of the mask rows */
+  float rms_eps;        /* RMSNorm epsilon */
+  int32_t dtype;        /* dflash_dtype: weights and target states */
+  int32_t cache_dtype;  /* dflash_dtype: H_t and the KV cache */
+} dflash_dims;
+
+/* Non-owning device pointers to the drafter's weights, all in the weight type.
+ * Only the fields a call uses must be set (see each call). */
+typedef struct {
+  const void* w_c;      /* [D][n_tgt_layers*D]  fusion projection W_c ([JP] "KV Injection 메커니즘") */
+  const void* g_c;      /* [D]  gain of the fusion RMSNorm */
+  const void* w_qkv;    /* [L][(Hq+2*Hkv)*d][D]  per layer: W_Q rows, then W_K, then W_V */
+  const void* w_o;      /* [L][D][Hq*d] */
+  const void* w_gateup; /* [L][2*F][D]  per layer: F gate rows, then F up rows */
+  const void* w_down;   /* [L][D][F] */
+  const void* g_attn;   /* [L][D]  pre-attention RMSNorm gains */
+  const void* g_ffn;    /* [L][D]  pre-FFN RMSNorm gains */
+  const void* g_final;  /* [D]     final RMSNorm gain before the LM head */
+  const void* embed;    /* [V][D]  shared token embedding ([JP] "학습 방법": shared with the target) */
+  const void* lm_head;  /* [V][D]  shared LM head; may alias embed (tied) */
+} dflash_weights;
+
+/* The drafter's KV cache: injected context rows plus gamma scratch rows per
+ * sequence ([JP] "추론 구조", [GL] "KV 주입": injected K/V are cached and reused
+ * across drafting iterations).  Layouts, in the cache type:
+ *   k: [L][B][Hkv][cap][d]   row-major keys
+ *   v: [L][B][Hkv][d][cap]   values stored transposed (key index fastest)
+ * len[b] (HOST array, caller-owned) is the number of valid context rows of
+ * sequence b.  Rows [0, len[b]) are never written by draft_forward; inject_kv
+ * writes rows [len[b], len[b]+T_b) and then adds T_b to len[b]. */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t B;     /* sequences, 1..DFLASH_MAX_BATCH */
+  int32_t cap;   /* rows per (layer, sequence, head) */
+  int32_t* len;  /* host [B] */
+} dflash_kv_cache;
+
+/* Version string of the library. */
+const char* dflash_version(void);
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char* dflash_last_error(void);
+
+/* Bytes of workspace every call needs for up to B sequences, blocks of up to
+ * `gamma` rows and fuse/inject calls of up to `max_rows` rows in total.
+ * Pure host computation; enqueues nothing. */
+dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t gamma,
+                                    int32_t max_rows, size_t* bytes);
+
+/* (a) Context fusion, [JP] "KV Injection 메커니즘" (fusion equation) and [MG]
+ * section 3.1: H_t[t] = g_c * u / sqrt(mean(u^2) + eps) with
+ * u = W_c [h_tgt[0][t]; ...; h_tgt[n-1][t]] (sources in order, shallowest first;
+ * the concatenation is never materialised).
+ *   h_tgt  HOST array of n_tgt_layers device pointers, each [T][ld] weight type
+ *          (row t of source k starts at h_tgt[k] + t*ld, ld >= D)
+ *   T      rows (0 is allowed and does nothing)
+ *   H_t    out [T][D] cache type
+ * Uses weights->w_c, weights->g_c. */
+dflash_status dflash_fuse_context(const dflash_dims* dims, const dflash_weights* w,
+                                  const void* const* h_tgt, int64_t ld, int32_t T,
+                                  void* H_t, void* ws, size_t ws_bytes, void* stream);
+
+/* (b) KV injection, [JP] "KV Injection 메커니즘" and [MG] section 3.2: for every
+ * layer l, K = W_K^l H_t and V = W_V^l H_t (no norm, no bias, no position
+ * encoding), appended to sequence b's cache at rows [len[b], len[b]+T_b).
+ *   H_t           [sum_b T_b][D] cache type: the rows of sequence 0, then 1, ...
+ *   rows_per_seq  HOST [cache->B] row counts T_b >= 0
+ * Errors: DFLASH_ERR_CAPACITY if len[b] + T_b > cap for some b (checked before
+ * any work).  On success cache->len[b] += T_b (host), the rows land when the
+ * stream reaches the kernels.  Uses weights->w_qkv. */
+dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w, const void* H_t,
+                               const int32_t* rows_per_seq, dflash_kv_cache* cache, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* (c) One drafting forward pass over a block of `gamma` rows per sequence,
+ * [JP] "추론 구조" / "KV Injection 메커니즘" and [MG] section 3.3:
+ *   h = embed[block_tokens] (or embed_override); per layer:
+ *   a = RMSNorm(h; g_attn); Q = a W_Q^T; the block's K/V rows (a W_K^T, a W_V^T,
+ *   stored in the cache type) go to cache scratch rows [len[b], len[b]+gamma);
+ *   every query row attends, unmasked, to all len[b] context rows and all gamma
+ *   block rows (softmax scale 1/sqrt(d), query head h -> KV head h/G);
+ *   h += O W_O^T; f = RMSNorm(h; g_ffn); h += (SiLU(f W_gate^T) * f W_up^T) W_down^T.
+ *   h_final = RMSNorm(h; g_final).
+ *   block_tokens    [B][gamma] int32 (anchor at row 0, mask_id after it)
+ *   embed_override  nullable [B][gamma][D] float32 rows used instead of the
+ *                   embedding lookup (block_tokens may then be NULL)
+ *   h_final         out [B][gamma][D] float32
+ * B = cache->B.  Errors: DFLASH_ERR_CAPACITY if len[b] + gamma > cap.
+ * Cache rows below len[b] are read only; len is unchanged. */
+dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights* w,
+                                   const dflash_kv_cache* cache, const int32_t* block_tokens,
+                                   const float* embed_override, int32_t gamma, float* h_final,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+#define DFLASH_ARGMAX 1u
+#define DFLASH_ACCEPT 2u
+
+/* (d) LM head + argmax and greedy acceptance.
+ * DFLASH_ARGMAX ([MG] section 3.3; [JP] "학습 방법": shared LM head): for block
+ *   rows i = 1..gamma-1 of each sequence, logits = lm_head . h_final[b][i] and
+ *   draft[b][i-1] = argmax (lowest token id on ties).
+ * DFLASH_ACCEPT ([JP] "Preliminaries": 1 <= tau <= drafts + 1): m = length of the
+ *   longest prefix with draft[b][j] == target[b][j]; tau[b] = m + 1;
+ *   next_anchor[b] = target[b][m].
+ *   h_final      [B][gamma][D] float32 (ARGMAX)
+ *   draft        [B][gamma-1] int32: written by ARGMAX, read by ACCEPT
+ *   target       [B][gamma] int32: the target's token at each draft position,
+ *                then its bonus token (ACCEPT)
+ *   tau, next_anchor  out [B] int32 (ACCEPT)
+ *   logits_dbg   nullable out [B][gamma-1][V] float32 (ARGMAX)
+ *   top2_gap     nullable out [B][gamma-1] float32: best minus second-best logit
+ * flags: a non-empty subset of DFLASH_ARGMAX | DFLASH_ACCEPT.  Uses weights->lm_head. */
+dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights* w, uint32_t flags,
+                                   const float* h_final, int32_t B, int32_t gamma, int32_t* draft,
+                                   const int32_t* target, int32_t* tau, int32_t* next_anchor,
+                                   float* logits_dbg, float* top2_gap, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H_ */

@@ -1,0 +1,143 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments on the host with the documented status before any
+HIP call (no compute call is made here)."""
+import ctypes
+import re
+import os
+
+import pytest
+
+from block_diffusion_drafter_ctx_amd import binding as B
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dflash.h")
+
+
+def _dims(**kw):
+    d = dict(D=256, L=2, Hq=4, Hkv=2, head_dim=64, F=512, V=1000, n_tgt_layers=5, mask_id=999,
+             rms_eps=1e-6, dtype=B.BF16, cache_dtype=B.F32)
+    d.update(kw)
+    return B.Dims(**d)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libdflash.so is not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", open(HDR).read()))
+    assert declared == set(B.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert "gfx950" in B.version()
+
+
+def test_workspace_size_pure_host(lib):
+    n = B.workspace_size(_dims(), 1, 16, 128)
+    assert n > 0
+    big = B.workspace_size(_dims(D=4096, F=12288, Hq=32, Hkv=8, head_dim=128, V=151936, L=5), 16, 16, 65536)
+    assert big > n
+
+
+@pytest.mark.parametrize("bad", [
+    dict(D=100), dict(D=0), dict(F=100), dict(head_dim=96), dict(Hq=6, Hkv=4), dict(L=0),
+    dict(n_tgt_layers=0), dict(n_tgt_layers=9), dict(V=1), dict(mask_id=1000), dict(mask_id=-1),
+    dict(rms_eps=0.0), dict(rms_eps=float("nan")), dict(dtype=7), dict(cache_dtype=3),
+    dict(dtype=B.F32, cache_dtype=B.BF16),
+])
+def test_bad_dims_rejected(lib, bad):
+    with pytest.raises(B.DFlashError) as e:
+        B.workspace_size(_dims(**bad), 1, 16, 16)
+    assert e.value.status == B.ERR_INVALID_ARG
+    assert B.last_error()
+
+
+@pytest.mark.parametrize("gamma", [0, 1, 34, 100])
+def test_bad_gamma(lib, gamma):
+    with pytest.raises(B.DFlashError) as e:
+        B.workspace_size(_dims(), 1, gamma, 16)
+    assert e.value.status == B.ERR_INVALID_ARG
+
+
+def _cache(Bn=2, cap=64, lens=(0, 0), k=0x10000, v=0x20000):
+    arr = (ctypes.c_int32 * Bn)(*lens)
+    c = B.KVCache(k=k, v=v, B=Bn, cap=cap, len=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+    c._keep = arr
+    return c
+
+
+def test_inject_capacity_checked_before_any_work(lib):
+    c = _cache(lens=(60, 0))
+    w = B.Weights(w_qkv=0x1000)
+    with pytest.raises(B.DFlashError) as e:
+        B.inject_kv(_dims(), w, 0x3000, [5, 1], c, 0, 0)
+    assert e.value.status == B.ERR_CAPACITY
+    assert list(c._keep) == [60, 0]          # len untouched
+
+
+def test_draft_capacity_and_nulls(lib):
+    w = B.Weights(w_qkv=0x1000, w_o=0x1000, w_gateup=0x1000, w_down=0x1000, g_attn=0x1000, g_ffn=0x1000,
+                  g_final=0x1000, embed=0x1000, lm_head=0x1000)
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward(_dims(), w, _cache(lens=(50, 0)), 0x4000, None, 16, 0x5000, 0x100000, 1 << 30)
+    assert e.value.status == B.ERR_CAPACITY
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward(_dims(), w, _cache(), None, None, 16, 0x5000, 0x100000, 1 << 30)
+    assert e.value.status == B.ERR_INVALID_ARG
+    w2 = B.Weights(w_qkv=0x1000)
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward(_dims(), w2, _cache(), 0x4000, None, 16, 0x5000, 0x100000, 1 << 30)
+    assert e.value.status == B.ERR_INVALID_ARG
+
+
+def test_workspace_too_small(lib):
+    w = B.Weights(w_qkv=0x1000, w_o=0x1000, w_gateup=0x1000, w_down=0x1000, g_attn=0x1000, g_ffn=0x1000,
+                  g_final=0x1000, embed=0x1000, lm_head=0x1000)
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward(_dims(), w, _cache(), 0x4000, None, 16, 0x5000, 0x100000, 16)
+    assert e.value.status == B.ERR_WORKSPACE
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward(_dims(), w, _cache(), 0x4000, None, 16, 0x5000, 0, 0)
+    assert e.value.status == B.ERR_WORKSPACE
+
+
+def test_misaligned_and_bad_cache(lib):
+    w = B.Weights(w_c=0x1001, g_c=0x1000)
+    with pytest.raises(B.DFlashError) as e:
+        B.fuse_context(_dims(), w, [0x2000] * 5, 256, 4, 0x3000, 0x100000, 1 << 30)
+    assert e.value.status == B.ERR_INVALID_ARG
+    w = B.Weights(w_c=0x1000, g_c=0x1000)
+    with pytest.raises(B.DFlashError) as e:     # ld < D
+        B.fuse_context(_dims(), w, [0x2000] * 5, 128, 4, 0x3000, 0x100000, 1 << 30)
+    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.DFlashError) as e:     # cap not a multiple of 8
+        B.inject_kv(_dims(), B.Weights(w_qkv=0x1000), 0x3000, [1, 1], _cache(cap=60), 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.DFlashError) as e:     # B too large
+        B.inject_kv(_dims(), B.Weights(w_qkv=0x1000), 0x3000, [1] * 65,
+                    _cache(Bn=65, lens=[0] * 65), 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.DFlashError) as e:     # negative rows
+        B.inject_kv(_dims(), B.Weights(w_qkv=0x1000), 0x3000, [-1, 1], _cache(), 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+
+
+def test_argmax_accept_flags(lib):
+    for flags in (0, 4, 7):
+        with pytest.raises(B.DFlashError) as e:
+            B.argmax_accept(_dims(), B.Weights(lm_head=0x1000), flags, 0x2000, 1, 16, 0x3000, 0x4000,
+                            0x5000, 0x6000, None, None, 0, 0)
+        assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.DFlashError) as e:     # ACCEPT needs target/tau/next
+        B.argmax_accept(_dims(), None, B.ACCEPT, None, 1, 16, 0x3000, None, 0x5000, 0x6000, None, None, 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+
+
+def test_empty_calls_are_noops(lib):
+    # T = 0 and all-zero row counts return OK without touching the device
+    B.fuse_context(_dims(), B.Weights(), [0] * 5, 256, 0, 0, 0, 0)
+    c = _cache(lens=(3, 4))
+    B.inject_kv(_dims(), B.Weights(), 0, [0, 0], c, 0, 0)
+    assert list(c._keep) == [3, 4]

@@ -1,0 +1,135 @@
+"""HIP path against the CPU oracle on seeded inputs (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_drafter_ctx_amd import binding as B
+from block_diffusion_drafter_ctx_amd.runtime import upload
+from dflash_inputs import CONFIGS, Inputs, shrink
+from tests.parity_util import Workload, close, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU parity tests need a gfx950 GPU")
+    B.load()
+    log(f"library {B.version()} on {torch.cuda.get_device_name(0)}")
+
+
+def small(**kw):
+    """Several weight tiles, a ragged vocabulary tail, GQA 4, ragged context."""
+    base = dict(name="small_bf16", cid=101, D=512, L=2, Hq=8, Hkv=2, d=128, F=1536, V=1000, B=3,
+                ctx=(37, 300, 1), gammas=(16,), gain_std=0.1, iters=2)
+    base.update(kw)
+    return shrink(CONFIGS[2], **base)
+
+
+def test_small_bf16_tokens():
+    log("small bf16, token embeddings, 2 iterations")
+    Workload(small(), 16, 2).run()
+
+
+def test_small_bf16_override():
+    log("small bf16, distinct override rows")
+    Workload(small(cid=102), 16, 1, override=True).run()
+
+
+def test_small_bf16_cache():
+    log("small bf16 weights with a bf16 H_t / KV cache")
+    Workload(small(cid=108, cache_dtype="bf16"), 16, 2, override=True).run()
+
+
+@pytest.mark.parametrize("gamma", [2, 5, 33])
+def test_small_bf16_gamma_edges(gamma):
+    log(f"small bf16, gamma={gamma}")
+    Workload(small(cid=103, gammas=(gamma,)), gamma, 1, override=True).run()
+
+
+def test_small_head64_empty_context():
+    log("small bf16, head_dim 64, a sequence with no context rows")
+    cfg = small(cid=104, d=64, Hq=4, Hkv=4, ctx=(0, 70), B=2, V=777 * 2)
+    Workload(cfg, 8, 1, override=True).run()
+
+
+def test_config1_f32():
+    cfg = CONFIGS[1]
+    log("config 1: tiny fp32 drafter")
+    Workload(cfg, cfg.gamma, 3).run()
+
+
+def test_config1_f32_override():
+    cfg = shrink(CONFIGS[1], cid=105, gain_std=0.1)
+    Workload(cfg, cfg.gamma, 1, override=True).run()
+
+
+def test_determinism_and_untouched_context():
+    cfg = small(cid=106)
+    w = Workload(cfg, 16, 1, override=True)
+    w.ingest(w.inp.ctx_states(), list(cfg.ctx), "context")
+    k0, v0 = w.cache.k.clone(), w.cache.v.clone()
+    tok = torch.from_numpy(w.inp.block_tokens(16)).cuda()
+    outs = []
+    for _ in range(2):
+        h = torch.empty(cfg.B, 16, cfg.D, device="cuda")
+        w.dr.draft(w.cache, tok, None, 16, h)
+        d = torch.empty(cfg.B, 15, dtype=torch.int32, device="cuda")
+        w.dr.argmax_accept(B.ARGMAX, h, cfg.B, 16, d)
+        torch.cuda.synchronize()
+        outs.append((h.clone(), d.clone(), w.cache.k.clone(), w.cache.v.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][2], outs[1][2]) and torch.equal(outs[0][3], outs[1][3])
+    lens = w.cache.len_list()
+    for b in range(cfg.B):
+        assert torch.equal(w.cache.k[:, b, :, :lens[b]], k0[:, b, :, :lens[b]])
+        assert torch.equal(w.cache.v[:, b, :, :, :lens[b]], v0[:, b, :, :, :lens[b]])
+    # fuse + inject again from scratch gives bit-identical cache rows
+    c2 = w.dr.cache(cfg.B, w.cache.cap)
+    h_dev = [upload(h, cfg) for h in w.inp.ctx_states()]
+    Ht = w.dr.context_buffer(cfg.n_ctx_total)
+    w.dr.fuse(h_dev, cfg.n_ctx_total, Ht)
+    w.dr.inject(Ht, list(cfg.ctx), c2)
+    torch.cuda.synchronize()
+    for b in range(cfg.B):
+        assert torch.equal(c2.k[:, b, :, :lens[b]], k0[:, b, :, :lens[b]])
+        assert torch.equal(c2.v[:, b, :, :, :lens[b]], v0[:, b, :, :, :lens[b]])
+
+
+def test_errors_enqueue_nothing():
+    cfg = small(cid=107)
+    w = Workload(cfg, 16, 1)
+    w.ingest(w.inp.ctx_states(), list(cfg.ctx), "context")
+    k0 = w.cache.k.clone()
+    lens = w.cache.len_list()
+    w.cache.set_lens([w.cache.cap - 3] + lens[1:])
+    h = torch.full((cfg.B, 16, cfg.D), 7.0, device="cuda")
+    tok = torch.from_numpy(w.inp.block_tokens(16)).cuda()
+    with pytest.raises(B.DFlashError) as e:
+        w.dr.draft(w.cache, tok, None, 16, h)
+    assert e.value.status == B.ERR_CAPACITY
+    torch.cuda.synchronize()
+    assert torch.all(h == 7.0) and torch.equal(w.cache.k, k0)
+    w.cache.set_lens(lens)
+
+
+@pytest.mark.timeout(900)
+def test_config2_full():
+    cfg = CONFIGS[2]
+    log("config 2 full size (Qwen3-8B-shaped, N=2048), 2 iterations")
+    Workload(cfg, 16, 2).run()
+
+
+@pytest.mark.timeout(900)
+def test_config2_full_override():
+    cfg = shrink(CONFIGS[2], cid=202)
+    log("config 2 full size with distinct block rows (argmax on 15 different rows)")
+    Workload(cfg, 16, 1, override=True).run()
+
+
+@pytest.mark.timeout(900)
+def test_config2_full_bf16_cache():
+    cfg = shrink(CONFIGS[2], cid=203, cache_dtype="bf16")
+    log("config 2 full size, bf16 H_t / KV cache, distinct block rows")
+    Workload(cfg, 16, 1, override=True).run()
