@@ -30,6 +30,8 @@
 
 #include <stdlib.h>
 
+#include <type_traits>
+
 namespace dflash {
 namespace {
 
@@ -43,50 +45,50 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, int item, int& b,
   sp = local - j * a.nsplit[b];
 }
 
-// Loads of 8 key / value elements as MFMA operands (hi, and lo for fp32 caches).
+// Raw key / value loads (kept in registers until used, so the next block's
+// loads can be in flight during this block's math) and their conversion into
+// MFMA operands (bf16 as is; fp32 split into bf16 hi + lo).
 template <typename TKV> struct KVLoad;
 template <> struct KVLoad<uint16_t> {
   static constexpr bool kSplit = false;
+  struct Raw { uint4 u; };
   // 8 consecutive elements
-  static __device__ __forceinline__ void row8(const uint16_t* p, uint4& hi, uint4& lo) {
-    hi = *reinterpret_cast<const uint4*>(p);
-    lo = hi;
-  }
+  static __device__ __forceinline__ Raw row8(const uint16_t* p) { return Raw{*reinterpret_cast<const uint4*>(p)}; }
   // elements [k, k+4) and [k+16, k+20) of one transposed value row
-  static __device__ __forceinline__ void pair4(const uint16_t* p, int k, uint4& hi, uint4& lo) {
+  static __device__ __forceinline__ Raw pair4(const uint16_t* p, int k) {
     const uint2 v0 = *reinterpret_cast<const uint2*>(p + k);
     const uint2 v1 = *reinterpret_cast<const uint2*>(p + k + 16);
-    hi = make_uint4(v0.x, v0.y, v1.x, v1.y);
-    lo = hi;
+    return Raw{make_uint4(v0.x, v0.y, v1.x, v1.y)};
   }
   // same with every index clamped to <= last
-  static __device__ __forceinline__ void pair4_clamped(const uint16_t* p, int k, int last, uint4& hi, uint4& lo) {
+  static __device__ __forceinline__ Raw pair4_clamped(const uint16_t* p, int k, int last) {
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int kl = min(k + (e >> 1) * 16 + 2 * (e & 1), last), kh = min(k + (e >> 1) * 16 + 2 * (e & 1) + 1, last);
       w[e] = static_cast<uint32_t>(p[kl]) | (static_cast<uint32_t>(p[kh]) << 16);
     }
-    hi = make_uint4(w[0], w[1], w[2], w[3]);
-    lo = hi;
+    return Raw{make_uint4(w[0], w[1], w[2], w[3])};
   }
+  static __device__ __forceinline__ void ops(const Raw& r, uint4& hi, uint4& lo) { hi = r.u; lo = r.u; }
 };
 template <> struct KVLoad<float> {
   static constexpr bool kSplit = true;
-  static __device__ __forceinline__ void row8(const float* p, uint4& hi, uint4& lo) {
-    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    split8(x, hi, lo);
+  struct Raw { float4 a, b; };
+  static __device__ __forceinline__ Raw row8(const float* p) {
+    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
-  static __device__ __forceinline__ void pair4(const float* p, int k, uint4& hi, uint4& lo) {
-    const float4 a = *reinterpret_cast<const float4*>(p + k), b = *reinterpret_cast<const float4*>(p + k + 16);
-    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    split8(x, hi, lo);
+  static __device__ __forceinline__ Raw pair4(const float* p, int k) {
+    return Raw{*reinterpret_cast<const float4*>(p + k), *reinterpret_cast<const float4*>(p + k + 16)};
   }
-  static __device__ __forceinline__ void pair4_clamped(const float* p, int k, int last, uint4& hi, uint4& lo) {
+  static __device__ __forceinline__ Raw pair4_clamped(const float* p, int k, int last) {
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = p[min(k + (e >> 2) * 16 + (e & 3), last)];
+    return Raw{make_float4(x[0], x[1], x[2], x[3]), make_float4(x[4], x[5], x[6], x[7])};
+  }
+  static __device__ __forceinline__ void ops(const Raw& r, uint4& hi, uint4& lo) {
+    const float x[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
     split8(x, hi, lo);
   }
 };
@@ -132,37 +134,57 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  using Raw = typename LD::Raw;
+  Raw kr[2][DS], vr[DT];
 
-  for (int k0 = kbeg; k0 < kend; k0 += 32) {
-    const bool full = k0 + 32 <= kend;
-    // ---- scores S^T: rows = 32 keys (2 tiles), columns = this wave's 16 query rows
-    f32x4_t s[2];
+  // Loads of one 32-key block; FULL blocks need no clamping (the ragged tail of
+  // a key range is a separate, clamped block after the main loop).
+  auto load_k = [&](int k0, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = FULL ? k0 + kt * 16 + (lane & 15) : min(k0 + kt * 16 + (lane & 15), kend - 1);
+      const TKV* kp = kbase + static_cast<int64_t>(key) * HD;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) kr[kt][ds] = LD::row8(kp + ds * 32);
+    }
+  };
+  auto load_v = [&](int k0, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const TKV* vp = vbase + static_cast<int64_t>(dt * 16 + (lane & 15)) * a.cap;
+      vr[dt] = FULL ? LD::pair4(vp, k0 + 4 * g4) : LD::pair4_clamped(vp, k0 + 4 * g4, kend - 1);
+    }
+  };
+
+  // One block in two phases: scores (reads kr), then online softmax (base 2;
+  // the scale is folded into Q) and PV (reads vr).
+  auto scores = [&](f32x4_t (&s)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int key = min(k0 + kt * 16 + (lane & 15), kend - 1);
-      const TKV* kp = kbase + static_cast<int64_t>(key) * HD;
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
         uint4 kh, kl;
-        LD::row8(kp + ds * 32, kh, kl);
+        LD::ops(kr[kt][ds], kh, kl);
         s[kt] = mfma16x16x32(kh, qh[ds], s[kt]);
         s[kt] = mfma16x16x32(kh, ql[ds], s[kt]);
         if constexpr (LD::kSplit) s[kt] = mfma16x16x32(kl, qh[ds], s[kt]);
       }
     }
-    // ---- online softmax (base 2; the scale is folded into Q)
+  };
+  auto softmax_pv = [&](const f32x4_t (&s)[2], int k0, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     float p[8];
-    float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = k0 + kt * 16 + 4 * g4 + rr;
-        const float v = key < kend ? s[kt][rr] : -INFINITY;
-        p[kt * 4 + rr] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int rr = 0; rr < 4; ++rr)
+        p[kt * 4 + rr] = (FULL || k0 + kt * 16 + 4 * g4 + rr < kend) ? s[kt][rr] : -INFINITY;
+    float mx = p[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, p[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float m_new = fmaxf(m_run, mx);
@@ -175,22 +197,56 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
     }
     l_run = l_run * alpha + ps;
     m_run = m_new;
+    if (__any(alpha != 1.0f)) {            // skipped once every row's max has settled
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
     uint4 ph, pl;
     split8(p, ph, pl);
-    // ---- O^T += V^T P^T; k-slot e of lane group g4 <-> key k0 + 4*g4 + e (e < 4),
-    //      k0 + 16 + 4*g4 + (e - 4) (e >= 4): the layout S^T left in p[].
+    // O^T += V^T P^T; k-slot e of lane group g4 <-> key k0 + 4*g4 + e (e < 4),
+    // k0 + 16 + 4*g4 + (e - 4) (e >= 4): the layout S^T left in p[].
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const TKV* vp = vbase + static_cast<int64_t>(dt * 16 + (lane & 15)) * a.cap;
       uint4 vh, vl;
-      if (full) LD::pair4(vp, k0 + 4 * g4, vh, vl);
-      else LD::pair4_clamped(vp, k0 + 4 * g4, kend - 1, vh, vl);
+      LD::ops(vr[dt], vh, vl);
       o[dt] = mfma16x16x32(vh, ph, o[dt]);
       o[dt] = mfma16x16x32(vh, pl, o[dt]);
       if constexpr (LD::kSplit) o[dt] = mfma16x16x32(vl, ph, o[dt]);
     }
+  };
+
+  using Full = std::integral_constant<bool, true>;
+  using Tail = std::integral_constant<bool, false>;
+  const int kfull = kbeg + ((kend - kbeg) / 32) * 32;   // end of the full blocks
+  // bf16 caches prefetch the next block's keys during this block's softmax and
+  // PV and its values right after; fp32 caches (twice the registers per key)
+  // load keys and values together at the top of each block instead.
+  constexpr bool kPrefetch = !LD::kSplit;
+  if (kPrefetch && kbeg < kfull) {
+    load_k(kbeg, Full{});
+    load_v(kbeg, Full{});
+  }
+  for (int k0 = kbeg; k0 < kfull; k0 += 32) {
+    f32x4_t s[2];
+    if (!kPrefetch) {
+      load_k(k0, Full{});
+      load_v(k0, Full{});
+      scores(s);
+      softmax_pv(s, k0, Full{});
+    } else {
+      const bool more = k0 + 32 < kfull;
+      scores(s);
+      if (more) load_k(k0 + 32, Full{});   // next keys fly during softmax + PV
+      softmax_pv(s, k0, Full{});
+      if (more) load_v(k0 + 32, Full{});
+    }
+  }
+  if (kfull < kend) {
+    f32x4_t s[2];
+    load_k(kfull, Tail{});
+    load_v(kfull, Tail{});
+    scores(s);
+    softmax_pv(s, kfull, Tail{});
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
@@ -209,7 +265,13 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 }
 
 // Merge the key ranges of one (row, head): O = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
+// The split weights are computed once per row into LDS; the O loads of all
+// splits are then independent.
+constexpr int kMaxSplitsLds = 1024;
+
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float wts[kMaxSplitsLds];
+  __shared__ float inv_l;
   const int idx = blockIdx.x;
   const int m = idx / a.Hq, h = idx % a.Hq;
   const int b = m / a.gamma, i = m % a.gamma;
@@ -217,17 +279,26 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int r = (h - j * G) * a.gamma + i;
   const int ns = a.nsplit[b];
   const int it0 = a.item_off[b] + j * ns;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(static_cast<int64_t>(it0 + s) * a.Rpad + r) * 2]);
-  for (int c = threadIdx.x; c < a.d; c += blockDim.x) {
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const int64_t rowi = static_cast<int64_t>(it0 + s) * a.Rpad + r;
-      const float w = exp2f(a.part_ml[rowi * 2] - M);
-      L += w * a.part_ml[rowi * 2 + 1];
-      O += w * a.part_o[rowi * a.d + c];
+  if (threadIdx.x < 64) {
+    float M = -INFINITY;
+    for (int s = threadIdx.x; s < ns; s += 64) M = fmaxf(M, a.part_ml[(static_cast<int64_t>(it0 + s) * a.Rpad + r) * 2]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int s = threadIdx.x; s < ns; s += 64) {
+      const float* ml = a.part_ml + (static_cast<int64_t>(it0 + s) * a.Rpad + r) * 2;
+      const float w = exp2f(ml[0] - M);
+      wts[s] = w;
+      L += w * ml[1];
     }
-    a.o_out[(static_cast<int64_t>(m) * a.Hq + h) * a.d + c] = O / L;
+    L = wave_sum(L);
+    if (threadIdx.x == 0) inv_l = 1.0f / L;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < a.d; c += blockDim.x) {
+    float O = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) O += wts[s] * a.part_o[(static_cast<int64_t>(it0 + s) * a.Rpad + r) * a.d + c];
+    a.o_out[(static_cast<int64_t>(m) * a.Hq + h) * a.d + c] = O * inv_l;
   }
 }
 
@@ -286,6 +357,10 @@ AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d) {
   int64_t sk = (total * Hkv + target - 1) / target;
   sk = ((sk + 31) / 32) * 32;
   if (sk < min_keys) sk = ((min_keys + 31) / 32) * 32;
+  int maxk = 0;
+  for (int b = 0; b < B; ++b) maxk = nkeys[b] > maxk ? nkeys[b] : maxk;
+  const int64_t sk_min = ((maxk + kMaxSplitsLds - 1) / kMaxSplitsLds + 31) / 32 * 32;   // combine's LDS table
+  if (sk < sk_min) sk = sk_min;
   p.split_keys = static_cast<int>(sk);
   p.item_off[0] = 0;
   for (int b = 0; b < B; ++b) {

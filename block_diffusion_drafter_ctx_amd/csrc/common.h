@@ -9,6 +9,8 @@
 namespace dflash {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -18,11 +20,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
-// Round to nearest even (finite inputs).
+// Round to nearest even (gfx950's v_cvt_pk_bf16_f32 in the default rounding mode).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two floats -> packed bf16 pair (a in the low half), one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
 }
 
 // Storage-type traits: bf16 is held as uint16_t bit patterns.
@@ -40,15 +45,15 @@ template <> struct Store<float> {
 // with |x - hi - lo| <= 2^-16 |x| (so an MFMA pair on (hi, lo) keeps ~16
 // significant bits of an fp32 activation against exact bf16 weights).
 __device__ __forceinline__ void split8(const float* x, uint4& hi, uint4& lo) {
-  uint32_t h[8], l[8];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint16_t hb = f32_to_bf16(x[i]);
-    h[i] = hb;
-    l[i] = f32_to_bf16(x[i] - bf16_to_f32(hb));
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    const float h0 = __uint_as_float(h[i] << 16), h1 = __uint_as_float(h[i] & 0xffff0000u);
+    l[i] = pack_bf16x2(x[2 * i] - h0, x[2 * i + 1] - h1);
   }
-  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 // D += A (16 rows x 32 k) * B (32 k x 16 cols).  Lane l supplies A row (l % 16)

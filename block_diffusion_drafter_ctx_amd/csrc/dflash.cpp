@@ -49,7 +49,7 @@ dflash_status ok() {
   } while (0)
 
 constexpr size_t kAlign = 256;
-constexpr int kRowBlock = 4096;   // rows per fuse / inject GEMM pass
+constexpr int kRowBlock = 512;    // rows per fuse / inject GEMM pass
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -149,18 +149,20 @@ struct Carve {
   }
 };
 
-size_t gemm_part_floats(const dflash_dims* d, int M, int N, int K, bool single) {
+size_t gemm_part_floats(const dflash_dims* d, int M, int N, int K, GemmAKind ak, bool wide = false) {
   if (M <= 0) return 0;
   if (d->dtype == DFLASH_F32) return static_cast<size_t>(M) * N;
-  return plan_gemm_mfma(M, N, K, single).part_floats;
+  return plan_gemm_mfma(M, N, K, ak, wide).part_floats;
 }
+
+GemmAKind ctx_a_kind(const dflash_dims* d) { return d->cache_dtype == DFLASH_BF16 ? A_BF16 : A_F32_SPLIT; }
 
 // fuse: partials of one row-block pass
 size_t fuse_ws(const dflash_dims* d, int max_rows) {
   size_t best = 0;
   const int hi = max_rows < kRowBlock ? max_rows : kRowBlock;
   for (int M = 1; M <= hi; ++M) {
-    const size_t f = gemm_part_floats(d, M, d->D, d->n_tgt_layers * d->D, false);
+    const size_t f = gemm_part_floats(d, M, d->D, d->n_tgt_layers * d->D, A_BF16);
     if (f > best) best = f;
   }
   return best ? align_up(best * 4) : 0;
@@ -171,7 +173,7 @@ size_t inject_ws(const dflash_dims* d, int max_rows) {
   const int N = 2 * d->L * d->Hkv * d->head_dim;
   const int hi = max_rows < kRowBlock ? max_rows : kRowBlock;
   for (int M = 1; M <= hi; ++M) {
-    const size_t f = gemm_part_floats(d, M, N, d->D, false);
+    const size_t f = gemm_part_floats(d, M, N, d->D, ctx_a_kind(d));
     if (f > best) best = f;
   }
   return best ? align_up(best * 4) : 0;
@@ -187,7 +189,7 @@ DraftWs draft_ws(const dflash_dims* d, int B, int gamma) {
   const int nqkv = (d->Hq + 2 * d->Hkv) * d->head_dim;
   size_t part = 0;
   auto upd = [&](int N, int K) {
-    const size_t f = gemm_part_floats(d, M, N, K, false);
+    const size_t f = gemm_part_floats(d, M, N, K, A_F32_SPLIT);
     if (f > part) part = f;
   };
   upd(nqkv, d->D);
@@ -211,11 +213,23 @@ DraftWs draft_ws(const dflash_dims* d, int B, int gamma) {
   return w;
 }
 
-size_t argmax_ws(const dflash_dims* d, int B, int gamma) {
+// LM head: split-K partials [S][M][V], then per-128-column top-2 [ceil(V/128)][M][3]
+struct ArgmaxWs {
+  size_t part, top2, total;
+};
+
+ArgmaxWs argmax_ws(const dflash_dims* d, int B, int gamma) {
   const int M = B * (gamma - 1);
-  if (d->dtype == DFLASH_F32) return align_up(static_cast<size_t>(M) * d->V * 4);
-  const GemmPlan p = plan_gemm_mfma(M, d->V, d->D, true);
-  return align_up(static_cast<size_t>(p.ntiles) * M * 3 * 4);
+  ArgmaxWs w{};
+  Carve c;
+  if (d->dtype == DFLASH_F32) {
+    w.part = c.take(static_cast<size_t>(M) * d->V * 4);
+  } else {
+    w.part = c.take(gemm_part_floats(d, M, d->V, d->D, A_F32_SPLIT, true) * 4);
+    w.top2 = c.take(static_cast<size_t>((d->V + 511) / 512) * M * 3 * 4);
+  }
+  w.total = c.off;
+  return w;
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -237,7 +251,7 @@ dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t 
   DF_REQUIRE(max_rows >= 0, DFLASH_ERR_INVALID_ARG, "max_rows=%d < 0", max_rows);
   DF_REQUIRE(bytes != nullptr, DFLASH_ERR_INVALID_ARG, "bytes is NULL");
   size_t need = draft_ws(dims, B, gamma).total;
-  const size_t f = fuse_ws(dims, max_rows), i = inject_ws(dims, max_rows), a = argmax_ws(dims, B, gamma);
+  const size_t f = fuse_ws(dims, max_rows), i = inject_ws(dims, max_rows), a = argmax_ws(dims, B, gamma).total;
   if (f > need) need = f;
   if (i > need) need = i;
   if (a > need) need = a;
@@ -290,9 +304,9 @@ dflash_status dflash_fuse_context(const dflash_dims* dims, const dflash_weights*
     g.part = part;
     int S = 1;
     if (bf) {
-      const GemmPlan p = plan_gemm_mfma(M, D, K, false);
+      const GemmPlan p = plan_gemm_mfma(M, D, K, A_BF16, false);
       S = p.S;
-      DF_HIP(launch_gemm_mfma(g, A_BF16, p, false, s));
+      DF_HIP(launch_gemm_mfma(g, A_BF16, p, s));
     } else {
       DF_HIP(launch_gemm_f32(g, s));
     }
@@ -354,10 +368,10 @@ dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w,
     g.part = part;
     int S = 1;
     if (bf) {
-      const GemmPlan p = plan_gemm_mfma(M, N, D, false);
-      S = p.S;
       // an fp32 H_t is split hi + lo against the bf16 weights like any fp32 activation
-      DF_HIP(launch_gemm_mfma(g, cbf ? A_BF16 : A_F32_SPLIT, p, false, s));
+      const GemmPlan p = plan_gemm_mfma(M, N, D, ctx_a_kind(dims), false);
+      S = p.S;
+      DF_HIP(launch_gemm_mfma(g, ctx_a_kind(dims), p, s));
     } else {
       DF_HIP(launch_gemm_f32(g, s));
     }
@@ -451,9 +465,9 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
       *S = 1;
       return launch_gemm_f32(g, s);
     }
-    const GemmPlan p = plan_gemm_mfma(M, N, K, false);
+    const GemmPlan p = plan_gemm_mfma(M, N, K, A_F32_SPLIT, false);
     *S = p.S;
-    return launch_gemm_mfma(g, A_F32_SPLIT, p, false, s);
+    return launch_gemm_mfma(g, A_F32_SPLIT, p, s);
   };
 
   int32_t nkeys[kMaxSeq];
@@ -536,7 +550,7 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
     if ((st = check_ptr(w->lm_head, "lm_head")) != DFLASH_OK) return st;
     if ((st = check_ptr(h_final, "h_final")) != DFLASH_OK) return st;
     if (logits_dbg != nullptr && (st = check_ptr(logits_dbg, "logits_dbg")) != DFLASH_OK) return st;
-    need = argmax_ws(dims, B, gamma);
+    need = argmax_ws(dims, B, gamma).total;
   }
   if (flags & DFLASH_ACCEPT) {
     DF_REQUIRE(target != nullptr && tau != nullptr && next_anchor != nullptr, DFLASH_ERR_INVALID_ARG,
@@ -562,12 +576,16 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
     g.M = Mr;
     g.N = dims->V;
     g.K = D;
+    const ArgmaxWs lay = argmax_ws(dims, B, gamma);
+    char* base = static_cast<char*>(ws);
     if (dims->dtype == DFLASH_BF16) {
-      const GemmPlan p = plan_gemm_mfma(Mr, dims->V, D, true);
-      g.top2 = static_cast<float*>(ws);
-      g.logits = logits_dbg;
-      DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, true, s));
-      DF_HIP(launch_argmax_final(g.top2, p.ntiles, Mr, draft, top2_gap, s));
+      const GemmPlan p = plan_gemm_mfma(Mr, dims->V, D, A_F32_SPLIT, true);
+      g.part = reinterpret_cast<float*>(base + lay.part);
+      float* top2 = reinterpret_cast<float*>(base + lay.top2);
+      DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, s));
+      int nt = 0;
+      DF_HIP(launch_reduce_top2(g.part, p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
+      DF_HIP(launch_argmax_final(top2, nt, Mr, draft, top2_gap, s));
     } else {
       float* lg = logits_dbg != nullptr ? logits_dbg : static_cast<float*>(ws);
       g.part = lg;

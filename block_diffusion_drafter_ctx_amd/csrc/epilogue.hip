@@ -18,6 +18,13 @@ namespace {
 
 constexpr int kRowThreads = 256;
 
+// Threads per row kernel: one float4 group per thread where possible.
+int row_threads(int D) {
+  int t = D / 4;
+  t = t < 64 ? 64 : (t > 1024 ? 1024 : t);
+  return (t + 63) / 64 * 64;
+}
+
 template <typename T>
 __device__ __forceinline__ float ldw(const void* p, int64_t i) {
   return Store<T>::ld(static_cast<const T*>(p) + i);
@@ -29,95 +36,144 @@ __device__ __forceinline__ float sum_parts(const float* part, int S, int64_t str
   return v;
 }
 
+// Row kernels: one workgroup per row, each thread owns float4 column groups
+// (D / 4 / blockDim of them); every split-K partial of a group is loaded before
+// any is added, so a row costs one or two memory latencies instead of S*D/256.
+constexpr int kRowMaxGroups = 4;     // float4 groups per thread (D <= 4 * 4 * blockDim)
+
+__device__ __forceinline__ float4 f4add(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+__device__ __forceinline__ float4 sum_parts4(const float* part, int S, int64_t stride, int64_t i) {
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = 0;
+  for (; s + 4 <= S; s += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(part + (s + 0) * stride + i);
+    const float4 b = *reinterpret_cast<const float4*>(part + (s + 1) * stride + i);
+    const float4 c = *reinterpret_cast<const float4*>(part + (s + 2) * stride + i);
+    const float4 d = *reinterpret_cast<const float4*>(part + (s + 3) * stride + i);
+    v = f4add(f4add(f4add(f4add(v, a), b), c), d);
+  }
+  for (; s < S; ++s) v = f4add(v, *reinterpret_cast<const float4*>(part + s * stride + i));
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ float4 ld4(const void* p, int64_t i) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    return make_float4(bf16_to_f32(u.x & 0xffff), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffff),
+                       bf16_to_f32(u.y >> 16));
+  } else {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void st4(void* p, int64_t i, float4 v) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t lo = f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+    const uint32_t hi = f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = v;
+  }
+}
+
+__device__ __forceinline__ float4 f4scale(float4 a, float4 g, float s) {
+  return make_float4(g.x * (a.x * s), g.y * (a.y * s), g.z * (a.z * s), g.w * (a.w * s));
+}
+
 // ------------------------------------------------------------- ctx_norm
 template <typename TW, typename TC>
-__global__ __launch_bounds__(kRowThreads) void ctx_norm_kernel(const float* part, int S, int T_, int D,
-                                                               const void* g, float eps, TC* out) {
+__global__ __launch_bounds__(1024) void ctx_norm_kernel(const float* part, int S, int T_, int D,
+                                                        const void* g, float eps, TC* out) {
   __shared__ float red[16];
-  extern __shared__ float row[];
   const int t = blockIdx.x;
   const int64_t stride = static_cast<int64_t>(T_) * D;
+  float4 u[kRowMaxGroups];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    const float u = sum_parts(part, S, stride, static_cast<int64_t>(t) * D + c);
-    row[c] = u;
-    ss += u * u;
+#pragma unroll
+  for (int j = 0; j < kRowMaxGroups; ++j) {
+    const int c = 4 * (threadIdx.x + j * blockDim.x);
+    if (c < D) {
+      u[j] = sum_parts4(part, S, stride, static_cast<int64_t>(t) * D + c);
+      ss += u[j].x * u[j].x + u[j].y * u[j].y + u[j].z * u[j].z + u[j].w * u[j].w;
+    }
   }
   const float inv = 1.0f / sqrtf(block_sum(ss, red) / D + eps);
-  for (int c = threadIdx.x; c < D; c += blockDim.x)
-    Store<TC>::st(out + static_cast<int64_t>(t) * D + c, ldw<TW>(g, c) * (row[c] * inv));
+#pragma unroll
+  for (int j = 0; j < kRowMaxGroups; ++j) {
+    const int c = 4 * (threadIdx.x + j * blockDim.x);
+    if (c < D) st4<TC>(out, static_cast<int64_t>(t) * D + c, f4scale(u[j], ld4<TW>(g, c), inv));
+  }
 }
 
 // ------------------------------------------------------------- scatter_kv
-// Tile of 32 rows x 64 columns; keys are written along d, values along rows.
+// Tile of 16 rows x 64 columns, 256 threads: thread t owns row t % 16 and the
+// float4 column group t / 16.  Query and key columns are written along the
+// column index; value columns go to the transposed value rows, where the 16
+// threads of a column group write 16 consecutive cache positions.
 template <typename T>
 __global__ __launch_bounds__(256) void scatter_kv_kernel(ScatterArgs a) {
-  __shared__ float tile[32][65];
-  const int n0 = blockIdx.x * 64, r0 = blockIdx.y * 32;
+  const int rr = threadIdx.x & 15, cg = threadIdx.x >> 4;
+  const int r = blockIdx.y * 16 + rr, n = blockIdx.x * 64 + 4 * cg;
+  if (r >= a.M || n >= a.N) return;
   const int64_t stride = static_cast<int64_t>(a.M) * a.N;
-  for (int e = threadIdx.x; e < 32 * 64; e += 256) {
-    const int rr = e >> 6, cc = e & 63, r = r0 + rr, n = n0 + cc;
-    float v = 0.f;
-    if (r < a.M && n < a.N) v = sum_parts(a.part, a.S, stride, static_cast<int64_t>(r) * a.N + n);
-    tile[rr][cc] = v;
+  const float4 v = sum_parts4(a.part, a.S, stride, static_cast<int64_t>(r) * a.N + n);
+  if (n < a.nq) {
+    *reinterpret_cast<float4*>(a.q_out + static_cast<int64_t>(r) * a.nq + n) = v;
+    return;
   }
-  __syncthreads();
   const int hd = a.Hkv * a.d;
-  // query columns and key columns: write along the column index
-  for (int e = threadIdx.x; e < 32 * 64; e += 256) {
-    const int rr = e >> 6, cc = e & 63, r = r0 + rr, n = n0 + cc;
-    if (r >= a.M || n >= a.N) continue;
-    if (n < a.nq) {
-      a.q_out[static_cast<int64_t>(r) * a.nq + n] = tile[rr][cc];
-      continue;
-    }
-    const int kvn = n - a.nq;
-    const int layer = a.layer0 + kvn / (2 * hd);
-    const int rem = kvn % (2 * hd);
-    if (rem >= hd) continue;                       // value column: second pass
-    int b = 0;
-    while (b + 1 < a.rows.B && r >= a.rows.row_off[b + 1]) ++b;
-    const int pos = a.rows.pos0[b] + (r - a.rows.row_off[b]);
+  const int kvn = n - a.nq;
+  const int layer = a.layer0 + kvn / (2 * hd);
+  const int rem = kvn % (2 * hd);
+  int b = 0;
+  while (b + 1 < a.rows.B && r >= a.rows.row_off[b + 1]) ++b;
+  const int pos = a.rows.pos0[b] + (r - a.rows.row_off[b]);
+  const int64_t head0 = (static_cast<int64_t>(layer) * a.B + b) * a.Hkv;
+  if (rem < hd) {
     const int j = rem / a.d, c = rem % a.d;
-    const int64_t off = ((static_cast<int64_t>(layer) * a.B + b) * a.Hkv + j) * a.cap + pos;
-    Store<T>::st(static_cast<T*>(a.kc) + off * a.d + c, tile[rr][cc]);
-  }
-  // value columns: write along the row (cache position) index
-  for (int e = threadIdx.x; e < 32 * 64; e += 256) {
-    const int cc = e >> 5, rr = e & 31, r = r0 + rr, n = n0 + cc;
-    if (r >= a.M || n >= a.N || n < a.nq) continue;
-    const int kvn = n - a.nq;
-    const int layer = a.layer0 + kvn / (2 * hd);
-    const int rem = kvn % (2 * hd);
-    if (rem < hd) continue;
-    int b = 0;
-    while (b + 1 < a.rows.B && r >= a.rows.row_off[b + 1]) ++b;
-    const int pos = a.rows.pos0[b] + (r - a.rows.row_off[b]);
+    st4<T>(a.kc, ((head0 + j) * a.cap + pos) * a.d + c, v);
+  } else {
     const int j = (rem - hd) / a.d, c = (rem - hd) % a.d;
-    const int64_t off = (((static_cast<int64_t>(layer) * a.B + b) * a.Hkv + j) * a.d + c) * a.cap + pos;
-    Store<T>::st(static_cast<T*>(a.vc) + off, tile[rr][cc]);
+    T* vp = static_cast<T*>(a.vc) + ((head0 + j) * a.d + c) * a.cap + pos;
+    Store<T>::st(vp, v.x);
+    Store<T>::st(vp + a.cap, v.y);
+    Store<T>::st(vp + 2 * a.cap, v.z);
+    Store<T>::st(vp + 3 * a.cap, v.w);
   }
 }
 
 // ------------------------------------------------------------- residual_norm
 template <typename T>
-__global__ __launch_bounds__(kRowThreads) void residual_norm_kernel(const float* part, int S, int M, int D,
-                                                                    float* h, const void* g, float eps,
-                                                                    float* a_out) {
+__global__ __launch_bounds__(1024) void residual_norm_kernel(const float* part, int S, int M, int D, float* h,
+                                                             const void* g, float eps, float* a_out) {
   __shared__ float red[16];
   const int m = blockIdx.x;
   const int64_t stride = static_cast<int64_t>(M) * D;
-  float* hr = h + static_cast<int64_t>(m) * D;
+  float4 v[kRowMaxGroups];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float v = hr[c];
-    if (part != nullptr) v += sum_parts(part, S, stride, static_cast<int64_t>(m) * D + c);
-    hr[c] = v;
-    ss += v * v;
+#pragma unroll
+  for (int j = 0; j < kRowMaxGroups; ++j) {
+    const int c = 4 * (threadIdx.x + j * blockDim.x);
+    if (c < D) {
+      const int64_t i = static_cast<int64_t>(m) * D + c;
+      v[j] = *reinterpret_cast<const float4*>(h + i);
+      if (part != nullptr) v[j] = f4add(v[j], sum_parts4(part, S, stride, i));
+      *reinterpret_cast<float4*>(h + i) = v[j];
+      ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    }
   }
   const float inv = 1.0f / sqrtf(block_sum(ss, red) / D + eps);
-  for (int c = threadIdx.x; c < D; c += blockDim.x)
-    a_out[static_cast<int64_t>(m) * D + c] = ldw<T>(g, c) * (hr[c] * inv);
+#pragma unroll
+  for (int j = 0; j < kRowMaxGroups; ++j) {
+    const int c = 4 * (threadIdx.x + j * blockDim.x);
+    if (c < D)
+      *reinterpret_cast<float4*>(a_out + static_cast<int64_t>(m) * D + c) = f4scale(v[j], ld4<T>(g, c), inv);
+  }
 }
 
 // ------------------------------------------------------------- swiglu
@@ -136,22 +192,30 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* part, int S, i
 // outside [0, V) are clamped into range so a bad id can never read outside the
 // embedding table.
 template <typename T>
-__global__ __launch_bounds__(kRowThreads) void embed_norm_kernel(const int32_t* tok, const float* ov,
-                                                                 const void* embed, int V, int D, const void* g,
-                                                                 float eps, float* h, float* a) {
+__global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* tok, const float* ov, const void* embed,
+                                                          int V, int D, const void* g, float eps, float* h,
+                                                          float* a) {
   __shared__ float red[16];
   const int m = blockIdx.x;
-  float* hr = h + static_cast<int64_t>(m) * D;
   const int64_t src = ov != nullptr ? 0 : static_cast<int64_t>(min(max(tok[m], 0), V - 1)) * D;
+  float4 v[kRowMaxGroups];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    const float v = ov != nullptr ? ov[static_cast<int64_t>(m) * D + c] : ldw<T>(embed, src + c);
-    hr[c] = v;
-    ss += v * v;
+#pragma unroll
+  for (int j = 0; j < kRowMaxGroups; ++j) {
+    const int c = 4 * (threadIdx.x + j * blockDim.x);
+    if (c < D) {
+      v[j] = ov != nullptr ? *reinterpret_cast<const float4*>(ov + static_cast<int64_t>(m) * D + c)
+                           : ld4<T>(embed, src + c);
+      *reinterpret_cast<float4*>(h + static_cast<int64_t>(m) * D + c) = v[j];
+      ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    }
   }
   const float inv = 1.0f / sqrtf(block_sum(ss, red) / D + eps);
-  for (int c = threadIdx.x; c < D; c += blockDim.x)
-    a[static_cast<int64_t>(m) * D + c] = ldw<T>(g, c) * (hr[c] * inv);
+#pragma unroll
+  for (int j = 0; j < kRowMaxGroups; ++j) {
+    const int c = 4 * (threadIdx.x + j * blockDim.x);
+    if (c < D) *reinterpret_cast<float4*>(a + static_cast<int64_t>(m) * D + c) = f4scale(v[j], ld4<T>(g, c), inv);
+  }
 }
 
 // ------------------------------------------------------------- argmax
@@ -190,6 +254,50 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(const float* logits, i
   block_top2_write(t, m, draft, gap);
 }
 
+// ------------------------------------------------------------- reduce_top2
+// LM head: one workgroup of 128 threads per (512-column tile, row); each thread
+// sums the split-K partials of 4 consecutive logits, optionally stores them, and
+// the tile's top-2 is merged over the workgroup.
+constexpr int kTop2Tile = 512;
+
+__global__ __launch_bounds__(128) void reduce_top2_kernel(const float* part, int S, int M, int N, float* logits,
+                                                          float* top2) {
+  __shared__ float sv1[2], sv2[2];
+  __shared__ int si1[2];
+  const int tile = blockIdx.x, m = blockIdx.y;
+  const int n = tile * kTop2Tile + 4 * threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t stride = static_cast<int64_t>(M) * N;
+  const int64_t i = static_cast<int64_t>(m) * N + n;
+  Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+  if ((N & 3) == 0 && n + 3 < N) {
+    const float4 v = sum_parts4(part, S, stride, i);
+    if (logits != nullptr) *reinterpret_cast<float4*>(logits + i) = v;
+    t = top2_push(t, v.x, n);
+    t = top2_push(t, v.y, n + 1);
+    t = top2_push(t, v.z, n + 2);
+    t = top2_push(t, v.w, n + 3);
+  } else {
+    for (int e = 0; e < 4 && n + e < N; ++e) {
+      float v = 0.f;
+      for (int s = 0; s < S; ++s) v += part[s * stride + i + e];
+      if (logits != nullptr) logits[i + e] = v;
+      t = top2_push(t, v, n + e);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) t = top2_merge(t, top2_shfl_xor(t, o));
+  if (lane == 0) { sv1[w] = t.v1; si1[w] = t.i1; sv2[w] = t.v2; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const Top2 r = top2_merge(Top2{sv1[0], si1[0], sv2[0]}, Top2{sv1[1], si1[1], sv2[1]});
+    float* o = top2 + (static_cast<int64_t>(tile) * M + m) * 3;
+    o[0] = r.v1;
+    o[1] = __int_as_float(r.i1);
+    o[2] = r.v2;
+  }
+}
+
 // ------------------------------------------------------------- accept
 __global__ __launch_bounds__(64) void accept_kernel(const int32_t* draft, const int32_t* target, int n,
                                                     int32_t* tau, int32_t* next_anchor) {
@@ -208,8 +316,8 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t* draft, const 
 hipError_t launch_ctx_norm(const float* part, int S, int T, int D, const void* g, float eps, void* out,
                            bool bf16_weights, bool bf16_cache, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const size_t sh = static_cast<size_t>(D) * sizeof(float);
-  const dim3 grid(T), block(kRowThreads);
+  const size_t sh = 0;
+  const dim3 grid(T), block(row_threads(D));
   if (bf16_weights && bf16_cache)
     hipLaunchKernelGGL((ctx_norm_kernel<uint16_t, uint16_t>), grid, block, sh, st, part, S, T, D, g, eps,
                        static_cast<uint16_t*>(out));
@@ -224,7 +332,7 @@ hipError_t launch_ctx_norm(const float* part, int S, int T, int D, const void* g
 
 hipError_t launch_scatter_kv(const ScatterArgs& a, bool bf16_cache, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  dim3 grid((a.N + 63) / 64, (a.M + 31) / 32);
+  dim3 grid((a.N + 63) / 64, (a.M + 15) / 16);
   if (bf16_cache) hipLaunchKernelGGL(scatter_kv_kernel<uint16_t>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(scatter_kv_kernel<float>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
@@ -232,8 +340,9 @@ hipError_t launch_scatter_kv(const ScatterArgs& a, bool bf16_cache, hipStream_t 
 
 hipError_t launch_residual_norm(const float* part, int S, int M, int D, float* h, const void* g, float eps,
                                 float* a_out, bool bf16, hipStream_t st) {
-  if (bf16) hipLaunchKernelGGL(residual_norm_kernel<uint16_t>, dim3(M), dim3(kRowThreads), 0, st, part, S, M, D, h, g, eps, a_out);
-  else hipLaunchKernelGGL(residual_norm_kernel<float>, dim3(M), dim3(kRowThreads), 0, st, part, S, M, D, h, g, eps, a_out);
+  const dim3 block(row_threads(D));
+  if (bf16) hipLaunchKernelGGL(residual_norm_kernel<uint16_t>, dim3(M), block, 0, st, part, S, M, D, h, g, eps, a_out);
+  else hipLaunchKernelGGL(residual_norm_kernel<float>, dim3(M), block, 0, st, part, S, M, D, h, g, eps, a_out);
   return hipGetLastError();
 }
 
@@ -245,8 +354,17 @@ hipError_t launch_swiglu(const float* part, int S, int M, int F, float* s_out, h
 
 hipError_t launch_embed_norm(const int32_t* tok, const float* ov, const void* embed, int V, int M, int D,
                              const void* g, float eps, float* h, float* a, bool bf16, hipStream_t st) {
-  if (bf16) hipLaunchKernelGGL(embed_norm_kernel<uint16_t>, dim3(M), dim3(kRowThreads), 0, st, tok, ov, embed, V, D, g, eps, h, a);
-  else hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(M), dim3(kRowThreads), 0, st, tok, ov, embed, V, D, g, eps, h, a);
+  const dim3 block(row_threads(D));
+  if (bf16) hipLaunchKernelGGL(embed_norm_kernel<uint16_t>, dim3(M), block, 0, st, tok, ov, embed, V, D, g, eps, h, a);
+  else hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(M), block, 0, st, tok, ov, embed, V, D, g, eps, h, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_top2(const float* part, int S, int M, int N, float* logits, float* top2, int* ntiles_out,
+                              hipStream_t st) {
+  const int nt = (N + kTop2Tile - 1) / kTop2Tile;
+  if (ntiles_out != nullptr) *ntiles_out = nt;
+  hipLaunchKernelGGL(reduce_top2_kernel, dim3(nt, M), dim3(128), 0, st, part, S, M, N, logits, top2);
   return hipGetLastError();
 }
 

@@ -2,20 +2,20 @@
 //
 // Every projection on the drafting path is "few activation rows x a large bf16
 // weight matrix" (M = B*gamma <= 256 rows against up to 151936 x 4096 weights),
-// so the kernel is built to stream W from HBM once at full width:
-//   * a workgroup of 4 waves owns 128 consecutive weight rows (each wave two
-//     16-row MFMA strips) and one K range (split-K across workgroups);
-//   * each lane loads 16 B of one weight row per 32-wide k step (the A operand
-//     of v_mfma_f32_16x16x32_bf16), prefetched one 128-wide chunk ahead;
-//   * the activation chunk [MT rows x 128 k] is staged once per workgroup in
-//     LDS, already in MFMA B-operand order (one conflict-free 16 B read per
-//     lane), double-buffered so one barrier per chunk suffices;
+// so the kernel is built to stream W from HBM once, at full width, with as many
+// bytes in flight as the chip needs and no barrier in the streaming loop:
+//   * each wave owns one 16-row MFMA strip of W (the A operand of
+//     v_mfma_f32_16x16x32_bf16: lane l loads 16 B of row l%16) and walks the
+//     workgroup's K range with 8 k-steps (8 KB) of loads in flight, double
+//     buffered in registers;
+//   * the activation slice [MT rows x K range] is staged once per workgroup into
+//     LDS in MFMA B-operand order (one conflict-free 16 B read per lane); the K
+//     range is bounded by the LDS slice (split-K across workgroups otherwise);
 //   * fp32 activations are split into bf16 hi + lo and multiplied twice, which
 //     keeps ~16 significant bits against the exact bf16 weights at no cost on an
 //     HBM-bound kernel;
-//   * partial sums go to a [split][M][N] fp32 buffer reduced in a fixed order by
-//     the consumer (deterministic, no float atomics), or, for the LM head, are
-//     reduced in-kernel to one top-2 (value, index) per row and weight tile.
+//   * partial sums go to a [split][M][N] fp32 buffer that the consumer reduces
+//     in split order (deterministic, no float atomics).
 // The fp32 storage path uses a plain LDS-tiled FMA GEMM (tiny workloads only).
 #include "common.h"
 #include "launch.h"
@@ -25,9 +25,7 @@
 namespace dflash {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kStrips = 2;
-constexpr int kKS = kGemmKC / 32;   // 32-wide k steps per chunk
+constexpr int kStreamU = 8;          // weight k steps in flight per wave
 
 template <typename T>
 __device__ __forceinline__ const T* pick_src(const GemmArgs& g, int s) {
@@ -42,203 +40,173 @@ __device__ __forceinline__ int64_t a_row_off(const GemmArgs& g, int r) {
   return static_cast<int64_t>(r / g.a_rg) * g.a_gs + static_cast<int64_t>(r % g.a_rg) * g.a_ld;
 }
 
-template <int MT, int AK, bool TOP2>
-__global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs g) {
+// Persistent workgroups of WAVES waves.  The work is a list of units
+// (split, m-tile, n-tile) with unit u -> split u % S, then n-tile, then m-tile;
+// workgroup i takes units i, i + P, i + 2P, ... (P = gridDim.x, a multiple of S,
+// so a workgroup keeps one K range and stages its activation slice once).
+// Wave w of a unit streams weight rows [tile*16*WAVES + 16w, +16) over the K
+// range with U k-steps (U KB) of loads in flight, double buffered in registers;
+// the stream continues across unit boundaries without a bubble.  After the
+// activation slice is staged the loop has no barrier.
+template <int MT, int AK, int WAVES, int KR>
+__global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(GemmArgs g) {
   constexpr int MTL = MT / 16;
   constexpr int HL = (AK == A_F32_SPLIT) ? 2 : 1;
-  constexpr int NG = MT / 16;                 // 8-wide A groups per thread per chunk
-  constexpr int BUF = kKS * MTL * HL * 64;    // uint4 per LDS buffer
-  __shared__ uint4 lds[2 * BUF];
+  constexpr int NT = 64 * WAVES;
+  constexpr int U = kStreamU;
+  extern __shared__ uint4 lds[];              // [KR/32][MTL][HL][64]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntile = blockIdx.x, split = blockIdx.y, mtile = blockIdx.z;
-  const int m0 = mtile * MT;
-  const int nchunks = (g.K + kGemmKC - 1) / kGemmKC;
-  const int c_begin = split * g.chunks_per_split;
-  const int c_end = min(nchunks, c_begin + g.chunks_per_split);
+  const int S = g.S, ntiles = g.ntiles;
+  const int units = S * ntiles * g.mtiles;
+  const int P = gridDim.x;
+  const int cps = g.chunks_per_split;         // k steps per split
+  int u = blockIdx.x;
+  if (u >= units) return;
 
-  // ---- weight row pointers (rows past N are clamped; their results are dropped)
-  const uint16_t* wrow[kStrips];
-#pragma unroll
-  for (int st = 0; st < kStrips; ++st) {
-    int n = ntile * kGemmTileN + wave * 32 + st * 16 + (lane & 15);
-    n = min(n, g.N - 1);
-    const int64_t row = static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg;
-    wrow[st] = static_cast<const uint16_t*>(g.w) + row * g.w_ld + 8 * (lane >> 4);
-  }
-
-  // ---- A staging geometry: group q = tid + 256*i covers row q/16, k 8*(q%16)..+7
-  int64_t arow[NG];
-  bool avalid[NG];
-  int lds_slot[NG];
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    const int q = tid + kThreads * i, m = q >> 4, k8 = q & 15;
-    const int r = m0 + m;
-    avalid[i] = r < g.M;
-    arow[i] = avalid[i] ? a_row_off(g, r) : 0;
-    lds_slot[i] = (((k8 >> 2) * MTL + (m >> 4)) * HL) * 64 + (k8 & 3) * 16 + (m & 15);
-  }
-
-  auto load_w = [&](uint4 (&wr)[kKS][kStrips], int c) {
-    const int kb = c * kGemmKC;
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
-      if (kb + ks * 32 < g.K) {
-#pragma unroll
-        for (int st = 0; st < kStrips; ++st)
-          wr[ks][st] = *reinterpret_cast<const uint4*>(wrow[st] + kb + ks * 32);
-      }
-    }
+  // geometry of a unit for this lane
+  auto nks_of = [&](int uu) { const int sp = uu % S; return min(g.K / 32 - sp * cps, cps); };
+  auto wptr_of = [&](int uu) {
+    const int sp = uu % S, rest = uu / S, tile = rest % ntiles;
+    int n = tile * 16 * WAVES + wave * 16 + (lane & 15);
+    n = min(n, g.N - 1);                       // rows past N are clamped; their results are dropped
+    const int64_t wrow = static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg;
+    return static_cast<const uint16_t*>(g.w) + wrow * g.w_ld + sp * cps * 32 + 8 * (lane >> 4);
   };
+  auto key_of = [&](int uu) { return (uu % S) + S * ((uu / S) / ntiles); };   // (split, m-tile)
 
-  // A registers for the chunk being staged
-  float af[(AK == A_F32_SPLIT) ? NG * 8 : 1];
-  uint4 ab[(AK == A_BF16) ? NG : 1];
-
-  auto load_a = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int q = tid + kThreads * i;
-      const int k = c * kGemmKC + 8 * (q & 15);
-      const bool ok = avalid[i] && k < g.K;
+  // stage the activation slice of unit uu: group q -> row q / kg8, k = k0 + 8 * (q % kg8)
+  auto stage = [&](int uu) {
+    const int sp = uu % S, mtile = (uu / S) / ntiles;
+    const int m0 = mtile * MT, k0 = sp * cps * 32, kg8 = nks_of(uu) * 4;
+    for (int q = tid; q < MT * kg8; q += NT) {
+      const int m = q / kg8, kq = q - m * kg8;
+      const int r = m0 + m;
+      const int k = k0 + 8 * kq;
+      const int slot = (((kq >> 2) * MTL + (m >> 4)) * HL) * 64 + (kq & 3) * 16 + (m & 15);
+      const bool ok = r < g.M;
       const int s = k / g.a_cols, col = k - s * g.a_cols;
       if constexpr (AK == A_F32_SPLIT) {
-        float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (ok) {
-          const float* p = pick_src<float>(g, s) + arow[i] + col;
-          x0 = *reinterpret_cast<const float4*>(p);
-          x1 = *reinterpret_cast<const float4*>(p + 4);
+          const float* p = pick_src<float>(g, s) + a_row_off(g, r) + col;
+          const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
+          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
         }
-        af[i * 8 + 0] = x0.x; af[i * 8 + 1] = x0.y; af[i * 8 + 2] = x0.z; af[i * 8 + 3] = x0.w;
-        af[i * 8 + 4] = x1.x; af[i * 8 + 5] = x1.y; af[i * 8 + 6] = x1.z; af[i * 8 + 7] = x1.w;
+        uint4 hi, lo;
+        split8(x, hi, lo);
+        lds[slot] = hi;
+        lds[slot + 64] = lo;
       } else {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (ok) v = *reinterpret_cast<const uint4*>(pick_src<uint16_t>(g, s) + arow[i] + col);
-        ab[i] = v;
+        if (ok) v = *reinterpret_cast<const uint4*>(pick_src<uint16_t>(g, s) + a_row_off(g, r) + col);
+        lds[slot] = v;
       }
     }
   };
 
-  auto store_a = [&](uint4* buf) {
+  uint4 wb0[U], wb1[U];
+  auto load_w = [&](uint4 (&wb)[U], const uint16_t* wp, int nks, int grp) {
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      if constexpr (AK == A_F32_SPLIT) {
-        uint4 hi, lo;
-        split8(&af[i * 8], hi, lo);
-        buf[lds_slot[i]] = hi;
-        buf[lds_slot[i] + 64] = lo;
-      } else {
-        buf[lds_slot[i]] = ab[i];
-      }
+    for (int x = 0; x < U; ++x) {
+      const int ks = grp * U + x;
+      if (ks < nks) wb[x] = *reinterpret_cast<const uint4*>(wp + ks * 32);
     }
   };
 
-  f32x4_t acc[kStrips][MTL];
+  f32x4_t acc[MTL];
 #pragma unroll
-  for (int st = 0; st < kStrips; ++st)
-#pragma unroll
-    for (int mt = 0; mt < MTL; ++mt) acc[st][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MTL; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint4 (&wr)[kKS][kStrips], const uint4* buf, int c) {
-    const int nks = min(kKS, (g.K - c * kGemmKC) / 32);
+  auto compute = [&](const uint4 (&wb)[U], int nks, int grp) {
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
+    for (int x = 0; x < U; ++x) {
+      const int ks = grp * U + x;
       if (ks < nks) {
 #pragma unroll
         for (int mt = 0; mt < MTL; ++mt) {
-          const uint4 bh = buf[((ks * MTL + mt) * HL) * 64 + lane];
-#pragma unroll
-          for (int st = 0; st < kStrips; ++st) acc[st][mt] = mfma16x16x32(wr[ks][st], bh, acc[st][mt]);
-          if constexpr (HL == 2) {
-            const uint4 bl = buf[((ks * MTL + mt) * HL + 1) * 64 + lane];
-#pragma unroll
-            for (int st = 0; st < kStrips; ++st) acc[st][mt] = mfma16x16x32(wr[ks][st], bl, acc[st][mt]);
-          }
+          const uint4* bp = lds + ((ks * MTL + mt) * HL) * 64 + lane;
+          acc[mt] = mfma16x16x32(wb[x], bp[0], acc[mt]);
+          if constexpr (HL == 2) acc[mt] = mfma16x16x32(wb[x], bp[64], acc[mt]);
         }
       }
     }
   };
 
-  uint4 wr0[kKS][kStrips], wr1[kKS][kStrips];
-  if (c_begin < c_end) {
-    load_w(wr0, c_begin);
-    load_a(c_begin);
-    store_a(lds);
-    __syncthreads();
-    for (int c = c_begin; c < c_end; c += 2) {
-      const bool has1 = c + 1 < c_end;
-      if (has1) { load_w(wr1, c + 1); load_a(c + 1); }
-      compute(wr0, lds, c);
-      if (has1) store_a(lds + BUF);
-      __syncthreads();
-      if (!has1) break;
-      const bool has2 = c + 2 < c_end;
-      if (has2) { load_w(wr0, c + 2); load_a(c + 2); }
-      compute(wr1, lds + BUF, c + 1);
-      if (has2) store_a(lds);
-      __syncthreads();
-    }
-  }
-
-  const int nbase = ntile * kGemmTileN + wave * 32 + 4 * (lane >> 4);
-  if constexpr (!TOP2) {
-#pragma unroll
-    for (int st = 0; st < kStrips; ++st) {
-#pragma unroll
-      for (int mt = 0; mt < MTL; ++mt) {
-        const int m = m0 + mt * 16 + (lane & 15);
-        const int n = nbase + st * 16;
-        if (m < g.M) {
-          float* out = g.part + (static_cast<int64_t>(split) * g.M + m) * g.N + n;
-          if (n + 3 < g.N && (g.N & 3) == 0) {
-            *reinterpret_cast<float4*>(out) =
-                make_float4(acc[st][mt][0], acc[st][mt][1], acc[st][mt][2], acc[st][mt][3]);
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (n + r < g.N) out[r] = acc[st][mt][r];
-          }
-        }
-      }
-    }
-  } else {
-    // LM head: per-row top-2 over this workgroup's 128 weight rows.
-    __shared__ float red[4][MT][3];
+  auto flush = [&](int uu) {
+    const int rest = uu / S, tile = rest % ntiles, mtile = rest / ntiles, sp = uu % S;
+    const int nb = tile * 16 * WAVES + wave * 16 + 4 * (lane >> 4);
 #pragma unroll
     for (int mt = 0; mt < MTL; ++mt) {
-      const int m = m0 + mt * 16 + (lane & 15);
-      Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+      const int m = mtile * MT + mt * 16 + (lane & 15);
+      if (m < g.M) {
+        float* out = g.part + (static_cast<int64_t>(sp) * g.M + m) * g.N + nb;
+        if (nb + 3 < g.N && (g.N & 3) == 0) {
+          *reinterpret_cast<float4*>(out) = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+        } else {
 #pragma unroll
-      for (int st = 0; st < kStrips; ++st) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = nbase + st * 16 + r;
-          if (n < g.N) {
-            t = top2_push(t, acc[st][mt][r], n);
-            if (g.logits != nullptr && m < g.M) g.logits[static_cast<int64_t>(m) * g.N + n] = acc[st][mt][r];
-          }
+          for (int r = 0; r < 4; ++r)
+            if (nb + r < g.N) out[r] = acc[mt][r];
         }
       }
-      t = top2_merge(t, top2_shfl_xor(t, 16));
-      t = top2_merge(t, top2_shfl_xor(t, 32));
-      if (lane < 16) {
-        red[wave][mt * 16 + lane][0] = t.v1;
-        red[wave][mt * 16 + lane][1] = __int_as_float(t.i1);
-        red[wave][mt * 16 + lane][2] = t.v2;
-      }
+      acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
-    if (tid < MT && m0 + tid < g.M) {
-      Top2 t{red[0][tid][0], __float_as_int(red[0][tid][1]), red[0][tid][2]};
-#pragma unroll
-      for (int w = 1; w < 4; ++w)
-        t = top2_merge(t, Top2{red[w][tid][0], __float_as_int(red[w][tid][1]), red[w][tid][2]});
-      float* o = g.top2 + (static_cast<int64_t>(ntile) * g.M + m0 + tid) * 3;
-      o[0] = t.v1;
-      o[1] = __int_as_float(t.i1);
-      o[2] = t.v2;
+  };
+
+  // ---- (unit, group) cursor: current cu/cg in buffer 0 or 1, next prefetched into the other
+  int key = key_of(u);
+  const uint16_t* wp = wptr_of(u);
+  int nks = nks_of(u), ngrp = (nks + U - 1) / U, grp = 0;
+  load_w(wb0, wp, nks, 0);                     // first weight group flies during staging
+  stage(u);
+  __syncthreads();
+
+  // Advance to the next (unit, group); returns false when the list is done.  If
+  // the next unit needs another activation slice the prefetch is skipped and
+  // `restage` is set.
+  auto next = [&](int& nu, int& ng, const uint16_t*& nwp, int& nnks, int& nngrp) {
+    nu = u; ng = grp + 1; nwp = wp; nnks = nks; nngrp = ngrp;
+    if (ng >= ngrp) {
+      nu = u + P;
+      ng = 0;
+      if (nu < units) { nwp = wptr_of(nu); nnks = nks_of(nu); nngrp = (nnks + U - 1) / U; }
     }
+    return nu < units;
+  };
+
+  for (;;) {
+    // ---- step with wb0 current
+    int nu, ng, nnks, nngrp;
+    const uint16_t* nwp;
+    bool more = next(nu, ng, nwp, nnks, nngrp);
+    bool same = more && key_of(nu) == key;
+    if (same) load_w(wb1, nwp, nnks, ng);
+    compute(wb0, nks, grp);
+    if (grp == ngrp - 1) flush(u);
+    if (!more) break;
+    if (!same) {
+      __syncthreads();
+      key = key_of(nu);
+      load_w(wb1, nwp, nnks, ng);
+      stage(nu);
+      __syncthreads();
+    }
+    u = nu; grp = ng; wp = nwp; nks = nnks; ngrp = nngrp;
+    // ---- step with wb1 current
+    more = next(nu, ng, nwp, nnks, nngrp);
+    same = more && key_of(nu) == key;
+    if (same) load_w(wb0, nwp, nnks, ng);
+    compute(wb1, nks, grp);
+    if (grp == ngrp - 1) flush(u);
+    if (!more) break;
+    if (!same) {
+      __syncthreads();
+      key = key_of(nu);
+      load_w(wb0, nwp, nnks, ng);
+      stage(nu);
+      __syncthreads();
+    }
+    u = nu; grp = ng; wp = nwp; nks = nnks; ngrp = nngrp;
   }
 }
 
@@ -300,48 +268,100 @@ int env_int(const char* name, int dflt) {
   return v > 0 ? v : dflt;
 }
 
-template <int MT, int AK, bool TOP2>
-hipError_t launch3(const GemmArgs& a, const GemmPlan& p, hipStream_t st) {
-  dim3 grid(p.ntiles, p.S, p.mtiles);
-  hipLaunchKernelGGL((gemm_mfma_kernel<MT, AK, TOP2>), grid, dim3(kThreads), 0, st, a);
+template <int MT, int AK, int WAVES, int KR>
+hipError_t launch_v(const GemmArgs& a, const GemmPlan& p, hipStream_t st) {
+  constexpr int HL = (AK == A_F32_SPLIT) ? 2 : 1;
+  const size_t lds = static_cast<size_t>(KR / 32) * (MT / 16) * HL * 64 * sizeof(uint4);
+  auto kern = gemm_stream_kernel<MT, AK, WAVES, KR>;
+  static bool attr_set = false;   // one-time opt-in to large dynamic LDS for this instantiation
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * WAVES), lds, st, a);
   return hipGetLastError();
 }
 
+// LDS holds KR k values of MT activation rows (hi + lo for fp32 activations):
+// 64 KB per workgroup for the 8-wave variants, 128 KB for the 16-wave one.
 template <int MT>
-hipError_t launch2(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, bool top2, hipStream_t st) {
-  if (ak == A_BF16) return top2 ? launch3<MT, A_BF16, true>(a, p, st) : launch3<MT, A_BF16, false>(a, p, st);
-  return top2 ? launch3<MT, A_F32_SPLIT, true>(a, p, st) : launch3<MT, A_F32_SPLIT, false>(a, p, st);
+hipError_t launch_mt(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, hipStream_t st) {
+  if (p.waves == 16) {
+    if (ak == A_BF16) return launch_v<MT, A_BF16, 16, 65536 / MT>(a, p, st);
+    return launch_v<MT, A_F32_SPLIT, 16, 32768 / MT>(a, p, st);
+  }
+  if (ak == A_BF16) return launch_v<MT, A_BF16, 8, 32768 / MT>(a, p, st);
+  return launch_v<MT, A_F32_SPLIT, 8, 16384 / MT>(a, p, st);
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 }  // namespace
 
-GemmPlan plan_gemm_mfma(int M, int N, int K, bool force_single_split) {
+// Tile = 16 rows per wave x WAVES.  The split-K count S is chosen by a small
+// cost model: the persistent grid (workgroups resident at once: 2 per CU with a
+// 64 KB activation slice, 1 with 128 KB, rounded down to a multiple of S) works
+// through S * tiles units, so the time is ~ rounds * (k steps per unit + a fixed
+// per-unit overhead); the K range of a unit must fit the LDS slice.  Ties go to
+// the smaller S (fewer partial sums).
+GemmPlan plan_gemm_mfma(int M, int N, int K, GemmAKind ak, bool wide) {
   GemmPlan p;
   p.MT = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
   p.mtiles = (M + p.MT - 1) / p.MT;
-  p.ntiles = (N + kGemmTileN - 1) / kGemmTileN;
-  p.nchunks = (K + kGemmKC - 1) / kGemmKC;
-  int want = 1;
-  if (!force_single_split) {
-    const int target = env_int("DFLASH_GEMM_WG_TARGET", 512);
-    const int tiles = p.ntiles * p.mtiles;
-    want = (target + tiles - 1) / tiles;
-    want = want < 1 ? 1 : (want > p.nchunks ? p.nchunks : want);
+  p.waves = wide ? 16 : 8;
+  const int hl = ak == A_F32_SPLIT ? 2 : 1;
+  const int kr_max = (wide ? 65536 : 32768) / p.MT / hl;          // k values the LDS slice holds
+  p.ntiles = (N + 16 * p.waves - 1) / (16 * p.waves);
+  const int ksteps = K / 32;
+  const int tiles = p.ntiles * p.mtiles;
+  const int cap = device_cus() * (wide ? 1 : 2);
+  const int overhead = env_int("DFLASH_GEMM_UNIT_OVERHEAD", 4);  // in k steps
+  const int min_cps = 1;
+  const int max_cps = kr_max / 32;
+  long best_cost = -1;
+  for (int cps = max_cps < ksteps ? max_cps : ksteps; cps >= min_cps; --cps) {
+    const int S = (ksteps + cps - 1) / cps;
+    if ((ksteps + S - 1) / S != cps) continue;                     // each S once, with its smallest cps
+    int grid = cap / S * S;
+    if (grid < S) grid = S;
+    const long units = static_cast<long>(S) * tiles;
+    const long used = units < grid ? units : grid;
+    const long rounds = (units + used - 1) / used;
+    const long cost = rounds * (cps + overhead);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      p.cps = cps;
+      p.S = S;
+      p.grid = static_cast<int>(used);
+    }
   }
-  p.cps = (p.nchunks + want - 1) / want;
-  p.S = (p.nchunks + p.cps - 1) / p.cps;
+  p.nchunks = ksteps;
   p.part_floats = static_cast<size_t>(p.S) * M * N;
   return p;
 }
 
-hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p, bool top2,
-                            hipStream_t st) {
+hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p, hipStream_t st) {
   GemmArgs a = a0;
   a.chunks_per_split = p.cps;
+  a.S = p.S;
+  a.ntiles = p.ntiles;
+  a.mtiles = p.mtiles;
   switch (p.MT) {
-    case 16: return launch2<16>(a, ak, p, top2, st);
-    case 32: return launch2<32>(a, ak, p, top2, st);
-    default: return launch2<64>(a, ak, p, top2, st);
+    case 16: return launch_mt<16>(a, ak, p, st);
+    case 32: return launch_mt<32>(a, ak, p, st);
+    default: return launch_mt<64>(a, ak, p, st);
   }
 }
 

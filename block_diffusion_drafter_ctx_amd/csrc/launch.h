@@ -14,7 +14,7 @@ constexpr int kMaxSeq = 64;
 
 // ------------------------------------------------------------------- GEMMs
 // C[m][n] = sum_k A[m][k] * W[n][k] over a K range, written as split-K partials
-// part[s][m][n] (fp32), or reduced in-kernel to per-tile top-2 for the LM head.
+// part[s][m][n] (fp32).
 //   A row m, column k: src[k / a_cols] + (m / a_rg) * a_gs + (m % a_rg) * a_ld + k % a_cols
 //   W row n: w + ((n / w_rg) * w_gs + w_off + n % w_rg) * w_ld
 struct GemmArgs {
@@ -26,25 +26,27 @@ struct GemmArgs {
   int64_t w_ld, w_gs, w_off;
   int32_t w_rg;
   int32_t M, N, K;
-  int32_t chunks_per_split;   // in 128-element K chunks (MFMA path)
+  int32_t chunks_per_split;   // 32-wide k steps per split (MFMA path)
+  int32_t S, ntiles, mtiles;  // work decomposition (MFMA path; set by the launcher)
   float* part;                // [S][M][N]
-  float* top2;                // [ntiles][M][3] (LM head)
-  float* logits;              // nullable [M][N] (LM head)
 };
 
 enum GemmAKind { A_BF16 = 0, A_F32_SPLIT = 1 };  // exact bf16 A, or fp32 A split hi/lo
 
 struct GemmPlan {
-  int MT = 16, mtiles = 1, ntiles = 1, nchunks = 1, cps = 1, S = 1;
+  int MT = 16, mtiles = 1, ntiles = 1, nchunks = 1, cps = 1, S = 1, waves = 8, grid = 1;
   size_t part_floats = 0;
 };
 
-constexpr int kGemmTileN = 128;   // weight rows per workgroup (MFMA path)
-constexpr int kGemmKC = 128;      // K elements per pipeline chunk
+// wide = 16-wave workgroups with a 128 KB activation slice (fewer K splits for
+// very tall weights such as the LM head); otherwise 8 waves and 64 KB.
+GemmPlan plan_gemm_mfma(int M, int N, int K, GemmAKind ak, bool wide);
+hipError_t launch_gemm_mfma(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, hipStream_t st);
 
-GemmPlan plan_gemm_mfma(int M, int N, int K, bool force_single_split);
-hipError_t launch_gemm_mfma(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, bool top2_epilogue,
-                            hipStream_t st);
+// Sum the split-K partials of logits [S][M][N] per 512-column tile, optionally
+// store the logits, and write each (tile, row) top-2 to top2 [ntiles][M][3].
+hipError_t launch_reduce_top2(const float* part, int S, int M, int N, float* logits, float* top2,
+                              int* ntiles_out, hipStream_t st);
 
 // fp32 storage path: plain FMA GEMM, single split; writes part[0][m][n].
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);

@@ -133,3 +133,47 @@ def test_config2_full_bf16_cache():
     cfg = shrink(CONFIGS[2], cid=203, cache_dtype="bf16")
     log("config 2 full size, bf16 H_t / KV cache, distinct block rows")
     Workload(cfg, 16, 1, override=True).run()
+
+
+def test_bf16_storage_rounding_is_rne():
+    """Cache K values that are exact fp32 sums on and around bf16 ties must be
+    stored with round-to-nearest-even, bit for bit (checked against the oracle's
+    rounding)."""
+    import ctypes
+    from oracle import dflash_oracle as O
+    D, d, Hq, Hkv, L = 64, 64, 1, 1, 1
+    dims = B.Dims(D=D, L=L, Hq=Hq, Hkv=Hkv, head_dim=d, F=64, V=8, n_tgt_layers=5, mask_id=7,
+                  rms_eps=1e-6, dtype=B.BF16, cache_dtype=B.BF16)
+    base = [1.0, 2.0 ** -9, 2.0 ** -8, 3 * 2.0 ** -8, 2.0 ** -7, 3 * 2.0 ** -9, -1.0, -(2.0 ** -8)]
+    H = np.zeros((4, D), dtype=np.float32)
+    for t in range(4):
+        H[t, :8] = np.array(base, dtype=np.float32) * (2.0 ** t)
+    # key column c = H[c % 8 pair]: sums of two bf16 entries, exact in fp32
+    pairs = [(0, 1), (0, 2), (0, 3), (0, 4), (0, 5), (6, 7), (6, 2), (1, 2)]
+    w = np.zeros(((Hq + 2 * Hkv) * d, D), dtype=np.float32)
+    for c in range(d):
+        a, b = pairs[c % 8]
+        w[Hq * d + c, a] = 1.0
+        w[Hq * d + c, b] = 1.0
+        w[(Hq + Hkv) * d + c, a] = 1.0
+        w[(Hq + Hkv) * d + c, b] = -1.0
+    Ht = torch.from_numpy(H).cuda().to(torch.bfloat16)
+    wq = torch.from_numpy(w).cuda().to(torch.bfloat16)
+    kc = torch.zeros(L, 1, Hkv, 8, d, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(L, 1, Hkv, d, 8, dtype=torch.bfloat16, device="cuda")
+    lens = (ctypes.c_int32 * 1)(0)
+    cache = B.KVCache(k=kc.data_ptr(), v=vc.data_ptr(), B=1, cap=8, len=ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
+    wts = B.Weights(w_qkv=wq.data_ptr())
+    nbytes = B.workspace_size(dims, 1, 2, 4)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    B.inject_kv(dims, wts, Ht.data_ptr(), [4], cache, ws.data_ptr(), nbytes, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert lens[0] == 4
+    exact_k = H.astype(np.float64) @ w[Hq * d:(Hq + Hkv) * d].astype(np.float64).T     # [4, d]
+    exact_v = H.astype(np.float64) @ w[(Hq + Hkv) * d:].astype(np.float64).T
+    got_k = kc[0, 0, 0, :4].float().cpu().numpy()
+    got_v = vc[0, 0, 0, :, :4].float().cpu().numpy().T
+    assert np.array_equal(got_k, O.to_bf16(exact_k)), (got_k[0, :8], O.to_bf16(exact_k)[0, :8])
+    assert np.array_equal(got_v, O.to_bf16(exact_v))
+    # the test really exercises ties: some exact values are not bf16 numbers
+    assert not np.array_equal(exact_k, O.to_bf16(exact_k))
