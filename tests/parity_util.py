@@ -223,6 +223,16 @@ class Workload:
             f"({excl} near-tie rows excluded), tau {tau_o.tolist()}")
         return nxt_o, h_final, draft
 
+    def run_gammas(self, gammas):
+        """Ingest the context once, then one drafting pass per block length on it
+        (no appends: every pass sees the same cache)."""
+        self.ingest(self.inp.ctx_states(), list(self.cfg.ctx), "context")
+        anchors = self.inp.anchors()
+        for g in gammas:
+            self.gamma = g
+            self.draft_iteration(0, anchors)
+        return self.report
+
     def run(self, iters=None):
         cfg = self.cfg
         self.ingest(self.inp.ctx_states(), list(cfg.ctx), "context")

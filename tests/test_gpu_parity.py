@@ -177,3 +177,25 @@ def test_bf16_storage_rounding_is_rne():
     assert np.array_equal(got_v, O.to_bf16(exact_v))
     # the test really exercises ties: some exact values are not bf16 numbers
     assert not np.array_equal(exact_k, O.to_bf16(exact_k))
+
+
+@pytest.mark.timeout(1200)
+def test_config3_full():
+    cfg = CONFIGS[3]
+    log("config 3 full size: 32768-row context, 1 iteration + append")
+    Workload(cfg, 16, 1).run()
+
+
+@pytest.mark.timeout(1200)
+def test_config4_full():
+    cfg = CONFIGS[4]
+    log(f"config 4 full size: 16 ragged sequences {list(cfg.ctx)}, 1 iteration + append")
+    Workload(cfg, 16, 1).run()
+
+
+@pytest.mark.timeout(1200)
+def test_config5_full_gamma_sweep():
+    cfg = CONFIGS[5]
+    log("config 5 full size: 8 layers, 4 x 8192 context, gamma 8 / 16 / 32 on one cache")
+    w = Workload(cfg, max(cfg.gammas), 1)
+    w.run_gammas(list(cfg.gammas))
