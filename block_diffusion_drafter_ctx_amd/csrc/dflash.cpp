@@ -49,7 +49,7 @@ dflash_status ok() {
   } while (0)
 
 constexpr size_t kAlign = 256;
-constexpr int kRowBlock = 512;    // rows per fuse / inject GEMM pass
+constexpr int kRowBlock = 4096;   // rows per fuse / inject GEMM pass
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -152,7 +152,7 @@ struct Carve {
 size_t gemm_part_floats(const dflash_dims* d, int M, int N, int K, GemmAKind ak, bool wide = false) {
   if (M <= 0) return 0;
   if (d->dtype == DFLASH_F32) return static_cast<size_t>(M) * N;
-  return plan_gemm_mfma(M, N, K, ak, wide).part_floats;
+  return plan_gemm(M, N, K, ak, wide).part_floats;
 }
 
 GemmAKind ctx_a_kind(const dflash_dims* d) { return d->cache_dtype == DFLASH_BF16 ? A_BF16 : A_F32_SPLIT; }
@@ -250,11 +250,18 @@ dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t 
   DF_REQUIRE(B >= 1 && B <= DFLASH_MAX_BATCH, DFLASH_ERR_INVALID_ARG, "B=%d outside [1, %d]", B, DFLASH_MAX_BATCH);
   DF_REQUIRE(max_rows >= 0, DFLASH_ERR_INVALID_ARG, "max_rows=%d < 0", max_rows);
   DF_REQUIRE(bytes != nullptr, DFLASH_ERR_INVALID_ARG, "bytes is NULL");
-  size_t need = draft_ws(dims, B, gamma).total;
-  const size_t f = fuse_ws(dims, max_rows), i = inject_ws(dims, max_rows), a = argmax_ws(dims, B, gamma).total;
+  // The kernels chosen (and so the scratch they need) depend on the row counts,
+  // not monotonically: take the maximum over every batch <= B and block <= gamma.
+  size_t need = 0;
+  for (int b = 1; b <= B; ++b)
+    for (int g = DFLASH_MIN_GAMMA; g <= gamma; ++g) {
+      const size_t dw = draft_ws(dims, b, g).total, aw = argmax_ws(dims, b, g).total;
+      if (dw > need) need = dw;
+      if (aw > need) need = aw;
+    }
+  const size_t f = fuse_ws(dims, max_rows), i = inject_ws(dims, max_rows);
   if (f > need) need = f;
   if (i > need) need = i;
-  if (a > need) need = a;
   *bytes = need;
   return ok();
 }
@@ -304,7 +311,7 @@ dflash_status dflash_fuse_context(const dflash_dims* dims, const dflash_weights*
     g.part = part;
     int S = 1;
     if (bf) {
-      const GemmPlan p = plan_gemm_mfma(M, D, K, A_BF16, false);
+      const GemmPlan p = plan_gemm(M, D, K, A_BF16, false);
       S = p.S;
       DF_HIP(launch_gemm_mfma(g, A_BF16, p, s));
     } else {
@@ -369,7 +376,7 @@ dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w,
     int S = 1;
     if (bf) {
       // an fp32 H_t is split hi + lo against the bf16 weights like any fp32 activation
-      const GemmPlan p = plan_gemm_mfma(M, N, D, ctx_a_kind(dims), false);
+      const GemmPlan p = plan_gemm(M, N, D, ctx_a_kind(dims), false);
       S = p.S;
       DF_HIP(launch_gemm_mfma(g, ctx_a_kind(dims), p, s));
     } else {
@@ -465,7 +472,7 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
       *S = 1;
       return launch_gemm_f32(g, s);
     }
-    const GemmPlan p = plan_gemm_mfma(M, N, K, A_F32_SPLIT, false);
+    const GemmPlan p = plan_gemm(M, N, K, A_F32_SPLIT, false);
     *S = p.S;
     return launch_gemm_mfma(g, A_F32_SPLIT, p, s);
   };
@@ -579,7 +586,7 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
     const ArgmaxWs lay = argmax_ws(dims, B, gamma);
     char* base = static_cast<char*>(ws);
     if (dims->dtype == DFLASH_BF16) {
-      const GemmPlan p = plan_gemm_mfma(Mr, dims->V, D, A_F32_SPLIT, true);
+      const GemmPlan p = plan_gemm(Mr, dims->V, D, A_F32_SPLIT, true);
       g.part = reinterpret_cast<float*>(base + lay.part);
       float* top2 = reinterpret_cast<float*>(base + lay.top2);
       DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, s));

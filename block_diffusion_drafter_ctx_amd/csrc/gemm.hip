@@ -210,6 +210,152 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------------------------ tiled path
+// Many activation rows (context ingest, big batches): a classic LDS-tiled MFMA
+// GEMM.  Workgroup tile 128 weight rows x 128 activation rows x 64 k; 4 waves
+// in a 2 x 2 layout, each computing 64 x 64 with 16 MFMA accumulators.  Both
+// operand tiles are staged in LDS in MFMA fragment order (conflict-free 16 B
+// reads), double-buffered, with the next tile's global loads in flight while
+// the current one is multiplied.  grid = (N / 128, M / 128, splits).
+constexpr int kTileN = 128, kTileM = 128, kTileK = 64;
+
+template <int AK>
+__global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
+  constexpr int HL = (AK == A_F32_SPLIT) ? 2 : 1;
+  constexpr int WFR = (kTileN / 16) * (kTileK / 32);        // W fragments per tile (16)
+  constexpr int AFR = (kTileM / 16) * (kTileK / 32) * HL;   // A fragments per tile
+  constexpr int BUF = (WFR + AFR) * 64;                     // uint4 per buffer
+  extern __shared__ uint4 lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int n0 = blockIdx.x * kTileN, m0 = blockIdx.y * kTileM;
+  const int split = blockIdx.z;
+  const int ktiles = g.K / kTileK;
+  const int kt_begin = split * g.chunks_per_split;
+  const int kt_end = min(ktiles, kt_begin + g.chunks_per_split);
+
+  // Per-thread global chunks: c = tid + 256*i -> row c / 8 (= tid/8 + 32 i), k8
+  // group q = tid % 8 (the same for all four chunks of a thread).
+  const int q = tid & 7, r0 = tid >> 3;
+  const uint16_t* wbase[4];
+  int64_t abase[4];
+  uint32_t akeep = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + 32 * i;
+    const int n = min(n0 + r, g.N - 1);
+    wbase[i] = static_cast<const uint16_t*>(g.w) +
+               (static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg) * g.w_ld + 8 * q;
+    const int m = m0 + r;
+    if (m < g.M) akeep |= 1u << i;
+    abase[i] = a_row_off(g, min(m, g.M - 1)) + 8 * q;   // rows past M load row M-1 and are zeroed
+  }
+  const int slot0 = (q >> 2) * 64 + (q & 3) * 16 + (r0 & 15);   // + (row/16)*2*64 (+ hl)
+
+  uint4 wreg0, wreg1, wreg2, wreg3;
+  uint4 areg_b[AK == A_BF16 ? 4 : 1];
+  float areg_f[AK == A_F32_SPLIT ? 32 : 1];
+  auto gload = [&](int kt) __attribute__((always_inline)) {
+    const int kb = kt * kTileK;
+    const int s = kb / g.a_cols, col = kb - s * g.a_cols;     // a 64-wide k tile never straddles sources
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 wv = *reinterpret_cast<const uint4*>(wbase[i] + kb);
+      if (i == 0) wreg0 = wv; else if (i == 1) wreg1 = wv; else if (i == 2) wreg2 = wv; else wreg3 = wv;
+      const bool ok = (akeep >> i) & 1u;
+      if constexpr (AK == A_BF16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(pick_src<uint16_t>(g, s) + abase[i] + col);
+        const uint32_t keep = ok ? 0xffffffffu : 0u;
+        areg_b[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+      } else {
+        const float* p = pick_src<float>(g, s) + abase[i] + col;
+        const float4 v0 = *reinterpret_cast<const float4*>(p), v1 = *reinterpret_cast<const float4*>(p + 4);
+        const float keep = ok ? 1.0f : 0.0f;
+        areg_f[8 * i + 0] = v0.x * keep; areg_f[8 * i + 1] = v0.y * keep;
+        areg_f[8 * i + 2] = v0.z * keep; areg_f[8 * i + 3] = v0.w * keep;
+        areg_f[8 * i + 4] = v1.x * keep; areg_f[8 * i + 5] = v1.y * keep;
+        areg_f[8 * i + 6] = v1.z * keep; areg_f[8 * i + 7] = v1.w * keep;
+      }
+    }
+  };
+  auto lstore = [&](uint4* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int frag_row = ((r0 + 32 * i) >> 4) * 2;          // (row / 16) * (k steps per tile)
+      buf[frag_row * 64 + slot0] = i == 0 ? wreg0 : (i == 1 ? wreg1 : (i == 2 ? wreg2 : wreg3));
+      if constexpr (AK == A_BF16) {
+        buf[WFR * 64 + frag_row * 64 + slot0] = areg_b[i];
+      } else {
+        uint4 hi, lo;
+        split8(&areg_f[8 * i], hi, lo);
+        const int sl = WFR * 64 + (frag_row * HL) * 64 + ((q >> 2) * HL) * 64 + (q & 3) * 16 + (r0 & 15);
+        buf[sl] = hi;
+        buf[sl + 64] = lo;
+      }
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint4* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 wf[4], af[4], al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wf[i] = buf[((wn * 4 + i) * 2 + ks) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        af[j] = buf[WFR * 64 + (((wm * 4 + j) * 2 + ks) * HL) * 64 + lane];
+        if constexpr (HL == 2) al[j] = buf[WFR * 64 + (((wm * 4 + j) * 2 + ks) * HL + 1) * 64 + lane];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = mfma16x16x32(wf[i], af[j], acc[i][j]);
+          if constexpr (HL == 2) acc[i][j] = mfma16x16x32(wf[i], al[j], acc[i][j]);
+        }
+    }
+  };
+
+  if (kt_begin < kt_end) {
+    gload(kt_begin);
+    lstore(lds);
+    __syncthreads();
+    int cur = 0;
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      const bool more = kt + 1 < kt_end;
+      if (more) gload(kt + 1);
+      compute(lds + cur * BUF);
+      if (more) lstore(lds + (cur ^ 1) * BUF);
+      __syncthreads();
+      cur ^= 1;
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + wn * 64 + i * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 64 + j * 16 + (lane & 15);
+      if (m >= g.M) continue;
+      float* out = g.part + (static_cast<int64_t>(split) * g.M + m) * g.N + n;
+      if (n + 3 < g.N && (g.N & 3) == 0) {
+        *reinterpret_cast<float4*>(out) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < g.N) out[r] = acc[i][j][r];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32 path
 constexpr int kF32Tile = 64;
 constexpr int kF32K = 16;
@@ -352,7 +498,52 @@ GemmPlan plan_gemm_mfma(int M, int N, int K, GemmAKind ak, bool wide) {
   return p;
 }
 
+GemmPlan plan_gemm_tiled(int M, int N, int K) {
+  GemmPlan p;
+  p.tiled = true;
+  p.MT = kTileM;
+  p.mtiles = (M + kTileM - 1) / kTileM;
+  p.ntiles = (N + kTileN - 1) / kTileN;
+  const int ktiles = K / kTileK;
+  const int tiles = p.mtiles * p.ntiles;
+  const int target = 2 * device_cus();
+  int want = (target + tiles - 1) / tiles;
+  if (want < 1) want = 1;
+  if (want > ktiles / 4) want = ktiles / 4 > 0 ? ktiles / 4 : 1;   // keep >= 4 k tiles per split
+  p.cps = (ktiles + want - 1) / want;
+  p.S = (ktiles + p.cps - 1) / p.cps;
+  p.part_floats = static_cast<size_t>(p.S) * M * N;
+  return p;
+}
+
 hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p, hipStream_t st) {
+  if (p.tiled) {
+    GemmArgs a = a0;
+    a.chunks_per_split = p.cps;
+    const int hl = ak == A_F32_SPLIT ? 2 : 1;
+    const size_t lds = static_cast<size_t>(2) * ((kTileN / 16) * 2 + (kTileM / 16) * 2 * hl) * 64 * sizeof(uint4);
+    const dim3 grid(p.ntiles, p.mtiles, p.S);
+    if (ak == A_BF16) {
+      static bool set_b = false;
+      if (!set_b) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_kernel<A_BF16>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+        set_b = true;
+      }
+      hipLaunchKernelGGL(gemm_tile_kernel<A_BF16>, grid, dim3(256), lds, st, a);
+    } else {
+      static bool set_f = false;
+      if (!set_f) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_kernel<A_F32_SPLIT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+        set_f = true;
+      }
+      hipLaunchKernelGGL(gemm_tile_kernel<A_F32_SPLIT>, grid, dim3(256), lds, st, a);
+    }
+    return hipGetLastError();
+  }
   GemmArgs a = a0;
   a.chunks_per_split = p.cps;
   a.S = p.S;
@@ -363,6 +554,11 @@ hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p,
     case 32: return launch_mt<32>(a, ak, p, st);
     default: return launch_mt<64>(a, ak, p, st);
   }
+}
+
+GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
+  if (M > 64 && K % kTileK == 0 && env_int("DFLASH_GEMM_NO_TILED", 0) == 0) return plan_gemm_tiled(M, N, K);
+  return plan_gemm_mfma(M, N, K, ak, wide);
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st) {

@@ -35,12 +35,18 @@ enum GemmAKind { A_BF16 = 0, A_F32_SPLIT = 1 };  // exact bf16 A, or fp32 A spli
 
 struct GemmPlan {
   int MT = 16, mtiles = 1, ntiles = 1, nchunks = 1, cps = 1, S = 1, waves = 8, grid = 1;
+  bool tiled = false;   // LDS-tiled kernel for many activation rows
   size_t part_floats = 0;
 };
 
 // wide = 16-wave workgroups with a 128 KB activation slice (fewer K splits for
 // very tall weights such as the LM head); otherwise 8 waves and 64 KB.
 GemmPlan plan_gemm_mfma(int M, int N, int K, GemmAKind ak, bool wide);
+// Many activation rows: 128 x 128 x 64 LDS-tiled MFMA kernel (K % 64 == 0).
+GemmPlan plan_gemm_tiled(int M, int N, int K);
+// The plan the library uses for an M x N x K product (tiled for M > 64 when
+// K % 64 == 0, streaming otherwise).
+GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide);
 hipError_t launch_gemm_mfma(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, hipStream_t st);
 
 // Sum the split-K partials of logits [S][M][N] per 512-column tile, optionally

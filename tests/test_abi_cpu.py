@@ -141,3 +141,14 @@ def test_empty_calls_are_noops(lib):
     c = _cache(lens=(3, 4))
     B.inject_kv(_dims(), B.Weights(), 0, [0, 0], c, 0, 0)
     assert list(c._keep) == [3, 4]
+
+
+def test_workspace_covers_smaller_calls(lib):
+    # the returned size bounds every call with fewer sequences / a shorter block
+    d = _dims(D=1024, F=2048, Hq=8, Hkv=2, head_dim=128, V=5000, L=2)
+    big = B.workspace_size(d, 4, 33, 3000)
+    for b in (1, 2, 4):
+        for g in (2, 8, 16, 17, 32, 33):
+            assert B.workspace_size(d, b, g, 3000) <= big
+    for rows in (1, 16, 100, 3000):
+        assert B.workspace_size(d, 4, 33, rows) <= big
