@@ -40,7 +40,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--fwd-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-iters", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="run the CPU oracle for about this long (whole iterations)")
     ap.add_argument("--cache", choices=["f32", "bf16"], default="f32",
                     help="storage type of H_t and the KV cache")
     args = ap.parse_args()
@@ -116,20 +117,26 @@ def main():
     nxt = tokens[:, 0] if Bn == 1 else torch.empty(Bn, dtype=torch.int32, device=dev)
     tmp = torch.empty(Bn, n, dtype=torch.int32, device=dev)
     V = cfg.V
-    lm_ev = []
 
-    def step(i, time_lm=False):
+    def make_events(n):
+        """n (start, stop) event pairs, each created on the device up front (the
+        library records them on its stream through the profiling hook)."""
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in pairs:
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return pairs
+
+    def hook(role, pairs):
+        return B.profile_events(role, [a.cuda_event for a, _ in pairs], [b.cuda_event for _, b in pairs])
+
+    def step(i):
         it = i % CYCLE
         if it == 0:
             cache.set_lens(base_lens)
         dr.draft(cache, tokens, None, gamma, h_final)
-        if time_lm:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
         dr.argmax_accept(B.ARGMAX, h_final, Bn, gamma, draft)
-        if time_lm:
-            b.record(stream)
-            lm_ev.append((a, b))
         d = app[it]
         target = d["target"]
         torch.add(draft, d["shift"], out=tmp)
@@ -142,21 +149,52 @@ def main():
 
     for i in range(args.warmup):
         step(i)
+    lm_ev = make_events(args.steps)
     torch.cuda.synchronize()
-    lm_ev.clear()
     t_start = time.perf_counter()
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s0.record(stream)
+    hook(B.PROF_LM_HEAD, lm_ev)          # the LM-head kernel of every timed step
     for i in range(args.steps):
-        step(args.warmup + i, time_lm=True)
+        step(args.warmup + i)
     s1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    n_lm = hook(B.PROF_NONE, [])
+    assert n_lm == args.steps, (n_lm, args.steps)
     gpu_ms = s0.elapsed_time(s1)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
     blocks_per_s = Bn * args.steps / (ms_per_step * args.steps / 1e3)
     lm_us = float(np.mean([a.elapsed_time(b) for a, b in lm_ev])) * 1e3
     taus = tau.cpu().numpy()
+
+    # ---- every other kernel role over one cycle of steps (outside the timed region)
+    es0, cs0 = (2 if cfg.dtype == "bf16" else 4), (2 if cfg.cache_dtype == "bf16" else 4)
+    M = Bn * gamma
+    T_app = Bn * cfg.append_rows
+    nqkv = (cfg.Hq + 2 * cfg.Hkv) * cfg.d
+    mean_keys = sum(cfg.ctx) / Bn + cfg.append_rows * (CYCLE - 1) / 2 + gamma
+    roles = {
+        "qkv": (B.PROF_QKV, cfg.L, RF.gemm_bytes(nqkv, cfg.D, M, es0)),
+        "o_proj": (B.PROF_O, cfg.L, RF.gemm_bytes(cfg.D, cfg.Hq * cfg.d, M, es0)),
+        "gate_up": (B.PROF_GATEUP, cfg.L, RF.gemm_bytes(2 * cfg.F, cfg.D, M, es0)),
+        "down": (B.PROF_DOWN, cfg.L, RF.gemm_bytes(cfg.D, cfg.F, M, es0)),
+        "attention": (B.PROF_ATTENTION, cfg.L,
+                      int(Bn * mean_keys * 2 * cfg.Hkv * cfg.d * cs0 + 2 * M * cfg.Hq * cfg.d * 4)),
+        "fuse_append": (B.PROF_FUSE, 1, RF.fuse_bytes(T_app, cfg.D, cfg.n_tgt, es0, cs0)),
+        "inject_append": (B.PROF_INJECT, 1, RF.inject_bytes(T_app, cfg.D, cfg.L, cfg.Hkv, cfg.d, es0, cs0)),
+    }
+    per_kernel = {}
+    for name, (role, per_step, nbytes) in roles.items():
+        pairs = make_events(per_step * CYCLE)
+        hook(role, pairs)
+        for i in range(CYCLE):
+            step(i)
+        torch.cuda.synchronize()
+        got = hook(B.PROF_NONE, [])
+        us = float(np.mean([a.elapsed_time(b) for a, b in pairs[:got]])) * 1e3
+        per_kernel[name] = {"us": round(us, 2), "bytes": int(nbytes), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4)}
 
     # ---- draft forward us at a fixed cache length (draft forward + LM-head argmax)
     cache.set_lens(base_lens)
@@ -213,23 +251,35 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / RF.HBM_PEAK_GBS, 4),
         "context_us": round(context_us, 1),
         "context_mfma_frac": round(ctx_flops / (context_us * 1e-6) / 1e12 / RF.MFMA_BF16_TFLOPS, 4),
+        "per_kernel": per_kernel,
         "roofline": {
-            "kernel": "gemm_mfma_kernel<16, A_F32_SPLIT, top2> (LM head 151936x4096 + argmax partials) "
-                      "and its top-2 merge, bracketed by HIP events on the library stream",
+            "kernel": "gemm_stream_kernel<16, 1, 16, 2048> (LM-head weight stream, 151936 x 4096 bf16 against "
+                      "the 15 mask rows split hi/lo), one launch per step, HIP events recorded around that "
+                      "launch on the library stream by dflash_profile_events",
             "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": RF.HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(lm_gbs / RF.HBM_PEAK_GBS, 4), "traffic": None,
             "bytes_per_launch": lm_bytes, "us_per_launch": round(lm_us, 2),
         },
     }
 
+    # A plain device copy of a known size: the reference that scales rocprofv3's
+    # FETCH_SIZE / WRITE_SIZE counters into bytes (256 MiB read + 256 MiB written).
+    src = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_iters)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, inp, iters):
-    """The CPU oracle, as it stands, on one (or ``iters``) full drafting iteration(s)
-    of the same workload: draft forward + LM-head argmax + accept + append."""
+def cpu_baseline(cfg, inp, seconds):
+    """The CPU oracle, as it stands, on whole drafting iterations of the same
+    workload (draft forward + LM-head argmax + accept + 16-row append), repeated
+    for about ``seconds`` with the GPU loop's 8-iteration cache reset."""
     import numpy as np
     from oracle import dflash_oracle as O
     from dflash_inputs import build_target_np
@@ -246,35 +296,43 @@ def cpu_baseline(cfg, inp, iters):
     E = f(inp.embed())
     gf = f(inp.g_final())
     wc, gc = inp.w_c(), inp.g_c()
-    cache = O.OracleCache(cfg.L, cfg.B, cfg.Hkv, cfg.d)
-    Ht = O.fuse_context(inp.ctx_states(), wc, gc, cfg.eps, cfg.dtype)
+    Ht = O.fuse_context(inp.ctx_states(), wc, gc, cfg.eps, cfg.cache_dtype)
     off = np.concatenate([[0], np.cumsum(cfg.ctx)])
-    for l in range(cfg.L):
-        for b in range(cfg.B):
-            k, v = O.inject_kv(Ht[off[b]:off[b + 1]], layers[l]["w_qkv"], cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype)
-            cache.append(l, b, k, v)
+    base = [[O.inject_kv(Ht[off[b]:off[b + 1]], layers[l]["w_qkv"], cfg.Hq, cfg.Hkv, cfg.d, cfg.cache_dtype)
+             for b in range(cfg.B)] for l in range(cfg.L)]
+    appends = [inp.append_states(it) for it in range(cfg.iters)]
+    draws = [inp.verify_draws(it, cfg.gamma) for it in range(cfg.iters)]
     gamma = cfg.gamma
     anchors = inp.anchors()
+    done = 0
     t0 = time.perf_counter()
-    for it in range(iters):
+    cache = None
+    while done < 256 and (done == 0 or time.perf_counter() - t0 < seconds):
+        it = done % cfg.iters
+        if it == 0:
+            cache = O.OracleCache(cfg.L, cfg.B, cfg.Hkv, cfg.d)
+            for l in range(cfg.L):
+                for b in range(cfg.B):
+                    cache.append(l, b, *base[l][b])
         tokens = inp.block_tokens(gamma, anchors)
-        hf, _ = O.draft_forward(cfg, layers, gf, cache, gamma, embed=E, tokens=tokens, storage=cfg.dtype)
+        hf, _ = O.draft_forward(cfg, layers, gf, cache, gamma, embed=E, tokens=tokens, storage=cfg.cache_dtype)
         d, _, _ = O.lm_head_argmax(hf, E)
-        m, r, bonus = inp.verify_draws(it, gamma)
+        m, r, bonus = draws[it]
         tgt = build_target_np(d, m, r, bonus, cfg.V)
         _, anchors = O.accept(d, tgt)
-        st = inp.append_states(it)
-        Ha = O.fuse_context(st, wc, gc, cfg.eps, cfg.dtype)
+        Ha = O.fuse_context(appends[it], wc, gc, cfg.eps, cfg.cache_dtype)
         for l in range(cfg.L):
             for b in range(cfg.B):
                 rows = slice(b * cfg.append_rows, (b + 1) * cfg.append_rows)
-                k, v = O.inject_kv(Ha[rows], layers[l]["w_qkv"], cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype)
+                k, v = O.inject_kv(Ha[rows], layers[l]["w_qkv"], cfg.Hq, cfg.Hkv, cfg.d, cfg.cache_dtype)
                 cache.append(l, b, k, v)
+        done += 1
     dt = time.perf_counter() - t0
-    log(f"cpu baseline: {iters} iteration(s) in {dt:.1f}s on {cores} threads")
-    return {"value": round(cfg.B * iters / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{iters} full drafting iteration(s) of the same workload (draft forward + LM-head argmax "
-                      f"+ accept + 16-row append), float64 numpy oracle, after an untimed context ingest",
+    log(f"cpu baseline: {done} iteration(s) in {dt:.1f}s on {cores} threads")
+    return {"value": round(cfg.B * done / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} full drafting iterations of the same workload (draft forward + LM-head argmax "
+                      f"+ accept + 16-row append, cache reset every {cfg.iters}), float64 numpy oracle, "
+                      f"after an untimed context ingest",
             "seconds": round(dt, 2)}
 
 

@@ -19,7 +19,8 @@ ARGMAX, ACCEPT = 1, 2
 MAX_BATCH, MAX_TGT_LAYERS, MIN_GAMMA, MAX_GAMMA = 64, 8, 2, 33
 
 EXPORTED = ("dflash_version", "dflash_last_error", "dflash_workspace_size", "dflash_fuse_context",
-            "dflash_inject_kv", "dflash_draft_forward", "dflash_argmax_accept")
+            "dflash_inject_kv", "dflash_draft_forward", "dflash_argmax_accept", "dflash_profile_events")
+PROF_NONE, PROF_LM_HEAD, PROF_QKV, PROF_O, PROF_GATEUP, PROF_DOWN, PROF_FUSE, PROF_INJECT, PROF_ATTENTION = range(9)
 
 
 class Dims(ctypes.Structure):
@@ -75,6 +76,8 @@ def load():
     lib.dflash_argmax_accept.argtypes = [POINTER(Dims), POINTER(Weights), c_uint32, c_void_p, c_int32, c_int32,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_size_t, c_void_p]
+    lib.dflash_profile_events.restype = c_int32
+    lib.dflash_profile_events.argtypes = [c_int32, POINTER(c_void_p), POINTER(c_void_p), c_int32, POINTER(c_int32)]
     _lib = lib
     return lib
 
@@ -126,3 +129,20 @@ def argmax_accept(dims: Dims, w: Weights, flags: int, h_final, B: int, gamma: in
     _check(load().dflash_argmax_accept(ctypes.byref(dims), ctypes.byref(w) if w is not None else None, flags,
                                        _p(h_final), B, gamma, _p(draft), _p(target), _p(tau), _p(next_anchor),
                                        _p(logits_dbg), _p(top2_gap), _p(ws), ws_bytes, _p(stream)))
+
+
+_prof_keep = None
+
+
+def profile_events(role: int, starts=(), stops=()) -> int:
+    """Record HIP events around the next len(starts) launches of a kernel role
+    (handles as ints, e.g. torch.cuda.Event.cuda_event).  Returns the number of
+    launches recorded under the previous setting."""
+    global _prof_keep
+    n = len(starts)
+    a = (c_void_p * max(1, n))(*[int(x) for x in starts])
+    b = (c_void_p * max(1, n))(*[int(x) for x in stops])
+    rec = c_int32(0)
+    _check(load().dflash_profile_events(role, a, b, n, ctypes.byref(rec)))
+    _prof_keep = (a, b)
+    return rec.value

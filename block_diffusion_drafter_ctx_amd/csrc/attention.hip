@@ -383,10 +383,11 @@ size_t attention_part_bound(int B, int Hkv, int R, int d) {
 }
 
 hipError_t launch_attention(const AttnArgs& a0, const AttnPlan& p, bool bf16_weights, bool bf16_cache,
-                            hipStream_t st) {
+                            hipStream_t st, void* stop_event) {
   AttnArgs a = a0;
   if (!bf16_weights) {
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.B * a.gamma * a.Hq), dim3(64), 0, st, a);
+    if (stop_event != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(stop_event), st);
     return hipGetLastError();
   }
   a.split_keys = p.split_keys;
@@ -405,6 +406,7 @@ hipError_t launch_attention(const AttnArgs& a0, const AttnPlan& p, bool bf16_wei
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (stop_event != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(stop_event), st);
   hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.gamma * a.Hq), dim3(128), 0, st, a);
   return hipGetLastError();
 }

@@ -234,11 +234,50 @@ ArgmaxWs argmax_ws(const dflash_dims* d, int B, int gamma) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// ---------------------------------------------------------- profiling hook
+struct ProfHook {
+  int role = DFLASH_PROF_NONE;
+  void* const* start = nullptr;
+  void* const* stop = nullptr;
+  int n = 0, idx = 0;
+};
+thread_local ProfHook g_prof;
+
+// Record the hook's start event if this launch matches; returns the slot used.
+int prof_begin(int role, hipStream_t s) {
+  if (g_prof.role != role || g_prof.idx >= g_prof.n) return -1;
+  const int i = g_prof.idx++;
+  if (hipEventRecord(static_cast<hipEvent_t>(g_prof.start[i]), s) != hipSuccess) return -1;
+  return i;
+}
+
+void prof_end(int slot, hipStream_t s) {
+  if (slot >= 0) (void)hipEventRecord(static_cast<hipEvent_t>(g_prof.stop[slot]), s);
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* dflash_version(void) { return "dflash-mi355x 0.1.0 (gfx950)"; }
+
+dflash_status dflash_profile_events(int32_t role, void* const* start, void* const* stop, int32_t n,
+                                    int32_t* recorded) {
+  DF_REQUIRE(role >= DFLASH_PROF_NONE && role <= DFLASH_PROF_ATTENTION, DFLASH_ERR_INVALID_ARG,
+             "unknown profiling role %d", role);
+  DF_REQUIRE(n >= 0, DFLASH_ERR_INVALID_ARG, "n=%d < 0", n);
+  DF_REQUIRE(role == DFLASH_PROF_NONE || n == 0 || (start != nullptr && stop != nullptr), DFLASH_ERR_INVALID_ARG,
+             "event arrays are NULL");
+  if (recorded != nullptr) *recorded = g_prof.idx;
+  g_prof = ProfHook{};
+  if (role != DFLASH_PROF_NONE && n > 0) {
+    g_prof.role = role;
+    g_prof.start = start;
+    g_prof.stop = stop;
+    g_prof.n = n;
+  }
+  return ok();
+}
 
 const char* dflash_last_error(void) { return g_err.c_str(); }
 
@@ -313,7 +352,9 @@ dflash_status dflash_fuse_context(const dflash_dims* dims, const dflash_weights*
     if (bf) {
       const GemmPlan p = plan_gemm(M, D, K, A_BF16, false);
       S = p.S;
+      const int ps = prof_begin(DFLASH_PROF_FUSE, s);
       DF_HIP(launch_gemm_mfma(g, A_BF16, p, s));
+      prof_end(ps, s);
     } else {
       DF_HIP(launch_gemm_f32(g, s));
     }
@@ -378,7 +419,9 @@ dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w,
       // an fp32 H_t is split hi + lo against the bf16 weights like any fp32 activation
       const GemmPlan p = plan_gemm(M, N, D, ctx_a_kind(dims), false);
       S = p.S;
+      const int ps = prof_begin(DFLASH_PROF_INJECT, s);
       DF_HIP(launch_gemm_mfma(g, ctx_a_kind(dims), p, s));
+      prof_end(ps, s);
     } else {
       DF_HIP(launch_gemm_f32(g, s));
     }
@@ -452,7 +495,7 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
   auto wp = [&](const void* p, int64_t elems) { return static_cast<const char*>(p) + elems * es; };
 
   // GEMM on fp32 activations (rows = block rows), returns the split count.
-  auto gemm = [&](const float* A, int K, const void* W, int N, int* S) -> hipError_t {
+  auto gemm = [&](const float* A, int K, const void* W, int N, int* S, int role) -> hipError_t {
     GemmArgs g{};
     for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = A;
     g.a_cols = K;
@@ -474,7 +517,10 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
     }
     const GemmPlan p = plan_gemm(M, N, K, A_F32_SPLIT, false);
     *S = p.S;
-    return launch_gemm_mfma(g, A_F32_SPLIT, p, s);
+    const int ps = prof_begin(role, s);
+    const hipError_t e = launch_gemm_mfma(g, A_F32_SPLIT, p, s);
+    prof_end(ps, s);
+    return e;
   };
 
   int32_t nkeys[kMaxSeq];
@@ -486,7 +532,7 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
   DF_HIP(launch_embed_norm(block_tokens, embed_override, w->embed, dims->V, M, D, w->g_attn, dims->rms_eps, h, a, bf, s));
   for (int l = 0; l < L; ++l) {
     int S = 1;
-    DF_HIP(gemm(a, D, wp(w->w_qkv, static_cast<int64_t>(l) * nqkv * D), nqkv, &S));
+    DF_HIP(gemm(a, D, wp(w->w_qkv, static_cast<int64_t>(l) * nqkv * D), nqkv, &S, DFLASH_PROF_QKV));
     ScatterArgs sa{};
     sa.part = part;
     sa.S = S;
@@ -525,13 +571,14 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
     at.R = R;
     at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
     for (int b = 0; b < B; ++b) at.nkeys[b] = nkeys[b];
-    DF_HIP(launch_attention(at, ap, bf, cbf, s));
+    const int pa = prof_begin(DFLASH_PROF_ATTENTION, s);
+    DF_HIP(launch_attention(at, ap, bf, cbf, s, pa >= 0 ? g_prof.stop[pa] : nullptr));
 
-    DF_HIP(gemm(o, hd, wp(w->w_o, static_cast<int64_t>(l) * D * hd), D, &S));
+    DF_HIP(gemm(o, hd, wp(w->w_o, static_cast<int64_t>(l) * D * hd), D, &S, DFLASH_PROF_O));
     DF_HIP(launch_residual_norm(part, S, M, D, h, wp(w->g_ffn, static_cast<int64_t>(l) * D), dims->rms_eps, a, bf, s));
-    DF_HIP(gemm(a, D, wp(w->w_gateup, static_cast<int64_t>(l) * 2 * F * D), 2 * F, &S));
+    DF_HIP(gemm(a, D, wp(w->w_gateup, static_cast<int64_t>(l) * 2 * F * D), 2 * F, &S, DFLASH_PROF_GATEUP));
     DF_HIP(launch_swiglu(part, S, M, F, sw, s));
-    DF_HIP(gemm(sw, F, wp(w->w_down, static_cast<int64_t>(l) * D * F), D, &S));
+    DF_HIP(gemm(sw, F, wp(w->w_down, static_cast<int64_t>(l) * D * F), D, &S, DFLASH_PROF_DOWN));
     const bool last = l + 1 == L;
     DF_HIP(launch_residual_norm(part, S, M, D, h,
                                 last ? w->g_final : wp(w->g_attn, static_cast<int64_t>(l + 1) * D),
@@ -589,7 +636,9 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
       const GemmPlan p = plan_gemm(Mr, dims->V, D, A_F32_SPLIT, true);
       g.part = reinterpret_cast<float*>(base + lay.part);
       float* top2 = reinterpret_cast<float*>(base + lay.top2);
+      const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
       DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, s));
+      prof_end(ps, s);
       int nt = 0;
       DF_HIP(launch_reduce_top2(g.part, p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
       DF_HIP(launch_argmax_final(top2, nt, Mr, draft, top2_gap, s));

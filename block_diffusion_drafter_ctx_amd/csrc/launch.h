@@ -132,7 +132,9 @@ struct AttnPlan {
 
 AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d);
 size_t attention_part_bound(int B, int Hkv, int R, int d);
+// stop_event (nullable hipEvent_t) is recorded right after the main attention
+// kernel, before its combine step (profiling hook).
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, bool bf16_weights, bool bf16_cache,
-                            hipStream_t st);
+                            hipStream_t st, void* stop_event = nullptr);
 
 }  // namespace dflash

@@ -102,3 +102,8 @@ def attention_bytes(L: int, Hkv: int, d: int, gamma: int, ctx_lens, es: int = 2)
 
 def accept_bytes(B: int, n: int) -> int:
     return B * (2 * n + 1) * 4 + B * 8
+
+
+def gemm_bytes(N: int, K: int, M: int, es: int = 2, a_bytes: int = 4, out_bytes: int = 4) -> int:
+    """Weight stream [N, K] once, the M activation rows in, the M output rows out."""
+    return N * K * es + M * K * a_bytes + M * N * out_bytes

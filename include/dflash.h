@@ -198,6 +198,31 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
                                    float* logits_dbg, float* top2_gap, void* ws, size_t ws_bytes,
                                    void* stream);
 
+/* Kernel roles the profiling hook can bracket. */
+typedef enum {
+  DFLASH_PROF_NONE = 0,
+  DFLASH_PROF_LM_HEAD = 1,   /* LM-head weight stream of dflash_argmax_accept */
+  DFLASH_PROF_QKV = 2,       /* per-layer Q/K/V projection */
+  DFLASH_PROF_O = 3,         /* per-layer output projection */
+  DFLASH_PROF_GATEUP = 4,    /* per-layer gate/up projection */
+  DFLASH_PROF_DOWN = 5,      /* per-layer down projection */
+  DFLASH_PROF_FUSE = 6,      /* W_c projection of dflash_fuse_context */
+  DFLASH_PROF_INJECT = 7,    /* W_K/W_V projection of dflash_inject_kv */
+  DFLASH_PROF_ATTENTION = 8  /* injected-context attention (without its combine step) */
+} dflash_prof_role;
+
+/* Profiling hook (measurement only; not needed to run the path).  From now on,
+ * on the calling thread, the i-th kernel launch of `role` records start[i]
+ * (a hipEvent_t) on its stream right before the launch and stop[i] right after
+ * it, for i < n; later launches of the role record nothing.  The caller owns the
+ * events and must keep the arrays alive until it calls this again.  role ==
+ * DFLASH_PROF_NONE (or n == 0) turns the hook off.  Returns the number of
+ * launches recorded since the previous call in *recorded (nullable).
+ * Allocates nothing; errors: DFLASH_ERR_INVALID_ARG for an unknown role or
+ * n > 0 with NULL arrays. */
+dflash_status dflash_profile_events(int32_t role, void* const* start, void* const* stop, int32_t n,
+                                    int32_t* recorded);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,3 +152,10 @@ def test_workspace_covers_smaller_calls(lib):
             assert B.workspace_size(d, b, g, 3000) <= big
     for rows in (1, 16, 100, 3000):
         assert B.workspace_size(d, 4, 33, rows) <= big
+
+
+def test_profile_hook_validation(lib):
+    assert B.profile_events(B.PROF_NONE) == 0
+    with pytest.raises(B.DFlashError) as e:
+        B.profile_events(42)
+    assert e.value.status == B.ERR_INVALID_ARG
