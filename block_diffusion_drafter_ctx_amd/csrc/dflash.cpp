@@ -225,8 +225,14 @@ ArgmaxWs argmax_ws(const dflash_dims* d, int B, int gamma) {
   if (d->dtype == DFLASH_F32) {
     w.part = c.take(static_cast<size_t>(M) * d->V * 4);
   } else {
-    w.part = c.take(gemm_part_floats(d, M, d->V, d->D, A_F32_SPLIT, true) * 4);
-    w.top2 = c.take(static_cast<size_t>((d->V + 511) / 512) * M * 3 * 4);
+    size_t pf = gemm_part_floats(d, M, d->V, d->D, A_F32_SPLIT, true);
+    const size_t pf_stream = plan_gemm_mfma(M, d->V, d->D, A_F32_SPLIT, true).part_floats;
+    if (pf_stream > pf) pf = pf_stream;
+    w.part = c.take(pf * 4);
+    // top-2 candidates: one row per 512-column tile, or per register-K workgroup
+    size_t t2 = static_cast<size_t>((d->V + 511) / 512);
+    if (t2 < static_cast<size_t>(kRkMaxGrid)) t2 = kRkMaxGrid;
+    w.top2 = c.take(t2 * M * 3 * 4);
   }
   w.total = c.off;
   return w;
@@ -633,15 +639,24 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
     const ArgmaxWs lay = argmax_ws(dims, B, gamma);
     char* base = static_cast<char*>(ws);
     if (dims->dtype == DFLASH_BF16) {
-      const GemmPlan p = plan_gemm(Mr, dims->V, D, A_F32_SPLIT, true);
       g.part = reinterpret_cast<float*>(base + lay.part);
       float* top2 = reinterpret_cast<float*>(base + lay.top2);
-      const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-      DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, s));
-      prof_end(ps, s);
-      int nt = 0;
-      DF_HIP(launch_reduce_top2(g.part, p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
-      DF_HIP(launch_argmax_final(top2, nt, Mr, draft, top2_gap, s));
+      const GemmPlan rk = plan_gemm_rk(Mr, dims->V, D, true);
+      if (rk.rk) {
+        // one pass over the LM head: logits reduced in-register, top-2 per workgroup
+        const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
+        DF_HIP(launch_gemm_rk(g, rk, top2, logits_dbg, s));
+        prof_end(ps, s);
+        DF_HIP(launch_argmax_final(top2, rk.grid, Mr, draft, top2_gap, s));
+      } else {
+        const GemmPlan p = plan_gemm(Mr, dims->V, D, A_F32_SPLIT, true);
+        const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
+        DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, s));
+        prof_end(ps, s);
+        int nt = 0;
+        DF_HIP(launch_reduce_top2(g.part, p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
+        DF_HIP(launch_argmax_final(top2, nt, Mr, draft, top2_gap, s));
+      }
     } else {
       float* lg = logits_dbg != nullptr ? logits_dbg : static_cast<float*>(ws);
       g.part = lg;

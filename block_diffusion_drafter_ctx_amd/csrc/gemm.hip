@@ -210,6 +210,138 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------------------- register-K path
+// One block of <= 16 activation rows against a tall weight (the LM head, the
+// FFN gate/up projection).  Sixteen waves split the K range of a workgroup
+// (wave w owns KS k-steps) and keep their activation fragments (hi + lo) in
+// registers for the whole kernel, so a workgroup needs no split-K partner and
+// no LDS slice: every output tile of 16 weight rows is one contiguous
+// 16 x K block of W, streamed by all sixteen waves at once through a ring of
+// KS loads per wave (the next tile's loads are issued as the current tile's
+// MFMAs retire).  The sixteen per-wave partial tiles are summed through LDS
+// in wave order (deterministic).  Epilogue: the [split][M][N] store, or the
+// LM head's running top-2 per row (plus the logits when asked for), merged
+// per workgroup into top2[block][m] = (best value, its index, runner-up).
+constexpr int kRkWaves = 16;
+constexpr int kRkMinN = 16384;   // weight rows below which the split-K streaming kernel wins
+
+template <int KS, bool TOP2>
+__global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, float* top2, float* logits) {
+  __shared__ float red[2][kRkWaves][256];
+  __shared__ float tv1[4][16], tv2[4][16];
+  __shared__ int ti1[4][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = g.S;
+  const int units = S * g.ntiles;
+  const int P = gridDim.x;
+  int u = blockIdx.x;
+  if (u >= units) return;                     // uniform per workgroup
+  const int sp = u % S;                       // P % S == 0: the split never changes
+  const int kwave = sp * (32 * KS * kRkWaves) + wave * (32 * KS);
+  const int kl = kwave + 8 * (lane >> 4);
+  auto wrow = [&](int uu) {
+    int n = (uu / S) * 16 + (lane & 15);
+    n = min(n, g.N - 1);                       // rows past N are clamped; their results are dropped
+    const int64_t r = static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg;
+    return static_cast<const uint16_t*>(g.w) + r * g.w_ld + kl;
+  };
+  uint4 wb[KS];
+  const uint16_t* wp = wrow(u);
+#pragma unroll
+  for (int x = 0; x < KS; ++x) wb[x] = *reinterpret_cast<const uint4*>(wp + x * 32);
+  __builtin_amdgcn_sched_barrier(0);          // the first tile's weights go out before the activation loads
+
+  uint4 bh[KS], bl[KS];
+  {
+    // the host guarantees a_cols % (32 * KS) == 0: a wave's k range lies in one source
+    const int s = __builtin_amdgcn_readfirstlane(kwave / g.a_cols);
+    const int m = lane & 15;
+    const bool ok = m < g.M;
+    const float* p = pick_src<float>(g, s) + a_row_off(g, ok ? m : 0) + (kl - s * g.a_cols);
+    float4 av[2 * KS];
+#pragma unroll
+    for (int x = 0; x < KS; ++x) {
+      av[2 * x] = *reinterpret_cast<const float4*>(p + x * 32);
+      av[2 * x + 1] = *reinterpret_cast<const float4*>(p + x * 32 + 4);
+    }
+    const float keep = ok ? 1.f : 0.f;
+#pragma unroll
+    for (int x = 0; x < KS; ++x) {
+      float v[8] = {av[2 * x].x * keep,     av[2 * x].y * keep,     av[2 * x].z * keep,     av[2 * x].w * keep,
+                    av[2 * x + 1].x * keep, av[2 * x + 1].y * keep, av[2 * x + 1].z * keep, av[2 * x + 1].w * keep};
+      split8(v, bh[x], bl[x]);
+    }
+  }
+
+  // reduction thread tid < 256 owns output (n = 16 * tile + 4 * (ln / 16) + r, m = ln % 16), ln = tid / 4
+  const int ln = tid >> 2;
+  const int mo = ln & 15, no = 4 * (ln >> 4) + (tid & 3);
+  Top2 best{-INFINITY, 0x7fffffff, -INFINITY};
+  int buf = 0;
+  for (;;) {
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nu = u + P;
+    const bool more = nu < units;             // uniform per workgroup
+    if (more) {
+      const uint16_t* np = wrow(nu);
+#pragma unroll
+      for (int x = 0; x < KS; ++x) {
+        acc = mfma16x16x32(wb[x], bh[x], acc);
+        acc = mfma16x16x32(wb[x], bl[x], acc);
+        wb[x] = *reinterpret_cast<const uint4*>(np + x * 32);
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < KS; ++x) {
+        acc = mfma16x16x32(wb[x], bh[x], acc);
+        acc = mfma16x16x32(wb[x], bl[x], acc);
+      }
+    }
+    *reinterpret_cast<float4*>(&red[buf][wave][lane * 4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+    if (tid < 256) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kRkWaves; ++w) v += red[buf][w][tid];
+      const int n = (u / S) * 16 + no;
+      if (mo < g.M && n < g.N) {
+        if constexpr (TOP2) {
+          if (logits != nullptr) logits[static_cast<int64_t>(mo) * g.N + n] = v;
+          best = top2_push(best, v, n);
+        } else {
+          g.part[(static_cast<int64_t>(sp) * g.M + mo) * g.N + n] = v;
+        }
+      }
+    }
+    buf ^= 1;
+    if (!more) break;
+    u = nu;
+  }
+
+  if constexpr (TOP2) {
+    // merge the 16 owners of each row: lanes 4m..4m+3 of waves 0..3
+    if (tid < 256) {
+      best = top2_merge(best, top2_shfl_xor(best, 1));
+      best = top2_merge(best, top2_shfl_xor(best, 2));
+      if ((lane & 3) == 0) {
+        tv1[wave][lane >> 2] = best.v1;
+        ti1[wave][lane >> 2] = best.i1;
+        tv2[wave][lane >> 2] = best.v2;
+      }
+    }
+    __syncthreads();
+    if (tid < 16 && tid < g.M) {
+      Top2 t{tv1[0][tid], ti1[0][tid], tv2[0][tid]};
+#pragma unroll
+      for (int w = 1; w < 4; ++w) t = top2_merge(t, Top2{tv1[w][tid], ti1[w][tid], tv2[w][tid]});
+      float* o = top2 + (static_cast<int64_t>(blockIdx.x) * g.M + tid) * 3;
+      o[0] = t.v1;
+      o[1] = __int_as_float(t.i1);
+      o[2] = t.v2;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ tiled path
 // Many activation rows (context ingest, big batches): a classic LDS-tiled MFMA
 // GEMM.  Workgroup tile 128 weight rows x 128 activation rows x 64 k; 4 waves
@@ -517,6 +649,7 @@ GemmPlan plan_gemm_tiled(int M, int N, int K) {
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p, hipStream_t st) {
+  if (p.rk) return ak == A_F32_SPLIT ? launch_gemm_rk(a0, p, nullptr, nullptr, st) : hipErrorInvalidValue;
   if (p.tiled) {
     GemmArgs a = a0;
     a.chunks_per_split = p.cps;
@@ -556,9 +689,62 @@ hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p,
   }
 }
 
+// Register-K plan: <= 16 rows, K a multiple of 16 waves x KS k-steps (KS = 8,
+// else 4), at most one workgroup per CU (the grid is a multiple of the split
+// count so that a workgroup keeps its K range).  Only worth it when the weight
+// is tall: every workgroup reads the whole activation block once (M x K x 4
+// bytes from L2), which must stay small against its share of W.
+GemmPlan plan_gemm_rk(int M, int N, int K, bool top2) {
+  GemmPlan p;
+  if (M < 1 || M > 16 || N < kRkMinN || env_int("DFLASH_GEMM_NO_RK", 0) != 0) return p;
+  int ks = 0;
+  if (K % (32 * 8 * kRkWaves) == 0) ks = 8;
+  else if (K % (32 * 4 * kRkWaves) == 0) ks = 4;
+  if (ks == 0) return p;
+  const int S = K / (32 * ks * kRkWaves);
+  if (top2 && S != 1) return p;
+  p.rk = true;
+  p.ks = ks;
+  p.S = S;
+  p.MT = 16;
+  p.mtiles = 1;
+  p.ntiles = (N + 15) / 16;
+  p.cps = ks * kRkWaves;
+  p.nchunks = K / 32;
+  const long units = static_cast<long>(S) * p.ntiles;
+  int grid = device_cus() / S * S;
+  if (grid > kRkMaxGrid) grid = kRkMaxGrid / S * S;
+  if (grid < S) grid = S;
+  p.grid = static_cast<int>(units < grid ? units : grid);
+  p.part_floats = top2 ? 0 : static_cast<size_t>(S) * M * N;
+  return p;
+}
+
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
+  if (ak == A_F32_SPLIT && M <= 16) {
+    const GemmPlan r = plan_gemm_rk(M, N, K, false);
+    if (r.rk && r.S == 1) return r;
+  }
   if (M > 64 && K % kTileK == 0 && env_int("DFLASH_GEMM_NO_TILED", 0) == 0) return plan_gemm_tiled(M, N, K);
   return plan_gemm_mfma(M, N, K, ak, wide);
+}
+
+hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, float* logits, hipStream_t st) {
+  if (!p.rk || a0.a_cols % (32 * p.ks) != 0 || (top2 != nullptr && p.S != 1)) return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  a.S = p.S;
+  a.ntiles = p.ntiles;
+  a.mtiles = 1;
+  a.chunks_per_split = p.cps;
+  const dim3 grid(p.grid), block(64 * kRkWaves);
+  if (top2 != nullptr) {
+    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, true>), grid, block, 0, st, a, top2, logits);
+    else hipLaunchKernelGGL((gemm_rk_kernel<4, true>), grid, block, 0, st, a, top2, logits);
+  } else {
+    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, false>), grid, block, 0, st, a, nullptr, nullptr);
+    else hipLaunchKernelGGL((gemm_rk_kernel<4, false>), grid, block, 0, st, a, nullptr, nullptr);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st) {

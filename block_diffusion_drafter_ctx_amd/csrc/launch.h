@@ -36,6 +36,8 @@ enum GemmAKind { A_BF16 = 0, A_F32_SPLIT = 1 };  // exact bf16 A, or fp32 A spli
 struct GemmPlan {
   int MT = 16, mtiles = 1, ntiles = 1, nchunks = 1, cps = 1, S = 1, waves = 8, grid = 1;
   bool tiled = false;   // LDS-tiled kernel for many activation rows
+  bool rk = false;      // register-K kernel (<= 16 rows, tall weight)
+  int ks = 8;           // register-K: k steps per wave
   size_t part_floats = 0;
 };
 
@@ -48,6 +50,16 @@ GemmPlan plan_gemm_tiled(int M, int N, int K);
 // K % 64 == 0, streaming otherwise).
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide);
 hipError_t launch_gemm_mfma(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, hipStream_t st);
+
+// Register-K kernel for <= 16 fp32 activation rows (split hi/lo) against a tall
+// bf16 weight; plan.rk is false when the shape does not qualify.  top2 = true
+// asks for the LM-head epilogue (a single K split).
+constexpr int kRkMaxGrid = 1024;   // bound on register-K workgroups (top-2 workspace rows)
+GemmPlan plan_gemm_rk(int M, int N, int K, bool top2);
+// top2 == nullptr: store part[s][m][n].  Otherwise write the per-workgroup top-2
+// of every row to top2 [p.grid][M][3] (value, index bits, runner-up) and, when
+// logits != nullptr, the logits [M][N].
+hipError_t launch_gemm_rk(const GemmArgs& a, const GemmPlan& p, float* top2, float* logits, hipStream_t st);
 
 // Sum the split-K partials of logits [S][M][N] per 512-column tile, optionally
 // store the logits, and write each (tile, row) top-2 to top2 [ntiles][M][3].

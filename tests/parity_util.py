@@ -173,7 +173,11 @@ class Workload:
         logits = torch.empty(Bn, n, cfg.V, dtype=torch.float32, device=self.dev)
         gap = torch.empty(Bn, n, dtype=torch.float32, device=self.dev)
         self.dr.argmax_accept(B.ARGMAX, h_final, Bn, g, draft, logits=logits, gap=gap)
+        # the same argmax without the debug outputs (the path a drafting loop takes)
+        draft_lean = torch.empty_like(draft)
+        self.dr.argmax_accept(B.ARGMAX, h_final, Bn, g, draft_lean)
         torch.cuda.synchronize()
+        assert torch.equal(draft, draft_lean), "argmax differs when logits / gap are not requested"
         assert self.cache.len_list() == lens
         for b in range(Bn):
             assert torch.equal(self.cache.k[:, b, :, :lens[b]], k_before[b]), "context K rows changed"
