@@ -95,7 +95,7 @@ def main():
     log(f"weights uploaded in {time.time() - t0:.1f}s ({B.version()}, {torch.cuda.get_device_name(0)})")
 
     cap = max(cfg.ctx) + CYCLE * cfg.append_rows + max(gamma, cfg.append_rows)
-    cap = (cap + 7) // 8 * 8
+    cap = (cap + 31) // 32 * 32
     cache = dr.cache(Bn, cap)
     dr.ensure_workspace(Bn, gamma, max(N, Bn * cfg.append_rows))
     stream = torch.cuda.current_stream()

@@ -45,59 +45,87 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, int item, int& b,
   sp = local - j * a.nsplit[b];
 }
 
-// Raw key / value loads (kept in registers until used, so the next block's
-// loads can be in flight during this block's math) and their conversion into
-// MFMA operands (bf16 as is; fp32 split into bf16 hi + lo).
-template <typename TKV> struct KVLoad;
-template <> struct KVLoad<uint16_t> {
-  static constexpr bool kSplit = false;
+// Key / value staging.  A workgroup streams its key range in 32-key blocks;
+// every block is loaded once, cooperatively by the first 256 threads (each owns
+// a fixed set of MFMA fragments of it), converted once into the bf16 operand
+// planes the MFMAs take (an fp32 element as hi + lo, a bf16 element as is) and
+// written to LDS in fragment order, so each wave reads its operands with one
+// conflict-free 16-byte LDS read per fragment, and the loads of the next block
+// are in flight while the current one is multiplied.
+//   K fragment (kt, ds, lane): key k0 + 16 kt + lane % 16, dims 32 ds + 8 (lane / 16) .. +7
+//   V fragment (dt, lane):     dim 16 dt + lane % 16 of the transposed V cache, keys
+//                              k0 + 4 (lane / 16) + {0..3} and k0 + 16 + 4 (lane / 16) + {0..3}
+// Blocks start at multiples of 32 keys and the cache capacity is a multiple of
+// 32, so a block never reads past its head's rows; keys at or past the end of
+// the range (unwritten rows) get zero values and -inf scores.
+template <typename TKV> struct KVStage;
+template <> struct KVStage<uint16_t> {
+  static constexpr int HL = 1;
   struct Raw { uint4 u; };
-  // 8 consecutive elements
-  static __device__ __forceinline__ Raw row8(const uint16_t* p) { return Raw{*reinterpret_cast<const uint4*>(p)}; }
-  // elements [k, k+4) and [k+16, k+20) of one transposed value row
-  static __device__ __forceinline__ Raw pair4(const uint16_t* p, int k) {
-    const uint2 v0 = *reinterpret_cast<const uint2*>(p + k);
-    const uint2 v1 = *reinterpret_cast<const uint2*>(p + k + 16);
+  static __device__ __forceinline__ Raw krow(const uint16_t* p) { return Raw{*reinterpret_cast<const uint4*>(p)}; }
+  static __device__ __forceinline__ Raw vpair(const uint16_t* p) {
+    const uint2 v0 = *reinterpret_cast<const uint2*>(p);
+    const uint2 v1 = *reinterpret_cast<const uint2*>(p + 16);
     return Raw{make_uint4(v0.x, v0.y, v1.x, v1.y)};
   }
-  // same with every index clamped to <= last
-  static __device__ __forceinline__ Raw pair4_clamped(const uint16_t* p, int k, int last) {
-    uint32_t w[4];
+  // zero the elements whose key (k + (e / 4) * 16 + e % 4) is >= kend
+  static __device__ __forceinline__ void vmask(Raw& r, int k, int kend) {
+    uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int kl = min(k + (e >> 1) * 16 + 2 * (e & 1), last), kh = min(k + (e >> 1) * 16 + 2 * (e & 1) + 1, last);
-      w[e] = static_cast<uint32_t>(p[kl]) | (static_cast<uint32_t>(p[kh]) << 16);
+      const int key = k + (e >> 1) * 16 + 2 * (e & 1);
+      const uint32_t lo = key < kend ? 0x0000ffffu : 0u, hi = key + 1 < kend ? 0xffff0000u : 0u;
+      w[e] &= lo | hi;
     }
-    return Raw{make_uint4(w[0], w[1], w[2], w[3])};
+    r.u = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  static __device__ __forceinline__ void ops(const Raw& r, uint4& hi, uint4& lo) { hi = r.u; lo = r.u; }
+  static __device__ __forceinline__ void put(uint4* dst, const Raw& r) { dst[0] = r.u; }
 };
-template <> struct KVLoad<float> {
-  static constexpr bool kSplit = true;
+template <> struct KVStage<float> {
+  static constexpr int HL = 2;
   struct Raw { float4 a, b; };
-  static __device__ __forceinline__ Raw row8(const float* p) {
+  static __device__ __forceinline__ Raw krow(const float* p) {
     return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
-  static __device__ __forceinline__ Raw pair4(const float* p, int k) {
-    return Raw{*reinterpret_cast<const float4*>(p + k), *reinterpret_cast<const float4*>(p + k + 16)};
+  static __device__ __forceinline__ Raw vpair(const float* p) {
+    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 16)};
   }
-  static __device__ __forceinline__ Raw pair4_clamped(const float* p, int k, int last) {
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = p[min(k + (e >> 2) * 16 + (e & 3), last)];
-    return Raw{make_float4(x[0], x[1], x[2], x[3]), make_float4(x[4], x[5], x[6], x[7])};
+  static __device__ __forceinline__ void vmask(Raw& r, int k, int kend) {
+    r.a.x = k + 0 < kend ? r.a.x : 0.f;
+    r.a.y = k + 1 < kend ? r.a.y : 0.f;
+    r.a.z = k + 2 < kend ? r.a.z : 0.f;
+    r.a.w = k + 3 < kend ? r.a.w : 0.f;
+    r.b.x = k + 16 < kend ? r.b.x : 0.f;
+    r.b.y = k + 17 < kend ? r.b.y : 0.f;
+    r.b.z = k + 18 < kend ? r.b.z : 0.f;
+    r.b.w = k + 19 < kend ? r.b.w : 0.f;
   }
-  static __device__ __forceinline__ void ops(const Raw& r, uint4& hi, uint4& lo) {
+  // hi plane at dst[0], lo plane 64 fragments further
+  static __device__ __forceinline__ void put(uint4* dst, const Raw& r) {
     const float x[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+    uint4 hi, lo;
     split8(x, hi, lo);
+    dst[0] = hi;
+    dst[64] = lo;
   }
 };
 
+
+constexpr int kAttnDepth = 2;      // 32-key blocks in flight per workgroup
+constexpr int kAttnWaves = 8;      // waves per workgroup: all stage, the first ceil(R / 16) compute
+
 template <int HD, typename TKV>
-__global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
-  using LD = KVLoad<TKV>;
-  constexpr int DS = HD / 32;   // 32-wide d steps of the score MFMA
-  constexpr int DT = HD / 16;   // 16-wide d tiles of the output MFMA
+__global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int NW = kAttnWaves, DEPTH = kAttnDepth;
+  using KV = KVStage<TKV>;
+  using Raw = typename KV::Raw;
+  constexpr int HL = KV::HL;
+  constexpr int DS = HD / 32;                 // 32-wide d steps of the score MFMA
+  constexpr int DT = HD / 16;                 // 16-wide d tiles of the output MFMA
+  constexpr int KFR = 2 * DS * 64;            // K fragments per block
+  constexpr int NFR = KFR + DT * 64;          // K + V fragments per block
+  constexpr int BUF = NFR * HL;               // uint4 per LDS block buffer
+  extern __shared__ uint4 stage[];            // [2][BUF]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g4 = lane >> 4;
   const int item = blockIdx.x;
   int b, j, sp;
@@ -107,8 +135,131 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int kend = min(nk, kbeg + a.split_keys);
   const int r = blockIdx.y * kRowsPerGroup + wave * 16 + (lane & 15);
   const int G = a.Hq / a.Hkv;
+  const bool computes = blockIdx.y * kRowsPerGroup + wave * 16 < a.R;   // uniform per wave
 
-  uint4 qh[DS], ql[DS];
+  uint4 qh[DS], ql[DS];                       // query fragments, loaded after the first key blocks
+  const int64_t head = static_cast<int64_t>(b) * a.Hkv + j;
+  const TKV* kbase = static_cast<const TKV*>(a.kc) + head * a.cap * HD;
+  const TKV* vbase = static_cast<const TKV*>(a.vc) + head * HD * a.cap;
+
+  // every thread stages fragments f = t + 64 NW i of each block; i < PER_K are K fragments
+  constexpr int STG = 64 * NW;
+  constexpr int PER = NFR / STG, PER_K = KFR / STG;
+  static_assert(NFR % STG == 0, "fragment split");
+  // K or V for fragment slot i: known at compile time when STG divides KFR
+  auto is_k = [&](int i, int f) { return (KFR % STG == 0) ? (i < PER_K) : (f < KFR); };
+  const int t = threadIdx.x;
+  auto load = [&](Raw (&rr)[PER], int k0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int f = t + STG * i;
+      const int ln = f & 63;
+      if (is_k(i, f)) {
+        const int kt = f / (DS * 64), ds = (f / 64) % DS;
+        const int key = k0 + kt * 16 + (ln & 15);
+        rr[i] = KV::krow(kbase + static_cast<int64_t>(key) * HD + ds * 32 + 8 * (ln >> 4));
+      } else {
+        const int dt = (f - KFR) / 64;
+        const int k = k0 + 4 * (ln >> 4);
+        rr[i] = KV::vpair(vbase + static_cast<int64_t>(dt * 16 + (ln & 15)) * a.cap + k);
+      }
+    }
+  };
+  auto store = [&](Raw (&rr)[PER], uint4* buf, int k0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int f = t + STG * i;
+      const int ln = f & 63, fr = f >> 6;       // fragment index: kt*DS + ds, or KFR/64 + dt
+      if (!is_k(i, f)) KV::vmask(rr[i], k0 + 4 * (ln >> 4), kend);
+      KV::put(buf + (fr * HL) * 64 + ln, rr[i]);
+    }
+  };
+
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto compute = [&](const uint4* buf, int k0, int klim) {   // keys >= klim do not count
+    // all K fragments of the block first (independent LDS reads, one wait), then
+    // the score MFMAs in four independent accumulation chains
+    uint4 kf[2][DS][HL];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+        for (int hl = 0; hl < HL; ++hl) kf[kt][ds][hl] = buf[((kt * DS + ds) * HL + hl) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t sa[2], sb[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) { sa[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; sb[kt] = sa[kt]; }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sa[kt] = mfma16x16x32(kf[kt][ds][0], qh[ds], sa[kt]);
+        sb[kt] = mfma16x16x32(kf[kt][ds][0], ql[ds], sb[kt]);
+        if constexpr (HL == 2) sb[kt] = mfma16x16x32(kf[kt][ds][1], qh[ds], sb[kt]);
+      }
+    // the value fragments are read now; their latency hides behind the softmax
+    uint4 vf[DT][HL];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int hl = 0; hl < HL; ++hl) vf[dt][hl] = buf[((KFR / 64 + dt) * HL + hl) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[kt] = sa[kt] + sb[kt];
+    float p[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[kt * 4 + e] = (k0 + kt * 16 + 4 * g4 + e < klim) ? s[kt][e] : -INFINITY;
+    float mx = p[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, p[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = exp2f(p[e] - m_new);
+      ps += p[e];
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (__any(alpha != 1.0f)) {               // skipped once every row's max has settled
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    uint4 ph, pl;
+    split8(p, ph, pl);
+    // O^T += V^T P^T; k-slot e of lane group g4 <-> key k0 + 4*g4 + e (e < 4),
+    // k0 + 16 + 4*g4 + (e - 4) (e >= 4): the layout S^T left in p[]
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt] = mfma16x16x32(vf[dt][0], ph, o[dt]);
+      o[dt] = mfma16x16x32(vf[dt][0], pl, o[dt]);
+      if constexpr (HL == 2) o[dt] = mfma16x16x32(vf[dt][1], ph, o[dt]);
+    }
+  };
+
+  // DEPTH blocks in flight in registers (block i in set i % DEPTH) and two LDS
+  // buffers (block i in buffer i % 2), one barrier per block: the buffer written
+  // for block i was last read for block i - 2, before the previous barrier.
+  // The loop has no data-dependent branch around a load, so that every step
+  // issues and retires its loads in the same order (precise waits): it runs a
+  // whole number of DEPTH steps, the steps past the last block re-stage the
+  // last block (a cache hit) and count no key.
+  const int nblk = (kend - kbeg + 31) / 32;   // >= 1: every key range is non-empty
+  auto blk = [&](int i) { return kbeg + min(i, nblk - 1) * 32; };
+  Raw rr[DEPTH][PER];
+#pragma unroll
+  for (int dd = 0; dd < DEPTH; ++dd) load(rr[dd], blk(dd));
   if (r < a.R) {
     const int h = j * G + r / a.gamma, i = r % a.gamma;
     const float* qp = a.q + (static_cast<int64_t>(b * a.gamma + i) * a.Hq + h) * HD + 8 * g4;
@@ -126,132 +277,21 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
     for (int ds = 0; ds < DS; ++ds) { qh[ds] = make_uint4(0, 0, 0, 0); ql[ds] = qh[ds]; }
   }
 
-  const int64_t head = static_cast<int64_t>(b) * a.Hkv + j;
-  const TKV* kbase = static_cast<const TKV*>(a.kc) + head * a.cap * HD + 8 * g4;
-  const TKV* vbase = static_cast<const TKV*>(a.vc) + head * HD * a.cap;
-
-  f32x4_t o[DT];
+  for (int bi = 0; bi < nblk; bi += DEPTH) {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  using Raw = typename LD::Raw;
-  Raw kr[2][DS], vr[DT];
-
-  // Loads of one 32-key block; FULL blocks need no clamping (the ragged tail of
-  // a key range is a separate, clamped block after the main loop).
-  auto load_k = [&](int k0, auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = FULL ? k0 + kt * 16 + (lane & 15) : min(k0 + kt * 16 + (lane & 15), kend - 1);
-      const TKV* kp = kbase + static_cast<int64_t>(key) * HD;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) kr[kt][ds] = LD::row8(kp + ds * 32);
+    for (int dd = 0; dd < DEPTH; ++dd) {
+      uint4* buf = stage + ((bi + dd) & 1) * BUF;
+      const int k0 = blk(bi + dd);
+      store(rr[dd], buf, k0);
+      load(rr[dd], blk(bi + dd + DEPTH));
+      __syncthreads();
+      if (computes) compute(buf, k0, bi + dd < nblk ? kend : k0);
     }
-  };
-  auto load_v = [&](int k0, auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const TKV* vp = vbase + static_cast<int64_t>(dt * 16 + (lane & 15)) * a.cap;
-      vr[dt] = FULL ? LD::pair4(vp, k0 + 4 * g4) : LD::pair4_clamped(vp, k0 + 4 * g4, kend - 1);
-    }
-  };
-
-  // One block in two phases: scores (reads kr), then online softmax (base 2;
-  // the scale is folded into Q) and PV (reads vr).
-  auto scores = [&](f32x4_t (&s)[2]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        uint4 kh, kl;
-        LD::ops(kr[kt][ds], kh, kl);
-        s[kt] = mfma16x16x32(kh, qh[ds], s[kt]);
-        s[kt] = mfma16x16x32(kh, ql[ds], s[kt]);
-        if constexpr (LD::kSplit) s[kt] = mfma16x16x32(kl, qh[ds], s[kt]);
-      }
-    }
-  };
-  auto softmax_pv = [&](const f32x4_t (&s)[2], int k0, auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    float p[8];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        p[kt * 4 + rr] = (FULL || k0 + kt * 16 + 4 * g4 + rr < kend) ? s[kt][rr] : -INFINITY;
-    float mx = p[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, p[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(p[e] - m_new);
-      ps += p[e];
-    }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    if (__any(alpha != 1.0f)) {            // skipped once every row's max has settled
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
-    uint4 ph, pl;
-    split8(p, ph, pl);
-    // O^T += V^T P^T; k-slot e of lane group g4 <-> key k0 + 4*g4 + e (e < 4),
-    // k0 + 16 + 4*g4 + (e - 4) (e >= 4): the layout S^T left in p[].
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      uint4 vh, vl;
-      LD::ops(vr[dt], vh, vl);
-      o[dt] = mfma16x16x32(vh, ph, o[dt]);
-      o[dt] = mfma16x16x32(vh, pl, o[dt]);
-      if constexpr (LD::kSplit) o[dt] = mfma16x16x32(vl, ph, o[dt]);
-    }
-  };
-
-  using Full = std::integral_constant<bool, true>;
-  using Tail = std::integral_constant<bool, false>;
-  const int kfull = kbeg + ((kend - kbeg) / 32) * 32;   // end of the full blocks
-  // bf16 caches prefetch the next block's keys during this block's softmax and
-  // PV and its values right after; fp32 caches (twice the registers per key)
-  // load keys and values together at the top of each block instead.
-  constexpr bool kPrefetch = !LD::kSplit;
-  if (kPrefetch && kbeg < kfull) {
-    load_k(kbeg, Full{});
-    load_v(kbeg, Full{});
-  }
-  for (int k0 = kbeg; k0 < kfull; k0 += 32) {
-    f32x4_t s[2];
-    if (!kPrefetch) {
-      load_k(k0, Full{});
-      load_v(k0, Full{});
-      scores(s);
-      softmax_pv(s, k0, Full{});
-    } else {
-      const bool more = k0 + 32 < kfull;
-      scores(s);
-      if (more) load_k(k0 + 32, Full{});   // next keys fly during softmax + PV
-      softmax_pv(s, k0, Full{});
-      if (more) load_v(k0 + 32, Full{});
-    }
-  }
-  if (kfull < kend) {
-    f32x4_t s[2];
-    load_k(kfull, Tail{});
-    load_v(kfull, Tail{});
-    scores(s);
-    softmax_pv(s, kfull, Tail{});
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
-  if (r < a.Rpad) {
+  if (computes && r < a.Rpad) {
     float* po = a.part_o + (static_cast<int64_t>(item) * a.Rpad + r) * HD + 4 * g4;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -396,14 +436,12 @@ hipError_t launch_attention(const AttnArgs& a0, const AttnPlan& p, bool bf16_wei
   for (int b = 0; b < a.B; ++b) { a.nsplit[b] = p.nsplit[b]; a.item_off[b] = p.item_off[b]; }
   a.item_off[a.B] = p.item_off[a.B];
   const dim3 grid(p.items, p.row_groups);
-  const dim3 block(64 * waves_per_group(a.R));
-  if (bf16_cache) {
-    if (a.d == 128) hipLaunchKernelGGL((attn_mfma_kernel<128, uint16_t>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_mfma_kernel<64, uint16_t>), grid, block, 0, st, a);
-  } else {
-    if (a.d == 128) hipLaunchKernelGGL((attn_mfma_kernel<128, float>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_mfma_kernel<64, float>), grid, block, 0, st, a);
-  }
+  const dim3 block(64 * kAttnWaves);
+  // LDS: two block buffers of (2 DS + DT) * 64 fragments, two planes for fp32
+  const size_t lds = static_cast<size_t>(2) * (a.d / 16 + a.d / 16) * 64 * (bf16_cache ? 1 : 2) * sizeof(uint4);
+  auto kern = bf16_cache ? (a.d == 128 ? attn_mfma_kernel<128, uint16_t> : attn_mfma_kernel<64, uint16_t>)
+                         : (a.d == 128 ? attn_mfma_kernel<128, float> : attn_mfma_kernel<64, float>);
+  hipLaunchKernelGGL(kern, grid, block, lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (stop_event != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(stop_event), st);

@@ -98,7 +98,7 @@ dflash_status check_cache(const dflash_kv_cache* c) {
   DF_REQUIRE(c->k != nullptr && c->v != nullptr && c->len != nullptr, DFLASH_ERR_INVALID_ARG,
              "cache k, v and len must be non-NULL");
   DF_REQUIRE(aligned16(c->k) && aligned16(c->v), DFLASH_ERR_INVALID_ARG, "cache k/v must be 16-byte aligned");
-  DF_REQUIRE(c->cap >= 8 && c->cap % 8 == 0, DFLASH_ERR_INVALID_ARG, "cache->cap=%d must be a positive multiple of 8",
+  DF_REQUIRE(c->cap >= 32 && c->cap % 32 == 0, DFLASH_ERR_INVALID_ARG, "cache->cap=%d must be a positive multiple of 32",
              c->cap);
   for (int b = 0; b < c->B; ++b)
     DF_REQUIRE(c->len[b] >= 0 && c->len[b] <= c->cap, DFLASH_ERR_INVALID_ARG, "cache->len[%d]=%d outside [0, cap]",

@@ -113,7 +113,8 @@ typedef struct {
   void* k;
   void* v;
   int32_t B;     /* sequences, 1..DFLASH_MAX_BATCH */
-  int32_t cap;   /* rows per (layer, sequence, head) */
+  int32_t cap;   /* rows per (layer, sequence, head); a positive multiple of 32 (the
+                    attention reads keys in aligned 32-row blocks) */
   int32_t* len;  /* host [B] */
 } dflash_kv_cache;
 

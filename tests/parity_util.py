@@ -106,7 +106,7 @@ class Workload:
         t0 = time.time()
         self.dr = DeviceDrafter(cfg, self.inp, device)
         cap = max(cfg.ctx) + iters * cfg.append_rows + max(gamma, cfg.append_rows) + extra_cap
-        cap = (cap + 7) // 8 * 8
+        cap = (cap + 31) // 32 * 32
         self.cache = self.dr.cache(cfg.B, cap)
         self.dr.ensure_workspace(cfg.B, gamma, max(cfg.n_ctx_total, cfg.B * cfg.append_rows, 1))
         # oracle weights in float64 (converted once)

@@ -112,8 +112,11 @@ def test_misaligned_and_bad_cache(lib):
     with pytest.raises(B.DFlashError) as e:     # ld < D
         B.fuse_context(_dims(), w, [0x2000] * 5, 128, 4, 0x3000, 0x100000, 1 << 30)
     assert e.value.status == B.ERR_INVALID_ARG
-    with pytest.raises(B.DFlashError) as e:     # cap not a multiple of 8
+    with pytest.raises(B.DFlashError) as e:     # cap not a multiple of 32
         B.inject_kv(_dims(), B.Weights(w_qkv=0x1000), 0x3000, [1, 1], _cache(cap=60), 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.DFlashError) as e:     # a multiple of 8 but not of 32
+        B.inject_kv(_dims(), B.Weights(w_qkv=0x1000), 0x3000, [1, 1], _cache(cap=40), 0, 0)
     assert e.value.status == B.ERR_INVALID_ARG
     with pytest.raises(B.DFlashError) as e:     # B too large
         B.inject_kv(_dims(), B.Weights(w_qkv=0x1000), 0x3000, [1] * 65,

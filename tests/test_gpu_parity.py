@@ -170,10 +170,10 @@ def test_bf16_storage_rounding_is_rne():
         w[(Hq + Hkv) * d + c, b] = -1.0
     Ht = torch.from_numpy(H).cuda().to(torch.bfloat16)
     wq = torch.from_numpy(w).cuda().to(torch.bfloat16)
-    kc = torch.zeros(L, 1, Hkv, 8, d, dtype=torch.bfloat16, device="cuda")
-    vc = torch.zeros(L, 1, Hkv, d, 8, dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(L, 1, Hkv, 32, d, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(L, 1, Hkv, d, 32, dtype=torch.bfloat16, device="cuda")
     lens = (ctypes.c_int32 * 1)(0)
-    cache = B.KVCache(k=kc.data_ptr(), v=vc.data_ptr(), B=1, cap=8, len=ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
+    cache = B.KVCache(k=kc.data_ptr(), v=vc.data_ptr(), B=1, cap=32, len=ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
     wts = B.Weights(w_qkv=wq.data_ptr())
     nbytes = B.workspace_size(dims, 1, 2, 4)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
