@@ -535,6 +535,7 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
   const AttnPlan ap = bf ? plan_attention(B, nkeys, Hkv, R, d) : AttnPlan{};
   const size_t layer_elems = static_cast<size_t>(B) * Hkv * cache->cap * d;
 
+  const GemmPlan swiglu_rk = bf ? plan_gemm_rk_swiglu(M, F, D) : GemmPlan{};
   DF_HIP(launch_embed_norm(block_tokens, embed_override, w->embed, dims->V, M, D, w->g_attn, dims->rms_eps, h, a, bf, s));
   for (int l = 0; l < L; ++l) {
     int S = 1;
@@ -582,8 +583,27 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
 
     DF_HIP(gemm(o, hd, wp(w->w_o, static_cast<int64_t>(l) * D * hd), D, &S, DFLASH_PROF_O));
     DF_HIP(launch_residual_norm(part, S, M, D, h, wp(w->g_ffn, static_cast<int64_t>(l) * D), dims->rms_eps, a, bf, s));
-    DF_HIP(gemm(a, D, wp(w->w_gateup, static_cast<int64_t>(l) * 2 * F * D), 2 * F, &S, DFLASH_PROF_GATEUP));
-    DF_HIP(launch_swiglu(part, S, M, F, sw, s));
+    if (swiglu_rk.rk) {
+      // gate/up GEMM with SwiGLU in its epilogue
+      GemmArgs g{};
+      for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = a;
+      g.a_cols = D;
+      g.a_rg = INT_MAX;
+      g.a_ld = D;
+      g.w = wp(w->w_gateup, static_cast<int64_t>(l) * 2 * F * D);
+      g.w_ld = D;
+      g.w_rg = INT_MAX;
+      g.M = M;
+      g.N = F;
+      g.K = D;
+      const int ps = prof_begin(DFLASH_PROF_GATEUP, s);
+      const hipError_t e = launch_gemm_rk_swiglu(g, swiglu_rk, sw, s);
+      prof_end(ps, s);
+      DF_HIP(e);
+    } else {
+      DF_HIP(gemm(a, D, wp(w->w_gateup, static_cast<int64_t>(l) * 2 * F * D), 2 * F, &S, DFLASH_PROF_GATEUP));
+      DF_HIP(launch_swiglu(part, S, M, F, sw, s));
+    }
     DF_HIP(gemm(sw, F, wp(w->w_down, static_cast<int64_t>(l) * D * F), D, &S, DFLASH_PROF_DOWN));
     const bool last = l + 1 == L;
     DF_HIP(launch_residual_norm(part, S, M, D, h,

@@ -219,14 +219,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(GemmArgs g) {
 // 16 x K block of W, streamed by all sixteen waves at once through a ring of
 // KS loads per wave (the next tile's loads are issued as the current tile's
 // MFMAs retire).  The sixteen per-wave partial tiles are summed through LDS
-// in wave order (deterministic).  Epilogue: the [split][M][N] store, or the
-// LM head's running top-2 per row (plus the logits when asked for), merged
-// per workgroup into top2[block][m] = (best value, its index, runner-up).
+// in wave order (deterministic).  Epilogues: the [split][M][N] store; the LM
+// head's running top-2 per row (plus the logits when asked for), merged per
+// workgroup into top2[block][m] = (best value, its index, runner-up); or the
+// FFN's SwiGLU, where a tile holds 8 gate rows and the 8 matching up rows of
+// the stacked [gate; up] weight, so s = silu(gate) * up leaves the kernel
+// directly (N = F outputs, 8 per tile).
 constexpr int kRkWaves = 16;
 constexpr int kRkMinN = 16384;   // weight rows below which the split-K streaming kernel wins
 
-template <int KS, bool TOP2>
+enum RkEpilogue { RK_PART = 0, RK_TOP2 = 1, RK_SWIGLU = 2 };
+
+template <int KS, int EP>
 __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, float* top2, float* logits) {
+  constexpr bool TOP2 = EP == RK_TOP2;
+  constexpr int TN = EP == RK_SWIGLU ? 8 : 16;   // outputs per tile
   __shared__ float red[2][kRkWaves][256];
   __shared__ float tv1[4][16], tv2[4][16];
   __shared__ int ti1[4][16];
@@ -240,8 +247,13 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
   const int kwave = sp * (32 * KS * kRkWaves) + wave * (32 * KS);
   const int kl = kwave + 8 * (lane >> 4);
   auto wrow = [&](int uu) {
-    int n = (uu / S) * 16 + (lane & 15);
-    n = min(n, g.N - 1);                       // rows past N are clamped; their results are dropped
+    int n;
+    if constexpr (EP == RK_SWIGLU) {
+      // lanes 0-7: gate rows 8t.., lanes 8-15: up rows F + 8t.. (rows past F clamped, results dropped)
+      n = min((uu / S) * 8 + (lane & 7), g.N - 1) + ((lane & 8) ? g.N : 0);
+    } else {
+      n = min((uu / S) * 16 + (lane & 15), g.N - 1);   // rows past N are clamped; their results are dropped
+    }
     const int64_t r = static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg;
     return static_cast<const uint16_t*>(g.w) + r * g.w_ld + kl;
   };
@@ -299,11 +311,24 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
     }
     *reinterpret_cast<float4*>(&red[buf][wave][lane * 4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     __syncthreads();
-    if (tid < 256) {
+    if constexpr (EP == RK_SWIGLU) {
+      // thread tid < 128 holds gate output j of row m at red index tid and the
+      // matching up output at tid + 128 (weight row j + 8 of the tile)
+      if (tid < 128) {
+        float vg = 0.f, vu = 0.f;
+#pragma unroll 4
+        for (int w = 0; w < kRkWaves; ++w) {
+          vg += red[buf][w][tid];
+          vu += red[buf][w][tid + 128];
+        }
+        const int f = (u / S) * TN + no;       // no < 8 for tid < 128
+        if (mo < g.M && f < g.N) g.part[static_cast<int64_t>(mo) * g.N + f] = vg / (1.0f + expf(-vg)) * vu;
+      }
+    } else if (tid < 256) {
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < kRkWaves; ++w) v += red[buf][w][tid];
-      const int n = (u / S) * 16 + no;
+      const int n = (u / S) * TN + no;
       if (mo < g.M && n < g.N) {
         if constexpr (TOP2) {
           if (logits != nullptr) logits[static_cast<int64_t>(mo) * g.N + n] = v;
@@ -738,12 +763,34 @@ hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, fl
   a.chunks_per_split = p.cps;
   const dim3 grid(p.grid), block(64 * kRkWaves);
   if (top2 != nullptr) {
-    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, true>), grid, block, 0, st, a, top2, logits);
-    else hipLaunchKernelGGL((gemm_rk_kernel<4, true>), grid, block, 0, st, a, top2, logits);
+    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_TOP2>), grid, block, 0, st, a, top2, logits);
+    else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_TOP2>), grid, block, 0, st, a, top2, logits);
   } else {
-    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, false>), grid, block, 0, st, a, nullptr, nullptr);
-    else hipLaunchKernelGGL((gemm_rk_kernel<4, false>), grid, block, 0, st, a, nullptr, nullptr);
+    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_PART>), grid, block, 0, st, a, nullptr, nullptr);
+    else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_PART>), grid, block, 0, st, a, nullptr, nullptr);
   }
+  return hipGetLastError();
+}
+
+GemmPlan plan_gemm_rk_swiglu(int M, int F, int K) {
+  GemmPlan p = plan_gemm_rk(M, 2 * F, K, true);   // a single K split
+  if (!p.rk) return p;
+  p.ntiles = (F + 7) / 8;
+  if (p.grid > p.ntiles) p.grid = p.ntiles;
+  return p;
+}
+
+hipError_t launch_gemm_rk_swiglu(const GemmArgs& a0, const GemmPlan& p, float* s_out, hipStream_t st) {
+  if (!p.rk || p.S != 1 || a0.a_cols % (32 * p.ks) != 0) return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  a.S = 1;
+  a.ntiles = p.ntiles;
+  a.mtiles = 1;
+  a.chunks_per_split = p.cps;
+  a.part = s_out;
+  const dim3 grid(p.grid), block(64 * kRkWaves);
+  if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_SWIGLU>), grid, block, 0, st, a, nullptr, nullptr);
+  else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_SWIGLU>), grid, block, 0, st, a, nullptr, nullptr);
   return hipGetLastError();
 }
 

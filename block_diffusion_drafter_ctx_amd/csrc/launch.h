@@ -60,6 +60,11 @@ GemmPlan plan_gemm_rk(int M, int N, int K, bool top2);
 // of every row to top2 [p.grid][M][3] (value, index bits, runner-up) and, when
 // logits != nullptr, the logits [M][N].
 hipError_t launch_gemm_rk(const GemmArgs& a, const GemmPlan& p, float* top2, float* logits, hipStream_t st);
+// FFN gate/up with SwiGLU fused: W is the stacked [gate (F rows); up (F rows)]
+// weight, a.N = F; writes s_out[m][f] = silu(gate) * up.  plan.rk is false when
+// the shape does not qualify (the caller then runs the GEMM and swiglu apart).
+GemmPlan plan_gemm_rk_swiglu(int M, int F, int K);
+hipError_t launch_gemm_rk_swiglu(const GemmArgs& a, const GemmPlan& p, float* s_out, hipStream_t st);
 
 // Sum the split-K partials of logits [S][M][N] per 512-column tile, optionally
 // store the logits, and write each (tile, row) top-2 to top2 [ntiles][M][3].
