@@ -613,46 +613,63 @@ int device_cus() {
 
 }  // namespace
 
-// Tile = 16 rows per wave x WAVES.  The split-K count S is chosen by a small
-// cost model: the persistent grid (workgroups resident at once: 2 per CU with a
-// 64 KB activation slice, 1 with 128 KB, rounded down to a multiple of S) works
-// through S * tiles units, so the time is ~ rounds * (k steps per unit + a fixed
-// per-unit overhead); the K range of a unit must fit the LDS slice.  Ties go to
-// the smaller S (fewer partial sums).
+// Tile = 16 rows per wave x WAVES.  The split-K count S and the wave count are
+// chosen by a small cost model.  The persistent grid (workgroups resident at
+// once: 2 per CU with a 64 KB activation slice and 8 waves, 1 with 128 KB and
+// 16 waves, rounded down to a multiple of S) works through S * tiles units of
+// cps k-steps each; a wave streams its k-steps in groups of kStreamU loads, so a
+// unit costs ceil(cps / U) * U steps plus a fixed per-unit overhead.  The HBM
+// stream is shared, so a workgroup that runs out of units leaves its bandwidth
+// to the others: the estimate is the mean work per workgroup plus a quarter of
+// the gap to the busiest one.  Ties prefer fewer rounds, then 16 waves for a
+// single round (one contiguous unit per CU) and 8 waves otherwise (more
+// workgroups to balance), then fewer splits.  The K range of a unit must fit
+// the LDS slice.  wide = true restricts the choice to 16 waves.
 GemmPlan plan_gemm_mfma(int M, int N, int K, GemmAKind ak, bool wide) {
-  GemmPlan p;
-  p.MT = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
-  p.mtiles = (M + p.MT - 1) / p.MT;
-  p.waves = wide ? 16 : 8;
+  GemmPlan best;
+  best.MT = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
+  best.mtiles = (M + best.MT - 1) / best.MT;
   const int hl = ak == A_F32_SPLIT ? 2 : 1;
-  const int kr_max = (wide ? 65536 : 32768) / p.MT / hl;          // k values the LDS slice holds
-  p.ntiles = (N + 16 * p.waves - 1) / (16 * p.waves);
   const int ksteps = K / 32;
-  const int tiles = p.ntiles * p.mtiles;
-  const int cap = device_cus() * (wide ? 1 : 2);
-  const int overhead = env_int("DFLASH_GEMM_UNIT_OVERHEAD", 4);  // in k steps
-  const int min_cps = 1;
-  const int max_cps = kr_max / 32;
-  long best_cost = -1;
-  for (int cps = max_cps < ksteps ? max_cps : ksteps; cps >= min_cps; --cps) {
-    const int S = (ksteps + cps - 1) / cps;
-    if ((ksteps + S - 1) / S != cps) continue;                     // each S once, with its smallest cps
-    int grid = cap / S * S;
-    if (grid < S) grid = S;
-    const long units = static_cast<long>(S) * tiles;
-    const long used = units < grid ? units : grid;
-    const long rounds = (units + used - 1) / used;
-    const long cost = rounds * (cps + overhead);
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      p.cps = cps;
-      p.S = S;
-      p.grid = static_cast<int>(used);
+  const int overhead = env_int("DFLASH_GEMM_UNIT_OVERHEAD", 4);   // in k steps
+  double best_cost = -1.0;
+  long best_rounds = 0;
+  for (int waves = wide ? 16 : 8; waves <= 16; waves += 8) {
+    const int kr_max = (waves == 16 ? 65536 : 32768) / best.MT / hl;   // k values the LDS slice holds
+    const int ntiles = (N + 16 * waves - 1) / (16 * waves);
+    const long tiles = static_cast<long>(ntiles) * best.mtiles;
+    const int cap = device_cus() * (waves == 16 ? 1 : 2);
+    const int max_cps = kr_max / 32;
+    for (int cps = max_cps < ksteps ? max_cps : ksteps; cps >= 1; --cps) {
+      const int S = (ksteps + cps - 1) / cps;
+      if ((ksteps + S - 1) / S != cps) continue;                    // each S once, with its smallest cps
+      int grid = cap / S * S;
+      if (grid < S) grid = S;
+      const long units = static_cast<long>(S) * tiles;
+      const long used = units < grid ? units : grid;
+      const long rounds = (units + used - 1) / used;
+      const long per_unit = (cps + kStreamU - 1) / kStreamU * kStreamU + overhead;
+      const double mean = static_cast<double>(units) * per_unit / used;
+      const double cost = mean + (rounds * per_unit - mean) / 4.0;
+      bool take = best_cost < 0 || cost < best_cost - 1e-9;
+      if (!take && cost <= best_cost + 1e-9) {
+        if (rounds != best_rounds) take = rounds < best_rounds;
+        else if (waves != best.waves) take = (rounds == 1) == (waves == 16);
+      }
+      if (take) {
+        best_cost = cost;
+        best_rounds = rounds;
+        best.waves = waves;
+        best.ntiles = ntiles;
+        best.cps = cps;
+        best.S = S;
+        best.grid = static_cast<int>(used);
+      }
     }
   }
-  p.nchunks = ksteps;
-  p.part_floats = static_cast<size_t>(p.S) * M * N;
-  return p;
+  best.nchunks = ksteps;
+  best.part_floats = static_cast<size_t>(best.S) * M * N;
+  return best;
 }
 
 GemmPlan plan_gemm_tiled(int M, int N, int K) {
