@@ -33,8 +33,8 @@ METRIC = "drafted gamma=16 blocks/sec + draft fwd us at 1 GPU; % HBM BW / % MFMA
 # FETCH_SIZE reads 0.5x the copy's bytes, WRITE_SIZE 1.0x.  Valid only for the
 # default workload and only while the GEMM sources hash to ``src``; otherwise
 # the traffic is reported as null.
-LM_HEAD_COUNTERS = {"src": "8a509942cfc6baf5", "config": 2, "cache": "f32",
-                    "fetch_kib": 622301.5, "write_kib": 28717.4, "fetch_scale": 1.9998, "write_scale": 1.0}
+LM_HEAD_COUNTERS = {"src": "ab24c224a24221ce", "config": 2, "cache": "f32",
+                    "fetch_kib": 608752.4, "write_kib": 52.0, "fetch_scale": 1.9998, "write_scale": 1.0}
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/launch.h")
 
 
@@ -275,9 +275,10 @@ def main():
         "context_mfma_frac": round(ctx_flops / (context_us * 1e-6) / 1e12 / RF.MFMA_BF16_TFLOPS, 4),
         "per_kernel": per_kernel,
         "roofline": {
-            "kernel": "gemm_stream_kernel<16, 1, 16, 2048> (LM-head weight stream, 151936 x 4096 bf16 against "
-                      "the 15 mask rows split hi/lo), one launch per step, HIP events recorded around that "
-                      "launch on the library stream by dflash_profile_events",
+            "kernel": "gemm_rk_kernel<8, RK_TOP2> (LM head: 151936 x 4096 bf16 streamed once against the 15 "
+                      "mask rows held in registers as bf16 hi + lo, logits reduced in-kernel to a top-2 per "
+                      "workgroup), one launch per step, HIP events recorded around that launch on the library "
+                      "stream by dflash_profile_events",
             "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": RF.HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(lm_gbs / RF.HBM_PEAK_GBS, 4), "traffic": lm_head_traffic(args.config, cfg.cache_dtype),
             "bytes_per_launch": lm_bytes, "us_per_launch": round(lm_us, 2),
