@@ -230,23 +230,25 @@ constexpr int kRkMinN = 16384;   // weight rows below which the split-K streamin
 
 enum RkEpilogue { RK_PART = 0, RK_TOP2 = 1, RK_SWIGLU = 2 };
 
-template <int KS, int EP>
+template <int KS, int EP, int T>
 __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, float* top2, float* logits) {
   constexpr bool TOP2 = EP == RK_TOP2;
   constexpr int TN = EP == RK_SWIGLU ? 8 : 16;   // outputs per tile
-  __shared__ float red[2][kRkWaves][256];
+  static_assert(EP == RK_PART || T == 1, "fused epilogues stream one tile at a time");
+  __shared__ float red[2][kRkWaves][T][256];
   __shared__ float tv1[4][16], tv2[4][16];
   __shared__ int ti1[4][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = g.S;
   const int units = S * g.ntiles;
   const int P = gridDim.x;
-  int u = blockIdx.x;
-  if (u >= units) return;                     // uniform per workgroup
-  const int sp = u % S;                       // P % S == 0: the split never changes
+  const int u0 = blockIdx.x;
+  if (u0 >= units) return;                    // uniform per workgroup
+  const int sp = u0 % S;                      // P % S == 0: the split never changes
   const int kwave = sp * (32 * KS * kRkWaves) + wave * (32 * KS);
   const int kl = kwave + 8 * (lane >> 4);
   auto wrow = [&](int uu) {
+    uu = uu < units ? uu : u0;                // past the last unit: re-read a valid one (result dropped)
     int n;
     if constexpr (EP == RK_SWIGLU) {
       // lanes 0-7: gate rows 8t.., lanes 8-15: up rows F + 8t.. (rows past F clamped, results dropped)
@@ -257,11 +259,15 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
     const int64_t r = static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg;
     return static_cast<const uint16_t*>(g.w) + r * g.w_ld + kl;
   };
-  uint4 wb[KS];
-  const uint16_t* wp = wrow(u);
+  // group q holds units u0 + P (T q + t), t < T; its weights stream through wb
+  uint4 wb[T][KS];
 #pragma unroll
-  for (int x = 0; x < KS; ++x) wb[x] = *reinterpret_cast<const uint4*>(wp + x * 32);
-  __builtin_amdgcn_sched_barrier(0);          // the first tile's weights go out before the activation loads
+  for (int t = 0; t < T; ++t) {
+    const uint16_t* wp = wrow(u0 + P * t);
+#pragma unroll
+    for (int x = 0; x < KS; ++x) wb[t][x] = *reinterpret_cast<const uint4*>(wp + x * 32);
+  }
+  __builtin_amdgcn_sched_barrier(0);          // the first tiles' weights go out before the activation loads
 
   uint4 bh[KS], bl[KS];
   {
@@ -285,31 +291,40 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
     }
   }
 
-  // reduction thread tid < 256 owns output (n = 16 * tile + 4 * (ln / 16) + r, m = ln % 16), ln = tid / 4
+  // reduction thread tid < 256 owns output (n = TN * tile + 4 * (ln / 16) + r, m = ln % 16), ln = tid / 4
   const int ln = tid >> 2;
   const int mo = ln & 15, no = 4 * (ln >> 4) + (tid & 3);
   Top2 best{-INFINITY, 0x7fffffff, -INFINITY};
   int buf = 0;
-  for (;;) {
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int nu = u + P;
-    const bool more = nu < units;             // uniform per workgroup
-    if (more) {
-      const uint16_t* np = wrow(nu);
+  for (int q = 0;; ++q) {
+    const int ub = u0 + P * T * q;
+    const bool more = ub + P * T < units;     // uniform per workgroup
+    f32x4_t acc[T];
 #pragma unroll
-      for (int x = 0; x < KS; ++x) {
-        acc = mfma16x16x32(wb[x], bh[x], acc);
-        acc = mfma16x16x32(wb[x], bl[x], acc);
-        wb[x] = *reinterpret_cast<const uint4*>(np + x * 32);
+    for (int t = 0; t < T; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint16_t* np = wrow(ub + P * T + P * t);
+#pragma unroll
+        for (int x = 0; x < KS; ++x) {
+          acc[t] = mfma16x16x32(wb[t][x], bh[x], acc[t]);
+          acc[t] = mfma16x16x32(wb[t][x], bl[x], acc[t]);
+          wb[t][x] = *reinterpret_cast<const uint4*>(np + x * 32);
+        }
       }
     } else {
 #pragma unroll
-      for (int x = 0; x < KS; ++x) {
-        acc = mfma16x16x32(wb[x], bh[x], acc);
-        acc = mfma16x16x32(wb[x], bl[x], acc);
-      }
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int x = 0; x < KS; ++x) {
+          acc[t] = mfma16x16x32(wb[t][x], bh[x], acc[t]);
+          acc[t] = mfma16x16x32(wb[t][x], bl[x], acc[t]);
+        }
     }
-    *reinterpret_cast<float4*>(&red[buf][wave][lane * 4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      *reinterpret_cast<float4*>(&red[buf][wave][t][lane * 4]) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
     __syncthreads();
     if constexpr (EP == RK_SWIGLU) {
       // thread tid < 128 holds gate output j of row m at red index tid and the
@@ -318,29 +333,34 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
         float vg = 0.f, vu = 0.f;
 #pragma unroll 4
         for (int w = 0; w < kRkWaves; ++w) {
-          vg += red[buf][w][tid];
-          vu += red[buf][w][tid + 128];
+          vg += red[buf][w][0][tid];
+          vu += red[buf][w][0][tid + 128];
         }
-        const int f = (u / S) * TN + no;       // no < 8 for tid < 128
+        const int f = (ub / S) * TN + no;      // no < 8 for tid < 128
         if (mo < g.M && f < g.N) g.part[static_cast<int64_t>(mo) * g.N + f] = vg / (1.0f + expf(-vg)) * vu;
       }
     } else if (tid < 256) {
-      float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < kRkWaves; ++w) v += red[buf][w][tid];
-      const int n = (u / S) * TN + no;
-      if (mo < g.M && n < g.N) {
-        if constexpr (TOP2) {
-          if (logits != nullptr) logits[static_cast<int64_t>(mo) * g.N + n] = v;
-          best = top2_push(best, v, n);
-        } else {
-          g.part[(static_cast<int64_t>(sp) * g.M + mo) * g.N + n] = v;
+      for (int t = 0; t < T; ++t) {
+        const int uu = ub + P * t;
+        if (uu < units) {
+          float v = 0.f;
+#pragma unroll 4
+          for (int w = 0; w < kRkWaves; ++w) v += red[buf][w][t][tid];
+          const int n = (uu / S) * TN + no;
+          if (mo < g.M && n < g.N) {
+            if constexpr (TOP2) {
+              if (logits != nullptr) logits[static_cast<int64_t>(mo) * g.N + n] = v;
+              best = top2_push(best, v, n);
+            } else {
+              g.part[(static_cast<int64_t>(sp) * g.M + mo) * g.N + n] = v;
+            }
+          }
         }
       }
     }
     buf ^= 1;
     if (!more) break;
-    u = nu;
   }
 
   if constexpr (TOP2) {
@@ -762,10 +782,36 @@ GemmPlan plan_gemm_rk(int M, int N, int K, bool top2) {
   return p;
 }
 
+// Register-K for a short weight: 2 k-steps per wave (a K range of 1024 per
+// workgroup, S = K / 1024 splits) and two tiles in flight per wave, so that a
+// workgroup reads only 64 KB of the activation block while its stream of 16 KB
+// weight pieces stays deep.
+GemmPlan plan_gemm_rk_short(int M, int N, int K) {
+  GemmPlan p;
+  if (M < 1 || M > 16 || K % (32 * 2 * kRkWaves) != 0 || env_int("DFLASH_GEMM_NO_RK", 0) != 0) return p;
+  p.rk = true;
+  p.ks = 2;
+  p.S = K / (32 * 2 * kRkWaves);
+  p.MT = 16;
+  p.mtiles = 1;
+  p.ntiles = (N + 15) / 16;
+  p.cps = 2 * kRkWaves;
+  p.nchunks = K / 32;
+  const long units = static_cast<long>(p.S) * p.ntiles;
+  int grid = device_cus() / p.S * p.S;
+  if (grid > kRkMaxGrid) grid = kRkMaxGrid / p.S * p.S;
+  if (grid < p.S) grid = p.S;
+  p.grid = static_cast<int>(units < grid ? units : grid);
+  p.part_floats = static_cast<size_t>(p.S) * M * N;
+  return p;
+}
+
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
   if (ak == A_F32_SPLIT && M <= 16) {
     const GemmPlan r = plan_gemm_rk(M, N, K, false);
     if (r.rk && r.S == 1) return r;
+    const GemmPlan q = plan_gemm_rk_short(M, N, K);
+    if (q.rk) return q;
   }
   if (M > 64 && K % kTileK == 0 && env_int("DFLASH_GEMM_NO_TILED", 0) == 0) return plan_gemm_tiled(M, N, K);
   return plan_gemm_mfma(M, N, K, ak, wide);
@@ -780,11 +826,12 @@ hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, fl
   a.chunks_per_split = p.cps;
   const dim3 grid(p.grid), block(64 * kRkWaves);
   if (top2 != nullptr) {
-    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_TOP2>), grid, block, 0, st, a, top2, logits);
-    else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_TOP2>), grid, block, 0, st, a, top2, logits);
+    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_TOP2, 1>), grid, block, 0, st, a, top2, logits);
+    else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_TOP2, 1>), grid, block, 0, st, a, top2, logits);
   } else {
-    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_PART>), grid, block, 0, st, a, nullptr, nullptr);
-    else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_PART>), grid, block, 0, st, a, nullptr, nullptr);
+    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_PART, 1>), grid, block, 0, st, a, nullptr, nullptr);
+    else if (p.ks == 4) hipLaunchKernelGGL((gemm_rk_kernel<4, RK_PART, 1>), grid, block, 0, st, a, nullptr, nullptr);
+    else hipLaunchKernelGGL((gemm_rk_kernel<2, RK_PART, 2>), grid, block, 0, st, a, nullptr, nullptr);
   }
   return hipGetLastError();
 }
@@ -806,8 +853,8 @@ hipError_t launch_gemm_rk_swiglu(const GemmArgs& a0, const GemmPlan& p, float* s
   a.chunks_per_split = p.cps;
   a.part = s_out;
   const dim3 grid(p.grid), block(64 * kRkWaves);
-  if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_SWIGLU>), grid, block, 0, st, a, nullptr, nullptr);
-  else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_SWIGLU>), grid, block, 0, st, a, nullptr, nullptr);
+  if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_SWIGLU, 1>), grid, block, 0, st, a, nullptr, nullptr);
+  else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_SWIGLU, 1>), grid, block, 0, st, a, nullptr, nullptr);
   return hipGetLastError();
 }
 
