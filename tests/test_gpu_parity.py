@@ -58,11 +58,15 @@ def test_register_k_shapes():
     # one sequence of gamma = 16: 16 block rows and 15 LM-head rows, D = 2048
     # (4 k-steps per wave), a gate/up weight of 2F = 16384 rows and an odd
     # vocabulary (ragged last tile) take the register-K GEMM, with the LM-head
-    # top-2 epilogue; a 2-wide batch of the same shape takes the other kernels
+    # top-2 and SwiGLU epilogues; the short weights take its split-K form
     log("register-K shapes: D=2048, 2F=16384, V=20001, batch 1")
     cfg = small(cid=109, D=2048, L=1, Hq=16, Hkv=4, d=128, F=8192, V=20001, B=1, ctx=(256,), iters=2)
     Workload(cfg, 16, 2, override=True).run()
     Workload(shrink(cfg, cid=110), 16, 1).run()
+    # partial row blocks: 5 block rows / 4 LM-head rows (rows past M masked),
+    # and a 2-sequence batch of 7 (14 rows) through the same kernels
+    Workload(shrink(cfg, cid=111, gammas=(5,)), 5, 1, override=True).run()
+    Workload(shrink(cfg, cid=112, B=2, ctx=(40, 300), gammas=(7,)), 7, 1, override=True).run()
 
 
 def test_config1_f32():
