@@ -168,15 +168,28 @@ size_t fuse_ws(const dflash_dims* d, int max_rows) {
   return best ? align_up(best * 4) : 0;
 }
 
+// Row passes of inject that take the tiled GEMM with an fp32 H_t split first
+// into bf16 hi / lo planes (placed after the partial sums).
+bool inject_splits(const dflash_dims* d, int M) {
+  return d->dtype == DFLASH_BF16 && ctx_a_kind(d) == A_F32_SPLIT &&
+         plan_gemm(M, 2 * d->L * d->Hkv * d->head_dim, d->D, A_F32_SPLIT, false).tiled;
+}
+
+GemmAKind inject_kind(const dflash_dims* d, int M) { return inject_splits(d, M) ? A_BF16_HILO : ctx_a_kind(d); }
+
 size_t inject_ws(const dflash_dims* d, int max_rows) {
-  size_t best = 0;
+  size_t best = 0, planes = 0;
   const int N = 2 * d->L * d->Hkv * d->head_dim;
   const int hi = max_rows < kRowBlock ? max_rows : kRowBlock;
   for (int M = 1; M <= hi; ++M) {
-    const size_t f = gemm_part_floats(d, M, N, d->D, ctx_a_kind(d));
+    const size_t f = gemm_part_floats(d, M, N, d->D, inject_kind(d, M));
     if (f > best) best = f;
+    if (inject_splits(d, M)) {
+      const size_t pl = 2 * align_up(static_cast<size_t>(M) * d->D * 2);
+      if (pl > planes) planes = pl;
+    }
   }
-  return best ? align_up(best * 4) : 0;
+  return best || planes ? align_up(best * 4) + planes : 0;
 }
 
 struct DraftWs {
@@ -422,11 +435,20 @@ dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w,
     g.part = part;
     int S = 1;
     if (bf) {
-      // an fp32 H_t is split hi + lo against the bf16 weights like any fp32 activation
-      const GemmPlan p = plan_gemm(M, N, D, ctx_a_kind(dims), false);
+      // an fp32 H_t is split hi + lo against the bf16 weights like any fp32
+      // activation: on the fly, or (many rows, tiled GEMM) once into two planes
+      const GemmAKind kind = inject_kind(dims, M);
+      const GemmPlan p = plan_gemm(M, N, D, kind, false);
       S = p.S;
+      if (kind == A_BF16_HILO) {
+        uint16_t* hi = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align_up(p.part_floats * 4));
+        uint16_t* lo = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(hi) + align_up(static_cast<size_t>(M) * D * 2));
+        DF_HIP(launch_split_hilo(static_cast<const float*>(g.a_src[0]), D, M, D, hi, lo, s));
+        for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = hi;
+        g.a_lo = lo;
+      }
       const int ps = prof_begin(DFLASH_PROF_INJECT, s);
-      DF_HIP(launch_gemm_mfma(g, ctx_a_kind(dims), p, s));
+      DF_HIP(launch_gemm_mfma(g, kind, p, s));
       prof_end(ps, s);
     } else {
       DF_HIP(launch_gemm_f32(g, s));

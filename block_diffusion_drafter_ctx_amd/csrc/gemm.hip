@@ -395,6 +395,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
 // reads), double-buffered, with the next tile's global loads in flight while
 // the current one is multiplied.  grid = (N / 128, M / 128, splits).
 constexpr int kTileN = 128, kTileM = 128, kTileK = 64;
+constexpr int kTileNLds = 256;   // weight rows per tile of the LDS-direct kernel (8 waves)
 
 template <int AK>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
@@ -531,6 +532,169 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
       }
     }
   }
+}
+
+// ------------------------------------------------------- tiled path, LDS-direct
+// The same 128 x 128 x 64 tile and 2 x 2 wave layout, fed by gfx950's
+// global-to-LDS loads: each wave-wide 16-byte load lands lane l at LDS base +
+// 16 l, so pointing lane l at the element that MFMA lane l needs writes a whole
+// fragment (16 rows x 32 k) in fragment order with no register staging and no
+// conversion.  NSTAGE k-tiles live in LDS: while tile kt is multiplied, tiles
+// kt + 1 .. kt + NSTAGE - 1 are in flight.  One barrier per k-tile: the buffer
+// refilled at iteration kt was last read at kt - 1, before that barrier.  The
+// loads are issued unconditionally (past the end of the K range they repeat
+// the last tile) so every iteration waits on an exact count.  A is exact bf16
+// (HL = 1) or the hi and lo planes of an fp32 matrix (HL = 2, two MFMAs per
+// product).
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One wave-wide 16-byte global-to-LDS load: lane l reads src (its own address)
+// and lands at LDS lds_frag + 16 l (lds_frag uniform over the wave).  Issued as
+// inline assembly so that the compiler does not treat every later LDS read as
+// depending on it (it would wait for all loads in flight); the kernel waits
+// on exact counts itself.
+__device__ __forceinline__ void load_frag_to_lds(const void* src, uint4* lds_frag) {
+  const unsigned la = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)lds_frag)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(la) : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt = n (others at their maximum): gfx9 encoding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int HL, int NSTAGE, int TN>
+__global__ __launch_bounds__(TN * 2) void gemm_tile_lds_kernel(GemmArgs g) {
+  constexpr int NW = TN / 64 * 2;                           // waves: (TN / 64) x 2 of 64 x 64 each
+  constexpr int WFR = (TN / 16) * (kTileK / 32);            // W fragments per tile
+  constexpr int AFR = (kTileM / 16) * (kTileK / 32) * HL;   // A fragments per tile
+  constexpr int NFR = WFR + AFR;
+  constexpr int BUF = NFR * 64;                             // uint4 per stage
+  constexpr int LPW = NFR / NW;                             // fragment loads per wave per stage
+  static_assert(NFR % NW == 0, "fragments split evenly over the waves");
+  extern __shared__ uint4 lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave % (TN / 64), wm = wave / (TN / 64);
+  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * kTileM;
+  const int split = blockIdx.z;
+  const int ktiles = g.K / kTileK;
+  const int kt_begin = split * g.chunks_per_split;
+  const int kt_end = min(ktiles, kt_begin + g.chunks_per_split);
+  if (kt_begin >= kt_end) return;                           // uniform per workgroup
+  const int nk = kt_end - kt_begin;
+
+  // fragment f = wave + NW i of a stage: W fragments first (row group f / 2,
+  // k-step f % 2), then A (row group, k-step, plane); per lane: the element
+  // offset of its row (W: into w; A: into its source) and of its k position
+  int64_t roff[LPW];
+  int koff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int f = wave + NW * i;
+    if (f < WFR) {
+      const int n = min(n0 + (f >> 1) * 16 + (lane & 15), g.N - 1);   // rows past N: results dropped
+      roff[i] = (static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg) * g.w_ld;
+      koff[i] = (f & 1) * 32 + 8 * (lane >> 4);
+    } else {
+      const int rest = (f - WFR) / HL;
+      const int m = min(m0 + (rest >> 1) * 16 + (lane & 15), g.M - 1); // rows past M: results dropped
+      roff[i] = a_row_off(g, m);
+      koff[i] = (rest & 1) * 32 + 8 * (lane >> 4);
+    }
+  }
+  const uint16_t* wbase = static_cast<const uint16_t*>(g.w);
+  auto issue = [&](int t, int stage) {                      // t: k-tile index within [0, nk)
+    const int kb = (kt_begin + min(t, nk - 1)) * kTileK;
+    // a 64-wide k tile never straddles A sources (a_cols % 64 == 0)
+    const int s = kb / g.a_cols, col = kb - s * g.a_cols;
+    const uint16_t* ahi = pick_src<uint16_t>(g, s) + col;
+    const uint16_t* alo = HL == 2 ? static_cast<const uint16_t*>(g.a_lo) + col : ahi;   // HL == 2: one source
+    uint4* base = lds + stage * BUF;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int f = wave + NW * i;                           // uniform per wave
+      const uint16_t* p;
+      if (f < WFR) p = wbase + roff[i] + kb + koff[i];
+      else p = (((f - WFR) % HL) ? alo : ahi) + roff[i] + koff[i];
+      load_frag_to_lds(p, base + f * 64);
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint4* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 wf[4], af[4], al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wf[i] = buf[((wn * 4 + i) * 2 + ks) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        af[j] = buf[WFR * 64 + (((wm * 4 + j) * 2 + ks) * HL) * 64 + lane];
+        if constexpr (HL == 2) al[j] = buf[WFR * 64 + (((wm * 4 + j) * 2 + ks) * HL + 1) * 64 + lane];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = mfma16x16x32(wf[i], af[j], acc[i][j]);
+          if constexpr (HL == 2) acc[i][j] = mfma16x16x32(wf[i], al[j], acc[i][j]);
+        }
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st) issue(st, st);
+  for (int t = 0; t < nk; ++t) {
+    wait_vmcnt<(NSTAGE - 2) * LPW>();                        // this wave's loads of tile t landed
+    // ... and every other wave's.  A bare s_barrier: a fenced __syncthreads
+    // would also wait for the later tiles still in flight.  The empty asm
+    // statements keep the compiler from moving LDS accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(t + NSTAGE - 1, (t + NSTAGE - 1) % NSTAGE);
+    compute(lds + (t % NSTAGE) * BUF);
+  }
+  wait_vmcnt<0>();                                          // the trailing repeated tiles
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + wn * 64 + i * 16 + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 64 + j * 16 + (lane & 15);
+      if (m >= g.M) continue;
+      float* out = g.part + (static_cast<int64_t>(split) * g.M + m) * g.N + n;
+      if (n + 3 < g.N && (g.N & 3) == 0) {
+        *reinterpret_cast<float4*>(out) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < g.N) out[r] = acc[i][j][r];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void split_hilo_kernel(const float* x, int64_t ld, int M, int K, uint16_t* hi,
+                                                          uint16_t* lo) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+  if (i >= static_cast<int64_t>(M) * K) return;
+  const int m = static_cast<int>(i / K), k = static_cast<int>(i % K);   // K % 8 == 0
+  const float* p = x + m * ld + k;
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint4 h, l;
+  split8(v, h, l);
+  *reinterpret_cast<uint4*>(hi + i) = h;
+  *reinterpret_cast<uint4*>(lo + i) = l;
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -692,14 +856,33 @@ GemmPlan plan_gemm_mfma(int M, int N, int K, GemmAKind ak, bool wide) {
   return best;
 }
 
-GemmPlan plan_gemm_tiled(int M, int N, int K) {
+GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
   GemmPlan p;
   p.tiled = true;
   p.MT = kTileM;
   p.mtiles = (M + kTileM - 1) / kTileM;
-  p.ntiles = (N + kTileN - 1) / kTileN;
+  const int tn = ak == A_F32_SPLIT ? kTileN : kTileNLds;   // register-staged or LDS-direct kernel
+  p.ntiles = (N + tn - 1) / tn;
   const int ktiles = K / kTileK;
   const int tiles = p.mtiles * p.ntiles;
+  if (ak != A_F32_SPLIT) {
+    // LDS-direct kernel: one workgroup per CU (its stages fill most of the
+    // LDS).  Split K so that the last round of workgroups is not left mostly
+    // idle: the cost of S splits is ceil(tiles * S / CUs) rounds of 1 / S of
+    // the K range; the smallest S of least cost wins (each split adds an
+    // M x N fp32 partial for the consumer to read).
+    const int cus = device_cus();
+    int best_s = 1;
+    double best_cost = 1e30;
+    for (int s = 1; s <= 4 && s <= ktiles / 4; ++s) {
+      const double cost = static_cast<double>((static_cast<long>(tiles) * s + cus - 1) / cus) / s;
+      if (cost < best_cost - 1e-9) best_cost = cost, best_s = s;
+    }
+    p.cps = (ktiles + best_s - 1) / best_s;
+    p.S = (ktiles + p.cps - 1) / p.cps;
+    p.part_floats = static_cast<size_t>(p.S) * M * N;
+    return p;
+  }
   const int target = 2 * device_cus();
   int want = (target + tiles - 1) / tiles;
   if (want < 1) want = 1;
@@ -712,6 +895,37 @@ GemmPlan plan_gemm_tiled(int M, int N, int K) {
 
 hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p, hipStream_t st) {
   if (p.rk) return ak == A_F32_SPLIT ? launch_gemm_rk(a0, p, nullptr, nullptr, st) : hipErrorInvalidValue;
+  if (p.tiled && ak != A_F32_SPLIT) {
+    GemmArgs a = a0;
+    a.chunks_per_split = p.cps;
+    const dim3 grid(p.ntiles, p.mtiles, p.S);
+    if (a.a_cols % kTileK != 0 || p.MT != kTileM) return hipErrorInvalidValue;
+    constexpr int TN = kTileNLds;
+    if (ak == A_BF16) {
+      constexpr int NS = 3;
+      const size_t lds = static_cast<size_t>(NS) * ((TN / 16) * 2 + (kTileM / 16) * 2) * 64 * sizeof(uint4);
+      static bool set = false;
+      if (!set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<1, NS, TN>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+        set = true;
+      }
+      hipLaunchKernelGGL((gemm_tile_lds_kernel<1, NS, TN>), grid, dim3(TN * 2), lds, st, a);
+    } else {
+      constexpr int NS = 2;
+      const size_t lds = static_cast<size_t>(NS) * ((TN / 16) * 2 + (kTileM / 16) * 2 * 2) * 64 * sizeof(uint4);
+      static bool set = false;
+      if (!set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<2, NS, TN>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+        set = true;
+      }
+      hipLaunchKernelGGL((gemm_tile_lds_kernel<2, NS, TN>), grid, dim3(TN * 2), lds, st, a);
+    }
+    return hipGetLastError();
+  }
   if (p.tiled) {
     GemmArgs a = a0;
     a.chunks_per_split = p.cps;
@@ -813,7 +1027,7 @@ GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
     const GemmPlan q = plan_gemm_rk_short(M, N, K);
     if (q.rk) return q;
   }
-  if (M > 64 && K % kTileK == 0 && env_int("DFLASH_GEMM_NO_TILED", 0) == 0) return plan_gemm_tiled(M, N, K);
+  if (M > 64 && K % kTileK == 0 && env_int("DFLASH_GEMM_NO_TILED", 0) == 0) return plan_gemm_tiled(M, N, K, ak);
   return plan_gemm_mfma(M, N, K, ak, wide);
 }
 
@@ -855,6 +1069,15 @@ hipError_t launch_gemm_rk_swiglu(const GemmArgs& a0, const GemmPlan& p, float* s
   const dim3 grid(p.grid), block(64 * kRkWaves);
   if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_SWIGLU, 1>), grid, block, 0, st, a, nullptr, nullptr);
   else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_SWIGLU, 1>), grid, block, 0, st, a, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_hilo(const float* x, int64_t ld, int M, int K, uint16_t* hi, uint16_t* lo, hipStream_t st) {
+  if (K % 8 != 0 || ld % 4 != 0) return hipErrorInvalidValue;
+  const int64_t groups = static_cast<int64_t>(M) * K / 8;
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_hilo_kernel, dim3(static_cast<unsigned>((groups + 255) / 256)), dim3(256), 0, st, x, ld, M, K,
+                     hi, lo);
   return hipGetLastError();
 }
 

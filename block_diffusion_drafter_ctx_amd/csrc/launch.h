@@ -29,9 +29,12 @@ struct GemmArgs {
   int32_t chunks_per_split;   // 32-wide k steps per split (MFMA path)
   int32_t S, ntiles, mtiles;  // work decomposition (MFMA path; set by the launcher)
   float* part;                // [S][M][N]
+  const void* a_lo;           // A_BF16_HILO: the lo plane, laid out like a_src[0] (the hi plane)
 };
 
-enum GemmAKind { A_BF16 = 0, A_F32_SPLIT = 1 };  // exact bf16 A, or fp32 A split hi/lo
+// exact bf16 A; fp32 A split hi/lo on the fly; or A given as pre-split bf16
+// hi (a_src[0]) and lo (a_lo) planes of an fp32 matrix (tiled kernel only)
+enum GemmAKind { A_BF16 = 0, A_F32_SPLIT = 1, A_BF16_HILO = 2 };
 
 struct GemmPlan {
   int MT = 16, mtiles = 1, ntiles = 1, nchunks = 1, cps = 1, S = 1, waves = 8, grid = 1;
@@ -44,8 +47,10 @@ struct GemmPlan {
 // wide = 16-wave workgroups with a 128 KB activation slice (fewer K splits for
 // very tall weights such as the LM head); otherwise 8 waves and 64 KB.
 GemmPlan plan_gemm_mfma(int M, int N, int K, GemmAKind ak, bool wide);
-// Many activation rows: 128 x 128 x 64 LDS-tiled MFMA kernel (K % 64 == 0).
-GemmPlan plan_gemm_tiled(int M, int N, int K);
+// Many activation rows: LDS-tiled MFMA kernel (K % 64 == 0), 128 activation rows
+// per tile against 128 (fp32 A split on the fly) or 256 (bf16 A, or pre-split
+// hi/lo planes) weight rows.
+GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak);
 // The plan the library uses for an M x N x K product (tiled for M > 64 when
 // K % 64 == 0, streaming otherwise).
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide);
@@ -73,6 +78,10 @@ hipError_t launch_reduce_top2(const float* part, int S, int M, int N, float* log
 
 // fp32 storage path: plain FMA GEMM, single split; writes part[0][m][n].
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
+
+// hi[m][k] = bf16(x[m][k]), lo[m][k] = bf16(x - hi) for an fp32 [M][K] matrix
+// with row stride ld (elements); hi and lo are dense [M][K].
+hipError_t launch_split_hilo(const float* x, int64_t ld, int M, int K, uint16_t* hi, uint16_t* lo, hipStream_t st);
 
 // ------------------------------------------------------------ epilogues
 // Per-sequence row table: rows [row_off[b], row_off[b+1]) of a GEMM output belong
