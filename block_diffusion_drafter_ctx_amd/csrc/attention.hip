@@ -6,25 +6,24 @@
 // Block Diffusion for Flash Speculative Decoding 논문 정리", section "KV
 // Injection 메커니즘"; bidirectional inside the block, section "추론 구조").
 //
-// gfx950 design (bf16 storage): few query rows against a long key stream, so
-// the kernel is HBM-bound and is split over keys:
+// gfx950 design: few query rows against a long key stream, so the kernels are
+// HBM-bound and split over keys:
 //   * one workgroup per (sequence, KV head, key range); one wave per 16 query
-//     rows; all waves of a workgroup read the same keys (L1/L2 shared);
-//   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16:
-//     each lane loads 16 B of a key row straight from the row-major K cache;
+//     rows, all waves sharing the key range's K/V blocks through LDS;
+//   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16;
 //     the fp32 queries (pre-scaled by log2(e)/sqrt(d)) are split into bf16
 //     hi + lo and multiplied twice;
 //   * online softmax per row with exp2; the MFMA output layout of S^T (4 keys of
-//     one row per lane) is exactly the B-operand layout P^T of the next MFMA
-//     after a fixed permutation of the 32 keys, so probabilities never leave
-//     registers;
+//     one row per lane) is the B-operand layout P^T of the value MFMA, so
+//     probabilities never leave registers;
 //   * O^T = V^T P^T reads values from the transposed V cache ([d][cap], keys
-//     contiguous) with two 8-byte loads per lane, P again split hi + lo;
+//     contiguous), P again split hi + lo;
 //   * each workgroup writes (max, sum, O) per row; a combine kernel merges the
 //     key ranges in a fixed order (log-sum-exp), so results are deterministic.
-// An fp32 KV cache (with bf16 weights) runs the same kernel with K and V split
-// into bf16 hi + lo on load (three MFMAs per product instead of two).  fp32
-// weights use a plain one-wave-per-(row, head) online-softmax kernel.
+// A bf16 cache streams K/V blocks straight into LDS (attn_dma_kernel); an fp32
+// cache stages them through registers, splitting each element once into bf16
+// hi + lo planes (attn_mfma_kernel, three MFMAs per product).  fp32 weights
+// use a plain one-wave-per-(row, head) online-softmax kernel.
 #include "common.h"
 #include "launch.h"
 
@@ -59,28 +58,6 @@ __device__ __forceinline__ void decode_item(const AttnArgs& a, int item, int& b,
 // 32, so a block never reads past its head's rows; keys at or past the end of
 // the range (unwritten rows) get zero values and -inf scores.
 template <typename TKV> struct KVStage;
-template <> struct KVStage<uint16_t> {
-  static constexpr int HL = 1;
-  struct Raw { uint4 u; };
-  static __device__ __forceinline__ Raw krow(const uint16_t* p) { return Raw{*reinterpret_cast<const uint4*>(p)}; }
-  static __device__ __forceinline__ Raw vpair(const uint16_t* p) {
-    const uint2 v0 = *reinterpret_cast<const uint2*>(p);
-    const uint2 v1 = *reinterpret_cast<const uint2*>(p + 16);
-    return Raw{make_uint4(v0.x, v0.y, v1.x, v1.y)};
-  }
-  // zero the elements whose key (k + (e / 4) * 16 + e % 4) is >= kend
-  static __device__ __forceinline__ void vmask(Raw& r, int k, int kend) {
-    uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = k + (e >> 1) * 16 + 2 * (e & 1);
-      const uint32_t lo = key < kend ? 0x0000ffffu : 0u, hi = key + 1 < kend ? 0xffff0000u : 0u;
-      w[e] &= lo | hi;
-    }
-    r.u = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  static __device__ __forceinline__ void put(uint4* dst, const Raw& r) { dst[0] = r.u; }
-};
 template <> struct KVStage<float> {
   static constexpr int HL = 2;
   struct Raw { float4 a, b; };
@@ -304,6 +281,243 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
   }
 }
 
+// ----------------------------------------------------------- bf16 cache path
+// K and V blocks go straight from HBM to LDS through gfx950's global-to-LDS
+// loads (lane l of a wave-wide 16-byte load lands at LDS base + 16 l): no
+// register staging, no conversion, and the stages in flight cost no
+// registers.  Inside a 32-key block the score tile kt takes keys in the order
+// row i -> key 8 (i / 4) + 4 kt + i % 4, so the S^T output leaves lane l (lane
+// group g = l / 16) holding keys 8 g + 4 kt + r of its query column; as the B
+// operand of the value MFMA, k-slot 8 g + e is then key 8 g + e, and the value
+// fragment of lane l is 8 consecutive keys of one row of the transposed V cache
+// (one 16-byte load, like a K fragment).  With G * gamma <= 64 query rows the
+// eight waves form two groups of four that take alternate blocks, each with its
+// own online-softmax state, merged through LDS at the end (two waves per SIMD
+// overlap one another's MFMA, softmax and LDS latency); with more rows one
+// group of eight waves takes every block.
+constexpr int kDmaStages = 3;   // LDS stages (one block per group each), two in flight
+
+template <int HD, int NG>
+__global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
+  constexpr int NW = 8, WPG = NW / NG, NST = kDmaStages;
+  constexpr int DS = HD / 32, DT = HD / 16;
+  constexpr int KFR = 2 * DS, NFR = KFR + DT;   // K and V fragments of a block
+  constexpr int LPW = NG * NFR / NW;            // loads per wave per stage
+  static_assert((NG * NFR) % NW == 0, "fragments split evenly over the waves");
+  extern __shared__ uint4 stage[];              // [NST][NG][NFR][64]
+  const int lane = threadIdx.x & 63, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave / WPG, wq = wave % WPG;
+  int b, j, sp;
+  decode_item(a, blockIdx.x, b, j, sp);
+  const int kbeg = sp * a.split_keys;
+  const int kend = min(a.nkeys[b], kbeg + a.split_keys);
+  const int nblk = (kend - kbeg + 31) / 32;     // >= 1: every key range is non-empty
+  const int nstep = (nblk + NG - 1) / NG;
+  const int row0 = blockIdx.y * 16 * WPG + wq * 16;
+  const int r = row0 + (lane & 15);
+  const bool computes = row0 < a.R;             // uniform per wave
+  const int G = a.Hq / a.Hkv;
+  const int64_t head = static_cast<int64_t>(b) * a.Hkv + j;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.kc) + head * a.cap * HD;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.vc) + head * HD * a.cap;
+  const unsigned lds0 = lds_addr(stage);
+
+  // byte offset of this lane's 16 bytes from its block's first key, for each
+  // fragment F = wave + NW i this wave loads (group F / NFR, fragment F % NFR)
+  uint32_t off[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int f = (wave + NW * i) % NFR;
+    if (f < KFR) {
+      const int kt = f / DS, ds = f % DS;
+      const int key = 8 * ((lane & 15) >> 2) + 4 * kt + (lane & 3);
+      off[i] = 2u * static_cast<uint32_t>(key * HD + ds * 32 + 8 * g4);
+    } else {
+      off[i] = 2u * static_cast<uint32_t>(((f - KFR) * 16 + (lane & 15)) * a.cap + 8 * g4);
+    }
+  }
+  // step u loads blocks NG u .. NG u + NG - 1 into stage st; past the last
+  // block it repeats the last one (so every wait has a fixed count)
+  auto issue = [&](int u, int st) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int F = wave + NW * i, f = F % NFR;
+      const int k0 = kbeg + min(NG * u + F / NFR, nblk - 1) * 32;
+      const uint16_t* base = f < KFR ? kbase + static_cast<int64_t>(k0) * HD : vbase + k0;
+      load_to_lds_sbase(off[i], base, lds0 + static_cast<unsigned>((st * NG * NFR + F) * 1024));
+    }
+  };
+
+  uint4 qh[DS], ql[DS];
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto compute = [&](const uint4* buf, int k0) {
+    uint4 kf[2][DS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) kf[kt][ds] = buf[(kt * DS + ds) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) sc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sc[kt] = mfma16x16x32(kf[kt][ds], qh[ds], sc[kt]);
+        sc[kt] = mfma16x16x32(kf[kt][ds], ql[ds], sc[kt]);
+      }
+    uint4 vf[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vf[dt] = buf[(KFR + dt) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+    float p[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[kt * 4 + e] = sc[kt][e];
+    const bool partial = k0 + 32 > kend;        // uniform: the last block of the range
+    if (partial) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (k0 + 8 * g4 + 4 * kt + e >= kend) p[kt * 4 + e] = -INFINITY;
+    }
+    float mx = p[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, p[e]);
+    const float m_new = fmaxf(m_run, max_across16(mx));   // finite: the block holds a valid key
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(p[e] - m_new);
+      ps += p[e];
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (__any(alpha != 1.0f)) {                 // skipped once every row's max has settled
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    if (partial) {                              // unwritten rows past the range: zero values
+      const int nv = kend - (k0 + 8 * g4);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        uint32_t w[4] = {vf[dt].x, vf[dt].y, vf[dt].z, vf[dt].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] &= (2 * e < nv ? 0x0000ffffu : 0u) | (2 * e + 1 < nv ? 0xffff0000u : 0u);
+        vf[dt] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    uint4 ph, pl;
+    split8(p, ph, pl);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt] = mfma16x16x32(vf[dt], ph, o[dt]);
+      o[dt] = mfma16x16x32(vf[dt], pl, o[dt]);
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) issue(st, st);
+  if (computes && r < a.R) {
+    const int h = j * G + r / a.gamma, i = r % a.gamma;
+    const float* qp = a.q + (static_cast<int64_t>(b * a.gamma + i) * a.Hq + h) * HD + 8 * g4;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qp + ds * 32);
+      const float4 x1 = *reinterpret_cast<const float4*>(qp + ds * 32 + 4);
+      float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= a.scale_log2;
+      split8(x, qh[ds], ql[ds]);
+    }
+  } else {
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) { qh[ds] = make_uint4(0, 0, 0, 0); ql[ds] = qh[ds]; }
+  }
+  for (int u = 0; u < nstep; ++u) {
+    wait_vmcnt<(NST - 2) * LPW>();              // this wave's loads of step u landed
+    bare_barrier();                             // ... and every other wave's; step u - 1 is consumed
+    issue(u + NST - 1, (u + NST - 1) % NST);
+    const int t = NG * u + grp;
+    if (computes && t < nblk) compute(stage + ((u % NST) * NG + grp) * NFR * 64, kbeg + t * 32);
+  }
+  wait_vmcnt<0>();                              // the trailing repeated blocks
+
+  float l_tot = sum_across16(l_run);
+  if constexpr (NG == 2) {
+    // group 1 hands (m, l, O) to group 0 through LDS; a group that saw no block
+    // has m = -inf, l = 0, O = 0 and weight 0
+    __syncthreads();
+    float* mo = reinterpret_cast<float*>(stage);   // [WPG][DT][64][4]
+    float* mml = mo + WPG * DT * 64 * 4;           // [WPG][64][2]
+    if (grp == 1 && computes) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(mo + ((wq * DT + dt) * 64 + lane) * 4) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+      mml[(wq * 64 + lane) * 2] = m_run;
+      mml[(wq * 64 + lane) * 2 + 1] = l_tot;
+    }
+    __syncthreads();
+    if (grp == 1 || !computes) return;
+    const float m1 = mml[(wq * 64 + lane) * 2], l1 = mml[(wq * 64 + lane) * 2 + 1];
+    const float M = fmaxf(m_run, m1);
+    const float w0 = __builtin_amdgcn_exp2f(m_run - M), w1 = __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const float4 x = *reinterpret_cast<const float4*>(mo + ((wq * DT + dt) * 64 + lane) * 4);
+      o[dt][0] = o[dt][0] * w0 + x.x * w1;
+      o[dt][1] = o[dt][1] * w0 + x.y * w1;
+      o[dt][2] = o[dt][2] * w0 + x.z * w1;
+      o[dt][3] = o[dt][3] * w0 + x.w * w1;
+    }
+    l_tot = l_tot * w0 + l1 * w1;
+    m_run = M;
+  }
+  if (computes && r < a.Rpad) {
+    float* po = a.part_o + (static_cast<int64_t>(blockIdx.x) * a.Rpad + r) * HD + 4 * g4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + dt * 16) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (g4 == 0) {
+      float* pm = a.part_ml + (static_cast<int64_t>(blockIdx.x) * a.Rpad + r) * 2;
+      pm[0] = m_run;
+      pm[1] = l_tot;
+    }
+  }
+}
+
+template <int HD, int NG>
+size_t attn_dma_lds() {
+  constexpr int DT = HD / 16, NFR = 2 * (HD / 32) + DT, WPG = 8 / NG;
+  const size_t stages = static_cast<size_t>(kDmaStages) * NG * NFR * 64 * sizeof(uint4);
+  const size_t merge = NG == 2 ? static_cast<size_t>(WPG) * DT * 64 * 16 + static_cast<size_t>(WPG) * 64 * 8 : 0;
+  return stages > merge ? stages : merge;
+}
+
+template <int HD, int NG>
+hipError_t launch_dma(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
+  const size_t lds = attn_dma_lds<HD, NG>();
+  static bool set = false;   // per instantiation
+  if (!set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_dma_kernel<HD, NG>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    set = true;
+  }
+  const int rows = 16 * 8 / NG;   // query rows per workgroup
+  hipLaunchKernelGGL((attn_dma_kernel<HD, NG>), dim3(p.items, (a.R + rows - 1) / rows), dim3(512), lds, st, a);
+  return hipGetLastError();
+}
+
 // Merge the key ranges of one (row, head): O = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
 // The split weights are computed once per row into LDS; the O loads of all
 // splits are then independent.
@@ -386,13 +600,25 @@ int waves_per_group(int R) {
 
 }  // namespace
 
-constexpr int kAttnItemTarget = 1024;
+// Work items (key ranges) per launch: about one per CU.  Each workgroup fills
+// most of a CU (eight waves; the bf16 path's stages take 96 KB of LDS), and
+// fewer, longer key ranges spend less on each range's start-up and on the
+// combine step.  The workspace bound allows up to kAttnItemMax.
+constexpr int kAttnItemMax = 1024;
+
+static int attn_item_target() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  const int t = env_int("DFLASH_ATTN_ITEMS", n);
+  return t < kAttnItemMax ? t : kAttnItemMax;
+}
 
 AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d) {
   AttnPlan p;
   int64_t total = 0;
   for (int b = 0; b < B; ++b) total += nkeys[b];
-  const int target = env_int("DFLASH_ATTN_ITEMS", kAttnItemTarget);
+  const int target = attn_item_target();
   const int min_keys = env_int("DFLASH_ATTN_MIN_KEYS", 128);
   int64_t sk = (total * Hkv + target - 1) / target;
   sk = ((sk + 31) / 32) * 32;
@@ -418,7 +644,7 @@ AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d) {
 size_t attention_part_bound(int B, int Hkv, int R, int d) {
   const int row_groups = (R + kRowsPerGroup - 1) / kRowsPerGroup;
   const int rpad = R > kRowsPerGroup ? row_groups * kRowsPerGroup : waves_per_group(R) * 16;
-  const size_t items = static_cast<size_t>(env_int("DFLASH_ATTN_ITEMS", kAttnItemTarget)) + static_cast<size_t>(B) * Hkv;
+  const size_t items = static_cast<size_t>(kAttnItemMax) + static_cast<size_t>(B) * Hkv;
   return items * rpad * (d + 2);
 }
 
@@ -435,14 +661,20 @@ hipError_t launch_attention(const AttnArgs& a0, const AttnPlan& p, bool bf16_wei
   a.Rpad = p.Rpad;
   for (int b = 0; b < a.B; ++b) { a.nsplit[b] = p.nsplit[b]; a.item_off[b] = p.item_off[b]; }
   a.item_off[a.B] = p.item_off[a.B];
-  const dim3 grid(p.items, p.row_groups);
-  const dim3 block(64 * kAttnWaves);
-  // LDS: two block buffers of (2 DS + DT) * 64 fragments, two planes for fp32
-  const size_t lds = static_cast<size_t>(2) * (a.d / 16 + a.d / 16) * 64 * (bf16_cache ? 1 : 2) * sizeof(uint4);
-  auto kern = bf16_cache ? (a.d == 128 ? attn_mfma_kernel<128, uint16_t> : attn_mfma_kernel<64, uint16_t>)
-                         : (a.d == 128 ? attn_mfma_kernel<128, float> : attn_mfma_kernel<64, float>);
-  hipLaunchKernelGGL(kern, grid, block, lds, st, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (bf16_cache) {
+    // the DMA kernel's per-lane byte offsets into one head's K or V are 32-bit
+    if (static_cast<int64_t>(a.cap) * a.d * 2 >= (int64_t{1} << 32)) return hipErrorInvalidValue;
+    const bool two = a.R <= 64;
+    e = a.d == 128 ? (two ? launch_dma<128, 2>(a, p, st) : launch_dma<128, 1>(a, p, st))
+                   : (two ? launch_dma<64, 2>(a, p, st) : launch_dma<64, 1>(a, p, st));
+  } else {
+    // LDS: two block buffers of (2 DS + DT) * 64 fragments, hi and lo planes
+    const size_t lds = static_cast<size_t>(2) * (a.d / 16 + a.d / 16) * 64 * 2 * sizeof(uint4);
+    auto kern = a.d == 128 ? attn_mfma_kernel<128, float> : attn_mfma_kernel<64, float>;
+    hipLaunchKernelGGL(kern, dim3(p.items, p.row_groups), dim3(64 * kAttnWaves), lds, st, a);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   if (stop_event != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(stop_event), st);
   hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.gamma * a.Hq), dim3(128), 0, st, a);

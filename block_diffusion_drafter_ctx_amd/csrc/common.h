@@ -65,6 +65,62 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// ------------------------------------------------------- global-to-LDS loads
+// gfx950's wave-wide 16-byte global-to-LDS load lands lane l's 16 bytes at LDS
+// address M0 + 16 l, with no register staging.  Both forms are issued as inline
+// assembly so that the compiler does not treat every later LDS read as
+// depending on them (it would wait for all loads in flight); kernels wait on
+// exact counts with wait_vmcnt.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void*)p)));
+}
+
+// lane l reads src (its own address) into LDS lds_frag + 16 l (lds_frag wave-uniform)
+__device__ __forceinline__ void load_frag_to_lds(const void* src, uint4* lds_frag) {
+  const unsigned la = lds_addr(lds_frag);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(la) : "memory", "m0");
+}
+
+// lane l reads base + voff (base wave-uniform, in scalar registers; voff a byte
+// offset) into LDS byte address m0 + 16 l
+__device__ __forceinline__ void load_to_lds_sbase(uint32_t voff, const void* base, unsigned m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0) : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt = n (the other counters at their maximum): gfx9 encoding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A workgroup barrier that waits for nothing else: the empty asm statements
+// keep the compiler from moving LDS accesses across it, and unlike
+// __syncthreads it does not wait for global-to-LDS loads still in flight.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ------------------------------------------------- lane-group reductions
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (gfx950 lane swaps:
+// permlane32_swap pairs lane l with l ^ 32, permlane16_swap pairs l with l ^ 16)
+__device__ __forceinline__ float max_across16(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_across16(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -546,25 +546,6 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
 // the last tile) so every iteration waits on an exact count.  A is exact bf16
 // (HL = 1) or the hi and lo planes of an fp32 matrix (HL = 2, two MFMAs per
 // product).
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One wave-wide 16-byte global-to-LDS load: lane l reads src (its own address)
-// and lands at LDS lds_frag + 16 l (lds_frag uniform over the wave).  Issued as
-// inline assembly so that the compiler does not treat every later LDS read as
-// depending on it (it would wait for all loads in flight); the kernel waits
-// on exact counts itself.
-__device__ __forceinline__ void load_frag_to_lds(const void* src, uint4* lds_frag) {
-  const unsigned la = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)lds_frag)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(la) : "memory", "m0");
-}
-
-// s_waitcnt with vmcnt = n (others at their maximum): gfx9 encoding
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 template <int HL, int NSTAGE, int TN>
 __global__ __launch_bounds__(TN * 2) void gemm_tile_lds_kernel(GemmArgs g) {
   constexpr int NW = TN / 64 * 2;                           // waves: (TN / 64) x 2 of 64 x 64 each
@@ -653,12 +634,7 @@ __global__ __launch_bounds__(TN * 2) void gemm_tile_lds_kernel(GemmArgs g) {
   for (int st = 0; st < NSTAGE - 1; ++st) issue(st, st);
   for (int t = 0; t < nk; ++t) {
     wait_vmcnt<(NSTAGE - 2) * LPW>();                        // this wave's loads of tile t landed
-    // ... and every other wave's.  A bare s_barrier: a fenced __syncthreads
-    // would also wait for the later tiles still in flight.  The empty asm
-    // statements keep the compiler from moving LDS accesses across it.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    bare_barrier();                                           // ... and every other wave's
     issue(t + NSTAGE - 1, (t + NSTAGE - 1) % NSTAGE);
     compute(lds + (t % NSTAGE) * BUF);
   }

@@ -48,6 +48,20 @@ def test_small_bf16_gamma_edges(gamma):
     Workload(small(cid=103, gammas=(gamma,)), gamma, 1, override=True).run()
 
 
+@pytest.mark.parametrize("gamma", [2, 5, 17, 33])
+def test_small_bf16_cache_gamma_edges(gamma):
+    # bf16 cache: G * gamma query rows per KV head of 8, 20 (two wave groups),
+    # 68 (one group of eight waves) and 132 (two row groups)
+    log(f"small bf16, bf16 cache, gamma={gamma}")
+    Workload(small(cid=109, gammas=(gamma,), cache_dtype="bf16"), gamma, 1, override=True).run()
+
+
+def test_small_head64_bf16_cache():
+    log("small bf16, head_dim 64, bf16 cache, a sequence with no context rows")
+    cfg = small(cid=110, d=64, Hq=4, Hkv=4, ctx=(0, 70), B=2, V=777 * 2, cache_dtype="bf16")
+    Workload(cfg, 8, 1, override=True).run()
+
+
 def test_small_head64_empty_context():
     log("small bf16, head_dim 64, a sequence with no context rows")
     cfg = small(cid=104, d=64, Hq=4, Hkv=4, ctx=(0, 70), B=2, V=777 * 2)
@@ -198,6 +212,13 @@ def test_bf16_storage_rounding_is_rne():
 def test_config3_full():
     cfg = CONFIGS[3]
     log("config 3 full size: 32768-row context, 1 iteration + append")
+    Workload(cfg, 16, 1).run()
+
+
+@pytest.mark.timeout(1200)
+def test_config3_full_bf16_cache():
+    cfg = shrink(CONFIGS[3], cid=303, cache_dtype="bf16")
+    log("config 3 full size with a bf16 H_t / KV cache: 32768-row context, 1 iteration + append")
     Workload(cfg, 16, 1).run()
 
 
