@@ -535,26 +535,28 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------- tiled path, LDS-direct
-// The same 128 x 128 x 64 tile and 2 x 2 wave layout, fed by gfx950's
-// global-to-LDS loads: each wave-wide 16-byte load lands lane l at LDS base +
-// 16 l, so pointing lane l at the element that MFMA lane l needs writes a whole
-// fragment (16 rows x 32 k) in fragment order with no register staging and no
-// conversion.  NSTAGE k-tiles live in LDS: while tile kt is multiplied, tiles
-// kt + 1 .. kt + NSTAGE - 1 are in flight.  One barrier per k-tile: the buffer
-// refilled at iteration kt was last read at kt - 1, before that barrier.  The
-// loads are issued unconditionally (past the end of the K range they repeat
-// the last tile) so every iteration waits on an exact count.  A is exact bf16
-// (HL = 1) or the hi and lo planes of an fp32 matrix (HL = 2, two MFMAs per
-// product).
+// 256 weight rows x 128 activation rows x 64 k per tile, eight waves of 64 x 64,
+// fed by gfx950's global-to-LDS loads (a wave-wide 16-byte load lands lane l at
+// LDS base + 16 l, no register staging).  Each load instruction brings whole
+// 128-byte lines: 8 rows x 64 k (lane l: row l / 8, 16-byte chunk l % 8) --
+// from L2 that runs 2.5x faster than MFMA-fragment order (16 rows x 64 bytes
+// per instruction).  In LDS a tile is row-major, 128 bytes per row, with chunk
+// c of row r stored at slot c ^ (r % 8): the 16-byte fragment reads of 8
+// consecutive rows then hit 8 different bank groups.  NSTAGE k-tiles are in
+// LDS at once; fragments are read one k-step ahead so that the LDS reads of the
+// next k-step are in flight while this one's MFMAs issue; stage t % NSTAGE is
+// refilled with tile t + NSTAGE right after the barrier that follows every
+// wave's last read of tile t.  Past the end of the K range the loads repeat the
+// last tile, so every wait has a fixed count.  A is exact bf16 (HL = 1) or the
+// hi and lo planes of an fp32 matrix (HL = 2, two MFMAs per product).
 template <int HL, int NSTAGE, int TN>
 __global__ __launch_bounds__(TN * 2) void gemm_tile_lds_kernel(GemmArgs g) {
   constexpr int NW = TN / 64 * 2;                           // waves: (TN / 64) x 2 of 64 x 64 each
-  constexpr int WFR = (TN / 16) * (kTileK / 32);            // W fragments per tile
-  constexpr int AFR = (kTileM / 16) * (kTileK / 32) * HL;   // A fragments per tile
-  constexpr int NFR = WFR + AFR;
-  constexpr int BUF = NFR * 64;                             // uint4 per stage
-  constexpr int LPW = NFR / NW;                             // fragment loads per wave per stage
-  static_assert(NFR % NW == 0, "fragments split evenly over the waves");
+  constexpr int WROWS = TN, AROWS = kTileM * HL;            // LDS rows per stage (A: planes stacked)
+  constexpr int NLD = (WROWS + AROWS) / 8;                  // 8-row load instructions per stage
+  constexpr int BUF = (WROWS + AROWS) * 8;                  // uint4 per stage
+  constexpr int LPW = NLD / NW;                             // loads per wave per stage
+  static_assert(NLD % NW == 0 && kTileK == 64, "loads split evenly over the waves");
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = wave % (TN / 64), wm = wave / (TN / 64);
@@ -566,23 +568,20 @@ __global__ __launch_bounds__(TN * 2) void gemm_tile_lds_kernel(GemmArgs g) {
   if (kt_begin >= kt_end) return;                           // uniform per workgroup
   const int nk = kt_end - kt_begin;
 
-  // fragment f = wave + NW i of a stage: W fragments first (row group f / 2,
-  // k-step f % 2), then A (row group, k-step, plane); per lane: the element
-  // offset of its row (W: into w; A: into its source) and of its k position
+  // load q = wave + NW i of a stage covers LDS rows 8q .. 8q + 7 (W rows first,
+  // then A: hi plane rows, lo plane rows); lane l fetches chunk
+  // (l % 8) ^ (l / 8) of row 8q + l / 8, the chunk its LDS slot l % 8 holds
+  const int kchunk = 8 * ((lane & 7) ^ (lane >> 3));
   int64_t roff[LPW];
-  int koff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    const int f = wave + NW * i;
-    if (f < WFR) {
-      const int n = min(n0 + (f >> 1) * 16 + (lane & 15), g.N - 1);   // rows past N: results dropped
-      roff[i] = (static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg) * g.w_ld;
-      koff[i] = (f & 1) * 32 + 8 * (lane >> 4);
+    const int row = 8 * (wave + NW * i) + (lane >> 3);
+    if (row < WROWS) {
+      const int n = min(n0 + row, g.N - 1);                 // rows past N: results dropped
+      roff[i] = (static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg) * g.w_ld + kchunk;
     } else {
-      const int rest = (f - WFR) / HL;
-      const int m = min(m0 + (rest >> 1) * 16 + (lane & 15), g.M - 1); // rows past M: results dropped
-      roff[i] = a_row_off(g, m);
-      koff[i] = (rest & 1) * 32 + 8 * (lane >> 4);
+      const int m = min(m0 + (row - WROWS) % kTileM, g.M - 1);   // rows past M: results dropped
+      roff[i] = a_row_off(g, m) + kchunk;
     }
   }
   const uint16_t* wbase = static_cast<const uint16_t*>(g.w);
@@ -595,11 +594,12 @@ __global__ __launch_bounds__(TN * 2) void gemm_tile_lds_kernel(GemmArgs g) {
     uint4* base = lds + stage * BUF;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int f = wave + NW * i;                           // uniform per wave
+      const int q = wave + NW * i;                           // uniform per wave
+      const int row0 = 8 * q;
       const uint16_t* p;
-      if (f < WFR) p = wbase + roff[i] + kb + koff[i];
-      else p = (((f - WFR) % HL) ? alo : ahi) + roff[i] + koff[i];
-      load_frag_to_lds(p, base + f * 64);
+      if (row0 < WROWS) p = wbase + roff[i] + kb;
+      else p = (row0 - WROWS >= kTileM ? alo : ahi) + roff[i];
+      load_frag_to_lds(p, base + q * 64);
     }
   };
 
@@ -609,36 +609,50 @@ __global__ __launch_bounds__(TN * 2) void gemm_tile_lds_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint4* buf) __attribute__((always_inline)) {
+  // fragment (row group of 16, k-step ks): lane l reads row (l % 16) of the
+  // group, chunk 4 ks + l / 16, at slot chunk ^ (row % 8)
+  const int xs = (lane >> 4) ^ (lane & 7);
+  const int wrow = (wn * 64 + (lane & 15)) * 8, arow = (WROWS + wm * 64 + (lane & 15)) * 8;
+  struct Frags { uint4 w[4], a[4 * HL]; };
+  auto rd = [&](Frags& f, const uint4* buf, int ks) __attribute__((always_inline)) {
+    const int slot = xs ^ (ks << 2);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 wf[4], af[4], al[4];
+    for (int i = 0; i < 4; ++i) f.w[i] = buf[wrow + i * 128 + slot];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wf[i] = buf[((wn * 4 + i) * 2 + ks) * 64 + lane];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        af[j] = buf[WFR * 64 + (((wm * 4 + j) * 2 + ks) * HL) * 64 + lane];
-        if constexpr (HL == 2) al[j] = buf[WFR * 64 + (((wm * 4 + j) * 2 + ks) * HL + 1) * 64 + lane];
-      }
+      for (int h = 0; h < HL; ++h) f.a[j * HL + h] = buf[arow + (h * kTileM + j * 16) * 8 + slot];
+  };
+  auto mm = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = mfma16x16x32(wf[i], af[j], acc[i][j]);
-          if constexpr (HL == 2) acc[i][j] = mfma16x16x32(wf[i], al[j], acc[i][j]);
-        }
-    }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < HL; ++h) acc[i][j] = mfma16x16x32(f.w[i], f.a[j * HL + h], acc[i][j]);
   };
 
 #pragma unroll
-  for (int st = 0; st < NSTAGE - 1; ++st) issue(st, st);
+  for (int st = 0; st < NSTAGE; ++st) issue(st, st);
+  wait_vmcnt<(NSTAGE - 1) * LPW>();                          // tile 0 landed
+  bare_barrier();
+  Frags fa, fb;
+  rd(fa, lds, 0);
   for (int t = 0; t < nk; ++t) {
-    wait_vmcnt<(NSTAGE - 2) * LPW>();                        // this wave's loads of tile t landed
-    bare_barrier();                                           // ... and every other wave's
-    issue(t + NSTAGE - 1, (t + NSTAGE - 1) % NSTAGE);
-    compute(lds + (t % NSTAGE) * BUF);
+    rd(fb, lds + (t % NSTAGE) * BUF, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mm(fa);                                                   // k-step 0 of tile t
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);                       // lgkmcnt(0): this wave is done reading tile t
+    wait_vmcnt<(NSTAGE - 2) * LPW>();                        // tile t + 1 landed
+    bare_barrier();                                           // ... for every wave; tile t is free
+    issue(t + NSTAGE, t % NSTAGE);
+    rd(fa, lds + ((t + 1) % NSTAGE) * BUF, 0);                // past the end: a repeated tile, unused
+    __builtin_amdgcn_sched_barrier(0);
+    mm(fb);                                                   // k-step 1 of tile t
+    __builtin_amdgcn_sched_barrier(0);
   }
-  wait_vmcnt<0>();                                          // the trailing repeated tiles
+  wait_vmcnt<0>();                                            // the trailing repeated tiles
 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
