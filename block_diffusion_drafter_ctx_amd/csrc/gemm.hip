@@ -395,7 +395,12 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
 // reads), double-buffered, with the next tile's global loads in flight while
 // the current one is multiplied.  grid = (N / 128, M / 128, splits).
 constexpr int kTileN = 128, kTileM = 128, kTileK = 64;
-constexpr int kTileNLds = 256;   // weight rows per tile of the LDS-direct kernel (8 waves)
+// LDS-direct kernel shapes: bf16 A takes 256 x 256 tiles in four waves of
+// 128 x 128 (one wave per SIMD, 256 accumulator registers); hi/lo planes take
+// 256 x 128 tiles in eight waves of 64 x 64 (a 256-row A tile's two planes would
+// not leave room for two LDS stages)
+struct TileShape { int tn, tm, wt, ns; };
+constexpr TileShape kTileBf16{256, 256, 128, 2}, kTileHiLo{256, 128, 64, 2};
 
 template <int AK>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
@@ -535,8 +540,8 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------- tiled path, LDS-direct
-// 256 weight rows x 128 activation rows x 64 k per tile, eight waves of 64 x 64,
-// fed by gfx950's global-to-LDS loads (a wave-wide 16-byte load lands lane l at
+// TN weight rows x TM activation rows x 64 k per tile, in waves of WT x WT
+// outputs, fed by gfx950's global-to-LDS loads (a wave-wide 16-byte load lands lane l at
 // LDS base + 16 l, no register staging).  Each load instruction brings whole
 // 128-byte lines: 8 rows x 64 k (lane l: row l / 8, 16-byte chunk l % 8) --
 // from L2 that runs 2.5x faster than MFMA-fragment order (16 rows x 64 bytes
@@ -549,18 +554,19 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
 // wave's last read of tile t.  Past the end of the K range the loads repeat the
 // last tile, so every wait has a fixed count.  A is exact bf16 (HL = 1) or the
 // hi and lo planes of an fp32 matrix (HL = 2, two MFMAs per product).
-template <int HL, int NSTAGE, int TN>
-__global__ __launch_bounds__(TN * 2) void gemm_tile_lds_kernel(GemmArgs g) {
-  constexpr int NW = TN / 64 * 2;                           // waves: (TN / 64) x 2 of 64 x 64 each
-  constexpr int WROWS = TN, AROWS = kTileM * HL;            // LDS rows per stage (A: planes stacked)
+template <int HL, int NSTAGE, int TN, int TM, int WT>
+__global__ __launch_bounds__((TN / WT) * (TM / WT) * 64) void gemm_tile_lds_kernel(GemmArgs g) {
+  constexpr int NW = (TN / WT) * (TM / WT);                 // waves of WT x WT outputs each
+  constexpr int FW = WT / 16;                               // 16-row fragments per wave and operand
+  constexpr int WROWS = TN, AROWS = TM * HL;                // LDS rows per stage (A: planes stacked)
   constexpr int NLD = (WROWS + AROWS) / 8;                  // 8-row load instructions per stage
   constexpr int BUF = (WROWS + AROWS) * 8;                  // uint4 per stage
   constexpr int LPW = NLD / NW;                             // loads per wave per stage
   static_assert(NLD % NW == 0 && kTileK == 64, "loads split evenly over the waves");
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wn = wave % (TN / 64), wm = wave / (TN / 64);
-  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * kTileM;
+  const int wn = wave % (TN / WT), wm = wave / (TN / WT);
+  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
   const int split = blockIdx.z;
   const int ktiles = g.K / kTileK;
   const int kt_begin = split * g.chunks_per_split;
@@ -580,56 +586,81 @@ __global__ __launch_bounds__(TN * 2) void gemm_tile_lds_kernel(GemmArgs g) {
       const int n = min(n0 + row, g.N - 1);                 // rows past N: results dropped
       roff[i] = (static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg) * g.w_ld + kchunk;
     } else {
-      const int m = min(m0 + (row - WROWS) % kTileM, g.M - 1);   // rows past M: results dropped
+      const int m = min(m0 + (row - WROWS) % TM, g.M - 1);       // rows past M: results dropped
       roff[i] = a_row_off(g, m) + kchunk;
     }
   }
   const uint16_t* wbase = static_cast<const uint16_t*>(g.w);
-  auto issue = [&](int t, int stage) {                      // t: k-tile index within [0, nk)
-    const int kb = (kt_begin + min(t, nk - 1)) * kTileK;
+  struct TileSrc { int kb; const uint16_t *ahi, *alo; };
+  auto tile_src = [&](int t) __attribute__((always_inline)) {   // t: k-tile index within [0, nk)
+    TileSrc r;
+    r.kb = (kt_begin + min(t, nk - 1)) * kTileK;
     // a 64-wide k tile never straddles A sources (a_cols % 64 == 0)
-    const int s = kb / g.a_cols, col = kb - s * g.a_cols;
-    const uint16_t* ahi = pick_src<uint16_t>(g, s) + col;
-    const uint16_t* alo = HL == 2 ? static_cast<const uint16_t*>(g.a_lo) + col : ahi;   // HL == 2: one source
-    uint4* base = lds + stage * BUF;
+    const int s = r.kb / g.a_cols, col = r.kb - s * g.a_cols;
+    r.ahi = pick_src<uint16_t>(g, s) + col;
+    r.alo = HL == 2 ? static_cast<const uint16_t*>(g.a_lo) + col : r.ahi;   // HL == 2: one source
+    return r;
+  };
+  auto issue_one = [&](int i, const TileSrc& src, int stage) __attribute__((always_inline)) {
+    const int q = wave + NW * i;                             // uniform per wave
+    const int row0 = 8 * q;
+    const uint16_t* p;
+    if (row0 < WROWS) p = wbase + roff[i] + src.kb;
+    else p = (row0 - WROWS >= TM ? src.alo : src.ahi) + roff[i];
+    load_frag_to_lds(p, lds + stage * BUF + q * 64);
+  };
+  auto issue = [&](int t, int stage) __attribute__((always_inline)) {
+    const TileSrc src = tile_src(t);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int q = wave + NW * i;                           // uniform per wave
-      const int row0 = 8 * q;
-      const uint16_t* p;
-      if (row0 < WROWS) p = wbase + roff[i] + kb;
-      else p = (row0 - WROWS >= kTileM ? alo : ahi) + roff[i];
-      load_frag_to_lds(p, base + q * 64);
-    }
+    for (int i = 0; i < LPW; ++i) issue_one(i, src, stage);
   };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[FW][FW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FW; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // fragment (row group of 16, k-step ks): lane l reads row (l % 16) of the
   // group, chunk 4 ks + l / 16, at slot chunk ^ (row % 8)
   const int xs = (lane >> 4) ^ (lane & 7);
-  const int wrow = (wn * 64 + (lane & 15)) * 8, arow = (WROWS + wm * 64 + (lane & 15)) * 8;
-  struct Frags { uint4 w[4], a[4 * HL]; };
+  const int wrow = (wn * WT + (lane & 15)) * 8, arow = (WROWS + wm * WT + (lane & 15)) * 8;
+  struct Frags { uint4 w[FW], a[FW * HL]; };
   auto rd = [&](Frags& f, const uint4* buf, int ks) __attribute__((always_inline)) {
     const int slot = xs ^ (ks << 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.w[i] = buf[wrow + i * 128 + slot];
+    for (int i = 0; i < FW; ++i) f.w[i] = buf[wrow + i * 128 + slot];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FW; ++j)
 #pragma unroll
-      for (int h = 0; h < HL; ++h) f.a[j * HL + h] = buf[arow + (h * kTileM + j * 16) * 8 + slot];
+      for (int h = 0; h < HL; ++h) f.a[j * HL + h] = buf[arow + (h * TM + j * 16) * 8 + slot];
   };
   auto mm = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FW; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < FW; ++j)
 #pragma unroll
         for (int h = 0; h < HL; ++h) acc[i][j] = mfma16x16x32(f.w[i], f.a[j * HL + h], acc[i][j]);
+  };
+  // the same MFMAs with the next tile's loads spread among them, so that the
+  // wave keeps the MFMA pipe fed while the load instructions are accepted
+  constexpr int NMF = FW * FW * HL, EVERY = (NMF + LPW - 1) / LPW;
+  auto mm_issue = [&](const Frags& f, const TileSrc& src, int stage) __attribute__((always_inline)) {
+    int q = 0;
+#pragma unroll
+    for (int x = 0; x < NMF; ++x) {
+      const int i = x / (FW * HL), j = (x / HL) % FW, h = x % HL;
+      acc[i][j] = mfma16x16x32(f.w[i], f.a[j * HL + h], acc[i][j]);
+      if (x % EVERY == EVERY - 1 && q < LPW) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_one(q++, src, stage);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < LPW; ++r)
+      if (r >= q) issue_one(r, src, stage);
   };
 
 #pragma unroll
@@ -646,20 +677,20 @@ __global__ __launch_bounds__(TN * 2) void gemm_tile_lds_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(0xC07F);                       // lgkmcnt(0): this wave is done reading tile t
     wait_vmcnt<(NSTAGE - 2) * LPW>();                        // tile t + 1 landed
     bare_barrier();                                           // ... for every wave; tile t is free
-    issue(t + NSTAGE, t % NSTAGE);
+    const TileSrc src = tile_src(t + NSTAGE);
     rd(fa, lds + ((t + 1) % NSTAGE) * BUF, 0);                // past the end: a repeated tile, unused
     __builtin_amdgcn_sched_barrier(0);
-    mm(fb);                                                   // k-step 1 of tile t
+    mm_issue(fb, src, t % NSTAGE);                            // k-step 1 of tile t; tile t + NSTAGE loads
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmcnt<0>();                                            // the trailing repeated tiles
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = n0 + wn * 64 + i * 16 + 4 * (lane >> 4);
+  for (int i = 0; i < FW; ++i) {
+    const int n = n0 + wn * WT + i * 16 + 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wm * 64 + j * 16 + (lane & 15);
+    for (int j = 0; j < FW; ++j) {
+      const int m = m0 + wm * WT + j * 16 + (lane & 15);
       if (m >= g.M) continue;
       float* out = g.part + (static_cast<int64_t>(split) * g.M + m) * g.N + n;
       if (n + 3 < g.N && (g.N & 3) == 0) {
@@ -849,9 +880,11 @@ GemmPlan plan_gemm_mfma(int M, int N, int K, GemmAKind ak, bool wide) {
 GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
   GemmPlan p;
   p.tiled = true;
-  p.MT = kTileM;
-  p.mtiles = (M + kTileM - 1) / kTileM;
-  const int tn = ak == A_F32_SPLIT ? kTileN : kTileNLds;   // register-staged or LDS-direct kernel
+  // register-staged kernel (fp32 A) or LDS-direct kernel
+  const int tn = ak == A_F32_SPLIT ? kTileN : ak == A_BF16 ? kTileBf16.tn : kTileHiLo.tn;
+  const int tm = ak == A_F32_SPLIT ? kTileM : ak == A_BF16 ? kTileBf16.tm : kTileHiLo.tm;
+  p.MT = tm;
+  p.mtiles = (M + tm - 1) / tm;
   p.ntiles = (N + tn - 1) / tn;
   const int ktiles = K / kTileK;
   const int tiles = p.mtiles * p.ntiles;
@@ -883,38 +916,35 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
   return p;
 }
 
+template <int HL, int NS, int TN, int TM, int WT>
+hipError_t launch_tile_lds(const GemmArgs& a, dim3 grid, hipStream_t st) {
+  const size_t lds = static_cast<size_t>(NS) * (TN + TM * HL) * 8 * sizeof(uint4);
+  static bool set = false;   // per instantiation
+  if (!set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WT>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    set = true;
+  }
+  hipLaunchKernelGGL((gemm_tile_lds_kernel<HL, NS, TN, TM, WT>), grid, dim3((TN / WT) * (TM / WT) * 64), lds, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p, hipStream_t st) {
   if (p.rk) return ak == A_F32_SPLIT ? launch_gemm_rk(a0, p, nullptr, nullptr, st) : hipErrorInvalidValue;
   if (p.tiled && ak != A_F32_SPLIT) {
     GemmArgs a = a0;
     a.chunks_per_split = p.cps;
     const dim3 grid(p.ntiles, p.mtiles, p.S);
-    if (a.a_cols % kTileK != 0 || p.MT != kTileM) return hipErrorInvalidValue;
-    constexpr int TN = kTileNLds;
+    if (a.a_cols % kTileK != 0) return hipErrorInvalidValue;
     if (ak == A_BF16) {
-      constexpr int NS = 3;
-      const size_t lds = static_cast<size_t>(NS) * ((TN / 16) * 2 + (kTileM / 16) * 2) * 64 * sizeof(uint4);
-      static bool set = false;
-      if (!set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<1, NS, TN>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-        set = true;
-      }
-      hipLaunchKernelGGL((gemm_tile_lds_kernel<1, NS, TN>), grid, dim3(TN * 2), lds, st, a);
-    } else {
-      constexpr int NS = 2;
-      const size_t lds = static_cast<size_t>(NS) * ((TN / 16) * 2 + (kTileM / 16) * 2 * 2) * 64 * sizeof(uint4);
-      static bool set = false;
-      if (!set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<2, NS, TN>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-        set = true;
-      }
-      hipLaunchKernelGGL((gemm_tile_lds_kernel<2, NS, TN>), grid, dim3(TN * 2), lds, st, a);
+      constexpr TileShape T = kTileBf16;
+      if (p.MT != T.tm) return hipErrorInvalidValue;
+      return launch_tile_lds<1, T.ns, T.tn, T.tm, T.wt>(a, grid, st);
     }
-    return hipGetLastError();
+    constexpr TileShape T = kTileHiLo;
+    if (p.MT != T.tm) return hipErrorInvalidValue;
+    return launch_tile_lds<2, T.ns, T.tn, T.tm, T.wt>(a, grid, st);
   }
   if (p.tiled) {
     GemmArgs a = a0;
