@@ -395,12 +395,13 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
 // reads), double-buffered, with the next tile's global loads in flight while
 // the current one is multiplied.  grid = (N / 128, M / 128, splits).
 constexpr int kTileN = 128, kTileM = 128, kTileK = 64;
-// LDS-direct kernel shapes: bf16 A takes 256 x 256 tiles in four waves of
-// 128 x 128 (one wave per SIMD, 256 accumulator registers); hi/lo planes take
-// 256 x 128 tiles in eight waves of 64 x 64 (a 256-row A tile's two planes would
-// not leave room for two LDS stages)
-struct TileShape { int tn, tm, wt, ns; };
-constexpr TileShape kTileBf16{256, 256, 128, 2}, kTileHiLo{256, 128, 64, 2};
+// LDS-direct kernel shapes: bf16 A takes 256 x 256 tiles in eight waves of
+// 64 weight rows x 128 activation rows (two waves per SIMD: one issues MFMAs
+// while the other's load instructions are being accepted); hi/lo planes take
+// 256 x 128 tiles in eight waves of 64 x 64 (a 256-row A tile's two planes
+// would not leave room for two LDS stages)
+struct TileShape { int tn, tm, wn, wm, ns; };
+constexpr TileShape kTileBf16{256, 256, 64, 128, 2}, kTileHiLo{256, 128, 64, 64, 2};
 
 template <int AK>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
@@ -540,7 +541,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------- tiled path, LDS-direct
-// TN weight rows x TM activation rows x 64 k per tile, in waves of WT x WT
+// TN weight rows x TM activation rows x 64 k per tile, in waves of WN x WM
 // outputs, fed by gfx950's global-to-LDS loads (a wave-wide 16-byte load lands lane l at
 // LDS base + 16 l, no register staging).  Each load instruction brings whole
 // 128-byte lines: 8 rows x 64 k (lane l: row l / 8, 16-byte chunk l % 8) --
@@ -554,10 +555,10 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
 // wave's last read of tile t.  Past the end of the K range the loads repeat the
 // last tile, so every wait has a fixed count.  A is exact bf16 (HL = 1) or the
 // hi and lo planes of an fp32 matrix (HL = 2, two MFMAs per product).
-template <int HL, int NSTAGE, int TN, int TM, int WT>
-__global__ __launch_bounds__((TN / WT) * (TM / WT) * 64) void gemm_tile_lds_kernel(GemmArgs g) {
-  constexpr int NW = (TN / WT) * (TM / WT);                 // waves of WT x WT outputs each
-  constexpr int FW = WT / 16;                               // 16-row fragments per wave and operand
+template <int HL, int NSTAGE, int TN, int TM, int WN, int WM>
+__global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kernel(GemmArgs g) {
+  constexpr int NW = (TN / WN) * (TM / WM);                 // waves of WN x WM outputs each
+  constexpr int FN = WN / 16, FM = WM / 16;                 // 16-row fragments per wave: W, A
   constexpr int WROWS = TN, AROWS = TM * HL;                // LDS rows per stage (A: planes stacked)
   constexpr int NLD = (WROWS + AROWS) / 8;                  // 8-row load instructions per stage
   constexpr int BUF = (WROWS + AROWS) * 8;                  // uint4 per stage
@@ -565,7 +566,7 @@ __global__ __launch_bounds__((TN / WT) * (TM / WT) * 64) void gemm_tile_lds_kern
   static_assert(NLD % NW == 0 && kTileK == 64, "loads split evenly over the waves");
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wn = wave % (TN / WT), wm = wave / (TN / WT);
+  const int wn = wave % (TN / WN), wm = wave / (TN / WN);
   const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
   const int split = blockIdx.z;
   const int ktiles = g.K / kTileK;
@@ -615,42 +616,42 @@ __global__ __launch_bounds__((TN / WT) * (TM / WT) * 64) void gemm_tile_lds_kern
     for (int i = 0; i < LPW; ++i) issue_one(i, src, stage);
   };
 
-  f32x4_t acc[FW][FW];
+  f32x4_t acc[FN][FM];
 #pragma unroll
-  for (int i = 0; i < FW; ++i)
+  for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < FW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // fragment (row group of 16, k-step ks): lane l reads row (l % 16) of the
   // group, chunk 4 ks + l / 16, at slot chunk ^ (row % 8)
   const int xs = (lane >> 4) ^ (lane & 7);
-  const int wrow = (wn * WT + (lane & 15)) * 8, arow = (WROWS + wm * WT + (lane & 15)) * 8;
-  struct Frags { uint4 w[FW], a[FW * HL]; };
+  const int wrow = (wn * WN + (lane & 15)) * 8, arow = (WROWS + wm * WM + (lane & 15)) * 8;
+  struct Frags { uint4 w[FN], a[FM * HL]; };
   auto rd = [&](Frags& f, const uint4* buf, int ks) __attribute__((always_inline)) {
     const int slot = xs ^ (ks << 2);
 #pragma unroll
-    for (int i = 0; i < FW; ++i) f.w[i] = buf[wrow + i * 128 + slot];
+    for (int i = 0; i < FN; ++i) f.w[i] = buf[wrow + i * 128 + slot];
 #pragma unroll
-    for (int j = 0; j < FW; ++j)
+    for (int j = 0; j < FM; ++j)
 #pragma unroll
       for (int h = 0; h < HL; ++h) f.a[j * HL + h] = buf[arow + (h * TM + j * 16) * 8 + slot];
   };
   auto mm = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < FW; ++i)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int j = 0; j < FW; ++j)
+      for (int j = 0; j < FM; ++j)
 #pragma unroll
         for (int h = 0; h < HL; ++h) acc[i][j] = mfma16x16x32(f.w[i], f.a[j * HL + h], acc[i][j]);
   };
   // the same MFMAs with the next tile's loads spread among them, so that the
   // wave keeps the MFMA pipe fed while the load instructions are accepted
-  constexpr int NMF = FW * FW * HL, EVERY = (NMF + LPW - 1) / LPW;
+  constexpr int NMF = FN * FM * HL, EVERY = (NMF + LPW - 1) / LPW;
   auto mm_issue = [&](const Frags& f, const TileSrc& src, int stage) __attribute__((always_inline)) {
     int q = 0;
 #pragma unroll
     for (int x = 0; x < NMF; ++x) {
-      const int i = x / (FW * HL), j = (x / HL) % FW, h = x % HL;
+      const int i = x / (FM * HL), j = (x / HL) % FM, h = x % HL;
       acc[i][j] = mfma16x16x32(f.w[i], f.a[j * HL + h], acc[i][j]);
       if (x % EVERY == EVERY - 1 && q < LPW) {
         __builtin_amdgcn_sched_barrier(0);
@@ -686,11 +687,11 @@ __global__ __launch_bounds__((TN / WT) * (TM / WT) * 64) void gemm_tile_lds_kern
   wait_vmcnt<0>();                                            // the trailing repeated tiles
 
 #pragma unroll
-  for (int i = 0; i < FW; ++i) {
-    const int n = n0 + wn * WT + i * 16 + 4 * (lane >> 4);
+  for (int i = 0; i < FN; ++i) {
+    const int n = n0 + wn * WN + i * 16 + 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < FW; ++j) {
-      const int m = m0 + wm * WT + j * 16 + (lane & 15);
+    for (int j = 0; j < FM; ++j) {
+      const int m = m0 + wm * WM + j * 16 + (lane & 15);
       if (m >= g.M) continue;
       float* out = g.part + (static_cast<int64_t>(split) * g.M + m) * g.N + n;
       if (n + 3 < g.N && (g.N & 3) == 0) {
@@ -916,17 +917,17 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
   return p;
 }
 
-template <int HL, int NS, int TN, int TM, int WT>
+template <int HL, int NS, int TN, int TM, int WN, int WM>
 hipError_t launch_tile_lds(const GemmArgs& a, dim3 grid, hipStream_t st) {
   const size_t lds = static_cast<size_t>(NS) * (TN + TM * HL) * 8 * sizeof(uint4);
   static bool set = false;   // per instantiation
   if (!set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WT>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     set = true;
   }
-  hipLaunchKernelGGL((gemm_tile_lds_kernel<HL, NS, TN, TM, WT>), grid, dim3((TN / WT) * (TM / WT) * 64), lds, st, a);
+  hipLaunchKernelGGL((gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM>), grid, dim3((TN / WN) * (TM / WM) * 64), lds, st, a);
   return hipGetLastError();
 }
 
@@ -940,11 +941,11 @@ hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p,
     if (ak == A_BF16) {
       constexpr TileShape T = kTileBf16;
       if (p.MT != T.tm) return hipErrorInvalidValue;
-      return launch_tile_lds<1, T.ns, T.tn, T.tm, T.wt>(a, grid, st);
+      return launch_tile_lds<1, T.ns, T.tn, T.tm, T.wn, T.wm>(a, grid, st);
     }
     constexpr TileShape T = kTileHiLo;
     if (p.MT != T.tm) return hipErrorInvalidValue;
-    return launch_tile_lds<2, T.ns, T.tn, T.tm, T.wt>(a, grid, st);
+    return launch_tile_lds<2, T.ns, T.tn, T.tm, T.wn, T.wm>(a, grid, st);
   }
   if (p.tiled) {
     GemmArgs a = a0;
