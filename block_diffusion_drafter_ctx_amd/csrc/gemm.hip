@@ -230,7 +230,7 @@ constexpr int kRkMinN = 16384;   // weight rows below which the split-K streamin
 
 enum RkEpilogue { RK_PART = 0, RK_TOP2 = 1, RK_SWIGLU = 2 };
 
-template <int KS, int EP, int T>
+template <int KS, int EP, int T, int AK = A_F32_SPLIT>
 __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, float* top2, float* logits) {
   constexpr bool TOP2 = EP == RK_TOP2;
   constexpr int TN = EP == RK_SWIGLU ? 8 : 16;   // outputs per tile
@@ -269,8 +269,19 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
   }
   __builtin_amdgcn_sched_barrier(0);          // the first tiles' weights go out before the activation loads
 
-  uint4 bh[KS], bl[KS];
-  {
+  constexpr bool SPLIT = AK == A_F32_SPLIT;    // fp32 activations as bf16 hi + lo; else exact bf16
+  uint4 bh[KS], bl[SPLIT ? KS : 1];
+  if constexpr (!SPLIT) {
+    const int s = __builtin_amdgcn_readfirstlane(kwave / g.a_cols);
+    const int m = lane & 15;
+    const bool ok = m < g.M;
+    const uint16_t* p = pick_src<uint16_t>(g, s) + a_row_off(g, ok ? m : 0) + (kl - s * g.a_cols);
+#pragma unroll
+    for (int x = 0; x < KS; ++x) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + x * 32);
+      bh[x] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+  } else {
     // the host guarantees a_cols % (32 * KS) == 0: a wave's k range lies in one source
     const int s = __builtin_amdgcn_readfirstlane(kwave / g.a_cols);
     const int m = lane & 15;
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
 #pragma unroll
         for (int x = 0; x < KS; ++x) {
           acc[t] = mfma16x16x32(wb[t][x], bh[x], acc[t]);
-          acc[t] = mfma16x16x32(wb[t][x], bl[x], acc[t]);
+          if constexpr (SPLIT) acc[t] = mfma16x16x32(wb[t][x], bl[x], acc[t]);
           wb[t][x] = *reinterpret_cast<const uint4*>(np + x * 32);
         }
       }
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
 #pragma unroll
         for (int x = 0; x < KS; ++x) {
           acc[t] = mfma16x16x32(wb[t][x], bh[x], acc[t]);
-          acc[t] = mfma16x16x32(wb[t][x], bl[x], acc[t]);
+          if constexpr (SPLIT) acc[t] = mfma16x16x32(wb[t][x], bl[x], acc[t]);
         }
     }
 #pragma unroll
@@ -932,7 +943,7 @@ hipError_t launch_tile_lds(const GemmArgs& a, dim3 grid, hipStream_t st) {
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p, hipStream_t st) {
-  if (p.rk) return ak == A_F32_SPLIT ? launch_gemm_rk(a0, p, nullptr, nullptr, st) : hipErrorInvalidValue;
+  if (p.rk) return launch_gemm_rk(a0, p, nullptr, nullptr, st, ak);
   if (p.tiled && ak != A_F32_SPLIT) {
     GemmArgs a = a0;
     a.chunks_per_split = p.cps;
@@ -1042,7 +1053,7 @@ GemmPlan plan_gemm_rk_short(int M, int N, int K) {
 }
 
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
-  if (ak == A_F32_SPLIT && M <= 16) {
+  if ((ak == A_F32_SPLIT || ak == A_BF16) && M <= 16) {
     const GemmPlan r = plan_gemm_rk(M, N, K, false);
     if (r.rk && r.S == 1) return r;
     const GemmPlan q = plan_gemm_rk_short(M, N, K);
@@ -1052,8 +1063,10 @@ GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
   return plan_gemm_mfma(M, N, K, ak, wide);
 }
 
-hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, float* logits, hipStream_t st) {
+hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, float* logits, hipStream_t st,
+                          GemmAKind ak) {
   if (!p.rk || a0.a_cols % (32 * p.ks) != 0 || (top2 != nullptr && p.S != 1)) return hipErrorInvalidValue;
+  if (ak != A_F32_SPLIT && (ak != A_BF16 || top2 != nullptr)) return hipErrorInvalidValue;
   GemmArgs a = a0;
   a.S = p.S;
   a.ntiles = p.ntiles;
@@ -1064,9 +1077,17 @@ hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, fl
     if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_TOP2, 1>), grid, block, 0, st, a, top2, logits);
     else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_TOP2, 1>), grid, block, 0, st, a, top2, logits);
   } else {
-    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_PART, 1>), grid, block, 0, st, a, nullptr, nullptr);
-    else if (p.ks == 4) hipLaunchKernelGGL((gemm_rk_kernel<4, RK_PART, 1>), grid, block, 0, st, a, nullptr, nullptr);
-    else hipLaunchKernelGGL((gemm_rk_kernel<2, RK_PART, 2>), grid, block, 0, st, a, nullptr, nullptr);
+    if (ak == A_BF16) {
+      if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_PART, 1, A_BF16>), grid, block, 0, st, a, nullptr, nullptr);
+      else if (p.ks == 4) hipLaunchKernelGGL((gemm_rk_kernel<4, RK_PART, 1, A_BF16>), grid, block, 0, st, a, nullptr, nullptr);
+      else hipLaunchKernelGGL((gemm_rk_kernel<2, RK_PART, 2, A_BF16>), grid, block, 0, st, a, nullptr, nullptr);
+    } else if (p.ks == 8) {
+      hipLaunchKernelGGL((gemm_rk_kernel<8, RK_PART, 1>), grid, block, 0, st, a, nullptr, nullptr);
+    } else if (p.ks == 4) {
+      hipLaunchKernelGGL((gemm_rk_kernel<4, RK_PART, 1>), grid, block, 0, st, a, nullptr, nullptr);
+    } else {
+      hipLaunchKernelGGL((gemm_rk_kernel<2, RK_PART, 2>), grid, block, 0, st, a, nullptr, nullptr);
+    }
   }
   return hipGetLastError();
 }

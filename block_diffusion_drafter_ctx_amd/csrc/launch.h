@@ -56,15 +56,16 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak);
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide);
 hipError_t launch_gemm_mfma(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, hipStream_t st);
 
-// Register-K kernel for <= 16 fp32 activation rows (split hi/lo) against a tall
-// bf16 weight; plan.rk is false when the shape does not qualify.  top2 = true
-// asks for the LM-head epilogue (a single K split).
+// Register-K kernel for <= 16 activation rows (fp32 split hi/lo, or exact bf16
+// with ak = A_BF16) against a bf16 weight; plan.rk is false when the shape does
+// not qualify.  top2 = true asks for the LM-head epilogue (a single K split).
 constexpr int kRkMaxGrid = 1024;   // bound on register-K workgroups (top-2 workspace rows)
 GemmPlan plan_gemm_rk(int M, int N, int K, bool top2);
 // top2 == nullptr: store part[s][m][n].  Otherwise write the per-workgroup top-2
 // of every row to top2 [p.grid][M][3] (value, index bits, runner-up) and, when
 // logits != nullptr, the logits [M][N].
-hipError_t launch_gemm_rk(const GemmArgs& a, const GemmPlan& p, float* top2, float* logits, hipStream_t st);
+hipError_t launch_gemm_rk(const GemmArgs& a, const GemmPlan& p, float* top2, float* logits, hipStream_t st,
+                          GemmAKind ak = A_F32_SPLIT);
 // FFN gate/up with SwiGLU fused: W is the stacked [gate (F rows); up (F rows)]
 // weight, a.N = F; writes s_out[m][f] = silu(gate) * up.  plan.rk is false when
 // the shape does not qualify (the caller then runs the GEMM and swiglu apart).
