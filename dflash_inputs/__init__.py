@@ -8,7 +8,7 @@ here.  Every tensor is drawn from numpy's PCG64 seeded by
 (or any 4M-element chunk of one) can be regenerated independently.
 """
 from .configs import CONFIGS, Config, get_config, shrink
-from .gen import Inputs, bf16_round_f32, build_target_np
+from .gen import Inputs, bf16_round_f32, build_target_logits_np, build_target_np
 
 __all__ = ["CONFIGS", "Config", "get_config", "shrink", "Inputs",
-           "bf16_round_f32", "build_target_np"]
+           "bf16_round_f32", "build_target_logits_np", "build_target_np"]

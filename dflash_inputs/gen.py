@@ -8,7 +8,14 @@ Recipe (the same for the oracle and the GPU path):
   * anchors ~ U{0..V-2}; the mask token id is V-1;
   * synthetic target tokens per drafting iteration: position j of sequence b
     matches the draft with probability p_j, otherwise it is the draft shifted by
-    r ~ U{1..V-1} (mod V); the bonus token is U{0..V-1}.
+    r ~ U{1..V-1} (mod V); the bonus token is U{0..V-1};
+  * sampled decoding: uniforms strictly inside (0, 1) of the form
+    (2k + 1) * 2**-24, k ~ U{0..2**23-1} (exact in float32, never 0 or 1), one
+    per (row, vocabulary entry) for the draft draws, one per draft for the
+    accept tests and one per (sequence, vocabulary entry) for the emitted
+    token; synthetic target logits are the draft logits plus N(0, 0.5^2) noise
+    at each draft position (per-position acceptance 2 Phi(-0.25 / T), 0.80 at
+    T = 1) and N(0, 1) at the bonus position.
 
 Large tensors are drawn in 4M-element chunks, each from its own
 ``SeedSequence([base_seed, config_id, tensor_id, chunk])``, on a thread pool.
@@ -33,6 +40,7 @@ T_APPEND = 40        # + iteration
 T_MATCH = 60         # + iteration
 T_LAYER = 100        # + 10*layer + {0: qkv, 1: o, 2: gateup, 3: down, 4: g_attn, 5: g_ffn}
 T_OVERRIDE = 5000    # + gamma
+T_SAMPLE = 7000      # + 100 * gamma + 10 * iteration + {0: draws, 1: accept, 2: emit, 3: noise, 4: logits, 5: ids, 6: h}
 
 
 def bf16_round_f32(a: np.ndarray) -> np.ndarray:
@@ -79,6 +87,37 @@ def _normal(seed_key: tuple, shape, std: float, mean: float, bf16: bool) -> np.n
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(fill, range(nch)))
     return out.reshape(shape)
+
+
+def _uniform_open(seed_key: tuple, shape) -> np.ndarray:
+    """float32 uniforms (2k + 1) * 2**-24 with k ~ U{0..2**23-1}: strictly inside (0, 1)."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.float32)
+
+    def fill(c: int):
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(seed_key) + [c])))
+        k = rng.integers(0, 1 << 23, size=hi - lo, dtype=np.int32)
+        out[lo:hi] = (2 * k + 1).astype(np.float32) * np.float32(2.0 ** -24)
+
+    nch = (n + CHUNK - 1) // CHUNK
+    if nch <= 1:
+        for c in range(nch):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nch)))
+    return out.reshape(shape)
+
+
+def build_target_logits_np(draft_logits: np.ndarray, noise: np.ndarray, sigma: float = 0.5) -> np.ndarray:
+    """Synthetic target logits [B, n+1, V] (harness, not method): the draft logits
+    plus sigma * noise at the n draft positions, the noise itself at the bonus."""
+    z = np.asarray(draft_logits, dtype=np.float32)
+    t = np.array(noise, dtype=np.float32, copy=True)
+    t[:, :-1] *= np.float32(sigma)
+    t[:, :-1] += z
+    return t
 
 
 def build_target_np(draft: np.ndarray, match: np.ndarray, r: np.ndarray,
@@ -196,3 +235,37 @@ class Inputs:
         r = rng.integers(1, c.V, size=(c.B, n))
         bonus = rng.integers(0, c.V, size=c.B)
         return match, r, bonus
+
+    # -- sampled decoding ------------------------------------------------------
+    def _skey(self, gamma: int, it: int, kind: int) -> tuple:
+        return self._key(T_SAMPLE + 100 * gamma + 10 * it + kind)
+
+    def sample_uniforms(self, it: int, gamma: int):
+        """(draws [B, n, V], accept [B, n], emit [B, V]) float32 uniforms in (0, 1)."""
+        c = self.cfg
+        n = gamma - 1
+        return (_uniform_open(self._skey(gamma, it, 0), (c.B, n, c.V)),
+                _uniform_open(self._skey(gamma, it, 1), (c.B, n)),
+                _uniform_open(self._skey(gamma, it, 2), (c.B, c.V)))
+
+    def target_noise(self, it: int, gamma: int) -> np.ndarray:
+        """[B, n+1, V] float32 ~ N(0, 1) for synthetic target logits."""
+        c = self.cfg
+        return _normal(self._skey(gamma, it, 3), (c.B, gamma, c.V), 1.0, 0.0, False)
+
+    def synthetic_logits(self, it: int, gamma: int, std: float) -> np.ndarray:
+        """[B, n, V] float32 ~ N(0, std^2): stand-in draft logits for verify-only tests."""
+        c = self.cfg
+        return _normal(self._skey(gamma, it, 4), (c.B, gamma - 1, c.V), std, 0.0, False)
+
+    def random_ids(self, it: int, gamma: int) -> np.ndarray:
+        """[B, n] int32 ~ U{0..V-1}: stand-in drafts for verify-only tests."""
+        c = self.cfg
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(self._skey(gamma, it, 5)) + [0])))
+        return rng.integers(0, c.V, size=(c.B, gamma - 1)).astype(np.int32)
+
+    def final_states(self, gamma: int) -> np.ndarray:
+        """[B, gamma, D] float32 ~ N(0, 1): stand-in h_final rows (unit RMS on
+        average, like the drafter's final RMSNorm output) for LM-head tests."""
+        c = self.cfg
+        return _normal(self._skey(gamma, 0, 6), (c.B, gamma, c.D), 1.0, 0.0, False)

@@ -6,6 +6,7 @@ execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
 library.
 """
 from .dflash_oracle import (  # noqa: F401
-    OracleCache, accept, attention, draft_forward, fuse_context, inject_kv,
-    lm_head_argmax, rmsnorm, silu, store, to_bf16,
+    OracleCache, accept, attention, draft_forward, fuse_context, gumbel_pick,
+    inject_kv, lm_head_argmax, log_softmax_t, logsumexp_t, rmsnorm,
+    sample_accept, sample_drafts, silu, store, to_bf16,
 )

@@ -248,3 +248,103 @@ def accept(draft, target):
         tau[b] = m + 1
         nxt[b] = target[b, m]
     return tau, nxt
+
+
+# ---------------------------------------------------------------------------
+# sampled drafting and lossless verification at temperature T > 0
+# ---------------------------------------------------------------------------
+def log_softmax_t(logits, T: float) -> np.ndarray:
+    """log softmax(logits / T) over the last axis (max-shifted)."""
+    x = np.asarray(logits, dtype=F64) / float(T)
+    mx = np.max(x, axis=-1, keepdims=True)
+    return x - (mx + np.log(np.sum(np.exp(x - mx), axis=-1, keepdims=True)))
+
+
+def logsumexp_t(logits, T: float) -> np.ndarray:
+    """log sum_v exp(logits_v / T) over the last axis."""
+    x = np.asarray(logits, dtype=F64) / float(T)
+    mx = np.max(x, axis=-1)
+    return mx + np.log(np.sum(np.exp(x - mx[..., None]), axis=-1))
+
+
+def gumbel_pick(logw, u):
+    """One categorical draw from weights proportional to exp(logw) along the
+    last axis, using one uniform u_v in (0, 1) per category: the Gumbel-max
+    rule picks argmax_v (logw_v - log(-log u_v)).  Entries with logw = -inf
+    have weight 0.  Ties go to the lowest index.
+    Returns (index, best key minus second-best key)."""
+    key = np.asarray(logw, dtype=F64) - np.log(-np.log(np.asarray(u, dtype=F64)))
+    idx = np.argmax(key, axis=-1)
+    if key.shape[-1] < 2:
+        return idx.astype(np.int32), np.full(idx.shape, np.inf)
+    top = -np.partition(-key, 1, axis=-1)[..., :2]
+    return idx.astype(np.int32), top[..., 0] - top[..., 1]
+
+
+def sample_drafts(h_final, lm_head, T: float, u):
+    """Draft tokens sampled from the drafter's temperature-T distribution.
+
+    [JP] "주요 결과" reports DFlash at temperature 1 (sampling) next to greedy
+    decoding, and "학습 방법" has the drafter predict all block positions after
+    the anchor in parallel: each mask row i = 1..gamma-1 gets its own logits
+    z = lm_head . h_final[b][i] and its draft token is one draw from
+    q = softmax(z / T), made here with the Gumbel-max rule and the caller's
+    uniforms u[b][i-1][:] (one per vocabulary entry).
+    Returns (draft [B, n] int32, logits z [B, n, V], log sum exp(z / T) [B, n],
+    key gap [B, n]: the winning perturbed key minus the runner-up).
+    """
+    z = np.asarray(h_final, dtype=F64)[:, 1:, :] @ np.asarray(lm_head, dtype=F64).T
+    draft, gap = gumbel_pick(z / float(T), u)
+    return draft, z, logsumexp_t(z, T), gap
+
+
+def sample_accept(draft, draft_logits, target_logits, T: float, accept_u, resid_u):
+    """Lossless verification of a sampled block (speculative sampling).
+
+    [GL] "비용 구조의 차이가 만드는 성능 격차": DFlash's speedup is lossless, since
+    the rejection/acceptance sampling of speculative decoding makes every output
+    token follow the target model's own distribution.  The rule written out here
+    is the standard one with that property.  With q_j = softmax(draft_logits[j] / T)
+    and p_j = softmax(target_logits[j] / T):
+      * for j = 0, 1, ... in order, draft j is accepted when
+        accept_u[j] < p_j(d_j) / q_j(d_j); the first j that fails is m (m = n when
+        every draft is accepted);
+      * m < n: the emitted token is a draw from max(0, p_m - q_m) (normalised);
+        should that residual have no positive entry, the draw is from p_m;
+      * m = n: the emitted token is the bonus, a draw from p_n;
+    both draws use the Gumbel-max rule with the uniforms resid_u[b][:].
+    tau = m + 1 tokens are committed: d_0..d_{m-1} and the emitted token, which
+    is also the next block's anchor.
+    draft [B, n]; draft_logits [B, n, V]; target_logits [B, n+1, V];
+    accept_u [B, n]; resid_u [B, V].
+    Returns (tau [B], next_anchor [B], info) where info holds, per sequence,
+    "m", "log_ratio" [B, n] (log p_j(d_j) - log q_j(d_j)), "resid_empty" and
+    "key_gap" (margin of the final draw).
+    """
+    draft = np.asarray(draft)
+    B, n = draft.shape
+    lq = log_softmax_t(draft_logits, T)                    # [B, n, V]
+    lp = log_softmax_t(target_logits, T)                   # [B, n+1, V]
+    bi = np.arange(B)[:, None]
+    ji = np.arange(n)[None, :]
+    log_ratio = lp[:, :n][bi, ji, draft] - lq[bi, ji, draft]
+    accepted = np.asarray(accept_u, dtype=F64) < np.exp(log_ratio)
+    tau = np.zeros(B, dtype=np.int32)
+    nxt = np.zeros(B, dtype=np.int32)
+    m_all = np.zeros(B, dtype=np.int32)
+    empty = np.zeros(B, dtype=bool)
+    key_gap = np.zeros(B)
+    for b in range(B):
+        m = 0
+        while m < n and accepted[b, m]:
+            m += 1
+        if m < n:
+            r = np.maximum(0.0, np.exp(lp[b, m]) - np.exp(lq[b, m]))
+            empty[b] = not np.any(r > 0.0)
+            with np.errstate(divide="ignore"):
+                logw = lp[b, m] if empty[b] else np.log(r)
+        else:
+            logw = lp[b, n]
+        tok, gap = gumbel_pick(logw, resid_u[b])
+        m_all[b], tau[b], nxt[b], key_gap[b] = m, m + 1, tok, gap
+    return tau, nxt, dict(m=m_all, log_ratio=log_ratio, resid_empty=empty, key_gap=key_gap)

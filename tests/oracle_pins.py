@@ -467,4 +467,162 @@ def pin_accept_expectation(o):
         assert abs(tau.mean() - mu) < 3.5 * sd + 1e-9, (tau.mean(), mu)
 
 
+# ---------------------------------------------------------------------------
+# sampled drafting / lossless verification
+# ---------------------------------------------------------------------------
+def _softmax(x, T=1.0):
+    from scipy.special import softmax
+    return softmax(np.asarray(x, dtype=F64) / T, axis=-1)
+
+
+def _freq_ok(samples, probs, n_sigma=5.0):
+    """Empirical category frequencies of integer samples within n_sigma binomial
+    standard errors of probs (and no sample outside the support)."""
+    samples = np.asarray(samples).reshape(-1)
+    N, V = samples.size, len(probs)
+    assert N > 0
+    cnt = np.bincount(samples, minlength=V)
+    assert cnt.size == V, "sample outside the vocabulary"
+    f = cnt / N
+    se = np.sqrt(np.maximum(probs * (1 - probs), 1e-12) / N)
+    return bool(np.all(np.abs(f - probs) <= n_sigma * se + 1e-12)), f
+
+
+def pin_gumbel_pick_distribution(o):
+    # The Gumbel-max draw follows softmax(logw); a -inf weight is never drawn;
+    # for two categories P(0) = sigmoid(logw0 - logw1) (closed form).
+    rng = _rng(30)
+    N = 200000
+    logw = np.array([0.3, -1.2, 1.1, -np.inf, 0.0])
+    u = rng.random((N, 5))
+    idx, gap = o.gumbel_pick(np.broadcast_to(logw, (N, 5)), u)
+    ok, f = _freq_ok(idx, _softmax(np.where(np.isinf(logw), -1e300, logw)))
+    assert ok, f
+    assert not np.any(idx == 3)
+    assert np.all(gap >= 0)
+    lw2 = np.array([0.7, -0.4])
+    idx2, _ = o.gumbel_pick(np.broadcast_to(lw2, (N, 2)), u[:, :2])
+    p0 = 1.0 / (1.0 + math.exp(-(lw2[0] - lw2[1])))
+    assert abs(np.mean(idx2 == 0) - p0) < 5 * math.sqrt(p0 * (1 - p0) / N)
+    # exact ties (equal weights, equal uniforms) go to the lowest index
+    t_idx, t_gap = o.gumbel_pick(np.zeros((1, 4)), np.full((1, 4), 0.5))
+    assert t_idx[0] == 0 and t_gap[0] == 0.0
+
+
+def pin_logsumexp_library(o):
+    from scipy.special import logsumexp
+    rng = _rng(31)
+    z = rng.normal(0, 3.0, (3, 4, 257))
+    for T in (1.0, 0.6, 2.5):
+        assert np.allclose(o.logsumexp_t(z, T), logsumexp(z / T, axis=-1), rtol=0, atol=1e-12)
+        ref = torch.log_softmax(torch.from_numpy(z / T), dim=-1).numpy()
+        assert np.allclose(o.log_softmax_t(z, T), ref, rtol=0, atol=1e-12)
+
+
+def pin_sample_drafts_distribution(o):
+    # Block rows e_1, e_2 against an LM head whose column i holds the logits of
+    # row i: the drafts at mask row i follow softmax(column_i / T); the anchor
+    # row is not drafted; logits and log-normalisers match the closed forms.
+    from scipy.special import logsumexp
+    rng = _rng(32)
+    V, D, N, T = 6, 3, 60000, 0.7
+    E = rng.normal(0, 1.2, (V, D))
+    h = np.zeros((N, 3, D))
+    h[:, 0, 0] = 1.0       # anchor row: never drafted
+    h[:, 1, 1] = 1.0
+    h[:, 2, 2] = 1.0
+    u = rng.random((N, 2, V))
+    d, z, lse, gap = o.sample_drafts(h, E, T, u)
+    assert d.shape == (N, 2) and z.shape == (N, 2, V)
+    assert np.allclose(z[0, 0], E[:, 1]) and np.allclose(z[0, 1], E[:, 2])
+    assert np.allclose(lse[0], logsumexp(E[:, 1:3].T / T, axis=-1), atol=1e-12)
+    for i in (1, 2):
+        ok, f = _freq_ok(d[:, i - 1], _softmax(E[:, i], T))
+        assert ok, (i, f)
+    # the two positions are drawn independently (uniforms of their own)
+    joint = np.mean((d[:, 0] == 0) & (d[:, 1] == 0))
+    pa, pb = _softmax(E[:, 1], T)[0], _softmax(E[:, 2], T)[0]
+    assert abs(joint - pa * pb) < 5 * math.sqrt(pa * pb / N)
+    # temperature -> 0 with well separated logits: the draw is the greedy argmax
+    h1 = rng.normal(0, 1, (4, 5, D))
+    E1 = rng.normal(0, 1, (V, D))
+    g_d, g_gap, _ = o.lm_head_argmax(h1, E1)
+    s_d, _, _, _ = o.sample_drafts(h1, E1, 1e-6, rng.uniform(0.01, 0.99, (4, 4, V)))
+    keep = g_gap > 1e-3
+    assert np.array_equal(s_d[keep], g_d[keep])
+
+
+def _committed(draft, tau, nxt):
+    """Committed tokens of each block: d_0..d_{tau-2} then the emitted token."""
+    out = []
+    for b in range(len(tau)):
+        out.append(list(draft[b, :tau[b] - 1]) + [int(nxt[b])])
+    return out
+
+
+def pin_sample_accept_lossless(o):
+    # Losslessness ([GL] "비용 구조의 차이가 만드는 성능 격차"): with drafts drawn
+    # from q_j, the token committed at every position follows the target's p_j,
+    # and position k is reached with probability prod_{j<k} sum_v min(p_j, q_j).
+    rng = _rng(33)
+    V, n, T, N = 4, 3, 0.8, 40000
+    z = rng.normal(0, 1.5, (n, V))
+    t = rng.normal(0, 1.5, (n + 1, V))
+    q, p = _softmax(z, T), _softmax(t, T)
+    d = np.stack([rng.choice(V, size=N, p=q[j]) for j in range(n)], axis=1)
+    au = rng.random((N, n))
+    ru = rng.random((N, V))
+    tau, nxt, info = o.sample_accept(d, np.broadcast_to(z, (N, n, V)), np.broadcast_to(t, (N, n + 1, V)),
+                                     T, au, ru)
+    assert np.all((tau >= 1) & (tau <= n + 1))
+    com = _committed(d, tau, nxt)
+    for k in range(n + 1):
+        toks = np.array([c[k] for c in com if len(c) > k])
+        ok, f = _freq_ok(toks, p[k])
+        assert ok, (k, f, p[k])
+    beta = np.minimum(p[:n], q).sum(axis=1)
+    reach = 1.0
+    for k in range(n + 1):
+        emp = np.mean(tau >= k + 1)
+        assert abs(emp - reach) <= 5 * math.sqrt(max(reach * (1 - reach), 1e-12) / N) + 1e-12, (k, emp, reach)
+        if k < n:
+            reach *= beta[k]
+
+
+def pin_sample_accept_cases(o):
+    V, n, T = 8, 3, 1.0
+    rng = _rng(34)
+    z = rng.normal(0, 1, (1, n, V))
+    d = np.array([[2, 5, 1]])
+    ru = rng.random((1, V))
+    # identical draft and target distributions: everything is accepted (u < 1)
+    t = np.concatenate([z, np.zeros((1, 1, V))], axis=1)
+    t[0, n, 6] = 60.0                                   # bonus row: one-hot on 6
+    tau, nxt, _ = o.sample_accept(d, z, t, T, np.full((1, n), 0.999), ru)
+    assert tau[0] == n + 1 and nxt[0] == 6
+    # the target gives draft 0 (almost) no mass and peaks on token 7: rejected at
+    # 0, and the residual max(0, p - q) is (almost) all on token 7
+    t2 = t.copy()
+    t2[0, 0] = 0.0
+    t2[0, 0, 7] = 60.0
+    tau, nxt, info = o.sample_accept(d, z, t2, T, np.full((1, n), 1e-9), ru)
+    assert tau[0] == 1 and nxt[0] == 7 and info["m"][0] == 0
+    # p(d_j) > q(d_j) is accepted whatever the uniform; rejection at 1 from a
+    # target that puts no mass on d_1 = 5
+    t3 = t.copy()
+    t3[0, 0, 2] = z[0, 0, 2] + 3.0
+    t3[0, 1, 5] = -60.0
+    tau, nxt, info = o.sample_accept(d, z, t3, T, np.array([[0.999999, 1e-9, 0.5]]), ru)
+    assert tau[0] == 2 and nxt[0] != 5 and info["log_ratio"][0, 0] > 0
+    # a rejection with p == q (only a uniform of 1 rejects) leaves an empty
+    # residual: the draw then comes from p_m itself
+    t4 = t.copy()
+    t4[0, 1] = z[0, 1]
+    z4 = z.copy()
+    z4[0, 1, 3] = 60.0
+    t4[0, 1, 3] = 60.0
+    tau, nxt, info = o.sample_accept(d, z4, t4, T, np.array([[0.5, 1.0, 0.5]]), ru)
+    assert tau[0] == 2 and nxt[0] == 3 and info["resid_empty"][0]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -50,3 +50,32 @@ def test_block_tokens_and_targets():
     assert tgt.shape == (16, 16)
     assert np.array_equal(tgt[:, :15] == d, match)
     assert np.all((tgt >= 0) & (tgt < cfg.V))
+
+
+def test_sampling_uniforms_open_and_exact():
+    cfg = shrink(CONFIGS[2], V=5000, B=2)
+    inp = Inputs(cfg)
+    g, a, e = inp.sample_uniforms(0, 16)
+    assert g.shape == (2, 15, 5000) and a.shape == (2, 15) and e.shape == (2, 5000)
+    for u in (g, a, e):
+        assert u.dtype == np.float32 and u.min() > 0.0 and u.max() < 1.0
+        k = u.astype(np.float64) * 2.0 ** 24               # odd integers: exact in float32
+        assert np.array_equal(k, np.round(k)) and np.all(np.round(k) % 2 == 1)
+    g2, _, _ = Inputs(cfg).sample_uniforms(0, 16)
+    assert np.array_equal(g, g2)
+    assert not np.array_equal(g, inp.sample_uniforms(1, 16)[0])
+    assert abs(g.mean() - 0.5) < 0.01
+
+
+def test_synthetic_target_logits():
+    from dflash_inputs import build_target_logits_np
+    cfg = shrink(CONFIGS[2], V=3000, B=2)
+    inp = Inputs(cfg)
+    z = inp.synthetic_logits(0, 16, 1.28)
+    nz = inp.target_noise(0, 16)
+    t = build_target_logits_np(z, nz)
+    assert t.shape == (2, 16, 3000) and abs(z.std() - 1.28) < 0.02
+    assert np.allclose(t[:, :15] - z, 0.5 * nz[:, :15], atol=1e-6)
+    assert np.array_equal(t[:, 15], nz[:, 15])
+    ids = inp.random_ids(0, 16)
+    assert ids.shape == (2, 15) and ids.min() >= 0 and ids.max() < 3000

@@ -54,6 +54,33 @@ MUTANTS = [
     ("accept_counts_all_matches", "while m < n and int(draft[b, m]) == int(target[b, m]):\n            m += 1",
      "m = int(np.sum(draft[b] == target[b, :n]))"),
     ("accept_next_is_draft", "nxt[b] = target[b, m]", "nxt[b] = draft[b, min(m, n - 1)]"),
+    ("gumbel_sign", "key = np.asarray(logw, dtype=F64) - np.log(-np.log(",
+     "key = np.asarray(logw, dtype=F64) + np.log(-np.log("),
+    ("gumbel_plain_uniform", "key = np.asarray(logw, dtype=F64) - np.log(-np.log(np.asarray(u, dtype=F64)))",
+     "key = np.asarray(logw, dtype=F64) + np.asarray(u, dtype=F64)"),
+    ("gumbel_last_tie", "idx = np.argmax(key, axis=-1)",
+     "idx = key.shape[-1] - 1 - np.argmax(key[..., ::-1], axis=-1)"),
+    ("log_softmax_no_temperature", "x = np.asarray(logits, dtype=F64) / float(T)\n    mx = np.max(x, axis=-1, keepdims=True)",
+     "x = np.asarray(logits, dtype=F64)\n    mx = np.max(x, axis=-1, keepdims=True)"),
+    ("lse_drops_max", "return mx + np.log(np.sum(np.exp(x - mx[..., None]), axis=-1))",
+     "return np.log(np.sum(np.exp(x - mx[..., None]), axis=-1))"),
+    ("sample_no_temperature", "draft, gap = gumbel_pick(z / float(T), u)", "draft, gap = gumbel_pick(z, u)"),
+    ("sample_includes_anchor", "z = np.asarray(h_final, dtype=F64)[:, 1:, :] @ np.asarray(lm_head",
+     "z = np.asarray(h_final, dtype=F64)[:, :-1, :] @ np.asarray(lm_head"),
+    ("accept_ratio_inverted", "log_ratio = lp[:, :n][bi, ji, draft] - lq[bi, ji, draft]",
+     "log_ratio = lq[bi, ji, draft] - lp[:, :n][bi, ji, draft]"),
+    ("accept_ratio_next_row", "log_ratio = lp[:, :n][bi, ji, draft] - lq[bi, ji, draft]",
+     "log_ratio = lp[:, 1:][bi, ji, draft] - lq[bi, ji, draft]"),
+    ("accept_always_capped_half", "accepted = np.asarray(accept_u, dtype=F64) < np.exp(log_ratio)",
+     "accepted = np.asarray(accept_u, dtype=F64) < np.minimum(0.5, np.exp(log_ratio))"),
+    ("resid_from_p", "logw = lp[b, m] if empty[b] else np.log(r)", "logw = lp[b, m]"),
+    ("resid_q_minus_p", "r = np.maximum(0.0, np.exp(lp[b, m]) - np.exp(lq[b, m]))",
+     "r = np.maximum(0.0, np.exp(lq[b, m]) - np.exp(lp[b, m]))"),
+    ("bonus_from_draft_row", "logw = lp[b, n]", "logw = lq[b, n - 1]"),
+    ("sample_tau_no_bonus", "m_all[b], tau[b], nxt[b], key_gap[b] = m, m + 1, tok, gap",
+     "m_all[b], tau[b], nxt[b], key_gap[b] = m, max(m, 1), tok, gap"),
+    ("sample_counts_all_accepts", "while m < n and accepted[b, m]:\n            m += 1",
+     "m = int(np.sum(accepted[b]))"),
 ]
 
 
