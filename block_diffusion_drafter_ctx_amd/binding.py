@@ -19,7 +19,8 @@ ARGMAX, ACCEPT = 1, 2
 MAX_BATCH, MAX_TGT_LAYERS, MIN_GAMMA, MAX_GAMMA = 64, 8, 2, 33
 
 EXPORTED = ("dflash_version", "dflash_last_error", "dflash_workspace_size", "dflash_fuse_context",
-            "dflash_inject_kv", "dflash_draft_forward", "dflash_argmax_accept", "dflash_profile_events")
+            "dflash_inject_kv", "dflash_draft_forward", "dflash_argmax_accept", "dflash_sample_drafts",
+            "dflash_sample_accept", "dflash_profile_events")
 PROF_NONE, PROF_LM_HEAD, PROF_QKV, PROF_O, PROF_GATEUP, PROF_DOWN, PROF_FUSE, PROF_INJECT, PROF_ATTENTION = range(9)
 
 
@@ -76,6 +77,13 @@ def load():
     lib.dflash_argmax_accept.argtypes = [POINTER(Dims), POINTER(Weights), c_uint32, c_void_p, c_int32, c_int32,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_size_t, c_void_p]
+    lib.dflash_sample_drafts.restype = c_int32
+    lib.dflash_sample_drafts.argtypes = [POINTER(Dims), POINTER(Weights), c_void_p, c_int32, c_int32, c_float,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dflash_sample_accept.restype = c_int32
+    lib.dflash_sample_accept.argtypes = [POINTER(Dims), c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                         c_void_p]
     lib.dflash_profile_events.restype = c_int32
     lib.dflash_profile_events.argtypes = [c_int32, POINTER(c_void_p), POINTER(c_void_p), c_int32, POINTER(c_int32)]
     _lib = lib
@@ -129,6 +137,20 @@ def argmax_accept(dims: Dims, w: Weights, flags: int, h_final, B: int, gamma: in
     _check(load().dflash_argmax_accept(ctypes.byref(dims), ctypes.byref(w) if w is not None else None, flags,
                                        _p(h_final), B, gamma, _p(draft), _p(target), _p(tau), _p(next_anchor),
                                        _p(logits_dbg), _p(top2_gap), _p(ws), ws_bytes, _p(stream)))
+
+
+def sample_drafts(dims: Dims, w: Weights, h_final, B: int, gamma: int, temperature: float, uniforms, draft,
+                  logits, lse, ws, ws_bytes: int, stream=0):
+    _check(load().dflash_sample_drafts(ctypes.byref(dims), ctypes.byref(w) if w is not None else None,
+                                       _p(h_final), B, gamma, temperature, _p(uniforms), _p(draft), _p(logits),
+                                       _p(lse), _p(ws), ws_bytes, _p(stream)))
+
+
+def sample_accept(dims: Dims, B: int, gamma: int, temperature: float, draft, draft_logits, draft_lse,
+                  target_logits, accept_u, resid_u, tau, next_anchor, ws, ws_bytes: int, stream=0):
+    _check(load().dflash_sample_accept(ctypes.byref(dims), B, gamma, temperature, _p(draft), _p(draft_logits),
+                                       _p(draft_lse), _p(target_logits), _p(accept_u), _p(resid_u), _p(tau),
+                                       _p(next_anchor), _p(ws), ws_bytes, _p(stream)))
 
 
 _prof_keep = None

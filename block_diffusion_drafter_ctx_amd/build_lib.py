@@ -25,7 +25,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["gemm.hip", "epilogue.hip", "attention.hip", "dflash.cpp"]
+SOURCES = ["gemm.hip", "epilogue.hip", "attention.hip", "sampling.hip", "dflash.cpp"]
 
 
 def _compile(src: str) -> str:

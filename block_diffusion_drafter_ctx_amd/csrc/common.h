@@ -181,4 +181,63 @@ __device__ __forceinline__ Top2 top2_shfl_xor(Top2 a, int m) {
   return b;
 }
 
+// Temperature sampling statistics of (a piece of) one logits row: the best
+// Gumbel-perturbed key with its index ("larger key, then lower index"), and the
+// running log-sum-exp state of x = logit / T as (mx, se) with
+// sum exp(x) = se * exp(mx).  An empty piece is {-inf, INT_MAX, -inf, 0}.
+struct SampleStat {
+  float key;
+  int idx;
+  float mx;
+  float se;
+};
+
+__device__ __forceinline__ SampleStat sstat_empty() { return SampleStat{-INFINITY, 0x7fffffff, -INFINITY, 0.f}; }
+
+// A standard Gumbel variate from a uniform u in (0, 1).
+__device__ __forceinline__ float gumbel_noise(float u) { return -logf(-logf(u)); }
+
+__device__ __forceinline__ void sstat_push_lse(SampleStat& s, float x) {
+  if (x > s.mx) {
+    s.se = s.se * expf(s.mx - x) + 1.f;
+    s.mx = x;
+  } else {
+    s.se += expf(x - s.mx);
+  }
+}
+
+__device__ __forceinline__ void sstat_push_key(SampleStat& s, float key, int i) {
+  if (better(key, i, s.key, s.idx)) {
+    s.key = key;
+    s.idx = i;
+  }
+}
+
+__device__ __forceinline__ SampleStat sstat_merge(SampleStat a, SampleStat b) {
+  SampleStat r;
+  const bool bk = better(b.key, b.idx, a.key, a.idx);
+  r.key = bk ? b.key : a.key;
+  r.idx = bk ? b.idx : a.idx;
+  r.mx = fmaxf(a.mx, b.mx);
+  r.se = r.mx == -INFINITY ? 0.f : a.se * expf(a.mx - r.mx) + b.se * expf(b.mx - r.mx);
+  return r;
+}
+
+__device__ __forceinline__ SampleStat sstat_shfl_xor(SampleStat a, int m) {
+  SampleStat b;
+  b.key = __shfl_xor(a.key, m, kWave);
+  b.idx = __shfl_xor(a.idx, m, kWave);
+  b.mx = __shfl_xor(a.mx, m, kWave);
+  b.se = __shfl_xor(a.se, m, kWave);
+  return b;
+}
+
+__device__ __forceinline__ float4 sstat_pack(SampleStat s) {
+  return make_float4(s.key, __int_as_float(s.idx), s.mx, s.se);
+}
+
+__device__ __forceinline__ SampleStat sstat_unpack(float4 v) {
+  return SampleStat{v.x, __float_as_int(v.y), v.z, v.w};
+}
+
 }  // namespace dflash

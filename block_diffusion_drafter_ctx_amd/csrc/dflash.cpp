@@ -251,6 +251,60 @@ ArgmaxWs argmax_ws(const dflash_dims* d, int B, int gamma) {
   return w;
 }
 
+// Sampled drafting: the LM head's split-K partials (streaming kernel, bf16
+// weights with more than 16 rows) and the per-row sampling statistics
+// [pieces][M] (one piece per register-K workgroup or per column chunk).
+struct SampleWs {
+  size_t part, stats, total;
+};
+
+SampleWs sample_ws(const dflash_dims* d, int B, int gamma) {
+  const int M = B * (gamma - 1);
+  SampleWs w{};
+  Carve c;
+  const size_t nchunk = static_cast<size_t>((d->V + sample_chunk(d->V) - 1) / sample_chunk(d->V));
+  size_t pieces = nchunk;
+  if (d->dtype == DFLASH_BF16) {
+    const GemmPlan rk = plan_gemm_rk(M, d->V, d->D, true);
+    if (rk.rk) {
+      if (static_cast<size_t>(rk.grid) > pieces) pieces = rk.grid;
+    } else {
+      w.part = c.take(plan_gemm(M, d->V, d->D, A_F32_SPLIT, true).part_floats * 4);
+    }
+  }
+  w.stats = c.take(pieces * M * sizeof(float4));
+  w.total = c.off;
+  return w;
+}
+
+// Sampled verification: row statistics of the target rows (and of the draft
+// rows when their log-normalisers are not given), the per-chunk candidate
+// draws and the first-rejection index.
+struct AcceptWs {
+  size_t stats, part, m, total;
+  int chunk, nchunk, rows;
+};
+
+AcceptWs sample_accept_ws(const dflash_dims* d, int B, int gamma, bool lse_given) {
+  const int n = gamma - 1;
+  AcceptWs w{};
+  w.chunk = sample_chunk(d->V);
+  w.nchunk = (d->V + w.chunk - 1) / w.chunk;
+  w.rows = B * (n + 1) + (lse_given ? 0 : B * n);
+  Carve c;
+  w.stats = c.take(static_cast<size_t>(w.nchunk) * w.rows * sizeof(float4));
+  w.part = c.take(static_cast<size_t>(B) * w.nchunk * sizeof(float4));
+  w.m = c.take(static_cast<size_t>(B) * 4);
+  w.total = c.off;
+  return w;
+}
+
+dflash_status check_temperature(float T) {
+  DF_REQUIRE(std::isfinite(T) && T > 0.f && std::isfinite(1.0f / T), DFLASH_ERR_INVALID_ARG,
+             "temperature=%g must be positive and finite (with a finite reciprocal)", static_cast<double>(T));
+  return DFLASH_OK;
+}
+
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // ---------------------------------------------------------- profiling hook
@@ -314,8 +368,11 @@ dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t 
   for (int b = 1; b <= B; ++b)
     for (int g = DFLASH_MIN_GAMMA; g <= gamma; ++g) {
       const size_t dw = draft_ws(dims, b, g).total, aw = argmax_ws(dims, b, g).total;
+      const size_t sw = sample_ws(dims, b, g).total, vw = sample_accept_ws(dims, b, g, false).total;
       if (dw > need) need = dw;
       if (aw > need) need = aw;
+      if (sw > need) need = sw;
+      if (vw > need) need = vw;
     }
   const size_t f = fuse_ws(dims, max_rows), i = inject_ws(dims, max_rows);
   if (f > need) need = f;
@@ -707,6 +764,143 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
     }
   }
   if (flags & DFLASH_ACCEPT) DF_HIP(launch_accept(draft, target, B, n, tau, next_anchor, s));
+  return ok();
+}
+
+dflash_status dflash_sample_drafts(const dflash_dims* dims, const dflash_weights* w, const float* h_final,
+                                   int32_t B, int32_t gamma, float temperature, const float* uniforms,
+                                   int32_t* draft, float* logits, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_gamma(gamma)) != DFLASH_OK) return st;
+  if ((st = check_temperature(temperature)) != DFLASH_OK) return st;
+  DF_REQUIRE(B >= 1 && B <= DFLASH_MAX_BATCH, DFLASH_ERR_INVALID_ARG, "B=%d outside [1, %d]", B, DFLASH_MAX_BATCH);
+  DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
+  if ((st = check_ptr(w->lm_head, "lm_head")) != DFLASH_OK) return st;
+  if ((st = check_ptr(h_final, "h_final")) != DFLASH_OK) return st;
+  if ((st = check_ptr(uniforms, "uniforms")) != DFLASH_OK) return st;
+  if ((st = check_ptr(logits, "logits")) != DFLASH_OK) return st;
+  DF_REQUIRE(draft != nullptr, DFLASH_ERR_INVALID_ARG, "draft is NULL");
+  const SampleWs lay = sample_ws(dims, B, gamma);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != DFLASH_OK) return st;
+  if ((st = check_device()) != DFLASH_OK) return st;
+
+  hipStream_t s = as_stream(stream);
+  const int n = gamma - 1, Mr = B * n, D = dims->D, V = dims->V;
+  const float inv_t = 1.0f / temperature;
+  char* base = static_cast<char*>(ws);
+  float4* stats = reinterpret_cast<float4*>(base + lay.stats);
+  GemmArgs g{};
+  for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = h_final + D;   // block row 1 of sequence 0
+  g.a_cols = D;
+  g.a_rg = n;
+  g.a_gs = static_cast<int64_t>(gamma) * D;
+  g.a_ld = D;
+  g.w = w->lm_head;
+  g.w_ld = D;
+  g.w_rg = INT_MAX;
+  g.w_gs = 0;
+  g.w_off = 0;
+  g.M = Mr;
+  g.N = V;
+  g.K = D;
+  g.su = uniforms;
+  g.inv_t = inv_t;
+  RowStatArgs r{};
+  r.rows1 = r.rows = Mr;
+  r.N = V;
+  r.chunk = sample_chunk(V);
+  r.vec = V % 4 == 0;
+  r.su = uniforms;
+  r.inv_t = inv_t;
+  r.stats = stats;
+  r.S = 1;
+  const int nchunk = (V + r.chunk - 1) / r.chunk;
+  if (dims->dtype == DFLASH_BF16) {
+    const GemmPlan rk = plan_gemm_rk(Mr, V, D, true);
+    if (rk.rk) {
+      // one pass over the LM head: logits stored, sampling statistics per workgroup
+      const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
+      DF_HIP(launch_gemm_rk_sample(g, rk, stats, logits, s));
+      prof_end(ps, s);
+      DF_HIP(launch_sample_final(stats, rk.grid, Mr, draft, lse, s));
+      return ok();
+    }
+    const GemmPlan p = plan_gemm(Mr, V, D, A_F32_SPLIT, true);
+    g.part = reinterpret_cast<float*>(base + lay.part);
+    const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
+    DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, s));
+    prof_end(ps, s);
+    r.src = g.part;
+    r.S = p.S;
+    r.split_stride = static_cast<int64_t>(Mr) * V;
+    r.logits_out = logits;
+  } else {
+    g.part = logits;
+    DF_HIP(launch_gemm_f32(g, s));
+    r.src = logits;
+  }
+  DF_HIP(launch_row_stats(r, s));
+  DF_HIP(launch_sample_final(stats, nchunk, Mr, draft, lse, s));
+  return ok();
+}
+
+dflash_status dflash_sample_accept(const dflash_dims* dims, int32_t B, int32_t gamma, float temperature,
+                                   const int32_t* draft, const float* draft_logits, const float* draft_lse,
+                                   const float* target_logits, const float* accept_u, const float* resid_u,
+                                   int32_t* tau, int32_t* next_anchor, void* ws, size_t ws_bytes, void* stream) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_gamma(gamma)) != DFLASH_OK) return st;
+  if ((st = check_temperature(temperature)) != DFLASH_OK) return st;
+  DF_REQUIRE(B >= 1 && B <= DFLASH_MAX_BATCH, DFLASH_ERR_INVALID_ARG, "B=%d outside [1, %d]", B, DFLASH_MAX_BATCH);
+  if ((st = check_ptr(draft_logits, "draft_logits")) != DFLASH_OK) return st;
+  if ((st = check_ptr(target_logits, "target_logits")) != DFLASH_OK) return st;
+  if ((st = check_ptr(resid_u, "resid_u")) != DFLASH_OK) return st;
+  DF_REQUIRE(draft != nullptr && accept_u != nullptr && tau != nullptr && next_anchor != nullptr,
+             DFLASH_ERR_INVALID_ARG, "draft, accept_u, tau and next_anchor must be non-NULL");
+  const AcceptWs lay = sample_accept_ws(dims, B, gamma, draft_lse != nullptr);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != DFLASH_OK) return st;
+  if ((st = check_device()) != DFLASH_OK) return st;
+
+  hipStream_t s = as_stream(stream);
+  const int n = gamma - 1, V = dims->V;
+  const float inv_t = 1.0f / temperature;
+  char* base = static_cast<char*>(ws);
+  RowStatArgs r{};
+  r.src = target_logits;
+  r.S = 1;
+  r.rows1 = B * (n + 1);
+  r.src2 = draft_logits;
+  r.rows = lay.rows;
+  r.N = V;
+  r.chunk = lay.chunk;
+  r.vec = V % 4 == 0;
+  r.inv_t = inv_t;
+  r.stats = reinterpret_cast<float4*>(base + lay.stats);
+  DF_HIP(launch_row_stats(r, s));
+  SpecArgs a{};
+  a.draft = draft;
+  a.zq = draft_logits;
+  a.zp = target_logits;
+  a.lse_q = draft_lse;
+  a.accept_u = accept_u;
+  a.resid_u = resid_u;
+  a.stats = r.stats;
+  a.B = B;
+  a.n = n;
+  a.V = V;
+  a.chunk = lay.chunk;
+  a.nchunk = lay.nchunk;
+  a.rows = lay.rows;
+  a.vec = r.vec;
+  a.inv_t = inv_t;
+  a.part = reinterpret_cast<float4*>(base + lay.part);
+  a.m_out = reinterpret_cast<int32_t*>(base + lay.m);
+  a.tau = tau;
+  a.next_anchor = next_anchor;
+  DF_HIP(launch_spec_verify(a, s));
   return ok();
 }
 

@@ -221,23 +221,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(GemmArgs g) {
 // MFMAs retire).  The sixteen per-wave partial tiles are summed through LDS
 // in wave order (deterministic).  Epilogues: the [split][M][N] store; the LM
 // head's running top-2 per row (plus the logits when asked for), merged per
-// workgroup into top2[block][m] = (best value, its index, runner-up); or the
+// workgroup into top2[block][m] = (best value, its index, runner-up); the LM
+// head's temperature-sampling statistics (logits stored, then per row the best
+// Gumbel-perturbed key x + G(u) with x = logit / T, and the log-sum-exp state of
+// x), merged per workgroup into stats[block][m]; or the
 // FFN's SwiGLU, where a tile holds 8 gate rows and the 8 matching up rows of
 // the stacked [gate; up] weight, so s = silu(gate) * up leaves the kernel
 // directly (N = F outputs, 8 per tile).
 constexpr int kRkWaves = 16;
 constexpr int kRkMinN = 16384;   // weight rows below which the split-K streaming kernel wins
 
-enum RkEpilogue { RK_PART = 0, RK_TOP2 = 1, RK_SWIGLU = 2 };
+enum RkEpilogue { RK_PART = 0, RK_TOP2 = 1, RK_SWIGLU = 2, RK_SAMPLE = 3 };
 
 template <int KS, int EP, int T, int AK = A_F32_SPLIT>
 __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, float* top2, float* logits) {
   constexpr bool TOP2 = EP == RK_TOP2;
+  constexpr bool SAMPLE = EP == RK_SAMPLE;
   constexpr int TN = EP == RK_SWIGLU ? 8 : 16;   // outputs per tile
   static_assert(EP == RK_PART || T == 1, "fused epilogues stream one tile at a time");
   __shared__ float red[2][kRkWaves][T][256];
   __shared__ float tv1[4][16], tv2[4][16];
   __shared__ int ti1[4][16];
+  __shared__ float4 sst[4][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = g.S;
   const int units = S * g.ntiles;
@@ -306,10 +311,16 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
   const int ln = tid >> 2;
   const int mo = ln & 15, no = 4 * (ln >> 4) + (tid & 3);
   Top2 best{-INFINITY, 0x7fffffff, -INFINITY};
+  SampleStat ss = sstat_empty();
   int buf = 0;
   for (int q = 0;; ++q) {
     const int ub = u0 + P * T * q;
     const bool more = ub + P * T < units;     // uniform per workgroup
+    float su = 0.5f;                          // this thread's sampling uniform, fetched before the MFMAs
+    if constexpr (SAMPLE) {
+      const int n = (ub / S) * TN + no;
+      if (tid < 256 && mo < g.M && n < g.N) su = g.su[static_cast<int64_t>(mo) * g.N + n];
+    }
     f32x4_t acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -363,6 +374,11 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
             if constexpr (TOP2) {
               if (logits != nullptr) logits[static_cast<int64_t>(mo) * g.N + n] = v;
               best = top2_push(best, v, n);
+            } else if constexpr (SAMPLE) {
+              logits[static_cast<int64_t>(mo) * g.N + n] = v;
+              const float x = v * g.inv_t;
+              sstat_push_lse(ss, x);
+              sstat_push_key(ss, x + gumbel_noise(su), n);
             } else {
               g.part[(static_cast<int64_t>(sp) * g.M + mo) * g.N + n] = v;
             }
@@ -394,6 +410,21 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
       o[0] = t.v1;
       o[1] = __int_as_float(t.i1);
       o[2] = t.v2;
+    }
+  }
+  if constexpr (SAMPLE) {
+    // same owner layout as the top-2 merge
+    if (tid < 256) {
+      ss = sstat_merge(ss, sstat_shfl_xor(ss, 1));
+      ss = sstat_merge(ss, sstat_shfl_xor(ss, 2));
+      if ((lane & 3) == 0) sst[wave][lane >> 2] = sstat_pack(ss);
+    }
+    __syncthreads();
+    if (tid < 16 && tid < g.M) {
+      SampleStat t = sstat_unpack(sst[0][tid]);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) t = sstat_merge(t, sstat_unpack(sst[w][tid]));
+      reinterpret_cast<float4*>(top2)[static_cast<int64_t>(blockIdx.x) * g.M + tid] = sstat_pack(t);
     }
   }
 }
@@ -1089,6 +1120,23 @@ hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, fl
       hipLaunchKernelGGL((gemm_rk_kernel<2, RK_PART, 2>), grid, block, 0, st, a, nullptr, nullptr);
     }
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_rk_sample(const GemmArgs& a0, const GemmPlan& p, float4* stats, float* logits,
+                                 hipStream_t st) {
+  if (!p.rk || p.S != 1 || a0.a_cols % (32 * p.ks) != 0 || stats == nullptr || logits == nullptr ||
+      a0.su == nullptr)
+    return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  a.S = 1;
+  a.ntiles = p.ntiles;
+  a.mtiles = 1;
+  a.chunks_per_split = p.cps;
+  float* sp = reinterpret_cast<float*>(stats);
+  const dim3 grid(p.grid), block(64 * kRkWaves);
+  if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_SAMPLE, 1>), grid, block, 0, st, a, sp, logits);
+  else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_SAMPLE, 1>), grid, block, 0, st, a, sp, logits);
   return hipGetLastError();
 }
 

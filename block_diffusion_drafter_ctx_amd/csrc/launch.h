@@ -30,6 +30,8 @@ struct GemmArgs {
   int32_t S, ntiles, mtiles;  // work decomposition (MFMA path; set by the launcher)
   float* part;                // [S][M][N]
   const void* a_lo;           // A_BF16_HILO: the lo plane, laid out like a_src[0] (the hi plane)
+  const float* su;            // LM-head sampling epilogue: uniforms [M][N] in (0, 1)
+  float inv_t;                // LM-head sampling epilogue: 1 / temperature
 };
 
 // exact bf16 A; fp32 A split hi/lo on the fly; or A given as pre-split bf16
@@ -66,6 +68,11 @@ GemmPlan plan_gemm_rk(int M, int N, int K, bool top2);
 // logits != nullptr, the logits [M][N].
 hipError_t launch_gemm_rk(const GemmArgs& a, const GemmPlan& p, float* top2, float* logits, hipStream_t st,
                           GemmAKind ak = A_F32_SPLIT);
+// LM head with the temperature-sampling epilogue (plan from plan_gemm_rk(.., true)):
+// stores logits [M][N] and writes each workgroup's per-row SampleStat (key over
+// x + G(a.su), x = logit * a.inv_t) to stats [p.grid][M].
+hipError_t launch_gemm_rk_sample(const GemmArgs& a, const GemmPlan& p, float4* stats, float* logits,
+                                 hipStream_t st);
 // FFN gate/up with SwiGLU fused: W is the stacked [gate (F rows); up (F rows)]
 // weight, a.N = F; writes s_out[m][f] = silu(gate) * up.  plan.rk is false when
 // the shape does not qualify (the caller then runs the GEMM and swiglu apart).
@@ -131,6 +138,57 @@ hipError_t launch_argmax_rows(const float* logits, int M, int V, int32_t* draft,
 
 hipError_t launch_accept(const int32_t* draft, const int32_t* target, int B, int n, int32_t* tau,
                          int32_t* next_anchor, hipStream_t st);
+
+// ------------------------------------------------------------ sampling
+constexpr int kSampleChunk = 4096;   // columns per row-statistics workgroup (at least)
+constexpr int kSpecMaxChunks = 64;   // row-statistics pieces per row, at most
+constexpr int kSpecMaxN = 32;        // drafts per block, at most
+
+// Row-statistics pass.  Rows [0, rows1) read src + r*N, summing S split-K
+// partials split_stride apart; rows [rows1, rows) read src2 + (r - rows1)*N.
+// Per (row, chunk of `chunk` columns) it writes stats[chunk][row]: the
+// log-sum-exp state of x = value * inv_t and, when su is given (rows of src
+// only, su [rows1][N]), the best Gumbel key x + G(su).  logits_out (nullable)
+// receives the summed src rows.
+struct RowStatArgs {
+  const float* src;
+  int64_t split_stride;
+  int32_t S;
+  const float* src2;
+  int32_t rows1, rows, N, chunk;
+  int32_t vec;             // 1: N % 4 == 0 and every row 16-byte aligned
+  float* logits_out;
+  const float* su;
+  float inv_t;
+  float4* stats;
+};
+
+// Columns per row-statistics chunk for a vocabulary of V (a multiple of
+// kSampleChunk; at most kSpecMaxChunks chunks per row).
+int sample_chunk(int V);
+hipError_t launch_row_stats(const RowStatArgs& a, hipStream_t st);
+// merge stats [nparts][M] per row: draft[m] = best key's index, lse[m] (nullable)
+// = log sum exp(x)
+hipError_t launch_sample_final(const float4* stats, int nparts, int M, int32_t* draft, float* lse, hipStream_t st);
+
+// Lossless verification of a sampled block (spec_verify + spec_final kernels).
+struct SpecArgs {
+  const int32_t* draft;    // [B][n]
+  const float* zq;         // draft logits [B][n][V]
+  const float* zp;         // target logits [B][n+1][V]
+  const float* lse_q;      // nullable [B][n]: log sum exp(zq / T) of the draft rows
+  const float* accept_u;   // [B][n]
+  const float* resid_u;    // [B][V]
+  const float4* stats;     // row statistics [nchunk][rows]: target row j of sequence b at
+                           // b*(n+1)+j, then (lse_q null) draft rows at B*(n+1)+b*n+j
+  int32_t B, n, V, chunk, nchunk, rows, vec;
+  float inv_t;
+  float4* part;            // scratch [B][nchunk]
+  int32_t* m_out;          // scratch [B]
+  int32_t* tau;            // out [B]
+  int32_t* next_anchor;    // out [B]
+};
+hipError_t launch_spec_verify(const SpecArgs& a, hipStream_t st);
 
 // ------------------------------------------------------------ attention
 struct AttnArgs {

@@ -129,3 +129,16 @@ class DeviceDrafter:
         p = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
         B.argmax_accept(self.dims, self.weights, flags, p(h_final), B_, gamma, p(draft), p(target), p(tau),
                         p(nxt), p(logits), p(gap), p(self.ws), self.ws_bytes, _stream())
+
+    # ---- sampled drafting and verification (temperature T > 0)
+    def sample_drafts(self, h_final, B_, gamma, temperature, uniforms, draft, logits, lse=None):
+        p = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+        B.sample_drafts(self.dims, self.weights, p(h_final), B_, gamma, temperature, p(uniforms), p(draft),
+                        p(logits), p(lse), p(self.ws), self.ws_bytes, _stream())
+
+    def sample_accept(self, B_, gamma, temperature, draft, draft_logits, target_logits, accept_u, resid_u, tau,
+                      nxt, draft_lse=None):
+        p = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+        B.sample_accept(self.dims, B_, gamma, temperature, p(draft), p(draft_logits), p(draft_lse),
+                        p(target_logits), p(accept_u), p(resid_u), p(tau), p(nxt), p(self.ws), self.ws_bytes,
+                        _stream())

@@ -10,6 +10,10 @@
  *                             rows), bidirectional over [context ; block]
  *   dflash_argmax_accept  (d) LM-head argmax of the mask rows and greedy
  *                             acceptance length against the target's tokens
+ * and, for decoding at a temperature T > 0, the sampled counterpart of (d):
+ *   dflash_sample_drafts  draft tokens drawn from softmax(logits / T)
+ *   dflash_sample_accept  lossless acceptance of a sampled block against the
+ *                         target's temperature-T distributions
  *
  * Sources (page titles as published):
  *   [JP] "DFlash: Block Diffusion for Flash Speculative Decoding 논문 정리"
@@ -199,10 +203,57 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
                                    float* logits_dbg, float* top2_gap, void* ws, size_t ws_bytes,
                                    void* stream);
 
+/* Sampled drafting at temperature T ([JP] "주요 결과": DFlash decodes at
+ * temperature 1 as well as greedily; [JP] "학습 방법": all block positions after
+ * the anchor are predicted in one parallel pass).  For block rows i = 1..gamma-1
+ * of each sequence: z = lm_head . h_final[b][i] (the logits of
+ * dflash_argmax_accept), and draft[b][i-1] is one draw from q = softmax(z / T)
+ * made with the Gumbel-max rule: the token v maximising
+ * z_v / T - log(-log uniforms[b][i-1][v]) (lowest id on ties).
+ *   h_final      [B][gamma][D] float32
+ *   temperature  T > 0, finite, with a finite 1/T (the kernels use 1/T in fp32)
+ *   uniforms     [B][gamma-1][V] float32, every value strictly inside (0, 1)
+ *                (a 0 never wins, a 1 always wins)
+ *   draft        out [B][gamma-1] int32
+ *   logits       out [B][gamma-1][V] float32: z (needed by dflash_sample_accept)
+ *   lse          nullable out [B][gamma-1] float32: log sum_v exp(z_v / T)
+ * Uses weights->lm_head.  Workspace: dflash_workspace_size. */
+dflash_status dflash_sample_drafts(const dflash_dims* dims, const dflash_weights* w, const float* h_final,
+                                   int32_t B, int32_t gamma, float temperature, const float* uniforms,
+                                   int32_t* draft, float* logits, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* Lossless acceptance of a sampled block ([GL] "비용 구조의 차이가 만드는 성능
+ * 격차": through rejection/acceptance sampling the emitted tokens follow the
+ * target model's own distribution).  With n = gamma-1, q_j = softmax(draft_logits
+ * [b][j] / T) and p_j = softmax(target_logits[b][j] / T):
+ *   draft j is accepted when accept_u[b][j] < p_j(d_j) / q_j(d_j), in order
+ *   j = 0, 1, ...; the first j that fails is m (m = n if none fails);
+ *   m < n: the emitted token is a draw from max(0, p_m - q_m) (normalised), or
+ *          from p_m when that residual has no positive entry (rounding only);
+ *   m = n: the emitted token is the bonus, a draw from p_n;
+ *   both draws use the Gumbel-max rule with resid_u[b][:] (as in
+ *   dflash_sample_drafts).  tau[b] = m + 1 tokens are committed: d_0..d_{m-1}
+ *   and the emitted token, returned as next_anchor[b].
+ *   draft          [B][n] int32 (ids outside [0, V) are clamped)
+ *   draft_logits   [B][n][V] float32 (the logits output of dflash_sample_drafts)
+ *   draft_lse      nullable [B][n] float32: log sum exp(draft_logits / T) as
+ *                  written by dflash_sample_drafts; NULL = computed here
+ *   target_logits  [B][n+1][V] float32: the target's logits at each draft
+ *                  position, then at the bonus position
+ *   accept_u       [B][n] float32 uniforms in [0, 1]
+ *   resid_u        [B][V] float32 uniforms strictly inside (0, 1)
+ *   tau, next_anchor  out [B] int32
+ * Workspace: dflash_workspace_size. */
+dflash_status dflash_sample_accept(const dflash_dims* dims, int32_t B, int32_t gamma, float temperature,
+                                   const int32_t* draft, const float* draft_logits, const float* draft_lse,
+                                   const float* target_logits, const float* accept_u, const float* resid_u,
+                                   int32_t* tau, int32_t* next_anchor, void* ws, size_t ws_bytes, void* stream);
+
 /* Kernel roles the profiling hook can bracket. */
 typedef enum {
   DFLASH_PROF_NONE = 0,
-  DFLASH_PROF_LM_HEAD = 1,   /* LM-head weight stream of dflash_argmax_accept */
+  DFLASH_PROF_LM_HEAD = 1,   /* LM-head weight stream of dflash_argmax_accept / dflash_sample_drafts */
   DFLASH_PROF_QKV = 2,       /* per-layer Q/K/V projection */
   DFLASH_PROF_O = 3,         /* per-layer output projection */
   DFLASH_PROF_GATEUP = 4,    /* per-layer gate/up projection */

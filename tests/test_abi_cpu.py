@@ -162,3 +162,48 @@ def test_profile_hook_validation(lib):
     with pytest.raises(B.DFlashError) as e:
         B.profile_events(42)
     assert e.value.status == B.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("T", [0.0, -1.0, float("nan"), float("inf"), 1e-45])
+def test_sampling_temperature_rejected(lib, T):
+    with pytest.raises(B.DFlashError) as e:
+        B.sample_drafts(_dims(), B.Weights(lm_head=0x1000), 0x2000, 1, 16, T, 0x3000, 0x4000, 0x5000, None, 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG and "temperature" in B.last_error()
+    with pytest.raises(B.DFlashError) as e:
+        B.sample_accept(_dims(), 1, 16, T, 0x1000, 0x2000, None, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+
+
+def test_sampling_arguments_checked(lib):
+    W = B.Weights(lm_head=0x1000)
+    good = dict(h=0x2000, u=0x3000, d=0x4000, z=0x5000)
+    for miss in good:
+        a = dict(good)
+        a[miss] = None
+        with pytest.raises(B.DFlashError) as e:
+            B.sample_drafts(_dims(), W, a["h"], 1, 16, 1.0, a["u"], a["d"], a["z"], None, 0, 0)
+        assert e.value.status == B.ERR_INVALID_ARG, miss
+    with pytest.raises(B.DFlashError) as e:       # misaligned logits
+        B.sample_drafts(_dims(), W, 0x2000, 1, 16, 1.0, 0x3000, 0x4000, 0x5004, None, 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.DFlashError) as e:       # batch out of range
+        B.sample_drafts(_dims(), W, 0x2000, 65, 16, 1.0, 0x3000, 0x4000, 0x5000, None, 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.DFlashError) as e:       # no workspace
+        B.sample_drafts(_dims(), W, 0x2000, 1, 16, 1.0, 0x3000, 0x4000, 0x5000, None, 0, 0)
+    assert e.value.status == B.ERR_WORKSPACE
+    acc = dict(d=0x1000, z=0x2000, t=0x3000, au=0x4000, ru=0x5000, tau=0x6000, nxt=0x7000)
+    for miss in acc:
+        a = dict(acc)
+        a[miss] = None
+        with pytest.raises(B.DFlashError) as e:
+            B.sample_accept(_dims(), 1, 16, 1.0, a["d"], a["z"], None, a["t"], a["au"], a["ru"], a["tau"],
+                            a["nxt"], 0, 0)
+        assert e.value.status == B.ERR_INVALID_ARG, miss
+    with pytest.raises(B.DFlashError) as e:       # gamma out of range
+        B.sample_accept(_dims(), 1, 34, 1.0, 0x1000, 0x2000, None, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.DFlashError) as e:       # workspace too small
+        B.sample_accept(_dims(), 1, 16, 1.0, 0x1000, 0x2000, None, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000,
+                        0x10000, 16)
+    assert e.value.status == B.ERR_WORKSPACE
