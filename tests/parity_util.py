@@ -211,15 +211,17 @@ class Workload:
         # the gap is a difference of two logits: compared in absolute terms only
         gmx = TOL[self.tol][0]
         assert np.abs(gg - gap_o).max() <= gmx, f"{tag} top2 gap: max-abs {np.abs(gg - gap_o).max():.3e}"
-        # accept on identical token inputs: the GPU drafts and synthetic targets
+        # accept on identical token inputs on both sides: the oracle's drafts and
+        # the synthetic targets built from them (nothing of the GPU's feeds the oracle)
         match, r, bonus = self.inp.verify_draws(it, g)
-        target = build_target_np(d_g, match, r, bonus, cfg.V)
+        target = build_target_np(d_o, match, r, bonus, cfg.V)
         tgt_dev = torch.from_numpy(target).to(self.dev)
+        d_o_dev = torch.from_numpy(np.ascontiguousarray(d_o, dtype=np.int32)).to(self.dev)
         tau = torch.empty(Bn, dtype=torch.int32, device=self.dev)
         nxt = torch.empty(Bn, dtype=torch.int32, device=self.dev)
-        self.dr.argmax_accept(B.ACCEPT, None, Bn, g, draft, target=tgt_dev, tau=tau, nxt=nxt)
+        self.dr.argmax_accept(B.ACCEPT, None, Bn, g, d_o_dev, target=tgt_dev, tau=tau, nxt=nxt)
         torch.cuda.synchronize()
-        tau_o, nxt_o = O.accept(d_g, target)
+        tau_o, nxt_o = O.accept(d_o, target)
         assert np.array_equal(tau.cpu().numpy(), tau_o), (tau.cpu().numpy(), tau_o)
         assert np.array_equal(nxt.cpu().numpy(), nxt_o)
         assert np.all((tau_o >= 1) & (tau_o <= n + 1))
