@@ -12,7 +12,11 @@ Prints one JSON line.  ``value`` is drafted blocks per second (batch x steps /
 time).  ``roofline`` covers the dominant kernel (the LM-head GEMM with its
 argmax, the largest single weight stream of a step) timed with HIP events on
 the library's stream; ``cpu_baseline`` times the CPU oracle on a bounded sample
-(one full iteration).
+(whole iterations).  ``sampling`` measures the same step decoded at temperature
+1: drafts drawn from softmax(z / T) in the LM head's epilogue, synthetic target
+logits (draft logits + N(0, 0.5^2) noise, the bonus row N(0, 1)), lossless
+verification, append; with its kernels' HBM fractions and its own oracle
+baseline.
 """
 from __future__ import annotations
 
@@ -66,6 +70,8 @@ def main():
                     help="run the CPU oracle for about this long (whole iterations)")
     ap.add_argument("--cache", choices=["f32", "bf16"], default="f32",
                     help="storage type of H_t and the KV cache")
+    ap.add_argument("--temperature", type=float, default=1.0, help="temperature of the sampled-decoding leg")
+    ap.add_argument("--no-sampling", action="store_true", help="skip the sampled-decoding leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the single-GPU path is "
@@ -285,6 +291,10 @@ def main():
         },
     }
 
+    if not args.no_sampling:
+        out["sampling"] = sampled_leg(args, cfg, inp, dr, cache, base_lens, tokens, h_final, draft, tau, nxt, app,
+                                      H_app, make_events, hook, ms_per_step)
+
     # A plain device copy of a known size: the reference that scales rocprofv3's
     # FETCH_SIZE / WRITE_SIZE counters into bytes (256 MiB read + 256 MiB written).
     src = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)
@@ -295,14 +305,130 @@ def main():
     del src, dst
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        greedy_cpu, sampled_cpu = cpu_baseline(cfg, inp, args.cpu_seconds,
+                                               None if args.no_sampling else args.temperature)
+        out["cpu_baseline"] = greedy_cpu
+        if sampled_cpu is not None:
+            out["sampling"]["cpu_baseline"] = sampled_cpu
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, inp, seconds):
+def sampled_leg(args, cfg, inp, dr, cache, base_lens, tokens, h_final, draft, tau, nxt, app, H_app, make_events,
+                hook, greedy_ms):
+    """The drafting step decoded at temperature T: timed like the greedy step,
+    then each sampling kernel role over one cycle (outside the timed region)."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_drafter_ctx_amd import binding as B
+    from block_diffusion_drafter_ctx_amd import roofline as RF
+
+    T = args.temperature
+    gamma, n, Bn, V, CYCLE = cfg.gamma, cfg.gamma - 1, cfg.B, cfg.V, cfg.iters
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    ug, ua, ur = inp.sample_uniforms(0, gamma)
+    u_draw = torch.from_numpy(ug).to(dev)
+    u_acc = torch.from_numpy(ua).to(dev)
+    u_emit = torch.from_numpy(ur).to(dev)
+    noise = torch.from_numpy(inp.target_noise(0, gamma)).to(dev)
+    z = torch.empty(Bn, n, V, dtype=torch.float32, device=dev)
+    lse = torch.empty(Bn, n, dtype=torch.float32, device=dev)
+    target = torch.empty(Bn, gamma, V, dtype=torch.float32, device=dev)
+    target[:, n].copy_(noise[:, n])
+    noise_d = noise[:, :n]
+
+    def sstep(i):
+        it = i % CYCLE
+        if it == 0:
+            cache.set_lens(base_lens)
+        dr.draft(cache, tokens, None, gamma, h_final)
+        dr.sample_drafts(h_final, Bn, gamma, T, u_draw, draft, z, lse)
+        torch.add(z, noise_d, alpha=0.5, out=target[:, :n])       # stands in for the target's verify forward
+        dr.sample_accept(Bn, gamma, T, draft, z, target, u_acc, u_emit, tau, nxt, draft_lse=lse)
+        if Bn > 1:
+            tokens[:, 0].copy_(nxt)
+        d = app[it]
+        dr.fuse(d["states"], Bn * cfg.append_rows, H_app)
+        dr.inject(H_app, [cfg.append_rows] * Bn, cache)
+
+    for i in range(args.warmup):
+        sstep(i)
+    lm_ev = make_events(args.steps)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    hook(B.PROF_LM_HEAD, lm_ev)
+    for i in range(args.steps):
+        sstep(args.warmup + i)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    assert hook(B.PROF_NONE, []) == args.steps
+    ms = max(s0.elapsed_time(s1), wall * 1e3) / args.steps
+    lm_us = float(np.mean([a.elapsed_time(b) for a, b in lm_ev])) * 1e3
+
+    taus = []
+    per = {}
+    for name, role, nbytes in (("row_stats", B.PROF_ROW_STATS, RF.row_stats_bytes(Bn * (n + 1), V)),
+                               ("verify", B.PROF_VERIFY, None)):
+        pairs = make_events(CYCLE)
+        hook(role, pairs)
+        for i in range(CYCLE):
+            sstep(i)
+            if role == B.PROF_ROW_STATS:
+                torch.cuda.synchronize()
+                taus.extend(tau.cpu().tolist())
+        torch.cuda.synchronize()
+        got = hook(B.PROF_NONE, [])
+        us = float(np.mean([a.elapsed_time(b) for a, b in pairs[:got]])) * 1e3
+        per[name] = {"us": round(us, 2)}
+        if nbytes is not None:
+            per[name].update(bytes=int(nbytes), GBps=round(nbytes / (us * 1e-6) / 1e9, 1),
+                             hbm_frac=round(nbytes / (us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4))
+    # the whole verification call (row statistics + verify kernels), events on the library's stream
+    cache.set_lens(base_lens)
+    ev = []
+    for rep in range(3 + 20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dr.sample_accept(Bn, gamma, T, draft, z, target, u_acc, u_emit, tau, nxt, draft_lse=lse)
+        b.record(stream)
+        if rep >= 3:
+            ev.append((a, b))
+    torch.cuda.synchronize()
+    call_us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    vb = RF.verify_bytes(Bn, n, V, lse_given=True)
+    lm_bytes = RF.lm_head_sample_bytes(V, cfg.D, Bn * n, RF.elem_bytes(cfg.dtype))
+    lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
+    log(f"sampled step {ms * 1e3:.1f} us (greedy {greedy_ms * 1e3:.1f}), LM head + sampling {lm_us:.1f} us "
+        f"({lm_gbs:.0f} GB/s), verify call {call_us:.1f} us, mean tau {np.mean(taus):.2f}")
+    return {
+        "temperature": T,
+        "step": ("draft forward -> LM head with in-epilogue Gumbel-max sampling and log-sum-exp -> synthetic "
+                 "target logits (draft logits + N(0, 0.5^2) noise; bonus row N(0, 1)) -> lossless verify -> "
+                 f"append {cfg.append_rows} rows"),
+        "blocks_per_s": round(Bn / (ms * 1e-3), 2),
+        "ms_per_step": round(ms, 4),
+        "vs_greedy_step": round(ms / greedy_ms, 4),
+        "mean_tau": round(float(np.mean(taus)), 3),
+        "lm_head_sample": {"us": round(lm_us, 2), "bytes": int(lm_bytes), "GBps": round(lm_gbs, 1),
+                           "hbm_frac": round(lm_gbs / RF.HBM_PEAK_GBS, 4)},
+        "row_stats": per["row_stats"],
+        "verify_kernels_us": per["verify"]["us"],
+        "verify_call": {"us": round(call_us, 2), "bytes": int(vb), "GBps": round(vb / (call_us * 1e-6) / 1e9, 1),
+                        "hbm_frac": round(vb / (call_us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4)},
+    }
+
+
+def cpu_baseline(cfg, inp, seconds, temperature=None):
     """The CPU oracle, as it stands, on whole drafting iterations of the same
     workload (draft forward + LM-head argmax + accept + 16-row append), repeated
-    for about ``seconds`` with the GPU loop's 8-iteration cache reset."""
+    for about ``seconds`` with the GPU loop's 8-iteration cache reset; then, when
+    ``temperature`` is given, the sampled iteration (draft forward + sampled
+    drafts + synthetic target logits + lossless verify + append) for about half
+    as long.  Returns (greedy, sampled or None)."""
     import numpy as np
     from oracle import dflash_oracle as O
     from dflash_inputs import build_target_np
@@ -326,37 +452,60 @@ def cpu_baseline(cfg, inp, seconds):
     appends = [inp.append_states(it) for it in range(cfg.iters)]
     draws = [inp.verify_draws(it, cfg.gamma) for it in range(cfg.iters)]
     gamma = cfg.gamma
-    anchors = inp.anchors()
-    done = 0
-    t0 = time.perf_counter()
-    cache = None
-    while done < 256 and (done == 0 or time.perf_counter() - t0 < seconds):
-        it = done % cfg.iters
-        if it == 0:
-            cache = O.OracleCache(cfg.L, cfg.B, cfg.Hkv, cfg.d)
+    if temperature is not None:
+        from dflash_inputs import build_target_logits_np
+        ug, ua, ur = inp.sample_uniforms(0, gamma)
+        noise = inp.target_noise(0, gamma)
+
+    def run(sampled, budget):
+        anchors = inp.anchors()
+        done = 0
+        t0 = time.perf_counter()
+        cache = None
+        while done < 256 and (done == 0 or time.perf_counter() - t0 < budget):
+            it = done % cfg.iters
+            if it == 0:
+                cache = O.OracleCache(cfg.L, cfg.B, cfg.Hkv, cfg.d)
+                for l in range(cfg.L):
+                    for b in range(cfg.B):
+                        cache.append(l, b, *base[l][b])
+            tokens = inp.block_tokens(gamma, anchors)
+            hf, _ = O.draft_forward(cfg, layers, gf, cache, gamma, embed=E, tokens=tokens, storage=cfg.cache_dtype)
+            if sampled:
+                d, z, _, _ = O.sample_drafts(hf, E, temperature, ug)
+                tgt = build_target_logits_np(z, noise)
+                _, anchors, _ = O.sample_accept(d, z, tgt, temperature, ua, ur)
+            else:
+                d, _, _ = O.lm_head_argmax(hf, E)
+                m, r, bonus = draws[it]
+                tgt = build_target_np(d, m, r, bonus, cfg.V)
+                _, anchors = O.accept(d, tgt)
+            Ha = O.fuse_context(appends[it], wc, gc, cfg.eps, cfg.cache_dtype)
             for l in range(cfg.L):
                 for b in range(cfg.B):
-                    cache.append(l, b, *base[l][b])
-        tokens = inp.block_tokens(gamma, anchors)
-        hf, _ = O.draft_forward(cfg, layers, gf, cache, gamma, embed=E, tokens=tokens, storage=cfg.cache_dtype)
-        d, _, _ = O.lm_head_argmax(hf, E)
-        m, r, bonus = draws[it]
-        tgt = build_target_np(d, m, r, bonus, cfg.V)
-        _, anchors = O.accept(d, tgt)
-        Ha = O.fuse_context(appends[it], wc, gc, cfg.eps, cfg.cache_dtype)
-        for l in range(cfg.L):
-            for b in range(cfg.B):
-                rows = slice(b * cfg.append_rows, (b + 1) * cfg.append_rows)
-                k, v = O.inject_kv(Ha[rows], layers[l]["w_qkv"], cfg.Hq, cfg.Hkv, cfg.d, cfg.cache_dtype)
-                cache.append(l, b, k, v)
-        done += 1
-    dt = time.perf_counter() - t0
+                    rows = slice(b * cfg.append_rows, (b + 1) * cfg.append_rows)
+                    k, v = O.inject_kv(Ha[rows], layers[l]["w_qkv"], cfg.Hq, cfg.Hkv, cfg.d, cfg.cache_dtype)
+                    cache.append(l, b, k, v)
+            done += 1
+        return done, time.perf_counter() - t0
+
+    done, dt = run(False, seconds)
     log(f"cpu baseline: {done} iteration(s) in {dt:.1f}s on {cores} threads")
-    return {"value": round(cfg.B * done / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} full drafting iterations of the same workload (draft forward + LM-head argmax "
-                      f"+ accept + 16-row append, cache reset every {cfg.iters}), float64 numpy oracle, "
-                      f"after an untimed context ingest",
-            "seconds": round(dt, 2)}
+    greedy = {"value": round(cfg.B * done / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+              "sample": f"{done} full drafting iterations of the same workload (draft forward + LM-head argmax "
+                        f"+ accept + 16-row append, cache reset every {cfg.iters}), float64 numpy oracle, "
+                        f"after an untimed context ingest",
+              "seconds": round(dt, 2)}
+    if temperature is None:
+        return greedy, None
+    done, dt = run(True, seconds / 2)
+    log(f"cpu baseline (sampled): {done} iteration(s) in {dt:.1f}s")
+    sampled = {"value": round(cfg.B * done / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"{done} sampled drafting iterations at T = {temperature} (draft forward + sampled "
+                         f"drafts + synthetic target logits + lossless verify + 16-row append), float64 "
+                         f"numpy oracle",
+               "seconds": round(dt, 2)}
+    return greedy, sampled
 
 
 if __name__ == "__main__":

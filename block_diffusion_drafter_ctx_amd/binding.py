@@ -21,7 +21,8 @@ MAX_BATCH, MAX_TGT_LAYERS, MIN_GAMMA, MAX_GAMMA = 64, 8, 2, 33
 EXPORTED = ("dflash_version", "dflash_last_error", "dflash_workspace_size", "dflash_fuse_context",
             "dflash_inject_kv", "dflash_draft_forward", "dflash_argmax_accept", "dflash_sample_drafts",
             "dflash_sample_accept", "dflash_profile_events")
-PROF_NONE, PROF_LM_HEAD, PROF_QKV, PROF_O, PROF_GATEUP, PROF_DOWN, PROF_FUSE, PROF_INJECT, PROF_ATTENTION = range(9)
+(PROF_NONE, PROF_LM_HEAD, PROF_QKV, PROF_O, PROF_GATEUP, PROF_DOWN, PROF_FUSE, PROF_INJECT, PROF_ATTENTION,
+ PROF_ROW_STATS, PROF_VERIFY) = range(11)
 
 
 class Dims(ctypes.Structure):

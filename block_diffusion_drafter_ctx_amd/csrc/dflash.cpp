@@ -293,7 +293,7 @@ AcceptWs sample_accept_ws(const dflash_dims* d, int B, int gamma, bool lse_given
   w.rows = B * (n + 1) + (lse_given ? 0 : B * n);
   Carve c;
   w.stats = c.take(static_cast<size_t>(w.nchunk) * w.rows * sizeof(float4));
-  w.part = c.take(static_cast<size_t>(B) * w.nchunk * sizeof(float4));
+  w.part = c.take(static_cast<size_t>(B) * ((d->V + kSpecDrawChunk - 1) / kSpecDrawChunk) * sizeof(float4));
   w.m = c.take(static_cast<size_t>(B) * 4);
   w.total = c.off;
   return w;
@@ -336,7 +336,7 @@ const char* dflash_version(void) { return "dflash-mi355x 0.1.0 (gfx950)"; }
 
 dflash_status dflash_profile_events(int32_t role, void* const* start, void* const* stop, int32_t n,
                                     int32_t* recorded) {
-  DF_REQUIRE(role >= DFLASH_PROF_NONE && role <= DFLASH_PROF_ATTENTION, DFLASH_ERR_INVALID_ARG,
+  DF_REQUIRE(role >= DFLASH_PROF_NONE && role <= DFLASH_PROF_VERIFY, DFLASH_ERR_INVALID_ARG,
              "unknown profiling role %d", role);
   DF_REQUIRE(n >= 0, DFLASH_ERR_INVALID_ARG, "n=%d < 0", n);
   DF_REQUIRE(role == DFLASH_PROF_NONE || n == 0 || (start != nullptr && stop != nullptr), DFLASH_ERR_INVALID_ARG,
@@ -841,7 +841,9 @@ dflash_status dflash_sample_drafts(const dflash_dims* dims, const dflash_weights
     DF_HIP(launch_gemm_f32(g, s));
     r.src = logits;
   }
+  const int ps = prof_begin(DFLASH_PROF_ROW_STATS, s);
   DF_HIP(launch_row_stats(r, s));
+  prof_end(ps, s);
   DF_HIP(launch_sample_final(stats, nchunk, Mr, draft, lse, s));
   return ok();
 }
@@ -879,7 +881,9 @@ dflash_status dflash_sample_accept(const dflash_dims* dims, int32_t B, int32_t g
   r.vec = V % 4 == 0;
   r.inv_t = inv_t;
   r.stats = reinterpret_cast<float4*>(base + lay.stats);
+  int ps = prof_begin(DFLASH_PROF_ROW_STATS, s);
   DF_HIP(launch_row_stats(r, s));
+  prof_end(ps, s);
   SpecArgs a{};
   a.draft = draft;
   a.zq = draft_logits;
@@ -891,8 +895,8 @@ dflash_status dflash_sample_accept(const dflash_dims* dims, int32_t B, int32_t g
   a.B = B;
   a.n = n;
   a.V = V;
-  a.chunk = lay.chunk;
   a.nchunk = lay.nchunk;
+  a.ndraw = (V + kSpecDrawChunk - 1) / kSpecDrawChunk;
   a.rows = lay.rows;
   a.vec = r.vec;
   a.inv_t = inv_t;
@@ -900,7 +904,9 @@ dflash_status dflash_sample_accept(const dflash_dims* dims, int32_t B, int32_t g
   a.m_out = reinterpret_cast<int32_t*>(base + lay.m);
   a.tau = tau;
   a.next_anchor = next_anchor;
+  ps = prof_begin(DFLASH_PROF_VERIFY, s);
   DF_HIP(launch_spec_verify(a, s));
+  prof_end(ps, s);
   return ok();
 }
 

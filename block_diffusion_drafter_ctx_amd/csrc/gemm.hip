@@ -229,6 +229,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(GemmArgs g) {
 // the stacked [gate; up] weight, so s = silu(gate) * up leaves the kernel
 // directly (N = F outputs, 8 per tile).
 constexpr int kRkWaves = 16;
+constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kRkMinN = 16384;   // weight rows below which the split-K streaming kernel wins
 
 enum RkEpilogue { RK_PART = 0, RK_TOP2 = 1, RK_SWIGLU = 2, RK_SAMPLE = 3 };
@@ -243,6 +244,13 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
   __shared__ float tv1[4][16], tv2[4][16];
   __shared__ int ti1[4][16];
   __shared__ float4 sst[4][16];
+  // Epilogues that write per tile (split-K partials, SwiGLU, sampled logits):
+  // when the launch provides dynamic LDS for it, every output tile of this
+  // workgroup stays in LDS ([slot][row][column], slot = (unit - u0) / P) and is
+  // written out once, after the weight stream.  Small writes interleaved with
+  // the read stream cost far more HBM time than their bytes.
+  extern __shared__ __attribute__((aligned(16))) float lt_all[];
+  constexpr int kOutCols = EP == RK_SWIGLU ? 8 : 16;   // output columns per tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = g.S;
   const int units = S * g.ntiles;
@@ -312,6 +320,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
   const int mo = ln & 15, no = 4 * (ln >> 4) + (tid & 3);
   Top2 best{-INFINITY, 0x7fffffff, -INFINITY};
   SampleStat ss = sstat_empty();
+  const bool staged = EP != RK_TOP2 && g.stage_tiles > 0;
   int buf = 0;
   for (int q = 0;; ++q) {
     const int ub = u0 + P * T * q;
@@ -359,7 +368,11 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
           vu += red[buf][w][0][tid + 128];
         }
         const int f = (ub / S) * TN + no;      // no < 8 for tid < 128
-        if (mo < g.M && f < g.N) g.part[static_cast<int64_t>(mo) * g.N + f] = vg / (1.0f + expf(-vg)) * vu;
+        if (mo < g.M && f < g.N) {
+          const float sv = vg / (1.0f + expf(-vg)) * vu;
+          if (staged) lt_all[q * 128 + mo * 8 + no] = sv;
+          else g.part[static_cast<int64_t>(mo) * g.N + f] = sv;
+        }
       }
     } else if (tid < 256) {
 #pragma unroll
@@ -375,10 +388,13 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
               if (logits != nullptr) logits[static_cast<int64_t>(mo) * g.N + n] = v;
               best = top2_push(best, v, n);
             } else if constexpr (SAMPLE) {
-              logits[static_cast<int64_t>(mo) * g.N + n] = v;
+              if (staged) lt_all[q * 256 + mo * 16 + no] = v;
+              else logits[static_cast<int64_t>(mo) * g.N + n] = v;
               const float x = v * g.inv_t;
               sstat_push_lse(ss, x);
               sstat_push_key(ss, x + gumbel_noise(su), n);
+            } else if (staged) {
+              lt_all[(q * T + t) * 256 + mo * 16 + no] = v;
             } else {
               g.part[(static_cast<int64_t>(sp) * g.M + mo) * g.N + n] = v;
             }
@@ -425,6 +441,28 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
 #pragma unroll
       for (int w = 1; w < 4; ++w) t = sstat_merge(t, sstat_unpack(sst[w][tid]));
       reinterpret_cast<float4*>(top2)[static_cast<int64_t>(blockIdx.x) * g.M + tid] = sstat_pack(t);
+    }
+  }
+  if (staged) {
+    if constexpr (!SAMPLE) __syncthreads();   // the last tile's epilogue is done
+    // piece i: slot i / PPT, row (i % PPT) / (PPT / 16), four columns from 4 (i % (PPT / 16))
+    constexpr int PPT = kOutCols * 16 / 4;     // float4 pieces per tile
+    constexpr int PPR = kOutCols / 4;          // float4 pieces per row
+    const int nslots = (units - u0 + P - 1) / P;
+    float* out = SAMPLE ? logits : g.part + static_cast<int64_t>(sp) * g.M * g.N;
+    for (int i = tid; i < nslots * PPT; i += 64 * kRkWaves) {
+      const int slot = i / PPT, r = (i % PPT) / PPR, c4 = 4 * (i % PPR);
+      const int n0 = ((u0 + P * slot) / S) * kOutCols;
+      if (r < g.M) {
+        float* dst = out + static_cast<int64_t>(r) * g.N + n0 + c4;
+        const float* src = &lt_all[slot * (16 * kOutCols) + r * kOutCols + c4];
+        if ((g.N & 3) == 0 && n0 + c4 + 3 < g.N) {
+          *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (n0 + c4 + e < g.N) dst[e] = src[e];
+        }
+      }
     }
   }
 }
@@ -1094,6 +1132,35 @@ GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
   return plan_gemm_mfma(M, N, K, ak, wide);
 }
 
+// Launch one register-K instantiation.  Epilogues that write per tile get
+// their workgroup's output tiles staged in dynamic LDS (written out after the
+// weight stream) whenever they fit beside the kernel's static LDS.
+template <int KS, int EP, int T, int AK = A_F32_SPLIT>
+hipError_t rk_launch(GemmArgs a, const GemmPlan& p, float* top2, float* logits, hipStream_t st) {
+  const void* kern = reinterpret_cast<const void*>(&gemm_rk_kernel<KS, EP, T, AK>);
+  static int stage_cap = -1;   // per instantiation: dynamic LDS bytes it may use (0: none)
+  if (stage_cap < 0) {
+    int cap = 0;
+    hipFuncAttributes fa{};
+    if (EP != RK_TOP2 && hipFuncGetAttributes(&fa, kern) == hipSuccess &&
+        fa.sharedSizeBytes + 1024 < static_cast<size_t>(kLdsBytes)) {
+      cap = static_cast<int>(kLdsBytes - fa.sharedSizeBytes) / 1024 * 1024;
+      if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, cap) != hipSuccess) cap = 0;
+    }
+    stage_cap = cap;
+  }
+  const size_t tile_bytes = (EP == RK_SWIGLU ? 8 : 16) * 16 * sizeof(float);
+  const int slots = (p.S * p.ntiles + p.grid - 1) / p.grid;   // units a workgroup handles
+  size_t shm = 0;
+  a.stage_tiles = 0;
+  if (EP != RK_TOP2 && static_cast<size_t>(slots) * tile_bytes <= static_cast<size_t>(stage_cap)) {
+    a.stage_tiles = slots;
+    shm = static_cast<size_t>(slots) * tile_bytes;
+  }
+  hipLaunchKernelGGL((gemm_rk_kernel<KS, EP, T, AK>), dim3(p.grid), dim3(64 * kRkWaves), shm, st, a, top2, logits);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, float* logits, hipStream_t st,
                           GemmAKind ak) {
   if (!p.rk || a0.a_cols % (32 * p.ks) != 0 || (top2 != nullptr && p.S != 1)) return hipErrorInvalidValue;
@@ -1103,24 +1170,18 @@ hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, fl
   a.ntiles = p.ntiles;
   a.mtiles = 1;
   a.chunks_per_split = p.cps;
-  const dim3 grid(p.grid), block(64 * kRkWaves);
   if (top2 != nullptr) {
-    if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_TOP2, 1>), grid, block, 0, st, a, top2, logits);
-    else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_TOP2, 1>), grid, block, 0, st, a, top2, logits);
-  } else {
-    if (ak == A_BF16) {
-      if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_PART, 1, A_BF16>), grid, block, 0, st, a, nullptr, nullptr);
-      else if (p.ks == 4) hipLaunchKernelGGL((gemm_rk_kernel<4, RK_PART, 1, A_BF16>), grid, block, 0, st, a, nullptr, nullptr);
-      else hipLaunchKernelGGL((gemm_rk_kernel<2, RK_PART, 2, A_BF16>), grid, block, 0, st, a, nullptr, nullptr);
-    } else if (p.ks == 8) {
-      hipLaunchKernelGGL((gemm_rk_kernel<8, RK_PART, 1>), grid, block, 0, st, a, nullptr, nullptr);
-    } else if (p.ks == 4) {
-      hipLaunchKernelGGL((gemm_rk_kernel<4, RK_PART, 1>), grid, block, 0, st, a, nullptr, nullptr);
-    } else {
-      hipLaunchKernelGGL((gemm_rk_kernel<2, RK_PART, 2>), grid, block, 0, st, a, nullptr, nullptr);
-    }
+    if (p.ks == 8) return rk_launch<8, RK_TOP2, 1>(a, p, top2, logits, st);
+    return rk_launch<4, RK_TOP2, 1>(a, p, top2, logits, st);
   }
-  return hipGetLastError();
+  if (ak == A_BF16) {
+    if (p.ks == 8) return rk_launch<8, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
+    if (p.ks == 4) return rk_launch<4, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
+    return rk_launch<2, RK_PART, 2, A_BF16>(a, p, nullptr, nullptr, st);
+  }
+  if (p.ks == 8) return rk_launch<8, RK_PART, 1>(a, p, nullptr, nullptr, st);
+  if (p.ks == 4) return rk_launch<4, RK_PART, 1>(a, p, nullptr, nullptr, st);
+  return rk_launch<2, RK_PART, 2>(a, p, nullptr, nullptr, st);
 }
 
 hipError_t launch_gemm_rk_sample(const GemmArgs& a0, const GemmPlan& p, float4* stats, float* logits,
@@ -1134,10 +1195,8 @@ hipError_t launch_gemm_rk_sample(const GemmArgs& a0, const GemmPlan& p, float4* 
   a.mtiles = 1;
   a.chunks_per_split = p.cps;
   float* sp = reinterpret_cast<float*>(stats);
-  const dim3 grid(p.grid), block(64 * kRkWaves);
-  if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_SAMPLE, 1>), grid, block, 0, st, a, sp, logits);
-  else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_SAMPLE, 1>), grid, block, 0, st, a, sp, logits);
-  return hipGetLastError();
+  if (p.ks == 8) return rk_launch<8, RK_SAMPLE, 1>(a, p, sp, logits, st);
+  return rk_launch<4, RK_SAMPLE, 1>(a, p, sp, logits, st);
 }
 
 GemmPlan plan_gemm_rk_swiglu(int M, int F, int K) {
@@ -1156,10 +1215,8 @@ hipError_t launch_gemm_rk_swiglu(const GemmArgs& a0, const GemmPlan& p, float* s
   a.mtiles = 1;
   a.chunks_per_split = p.cps;
   a.part = s_out;
-  const dim3 grid(p.grid), block(64 * kRkWaves);
-  if (p.ks == 8) hipLaunchKernelGGL((gemm_rk_kernel<8, RK_SWIGLU, 1>), grid, block, 0, st, a, nullptr, nullptr);
-  else hipLaunchKernelGGL((gemm_rk_kernel<4, RK_SWIGLU, 1>), grid, block, 0, st, a, nullptr, nullptr);
-  return hipGetLastError();
+  if (p.ks == 8) return rk_launch<8, RK_SWIGLU, 1>(a, p, nullptr, nullptr, st);
+  return rk_launch<4, RK_SWIGLU, 1>(a, p, nullptr, nullptr, st);
 }
 
 hipError_t launch_split_hilo(const float* x, int64_t ld, int M, int K, uint16_t* hi, uint16_t* lo, hipStream_t st) {

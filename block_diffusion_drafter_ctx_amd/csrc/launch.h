@@ -32,6 +32,7 @@ struct GemmArgs {
   const void* a_lo;           // A_BF16_HILO: the lo plane, laid out like a_src[0] (the hi plane)
   const float* su;            // LM-head sampling epilogue: uniforms [M][N] in (0, 1)
   float inv_t;                // LM-head sampling epilogue: 1 / temperature
+  int32_t stage_tiles;        // LM-head sampling epilogue: logits tiles held in LDS per workgroup (set by the launcher)
 };
 
 // exact bf16 A; fp32 A split hi/lo on the fly; or A given as pre-split bf16
@@ -143,6 +144,7 @@ hipError_t launch_accept(const int32_t* draft, const int32_t* target, int B, int
 constexpr int kSampleChunk = 4096;   // columns per row-statistics workgroup (at least)
 constexpr int kSpecMaxChunks = 64;   // row-statistics pieces per row, at most
 constexpr int kSpecMaxN = 32;        // drafts per block, at most
+constexpr int kSpecDrawChunk = 1024; // columns per workgroup of the emitted-token draw
 
 // Row-statistics pass.  Rows [0, rows1) read src + r*N, summing S split-K
 // partials split_stride apart; rows [rows1, rows) read src2 + (r - rows1)*N.
@@ -181,9 +183,10 @@ struct SpecArgs {
   const float* resid_u;    // [B][V]
   const float4* stats;     // row statistics [nchunk][rows]: target row j of sequence b at
                            // b*(n+1)+j, then (lse_q null) draft rows at B*(n+1)+b*n+j
-  int32_t B, n, V, chunk, nchunk, rows, vec;
+  int32_t B, n, V, nchunk, rows, vec;
+  int32_t ndraw;           // ceil(V / kSpecDrawChunk): workgroups per sequence of the draw
   float inv_t;
-  float4* part;            // scratch [B][nchunk]
+  float4* part;            // scratch [B][ndraw]
   int32_t* m_out;          // scratch [B]
   int32_t* tau;            // out [B]
   int32_t* next_anchor;    // out [B]

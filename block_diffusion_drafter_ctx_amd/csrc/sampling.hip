@@ -5,9 +5,9 @@
 //                 (best Gumbel key of x = logit / T when uniforms are given, and
 //                 the log-sum-exp state of x)
 //   sample_final  merge a row's SampleStat pieces: draft id and log sum exp(x)
-//   spec_verify   per (sequence, chunk): every workgroup of a sequence merges the
-//                 row log-normalisers, finds the first rejected draft m, then
-//                 draws its chunk's share of the emitted token: the best
+//   spec_verify   per (sequence, 1024-column chunk): every workgroup of a sequence
+//                 merges the row log-normalisers, finds the first rejected draft
+//                 m, then draws its chunk's share of the emitted token: the best
 //                 Gumbel key of the residual max(0, p_m - q_m) and of p_m (or of
 //                 the bonus row p_n when nothing was rejected)
 //   spec_final    merge the chunks: tau and the emitted token (next anchor)
@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kStatThreads = 256;
 constexpr int kStatVec = 4 * kStatThreads;   // columns per float4 sweep of a workgroup
+constexpr int kSweeps = kSampleChunk / kStatVec;   // float4 sweeps whose loads are issued together
 
 __device__ __forceinline__ SampleStat wave_sstat(SampleStat s) {
 #pragma unroll
@@ -61,18 +62,56 @@ __global__ __launch_bounds__(kStatThreads) void row_stats_kernel(RowStatArgs a) 
   const int c1 = min(a.N, c0 + a.chunk);
   SampleStat s = sstat_empty();
   if (a.vec) {
-    // whole float4 groups (N % 4 == 0, 16-byte aligned rows)
-    for (int c = c0 + 4 * threadIdx.x; c < c1; c += kStatVec) {
-      float4 v = *reinterpret_cast<const float4*>(src + c);
-      for (int sp = 1; sp < S; ++sp) {
-        const float4 t = *reinterpret_cast<const float4*>(src + sp * a.split_stride + c);
-        v = make_float4(v.x + t.x, v.y + t.y, v.z + t.z, v.w + t.w);
+    // whole float4 groups (N % 4 == 0, 16-byte aligned rows); the loads of
+    // kSweeps sweeps (and of each split level) are in flight together
+    for (int c = c0 + 4 * threadIdx.x; c < c1; c += kStatVec * kSweeps) {
+      float4 v[kSweeps], uv[kSweeps];
+#pragma unroll
+      for (int k = 0; k < kSweeps; ++k) {
+        const int ck = c + k * kStatVec;
+        v[k] = ck < c1 ? *reinterpret_cast<const float4*>(src + ck) : make_float4(0.f, 0.f, 0.f, 0.f);
+        uv[k] = (sample && ck < c1) ? *reinterpret_cast<const float4*>(su_row + ck) : make_float4(0.5f, 0.5f, 0.5f, 0.5f);
       }
-      if (lo != nullptr) *reinterpret_cast<float4*>(lo + c) = v;
-      stat_push(s, v.x, c, a.inv_t, su_row, sample);
-      stat_push(s, v.y, c + 1, a.inv_t, su_row, sample);
-      stat_push(s, v.z, c + 2, a.inv_t, su_row, sample);
-      stat_push(s, v.w, c + 3, a.inv_t, su_row, sample);
+      for (int sp = 1; sp < S; ++sp) {
+        float4 t[kSweeps];
+#pragma unroll
+        for (int k = 0; k < kSweeps; ++k) {
+          const int ck = c + k * kStatVec;
+          t[k] = ck < c1 ? *reinterpret_cast<const float4*>(src + sp * a.split_stride + ck) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < kSweeps; ++k) v[k] = make_float4(v[k].x + t[k].x, v[k].y + t[k].y, v[k].z + t[k].z, v[k].w + t[k].w);
+      }
+      // this thread's values of the block: maximum first, then one exp each
+      float xs[kSweeps * 4];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kSweeps; ++k) {
+        const int ck = c + k * kStatVec;
+        const bool ok = ck < c1;
+        if (ok && lo != nullptr) *reinterpret_cast<float4*>(lo + ck) = v[k];
+        xs[4 * k + 0] = ok ? v[k].x * a.inv_t : -INFINITY;
+        xs[4 * k + 1] = ok ? v[k].y * a.inv_t : -INFINITY;
+        xs[4 * k + 2] = ok ? v[k].z * a.inv_t : -INFINITY;
+        xs[4 * k + 3] = ok ? v[k].w * a.inv_t : -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bm = fmaxf(bm, xs[4 * k + e]);
+        if (sample && ok) {
+          sstat_push_key(s, xs[4 * k + 0] + gumbel_noise(uv[k].x), ck);
+          sstat_push_key(s, xs[4 * k + 1] + gumbel_noise(uv[k].y), ck + 1);
+          sstat_push_key(s, xs[4 * k + 2] + gumbel_noise(uv[k].z), ck + 2);
+          sstat_push_key(s, xs[4 * k + 3] + gumbel_noise(uv[k].w), ck + 3);
+        }
+      }
+      if (bm != -INFINITY) {
+        float se = 0.f;
+#pragma unroll
+        for (int e = 0; e < kSweeps * 4; ++e) se += expf(xs[e] - bm);   // exp(-inf) = 0 for columns past the row
+        SampleStat blk = sstat_empty();
+        blk.mx = bm;
+        blk.se = se;
+        s = sstat_merge(s, blk);
+      }
     }
   } else {
     for (int c = c0 + threadIdx.x; c < c1; c += kStatThreads) {
@@ -138,6 +177,21 @@ __global__ __launch_bounds__(kStatThreads) void spec_verify_kernel(SpecArgs a) {
   const int chunk = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = a.n, V = a.V;
+  const int c0 = chunk * kSpecDrawChunk, c1 = min(V, c0 + kSpecDrawChunk);
+  const float* ru = a.resid_u + static_cast<int64_t>(b) * V;
+  // the emitting uniforms do not depend on the decision: their load goes out first
+  const int cv = c0 + 4 * static_cast<int>(threadIdx.x);
+  float4 uv = make_float4(0.5f, 0.5f, 0.5f, 0.5f);
+  if (a.vec && cv < c1) uv = *reinterpret_cast<const float4*>(ru + cv);
+  // draft ids and acceptance uniforms (wave 0, lane j < n), then the gathered
+  // logits, overlapped with the row-statistics loads below
+  int dj = 0;
+  float uj = 0.f;
+  if (w == 0 && lane < n) {
+    dj = a.draft[b * n + lane];
+    dj = dj < 0 ? 0 : (dj >= V ? V - 1 : dj);
+    uj = a.accept_u[b * n + lane];
+  }
   // ---- log-normalisers of rows j < n: target rows, then draft rows unless given.
   // Wave w owns rows w, w + 4, ...; lane c < nchunk holds chunk c's piece.
   const int nrows = a.lse_q != nullptr ? n : 2 * n;
@@ -163,18 +217,19 @@ __global__ __launch_bounds__(kStatThreads) void spec_verify_kernel(SpecArgs a) {
       }
     }
   }
+  float tp = 0.f, zq = 0.f;
+  if (w == 0 && lane < n) {
+    tp = a.zp[(static_cast<int64_t>(b) * (n + 1) + lane) * V + dj];
+    zq = a.zq[(static_cast<int64_t>(b) * n + lane) * V + dj];
+  }
   if (a.lse_q != nullptr && threadIdx.x < n) s_lq[threadIdx.x] = a.lse_q[b * n + threadIdx.x];
   __syncthreads();
   // ---- first rejection: draft j is kept when u_j < p_j(d_j) / q_j(d_j)
   if (w == 0) {
     bool rej = false;
     if (lane < n) {
-      int d = a.draft[b * n + lane];
-      d = d < 0 ? 0 : (d >= V ? V - 1 : d);
-      const float tp = a.zp[(static_cast<int64_t>(b) * (n + 1) + lane) * V + d];
-      const float zq = a.zq[(static_cast<int64_t>(b) * n + lane) * V + d];
       const float lr = (tp * a.inv_t - s_lp[lane]) - (zq * a.inv_t - s_lq[lane]);
-      rej = !(a.accept_u[b * n + lane] < expf(lr));
+      rej = !(uj < expf(lr));
     }
     const unsigned long long mask = __ballot(rej);
     if (lane == 0) s_m = mask ? __ffsll(mask) - 1 : n;
@@ -185,9 +240,7 @@ __global__ __launch_bounds__(kStatThreads) void spec_verify_kernel(SpecArgs a) {
   const bool resid = m < n;
   const float* rp = a.zp + (static_cast<int64_t>(b) * (n + 1) + m) * V;
   const float* rq = a.zq + (static_cast<int64_t>(b) * n + (resid ? m : 0)) * V;
-  const float* ru = a.resid_u + static_cast<int64_t>(b) * V;
   const float lp0 = resid ? s_lp[m] : 0.f, lq0 = resid ? s_lq[m] : 0.f;
-  const int c0 = chunk * a.chunk, c1 = min(V, c0 + a.chunk);
   Picks pk = picks_empty();
   auto push = [&](float tv, float qv, float uv, int c) {
     const float g = gumbel_noise(uv);
@@ -204,14 +257,14 @@ __global__ __launch_bounds__(kStatThreads) void spec_verify_kernel(SpecArgs a) {
     }
   };
   if (a.vec) {
-    for (int c = c0 + 4 * threadIdx.x; c < c1; c += kStatVec) {
-      const float4 tv = *reinterpret_cast<const float4*>(rp + c);
-      const float4 uv = *reinterpret_cast<const float4*>(ru + c);
-      const float4 qv = resid ? *reinterpret_cast<const float4*>(rq + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-      push(tv.x, qv.x, uv.x, c);
-      push(tv.y, qv.y, uv.y, c + 1);
-      push(tv.z, qv.z, uv.z, c + 2);
-      push(tv.w, qv.w, uv.w, c + 3);
+    // one float4 per thread (the chunk is one sweep of the workgroup)
+    if (cv < c1) {
+      const float4 tv = *reinterpret_cast<const float4*>(rp + cv);
+      const float4 qv = resid ? *reinterpret_cast<const float4*>(rq + cv) : make_float4(0.f, 0.f, 0.f, 0.f);
+      push(tv.x, qv.x, uv.x, cv);
+      push(tv.y, qv.y, uv.y, cv + 1);
+      push(tv.z, qv.z, uv.z, cv + 2);
+      push(tv.w, qv.w, uv.w, cv + 3);
     }
   } else {
     for (int c = c0 + threadIdx.x; c < c1; c += kStatThreads) push(rp[c], resid ? rq[c] : 0.f, ru[c], c);
@@ -223,7 +276,7 @@ __global__ __launch_bounds__(kStatThreads) void spec_verify_kernel(SpecArgs a) {
   if (threadIdx.x == 0) {
     Picks r = picks_unpack(w4[0]);
     for (int i = 1; i < kStatThreads / kWave; ++i) r = picks_merge(r, picks_unpack(w4[i]));
-    a.part[static_cast<int64_t>(b) * a.nchunk + chunk] = picks_pack(r);
+    a.part[static_cast<int64_t>(b) * a.ndraw + chunk] = picks_pack(r);
     if (chunk == 0) a.m_out[b] = m;
   }
 }
@@ -268,12 +321,12 @@ hipError_t launch_sample_final(const float4* stats, int nparts, int M, int32_t* 
 
 hipError_t launch_spec_verify(const SpecArgs& a, hipStream_t st) {
   if (a.n < 1 || a.n > kSpecMaxN || a.nchunk < 1 || a.nchunk > kSpecMaxChunks ||
-      a.chunk % kStatVec != 0)
+      a.ndraw != (a.V + kSpecDrawChunk - 1) / kSpecDrawChunk)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(spec_verify_kernel, dim3(a.nchunk, a.B), dim3(kStatThreads), 0, st, a);
+  hipLaunchKernelGGL(spec_verify_kernel, dim3(a.ndraw, a.B), dim3(kStatThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(spec_final_kernel, dim3(a.B), dim3(64), 0, st, a.part, a.m_out, a.nchunk, a.n, a.tau,
+  hipLaunchKernelGGL(spec_final_kernel, dim3(a.B), dim3(64), 0, st, a.part, a.m_out, a.ndraw, a.n, a.tau,
                      a.next_anchor);
   return hipGetLastError();
 }

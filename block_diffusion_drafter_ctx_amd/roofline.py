@@ -96,6 +96,27 @@ def lm_head_flops(V: int, D: int, rows: int) -> int:
     return 2 * rows * V * D
 
 
+def lm_head_sample_bytes(V: int, D: int, rows: int, es: int = 2) -> int:
+    """LM head with the sampling epilogue: the [V, D] table once and the fp32 rows
+    in, one uniform read and one fp32 logit written per (row, token), ids and
+    log-normalisers out."""
+    return V * D * es + rows * D * 4 + 2 * rows * V * 4 + rows * 8
+
+
+def row_stats_bytes(rows: int, V: int) -> int:
+    """One read of each fp32 logits row (the log-sum-exp pass of the verify)."""
+    return rows * V * 4
+
+
+def verify_bytes(B: int, n: int, V: int, lse_given: bool = True) -> int:
+    """Lossless verification of B sampled blocks of n drafts: every target row
+    once (n + 1 per sequence), the draft rows once when their log-normalisers are
+    not given, per sequence the residual's draft row and the emitting uniforms
+    once, and the per-draft ids, uniforms, log-normalisers and gathered logits."""
+    rows = B * (n + 1) + (0 if lse_given else B * n)
+    return rows * V * 4 + B * 2 * V * 4 + B * n * 5 * 4 + B * 8
+
+
 def attention_bytes(L: int, Hkv: int, d: int, gamma: int, ctx_lens, es: int = 2) -> int:
     return L * sum(n + gamma for n in ctx_lens) * 2 * Hkv * d * es
 

@@ -260,7 +260,11 @@ typedef enum {
   DFLASH_PROF_DOWN = 5,      /* per-layer down projection */
   DFLASH_PROF_FUSE = 6,      /* W_c projection of dflash_fuse_context */
   DFLASH_PROF_INJECT = 7,    /* W_K/W_V projection of dflash_inject_kv */
-  DFLASH_PROF_ATTENTION = 8  /* injected-context attention (without its combine step) */
+  DFLASH_PROF_ATTENTION = 8, /* injected-context attention (without its combine step) */
+  DFLASH_PROF_ROW_STATS = 9, /* row log-sum-exp pass of dflash_sample_accept (and of dflash_sample_drafts
+                                when the LM head runs split-K) */
+  DFLASH_PROF_VERIFY = 10    /* first-rejection and emitted-token kernels of dflash_sample_accept
+                                (two launches, bracketed together) */
 } dflash_prof_role;
 
 /* Profiling hook (measurement only; not needed to run the path).  From now on,
