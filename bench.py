@@ -37,8 +37,8 @@ METRIC = "drafted gamma=16 blocks/sec + draft fwd us at 1 GPU; % HBM BW / % MFMA
 # FETCH_SIZE reads 0.5x the copy's bytes, WRITE_SIZE 1.0x.  Valid only for the
 # default workload and only while the GEMM sources hash to ``src``; otherwise
 # the traffic is reported as null.
-LM_HEAD_COUNTERS = {"src": "9f5cf2908db57314", "config": 2, "cache": "f32",
-                    "fetch_kib": 608751.7, "write_kib": 52.0, "fetch_scale": 1.9998, "write_scale": 1.0}
+LM_HEAD_COUNTERS = {"src": "f7103093c54c0cc5", "config": 2, "cache": "f32",
+                    "fetch_kib": 608752.1, "write_kib": 52.0, "fetch_scale": 1.9998, "write_scale": 1.0}
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/launch.h")
 
 
@@ -322,6 +322,10 @@ def sampled_leg(args, cfg, inp, dr, cache, base_lens, tokens, h_final, draft, ta
 
     from block_diffusion_drafter_ctx_amd import binding as B
     from block_diffusion_drafter_ctx_amd import roofline as RF
+    from dflash_inputs import Inputs, shrink
+
+    def Inputs16(c, b):
+        return Inputs(shrink(c, B=b))
 
     T = args.temperature
     gamma, n, Bn, V, CYCLE = cfg.gamma, cfg.gamma - 1, cfg.B, cfg.V, cfg.iters
@@ -400,6 +404,35 @@ def sampled_leg(args, cfg, inp, dr, cache, base_lens, tokens, h_final, draft, ta
     torch.cuda.synchronize()
     call_us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
     vb = RF.verify_bytes(Bn, n, V, lse_given=True)
+    # the same call on 16 sequences of seeded synthetic logits (draft logits
+    # N(0, 1.28^2), target = draft + N(0, 0.5^2), random drafts): the regime
+    # where the verification streams enough bytes to be bandwidth-bound
+    B16 = 16
+    i16 = Inputs16(cfg, B16)
+    z16 = torch.from_numpy(i16.synthetic_logits(0, gamma, 1.28)).to(dev)
+    t16 = torch.from_numpy(i16.target_noise(0, gamma)).to(dev)
+    t16[:, :n].mul_(0.5).add_(z16)
+    d16 = torch.from_numpy(i16.random_ids(0, gamma)).to(dev)
+    _, au16, ru16 = (torch.from_numpy(x).to(dev) for x in i16.sample_uniforms(0, gamma))
+    lse16 = torch.logsumexp(z16 / T, dim=-1)
+    tau16 = torch.empty(B16, dtype=torch.int32, device=dev)
+    nxt16 = torch.empty(B16, dtype=torch.int32, device=dev)
+    ws16_bytes = B.workspace_size(dr.dims, B16, gamma, 1)
+    ws16 = torch.empty(ws16_bytes, dtype=torch.uint8, device=dev)
+    ev16 = []
+    for rep in range(3 + 20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        B.sample_accept(dr.dims, B16, gamma, T, d16.data_ptr(), z16.data_ptr(), lse16.data_ptr(), t16.data_ptr(),
+                        au16.data_ptr(), ru16.data_ptr(), tau16.data_ptr(), nxt16.data_ptr(), ws16.data_ptr(),
+                        ws16_bytes, stream.cuda_stream)
+        b.record(stream)
+        if rep >= 3:
+            ev16.append((a, b))
+    torch.cuda.synchronize()
+    call16_us = float(np.median([a.elapsed_time(b) for a, b in ev16])) * 1e3
+    vb16 = RF.verify_bytes(B16, n, V, lse_given=True)
+    del z16, t16, ws16
     lm_bytes = RF.lm_head_sample_bytes(V, cfg.D, Bn * n, RF.elem_bytes(cfg.dtype))
     lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
     log(f"sampled step {ms * 1e3:.1f} us (greedy {greedy_ms * 1e3:.1f}), LM head + sampling {lm_us:.1f} us "
@@ -419,6 +452,10 @@ def sampled_leg(args, cfg, inp, dr, cache, base_lens, tokens, h_final, draft, ta
         "verify_kernels_us": per["verify"]["us"],
         "verify_call": {"us": round(call_us, 2), "bytes": int(vb), "GBps": round(vb / (call_us * 1e-6) / 1e9, 1),
                         "hbm_frac": round(vb / (call_us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4)},
+        "verify_call_b16": {"us": round(call16_us, 2), "bytes": int(vb16),
+                            "GBps": round(vb16 / (call16_us * 1e-6) / 1e9, 1),
+                            "hbm_frac": round(vb16 / (call16_us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4),
+                            "mean_tau": round(float(tau16.float().mean().item()), 3)},
     }
 
 

@@ -194,15 +194,24 @@ struct SampleStat {
 
 __device__ __forceinline__ SampleStat sstat_empty() { return SampleStat{-INFINITY, 0x7fffffff, -INFINITY, 0.f}; }
 
+// exp and log through the hardware base-2 units (v_exp_f32 / v_log_f32, about
+// one ulp, plus the rounding of the change of base): the sampling kernels'
+// per-element work, where the library functions' extra instructions would make
+// the large-batch passes ALU-bound.
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
+
 // A standard Gumbel variate from a uniform u in (0, 1).
-__device__ __forceinline__ float gumbel_noise(float u) { return -logf(-logf(u)); }
+__device__ __forceinline__ float gumbel_noise(float u) { return -fast_log(-fast_log(u)); }
 
 __device__ __forceinline__ void sstat_push_lse(SampleStat& s, float x) {
   if (x > s.mx) {
-    s.se = s.se * expf(s.mx - x) + 1.f;
+    s.se = s.se * fast_exp(s.mx - x) + 1.f;
     s.mx = x;
   } else {
-    s.se += expf(x - s.mx);
+    s.se += fast_exp(x - s.mx);
   }
 }
 
@@ -219,7 +228,7 @@ __device__ __forceinline__ SampleStat sstat_merge(SampleStat a, SampleStat b) {
   r.key = bk ? b.key : a.key;
   r.idx = bk ? b.idx : a.idx;
   r.mx = fmaxf(a.mx, b.mx);
-  r.se = r.mx == -INFINITY ? 0.f : a.se * expf(a.mx - r.mx) + b.se * expf(b.mx - r.mx);
+  r.se = r.mx == -INFINITY ? 0.f : a.se * fast_exp(a.mx - r.mx) + b.se * fast_exp(b.mx - r.mx);
   return r;
 }
 

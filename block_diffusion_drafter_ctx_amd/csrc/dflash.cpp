@@ -262,7 +262,8 @@ SampleWs sample_ws(const dflash_dims* d, int B, int gamma) {
   const int M = B * (gamma - 1);
   SampleWs w{};
   Carve c;
-  const size_t nchunk = static_cast<size_t>((d->V + sample_chunk(d->V) - 1) / sample_chunk(d->V));
+  const int chunk = sample_chunk(d->V, M);
+  const size_t nchunk = static_cast<size_t>((d->V + chunk - 1) / chunk);
   size_t pieces = nchunk;
   if (d->dtype == DFLASH_BF16) {
     const GemmPlan rk = plan_gemm_rk(M, d->V, d->D, true);
@@ -288,7 +289,7 @@ struct AcceptWs {
 AcceptWs sample_accept_ws(const dflash_dims* d, int B, int gamma, bool lse_given) {
   const int n = gamma - 1;
   AcceptWs w{};
-  w.chunk = sample_chunk(d->V);
+  w.chunk = sample_chunk(d->V, B * (n + 1) + (lse_given ? 0 : B * n));
   w.nchunk = (d->V + w.chunk - 1) / w.chunk;
   w.rows = B * (n + 1) + (lse_given ? 0 : B * n);
   Carve c;
@@ -368,11 +369,13 @@ dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t 
   for (int b = 1; b <= B; ++b)
     for (int g = DFLASH_MIN_GAMMA; g <= gamma; ++g) {
       const size_t dw = draft_ws(dims, b, g).total, aw = argmax_ws(dims, b, g).total;
-      const size_t sw = sample_ws(dims, b, g).total, vw = sample_accept_ws(dims, b, g, false).total;
+      const size_t sw = sample_ws(dims, b, g).total;
+      const size_t vw = sample_accept_ws(dims, b, g, false).total, vg = sample_accept_ws(dims, b, g, true).total;
       if (dw > need) need = dw;
       if (aw > need) need = aw;
       if (sw > need) need = sw;
       if (vw > need) need = vw;
+      if (vg > need) need = vg;
     }
   const size_t f = fuse_ws(dims, max_rows), i = inject_ws(dims, max_rows);
   if (f > need) need = f;
@@ -810,7 +813,7 @@ dflash_status dflash_sample_drafts(const dflash_dims* dims, const dflash_weights
   RowStatArgs r{};
   r.rows1 = r.rows = Mr;
   r.N = V;
-  r.chunk = sample_chunk(V);
+  r.chunk = sample_chunk(V, Mr);
   r.vec = V % 4 == 0;
   r.su = uniforms;
   r.inv_t = inv_t;

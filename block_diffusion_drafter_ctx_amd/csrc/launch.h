@@ -165,9 +165,11 @@ struct RowStatArgs {
   float4* stats;
 };
 
-// Columns per row-statistics chunk for a vocabulary of V (a multiple of
-// kSampleChunk; at most kSpecMaxChunks chunks per row).
-int sample_chunk(int V);
+// Columns per row-statistics chunk for `rows` rows of a vocabulary of V (a
+// multiple of kSampleChunk; at most kSpecMaxChunks chunks per row; never
+// smaller for fewer rows, so a layout sized for many rows bounds fewer).
+constexpr int kStatTargetGroups = 2048;
+int sample_chunk(int V, int rows);
 hipError_t launch_row_stats(const RowStatArgs& a, hipStream_t st);
 // merge stats [nparts][M] per row: draft[m] = best key's index, lse[m] (nullable)
 // = log sum exp(x)

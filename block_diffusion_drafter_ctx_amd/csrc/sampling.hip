@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kStatThreads) void row_stats_kernel(RowStatArgs a) 
       if (bm != -INFINITY) {
         float se = 0.f;
 #pragma unroll
-        for (int e = 0; e < kSweeps * 4; ++e) se += expf(xs[e] - bm);   // exp(-inf) = 0 for columns past the row
+        for (int e = 0; e < kSweeps * 4; ++e) se += fast_exp(xs[e] - bm);   // 0 for columns past the row
         SampleStat blk = sstat_empty();
         blk.mx = bm;
         blk.se = se;
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kStatThreads) void spec_verify_kernel(SpecArgs a) {
       const float lq = qv * a.inv_t - lq0;
       // log(p - q) = log p + log(1 - q / p) for p > q
       if (lp > lq) {
-        const float key_r = lp + logf(-expm1f(lq - lp)) + g;
+        const float key_r = lp + fast_log(-expm1f(lq - lp)) + g;
         if (better(key_r, c, pk.kr, pk.ir)) { pk.kr = key_r; pk.ir = c; }
       }
     }
@@ -298,10 +298,15 @@ __global__ __launch_bounds__(64) void spec_final_kernel(const float4* part, cons
 
 }  // namespace
 
-int sample_chunk(int V) {
-  // chunks of 4096 columns, widened so that a row has at most 64 of them
-  const int per = (V + kSpecMaxChunks - 1) / kSpecMaxChunks;
-  const int c = (per + kSampleChunk - 1) / kSampleChunk * kSampleChunk;
+int sample_chunk(int V, int rows) {
+  // chunks of 4096 columns, widened so that a row has at most 64 of them and
+  // the pass has about kStatTargetGroups workgroups (short-lived workgroups
+  // cost more than their bytes)
+  auto round_up = [](long x) { return static_cast<int>((x + kSampleChunk - 1) / kSampleChunk * kSampleChunk); };
+  int c = round_up((V + kSpecMaxChunks - 1) / kSpecMaxChunks);
+  const long want = rows > 0 ? (kStatTargetGroups + rows - 1) / rows : kSpecMaxChunks;   // chunks per row
+  const int by_groups = round_up((V + want - 1) / want);
+  if (by_groups > c) c = by_groups;
   return c > kSampleChunk ? c : kSampleChunk;
 }
 
