@@ -130,6 +130,13 @@ class OracleCache:
         self.k[l][b] = np.concatenate([self.k[l][b], k], axis=0)
         self.v[l][b] = np.concatenate([self.v[l][b], v], axis=0)
 
+    def sequence(self, b: int) -> "OracleCache":
+        """A one-sequence cache holding sequence b's rows (shared, not copied)."""
+        one = OracleCache.__new__(OracleCache)
+        one.k = [[self.k[l][b]] for l in range(len(self.k))]
+        one.v = [[self.v[l][b]] for l in range(len(self.v))]
+        return one
+
 
 # ---------------------------------------------------------------------------
 # (c) draft forward
@@ -205,6 +212,31 @@ def draft_forward(dims, layers, g_final, cache: OracleCache, gamma: int,
         s = silu(gu[..., :F]) * gu[..., F:]
         h = h + s @ np.asarray(w["w_down"], dtype=F64).T
     return rmsnorm(h, g_final, eps), block_kv
+
+
+def draft_forward_ragged(dims, layers, g_final, cache: OracleCache, gammas, embed=None, tokens=None,
+                         override=None, storage: str = "bf16"):
+    """One drafting pass over sequences whose blocks have lengths of their own.
+
+    [JP] "Ablation Study": a drafter trained with large blocks keeps its
+    acceptance with smaller inference blocks, which allows the block size to be
+    chosen per sequence at inference time ("한계와 주의사항" leaves that
+    scheduling open).  Sequences never interact in the drafter: each block
+    attends to its own context and its own rows only.  So the pass over a batch
+    with block lengths gammas[b] is, for every sequence, the one-sequence pass
+    of ``draft_forward`` over its own block.
+    tokens: list of [gammas[b]] id arrays (or override: list of [gammas[b], D]).
+    Returns (list of h_final [gammas[b], D], list of per-layer block K/V).
+    """
+    outs, kvs = [], []
+    for b, g in enumerate(gammas):
+        tok = None if tokens is None else np.asarray(tokens[b])[None]
+        ov = None if override is None else np.asarray(override[b])[None]
+        hf, kv = draft_forward(dims, layers, g_final, cache.sequence(b), int(g), embed=embed, tokens=tok,
+                               override=ov, storage=storage)
+        outs.append(hf[0])
+        kvs.append([(k[0], v[0]) for k, v in kv])
+    return outs, kvs
 
 
 # ---------------------------------------------------------------------------
@@ -348,3 +380,20 @@ def sample_accept(draft, draft_logits, target_logits, T: float, accept_u, resid_
         tok, gap = gumbel_pick(logw, resid_u[b])
         m_all[b], tau[b], nxt[b], key_gap[b] = m, m + 1, tok, gap
     return tau, nxt, dict(m=m_all, log_ratio=log_ratio, resid_empty=empty, key_gap=key_gap)
+
+
+def lm_head_argmax_ragged(h_final, lm_head):
+    """``lm_head_argmax`` per sequence of a ragged batch: h_final is a list of
+    [gamma_b, D] blocks; returns lists of drafts [gamma_b - 1], gaps, logits."""
+    out = [lm_head_argmax(np.asarray(h)[None], lm_head) for h in h_final]
+    return [d[0] for d, _, _ in out], [g[0] for _, g, _ in out], [z[0] for _, _, z in out]
+
+
+def accept_ragged(drafts, targets):
+    """``accept`` per sequence of a ragged batch: drafts[b] has n_b entries and
+    targets[b] has n_b + 1 (the target's token at each draft position, then its
+    bonus).  Returns (tau [B], next_anchor [B])."""
+    res = [accept(np.asarray(d)[None], np.asarray(t)[None]) for d, t in zip(drafts, targets)]
+    return (np.array([int(t[0]) for t, _ in res], dtype=np.int32),
+            np.array([int(x[0]) for _, x in res], dtype=np.int32))
+

@@ -468,6 +468,69 @@ def pin_accept_expectation(o):
 
 
 # ---------------------------------------------------------------------------
+# ragged blocks (a block length per sequence)
+# ---------------------------------------------------------------------------
+def pin_ragged_matches_torch_per_sequence(o):
+    # Each sequence of a ragged batch against the library-routine composition of
+    # the layers over its own context and its own block length (2, 5, 1+3).
+    rng = _rng(40)
+    dm = dims()
+    L = 2
+    layers = rand_layers(rng, dm, L)
+    gf = 1 + rng.normal(0, 0.2, dm.D)
+    lens = [6, 0, 3]
+    gammas = [2, 5, 4]
+    cache = cache_with(o, L, 3, dm.Hkv, dm.d, lens, rng)
+    h0 = [rng.normal(0, 1, (g, dm.D)) for g in gammas]
+    got, kv = o.draft_forward_ragged(dm, layers, gf, cache, gammas, override=h0, storage="f32")
+    assert [x.shape for x in got] == [(g, dm.D) for g in gammas]
+    for b in range(3):
+        ref = _torch_layer_forward(dm, layers, gf, [cache.k[l][b] for l in range(L)],
+                                   [cache.v[l][b] for l in range(L)], h0[b])
+        assert np.allclose(got[b], ref, rtol=1e-9, atol=1e-9), b
+        assert kv[b][0][0].shape == (gammas[b], dm.Hkv, dm.d)
+
+
+def pin_ragged_uniform_and_independent(o):
+    # Equal block lengths reproduce the batched pass exactly; changing one
+    # sequence's block length leaves every other sequence's output unchanged.
+    rng = _rng(41)
+    dm = dims()
+    L, B, g = 2, 3, 4
+    layers = rand_layers(rng, dm, L)
+    gf = 1 + rng.normal(0, 0.2, dm.D)
+    cache = cache_with(o, L, B, dm.Hkv, dm.d, [5, 2, 7], rng)
+    E = rng.normal(0, 0.3, (20, dm.D))
+    tok = rng.integers(0, 20, (B, g))
+    uni, _ = o.draft_forward(dm, layers, gf, cache, g, embed=E, tokens=tok, storage="bf16")
+    rag, _ = o.draft_forward_ragged(dm, layers, gf, cache, [g] * B, embed=E, tokens=list(tok), storage="bf16")
+    for b in range(B):
+        assert np.array_equal(rag[b], uni[b])
+    tok2 = [tok[0], np.concatenate([tok[1], [3, 9]]), tok[2]]
+    rag2, _ = o.draft_forward_ragged(dm, layers, gf, cache, [g, g + 2, g], embed=E, tokens=tok2, storage="bf16")
+    assert np.array_equal(rag2[0], rag[0]) and np.array_equal(rag2[2], rag[2])
+    assert rag2[1].shape == (g + 2, dm.D) and not np.allclose(rag2[1][:g], rag[1])   # block rows see each other
+
+
+def pin_ragged_argmax_accept(o):
+    # Per-sequence drafts and acceptance with their own lengths, against the
+    # batched functions on each sequence and hand-made cases.
+    rng = _rng(42)
+    D, V = 6, 30
+    E = rng.normal(0, 1, (V, D))
+    hs = [rng.normal(0, 1, (g, D)) for g in (2, 6, 4)]
+    d, gaps, z = o.lm_head_argmax_ragged(hs, E)
+    assert [x.shape for x in d] == [(1,), (5,), (3,)]
+    for b, h in enumerate(hs):
+        d1, _, z1 = o.lm_head_argmax(h[None], E)
+        assert np.array_equal(d[b], d1[0]) and np.allclose(z[b], z1[0])
+    drafts = [np.array([4]), np.array([1, 2, 3, 4, 5]), np.array([7, 8, 9])]
+    targets = [np.array([4, 11]), np.array([1, 2, 0, 4, 5, 6]), np.array([6, 8, 9, 2])]
+    tau, nxt = o.accept_ragged(drafts, targets)
+    assert list(tau) == [2, 3, 1] and list(nxt) == [11, 0, 6]
+
+
+# ---------------------------------------------------------------------------
 # sampled drafting / lossless verification
 # ---------------------------------------------------------------------------
 def _softmax(x, T=1.0):

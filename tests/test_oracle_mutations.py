@@ -79,6 +79,12 @@ MUTANTS = [
     ("bonus_from_draft_row", "logw = lp[b, n]", "logw = lq[b, n - 1]"),
     ("sample_tau_no_bonus", "m_all[b], tau[b], nxt[b], key_gap[b] = m, m + 1, tok, gap",
      "m_all[b], tau[b], nxt[b], key_gap[b] = m, max(m, 1), tok, gap"),
+    ("ragged_wrong_sequence_cache", "hf, kv = draft_forward(dims, layers, g_final, cache.sequence(b), int(g),",
+     "hf, kv = draft_forward(dims, layers, g_final, cache.sequence(0), int(g),"),
+    ("ragged_uniform_gamma", "hf, kv = draft_forward(dims, layers, g_final, cache.sequence(b), int(g),",
+     "hf, kv = draft_forward(dims, layers, g_final, cache.sequence(b), int(gammas[0]),"),
+    ("ragged_accept_shifted_targets", "res = [accept(np.asarray(d)[None], np.asarray(t)[None]) for d, t in zip(drafts, targets)]",
+     "res = [accept(np.asarray(d)[None], np.asarray(t)[None][:, ::-1]) for d, t in zip(drafts, targets)]"),
     ("sample_counts_all_accepts", "while m < n and accepted[b, m]:\n            m += 1",
      "m = int(np.sum(accepted[b]))"),
 ]
