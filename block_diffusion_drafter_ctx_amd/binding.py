@@ -19,7 +19,8 @@ ARGMAX, ACCEPT = 1, 2
 MAX_BATCH, MAX_TGT_LAYERS, MIN_GAMMA, MAX_GAMMA = 64, 8, 2, 33
 
 EXPORTED = ("dflash_version", "dflash_last_error", "dflash_workspace_size", "dflash_fuse_context",
-            "dflash_inject_kv", "dflash_draft_forward", "dflash_argmax_accept", "dflash_sample_drafts",
+            "dflash_inject_kv", "dflash_draft_forward", "dflash_draft_forward_ragged", "dflash_argmax_accept",
+            "dflash_argmax_accept_ragged", "dflash_sample_drafts",
             "dflash_sample_accept", "dflash_profile_events")
 (PROF_NONE, PROF_LM_HEAD, PROF_QKV, PROF_O, PROF_GATEUP, PROF_DOWN, PROF_FUSE, PROF_INJECT, PROF_ATTENTION,
  PROF_ROW_STATS, PROF_VERIFY) = range(11)
@@ -78,6 +79,13 @@ def load():
     lib.dflash_argmax_accept.argtypes = [POINTER(Dims), POINTER(Weights), c_uint32, c_void_p, c_int32, c_int32,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_size_t, c_void_p]
+    lib.dflash_draft_forward_ragged.restype = c_int32
+    lib.dflash_draft_forward_ragged.argtypes = [POINTER(Dims), POINTER(Weights), POINTER(KVCache), c_void_p,
+                                                c_void_p, POINTER(c_int32), c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dflash_argmax_accept_ragged.restype = c_int32
+    lib.dflash_argmax_accept_ragged.argtypes = [POINTER(Dims), POINTER(Weights), c_uint32, c_void_p, c_int32,
+                                                POINTER(c_int32), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                c_void_p, c_void_p, c_size_t, c_void_p]
     lib.dflash_sample_drafts.restype = c_int32
     lib.dflash_sample_drafts.argtypes = [POINTER(Dims), POINTER(Weights), c_void_p, c_int32, c_int32, c_float,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
@@ -138,6 +146,25 @@ def argmax_accept(dims: Dims, w: Weights, flags: int, h_final, B: int, gamma: in
     _check(load().dflash_argmax_accept(ctypes.byref(dims), ctypes.byref(w) if w is not None else None, flags,
                                        _p(h_final), B, gamma, _p(draft), _p(target), _p(tau), _p(next_anchor),
                                        _p(logits_dbg), _p(top2_gap), _p(ws), ws_bytes, _p(stream)))
+
+
+def _gammas(gammas):
+    return (c_int32 * max(1, len(gammas)))(*[int(g) for g in gammas])
+
+
+def draft_forward_ragged(dims: Dims, w: Weights, cache: KVCache, block_tokens, embed_override, gammas, h_final,
+                         ws, ws_bytes: int, stream=0):
+    _check(load().dflash_draft_forward_ragged(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(cache),
+                                              _p(block_tokens), _p(embed_override), _gammas(gammas), _p(h_final),
+                                              _p(ws), ws_bytes, _p(stream)))
+
+
+def argmax_accept_ragged(dims: Dims, w: Weights, flags: int, h_final, gammas, draft, target, tau, next_anchor,
+                         logits_dbg, top2_gap, ws, ws_bytes: int, stream=0):
+    _check(load().dflash_argmax_accept_ragged(ctypes.byref(dims), ctypes.byref(w) if w is not None else None,
+                                              flags, _p(h_final), len(gammas), _gammas(gammas), _p(draft),
+                                              _p(target), _p(tau), _p(next_anchor), _p(logits_dbg), _p(top2_gap),
+                                              _p(ws), ws_bytes, _p(stream)))
 
 
 def sample_drafts(dims: Dims, w: Weights, h_final, B: int, gamma: int, temperature: float, uniforms, draft,

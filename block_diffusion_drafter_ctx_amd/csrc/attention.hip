@@ -36,6 +36,13 @@ namespace {
 
 constexpr int kRowsPerGroup = 128;   // query rows per workgroup (8 waves)
 
+// Sequence of packed block row m (qrow0[b] <= m < qrow0[b + 1]).
+__device__ __forceinline__ int row_seq(const AttnArgs& a, int m) {
+  int b = 0;
+  while (b + 1 < a.B && m >= a.qrow0[b + 1]) ++b;
+  return b;
+}
+
 __device__ __forceinline__ void decode_item(const AttnArgs& a, int item, int& b, int& j, int& sp) {
   b = 0;
   while (b + 1 < a.B && item >= a.item_off[b + 1]) ++b;
@@ -112,7 +119,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
   const int kend = min(nk, kbeg + a.split_keys);
   const int r = blockIdx.y * kRowsPerGroup + wave * 16 + (lane & 15);
   const int G = a.Hq / a.Hkv;
-  const bool computes = blockIdx.y * kRowsPerGroup + wave * 16 < a.R;   // uniform per wave
+  const int gb = a.gam[b], Rb = G * gb;       // this sequence's block rows and query rows
+  const bool computes = blockIdx.y * kRowsPerGroup + wave * 16 < Rb;   // uniform per wave
 
   uint4 qh[DS], ql[DS];                       // query fragments, loaded after the first key blocks
   const int64_t head = static_cast<int64_t>(b) * a.Hkv + j;
@@ -237,9 +245,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
   Raw rr[DEPTH][PER];
 #pragma unroll
   for (int dd = 0; dd < DEPTH; ++dd) load(rr[dd], blk(dd));
-  if (r < a.R) {
-    const int h = j * G + r / a.gamma, i = r % a.gamma;
-    const float* qp = a.q + (static_cast<int64_t>(b * a.gamma + i) * a.Hq + h) * HD + 8 * g4;
+  if (r < Rb) {
+    const int h = j * G + r / gb, i = r % gb;
+    const float* qp = a.q + (static_cast<int64_t>(a.qrow0[b] + i) * a.Hq + h) * HD + 8 * g4;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       const float4 x0 = *reinterpret_cast<const float4*>(qp + ds * 32);
@@ -316,8 +324,9 @@ __global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
   const int nstep = (nblk + NG - 1) / NG;
   const int row0 = blockIdx.y * 16 * WPG + wq * 16;
   const int r = row0 + (lane & 15);
-  const bool computes = row0 < a.R;             // uniform per wave
   const int G = a.Hq / a.Hkv;
+  const int gb = a.gam[b], Rb = G * gb;         // this sequence's block rows and query rows
+  const bool computes = row0 < Rb;              // uniform per wave
   const int64_t head = static_cast<int64_t>(b) * a.Hkv + j;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.kc) + head * a.cap * HD;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.vc) + head * HD * a.cap;
@@ -427,9 +436,9 @@ __global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
 
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st) issue(st, st);
-  if (computes && r < a.R) {
-    const int h = j * G + r / a.gamma, i = r % a.gamma;
-    const float* qp = a.q + (static_cast<int64_t>(b * a.gamma + i) * a.Hq + h) * HD + 8 * g4;
+  if (computes && r < Rb) {
+    const int h = j * G + r / gb, i = r % gb;
+    const float* qp = a.q + (static_cast<int64_t>(a.qrow0[b] + i) * a.Hq + h) * HD + 8 * g4;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       const float4 x0 = *reinterpret_cast<const float4*>(qp + ds * 32);
@@ -528,9 +537,9 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   __shared__ float inv_l;
   const int idx = blockIdx.x;
   const int m = idx / a.Hq, h = idx % a.Hq;
-  const int b = m / a.gamma, i = m % a.gamma;
+  const int b = row_seq(a, m), i = m - a.qrow0[b];
   const int G = a.Hq / a.Hkv, j = h / G;
-  const int r = (h - j * G) * a.gamma + i;
+  const int r = (h - j * G) * a.gam[b] + i;
   const int ns = a.nsplit[b];
   const int it0 = a.item_off[b] + j * ns;
   if (threadIdx.x < 64) {
@@ -560,7 +569,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const int idx = blockIdx.x, lane = threadIdx.x;
   const int m = idx / a.Hq, h = idx % a.Hq;
-  const int b = m / a.gamma;
+  const int b = row_seq(a, m);
   const int G = a.Hq / a.Hkv, j = h / G;
   const float* qp = a.q + (static_cast<int64_t>(m) * a.Hq + h) * a.d;
   const float q0 = lane < a.d ? qp[lane] * a.scale_log2 : 0.f;
@@ -652,7 +661,7 @@ hipError_t launch_attention(const AttnArgs& a0, const AttnPlan& p, bool bf16_wei
                             hipStream_t st, void* stop_event) {
   AttnArgs a = a0;
   if (!bf16_weights) {
-    hipLaunchKernelGGL(attn_f32_kernel, dim3(a.B * a.gamma * a.Hq), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(attn_f32_kernel, dim3(a.qrow0[a.B] * a.Hq), dim3(64), 0, st, a);
     if (stop_event != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(stop_event), st);
     return hipGetLastError();
   }
@@ -677,7 +686,7 @@ hipError_t launch_attention(const AttnArgs& a0, const AttnPlan& p, bool bf16_wei
   }
   if (e != hipSuccess) return e;
   if (stop_event != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(stop_event), st);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.gamma * a.Hq), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.qrow0[a.B] * a.Hq), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 

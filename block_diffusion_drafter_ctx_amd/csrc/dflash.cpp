@@ -196,8 +196,8 @@ struct DraftWs {
   size_t h, a, q, o, s, part, att_o, att_ml, total;
 };
 
-DraftWs draft_ws(const dflash_dims* d, int B, int gamma) {
-  const int M = B * gamma;
+// M block rows in all (sum of the block lengths), the longest block gmax rows.
+DraftWs draft_ws(const dflash_dims* d, int B, int M, int gmax) {
   const int hd = d->Hq * d->head_dim;
   const int nqkv = (d->Hq + 2 * d->Hkv) * d->head_dim;
   size_t part = 0;
@@ -209,7 +209,7 @@ DraftWs draft_ws(const dflash_dims* d, int B, int gamma) {
   upd(d->D, hd);
   upd(2 * d->F, d->D);
   upd(d->D, d->F);
-  const int R = (d->Hq / d->Hkv) * gamma;
+  const int R = (d->Hq / d->Hkv) * gmax;
   const size_t att = d->dtype == DFLASH_BF16 ? attention_part_bound(B, d->Hkv, R, d->head_dim) : 0;
   const size_t rpad_rows = att / (d->head_dim + 2);
   DraftWs w{};
@@ -228,13 +228,15 @@ DraftWs draft_ws(const dflash_dims* d, int B, int gamma) {
 
 // LM head: split-K partials [S][M][V], then per-128-column top-2 [ceil(V/128)][M][3]
 struct ArgmaxWs {
-  size_t part, top2, total;
+  size_t part, top2, rows, total;
 };
 
-ArgmaxWs argmax_ws(const dflash_dims* d, int B, int gamma) {
-  const int M = B * (gamma - 1);
+// M mask rows (logits rows); `gathered` adds room for them as a dense [M][D]
+// block (a ragged batch's mask rows are gathered before the LM head).
+ArgmaxWs argmax_ws(const dflash_dims* d, int M, bool gathered = false) {
   ArgmaxWs w{};
   Carve c;
+  if (gathered) w.rows = c.take(static_cast<size_t>(M) * d->D * 4);
   if (d->dtype == DFLASH_F32) {
     w.part = c.take(static_cast<size_t>(M) * d->V * 4);
   } else {
@@ -364,18 +366,18 @@ dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t 
   DF_REQUIRE(max_rows >= 0, DFLASH_ERR_INVALID_ARG, "max_rows=%d < 0", max_rows);
   DF_REQUIRE(bytes != nullptr, DFLASH_ERR_INVALID_ARG, "bytes is NULL");
   // The kernels chosen (and so the scratch they need) depend on the row counts,
-  // not monotonically: take the maximum over every batch <= B and block <= gamma.
+  // not monotonically: take the maximum over every row count that a call with
+  // at most B sequences and blocks of at most gamma rows can have, uniform or
+  // ragged (the attention bound grows with B and the longest block).
   size_t need = 0;
+  auto upd = [&](size_t x) { need = x > need ? x : need; };
+  for (int M = DFLASH_MIN_GAMMA; M <= B * gamma; ++M) upd(draft_ws(dims, B, M, gamma).total);
+  for (int M = 1; M <= B * (gamma - 1); ++M) upd(argmax_ws(dims, M, true).total);
   for (int b = 1; b <= B; ++b)
     for (int g = DFLASH_MIN_GAMMA; g <= gamma; ++g) {
-      const size_t dw = draft_ws(dims, b, g).total, aw = argmax_ws(dims, b, g).total;
-      const size_t sw = sample_ws(dims, b, g).total;
-      const size_t vw = sample_accept_ws(dims, b, g, false).total, vg = sample_accept_ws(dims, b, g, true).total;
-      if (dw > need) need = dw;
-      if (aw > need) need = aw;
-      if (sw > need) need = sw;
-      if (vw > need) need = vw;
-      if (vg > need) need = vg;
+      upd(sample_ws(dims, b, g).total);
+      upd(sample_accept_ws(dims, b, g, false).total);
+      upd(sample_accept_ws(dims, b, g, true).total);
     }
   const size_t f = fuse_ws(dims, max_rows), i = inject_ws(dims, max_rows);
   if (f > need) need = f;
@@ -541,17 +543,28 @@ dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w,
   return ok();
 }
 
-dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights* w, const dflash_kv_cache* cache,
-                                   const int32_t* block_tokens, const float* embed_override, int32_t gamma,
-                                   float* h_final, void* ws, size_t ws_bytes, void* stream) {
+// The drafting pass over blocks of gammas[b] rows (host array), packed row
+// after row: sequence b's block rows start at the sum of the earlier lengths.
+static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_weights* w,
+                                        const dflash_kv_cache* cache, const int32_t* block_tokens,
+                                        const float* embed_override, const int32_t* gammas, float* h_final,
+                                        void* ws, size_t ws_bytes, void* stream) {
   dflash_status st = check_dims(dims);
   if (st != DFLASH_OK) return st;
-  if ((st = check_gamma(gamma)) != DFLASH_OK) return st;
   DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
   if ((st = check_cache(cache)) != DFLASH_OK) return st;
-  for (int b = 0; b < cache->B; ++b)
-    DF_REQUIRE(static_cast<int64_t>(cache->len[b]) + gamma <= cache->cap, DFLASH_ERR_CAPACITY,
-               "sequence %d: len %d + gamma %d exceeds cap %d", b, cache->len[b], gamma, cache->cap);
+  DF_REQUIRE(gammas != nullptr, DFLASH_ERR_INVALID_ARG, "gammas is NULL");
+  int M = 0, gmax = 0;
+  int32_t qrow0[kMaxSeq + 1];
+  for (int b = 0; b < cache->B; ++b) {
+    if ((st = check_gamma(gammas[b])) != DFLASH_OK) return st;
+    DF_REQUIRE(static_cast<int64_t>(cache->len[b]) + gammas[b] <= cache->cap, DFLASH_ERR_CAPACITY,
+               "sequence %d: len %d + gamma %d exceeds cap %d", b, cache->len[b], gammas[b], cache->cap);
+    qrow0[b] = M;
+    M += gammas[b];
+    gmax = gammas[b] > gmax ? gammas[b] : gmax;
+  }
+  qrow0[cache->B] = M;
   const char* names[] = {"w_qkv", "w_o", "w_gateup", "w_down", "g_attn", "g_ffn", "g_final"};
   const void* ptrs[] = {w->w_qkv, w->w_o, w->w_gateup, w->w_down, w->g_attn, w->g_ffn, w->g_final};
   for (int i = 0; i < 7; ++i)
@@ -564,13 +577,13 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
   }
   if ((st = check_ptr(h_final, "h_final")) != DFLASH_OK) return st;
   const int B = cache->B;
-  const DraftWs lay = draft_ws(dims, B, gamma);
+  const DraftWs lay = draft_ws(dims, B, M, gmax);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != DFLASH_OK) return st;
   if ((st = check_device()) != DFLASH_OK) return st;
 
   const bool bf = dims->dtype == DFLASH_BF16, cbf = dims->cache_dtype == DFLASH_BF16;
   const int D = dims->D, d = dims->head_dim, Hq = dims->Hq, Hkv = dims->Hkv, F = dims->F, L = dims->L;
-  const int M = B * gamma, hd = Hq * d, nqkv = (Hq + 2 * Hkv) * d;
+  const int hd = Hq * d, nqkv = (Hq + 2 * Hkv) * d;
   const size_t es = esize(dims), cs = csize(dims);
   char* base = static_cast<char*>(ws);
   float* h = reinterpret_cast<float*>(base + lay.h);
@@ -612,8 +625,8 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
   };
 
   int32_t nkeys[kMaxSeq];
-  for (int b = 0; b < B; ++b) nkeys[b] = cache->len[b] + gamma;
-  const int R = (Hq / Hkv) * gamma;
+  for (int b = 0; b < B; ++b) nkeys[b] = cache->len[b] + gammas[b];
+  const int R = (Hq / Hkv) * gmax;
   const AttnPlan ap = bf ? plan_attention(B, nkeys, Hkv, R, d) : AttnPlan{};
   const size_t layer_elems = static_cast<size_t>(B) * Hkv * cache->cap * d;
 
@@ -638,7 +651,7 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
     sa.cap = cache->cap;
     sa.rows.B = B;
     for (int b = 0; b < B; ++b) {
-      sa.rows.row_off[b] = b * gamma;
+      sa.rows.row_off[b] = qrow0[b];
       sa.rows.pos0[b] = cache->len[b];
     }
     sa.rows.row_off[B] = M;
@@ -652,14 +665,18 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
     at.part_ml = reinterpret_cast<float*>(base + lay.att_ml);
     at.o_out = o;
     at.B = B;
-    at.gamma = gamma;
     at.Hq = Hq;
     at.Hkv = Hkv;
     at.d = d;
     at.cap = cache->cap;
     at.R = R;
     at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
-    for (int b = 0; b < B; ++b) at.nkeys[b] = nkeys[b];
+    for (int b = 0; b < B; ++b) {
+      at.nkeys[b] = nkeys[b];
+      at.gam[b] = gammas[b];
+      at.qrow0[b] = qrow0[b];
+    }
+    at.qrow0[B] = M;
     const int pa = prof_begin(DFLASH_PROF_ATTENTION, s);
     DF_HIP(launch_attention(at, ap, bf, cbf, s, pa >= 0 ? g_prof.stop[pa] : nullptr));
 
@@ -695,6 +712,65 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
   return ok();
 }
 
+dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights* w, const dflash_kv_cache* cache,
+                                   const int32_t* block_tokens, const float* embed_override, int32_t gamma,
+                                   float* h_final, void* ws, size_t ws_bytes, void* stream) {
+  dflash_status st = check_gamma(gamma);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_cache(cache)) != DFLASH_OK) return st;
+  int32_t gammas[kMaxSeq];
+  for (int b = 0; b < cache->B; ++b) gammas[b] = gamma;
+  return draft_forward_impl(dims, w, cache, block_tokens, embed_override, gammas, h_final, ws, ws_bytes, stream);
+}
+
+dflash_status dflash_draft_forward_ragged(const dflash_dims* dims, const dflash_weights* w,
+                                          const dflash_kv_cache* cache, const int32_t* block_tokens,
+                                          const float* embed_override, const int32_t* gammas, float* h_final,
+                                          void* ws, size_t ws_bytes, void* stream) {
+  return draft_forward_impl(dims, w, cache, block_tokens, embed_override, gammas, h_final, ws, ws_bytes, stream);
+}
+
+// LM head + argmax over Mr activation rows that g's A mapping addresses (K = D).
+static dflash_status lm_head_argmax(const dflash_dims* dims, const dflash_weights* w, GemmArgs g, int Mr,
+                                    int32_t* draft, float* logits_dbg, float* top2_gap, char* base,
+                                    const ArgmaxWs& lay, void* ws, hipStream_t s) {
+  const int D = dims->D;
+  g.w = w->lm_head;
+  g.w_ld = D;
+  g.w_rg = INT_MAX;
+  g.w_gs = 0;
+  g.w_off = 0;
+  g.M = Mr;
+  g.N = dims->V;
+  g.K = D;
+  if (dims->dtype == DFLASH_BF16) {
+    g.part = reinterpret_cast<float*>(base + lay.part);
+    float* top2 = reinterpret_cast<float*>(base + lay.top2);
+    const GemmPlan rk = plan_gemm_rk(Mr, dims->V, D, true);
+    if (rk.rk) {
+      // one pass over the LM head: logits reduced in-register, top-2 per workgroup
+      const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
+      DF_HIP(launch_gemm_rk(g, rk, top2, logits_dbg, s));
+      prof_end(ps, s);
+      DF_HIP(launch_argmax_final(top2, rk.grid, Mr, draft, top2_gap, s));
+    } else {
+      const GemmPlan p = plan_gemm(Mr, dims->V, D, A_F32_SPLIT, true);
+      const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
+      DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, s));
+      prof_end(ps, s);
+      int nt = 0;
+      DF_HIP(launch_reduce_top2(g.part, p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
+      DF_HIP(launch_argmax_final(top2, nt, Mr, draft, top2_gap, s));
+    }
+  } else {
+    float* lg = logits_dbg != nullptr ? logits_dbg : reinterpret_cast<float*>(base + lay.part);
+    g.part = lg;
+    DF_HIP(launch_gemm_f32(g, s));
+    DF_HIP(launch_argmax_rows(lg, Mr, dims->V, draft, top2_gap, s));
+  }
+  return ok();
+}
+
 dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights* w, uint32_t flags,
                                    const float* h_final, int32_t B, int32_t gamma, int32_t* draft,
                                    const int32_t* target, int32_t* tau, int32_t* next_anchor, float* logits_dbg,
@@ -706,13 +782,14 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
              "flags=0x%x must be a non-empty subset of ARGMAX|ACCEPT", flags);
   DF_REQUIRE(B >= 1 && B <= DFLASH_MAX_BATCH, DFLASH_ERR_INVALID_ARG, "B=%d outside [1, %d]", B, DFLASH_MAX_BATCH);
   DF_REQUIRE(draft != nullptr, DFLASH_ERR_INVALID_ARG, "draft is NULL");
+  const int n = gamma - 1, Mr = B * n, D = dims->D;
   size_t need = 0;
   if (flags & DFLASH_ARGMAX) {
     DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
     if ((st = check_ptr(w->lm_head, "lm_head")) != DFLASH_OK) return st;
     if ((st = check_ptr(h_final, "h_final")) != DFLASH_OK) return st;
     if (logits_dbg != nullptr && (st = check_ptr(logits_dbg, "logits_dbg")) != DFLASH_OK) return st;
-    need = argmax_ws(dims, B, gamma).total;
+    need = argmax_ws(dims, Mr).total;
   }
   if (flags & DFLASH_ACCEPT) {
     DF_REQUIRE(target != nullptr && tau != nullptr && next_anchor != nullptr, DFLASH_ERR_INVALID_ARG,
@@ -722,7 +799,6 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
   if ((st = check_device()) != DFLASH_OK) return st;
 
   hipStream_t s = as_stream(stream);
-  const int n = gamma - 1, Mr = B * n, D = dims->D;
   if (flags & DFLASH_ARGMAX) {
     GemmArgs g{};
     for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = h_final + D;   // block row 1 of sequence 0
@@ -730,43 +806,71 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
     g.a_rg = n;
     g.a_gs = static_cast<int64_t>(gamma) * D;
     g.a_ld = D;
-    g.w = w->lm_head;
-    g.w_ld = D;
-    g.w_rg = INT_MAX;
-    g.w_gs = 0;
-    g.w_off = 0;
-    g.M = Mr;
-    g.N = dims->V;
-    g.K = D;
-    const ArgmaxWs lay = argmax_ws(dims, B, gamma);
-    char* base = static_cast<char*>(ws);
-    if (dims->dtype == DFLASH_BF16) {
-      g.part = reinterpret_cast<float*>(base + lay.part);
-      float* top2 = reinterpret_cast<float*>(base + lay.top2);
-      const GemmPlan rk = plan_gemm_rk(Mr, dims->V, D, true);
-      if (rk.rk) {
-        // one pass over the LM head: logits reduced in-register, top-2 per workgroup
-        const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-        DF_HIP(launch_gemm_rk(g, rk, top2, logits_dbg, s));
-        prof_end(ps, s);
-        DF_HIP(launch_argmax_final(top2, rk.grid, Mr, draft, top2_gap, s));
-      } else {
-        const GemmPlan p = plan_gemm(Mr, dims->V, D, A_F32_SPLIT, true);
-        const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-        DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, s));
-        prof_end(ps, s);
-        int nt = 0;
-        DF_HIP(launch_reduce_top2(g.part, p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
-        DF_HIP(launch_argmax_final(top2, nt, Mr, draft, top2_gap, s));
-      }
-    } else {
-      float* lg = logits_dbg != nullptr ? logits_dbg : static_cast<float*>(ws);
-      g.part = lg;
-      DF_HIP(launch_gemm_f32(g, s));
-      DF_HIP(launch_argmax_rows(lg, Mr, dims->V, draft, top2_gap, s));
-    }
+    if ((st = lm_head_argmax(dims, w, g, Mr, draft, logits_dbg, top2_gap, static_cast<char*>(ws),
+                             argmax_ws(dims, Mr), ws, s)) != DFLASH_OK)
+      return st;
   }
   if (flags & DFLASH_ACCEPT) DF_HIP(launch_accept(draft, target, B, n, tau, next_anchor, s));
+  return ok();
+}
+
+dflash_status dflash_argmax_accept_ragged(const dflash_dims* dims, const dflash_weights* w, uint32_t flags,
+                                          const float* h_final, int32_t B, const int32_t* gammas, int32_t* draft,
+                                          const int32_t* target, int32_t* tau, int32_t* next_anchor,
+                                          float* logits_dbg, float* top2_gap, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  DF_REQUIRE(flags != 0 && (flags & ~(DFLASH_ARGMAX | DFLASH_ACCEPT)) == 0, DFLASH_ERR_INVALID_ARG,
+             "flags=0x%x must be a non-empty subset of ARGMAX|ACCEPT", flags);
+  DF_REQUIRE(B >= 1 && B <= DFLASH_MAX_BATCH, DFLASH_ERR_INVALID_ARG, "B=%d outside [1, %d]", B, DFLASH_MAX_BATCH);
+  DF_REQUIRE(gammas != nullptr, DFLASH_ERR_INVALID_ARG, "gammas is NULL");
+  DF_REQUIRE(draft != nullptr, DFLASH_ERR_INVALID_ARG, "draft is NULL");
+  // block rows of sequence b start at qrow0[b]; its drafts at doff[b]
+  SeqRows mask{}, acc{};
+  mask.B = acc.B = B;
+  int M = 0, Mr = 0;
+  for (int b = 0; b < B; ++b) {
+    if ((st = check_gamma(gammas[b])) != DFLASH_OK) return st;
+    mask.row_off[b] = Mr;          // gathered mask rows [Mr, Mr + n_b) ...
+    mask.pos0[b] = M + 1;          // ... come from block rows M + 1 ..
+    acc.row_off[b] = Mr;           // drafts of sequence b
+    acc.pos0[b] = M;               // its targets (n_b + 1 of them) line up with its block rows
+    M += gammas[b];
+    Mr += gammas[b] - 1;
+  }
+  mask.row_off[B] = acc.row_off[B] = Mr;
+  const int D = dims->D;
+  size_t need = 0;
+  if (flags & DFLASH_ARGMAX) {
+    DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
+    if ((st = check_ptr(w->lm_head, "lm_head")) != DFLASH_OK) return st;
+    if ((st = check_ptr(h_final, "h_final")) != DFLASH_OK) return st;
+    if (logits_dbg != nullptr && (st = check_ptr(logits_dbg, "logits_dbg")) != DFLASH_OK) return st;
+    need = argmax_ws(dims, Mr, true).total;
+  }
+  if (flags & DFLASH_ACCEPT) {
+    DF_REQUIRE(target != nullptr && tau != nullptr && next_anchor != nullptr, DFLASH_ERR_INVALID_ARG,
+               "target, tau and next_anchor must be non-NULL for ACCEPT");
+  }
+  if ((st = check_ws(ws, ws_bytes, need)) != DFLASH_OK) return st;
+  if ((st = check_device()) != DFLASH_OK) return st;
+
+  hipStream_t s = as_stream(stream);
+  if (flags & DFLASH_ARGMAX) {
+    const ArgmaxWs lay = argmax_ws(dims, Mr, true);
+    char* base = static_cast<char*>(ws);
+    float* rows = reinterpret_cast<float*>(base + lay.rows);
+    DF_HIP(launch_gather_rows(h_final, rows, D, mask, s));
+    GemmArgs g{};
+    for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = rows;
+    g.a_cols = D;
+    g.a_rg = INT_MAX;
+    g.a_gs = 0;
+    g.a_ld = D;
+    if ((st = lm_head_argmax(dims, w, g, Mr, draft, logits_dbg, top2_gap, base, lay, ws, s)) != DFLASH_OK) return st;
+  }
+  if (flags & DFLASH_ACCEPT) DF_HIP(launch_accept_ragged(draft, target, acc, tau, next_anchor, s));
   return ok();
 }
 

@@ -9,6 +9,8 @@
 //   argmax_final   merge per-tile top-2 into draft ids and top-2 gaps
 //   argmax_rows    same from plain fp32 logits rows (fp32 storage path)
 //   accept         greedy acceptance length and next anchor (one wave per sequence)
+//   gather_rows    a ragged batch's mask rows into one dense block for the LM head
+//   accept_ragged  acceptance with a draft count per sequence
 // Every reduction sums partials in split order: results are bit-reproducible.
 #include "common.h"
 #include "launch.h"
@@ -311,7 +313,52 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t* draft, const 
   }
 }
 
+// ------------------------------------------------------------- ragged blocks
+// dst row m of sequence b (t.row_off[b] <= m < t.row_off[b + 1]) is src row
+// t.pos0[b] + (m - t.row_off[b]); one workgroup per row, float4 columns.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const float* src, float* dst, int D, SeqRows t) {
+  const int m = blockIdx.x;
+  int b = 0;
+  while (b + 1 < t.B && m >= t.row_off[b + 1]) ++b;
+  const int64_t sr = t.pos0[b] + (m - t.row_off[b]);
+  for (int c = 4 * threadIdx.x; c < D; c += 4 * blockDim.x)
+    *reinterpret_cast<float4*>(dst + static_cast<int64_t>(m) * D + c) =
+        *reinterpret_cast<const float4*>(src + sr * D + c);
+}
+
+// Sequence b's n_b = t.row_off[b + 1] - t.row_off[b] drafts start at draft +
+// t.row_off[b] and its n_b + 1 target tokens at target + t.pos0[b].
+__global__ __launch_bounds__(64) void accept_ragged_kernel(const int32_t* draft, const int32_t* target, SeqRows t,
+                                                           int32_t* tau, int32_t* next_anchor) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int n = t.row_off[b + 1] - t.row_off[b];
+  const int32_t* d = draft + t.row_off[b];
+  const int32_t* tg = target + t.pos0[b];
+  const bool miss = lane < n && d[lane] != tg[lane];
+  const unsigned long long mask = __ballot(miss);
+  const int m = mask ? __ffsll(mask) - 1 : n;
+  if (lane == 0) {
+    tau[b] = m + 1;
+    next_anchor[b] = tg[m];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_rows(const float* src, float* dst, int D, const SeqRows& t, hipStream_t st) {
+  const int M = t.row_off[t.B];
+  if (M <= 0) return hipSuccess;
+  if (D % 4 != 0) return hipErrorInvalidValue;
+  int threads = D / 4 < 256 ? (D / 4 + 63) / 64 * 64 : 256;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(M), dim3(threads), 0, st, src, dst, D, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_ragged(const int32_t* draft, const int32_t* target, const SeqRows& t, int32_t* tau,
+                                int32_t* next_anchor, hipStream_t st) {
+  hipLaunchKernelGGL(accept_ragged_kernel, dim3(t.B), dim3(64), 0, st, draft, target, t, tau, next_anchor);
+  return hipGetLastError();
+}
 
 hipError_t launch_ctx_norm(const float* part, int S, int T, int D, const void* g, float eps, void* out,
                            bool bf16_weights, bool bf16_cache, hipStream_t st) {

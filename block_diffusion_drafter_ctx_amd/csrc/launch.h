@@ -140,6 +140,14 @@ hipError_t launch_argmax_rows(const float* logits, int M, int V, int32_t* draft,
 hipError_t launch_accept(const int32_t* draft, const int32_t* target, int B, int n, int32_t* tau,
                          int32_t* next_anchor, hipStream_t st);
 
+// dst row m of sequence b (t.row_off[b] <= m < t.row_off[b+1]) = src row
+// t.pos0[b] + m - t.row_off[b]; rows of D floats (D % 4 == 0, 16-byte aligned)
+hipError_t launch_gather_rows(const float* src, float* dst, int D, const SeqRows& t, hipStream_t st);
+// greedy acceptance with n_b = t.row_off[b+1] - t.row_off[b] drafts at
+// draft + t.row_off[b] and n_b + 1 targets at target + t.pos0[b] (n_b <= 63)
+hipError_t launch_accept_ragged(const int32_t* draft, const int32_t* target, const SeqRows& t, int32_t* tau,
+                                int32_t* next_anchor, hipStream_t st);
+
 // ------------------------------------------------------------ sampling
 constexpr int kSampleChunk = 4096;   // columns per row-statistics workgroup (at least)
 constexpr int kSpecMaxChunks = 64;   // row-statistics pieces per row, at most
@@ -197,14 +205,16 @@ hipError_t launch_spec_verify(const SpecArgs& a, hipStream_t st);
 
 // ------------------------------------------------------------ attention
 struct AttnArgs {
-  const float* q;        // [B*gamma][Hq*d]
+  const float* q;        // [M][Hq*d], M = qrow0[B] block rows (sequence b's at qrow0[b] ..)
   const void* kc;        // layer base [B][Hkv][cap][d]
   const void* vc;        // layer base [B][Hkv][d][cap]
   float* part_o;         // [items][Rpad][d]
   float* part_ml;        // [items][Rpad][2]
   float* o_out;          // [B*gamma][Hq*d]
-  int32_t B, gamma, Hq, Hkv, d, cap;
-  int32_t R, Rpad;       // query rows per (b, kv head) = G*gamma, padded to 16
+  int32_t B, Hq, Hkv, d, cap;
+  int32_t R, Rpad;       // query rows per (b, kv head): the largest G*gam[b], padded to 16
+  int32_t gam[kMaxSeq];       // block rows of sequence b
+  int32_t qrow0[kMaxSeq + 1]; // first block row of sequence b in q / o_out (qrow0[B] = M)
   int32_t split_keys;    // keys per work item (multiple of 32)
   int32_t items;
   float scale_log2;      // log2(e) / sqrt(d)

@@ -142,3 +142,16 @@ class DeviceDrafter:
         B.sample_accept(self.dims, B_, gamma, temperature, p(draft), p(draft_logits), p(draft_lse),
                         p(target_logits), p(accept_u), p(resid_u), p(tau), p(nxt), p(self.ws), self.ws_bytes,
                         _stream())
+
+    # ---- blocks with a length per sequence
+    def draft_ragged(self, cache: DeviceCache, tokens, override, gammas, h_final: torch.Tensor):
+        B.draft_forward_ragged(self.dims, self.weights, cache.struct, 0 if tokens is None else tokens.data_ptr(),
+                               0 if override is None else override.data_ptr(), list(gammas), h_final.data_ptr(),
+                               self.ws.data_ptr(), self.ws_bytes, _stream())
+
+    def argmax_accept_ragged(self, flags, h_final, gammas, draft, target=None, tau=None, nxt=None, logits=None,
+                             gap=None):
+        p = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+        B.argmax_accept_ragged(self.dims, self.weights, flags, p(h_final), list(gammas), p(draft), p(target), p(tau),
+                               p(nxt), p(logits), p(gap), p(self.ws), self.ws_bytes, _stream())
+

@@ -10,6 +10,8 @@
  *                             rows), bidirectional over [context ; block]
  *   dflash_argmax_accept  (d) LM-head argmax of the mask rows and greedy
  *                             acceptance length against the target's tokens
+ * with variants for blocks whose length differs per sequence:
+ *   dflash_draft_forward_ragged, dflash_argmax_accept_ragged
  * and, for decoding at a temperature T > 0, the sampled counterpart of (d):
  *   dflash_sample_drafts  draft tokens drawn from softmax(logits / T)
  *   dflash_sample_accept  lossless acceptance of a sampled block against the
@@ -129,8 +131,9 @@ const char* dflash_version(void);
 const char* dflash_last_error(void);
 
 /* Bytes of workspace every call needs for up to B sequences, blocks of up to
- * `gamma` rows and fuse/inject calls of up to `max_rows` rows in total.
- * Pure host computation; enqueues nothing. */
+ * `gamma` rows (the same length for all sequences, or lengths of their own up
+ * to gamma in the _ragged calls) and fuse/inject calls of up to `max_rows`
+ * rows in total.  Pure host computation; enqueues nothing. */
 dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t gamma,
                                     int32_t max_rows, size_t* bytes);
 
@@ -179,6 +182,26 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
                                    const float* embed_override, int32_t gamma, float* h_final,
                                    void* ws, size_t ws_bytes, void* stream);
 
+/* (c) with a block length per sequence ([JP] "Ablation Study": a drafter
+ * trained with large blocks keeps its acceptance with smaller inference blocks,
+ * which allows choosing the block size per sequence at inference time;
+ * "한계와 주의사항" leaves that scheduling open).  The same pass as
+ * dflash_draft_forward, where sequence b's block has gammas[b] rows; the
+ * blocks are packed row after row (sequence b's rows start at
+ * G_b = gammas[0] + ... + gammas[b-1]) and every block attends only to its
+ * own context and its own rows.
+ *   gammas          HOST [cache->B], each in [DFLASH_MIN_GAMMA, DFLASH_MAX_GAMMA]
+ *   block_tokens    [sum gammas] int32 (each block: anchor, then mask ids)
+ *   embed_override  nullable [sum gammas][D] float32
+ *   h_final         out [sum gammas][D] float32
+ * Errors: DFLASH_ERR_CAPACITY if len[b] + gammas[b] > cap.  Scratch rows
+ * [len[b], len[b] + gammas[b]) of each sequence are written; len is unchanged.
+ * A workspace sized by dflash_workspace_size(dims, B, max gammas, ..) suffices. */
+dflash_status dflash_draft_forward_ragged(const dflash_dims* dims, const dflash_weights* w,
+                                          const dflash_kv_cache* cache, const int32_t* block_tokens,
+                                          const float* embed_override, const int32_t* gammas, float* h_final,
+                                          void* ws, size_t ws_bytes, void* stream);
+
 #define DFLASH_ARGMAX 1u
 #define DFLASH_ACCEPT 2u
 
@@ -202,6 +225,24 @@ dflash_status dflash_argmax_accept(const dflash_dims* dims, const dflash_weights
                                    const int32_t* target, int32_t* tau, int32_t* next_anchor,
                                    float* logits_dbg, float* top2_gap, void* ws, size_t ws_bytes,
                                    void* stream);
+
+/* (d) for blocks packed as dflash_draft_forward_ragged writes them: sequence b
+ * has n_b = gammas[b] - 1 drafts.
+ *   h_final      [sum gammas][D] float32 (ARGMAX)
+ *   gammas       HOST [B]
+ *   draft        [sum n_b] int32, sequence b's at n_0 + ... + n_{b-1}: written by
+ *                ARGMAX, read by ACCEPT
+ *   target       [sum gammas] int32: sequence b's n_b + 1 target tokens (at each
+ *                draft position, then the bonus) at gammas[0] + ... + gammas[b-1]
+ *   tau, next_anchor  out [B] int32 (ACCEPT)
+ *   logits_dbg   nullable out [sum n_b][V] float32; top2_gap nullable [sum n_b]
+ * Same rules as dflash_argmax_accept per sequence.  The mask rows are gathered
+ * into the workspace before the LM head. */
+dflash_status dflash_argmax_accept_ragged(const dflash_dims* dims, const dflash_weights* w, uint32_t flags,
+                                          const float* h_final, int32_t B, const int32_t* gammas, int32_t* draft,
+                                          const int32_t* target, int32_t* tau, int32_t* next_anchor,
+                                          float* logits_dbg, float* top2_gap, void* ws, size_t ws_bytes,
+                                          void* stream);
 
 /* Sampled drafting at temperature T ([JP] "주요 결과": DFlash decodes at
  * temperature 1 as well as greedily; [JP] "학습 방법": all block positions after

@@ -207,3 +207,45 @@ def test_sampling_arguments_checked(lib):
         B.sample_accept(_dims(), 1, 16, 1.0, 0x1000, 0x2000, None, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000,
                         0x10000, 16)
     assert e.value.status == B.ERR_WORKSPACE
+
+
+def test_ragged_draft_checks(lib):
+    w = B.Weights(w_qkv=0x1000, w_o=0x1000, w_gateup=0x1000, w_down=0x1000, g_attn=0x1000, g_ffn=0x1000,
+                  g_final=0x1000, embed=0x1000, lm_head=0x1000)
+    for gammas in ([16, 1], [34, 16], [0, 2]):           # a block length outside [2, 33]
+        with pytest.raises(B.DFlashError) as e:
+            B.draft_forward_ragged(_dims(), w, _cache(), 0x4000, None, gammas, 0x5000, 0x100000, 1 << 30)
+        assert e.value.status == B.ERR_INVALID_ARG
+    c = _cache(lens=(10, 40))
+    with pytest.raises(B.DFlashError) as e:              # only the second sequence overflows: 40 + 30 > 64
+        B.draft_forward_ragged(_dims(), w, c, 0x4000, None, [33, 30], 0x5000, 0x100000, 1 << 30)
+    assert e.value.status == B.ERR_CAPACITY and "sequence 1" in B.last_error()
+    assert list(c._keep) == [10, 40]
+    with pytest.raises(B.DFlashError) as e:              # workspace sized for a shorter block
+        small_ws = B.workspace_size(_dims(), 2, 4, 1)
+        B.draft_forward_ragged(_dims(), w, _cache(), 0x4000, None, [4, 20], 0x5000, 0x100000, small_ws)
+    assert e.value.status == B.ERR_WORKSPACE
+
+
+def test_ragged_argmax_accept_checks(lib):
+    W = B.Weights(lm_head=0x1000)
+    with pytest.raises(B.DFlashError) as e:
+        B.argmax_accept_ragged(_dims(), W, B.ARGMAX, 0x2000, [16, 1], 0x3000, None, None, None, None, None,
+                               0x100000, 1 << 30)
+    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.DFlashError) as e:              # ACCEPT needs target / tau / next
+        B.argmax_accept_ragged(_dims(), None, B.ACCEPT, None, [4, 8], 0x3000, None, 0x5000, 0x6000, None, None,
+                               0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+    with pytest.raises(B.DFlashError) as e:
+        B.argmax_accept_ragged(_dims(), W, B.ARGMAX, 0x2000, [4, 8], 0x3000, None, None, None, None, None, 0, 0)
+    assert e.value.status == B.ERR_WORKSPACE
+
+
+def test_workspace_covers_ragged_row_counts(lib):
+    # every total row count a ragged call can reach is covered by the size for
+    # its longest block (prime totals included)
+    d = _dims(D=1024, F=2048, Hq=8, Hkv=2, head_dim=128, V=5000, L=2)
+    big = B.workspace_size(d, 4, 16, 1)
+    assert big >= B.workspace_size(d, 4, 15, 1)
+    assert big >= B.workspace_size(d, 3, 16, 1)
