@@ -72,6 +72,7 @@ def main():
                     help="storage type of H_t and the KV cache")
     ap.add_argument("--temperature", type=float, default=1.0, help="temperature of the sampled-decoding leg")
     ap.add_argument("--no-sampling", action="store_true", help="skip the sampled-decoding leg")
+    ap.add_argument("--no-ragged", action="store_true", help="skip the per-sequence block-length leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the single-GPU path is "
@@ -294,6 +295,8 @@ def main():
     if not args.no_sampling:
         out["sampling"] = sampled_leg(args, cfg, inp, dr, cache, base_lens, tokens, h_final, draft, tau, nxt, app,
                                       H_app, make_events, hook, ms_per_step)
+    if not args.no_ragged and cfg.dtype == "bf16":
+        out["ragged"] = ragged_leg(cfg, dr)
 
     # A plain device copy of a known size: the reference that scales rocprofv3's
     # FETCH_SIZE / WRITE_SIZE counters into bytes (256 MiB read + 256 MiB written).
@@ -305,11 +308,14 @@ def main():
     del src, dst
 
     if not args.no_cpu_baseline:
-        greedy_cpu, sampled_cpu = cpu_baseline(cfg, inp, args.cpu_seconds,
-                                               None if args.no_sampling else args.temperature)
+        greedy_cpu, sampled_cpu, ragged_cpu = cpu_baseline(cfg, inp, args.cpu_seconds,
+                                                           None if args.no_sampling else args.temperature,
+                                                           "ragged" in out)
         out["cpu_baseline"] = greedy_cpu
         if sampled_cpu is not None:
             out["sampling"]["cpu_baseline"] = sampled_cpu
+        if ragged_cpu is not None:
+            out["ragged"]["cpu_baseline"] = ragged_cpu
     print(json.dumps(out), flush=True)
 
 
@@ -459,13 +465,99 @@ def sampled_leg(args, cfg, inp, dr, cache, base_lens, tokens, h_final, draft, ta
     }
 
 
-def cpu_baseline(cfg, inp, seconds, temperature=None):
+RAGGED_GAMMAS = [4, 8, 16, 32] * 4
+
+
+def ragged_leg(cfg, dr):
+    """Blocks with a length per sequence: 16 sequences with the batch16_ragged
+    context lengths (U[1024, 4096]) and block lengths 4/8/16/32, drafted in one
+    pass (draft forward + LM-head argmax), against the same batch padded to the
+    longest block (one uniform pass at gamma = 32)."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_drafter_ctx_amd import roofline as RF
+    from dflash_inputs import CONFIGS
+
+    dev = "cuda"
+    ctx = list(CONFIGS[4].ctx)
+    gs = RAGGED_GAMMAS
+    Bn, gmax, D, V = len(gs), max(gs), cfg.D, cfg.V
+    stream = torch.cuda.current_stream()
+    # seeded device-side context states (values do not change the timing)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261202)
+    N = sum(ctx)
+    cap = (max(ctx) + gmax + 31) // 32 * 32
+    cache = dr.cache(Bn, cap)
+    dr.ensure_workspace(Bn, gmax, N)
+    states = [torch.randn(N, D, generator=gen, device=dev).to(torch.bfloat16) for _ in range(cfg.n_tgt)]
+    H_t = dr.context_buffer(N)
+    dr.fuse(states, N, H_t)
+    dr.inject(H_t, ctx, cache)
+    del states, H_t
+    M, nd = sum(gs), sum(gs) - Bn
+    tok = torch.full((M,), cfg.mask_id, dtype=torch.int32, device=dev)
+    off = np.concatenate([[0], np.cumsum(gs)]).astype(int)
+    tok[torch.from_numpy(off[:-1]).to(dev)] = torch.arange(Bn, dtype=torch.int32, device=dev)
+    hf = torch.empty(M, D, dtype=torch.float32, device=dev)
+    dr_ = torch.empty(nd, dtype=torch.int32, device=dev)
+    tok_u = torch.full((Bn, gmax), cfg.mask_id, dtype=torch.int32, device=dev)
+    tok_u[:, 0] = torch.arange(Bn, dtype=torch.int32, device=dev)
+    hf_u = torch.empty(Bn, gmax, D, dtype=torch.float32, device=dev)
+    d_u = torch.empty(Bn, gmax - 1, dtype=torch.int32, device=dev)
+    from block_diffusion_drafter_ctx_amd import binding as B
+
+    def ragged():
+        dr.draft_ragged(cache, tok, None, gs, hf)
+        dr.argmax_accept_ragged(B.ARGMAX, hf, gs, dr_)
+
+    def padded():
+        dr.draft(cache, tok_u, None, gmax, hf_u)
+        dr.argmax_accept(B.ARGMAX, hf_u, Bn, gmax, d_u)
+
+    def timeit(fn, reps=20):
+        for _ in range(3):
+            fn()
+        ev = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+    rag_us = timeit(ragged)
+    pad_us = timeit(padded)
+    es = RF.elem_bytes(cfg.dtype)
+    cs = RF.elem_bytes(cfg.cache_dtype)
+    rb = RF.draft_forward_bytes_ragged(D, cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.F, V, gs, ctx, es, cs)
+    log(f"ragged: 16 sequences, blocks {sorted(set(gs))}: {rag_us:.1f} us vs {pad_us:.1f} us padded to {gmax}")
+    del cache
+    return {
+        "workload": (f"16 sequences, contexts U[1024, 4096] (batch16_ragged lengths, sum {N}), block lengths "
+                     f"4/8/16/32 ({M} block rows, {nd} drafts), {cfg.L} layers at the bench drafter's shape"),
+        "gammas": gs,
+        "draft_fwd_us": round(rag_us, 2),
+        "padded_to_32_us": round(pad_us, 2),
+        "speedup_vs_padded": round(pad_us / rag_us, 3),
+        "drafts_per_s": round(nd / (rag_us * 1e-6), 1),
+        "bytes": int(rb),
+        "GBps": round(rb / (rag_us * 1e-6) / 1e9, 1),
+        "hbm_frac": round(rb / (rag_us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4),
+    }
+
+
+def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False):
     """The CPU oracle, as it stands, on whole drafting iterations of the same
     workload (draft forward + LM-head argmax + accept + 16-row append), repeated
     for about ``seconds`` with the GPU loop's 8-iteration cache reset; then, when
     ``temperature`` is given, the sampled iteration (draft forward + sampled
     drafts + synthetic target logits + lossless verify + append) for about half
-    as long.  Returns (greedy, sampled or None)."""
+    as long; then, when ``ragged``, one ragged pass over a sample of the ragged
+    leg's batch.  Returns (greedy, sampled or None, ragged or None)."""
     import numpy as np
     from oracle import dflash_oracle as O
     from dflash_inputs import build_target_np
@@ -535,14 +627,39 @@ def cpu_baseline(cfg, inp, seconds, temperature=None):
               "seconds": round(dt, 2)}
     if temperature is None:
         return greedy, None
-    done, dt = run(True, seconds / 2)
-    log(f"cpu baseline (sampled): {done} iteration(s) in {dt:.1f}s")
-    sampled = {"value": round(cfg.B * done / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
-               "sample": f"{done} sampled drafting iterations at T = {temperature} (draft forward + sampled "
-                         f"drafts + synthetic target logits + lossless verify + 16-row append), float64 "
-                         f"numpy oracle",
-               "seconds": round(dt, 2)}
-    return greedy, sampled
+    sampled = None
+    if temperature is not None:
+        done, dt = run(True, seconds / 2)
+        log(f"cpu baseline (sampled): {done} iteration(s) in {dt:.1f}s")
+        sampled = {"value": round(cfg.B * done / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+                   "sample": f"{done} sampled drafting iterations at T = {temperature} (draft forward + sampled "
+                             f"drafts + synthetic target logits + lossless verify + 16-row append), float64 "
+                             f"numpy oracle",
+                   "seconds": round(dt, 2)}
+    if not ragged:
+        return greedy, sampled, None
+    # the first four sequences of the ragged leg (blocks 4, 8, 16, 32) over
+    # seeded random context K/V of their batch16_ragged lengths (stand-ins for
+    # an untimed ingest), one ragged pass + argmax
+    from dflash_inputs import CONFIGS
+    rng = np.random.default_rng(20261202)
+    gs = RAGGED_GAMMAS[:4]
+    ctx = list(CONFIGS[4].ctx[:4])
+    rc = O.OracleCache(cfg.L, len(gs), cfg.Hkv, cfg.d)
+    for l in range(cfg.L):
+        for b, n in enumerate(ctx):
+            rc.append(l, b, rng.normal(0, 1, (n, cfg.Hkv, cfg.d)), rng.normal(0, 1, (n, cfg.Hkv, cfg.d)))
+    toks = [np.array([b] + [cfg.mask_id] * (g - 1)) for b, g in enumerate(gs)]
+    t0 = time.perf_counter()
+    hf, _ = O.draft_forward_ragged(cfg, layers, gf, rc, gs, embed=E, tokens=toks, storage=cfg.cache_dtype)
+    O.lm_head_argmax_ragged(hf, E)
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline (ragged): 4 blocks in {dt:.1f}s")
+    rag = {"value": round(len(gs) / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"one ragged pass + LM-head argmax over 4 sequences (blocks {gs}, contexts {ctx}, random "
+                     f"context K/V), float64 numpy oracle",
+           "drafts_per_s": round(sum(g - 1 for g in gs) / dt, 3), "seconds": round(dt, 2)}
+    return greedy, sampled, rag
 
 
 if __name__ == "__main__":

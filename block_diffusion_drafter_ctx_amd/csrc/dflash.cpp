@@ -192,18 +192,62 @@ size_t inject_ws(const dflash_dims* d, int max_rows) {
   return best || planes ? align_up(best * 4) + planes : 0;
 }
 
+// An fp32-activation product against a bf16 weight.  When the tiled GEMM
+// takes it (many rows), the activations are split once into bf16 hi / lo
+// planes for the LDS-direct kernel; otherwise they are split on the fly.
+struct ActPlan {
+  GemmPlan p;
+  GemmAKind kind;
+};
+
+ActPlan plan_act(int M, int N, int K, bool wide) {
+  const GemmPlan p = plan_gemm(M, N, K, A_F32_SPLIT, wide);
+  if (!p.tiled) return ActPlan{p, A_F32_SPLIT};
+  return ActPlan{plan_gemm(M, N, K, A_BF16_HILO, wide), A_BF16_HILO};
+}
+
+size_t act_planes_bytes(const ActPlan& a, int M, int K) {
+  return a.kind == A_BF16_HILO ? 2 * align_up(static_cast<size_t>(M) * K * 2) : 0;
+}
+
+// g addresses fp32 activations (any row mapping of one source); planes:
+// act_planes_bytes of scratch.
+hipError_t launch_act_gemm(GemmArgs g, const ActPlan& a, void* planes, hipStream_t s) {
+  if (a.kind == A_BF16_HILO) {
+    uint16_t* hi = static_cast<uint16_t*>(planes);
+    uint16_t* lo = reinterpret_cast<uint16_t*>(static_cast<char*>(planes) +
+                                               align_up(static_cast<size_t>(g.M) * g.K * 2));
+    const hipError_t e = launch_split_hilo(static_cast<const float*>(g.a_src[0]), g.a_ld, g.M, g.K, hi, lo, s,
+                                           g.a_rg, g.a_gs);
+    if (e != hipSuccess) return e;
+    for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = hi;
+    g.a_lo = lo;
+    g.a_cols = g.K;
+    g.a_ld = g.K;
+    g.a_rg = INT_MAX;
+    g.a_gs = 0;
+  }
+  return launch_gemm_mfma(g, a.kind, a.p, s);
+}
+
 struct DraftWs {
-  size_t h, a, q, o, s, part, att_o, att_ml, total;
+  size_t h, a, q, o, s, part, att_o, att_ml, planes, total;
 };
 
 // M block rows in all (sum of the block lengths), the longest block gmax rows.
 DraftWs draft_ws(const dflash_dims* d, int B, int M, int gmax) {
   const int hd = d->Hq * d->head_dim;
   const int nqkv = (d->Hq + 2 * d->Hkv) * d->head_dim;
-  size_t part = 0;
+  size_t part = 0, planes = 0;
   auto upd = [&](int N, int K) {
-    const size_t f = gemm_part_floats(d, M, N, K, A_F32_SPLIT);
-    if (f > part) part = f;
+    if (d->dtype == DFLASH_F32) {
+      part = static_cast<size_t>(M) * N > part ? static_cast<size_t>(M) * N : part;
+      return;
+    }
+    const ActPlan ap = plan_act(M, N, K, false);
+    part = ap.p.part_floats > part ? ap.p.part_floats : part;
+    const size_t pl = act_planes_bytes(ap, M, K);
+    planes = pl > planes ? pl : planes;
   };
   upd(nqkv, d->D);
   upd(d->D, hd);
@@ -222,13 +266,14 @@ DraftWs draft_ws(const dflash_dims* d, int B, int M, int gmax) {
   w.part = c.take(part * 4);
   w.att_o = c.take(rpad_rows * d->head_dim * 4);
   w.att_ml = c.take(rpad_rows * 2 * 4);
+  w.planes = c.take(planes);
   w.total = c.off;
   return w;
 }
 
 // LM head: split-K partials [S][M][V], then per-128-column top-2 [ceil(V/128)][M][3]
 struct ArgmaxWs {
-  size_t part, top2, rows, total;
+  size_t part, top2, rows, planes, total;
 };
 
 // M mask rows (logits rows); `gathered` adds room for them as a dense [M][D]
@@ -240,10 +285,12 @@ ArgmaxWs argmax_ws(const dflash_dims* d, int M, bool gathered = false) {
   if (d->dtype == DFLASH_F32) {
     w.part = c.take(static_cast<size_t>(M) * d->V * 4);
   } else {
-    size_t pf = gemm_part_floats(d, M, d->V, d->D, A_F32_SPLIT, true);
+    const ActPlan ap = plan_act(M, d->V, d->D, true);
+    size_t pf = ap.p.part_floats;
     const size_t pf_stream = plan_gemm_mfma(M, d->V, d->D, A_F32_SPLIT, true).part_floats;
     if (pf_stream > pf) pf = pf_stream;
     w.part = c.take(pf * 4);
+    w.planes = c.take(act_planes_bytes(ap, M, d->D));
     // top-2 candidates: one row per 512-column tile, or per register-K workgroup
     size_t t2 = static_cast<size_t>((d->V + 511) / 512);
     if (t2 < static_cast<size_t>(kRkMaxGrid)) t2 = kRkMaxGrid;
@@ -257,7 +304,7 @@ ArgmaxWs argmax_ws(const dflash_dims* d, int M, bool gathered = false) {
 // weights with more than 16 rows) and the per-row sampling statistics
 // [pieces][M] (one piece per register-K workgroup or per column chunk).
 struct SampleWs {
-  size_t part, stats, total;
+  size_t part, stats, planes, total;
 };
 
 SampleWs sample_ws(const dflash_dims* d, int B, int gamma) {
@@ -272,7 +319,9 @@ SampleWs sample_ws(const dflash_dims* d, int B, int gamma) {
     if (rk.rk) {
       if (static_cast<size_t>(rk.grid) > pieces) pieces = rk.grid;
     } else {
-      w.part = c.take(plan_gemm(M, d->V, d->D, A_F32_SPLIT, true).part_floats * 4);
+      const ActPlan ap = plan_act(M, d->V, d->D, true);
+      w.part = c.take(ap.p.part_floats * 4);
+      w.planes = c.take(act_planes_bytes(ap, M, d->D));
     }
   }
   w.stats = c.take(pieces * M * sizeof(float4));
@@ -616,10 +665,10 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
       *S = 1;
       return launch_gemm_f32(g, s);
     }
-    const GemmPlan p = plan_gemm(M, N, K, A_F32_SPLIT, false);
-    *S = p.S;
+    const ActPlan ap = plan_act(M, N, K, false);
+    *S = ap.p.S;
     const int ps = prof_begin(role, s);
-    const hipError_t e = launch_gemm_mfma(g, A_F32_SPLIT, p, s);
+    const hipError_t e = launch_act_gemm(g, ap, base + lay.planes, s);
     prof_end(ps, s);
     return e;
   };
@@ -754,12 +803,12 @@ static dflash_status lm_head_argmax(const dflash_dims* dims, const dflash_weight
       prof_end(ps, s);
       DF_HIP(launch_argmax_final(top2, rk.grid, Mr, draft, top2_gap, s));
     } else {
-      const GemmPlan p = plan_gemm(Mr, dims->V, D, A_F32_SPLIT, true);
+      const ActPlan ap = plan_act(Mr, dims->V, D, true);
       const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-      DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, s));
+      DF_HIP(launch_act_gemm(g, ap, base + lay.planes, s));
       prof_end(ps, s);
       int nt = 0;
-      DF_HIP(launch_reduce_top2(g.part, p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
+      DF_HIP(launch_reduce_top2(g.part, ap.p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
       DF_HIP(launch_argmax_final(top2, nt, Mr, draft, top2_gap, s));
     }
   } else {
@@ -934,13 +983,13 @@ dflash_status dflash_sample_drafts(const dflash_dims* dims, const dflash_weights
       DF_HIP(launch_sample_final(stats, rk.grid, Mr, draft, lse, s));
       return ok();
     }
-    const GemmPlan p = plan_gemm(Mr, V, D, A_F32_SPLIT, true);
+    const ActPlan ap = plan_act(Mr, V, D, true);
     g.part = reinterpret_cast<float*>(base + lay.part);
     const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-    DF_HIP(launch_gemm_mfma(g, A_F32_SPLIT, p, s));
+    DF_HIP(launch_act_gemm(g, ap, base + lay.planes, s));
     prof_end(ps, s);
     r.src = g.part;
-    r.S = p.S;
+    r.S = ap.p.S;
     r.split_stride = static_cast<int64_t>(Mr) * V;
     r.logits_out = logits;
   } else {

@@ -785,12 +785,12 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kern
   }
 }
 
-__global__ __launch_bounds__(256) void split_hilo_kernel(const float* x, int64_t ld, int M, int K, uint16_t* hi,
-                                                          uint16_t* lo) {
+__global__ __launch_bounds__(256) void split_hilo_kernel(const float* x, int64_t ld, int rg, int64_t gs, int M,
+                                                          int K, uint16_t* hi, uint16_t* lo) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
   if (i >= static_cast<int64_t>(M) * K) return;
   const int m = static_cast<int>(i / K), k = static_cast<int>(i % K);   // K % 8 == 0
-  const float* p = x + m * ld + k;
+  const float* p = x + (m / rg) * gs + (m % rg) * ld + k;
   const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
   const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint4 h, l;
@@ -1219,12 +1219,13 @@ hipError_t launch_gemm_rk_swiglu(const GemmArgs& a0, const GemmPlan& p, float* s
   return rk_launch<4, RK_SWIGLU, 1>(a, p, nullptr, nullptr, st);
 }
 
-hipError_t launch_split_hilo(const float* x, int64_t ld, int M, int K, uint16_t* hi, uint16_t* lo, hipStream_t st) {
-  if (K % 8 != 0 || ld % 4 != 0) return hipErrorInvalidValue;
+hipError_t launch_split_hilo(const float* x, int64_t ld, int M, int K, uint16_t* hi, uint16_t* lo, hipStream_t st,
+                             int rg, int64_t gs) {
+  if (K % 8 != 0 || ld % 4 != 0 || gs % 4 != 0 || rg < 1) return hipErrorInvalidValue;
   const int64_t groups = static_cast<int64_t>(M) * K / 8;
   if (groups == 0) return hipSuccess;
-  hipLaunchKernelGGL(split_hilo_kernel, dim3(static_cast<unsigned>((groups + 255) / 256)), dim3(256), 0, st, x, ld, M, K,
-                     hi, lo);
+  hipLaunchKernelGGL(split_hilo_kernel, dim3(static_cast<unsigned>((groups + 255) / 256)), dim3(256), 0, st, x, ld, rg,
+                     gs, M, K, hi, lo);
   return hipGetLastError();
 }
 

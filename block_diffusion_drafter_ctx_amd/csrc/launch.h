@@ -89,8 +89,10 @@ hipError_t launch_reduce_top2(const float* part, int S, int M, int N, float* log
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st);
 
 // hi[m][k] = bf16(x[m][k]), lo[m][k] = bf16(x - hi) for an fp32 [M][K] matrix
-// with row stride ld (elements); hi and lo are dense [M][K].
-hipError_t launch_split_hilo(const float* x, int64_t ld, int M, int K, uint16_t* hi, uint16_t* lo, hipStream_t st);
+// whose row m starts at x + (m / rg) * gs + (m % rg) * ld (elements; rg = INT_MAX
+// for plain rows of stride ld); hi and lo are dense [M][K].
+hipError_t launch_split_hilo(const float* x, int64_t ld, int M, int K, uint16_t* hi, uint16_t* lo, hipStream_t st,
+                             int rg = 0x7fffffff, int64_t gs = 0);
 
 // ------------------------------------------------------------ epilogues
 // Per-sequence row table: rows [row_off[b], row_off[b+1]) of a GEMM output belong

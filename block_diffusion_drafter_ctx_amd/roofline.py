@@ -79,6 +79,16 @@ def draft_forward_bytes(D, L, Hq, Hkv, d, F, V, B, gamma, ctx_lens, es=2, cs=Non
     return (w + lm) * es + kv * cs + act
 
 
+def draft_forward_bytes_ragged(D, L, Hq, Hkv, d, F, V, gammas, ctx_lens, es=2, cs=None) -> int:
+    """``draft_forward_bytes`` for blocks of gammas[b] rows: each sequence's
+    context + block K/V once per layer, the weights and the LM head once."""
+    cs = es if cs is None else cs
+    w = L * layer_weight_elems(D, Hq, Hkv, d, F) + D
+    kv = L * sum(n + g for n, g in zip(ctx_lens, gammas)) * 2 * Hkv * d
+    act = sum(gammas) * D * 4 * 2
+    return (w + V * D) * es + kv * cs + act
+
+
 def draft_forward_flops(D, L, Hq, Hkv, d, F, V, B, gamma, ctx_lens) -> int:
     M = B * gamma
     proj = 2 * M * L * ((Hq + 2 * Hkv) * d * D + D * Hq * d + 2 * F * D + D * F)
