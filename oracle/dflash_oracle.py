@@ -132,9 +132,13 @@ class OracleCache:
 
     def sequence(self, b: int) -> "OracleCache":
         """A one-sequence cache holding sequence b's rows (shared, not copied)."""
+        return self.prefix(b, self.k[0][b].shape[0])
+
+    def prefix(self, b: int, n: int) -> "OracleCache":
+        """A one-sequence cache holding the first n rows of sequence b."""
         one = OracleCache.__new__(OracleCache)
-        one.k = [[self.k[l][b]] for l in range(len(self.k))]
-        one.v = [[self.v[l][b]] for l in range(len(self.v))]
+        one.k = [[self.k[l][b][:n]] for l in range(len(self.k))]
+        one.v = [[self.v[l][b][:n]] for l in range(len(self.v))]
         return one
 
 
@@ -237,6 +241,34 @@ def draft_forward_ragged(dims, layers, g_final, cache: OracleCache, gammas, embe
         outs.append(hf[0])
         kvs.append([(k[0], v[0]) for k, v in kv])
     return outs, kvs
+
+
+def draft_forward_blocks(dims, layers, g_final, cache: OracleCache, blocks, gamma: int, embed=None, tokens=None,
+                         override=None, storage: str = "bf16"):
+    """The drafter over many anchored blocks at once, as in training.
+
+    [JP] "학습 방법" (sparse attention mask): the blocks, each anchored at a
+    sampled position of a sequence, are processed together; a block's rows
+    attend to each other in both directions and to their sequence's injected
+    context features, and never to another block ([MG] describes a causal
+    mask across blocks instead; the reading here follows [JP]).  A block
+    anchored at position a sees the context features of positions [0, a): the
+    anchor is the block's first row, as at inference, where it is the token
+    right after the verified context.  Each block is therefore the one-sequence
+    pass of ``draft_forward`` over that context prefix.
+    blocks: list of (sequence index, anchor position a), a <= the sequence's
+    cache length.  tokens: [nblk, gamma] ids (or override: [nblk, gamma, D]).
+    Returns (h_final [nblk, gamma, D], per block the per-layer block K/V).
+    """
+    outs, kvs = [], []
+    for k, (sq, a) in enumerate(blocks):
+        tok = None if tokens is None else np.asarray(tokens[k])[None]
+        ov = None if override is None else np.asarray(override[k])[None]
+        hf, kv = draft_forward(dims, layers, g_final, cache.prefix(int(sq), int(a)), gamma, embed=embed,
+                               tokens=tok, override=ov, storage=storage)
+        outs.append(hf[0])
+        kvs.append([(kk[0], vv[0]) for kk, vv in kv])
+    return np.stack(outs), kvs
 
 
 # ---------------------------------------------------------------------------

@@ -531,6 +531,62 @@ def pin_ragged_argmax_accept(o):
 
 
 # ---------------------------------------------------------------------------
+# anchored blocks (the training-style forward)
+# ---------------------------------------------------------------------------
+def pin_blocks_match_torch_on_prefix(o):
+    # Each block against the torch composition of the layers over its own
+    # sequence's context rows [0, anchor) and its own rows only.
+    rng = _rng(50)
+    dm = dims()
+    L, g = 2, 4
+    layers = rand_layers(rng, dm, L)
+    gf = 1 + rng.normal(0, 0.2, dm.D)
+    cache = cache_with(o, L, 2, dm.Hkv, dm.d, [9, 6], rng)
+    blocks = [(0, 0), (0, 4), (1, 6), (0, 9)]
+    h0 = rng.normal(0, 1, (len(blocks), g, dm.D))
+    got, kv = o.draft_forward_blocks(dm, layers, gf, cache, blocks, g, override=h0, storage="f32")
+    assert got.shape == (4, g, dm.D) and len(kv) == 4
+    for k, (sq, a) in enumerate(blocks):
+        ref = _torch_layer_forward(dm, layers, gf, [cache.k[l][sq][:a] for l in range(L)],
+                                   [cache.v[l][sq][:a] for l in range(L)], h0[k])
+        assert np.allclose(got[k], ref, rtol=1e-9, atol=1e-9), k
+
+
+def pin_blocks_visibility(o):
+    # A block anchored at a: context rows before a change it, rows at or after a
+    # do not, nor does any other block's input; anchoring at the full length is
+    # the inference pass.
+    rng = _rng(51)
+    dm = dims()
+    L, g = 2, 3
+    layers = rand_layers(rng, dm, L)
+    gf = 1 + rng.normal(0, 0.2, dm.D)
+    cache = cache_with(o, L, 1, dm.Hkv, dm.d, [8], rng)
+    blocks = [(0, 5), (0, 2)]
+    h0 = rng.normal(0, 1, (2, g, dm.D))
+    base, _ = o.draft_forward_blocks(dm, layers, gf, cache, blocks, g, override=h0, storage="f32")
+    for row, changes in ((4, True), (0, True), (5, False), (7, False)):
+        c2 = cache_with(o, L, 1, dm.Hkv, dm.d, [0], rng)
+        for l in range(L):
+            k = cache.k[l][0].copy()
+            v = cache.v[l][0].copy()
+            k[row] += 0.5
+            v[row] -= 0.5
+            c2.append(l, 0, k, v)
+        got, _ = o.draft_forward_blocks(dm, layers, gf, c2, blocks, g, override=h0, storage="f32")
+        assert (not np.allclose(got[0], base[0])) == changes, row
+        assert np.all(np.any(np.abs(got[0] - base[0]) > 1e-12, axis=1)) == changes
+        assert np.array_equal(got[1], base[1]) == (row >= 2)
+    h1 = h0.copy()
+    h1[1] += 1.0
+    got, _ = o.draft_forward_blocks(dm, layers, gf, cache, blocks, g, override=h1, storage="f32")
+    assert np.array_equal(got[0], base[0])
+    full, _ = o.draft_forward_blocks(dm, layers, gf, cache, [(0, 8)], g, override=h0[:1], storage="f32")
+    inf, _ = o.draft_forward(dm, layers, gf, cache, g, override=h0[:1], storage="f32")
+    assert np.array_equal(full, inf)
+
+
+# ---------------------------------------------------------------------------
 # sampled drafting / lossless verification
 # ---------------------------------------------------------------------------
 def _softmax(x, T=1.0):

@@ -85,6 +85,12 @@ MUTANTS = [
      "hf, kv = draft_forward(dims, layers, g_final, cache.sequence(b), int(gammas[0]),"),
     ("ragged_accept_shifted_targets", "res = [accept(np.asarray(d)[None], np.asarray(t)[None]) for d, t in zip(drafts, targets)]",
      "res = [accept(np.asarray(d)[None], np.asarray(t)[None][:, ::-1]) for d, t in zip(drafts, targets)]"),
+    ("blocks_see_anchor_feature", "cache.prefix(int(sq), int(a)), gamma, embed=embed,",
+     "cache.prefix(int(sq), int(a) + 1), gamma, embed=embed,"),
+    ("blocks_see_whole_context", "cache.prefix(int(sq), int(a)), gamma, embed=embed,",
+     "cache.sequence(int(sq)), gamma, embed=embed,"),
+    ("blocks_wrong_sequence", "cache.prefix(int(sq), int(a)), gamma, embed=embed,",
+     "cache.prefix(0, int(a)), gamma, embed=embed,"),
     ("sample_counts_all_accepts", "while m < n and accepted[b, m]:\n            m += 1",
      "m = int(np.sum(accepted[b]))"),
 ]
