@@ -19,7 +19,8 @@ ARGMAX, ACCEPT = 1, 2
 MAX_BATCH, MAX_TGT_LAYERS, MIN_GAMMA, MAX_GAMMA = 64, 8, 2, 33
 
 EXPORTED = ("dflash_version", "dflash_last_error", "dflash_workspace_size", "dflash_fuse_context",
-            "dflash_inject_kv", "dflash_draft_forward", "dflash_draft_forward_ragged", "dflash_argmax_accept",
+            "dflash_inject_kv", "dflash_draft_forward", "dflash_draft_forward_ragged",
+            "dflash_draft_forward_blocks", "dflash_argmax_accept",
             "dflash_argmax_accept_ragged", "dflash_sample_drafts",
             "dflash_sample_accept", "dflash_profile_events")
 (PROF_NONE, PROF_LM_HEAD, PROF_QKV, PROF_O, PROF_GATEUP, PROF_DOWN, PROF_FUSE, PROF_INJECT, PROF_ATTENTION,
@@ -82,6 +83,10 @@ def load():
     lib.dflash_draft_forward_ragged.restype = c_int32
     lib.dflash_draft_forward_ragged.argtypes = [POINTER(Dims), POINTER(Weights), POINTER(KVCache), c_void_p,
                                                 c_void_p, POINTER(c_int32), c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dflash_draft_forward_blocks.restype = c_int32
+    lib.dflash_draft_forward_blocks.argtypes = [POINTER(Dims), POINTER(Weights), POINTER(KVCache), POINTER(c_int32),
+                                                POINTER(c_int32), c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                                c_void_p, c_size_t, c_void_p]
     lib.dflash_argmax_accept_ragged.restype = c_int32
     lib.dflash_argmax_accept_ragged.argtypes = [POINTER(Dims), POINTER(Weights), c_uint32, c_void_p, c_int32,
                                                 POINTER(c_int32), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -157,6 +162,14 @@ def draft_forward_ragged(dims: Dims, w: Weights, cache: KVCache, block_tokens, e
     _check(load().dflash_draft_forward_ragged(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(cache),
                                               _p(block_tokens), _p(embed_override), _gammas(gammas), _p(h_final),
                                               _p(ws), ws_bytes, _p(stream)))
+
+
+def draft_forward_blocks(dims: Dims, w: Weights, cache: KVCache, block_seq, anchors, gamma: int, block_tokens,
+                         embed_override, h_final, ws, ws_bytes: int, stream=0):
+    n = len(anchors)
+    _check(load().dflash_draft_forward_blocks(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(cache),
+                                              _gammas(block_seq), _gammas(anchors), n, gamma, _p(block_tokens),
+                                              _p(embed_override), _p(h_final), _p(ws), ws_bytes, _p(stream)))
 
 
 def argmax_accept_ragged(dims: Dims, w: Weights, flags: int, h_final, gammas, draft, target, tau, next_anchor,

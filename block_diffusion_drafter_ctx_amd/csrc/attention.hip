@@ -43,6 +43,19 @@ __device__ __forceinline__ int row_seq(const AttnArgs& a, int m) {
   return b;
 }
 
+// Key rows [kbeg, kend) of item (b, sp) in the cache of sequence kvseq[b]: a
+// range of the context rows [0, nkeys[b]), or, for the last item of a block
+// whose own rows are stored apart (blk0[b] >= 0), those gam[b] rows.
+__device__ __forceinline__ void item_keys(const AttnArgs& a, int b, int sp, int& kbeg, int& kend) {
+  if (a.blk0[b] >= 0 && sp == a.nsplit[b] - 1) {
+    kbeg = a.blk0[b];
+    kend = kbeg + a.gam[b];
+  } else {
+    kbeg = sp * a.split_keys;
+    kend = min(a.nkeys[b], kbeg + a.split_keys);
+  }
+}
+
 __device__ __forceinline__ void decode_item(const AttnArgs& a, int item, int& b, int& j, int& sp) {
   b = 0;
   while (b + 1 < a.B && item >= a.item_off[b + 1]) ++b;
@@ -114,16 +127,15 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
   const int item = blockIdx.x;
   int b, j, sp;
   decode_item(a, item, b, j, sp);
-  const int nk = a.nkeys[b];
-  const int kbeg = sp * a.split_keys;
-  const int kend = min(nk, kbeg + a.split_keys);
+  int kbeg, kend;
+  item_keys(a, b, sp, kbeg, kend);
   const int r = blockIdx.y * kRowsPerGroup + wave * 16 + (lane & 15);
   const int G = a.Hq / a.Hkv;
   const int gb = a.gam[b], Rb = G * gb;       // this sequence's block rows and query rows
   const bool computes = blockIdx.y * kRowsPerGroup + wave * 16 < Rb;   // uniform per wave
 
   uint4 qh[DS], ql[DS];                       // query fragments, loaded after the first key blocks
-  const int64_t head = static_cast<int64_t>(b) * a.Hkv + j;
+  const int64_t head = static_cast<int64_t>(a.kvseq[b]) * a.Hkv + j;
   const TKV* kbase = static_cast<const TKV*>(a.kc) + head * a.cap * HD;
   const TKV* vbase = static_cast<const TKV*>(a.vc) + head * HD * a.cap;
 
@@ -318,8 +330,8 @@ __global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
   const int grp = wave / WPG, wq = wave % WPG;
   int b, j, sp;
   decode_item(a, blockIdx.x, b, j, sp);
-  const int kbeg = sp * a.split_keys;
-  const int kend = min(a.nkeys[b], kbeg + a.split_keys);
+  int kbeg, kend;
+  item_keys(a, b, sp, kbeg, kend);
   const int nblk = (kend - kbeg + 31) / 32;     // >= 1: every key range is non-empty
   const int nstep = (nblk + NG - 1) / NG;
   const int row0 = blockIdx.y * 16 * WPG + wq * 16;
@@ -327,7 +339,7 @@ __global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
   const int G = a.Hq / a.Hkv;
   const int gb = a.gam[b], Rb = G * gb;         // this sequence's block rows and query rows
   const bool computes = row0 < Rb;              // uniform per wave
-  const int64_t head = static_cast<int64_t>(b) * a.Hkv + j;
+  const int64_t head = static_cast<int64_t>(a.kvseq[b]) * a.Hkv + j;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.kc) + head * a.cap * HD;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.vc) + head * HD * a.cap;
   const unsigned lds0 = lds_addr(stage);
@@ -574,11 +586,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const float* qp = a.q + (static_cast<int64_t>(m) * a.Hq + h) * a.d;
   const float q0 = lane < a.d ? qp[lane] * a.scale_log2 : 0.f;
   const float q1 = lane + 64 < a.d ? qp[lane + 64] * a.scale_log2 : 0.f;
-  const int64_t head = static_cast<int64_t>(b) * a.Hkv + j;
+  const int64_t head = static_cast<int64_t>(a.kvseq[b]) * a.Hkv + j;
   const float* kb = static_cast<const float*>(a.kc) + head * a.cap * a.d;
   const float* vb = static_cast<const float*>(a.vc) + head * a.d * a.cap;
   float m_run = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int t = 0; t < a.nkeys[b]; ++t) {
+  const int nctx = a.nkeys[b], nall = nctx + (a.blk0[b] >= 0 ? a.gam[b] : 0);
+  for (int tt = 0; tt < nall; ++tt) {
+    const int t = tt < nctx ? tt : a.blk0[b] + (tt - nctx);   // the block's own rows when stored apart
     const float* kp = kb + static_cast<int64_t>(t) * a.d;
     float part = lane < a.d ? q0 * kp[lane] : 0.f;
     if (lane + 64 < a.d) part += q1 * kp[lane + 64];
@@ -623,7 +637,7 @@ static int attn_item_target() {
   return t < kAttnItemMax ? t : kAttnItemMax;
 }
 
-AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d) {
+AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d, const int32_t* apart) {
   AttnPlan p;
   int64_t total = 0;
   for (int b = 0; b < B; ++b) total += nkeys[b];
@@ -634,12 +648,14 @@ AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d) {
   if (sk < min_keys) sk = ((min_keys + 31) / 32) * 32;
   int maxk = 0;
   for (int b = 0; b < B; ++b) maxk = nkeys[b] > maxk ? nkeys[b] : maxk;
-  const int64_t sk_min = ((maxk + kMaxSplitsLds - 1) / kMaxSplitsLds + 31) / 32 * 32;   // combine's LDS table
+  // the combine's LDS table holds kMaxSplitsLds splits: at most kMaxSplitsLds - 1
+  // context ranges, leaving room for a block stored apart
+  const int64_t sk_min = ((maxk + kMaxSplitsLds - 2) / (kMaxSplitsLds - 1) + 31) / 32 * 32;
   if (sk < sk_min) sk = sk_min;
   p.split_keys = static_cast<int>(sk);
   p.item_off[0] = 0;
   for (int b = 0; b < B; ++b) {
-    p.nsplit[b] = static_cast<int>((nkeys[b] + sk - 1) / sk);
+    p.nsplit[b] = static_cast<int>((nkeys[b] + sk - 1) / sk) + (apart != nullptr && apart[b] ? 1 : 0);
     p.item_off[b + 1] = p.item_off[b] + Hkv * p.nsplit[b];
   }
   p.items = p.item_off[B];
@@ -653,7 +669,9 @@ AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d) {
 size_t attention_part_bound(int B, int Hkv, int R, int d) {
   const int row_groups = (R + kRowsPerGroup - 1) / kRowsPerGroup;
   const int rpad = R > kRowsPerGroup ? row_groups * kRowsPerGroup : waves_per_group(R) * 16;
-  const size_t items = static_cast<size_t>(kAttnItemMax) + static_cast<size_t>(B) * Hkv;
+  // rounding up every (sequence, head)'s split count, plus one item per
+  // (sequence, head) for a block stored apart
+  const size_t items = static_cast<size_t>(kAttnItemMax) + 2 * static_cast<size_t>(B) * Hkv;
   return items * rpad * (d + 2);
 }
 

@@ -583,6 +583,7 @@ dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w,
       const int lo = row_off[b] - r0, hi = row_off[b + 1] - r0;
       sa.rows.row_off[b] = lo < 0 ? 0 : (lo > M ? M : lo);
       sa.rows.pos0[b] = cache->len[b] + (r0 > row_off[b] ? r0 - row_off[b] : 0);
+      sa.rows.seq[b] = b;
       (void)hi;
     }
     sa.rows.row_off[cache->B] = M;
@@ -592,28 +593,32 @@ dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w,
   return ok();
 }
 
-// The drafting pass over blocks of gammas[b] rows (host array), packed row
-// after row: sequence b's block rows start at the sum of the earlier lengths.
+// Query groups of a drafting pass (validated by the caller).  Group b has
+// gam[b] block rows (packed row after row), reads the K/V of cache sequence
+// kvseq[b], sees that sequence's context rows [0, nctx[b]) and its own rows,
+// and writes its own K/V to cache rows [pos0[b], pos0[b] + gam[b]).  At
+// inference pos0 = nctx = len: the block follows the context.  Anchored blocks
+// (apart) keep their rows in a scratch region past the context, read as a key
+// item of their own.
+struct QueryGroups {
+  int n = 0;
+  bool apart = false;
+  int32_t gam[kMaxSeq], kvseq[kMaxSeq], nctx[kMaxSeq], pos0[kMaxSeq];
+};
+
 static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_weights* w,
                                         const dflash_kv_cache* cache, const int32_t* block_tokens,
-                                        const float* embed_override, const int32_t* gammas, float* h_final,
+                                        const float* embed_override, const QueryGroups& qg, float* h_final,
                                         void* ws, size_t ws_bytes, void* stream) {
-  dflash_status st = check_dims(dims);
-  if (st != DFLASH_OK) return st;
-  DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
-  if ((st = check_cache(cache)) != DFLASH_OK) return st;
-  DF_REQUIRE(gammas != nullptr, DFLASH_ERR_INVALID_ARG, "gammas is NULL");
+  dflash_status st = DFLASH_OK;
   int M = 0, gmax = 0;
   int32_t qrow0[kMaxSeq + 1];
-  for (int b = 0; b < cache->B; ++b) {
-    if ((st = check_gamma(gammas[b])) != DFLASH_OK) return st;
-    DF_REQUIRE(static_cast<int64_t>(cache->len[b]) + gammas[b] <= cache->cap, DFLASH_ERR_CAPACITY,
-               "sequence %d: len %d + gamma %d exceeds cap %d", b, cache->len[b], gammas[b], cache->cap);
+  for (int b = 0; b < qg.n; ++b) {
     qrow0[b] = M;
-    M += gammas[b];
-    gmax = gammas[b] > gmax ? gammas[b] : gmax;
+    M += qg.gam[b];
+    gmax = qg.gam[b] > gmax ? qg.gam[b] : gmax;
   }
-  qrow0[cache->B] = M;
+  qrow0[qg.n] = M;
   const char* names[] = {"w_qkv", "w_o", "w_gateup", "w_down", "g_attn", "g_ffn", "g_final"};
   const void* ptrs[] = {w->w_qkv, w->w_o, w->w_gateup, w->w_down, w->g_attn, w->g_ffn, w->g_final};
   for (int i = 0; i < 7; ++i)
@@ -625,7 +630,7 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
     DF_REQUIRE(block_tokens != nullptr, DFLASH_ERR_INVALID_ARG, "block_tokens is NULL (and no embed_override)");
   }
   if ((st = check_ptr(h_final, "h_final")) != DFLASH_OK) return st;
-  const int B = cache->B;
+  const int B = qg.n;   // query groups (sequences, or anchored blocks)
   const DraftWs lay = draft_ws(dims, B, M, gmax);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != DFLASH_OK) return st;
   if ((st = check_device()) != DFLASH_OK) return st;
@@ -673,11 +678,15 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
     return e;
   };
 
-  int32_t nkeys[kMaxSeq];
-  for (int b = 0; b < B; ++b) nkeys[b] = cache->len[b] + gammas[b];
+  int32_t nkeys[kMaxSeq], apart[kMaxSeq];
+  for (int b = 0; b < B; ++b) {
+    nkeys[b] = qg.apart ? qg.nctx[b] : qg.nctx[b] + qg.gam[b];
+    apart[b] = qg.apart ? 1 : 0;
+  }
   const int R = (Hq / Hkv) * gmax;
-  const AttnPlan ap = bf ? plan_attention(B, nkeys, Hkv, R, d) : AttnPlan{};
-  const size_t layer_elems = static_cast<size_t>(B) * Hkv * cache->cap * d;
+  const AttnPlan ap = bf ? plan_attention(B, nkeys, Hkv, R, d, apart) : AttnPlan{};
+  // one layer of the cache holds all cache->B sequences (B counts query groups)
+  const size_t layer_elems = static_cast<size_t>(cache->B) * Hkv * cache->cap * d;
 
   const GemmPlan swiglu_rk = bf ? plan_gemm_rk_swiglu(M, F, D) : GemmPlan{};
   DF_HIP(launch_embed_norm(block_tokens, embed_override, w->embed, dims->V, M, D, w->g_attn, dims->rms_eps, h, a, bf, s));
@@ -694,14 +703,15 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
     sa.kc = cache->k;
     sa.vc = cache->v;
     sa.layer0 = l;
-    sa.B = B;
+    sa.B = cache->B;
     sa.Hkv = Hkv;
     sa.d = d;
     sa.cap = cache->cap;
     sa.rows.B = B;
     for (int b = 0; b < B; ++b) {
       sa.rows.row_off[b] = qrow0[b];
-      sa.rows.pos0[b] = cache->len[b];
+      sa.rows.pos0[b] = qg.pos0[b];
+      sa.rows.seq[b] = qg.kvseq[b];
     }
     sa.rows.row_off[B] = M;
     DF_HIP(launch_scatter_kv(sa, cbf, s));
@@ -722,8 +732,10 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
     at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
     for (int b = 0; b < B; ++b) {
       at.nkeys[b] = nkeys[b];
-      at.gam[b] = gammas[b];
+      at.gam[b] = qg.gam[b];
       at.qrow0[b] = qrow0[b];
+      at.kvseq[b] = qg.kvseq[b];
+      at.blk0[b] = qg.apart ? qg.pos0[b] : -1;
     }
     at.qrow0[B] = M;
     const int pa = prof_begin(DFLASH_PROF_ATTENTION, s);
@@ -761,6 +773,27 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
   return ok();
 }
 
+// Inference groups: sequence b's block of gammas[b] rows follows its context.
+static dflash_status inference_groups(const dflash_dims* dims, const dflash_weights* w,
+                                      const dflash_kv_cache* cache, const int32_t* gammas, QueryGroups* qg) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
+  if ((st = check_cache(cache)) != DFLASH_OK) return st;
+  DF_REQUIRE(gammas != nullptr, DFLASH_ERR_INVALID_ARG, "gammas is NULL");
+  qg->n = cache->B;
+  qg->apart = false;
+  for (int b = 0; b < cache->B; ++b) {
+    if ((st = check_gamma(gammas[b])) != DFLASH_OK) return st;
+    DF_REQUIRE(static_cast<int64_t>(cache->len[b]) + gammas[b] <= cache->cap, DFLASH_ERR_CAPACITY,
+               "sequence %d: len %d + gamma %d exceeds cap %d", b, cache->len[b], gammas[b], cache->cap);
+    qg->gam[b] = gammas[b];
+    qg->kvseq[b] = b;
+    qg->nctx[b] = qg->pos0[b] = cache->len[b];
+  }
+  return DFLASH_OK;
+}
+
 dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights* w, const dflash_kv_cache* cache,
                                    const int32_t* block_tokens, const float* embed_override, int32_t gamma,
                                    float* h_final, void* ws, size_t ws_bytes, void* stream) {
@@ -769,14 +802,57 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
   if ((st = check_cache(cache)) != DFLASH_OK) return st;
   int32_t gammas[kMaxSeq];
   for (int b = 0; b < cache->B; ++b) gammas[b] = gamma;
-  return draft_forward_impl(dims, w, cache, block_tokens, embed_override, gammas, h_final, ws, ws_bytes, stream);
+  QueryGroups qg;
+  if ((st = inference_groups(dims, w, cache, gammas, &qg)) != DFLASH_OK) return st;
+  return draft_forward_impl(dims, w, cache, block_tokens, embed_override, qg, h_final, ws, ws_bytes, stream);
 }
 
 dflash_status dflash_draft_forward_ragged(const dflash_dims* dims, const dflash_weights* w,
                                           const dflash_kv_cache* cache, const int32_t* block_tokens,
                                           const float* embed_override, const int32_t* gammas, float* h_final,
                                           void* ws, size_t ws_bytes, void* stream) {
-  return draft_forward_impl(dims, w, cache, block_tokens, embed_override, gammas, h_final, ws, ws_bytes, stream);
+  QueryGroups qg;
+  const dflash_status st = inference_groups(dims, w, cache, gammas, &qg);
+  if (st != DFLASH_OK) return st;
+  return draft_forward_impl(dims, w, cache, block_tokens, embed_override, qg, h_final, ws, ws_bytes, stream);
+}
+
+dflash_status dflash_draft_forward_blocks(const dflash_dims* dims, const dflash_weights* w,
+                                          const dflash_kv_cache* cache, const int32_t* block_seq,
+                                          const int32_t* anchors, int32_t nblk, int32_t gamma,
+                                          const int32_t* block_tokens, const float* embed_override, float* h_final,
+                                          void* ws, size_t ws_bytes, void* stream) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
+  if ((st = check_cache(cache)) != DFLASH_OK) return st;
+  if ((st = check_gamma(gamma)) != DFLASH_OK) return st;
+  DF_REQUIRE(nblk >= 1 && nblk <= DFLASH_MAX_BATCH, DFLASH_ERR_INVALID_ARG, "nblk=%d outside [1, %d]", nblk,
+             DFLASH_MAX_BATCH);
+  DF_REQUIRE(block_seq != nullptr && anchors != nullptr, DFLASH_ERR_INVALID_ARG, "block_seq / anchors is NULL");
+  QueryGroups qg;
+  qg.n = nblk;
+  qg.apart = true;
+  const int g32 = (gamma + 31) / 32 * 32;
+  int used[kMaxSeq] = {0};   // scratch slots taken per sequence
+  for (int k = 0; k < nblk; ++k) {
+    const int sq = block_seq[k];
+    DF_REQUIRE(sq >= 0 && sq < cache->B, DFLASH_ERR_INVALID_ARG, "block %d: sequence %d outside [0, %d)", k, sq,
+               cache->B);
+    DF_REQUIRE(anchors[k] >= 0 && anchors[k] <= cache->len[sq], DFLASH_ERR_INVALID_ARG,
+               "block %d: anchor %d outside [0, len %d]", k, anchors[k], cache->len[sq]);
+    // the block's own rows: 32-row slots past the sequence's context
+    const int64_t pos = (static_cast<int64_t>(cache->len[sq]) + 31) / 32 * 32 + static_cast<int64_t>(used[sq]) * g32;
+    DF_REQUIRE(pos + g32 <= cache->cap, DFLASH_ERR_CAPACITY,
+               "block %d: scratch rows [%lld, %lld) of sequence %d exceed cap %d", k, static_cast<long long>(pos),
+               static_cast<long long>(pos + g32), sq, cache->cap);
+    ++used[sq];
+    qg.gam[k] = gamma;
+    qg.kvseq[k] = sq;
+    qg.nctx[k] = anchors[k];
+    qg.pos0[k] = static_cast<int32_t>(pos);
+  }
+  return draft_forward_impl(dims, w, cache, block_tokens, embed_override, qg, h_final, ws, ws_bytes, stream);
 }
 
 // LM head + argmax over Mr activation rows that g's A mapping addresses (K = D).

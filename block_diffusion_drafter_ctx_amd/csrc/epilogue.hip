@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(ScatterArgs a) {
   int b = 0;
   while (b + 1 < a.rows.B && r >= a.rows.row_off[b + 1]) ++b;
   const int pos = a.rows.pos0[b] + (r - a.rows.row_off[b]);
-  const int64_t head0 = (static_cast<int64_t>(layer) * a.B + b) * a.Hkv;
+  const int64_t head0 = (static_cast<int64_t>(layer) * a.B + a.rows.seq[b]) * a.Hkv;
   if (rem < hd) {
     const int j = rem / a.d, c = rem % a.d;
     st4<T>(a.kc, ((head0 + j) * a.cap + pos) * a.d + c, v);

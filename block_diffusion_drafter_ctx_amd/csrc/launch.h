@@ -101,6 +101,7 @@ struct SeqRows {
   int32_t B;
   int32_t row_off[kMaxSeq + 1];
   int32_t pos0[kMaxSeq];
+  int32_t seq[kMaxSeq];   // scatter: cache sequence of group b
 };
 
 struct ScatterArgs {
@@ -217,6 +218,10 @@ struct AttnArgs {
   int32_t R, Rpad;       // query rows per (b, kv head): the largest G*gam[b], padded to 16
   int32_t gam[kMaxSeq];       // block rows of sequence b
   int32_t qrow0[kMaxSeq + 1]; // first block row of sequence b in q / o_out (qrow0[B] = M)
+  int32_t kvseq[kMaxSeq];     // cache sequence whose K/V block b reads
+  int32_t blk0[kMaxSeq];      // -1: the block's rows follow the context (keys [0, nkeys[b]));
+                              // else its own rows [blk0, blk0 + gam) are a separate key item
+                              // after the context keys [0, nkeys[b]) (blk0 % 32 == 0)
   int32_t split_keys;    // keys per work item (multiple of 32)
   int32_t items;
   float scale_log2;      // log2(e) / sqrt(d)
@@ -232,7 +237,9 @@ struct AttnPlan {
   size_t part_floats = 0;
 };
 
-AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d);
+// apart (nullable): apart[b] != 0 when block b's own rows are stored apart
+// from its context (one more key item per (b, kv head))
+AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d, const int32_t* apart = nullptr);
 size_t attention_part_bound(int B, int Hkv, int R, int d);
 // stop_event (nullable hipEvent_t) is recorded right after the main attention
 // kernel, before its combine step (profiling hook).

@@ -155,3 +155,10 @@ class DeviceDrafter:
         B.argmax_accept_ragged(self.dims, self.weights, flags, p(h_final), list(gammas), p(draft), p(target), p(tau),
                                p(nxt), p(logits), p(gap), p(self.ws), self.ws_bytes, _stream())
 
+    # ---- many anchored blocks at once (training-style mask)
+    def draft_blocks(self, cache: DeviceCache, block_seq, anchors, gamma, tokens, override, h_final: torch.Tensor):
+        B.draft_forward_blocks(self.dims, self.weights, cache.struct, list(block_seq), list(anchors), gamma,
+                               0 if tokens is None else tokens.data_ptr(),
+                               0 if override is None else override.data_ptr(), h_final.data_ptr(),
+                               self.ws.data_ptr(), self.ws_bytes, _stream())
+

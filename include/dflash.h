@@ -12,6 +12,8 @@
  *                             acceptance length against the target's tokens
  * with variants for blocks whose length differs per sequence:
  *   dflash_draft_forward_ragged, dflash_argmax_accept_ragged
+ * and the drafter over many anchored blocks at once (the training-style mask):
+ *   dflash_draft_forward_blocks
  * and, for decoding at a temperature T > 0, the sampled counterpart of (d):
  *   dflash_sample_drafts  draft tokens drawn from softmax(logits / T)
  *   dflash_sample_accept  lossless acceptance of a sampled block against the
@@ -200,6 +202,28 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
 dflash_status dflash_draft_forward_ragged(const dflash_dims* dims, const dflash_weights* w,
                                           const dflash_kv_cache* cache, const int32_t* block_tokens,
                                           const float* embed_override, const int32_t* gammas, float* h_final,
+                                          void* ws, size_t ws_bytes, void* stream);
+
+/* (c) over many blocks anchored inside the cached context at once, as in
+ * training ([JP] "학습 방법", sparse attention mask: every block attends to its
+ * own rows in both directions and to its sequence's injected context, never
+ * to another block).  Block k is anchored at position anchors[k] of sequence
+ * block_seq[k]: its gamma rows (the anchor token, then mask rows) see that
+ * sequence's context rows [0, anchors[k]) and its own rows only.
+ *   block_seq, anchors  HOST [nblk]; 0 <= anchors[k] <= len[block_seq[k]]
+ *   nblk                1 .. DFLASH_MAX_BATCH blocks per call
+ *   block_tokens        [nblk][gamma] int32 (or embed_override [nblk][gamma][D])
+ *   h_final             out [nblk][gamma][D] float32
+ * Each block's own K/V rows are written to scratch rows of its sequence past
+ * the context: the i-th block of sequence s (in call order) takes rows
+ * [L32 + i*G32, L32 + i*G32 + gamma), L32 = len[s] rounded up to a multiple
+ * of 32 and G32 = gamma rounded up likewise.  Errors: DFLASH_ERR_CAPACITY if
+ * L32 + (blocks of s)*G32 > cap.  Context rows and len are not changed.
+ * A workspace sized by dflash_workspace_size(dims, nblk, gamma, ..) suffices. */
+dflash_status dflash_draft_forward_blocks(const dflash_dims* dims, const dflash_weights* w,
+                                          const dflash_kv_cache* cache, const int32_t* block_seq,
+                                          const int32_t* anchors, int32_t nblk, int32_t gamma,
+                                          const int32_t* block_tokens, const float* embed_override, float* h_final,
                                           void* ws, size_t ws_bytes, void* stream);
 
 #define DFLASH_ARGMAX 1u

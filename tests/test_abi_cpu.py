@@ -249,3 +249,22 @@ def test_workspace_covers_ragged_row_counts(lib):
     big = B.workspace_size(d, 4, 16, 1)
     assert big >= B.workspace_size(d, 4, 15, 1)
     assert big >= B.workspace_size(d, 3, 16, 1)
+
+
+def test_blocks_checks(lib):
+    w = B.Weights(w_qkv=0x1000, w_o=0x1000, w_gateup=0x1000, w_down=0x1000, g_attn=0x1000, g_ffn=0x1000,
+                  g_final=0x1000, embed=0x1000, lm_head=0x1000)
+    c = _cache(cap=128, lens=(40, 10))
+    for seqs, anchors in (([2], [0]), ([0], [41]), ([1], [-1]), ([0] * 65, [0] * 65)):
+        with pytest.raises(B.DFlashError) as e:
+            B.draft_forward_blocks(_dims(), w, c, seqs, anchors, 16, 0x4000, None, 0x5000, 0x100000, 1 << 30)
+        assert e.value.status == B.ERR_INVALID_ARG, (seqs, anchors)
+    # sequence 0: context rounds up to 64, three 32-row slots reach 160 > 128
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward_blocks(_dims(), w, c, [0, 0, 1, 0], [5, 40, 3, 0], 16, 0x4000, None, 0x5000, 0x100000,
+                               1 << 30)
+    assert e.value.status == B.ERR_CAPACITY and "block 3" in B.last_error()
+    assert list(c._keep) == [40, 10]
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward_blocks(_dims(), w, c, [0, 1], [5, 3], 16, 0x4000, None, 0x5000, 0x100000, 16)
+    assert e.value.status == B.ERR_WORKSPACE

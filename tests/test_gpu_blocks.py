@@ -1,0 +1,122 @@
+"""Many anchored blocks at once (the training-style mask): HIP path against
+the CPU oracle.  Tolerances as in tests/parity_util.py."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_drafter_ctx_amd import binding as B
+from dflash_inputs import CONFIGS, shrink
+from oracle import dflash_oracle as O
+from tests.parity_util import GAP_MIN, GAP_MIN_BF16_CACHE, Workload, argmax_agree, close, close_stored, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU parity tests need a gfx950 GPU")
+    B.load()
+
+
+def small(**kw):
+    base = dict(name="small_bf16_blocks", cid=130, D=512, L=2, Hq=8, Hkv=2, d=128, F=1536, V=1000, B=2,
+                ctx=(37, 300), gammas=(16,), gain_std=0.1, iters=1, append_rows=0)
+    base.update(kw)
+    return shrink(CONFIGS[2], **base)
+
+
+class Blocks(Workload):
+    """A seeded context, then blocks anchored inside it."""
+
+    def __init__(self, cfg, blocks, gamma, override=False):
+        g32 = (gamma + 31) // 32 * 32
+        per_seq = max(sum(1 for s, _ in blocks if s == b) for b in range(cfg.B))
+        super().__init__(cfg, gamma, 1, override=override, extra_cap=32 + per_seq * g32)
+        self.blocks = [(int(s), int(a)) for s, a in blocks]
+        self.dr.ensure_workspace(max(cfg.B, len(blocks)), gamma, max(cfg.n_ctx_total, 1))
+
+    def run_blocks(self, tag="blocks"):
+        cfg, g, dev = self.cfg, self.gamma, self.dev
+        self.ingest(self.inp.ctx_states(), list(cfg.ctx), "context")
+        nb = len(self.blocks)
+        rng = np.random.default_rng([cfg.cid, 91])
+        toks = np.full((nb, g), cfg.mask_id, dtype=np.int32)
+        toks[:, 0] = rng.integers(0, cfg.V - 1, nb)
+        ov = rng.normal(0, 1, (nb, g, cfg.D)).astype(np.float32) if self.override else None
+        h_final = torch.empty(nb, g, cfg.D, dtype=torch.float32, device=dev)
+        lens = self.cache.len_list()
+        k_before = [self.cache.k[:, b, :, :lens[b]].clone() for b in range(cfg.B)]
+        v_before = [self.cache.v[:, b, :, :, :lens[b]].clone() for b in range(cfg.B)]
+        seqs = [s for s, _ in self.blocks]
+        anchors = [a for _, a in self.blocks]
+        self.dr.draft_blocks(self.cache, seqs, anchors, g, torch.from_numpy(toks).to(dev),
+                             None if ov is None else torch.from_numpy(ov).to(dev), h_final)
+        draft = torch.empty(nb, g - 1, dtype=torch.int32, device=dev)
+        logits = torch.empty(nb, g - 1, cfg.V, dtype=torch.float32, device=dev)
+        gap = torch.empty(nb, g - 1, dtype=torch.float32, device=dev)
+        self.dr.argmax_accept(B.ARGMAX, h_final, nb, g, draft, logits=logits, gap=gap)
+        torch.cuda.synchronize()
+        assert self.cache.len_list() == lens
+        for b in range(cfg.B):
+            assert torch.equal(self.cache.k[:, b, :, :lens[b]], k_before[b]), "context K rows changed"
+            assert torch.equal(self.cache.v[:, b, :, :, :lens[b]], v_before[b]), "context V rows changed"
+        hf_o, kv_o = O.draft_forward_blocks(cfg, self.o_layers, self.o_gfinal, self.ocache, self.blocks, g,
+                                            embed=self.o_embed, tokens=toks, override=ov, storage=self.st)
+        e = close(h_final.cpu().numpy(), hf_o, self.tol, f"{tag} h_final")
+        d_o, gap_o, z_o = O.lm_head_argmax(hf_o, self.o_embed)
+        close(logits.cpu().numpy(), z_o, self.tol, f"{tag} logits")
+        excl = argmax_agree(draft.cpu().numpy(), d_o, gap_o, f"{tag} drafts",
+                            GAP_MIN_BF16_CACHE if self.st == "bf16" else GAP_MIN)
+        # each block's own K/V rows sit in its scratch slot past its sequence's context
+        g32 = (g + 31) // 32 * 32
+        used = [0] * cfg.B
+        for k, (s, _) in enumerate(self.blocks):
+            pos = (lens[s] + 31) // 32 * 32 + used[s] * g32
+            used[s] += 1
+            for l in range(cfg.L):
+                gk = self.cache.k[l, s, :, pos:pos + g].float().cpu().numpy().transpose(1, 0, 2)
+                gv = self.cache.v[l, s, :, :, pos:pos + g].float().cpu().numpy().transpose(2, 0, 1)
+                close_stored(gk, kv_o[k][l][0], self.st, f"{tag} block {k} K l{l}", self.tol)
+                close_stored(gv, kv_o[k][l][1], self.st, f"{tag} block {k} V l{l}", self.tol)
+        log(f"{tag}: {nb} blocks {self.blocks[:8]}: h_final err {e[0]:.2e}, drafts agree "
+            f"({excl} near-tie rows excluded)")
+
+
+def test_blocks_small():
+    # anchors at 0 (no context), inside, and at the full length; three blocks
+    # per sequence share its scratch region
+    blocks = [(0, 0), (0, 20), (1, 150), (1, 300), (0, 37), (1, 1)]
+    log("anchored blocks, small bf16")
+    Blocks(small(), blocks, 16).run_blocks()
+
+
+def test_blocks_override_bf16_cache_gamma33():
+    blocks = [(0, 12), (1, 299), (1, 64), (0, 36)]
+    log("anchored blocks, bf16 cache, gamma 33 (two row groups)")
+    Blocks(small(cid=131, cache_dtype="bf16"), blocks, 33, override=True).run_blocks()
+
+
+def test_blocks_head64():
+    blocks = [(0, 5), (0, 0), (1, 70)]
+    log("anchored blocks, head_dim 64")
+    Blocks(small(cid=132, d=64, Hq=4, Hkv=4, ctx=(9, 70)), blocks, 8, override=True).run_blocks()
+
+
+def test_blocks_f32():
+    blocks = [(0, 100), (0, 3), (0, 128)]
+    log("anchored blocks, tiny fp32 drafter")
+    cfg = shrink(CONFIGS[1], cid=133, gain_std=0.1, append_rows=0)
+    Blocks(cfg, blocks, 16, override=True).run_blocks()
+
+
+def test_blocks_full_qwen_shape():
+    # the Qwen3-8B-shaped drafter at a 2048-token context, 8 blocks anchored in
+    # its second half (the response part of a training sequence): 128 block rows
+    cfg = shrink(CONFIGS[2], cid=134, append_rows=0)
+    rng = np.random.default_rng(134)
+    anchors = sorted(rng.integers(1024, 2049, 8).tolist())
+    log(f"anchored blocks, full shape, anchors {anchors}")
+    Blocks(cfg, [(0, a) for a in anchors], 16).run_blocks()
