@@ -73,6 +73,7 @@ def main():
     ap.add_argument("--temperature", type=float, default=1.0, help="temperature of the sampled-decoding leg")
     ap.add_argument("--no-sampling", action="store_true", help="skip the sampled-decoding leg")
     ap.add_argument("--no-ragged", action="store_true", help="skip the per-sequence block-length leg")
+    ap.add_argument("--no-blocks", action="store_true", help="skip the anchored-blocks (training-mask) leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the single-GPU path is "
@@ -297,6 +298,8 @@ def main():
                                       H_app, make_events, hook, ms_per_step)
     if not args.no_ragged and cfg.dtype == "bf16":
         out["ragged"] = ragged_leg(cfg, dr)
+    if not args.no_blocks and cfg.dtype == "bf16":
+        out["blocks"] = blocks_leg(cfg, dr)
 
     # A plain device copy of a known size: the reference that scales rocprofv3's
     # FETCH_SIZE / WRITE_SIZE counters into bytes (256 MiB read + 256 MiB written).
@@ -308,14 +311,16 @@ def main():
     del src, dst
 
     if not args.no_cpu_baseline:
-        greedy_cpu, sampled_cpu, ragged_cpu = cpu_baseline(cfg, inp, args.cpu_seconds,
-                                                           None if args.no_sampling else args.temperature,
-                                                           "ragged" in out)
+        greedy_cpu, sampled_cpu, ragged_cpu, blocks_cpu = cpu_baseline(
+            cfg, inp, args.cpu_seconds, None if args.no_sampling else args.temperature, "ragged" in out,
+            "blocks" in out)
         out["cpu_baseline"] = greedy_cpu
         if sampled_cpu is not None:
             out["sampling"]["cpu_baseline"] = sampled_cpu
         if ragged_cpu is not None:
             out["ragged"]["cpu_baseline"] = ragged_cpu
+        if blocks_cpu is not None:
+            out["blocks"]["cpu_baseline"] = blocks_cpu
     print(json.dumps(out), flush=True)
 
 
@@ -550,7 +555,79 @@ def ragged_leg(cfg, dr):
     }
 
 
-def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False):
+BLOCKS_CTX, BLOCKS_N, BLOCKS_GAMMA = 3072, 64, 16
+
+
+def blocks_anchors():
+    import numpy as np
+    rng = np.random.default_rng(20261202)
+    return sorted(rng.integers(BLOCKS_CTX // 2, BLOCKS_CTX + 1, BLOCKS_N).tolist())
+
+
+def blocks_leg(cfg, dr):
+    """Many anchored blocks in one pass (the training-style mask): one sequence
+    with a 3072-token context (the pages' longest training sequences) and 64
+    blocks of 16 rows anchored uniformly in its second half (the response),
+    each seeing the context before its anchor and its own rows."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_drafter_ctx_amd import roofline as RF
+
+    dev = "cuda"
+    anchors = blocks_anchors()
+    g = BLOCKS_GAMMA
+    nb, D = len(anchors), cfg.D
+    g32 = (g + 31) // 32 * 32
+    cap = (BLOCKS_CTX + 31) // 32 * 32 + nb * g32
+    cache = dr.cache(1, cap)
+    dr.ensure_workspace(nb, g, BLOCKS_CTX)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261203)
+    states = [torch.randn(BLOCKS_CTX, D, generator=gen, device=dev).to(torch.bfloat16) for _ in range(cfg.n_tgt)]
+    H_t = dr.context_buffer(BLOCKS_CTX)
+    dr.fuse(states, BLOCKS_CTX, H_t)
+    dr.inject(H_t, [BLOCKS_CTX], cache)
+    del states, H_t
+    tok = torch.full((nb, g), cfg.mask_id, dtype=torch.int32, device=dev)
+    tok[:, 0] = torch.arange(nb, dtype=torch.int32, device=dev)
+    hf = torch.empty(nb, g, D, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dr.draft_blocks(cache, [0] * nb, anchors, g, tok, None, hf)
+    ev = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dr.draft_blocks(cache, [0] * nb, anchors, g, tok, None, hf)
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    M = nb * g
+    flops = 2 * M * cfg.L * (RF.layer_weight_elems(cfg.D, cfg.Hq, cfg.Hkv, cfg.d, cfg.F) - 2 * D) + \
+        cfg.L * sum(4 * cfg.Hq * g * (a + g) * cfg.d for a in anchors)
+    cs = RF.elem_bytes(cfg.cache_dtype)
+    nbytes = (cfg.L * RF.layer_weight_elems(cfg.D, cfg.Hq, cfg.Hkv, cfg.d, cfg.F) * RF.elem_bytes(cfg.dtype)
+              + cfg.L * sum(a + g for a in anchors) * 2 * cfg.Hkv * cfg.d * cs + M * D * 4 * 2)
+    log(f"blocks: {nb} blocks of {g} rows in a {BLOCKS_CTX}-token context: {us:.1f} us")
+    del cache
+    return {
+        "workload": (f"one sequence, {BLOCKS_CTX}-token context, {nb} blocks of {g} rows anchored uniformly in "
+                     f"[{BLOCKS_CTX // 2}, {BLOCKS_CTX}] ({M} query rows), {cfg.L} layers at the bench drafter's "
+                     f"shape; forward pass only (no LM head)"),
+        "anchors": anchors,
+        "us": round(us, 1),
+        "gflop": round(flops / 1e9, 1),
+        "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+        "mfma_frac": round(flops / (us * 1e-6) / 1e12 / RF.MFMA_BF16_TFLOPS, 4),
+        "bytes": int(nbytes),
+        "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4),
+        "note": "FLOPs are algorithmic (one product per GEMM); the fp32 activations run as two bf16 products",
+    }
+
+
+def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False, blocks=False):
     """The CPU oracle, as it stands, on whole drafting iterations of the same
     workload (draft forward + LM-head argmax + accept + 16-row append), repeated
     for about ``seconds`` with the GPU loop's 8-iteration cache reset; then, when
@@ -636,8 +713,26 @@ def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False):
                              f"drafts + synthetic target logits + lossless verify + 16-row append), float64 "
                              f"numpy oracle",
                    "seconds": round(dt, 2)}
+    blk = None
+    if blocks:
+        # two of the blocks leg's anchored blocks over seeded random context K/V
+        rng = np.random.default_rng(20261203)
+        anchors = blocks_anchors()[:2]
+        bc = O.OracleCache(cfg.L, 1, cfg.Hkv, cfg.d)
+        for l in range(cfg.L):
+            bc.append(l, 0, rng.normal(0, 1, (BLOCKS_CTX, cfg.Hkv, cfg.d)), rng.normal(0, 1, (BLOCKS_CTX, cfg.Hkv, cfg.d)))
+        toks = np.full((2, BLOCKS_GAMMA), cfg.mask_id)
+        toks[:, 0] = [0, 1]
+        t0 = time.perf_counter()
+        O.draft_forward_blocks(cfg, layers, gf, bc, [(0, a) for a in anchors], BLOCKS_GAMMA, embed=E, tokens=toks,
+                               storage=cfg.cache_dtype)
+        dt = time.perf_counter() - t0
+        log(f"cpu baseline (blocks): 2 blocks in {dt:.1f}s")
+        blk = {"value": round(2 / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"two anchored blocks (anchors {anchors}) of the blocks leg over random context K/V, "
+                         f"float64 numpy oracle", "seconds": round(dt, 2)}
     if not ragged:
-        return greedy, sampled, None
+        return greedy, sampled, None, blk
     # the first four sequences of the ragged leg (blocks 4, 8, 16, 32) over
     # seeded random context K/V of their batch16_ragged lengths (stand-ins for
     # an untimed ingest), one ragged pass + argmax
@@ -659,7 +754,7 @@ def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False):
            "sample": f"one ragged pass + LM-head argmax over 4 sequences (blocks {gs}, contexts {ctx}, random "
                      f"context K/V), float64 numpy oracle",
            "drafts_per_s": round(sum(g - 1 for g in gs) / dt, 3), "seconds": round(dt, 2)}
-    return greedy, sampled, rag
+    return greedy, sampled, rag, blk
 
 
 if __name__ == "__main__":
