@@ -971,15 +971,20 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
   const int tiles = p.mtiles * p.ntiles;
   if (ak != A_F32_SPLIT) {
     // LDS-direct kernel: one workgroup per CU (its stages fill most of the
-    // LDS).  Split K so that the last round of workgroups is not left mostly
-    // idle: the cost of S splits is ceil(tiles * S / CUs) rounds of 1 / S of
-    // the K range; the smallest S of least cost wins (each split adds an
-    // M x N fp32 partial for the consumer to read).
+    // LDS).  Split K so that the CUs are kept busy: S splits cost
+    // ceil(tiles * S / CUs) rounds of 1 / S of the K range (in units of the
+    // whole product spread evenly over the CUs), plus the extra fp32 partials
+    // the consumer reads: (S - 1) * 8 bytes per output against the product's
+    // 2 * K FLOP per output per bf16 product, at ~200 FLOP per HBM byte for
+    // this kernel.  At most 16 splits of at least 4 k-tiles each; the smallest
+    // S of least cost wins.
     const int cus = device_cus();
+    const int products = ak == A_BF16_HILO ? 2 : 1;
     int best_s = 1;
     double best_cost = 1e30;
-    for (int s = 1; s <= 4 && s <= ktiles / 4; ++s) {
-      const double cost = static_cast<double>((static_cast<long>(tiles) * s + cus - 1) / cus) / s;
+    for (int s = 1; s <= 16 && s <= ktiles / 4; ++s) {
+      const double rounds = static_cast<double>((static_cast<long>(tiles) * s + cus - 1) / cus) / s;
+      const double cost = rounds * cus / tiles + (s - 1) * 800.0 / (static_cast<double>(products) * K);
       if (cost < best_cost - 1e-9) best_cost = cost, best_s = s;
     }
     p.cps = (ktiles + best_s - 1) / best_s;
