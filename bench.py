@@ -74,6 +74,7 @@ def main():
     ap.add_argument("--no-sampling", action="store_true", help="skip the sampled-decoding leg")
     ap.add_argument("--no-ragged", action="store_true", help="skip the per-sequence block-length leg")
     ap.add_argument("--no-blocks", action="store_true", help="skip the anchored-blocks (training-mask) leg")
+    ap.add_argument("--no-gamma-sweep", action="store_true", help="skip the block-length sweep on the 8-layer drafter")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the single-GPU path is "
@@ -300,6 +301,10 @@ def main():
         out["ragged"] = ragged_leg(cfg, dr)
     if not args.no_blocks and cfg.dtype == "bf16":
         out["blocks"] = blocks_leg(cfg, dr)
+    if not args.no_gamma_sweep and cfg.dtype == "bf16":
+        del dr, cache
+        torch.cuda.empty_cache()
+        out["gamma_sweep"] = gamma_sweep_leg()
 
     # A plain device copy of a known size: the reference that scales rocprofv3's
     # FETCH_SIZE / WRITE_SIZE counters into bytes (256 MiB read + 256 MiB written).
@@ -553,6 +558,68 @@ def ragged_leg(cfg, dr):
         "GBps": round(rb / (rag_us * 1e-6) / 1e9, 1),
         "hbm_frac": round(rb / (rag_us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4),
     }
+
+
+def gamma_sweep_leg():
+    """Draft forward + LM-head argmax of the deep8_b4_n8192 workload (8 layers,
+    4 sequences with 8192-token contexts) at blocks of 8, 16 and 32 rows, on one
+    fixed cache: the drafting cost should stay flat in the block size ([JP]
+    "Preliminaries": one pass whatever the block length)."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_drafter_ctx_amd import binding as B
+    from block_diffusion_drafter_ctx_amd import roofline as RF
+    from block_diffusion_drafter_ctx_amd.runtime import DeviceDrafter
+    from dflash_inputs import CONFIGS
+
+    cfg = CONFIGS[5]
+    dev = "cuda"
+    gammas = list(cfg.gammas)
+    gmax, Bn, N = max(gammas), cfg.B, cfg.ctx[0]
+    dr = DeviceDrafter.random_init(cfg, 20261205, dev)
+    cache = dr.cache(Bn, (N + gmax + 31) // 32 * 32)
+    dr.ensure_workspace(Bn, gmax, cfg.n_ctx_total)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261206)
+    states = [torch.randn(cfg.n_ctx_total, cfg.D, generator=gen, device=dev).to(torch.bfloat16)
+              for _ in range(cfg.n_tgt)]
+    H_t = dr.context_buffer(cfg.n_ctx_total)
+    dr.fuse(states, cfg.n_ctx_total, H_t)
+    dr.inject(H_t, list(cfg.ctx), cache)
+    del states, H_t
+    stream = torch.cuda.current_stream()
+    es, cs = RF.elem_bytes(cfg.dtype), RF.elem_bytes(cfg.cache_dtype)
+    res = {}
+    for g in gammas:
+        tok = torch.full((Bn, g), cfg.mask_id, dtype=torch.int32, device=dev)
+        tok[:, 0] = torch.arange(Bn, dtype=torch.int32, device=dev)
+        hf = torch.empty(Bn, g, cfg.D, dtype=torch.float32, device=dev)
+        d = torch.empty(Bn, g - 1, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            dr.draft(cache, tok, None, g, hf)
+            dr.argmax_accept(B.ARGMAX, hf, Bn, g, d)
+        ev = []
+        for _ in range(20):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dr.draft(cache, tok, None, g, hf)
+            dr.argmax_accept(B.ARGMAX, hf, Bn, g, d)
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+        nbytes = RF.draft_forward_bytes(cfg.D, cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.F, cfg.V, Bn, g, list(cfg.ctx),
+                                        es, cs)
+        res[str(g)] = {"us": round(us, 1), "bytes": int(nbytes),
+                       "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4)}
+    ratio = res[str(gmax)]["us"] / res[str(min(gammas))]["us"]
+    log(f"gamma sweep (8 layers, 4 x 8192): " + ", ".join(f"{g}: {v['us']:.0f} us" for g, v in res.items()) +
+        f"; us({gmax}) / us({min(gammas)}) = {ratio:.3f}")
+    del dr, cache
+    return {"workload": (f"{cfg.name}: {cfg.L} layers, {Bn} sequences x {N}-token contexts, draft forward + "
+                         f"LM-head argmax at a fixed cache (seeded device-side random-init weights)"),
+            "per_gamma": res, "us_ratio_max_over_min": round(ratio, 3)}
 
 
 BLOCKS_CTX, BLOCKS_N, BLOCKS_GAMMA = 3072, 64, 16

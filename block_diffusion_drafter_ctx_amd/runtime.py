@@ -94,6 +94,41 @@ class DeviceDrafter:
         self.ws = None
         self.ws_bytes = 0
 
+    @classmethod
+    def random_init(cls, cfg, seed: int, device="cuda"):
+        """Weights drawn on the device from a seeded generator (matrices
+        N(0, cfg.w_std), unit gains, tied embedding / LM head), for measurements
+        whose weights need not match the host-side seeded inputs."""
+        self = cls.__new__(cls)
+        self.cfg, self.device = cfg, device
+        self.dims = dims_of(cfg)
+        gen = torch.Generator(device=device)
+        gen.manual_seed(seed)
+        dt = torch_dtype(cfg)
+
+        def mat(*shape):
+            return (torch.randn(*shape, generator=gen, device=device) * cfg.w_std).to(dt)
+
+        L = cfg.L
+        self.w_c = mat(cfg.D, cfg.n_tgt * cfg.D)
+        self.g_c = torch.ones(cfg.D, dtype=dt, device=device)
+        self.w_qkv = mat(L, (cfg.Hq + 2 * cfg.Hkv) * cfg.d, cfg.D)
+        self.w_o = mat(L, cfg.D, cfg.Hq * cfg.d)
+        self.w_gateup = mat(L, 2 * cfg.F, cfg.D)
+        self.w_down = mat(L, cfg.D, cfg.F)
+        self.g_attn = torch.ones(L, cfg.D, dtype=dt, device=device)
+        self.g_ffn = torch.ones(L, cfg.D, dtype=dt, device=device)
+        self.g_final = torch.ones(cfg.D, dtype=dt, device=device)
+        self.embed = mat(cfg.V, cfg.D)
+        p = lambda t: t.data_ptr()  # noqa: E731
+        self.weights = B.Weights(w_c=p(self.w_c), g_c=p(self.g_c), w_qkv=p(self.w_qkv), w_o=p(self.w_o),
+                                 w_gateup=p(self.w_gateup), w_down=p(self.w_down), g_attn=p(self.g_attn),
+                                 g_ffn=p(self.g_ffn), g_final=p(self.g_final), embed=p(self.embed),
+                                 lm_head=p(self.embed))
+        self.ws = None
+        self.ws_bytes = 0
+        return self
+
     # ---- memory
     def cache(self, B_: int, cap: int) -> DeviceCache:
         return DeviceCache(self.cfg, B_, cap, self.device)
