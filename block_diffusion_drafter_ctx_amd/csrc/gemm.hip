@@ -211,7 +211,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(GemmArgs g) {
 }
 
 // ------------------------------------------------------------- register-K path
-// One block of <= 16 activation rows against a tall weight (the LM head, the
+// One block of <= 16 activation rows (a 16-row chunk of a larger block, see
+// rk_max_rows) against a tall weight (the LM head, the
 // FFN gate/up projection).  Sixteen waves split the K range of a workgroup
 // (wave w owns KS k-steps) and keep their activation fragments (hi + lo) in
 // registers for the whole kernel, so a workgroup needs no split-K partner and
@@ -254,8 +255,17 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = g.S;
   const int units = S * g.ntiles;
-  const int P = gridDim.x;
-  const int u0 = blockIdx.x;
+  // More than 16 activation rows: chunk c (rows 16c..16c+15) of unit group w
+  // runs on its own workgroup, (w / 8) * 8C + 8c + w % 8 in launch order.
+  // Workgroups 8 apart land on the same XCD and are dispatched together, so the
+  // C chunks of a unit group stream the same weight tiles through one L2 at
+  // about the same time.  The launcher makes P a multiple of 8 when C > 1.
+  const int C = g.rchunks > 1 ? g.rchunks : 1;
+  const int L = blockIdx.x;
+  const int chunk = C > 1 ? (L >> 3) % C : 0;
+  const int u0 = C > 1 ? (L / (8 * C)) * 8 + (L & 7) : L;   // unit group
+  const int m0 = 16 * chunk;                  // first activation row of the chunk
+  const int P = gridDim.x / C;
   if (u0 >= units) return;                    // uniform per workgroup
   const int sp = u0 % S;                      // P % S == 0: the split never changes
   const int kwave = sp * (32 * KS * kRkWaves) + wave * (32 * KS);
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
   uint4 bh[KS], bl[SPLIT ? KS : 1];
   if constexpr (!SPLIT) {
     const int s = __builtin_amdgcn_readfirstlane(kwave / g.a_cols);
-    const int m = lane & 15;
+    const int m = m0 + (lane & 15);
     const bool ok = m < g.M;
     const uint16_t* p = pick_src<uint16_t>(g, s) + a_row_off(g, ok ? m : 0) + (kl - s * g.a_cols);
 #pragma unroll
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
   } else {
     // the host guarantees a_cols % (32 * KS) == 0: a wave's k range lies in one source
     const int s = __builtin_amdgcn_readfirstlane(kwave / g.a_cols);
-    const int m = lane & 15;
+    const int m = m0 + (lane & 15);
     const bool ok = m < g.M;
     const float* p = pick_src<float>(g, s) + a_row_off(g, ok ? m : 0) + (kl - s * g.a_cols);
     float4 av[2 * KS];
@@ -315,9 +325,10 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
     }
   }
 
-  // reduction thread tid < 256 owns output (n = TN * tile + 4 * (ln / 16) + r, m = ln % 16), ln = tid / 4
+  // reduction thread tid < 256 owns output (n = TN * tile + 4 * (ln / 16) + r, m = m0 + ln % 16), ln = tid / 4
   const int ln = tid >> 2;
   const int mo = ln & 15, no = 4 * (ln >> 4) + (tid & 3);
+  const int mg = m0 + mo;                     // its activation row
   Top2 best{-INFINITY, 0x7fffffff, -INFINITY};
   SampleStat ss = sstat_empty();
   const bool staged = EP != RK_TOP2 && g.stage_tiles > 0;
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
     float su = 0.5f;                          // this thread's sampling uniform, fetched before the MFMAs
     if constexpr (SAMPLE) {
       const int n = (ub / S) * TN + no;
-      if (tid < 256 && mo < g.M && n < g.N) su = g.su[static_cast<int64_t>(mo) * g.N + n];
+      if (tid < 256 && mg < g.M && n < g.N) su = g.su[static_cast<int64_t>(mg) * g.N + n];
     }
     f32x4_t acc[T];
 #pragma unroll
@@ -368,10 +379,10 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
           vu += red[buf][w][0][tid + 128];
         }
         const int f = (ub / S) * TN + no;      // no < 8 for tid < 128
-        if (mo < g.M && f < g.N) {
+        if (mg < g.M && f < g.N) {
           const float sv = vg / (1.0f + expf(-vg)) * vu;
           if (staged) lt_all[q * 128 + mo * 8 + no] = sv;
-          else g.part[static_cast<int64_t>(mo) * g.N + f] = sv;
+          else g.part[static_cast<int64_t>(mg) * g.N + f] = sv;
         }
       }
     } else if (tid < 256) {
@@ -383,20 +394,20 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
 #pragma unroll 4
           for (int w = 0; w < kRkWaves; ++w) v += red[buf][w][t][tid];
           const int n = (uu / S) * TN + no;
-          if (mo < g.M && n < g.N) {
+          if (mg < g.M && n < g.N) {
             if constexpr (TOP2) {
-              if (logits != nullptr) logits[static_cast<int64_t>(mo) * g.N + n] = v;
+              if (logits != nullptr) logits[static_cast<int64_t>(mg) * g.N + n] = v;
               best = top2_push(best, v, n);
             } else if constexpr (SAMPLE) {
               if (staged) lt_all[q * 256 + mo * 16 + no] = v;
-              else logits[static_cast<int64_t>(mo) * g.N + n] = v;
+              else logits[static_cast<int64_t>(mg) * g.N + n] = v;
               const float x = v * g.inv_t;
               sstat_push_lse(ss, x);
               sstat_push_key(ss, x + gumbel_noise(su), n);
             } else if (staged) {
               lt_all[(q * T + t) * 256 + mo * 16 + no] = v;
             } else {
-              g.part[(static_cast<int64_t>(sp) * g.M + mo) * g.N + n] = v;
+              g.part[(static_cast<int64_t>(sp) * g.M + mg) * g.N + n] = v;
             }
           }
         }
@@ -418,11 +429,11 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
       }
     }
     __syncthreads();
-    if (tid < 16 && tid < g.M) {
+    if (tid < 16 && m0 + tid < g.M) {
       Top2 t{tv1[0][tid], ti1[0][tid], tv2[0][tid]};
 #pragma unroll
       for (int w = 1; w < 4; ++w) t = top2_merge(t, Top2{tv1[w][tid], ti1[w][tid], tv2[w][tid]});
-      float* o = top2 + (static_cast<int64_t>(blockIdx.x) * g.M + tid) * 3;
+      float* o = top2 + (static_cast<int64_t>(u0) * g.M + m0 + tid) * 3;
       o[0] = t.v1;
       o[1] = __int_as_float(t.i1);
       o[2] = t.v2;
@@ -436,11 +447,11 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
       if ((lane & 3) == 0) sst[wave][lane >> 2] = sstat_pack(ss);
     }
     __syncthreads();
-    if (tid < 16 && tid < g.M) {
+    if (tid < 16 && m0 + tid < g.M) {
       SampleStat t = sstat_unpack(sst[0][tid]);
 #pragma unroll
       for (int w = 1; w < 4; ++w) t = sstat_merge(t, sstat_unpack(sst[w][tid]));
-      reinterpret_cast<float4*>(top2)[static_cast<int64_t>(blockIdx.x) * g.M + tid] = sstat_pack(t);
+      reinterpret_cast<float4*>(top2)[static_cast<int64_t>(u0) * g.M + m0 + tid] = sstat_pack(t);
     }
   }
   if (staged) {
@@ -453,8 +464,8 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
     for (int i = tid; i < nslots * PPT; i += 64 * kRkWaves) {
       const int slot = i / PPT, r = (i % PPT) / PPR, c4 = 4 * (i % PPR);
       const int n0 = ((u0 + P * slot) / S) * kOutCols;
-      if (r < g.M) {
-        float* dst = out + static_cast<int64_t>(r) * g.N + n0 + c4;
+      if (m0 + r < g.M) {
+        float* dst = out + static_cast<int64_t>(m0 + r) * g.N + n0 + c4;
         const float* src = &lt_all[slot * (16 * kOutCols) + r * kOutCols + c4];
         if ((g.N & 3) == 0 && n0 + c4 + 3 < g.N) {
           *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
@@ -1071,33 +1082,68 @@ hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p,
   }
 }
 
-// Register-K plan: <= 16 rows, K a multiple of 16 waves x KS k-steps (KS = 8,
+// Rows beyond 16 run as C = ceil(M / 16) chunks on C workgroups per unit
+// group.  The chunks of a unit group read the same weight tiles at the same
+// time, so the launch has only 1 / C as many distinct weight streams in flight
+// (each latency-bound, as one stream per CU is at 16 rows): measured on the
+// 151936 x 4096 LM head, 28 rows (C = 2) take 268 us against 296 us for the
+// streaming kernel and its top-2 pass, but C = 4 takes 521 us and C = 8 1022
+// us.  So the tall forms (LM head, gate/up with SwiGLU) take up to 32 rows and
+// the short split-K form stays at 16.
+int rk_max_rows(bool tall) {
+  const int r = env_int("DFLASH_RK_MAX_ROWS", tall ? kRkMaxRowsTall : 16);
+  return r < 16 ? 16 : (r > kRkMaxRows ? kRkMaxRows : r / 16 * 16);
+}
+
+// Unit groups P of a register-K launch over `units` units (a multiple of S),
+// C chunks: one workgroup per CU in all, P a multiple of S (a workgroup keeps
+// its K range) and, when C > 1, of 8 (the chunk layout); every unit group must
+// own a unit.  0: the shape does not fit.
+static int rk_unit_groups(int S, int C, long units) {
+  const int cus = device_cus();
+  if (C == 1) {
+    int grid = cus / S * S;
+    if (grid > kRkMaxGrid) grid = kRkMaxGrid / S * S;
+    if (grid < S) grid = S;
+    return static_cast<int>(units < grid ? units : grid);
+  }
+  int a = S, b = 8;
+  while (b != 0) { const int t = a % b; a = b; b = t; }
+  const int step = S / a * 8;                 // lcm(S, 8)
+  int grid = cus / C / step * step;
+  if (grid < step) grid = step;
+  if (grid > kRkMaxGrid || grid > units) return 0;
+  return grid;
+}
+
+// Register-K plan: 16-row chunks, K a multiple of 16 waves x KS k-steps (KS = 8,
 // else 4), at most one workgroup per CU (the grid is a multiple of the split
 // count so that a workgroup keeps its K range).  Only worth it when the weight
 // is tall: every workgroup reads the whole activation block once (M x K x 4
 // bytes from L2), which must stay small against its share of W.
 GemmPlan plan_gemm_rk(int M, int N, int K, bool top2) {
   GemmPlan p;
-  if (M < 1 || M > 16 || N < kRkMinN || env_int("DFLASH_GEMM_NO_RK", 0) != 0) return p;
+  if (M < 1 || M > rk_max_rows(true) || N < kRkMinN || env_int("DFLASH_GEMM_NO_RK", 0) != 0) return p;
   int ks = 0;
   if (K % (32 * 8 * kRkWaves) == 0) ks = 8;
   else if (K % (32 * 4 * kRkWaves) == 0) ks = 4;
   if (ks == 0) return p;
   const int S = K / (32 * ks * kRkWaves);
   if (top2 && S != 1) return p;
+  const int C = (M + 15) / 16;
+  const int ntiles = (N + 15) / 16;
+  const int grid = rk_unit_groups(S, C, static_cast<long>(S) * ntiles);
+  if (grid == 0) return p;
   p.rk = true;
   p.ks = ks;
   p.S = S;
   p.MT = 16;
   p.mtiles = 1;
-  p.ntiles = (N + 15) / 16;
+  p.mr = C;
+  p.ntiles = ntiles;
   p.cps = ks * kRkWaves;
   p.nchunks = K / 32;
-  const long units = static_cast<long>(S) * p.ntiles;
-  int grid = device_cus() / S * S;
-  if (grid > kRkMaxGrid) grid = kRkMaxGrid / S * S;
-  if (grid < S) grid = S;
-  p.grid = static_cast<int>(units < grid ? units : grid);
+  p.grid = grid;
   p.part_floats = top2 ? 0 : static_cast<size_t>(S) * M * N;
   return p;
 }
@@ -1108,26 +1154,28 @@ GemmPlan plan_gemm_rk(int M, int N, int K, bool top2) {
 // weight pieces stays deep.
 GemmPlan plan_gemm_rk_short(int M, int N, int K) {
   GemmPlan p;
-  if (M < 1 || M > 16 || K % (32 * 2 * kRkWaves) != 0 || env_int("DFLASH_GEMM_NO_RK", 0) != 0) return p;
+  if (M < 1 || M > rk_max_rows(false) || K % (32 * 2 * kRkWaves) != 0 || env_int("DFLASH_GEMM_NO_RK", 0) != 0) return p;
+  const int S = K / (32 * 2 * kRkWaves);
+  const int C = (M + 15) / 16;
+  const int ntiles = (N + 15) / 16;
+  const int grid = rk_unit_groups(S, C, static_cast<long>(S) * ntiles);
+  if (grid == 0) return p;
   p.rk = true;
   p.ks = 2;
-  p.S = K / (32 * 2 * kRkWaves);
+  p.S = S;
   p.MT = 16;
   p.mtiles = 1;
-  p.ntiles = (N + 15) / 16;
+  p.mr = C;
+  p.ntiles = ntiles;
   p.cps = 2 * kRkWaves;
   p.nchunks = K / 32;
-  const long units = static_cast<long>(p.S) * p.ntiles;
-  int grid = device_cus() / p.S * p.S;
-  if (grid > kRkMaxGrid) grid = kRkMaxGrid / p.S * p.S;
-  if (grid < p.S) grid = p.S;
-  p.grid = static_cast<int>(units < grid ? units : grid);
+  p.grid = grid;
   p.part_floats = static_cast<size_t>(p.S) * M * N;
   return p;
 }
 
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
-  if ((ak == A_F32_SPLIT || ak == A_BF16) && M <= 16) {
+  if ((ak == A_F32_SPLIT || ak == A_BF16) && M <= rk_max_rows(true)) {
     const GemmPlan r = plan_gemm_rk(M, N, K, false);
     if (r.rk && r.S == 1) return r;
     const GemmPlan q = plan_gemm_rk_short(M, N, K);
@@ -1156,13 +1204,18 @@ hipError_t rk_launch(GemmArgs a, const GemmPlan& p, float* top2, float* logits, 
   }
   const size_t tile_bytes = (EP == RK_SWIGLU ? 8 : 16) * 16 * sizeof(float);
   const int slots = (p.S * p.ntiles + p.grid - 1) / p.grid;   // units a workgroup handles
+  // the chunk layout: M rows in mr chunks, and unit groups in whole XCD rounds
+  if (p.mr < 1 || (p.mr - 1) * 16 >= a.M || p.mr * 16 < a.M || (p.mr > 1 && p.grid % 8 != 0))
+    return hipErrorInvalidValue;
   size_t shm = 0;
   a.stage_tiles = 0;
+  a.rchunks = p.mr;
   if (EP != RK_TOP2 && static_cast<size_t>(slots) * tile_bytes <= static_cast<size_t>(stage_cap)) {
     a.stage_tiles = slots;
     shm = static_cast<size_t>(slots) * tile_bytes;
   }
-  hipLaunchKernelGGL((gemm_rk_kernel<KS, EP, T, AK>), dim3(p.grid), dim3(64 * kRkWaves), shm, st, a, top2, logits);
+  hipLaunchKernelGGL((gemm_rk_kernel<KS, EP, T, AK>), dim3(p.grid * p.mr), dim3(64 * kRkWaves), shm, st, a, top2,
+                     logits);
   return hipGetLastError();
 }
 
@@ -1208,7 +1261,10 @@ GemmPlan plan_gemm_rk_swiglu(int M, int F, int K) {
   GemmPlan p = plan_gemm_rk(M, 2 * F, K, true);   // a single K split
   if (!p.rk) return p;
   p.ntiles = (F + 7) / 8;
-  if (p.grid > p.ntiles) p.grid = p.ntiles;
+  if (p.grid > p.ntiles) {
+    if (p.mr > 1) return GemmPlan{};   // unit groups stay a multiple of 8
+    p.grid = p.ntiles;
+  }
   return p;
 }
 

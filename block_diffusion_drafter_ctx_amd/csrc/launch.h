@@ -33,6 +33,7 @@ struct GemmArgs {
   const float* su;            // LM-head sampling epilogue: uniforms [M][N] in (0, 1)
   float inv_t;                // LM-head sampling epilogue: 1 / temperature
   int32_t stage_tiles;        // LM-head sampling epilogue: logits tiles held in LDS per workgroup (set by the launcher)
+  int32_t rchunks;            // register-K: 16-row chunks of A, one workgroup each (set by the launcher)
 };
 
 // exact bf16 A; fp32 A split hi/lo on the fly; or A given as pre-split bf16
@@ -42,8 +43,9 @@ enum GemmAKind { A_BF16 = 0, A_F32_SPLIT = 1, A_BF16_HILO = 2 };
 struct GemmPlan {
   int MT = 16, mtiles = 1, ntiles = 1, nchunks = 1, cps = 1, S = 1, waves = 8, grid = 1;
   bool tiled = false;   // LDS-tiled kernel for many activation rows
-  bool rk = false;      // register-K kernel (<= 16 rows, tall weight)
+  bool rk = false;      // register-K kernel (16-row chunks, tall weight)
   int ks = 8;           // register-K: k steps per wave
+  int mr = 1;           // register-K: 16-row chunks (the launch has mr * grid workgroups)
   size_t part_floats = 0;
 };
 
@@ -59,10 +61,14 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak);
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide);
 hipError_t launch_gemm_mfma(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, hipStream_t st);
 
-// Register-K kernel for <= 16 activation rows (fp32 split hi/lo, or exact bf16
-// with ak = A_BF16) against a bf16 weight; plan.rk is false when the shape does
-// not qualify.  top2 = true asks for the LM-head epilogue (a single K split).
-constexpr int kRkMaxGrid = 1024;   // bound on register-K workgroups (top-2 workspace rows)
+// Register-K kernel for up to rk_max_rows(tall) activation rows (fp32 split
+// hi/lo, or exact bf16 with ak = A_BF16) against a bf16 weight, 16 rows per
+// workgroup; plan.rk is false when the shape does not qualify.  top2 = true
+// asks for the LM-head epilogue (a single K split).
+constexpr int kRkMaxGrid = 1024;   // bound on register-K unit groups (top-2 workspace rows)
+constexpr int kRkMaxRows = 128;    // largest row count the register-K form may be set to take
+constexpr int kRkMaxRowsTall = 32; // default for the tall forms (a single K split); the short form takes 16
+int rk_max_rows(bool tall);
 GemmPlan plan_gemm_rk(int M, int N, int K, bool top2);
 // top2 == nullptr: store part[s][m][n].  Otherwise write the per-workgroup top-2
 // of every row to top2 [p.grid][M][3] (value, index bits, runner-up) and, when

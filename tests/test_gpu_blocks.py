@@ -120,3 +120,13 @@ def test_blocks_full_qwen_shape():
     anchors = sorted(rng.integers(1024, 2049, 8).tolist())
     log(f"anchored blocks, full shape, anchors {anchors}")
     Blocks(cfg, [(0, a) for a in anchors], 16).run_blocks()
+
+
+def test_blocks_max_per_call():
+    # 64 blocks (the most one call takes) over two sequences, anchors drawn
+    # uniformly in [0, len]: up to 33 blocks share one sequence's scratch region
+    rng = np.random.default_rng(7)
+    ctx = (37, 300)
+    blocks = [(int(s), int(rng.integers(0, ctx[s] + 1))) for s in rng.integers(0, 2, 64)]
+    log(f"anchored blocks, 64 per call, {sum(1 for s, _ in blocks if s == 1)} in sequence 1")
+    Blocks(small(cid=135, ctx=ctx), blocks, 16).run_blocks()

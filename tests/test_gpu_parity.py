@@ -83,6 +83,25 @@ def test_register_k_shapes():
     Workload(shrink(cfg, cid=112, B=2, ctx=(40, 300), gammas=(7,)), 7, 1, override=True).run()
 
 
+def test_register_k_row_chunks(monkeypatch):
+    # more than 16 activation rows on the register-K kernel, one workgroup per
+    # 16-row chunk.  By default the tall forms take up to 32 rows: 2 sequences
+    # of 13 give 26 block rows (gate/up with SwiGLU) and 24 LM-head rows (top-2),
+    # two chunks, the second partial.
+    log("register-K row chunks: D=2048, 2F=16384, V=20001, 26 block / 24 LM-head rows")
+    cfg = small(cid=113, D=2048, L=1, Hq=16, Hkv=4, d=128, F=8192, V=20001, B=2, ctx=(256, 7), gammas=(13,),
+                iters=2)
+    Workload(cfg, 13, 2, override=True).run()
+    # every form allowed up to 128 rows: 39 block rows and 36 LM-head rows
+    # (three chunks), 48 appended rows through the fuse and inject GEMMs, and 8
+    # sequences of 16 (128 block rows, 120 LM-head rows: eight chunks)
+    monkeypatch.setenv("DFLASH_RK_MAX_ROWS", "128")
+    log("register-K row chunks up to 128 rows: 39 / 36 / 48 rows, then 128 / 120")
+    Workload(shrink(cfg, cid=115, B=3, ctx=(256, 40, 7)), 13, 2, override=True).run()
+    cfg8 = shrink(cfg, cid=114, B=8, ctx=(256, 40, 7, 0, 100, 31, 64, 200), gammas=(16,), iters=1)
+    Workload(cfg8, 16, 1).run()
+
+
 def test_config1_f32():
     cfg = CONFIGS[1]
     log("config 1: tiny fp32 drafter")

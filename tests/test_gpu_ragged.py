@@ -170,3 +170,13 @@ def test_ragged_full_batch16():
     gammas = [4, 8, 16, 32] * 4
     log(f"ragged full batch16: gammas {gammas}")
     Ragged(cfg, gammas).run_ragged()
+
+
+def test_ragged_max_batch():
+    # 64 sequences (the most one call takes) with block lengths drawn over the
+    # whole allowed range [2, 33] and contexts from empty to 200 rows
+    rng = np.random.default_rng(126)
+    ctx = tuple(int(c) for c in rng.integers(0, 201, 64))
+    gammas = [int(g) for g in rng.integers(2, 34, 64)]
+    log(f"ragged 64 sequences: gammas {gammas[:8]}..., contexts {ctx[:8]}...")
+    Ragged(small(cid=126, B=64, ctx=ctx), gammas).run_ragged()

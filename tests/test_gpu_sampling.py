@@ -126,6 +126,7 @@ DRAFT_CASES = [
     ("bf16_rk_m15", 2, dict(D=2048, V=20000, B=1), 16, 1.0),
     ("bf16_rk_m16_ragged_v", 2, dict(D=2048, V=20001, B=1), 17, 0.8),
     ("bf16_rk_m1", 2, dict(D=2048, V=20000, B=1), 2, 1.3),
+    ("bf16_rk_chunks_m30", 2, dict(D=2048, V=20001, B=2), 16, 1.0),
     ("bf16_stream_m60", 2, dict(D=2048, V=20000, B=4), 16, 1.0),
     ("bf16_tiled_m75_ragged_v", 2, dict(D=2048, V=20001, B=5), 16, 1.0),
     ("bf16_small_v", 2, dict(D=256, V=1000, B=2), 16, 0.5),
