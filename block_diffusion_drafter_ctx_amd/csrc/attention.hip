@@ -573,7 +573,9 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
     float O = 0.f;
 #pragma unroll 8
     for (int s = 0; s < ns; ++s) O += wts[s] * a.part_o[(static_cast<int64_t>(it0 + s) * a.Rpad + r) * a.d + c];
-    a.o_out[(static_cast<int64_t>(m) * a.Hq + h) * a.d + c] = O * inv_l;
+    const int64_t oi = (static_cast<int64_t>(m) * a.Hq + h) * a.d + c;
+    if (a.o_hi != nullptr) split1(O * inv_l, a.o_hi[oi], a.o_lo[oi]);
+    else a.o_out[oi] = O * inv_l;
   }
 }
 

@@ -56,6 +56,19 @@ __device__ __forceinline__ void split8(const float* x, uint4& hi, uint4& lo) {
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
+// The same split for 4 values (two packed pairs each) and for one value.
+__device__ __forceinline__ void split4(const float4& x, uint2& hi, uint2& lo) {
+  const uint32_t h0 = pack_bf16x2(x.x, x.y), h1 = pack_bf16x2(x.z, x.w);
+  hi = make_uint2(h0, h1);
+  lo = make_uint2(pack_bf16x2(x.x - __uint_as_float(h0 << 16), x.y - __uint_as_float(h0 & 0xffff0000u)),
+                  pack_bf16x2(x.z - __uint_as_float(h1 << 16), x.w - __uint_as_float(h1 & 0xffff0000u)));
+}
+__device__ __forceinline__ void split1(float x, uint16_t& hi, uint16_t& lo) {
+  const uint32_t h = pack_bf16x2(x, 0.f);
+  hi = static_cast<uint16_t>(h & 0xffffu);
+  lo = static_cast<uint16_t>(pack_bf16x2(x - __uint_as_float(h << 16), 0.f) & 0xffffu);
+}
+
 // D += A (16 rows x 32 k) * B (32 k x 16 cols).  Lane l supplies A row (l % 16)
 // and B column (l % 16), k-slots 8*(l/16)..+7 of each; D lane l holds rows
 // 4*(l/16)+r, column l%16 (r = 0..3).  The k-slot -> k map only has to agree

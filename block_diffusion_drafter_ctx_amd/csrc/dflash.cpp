@@ -210,16 +210,29 @@ size_t act_planes_bytes(const ActPlan& a, int M, int K) {
   return a.kind == A_BF16_HILO ? 2 * align_up(static_cast<size_t>(M) * K * 2) : 0;
 }
 
+// Where the hi / lo planes of an M x K activation block sit in `planes` (the
+// lo plane after the hi plane, 256-byte aligned).
+HiLo act_planes(const ActPlan& a, void* planes, int M, int K) {
+  if (a.kind != A_BF16_HILO) return HiLo{};
+  HiLo pl;
+  pl.hi = static_cast<uint16_t*>(planes);
+  pl.lo = reinterpret_cast<uint16_t*>(static_cast<char*>(planes) + align_up(static_cast<size_t>(M) * K * 2));
+  return pl;
+}
+
 // g addresses fp32 activations (any row mapping of one source); planes:
-// act_planes_bytes of scratch.
-hipError_t launch_act_gemm(GemmArgs g, const ActPlan& a, void* planes, hipStream_t s) {
+// act_planes_bytes of scratch.  ready: the producer of A has already written
+// the planes (act_planes) in place of g's fp32 rows.
+hipError_t launch_act_gemm(GemmArgs g, const ActPlan& a, void* planes, hipStream_t s, bool ready = false) {
   if (a.kind == A_BF16_HILO) {
-    uint16_t* hi = static_cast<uint16_t*>(planes);
-    uint16_t* lo = reinterpret_cast<uint16_t*>(static_cast<char*>(planes) +
-                                               align_up(static_cast<size_t>(g.M) * g.K * 2));
-    const hipError_t e = launch_split_hilo(static_cast<const float*>(g.a_src[0]), g.a_ld, g.M, g.K, hi, lo, s,
-                                           g.a_rg, g.a_gs);
-    if (e != hipSuccess) return e;
+    const HiLo pl = act_planes(a, planes, g.M, g.K);
+    uint16_t* hi = pl.hi;
+    uint16_t* lo = pl.lo;
+    if (!ready) {
+      const hipError_t e = launch_split_hilo(static_cast<const float*>(g.a_src[0]), g.a_ld, g.M, g.K, hi, lo, s,
+                                             g.a_rg, g.a_gs);
+      if (e != hipSuccess) return e;
+    }
     for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = hi;
     g.a_lo = lo;
     g.a_cols = g.K;
@@ -649,8 +662,22 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
   hipStream_t s = as_stream(stream);
   auto wp = [&](const void* p, int64_t elems) { return static_cast<const char*>(p) + elems * es; };
 
-  // GEMM on fp32 activations (rows = block rows), returns the split count.
-  auto gemm = [&](const float* A, int K, const void* W, int N, int* S, int role) -> hipError_t {
+  // Activation planes: when a GEMM takes the tiled kernel (many rows) its
+  // producer (embedding / residual norm, attention combine, SwiGLU) writes the
+  // bf16 hi / lo planes of its output directly, and the GEMM skips its split.
+  const ActPlan ap_qkv = bf ? plan_act(M, nqkv, D, false) : ActPlan{};
+  const ActPlan ap_o = bf ? plan_act(M, D, hd, false) : ActPlan{};
+  const ActPlan ap_gu = bf ? plan_act(M, 2 * F, D, false) : ActPlan{};
+  const ActPlan ap_dn = bf ? plan_act(M, D, F, false) : ActPlan{};
+  void* planes = base + lay.planes;
+  const HiLo pl_qkv = bf ? act_planes(ap_qkv, planes, M, D) : HiLo{};
+  const HiLo pl_o = bf ? act_planes(ap_o, planes, M, hd) : HiLo{};
+  const HiLo pl_gu = bf ? act_planes(ap_gu, planes, M, D) : HiLo{};
+  const HiLo pl_dn = bf ? act_planes(ap_dn, planes, M, F) : HiLo{};
+
+  // GEMM on fp32 activations (rows = block rows), returns the split count;
+  // ready: A's planes were written by its producer.
+  auto gemm = [&](const float* A, int K, const void* W, int N, int* S, int role, bool ready) -> hipError_t {
     GemmArgs g{};
     for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = A;
     g.a_cols = K;
@@ -673,7 +700,7 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
     const ActPlan ap = plan_act(M, N, K, false);
     *S = ap.p.S;
     const int ps = prof_begin(role, s);
-    const hipError_t e = launch_act_gemm(g, ap, base + lay.planes, s);
+    const hipError_t e = launch_act_gemm(g, ap, planes, s, ready);
     prof_end(ps, s);
     return e;
   };
@@ -689,10 +716,12 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
   const size_t layer_elems = static_cast<size_t>(cache->B) * Hkv * cache->cap * d;
 
   const GemmPlan swiglu_rk = bf ? plan_gemm_rk_swiglu(M, F, D) : GemmPlan{};
-  DF_HIP(launch_embed_norm(block_tokens, embed_override, w->embed, dims->V, M, D, w->g_attn, dims->rms_eps, h, a, bf, s));
+  DF_HIP(launch_embed_norm(block_tokens, embed_override, w->embed, dims->V, M, D, w->g_attn, dims->rms_eps, h, a, bf, s,
+                           pl_qkv));
   for (int l = 0; l < L; ++l) {
     int S = 1;
-    DF_HIP(gemm(a, D, wp(w->w_qkv, static_cast<int64_t>(l) * nqkv * D), nqkv, &S, DFLASH_PROF_QKV));
+    DF_HIP(gemm(a, D, wp(w->w_qkv, static_cast<int64_t>(l) * nqkv * D), nqkv, &S, DFLASH_PROF_QKV,
+                pl_qkv.hi != nullptr));
     ScatterArgs sa{};
     sa.part = part;
     sa.S = S;
@@ -723,6 +752,8 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
     at.part_o = reinterpret_cast<float*>(base + lay.att_o);
     at.part_ml = reinterpret_cast<float*>(base + lay.att_ml);
     at.o_out = o;
+    at.o_hi = pl_o.hi;
+    at.o_lo = pl_o.lo;
     at.B = B;
     at.Hq = Hq;
     at.Hkv = Hkv;
@@ -741,8 +772,9 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
     const int pa = prof_begin(DFLASH_PROF_ATTENTION, s);
     DF_HIP(launch_attention(at, ap, bf, cbf, s, pa >= 0 ? g_prof.stop[pa] : nullptr));
 
-    DF_HIP(gemm(o, hd, wp(w->w_o, static_cast<int64_t>(l) * D * hd), D, &S, DFLASH_PROF_O));
-    DF_HIP(launch_residual_norm(part, S, M, D, h, wp(w->g_ffn, static_cast<int64_t>(l) * D), dims->rms_eps, a, bf, s));
+    DF_HIP(gemm(o, hd, wp(w->w_o, static_cast<int64_t>(l) * D * hd), D, &S, DFLASH_PROF_O, pl_o.hi != nullptr));
+    DF_HIP(launch_residual_norm(part, S, M, D, h, wp(w->g_ffn, static_cast<int64_t>(l) * D), dims->rms_eps, a, bf, s,
+                                swiglu_rk.rk ? HiLo{} : pl_gu));
     if (swiglu_rk.rk) {
       // gate/up GEMM with SwiGLU in its epilogue
       GemmArgs g{};
@@ -761,14 +793,16 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
       prof_end(ps, s);
       DF_HIP(e);
     } else {
-      DF_HIP(gemm(a, D, wp(w->w_gateup, static_cast<int64_t>(l) * 2 * F * D), 2 * F, &S, DFLASH_PROF_GATEUP));
-      DF_HIP(launch_swiglu(part, S, M, F, sw, s));
+      DF_HIP(gemm(a, D, wp(w->w_gateup, static_cast<int64_t>(l) * 2 * F * D), 2 * F, &S, DFLASH_PROF_GATEUP,
+                  pl_gu.hi != nullptr));
+      DF_HIP(launch_swiglu(part, S, M, F, sw, s, pl_dn));
     }
-    DF_HIP(gemm(sw, F, wp(w->w_down, static_cast<int64_t>(l) * D * F), D, &S, DFLASH_PROF_DOWN));
+    DF_HIP(gemm(sw, F, wp(w->w_down, static_cast<int64_t>(l) * D * F), D, &S, DFLASH_PROF_DOWN,
+                pl_dn.hi != nullptr && !swiglu_rk.rk));
     const bool last = l + 1 == L;
     DF_HIP(launch_residual_norm(part, S, M, D, h,
                                 last ? w->g_final : wp(w->g_attn, static_cast<int64_t>(l + 1) * D),
-                                dims->rms_eps, last ? h_final : a, bf, s));
+                                dims->rms_eps, last ? h_final : a, bf, s, last ? HiLo{} : pl_qkv));
   }
   return ok();
 }

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(ScatterArgs a) {
 // ------------------------------------------------------------- residual_norm
 template <typename T>
 __global__ __launch_bounds__(1024) void residual_norm_kernel(const float* part, int S, int M, int D, float* h,
-                                                             const void* g, float eps, float* a_out) {
+                                                             const void* g, float eps, float* a_out, HiLo pl) {
   __shared__ float red[16];
   const int m = blockIdx.x;
   const int64_t stride = static_cast<int64_t>(M) * D;
@@ -173,20 +173,32 @@ __global__ __launch_bounds__(1024) void residual_norm_kernel(const float* part, 
 #pragma unroll
   for (int j = 0; j < kRowMaxGroups; ++j) {
     const int c = 4 * (threadIdx.x + j * blockDim.x);
-    if (c < D)
-      *reinterpret_cast<float4*>(a_out + static_cast<int64_t>(m) * D + c) = f4scale(v[j], ld4<T>(g, c), inv);
+    if (c < D) {
+      const float4 y = f4scale(v[j], ld4<T>(g, c), inv);
+      const int64_t o = static_cast<int64_t>(m) * D + c;
+      if (pl.hi != nullptr) {
+        uint2 hh, ll;
+        split4(y, hh, ll);
+        *reinterpret_cast<uint2*>(pl.hi + o) = hh;
+        *reinterpret_cast<uint2*>(pl.lo + o) = ll;
+      } else {
+        *reinterpret_cast<float4*>(a_out + o) = y;
+      }
+    }
   }
 }
 
 // ------------------------------------------------------------- swiglu
-__global__ __launch_bounds__(256) void swiglu_kernel(const float* part, int S, int M, int F, float* s_out) {
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* part, int S, int M, int F, float* s_out, HiLo pl) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= static_cast<int64_t>(M) * F) return;
   const int m = static_cast<int>(i / F), f = static_cast<int>(i % F);
   const int64_t stride = static_cast<int64_t>(M) * 2 * F;
   const float gt = sum_parts(part, S, stride, static_cast<int64_t>(m) * 2 * F + f);
   const float up = sum_parts(part, S, stride, static_cast<int64_t>(m) * 2 * F + F + f);
-  s_out[i] = gt / (1.0f + expf(-gt)) * up;
+  const float v = gt / (1.0f + expf(-gt)) * up;
+  if (pl.hi != nullptr) split1(v, pl.hi[i], pl.lo[i]);
+  else s_out[i] = v;
 }
 
 // ------------------------------------------------------------- embed_norm
@@ -196,7 +208,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* part, int S, i
 template <typename T>
 __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* tok, const float* ov, const void* embed,
                                                           int V, int D, const void* g, float eps, float* h,
-                                                          float* a) {
+                                                          float* a, HiLo pl) {
   __shared__ float red[16];
   const int m = blockIdx.x;
   const int64_t src = ov != nullptr ? 0 : static_cast<int64_t>(min(max(tok[m], 0), V - 1)) * D;
@@ -216,7 +228,18 @@ __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* tok, co
 #pragma unroll
   for (int j = 0; j < kRowMaxGroups; ++j) {
     const int c = 4 * (threadIdx.x + j * blockDim.x);
-    if (c < D) *reinterpret_cast<float4*>(a + static_cast<int64_t>(m) * D + c) = f4scale(v[j], ld4<T>(g, c), inv);
+    if (c < D) {
+      const float4 y = f4scale(v[j], ld4<T>(g, c), inv);
+      const int64_t o = static_cast<int64_t>(m) * D + c;
+      if (pl.hi != nullptr) {
+        uint2 hh, ll;
+        split4(y, hh, ll);
+        *reinterpret_cast<uint2*>(pl.hi + o) = hh;
+        *reinterpret_cast<uint2*>(pl.lo + o) = ll;
+      } else {
+        *reinterpret_cast<float4*>(a + o) = y;
+      }
+    }
   }
 }
 
@@ -386,24 +409,30 @@ hipError_t launch_scatter_kv(const ScatterArgs& a, bool bf16_cache, hipStream_t 
 }
 
 hipError_t launch_residual_norm(const float* part, int S, int M, int D, float* h, const void* g, float eps,
-                                float* a_out, bool bf16, hipStream_t st) {
+                                float* a_out, bool bf16, hipStream_t st, HiLo pl) {
   const dim3 block(row_threads(D));
-  if (bf16) hipLaunchKernelGGL(residual_norm_kernel<uint16_t>, dim3(M), block, 0, st, part, S, M, D, h, g, eps, a_out);
-  else hipLaunchKernelGGL(residual_norm_kernel<float>, dim3(M), block, 0, st, part, S, M, D, h, g, eps, a_out);
+  if ((pl.hi == nullptr) != (pl.lo == nullptr) || (pl.hi != nullptr && !bf16)) return hipErrorInvalidValue;
+  if (bf16)
+    hipLaunchKernelGGL(residual_norm_kernel<uint16_t>, dim3(M), block, 0, st, part, S, M, D, h, g, eps, a_out, pl);
+  else hipLaunchKernelGGL(residual_norm_kernel<float>, dim3(M), block, 0, st, part, S, M, D, h, g, eps, a_out, pl);
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu(const float* part, int S, int M, int F, float* s_out, hipStream_t st) {
+hipError_t launch_swiglu(const float* part, int S, int M, int F, float* s_out, hipStream_t st, HiLo pl) {
+  if ((pl.hi == nullptr) != (pl.lo == nullptr)) return hipErrorInvalidValue;
   const int64_t n = static_cast<int64_t>(M) * F;
-  hipLaunchKernelGGL(swiglu_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, part, S, M, F, s_out);
+  hipLaunchKernelGGL(swiglu_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, part, S, M, F, s_out,
+                     pl);
   return hipGetLastError();
 }
 
 hipError_t launch_embed_norm(const int32_t* tok, const float* ov, const void* embed, int V, int M, int D,
-                             const void* g, float eps, float* h, float* a, bool bf16, hipStream_t st) {
+                             const void* g, float eps, float* h, float* a, bool bf16, hipStream_t st, HiLo pl) {
   const dim3 block(row_threads(D));
-  if (bf16) hipLaunchKernelGGL(embed_norm_kernel<uint16_t>, dim3(M), block, 0, st, tok, ov, embed, V, D, g, eps, h, a);
-  else hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(M), block, 0, st, tok, ov, embed, V, D, g, eps, h, a);
+  if ((pl.hi == nullptr) != (pl.lo == nullptr) || (pl.hi != nullptr && !bf16)) return hipErrorInvalidValue;
+  if (bf16)
+    hipLaunchKernelGGL(embed_norm_kernel<uint16_t>, dim3(M), block, 0, st, tok, ov, embed, V, D, g, eps, h, a, pl);
+  else hipLaunchKernelGGL(embed_norm_kernel<float>, dim3(M), block, 0, st, tok, ov, embed, V, D, g, eps, h, a, pl);
   return hipGetLastError();
 }
 

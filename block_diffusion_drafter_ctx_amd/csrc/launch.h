@@ -128,16 +128,28 @@ hipError_t launch_scatter_kv(const ScatterArgs& a, bool bf16_cache, hipStream_t 
 hipError_t launch_ctx_norm(const float* part, int S, int T, int D, const void* g, float eps,
                            void* out, bool bf16_weights, bool bf16_cache, hipStream_t st);
 
-// h[m] += sum_s part[s][m]; a[m] = g * h / sqrt(mean(h^2)+eps)   (part may be null)
+// bf16 hi / lo planes [M][K] (row-major) of an fp32 matrix, x ~= hi + lo: the
+// A operand of the tiled GEMM.  A producer given planes (hi != nullptr) writes
+// them in place of its fp32 rows, with the split the GEMM's own split pass
+// would apply to those rows.
+struct HiLo {
+  uint16_t* hi = nullptr;
+  uint16_t* lo = nullptr;
+};
+
+// h[m] += sum_s part[s][m]; a[m] = g * h / sqrt(mean(h^2)+eps)   (part may be null;
+// a as planes when pl.hi is set)
 hipError_t launch_residual_norm(const float* part, int S, int M, int D, float* h, const void* g,
-                                float eps, float* a_out, bool bf16, hipStream_t st);
+                                float eps, float* a_out, bool bf16, hipStream_t st, HiLo pl = HiLo{});
 
-// s[m][f] = silu(sum_s part[s][m][f]) * sum_s part[s][m][F+f]
-hipError_t launch_swiglu(const float* part, int S, int M, int F, float* s_out, hipStream_t st);
+// s[m][f] = silu(sum_s part[s][m][f]) * sum_s part[s][m][F+f]   (s as planes when pl.hi is set)
+hipError_t launch_swiglu(const float* part, int S, int M, int F, float* s_out, hipStream_t st, HiLo pl = HiLo{});
 
-// h[m] = embed[tok[m]] or override[m]; a[m] = RMSNorm(h[m]; g)   (ids clamped to [0, V))
+// h[m] = embed[tok[m]] or override[m]; a[m] = RMSNorm(h[m]; g)   (ids clamped to [0, V);
+// a as planes when pl.hi is set)
 hipError_t launch_embed_norm(const int32_t* tok, const float* ov, const void* embed, int V, int M, int D,
-                             const void* g, float eps, float* h, float* a, bool bf16, hipStream_t st);
+                             const void* g, float eps, float* h, float* a, bool bf16, hipStream_t st,
+                             HiLo pl = HiLo{});
 
 // top-2 partials [ntiles][M] -> draft[m], gap[m]
 hipError_t launch_argmax_final(const float* top2, int ntiles, int M, int32_t* draft, float* gap,
@@ -220,6 +232,8 @@ struct AttnArgs {
   float* part_o;         // [items][Rpad][d]
   float* part_ml;        // [items][Rpad][2]
   float* o_out;          // [B*gamma][Hq*d]
+  uint16_t* o_hi;        // when set: o_out written as bf16 hi / lo planes instead (same layout)
+  uint16_t* o_lo;
   int32_t B, Hq, Hkv, d, cap;
   int32_t R, Rpad;       // query rows per (b, kv head): the largest G*gam[b], padded to 16
   int32_t gam[kMaxSeq];       // block rows of sequence b
