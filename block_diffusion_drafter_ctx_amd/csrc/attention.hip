@@ -29,6 +29,7 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace dflash {
@@ -654,6 +655,34 @@ AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d, cons
   // context ranges, leaving room for a block stored apart
   const int64_t sk_min = ((maxk + kMaxSplitsLds - 2) / (kMaxSplitsLds - 1) + 31) / 32 * 32;
   if (sk < sk_min) sk = sk_min;
+  // Many sequences: rounding each sequence's key count up to whole ranges can
+  // leave a few more items than CUs, and the CUs that take two items set the
+  // time (16 sequences of 1024-4096 keys: 312 items of <= 1280 keys, 135 us
+  // per layer, against ~100 us with 500-800 shorter items).  So the range
+  // length is the one of least ceil(items / CUs) * (longest item + 32 keys of
+  // start-up), searched in 32-key steps down to a quarter of the
+  // one-range-per-CU length (at most ~256 candidates); ties keep the longer
+  // ranges (fewer items, a cheaper combine).  A single long sequence keeps one
+  // range per CU.
+  if (getenv("DFLASH_ATTN_ITEMS") == nullptr) {
+    const int cus = attn_item_target();
+    const int64_t lo_keys = std::max<int64_t>(std::max<int64_t>((min_keys + 31) / 32 * 32, sk_min), (sk / 4 + 31) / 32 * 32);
+    const int64_t max_items = kAttnItemMax + 2 * static_cast<int64_t>(B) * Hkv;   // workspace bound
+    auto items_of = [&](int64_t k) {
+      int64_t n = 0;
+      for (int b = 0; b < B; ++b) n += ((nkeys[b] + k - 1) / k + (apart != nullptr && apart[b] ? 1 : 0)) * Hkv;
+      return n;
+    };
+    int64_t best_sk = sk, best_cost = -1;
+    const int64_t step = std::max<int64_t>(32, (sk - lo_keys) / 256 / 32 * 32);   // at most ~256 candidates
+    for (int64_t k = sk; k >= lo_keys; k -= step) {
+      const int64_t n = items_of(k);
+      if (n > max_items) continue;
+      const int64_t cost = (n + cus - 1) / cus * (std::min<int64_t>(k, std::max(maxk, 1)) + 32);
+      if (best_cost < 0 || cost < best_cost) best_cost = cost, best_sk = k;
+    }
+    sk = best_sk;
+  }
   p.split_keys = static_cast<int>(sk);
   p.item_off[0] = 0;
   for (int b = 0; b < B; ++b) {
