@@ -658,8 +658,22 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kern
   extern __shared__ uint4 lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = wave % (TN / WN), wm = wave / (TN / WN);
-  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
-  const int split = blockIdx.z;
+  int nt = blockIdx.x, mt = blockIdx.y, split = blockIdx.z;
+  if (g.xcd_tiles) {
+    // 1-D launch over T = S * ntiles * mtiles tiles, padded to a multiple of 8.
+    // Workgroups go to the XCDs in turn (launch slot L on XCD L % 8), so XCD
+    // x takes tile indices [x P, (x + 1) P) in launch order, the tile index
+    // running m-tile fastest, then n-tile, then split: the m-tiles that read
+    // one weight tile run together on one XCD and share its L2.
+    const int T = g.S * g.ntiles * g.mtiles;
+    const int P = (T + 7) / 8;
+    const int w = (blockIdx.x & 7) * P + (blockIdx.x >> 3);
+    if (w >= T) return;                                     // padding; uniform per workgroup
+    mt = w % g.mtiles;
+    nt = (w / g.mtiles) % g.ntiles;
+    split = w / (g.mtiles * g.ntiles);
+  }
+  const int n0 = nt * TN, m0 = mt * TM;
   const int ktiles = g.K / kTileK;
   const int kt_begin = split * g.chunks_per_split;
   const int kt_end = min(ktiles, kt_begin + g.chunks_per_split);
@@ -1014,8 +1028,16 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
 }
 
 template <int HL, int NS, int TN, int TM, int WN, int WM>
-hipError_t launch_tile_lds(const GemmArgs& a, dim3 grid, hipStream_t st) {
+hipError_t launch_tile_lds(GemmArgs a, dim3 grid, hipStream_t st) {
   const size_t lds = static_cast<size_t>(NS) * (TN + TM * HL) * 8 * sizeof(uint4);
+  a.xcd_tiles = env_int("DFLASH_TILE_XCD", 1) == 1 ? 1 : 0;   // 2: grid order (measurement)
+  if (a.xcd_tiles) {
+    a.ntiles = static_cast<int>(grid.x);
+    a.mtiles = static_cast<int>(grid.y);
+    a.S = static_cast<int>(grid.z);
+    const long T = static_cast<long>(grid.x) * grid.y * grid.z;
+    grid = dim3(static_cast<unsigned>((T + 7) / 8 * 8));
+  }
   static bool set = false;   // per instantiation
   if (!set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM>),

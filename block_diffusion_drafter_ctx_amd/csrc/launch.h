@@ -34,6 +34,7 @@ struct GemmArgs {
   float inv_t;                // LM-head sampling epilogue: 1 / temperature
   int32_t stage_tiles;        // LM-head sampling epilogue: logits tiles held in LDS per workgroup (set by the launcher)
   int32_t rchunks;            // register-K: 16-row chunks of A, one workgroup each (set by the launcher)
+  int32_t xcd_tiles;          // tiled kernel: 1-D launch in XCD-grouped tile order (set by the launcher)
 };
 
 // exact bf16 A; fp32 A split hi/lo on the fly; or A given as pre-split bf16
