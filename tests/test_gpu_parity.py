@@ -102,6 +102,29 @@ def test_register_k_row_chunks(monkeypatch):
     Workload(cfg8, 16, 1).run()
 
 
+def test_tile_order_bit_identical(monkeypatch):
+    # the tiled GEMM's XCD-grouped launch order only moves tiles between
+    # workgroups: 5 sequences of 16 (80 block rows, 75 LM-head rows, tiled
+    # GEMMs with hi/lo planes) give the same bits in grid order
+    cfg = small(cid=116, B=5, ctx=(37, 300, 1, 64, 129))
+    w = Workload(cfg, 16, 1, override=True)
+    w.ingest(w.inp.ctx_states(), list(cfg.ctx), "context")
+    ov = torch.from_numpy(w.inp.embed_override(16)).cuda()
+    outs = []
+    for order in ("1", "2"):
+        monkeypatch.setenv("DFLASH_TILE_XCD", order)
+        h = torch.empty(cfg.B, 16, cfg.D, device="cuda")
+        w.dr.draft(w.cache, None, ov, 16, h)
+        d = torch.empty(cfg.B, 15, dtype=torch.int32, device="cuda")
+        z = torch.empty(cfg.B, 15, cfg.V, device="cuda")
+        w.dr.argmax_accept(B.ARGMAX, h, cfg.B, 16, d, logits=z)
+        torch.cuda.synchronize()
+        outs.append((h.clone(), d.clone(), z.clone()))
+    log("tile order: XCD-grouped and grid order agree bit for bit")
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_config1_f32():
     cfg = CONFIGS[1]
     log("config 1: tiny fp32 drafter")
