@@ -220,10 +220,9 @@ HiLo act_planes(const ActPlan& a, void* planes, int M, int K) {
   return pl;
 }
 
-// g addresses fp32 activations (any row mapping of one source); planes:
-// act_planes_bytes of scratch.  ready: the producer of A has already written
-// the planes (act_planes) in place of g's fp32 rows.
-hipError_t launch_act_gemm(GemmArgs g, const ActPlan& a, void* planes, hipStream_t s, bool ready = false) {
+// Points g at the activation planes (splitting g's fp32 rows into them unless
+// ready) when the plan takes them; otherwise leaves g as it is.
+hipError_t prepare_act(GemmArgs& g, const ActPlan& a, void* planes, hipStream_t s, bool ready) {
   if (a.kind == A_BF16_HILO) {
     const HiLo pl = act_planes(a, planes, g.M, g.K);
     uint16_t* hi = pl.hi;
@@ -240,6 +239,15 @@ hipError_t launch_act_gemm(GemmArgs g, const ActPlan& a, void* planes, hipStream
     g.a_rg = INT_MAX;
     g.a_gs = 0;
   }
+  return hipSuccess;
+}
+
+// g addresses fp32 activations (any row mapping of one source); planes:
+// act_planes_bytes of scratch.  ready: the producer of A has already written
+// the planes (act_planes) in place of g's fp32 rows.
+hipError_t launch_act_gemm(GemmArgs g, const ActPlan& a, void* planes, hipStream_t s, bool ready = false) {
+  const hipError_t e = prepare_act(g, a, planes, s, ready);
+  if (e != hipSuccess) return e;
   return launch_gemm_mfma(g, a.kind, a.p, s);
 }
 
@@ -304,8 +312,9 @@ ArgmaxWs argmax_ws(const dflash_dims* d, int M, bool gathered = false) {
     if (pf_stream > pf) pf = pf_stream;
     w.part = c.take(pf * 4);
     w.planes = c.take(act_planes_bytes(ap, M, d->D));
-    // top-2 candidates: one row per 512-column tile, or per register-K workgroup
-    size_t t2 = static_cast<size_t>((d->V + 511) / 512);
+    // top-2 candidates: one row per 512-column reduce tile, 256-column tiled
+    // GEMM tile, or register-K workgroup
+    size_t t2 = static_cast<size_t>((d->V + 255) / 256);
     if (t2 < static_cast<size_t>(kRkMaxGrid)) t2 = kRkMaxGrid;
     w.top2 = c.take(t2 * M * 3 * 4);
   }
@@ -914,12 +923,22 @@ static dflash_status lm_head_argmax(const dflash_dims* dims, const dflash_weight
       DF_HIP(launch_argmax_final(top2, rk.grid, Mr, draft, top2_gap, s));
     } else {
       const ActPlan ap = plan_act(Mr, dims->V, D, true);
-      const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-      DF_HIP(launch_act_gemm(g, ap, base + lay.planes, s));
-      prof_end(ps, s);
-      int nt = 0;
-      DF_HIP(launch_reduce_top2(g.part, ap.p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
-      DF_HIP(launch_argmax_final(top2, nt, Mr, draft, top2_gap, s));
+      if (ap.kind == A_BF16_HILO && ap.p.S == 1) {
+        // tiled, one K split: each workgroup reduces its tile to a top-2 per
+        // row (no logits round trip unless they are asked for)
+        DF_HIP(prepare_act(g, ap, base + lay.planes, s, false));
+        const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
+        DF_HIP(launch_gemm_tiled_top2(g, ap.p, top2, logits_dbg, s));
+        prof_end(ps, s);
+        DF_HIP(launch_argmax_final(top2, ap.p.ntiles, Mr, draft, top2_gap, s));
+      } else {
+        const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
+        DF_HIP(launch_act_gemm(g, ap, base + lay.planes, s));
+        prof_end(ps, s);
+        int nt = 0;
+        DF_HIP(launch_reduce_top2(g.part, ap.p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
+        DF_HIP(launch_argmax_final(top2, nt, Mr, draft, top2_gap, s));
+      }
     }
   } else {
     float* lg = logits_dbg != nullptr ? logits_dbg : reinterpret_cast<float*>(base + lay.part);

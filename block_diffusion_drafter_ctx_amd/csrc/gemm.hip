@@ -646,8 +646,12 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
 // wave's last read of tile t.  Past the end of the K range the loads repeat the
 // last tile, so every wait has a fixed count.  A is exact bf16 (HL = 1) or the
 // hi and lo planes of an fp32 matrix (HL = 2, two MFMAs per product).
-template <int HL, int NSTAGE, int TN, int TM, int WN, int WM>
-__global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kernel(GemmArgs g) {
+// TOP2 (the LM head with a single K split): instead of partial sums the
+// workgroup writes, for every activation row, the top-2 of its TN weight rows
+// to top2[(n-tile * M + m) * 3] (value, index bits, runner-up; lower index on
+// ties), plus the logits to g.part when that is set.
+template <int HL, int NSTAGE, int TN, int TM, int WN, int WM, bool TOP2 = false>
+__global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kernel(GemmArgs g, float* top2) {
   constexpr int NW = (TN / WN) * (TM / WM);                 // waves of WN x WM outputs each
   constexpr int FN = WN / 16, FM = WM / 16;                 // 16-row fragments per wave: W, A
   constexpr int WROWS = TN, AROWS = TM * HL;                // LDS rows per stage (A: planes stacked)
@@ -790,6 +794,57 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kern
     __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmcnt<0>();                                            // the trailing repeated tiles
+
+  if constexpr (TOP2) {
+    // lane l holds rows m0 + wm WM + 16 j + l % 16 against weight rows
+    // n0 + wn WN + 16 i + 4 (l / 16) + r: a running top-2 per (j, lane), then
+    // across the four lane groups, then across the TN / WN waves of a row
+    __shared__ float tv1[TN / WN][TM], tv2[TN / WN][TM];
+    __shared__ int ti1[TN / WN][TM];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = m0 + wm * WM + j * 16 + (lane & 15);
+      Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const int n = n0 + wn * WN + i * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < g.N) t = top2_push(t, acc[i][j][r], n + r);
+        if (g.part != nullptr && m < g.M) {
+          float* out = g.part + static_cast<int64_t>(m) * g.N + n;
+          if (n + 3 < g.N && (g.N & 3) == 0) {
+            *reinterpret_cast<float4*>(out) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < g.N) out[r] = acc[i][j][r];
+          }
+        }
+      }
+      t = top2_merge(t, top2_shfl_xor(t, 16));
+      t = top2_merge(t, top2_shfl_xor(t, 32));
+      if (lane < 16) {
+        const int row = wm * WM + j * 16 + lane;
+        tv1[wn][row] = t.v1;
+        ti1[wn][row] = t.i1;
+        tv2[wn][row] = t.v2;
+      }
+    }
+    __syncthreads();
+    for (int row = threadIdx.x; row < TM; row += NW * 64) {
+      const int m = m0 + row;
+      if (m >= g.M) continue;
+      Top2 t{tv1[0][row], ti1[0][row], tv2[0][row]};
+#pragma unroll
+      for (int w = 1; w < TN / WN; ++w) t = top2_merge(t, Top2{tv1[w][row], ti1[w][row], tv2[w][row]});
+      float* o = top2 + (static_cast<int64_t>(nt) * g.M + m) * 3;
+      o[0] = t.v1;
+      o[1] = __int_as_float(t.i1);
+      o[2] = t.v2;
+    }
+    return;
+  }
 
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
@@ -1027,8 +1082,8 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
   return p;
 }
 
-template <int HL, int NS, int TN, int TM, int WN, int WM>
-hipError_t launch_tile_lds(GemmArgs a, dim3 grid, hipStream_t st) {
+template <int HL, int NS, int TN, int TM, int WN, int WM, bool TOP2 = false>
+hipError_t launch_tile_lds(GemmArgs a, dim3 grid, hipStream_t st, float* top2 = nullptr) {
   const size_t lds = static_cast<size_t>(NS) * (TN + TM * HL) * 8 * sizeof(uint4);
   a.xcd_tiles = env_int("DFLASH_TILE_XCD", 1) == 1 ? 1 : 0;   // 2: grid order (measurement)
   if (a.xcd_tiles) {
@@ -1040,13 +1095,24 @@ hipError_t launch_tile_lds(GemmArgs a, dim3 grid, hipStream_t st) {
   }
   static bool set = false;   // per instantiation
   if (!set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     set = true;
   }
-  hipLaunchKernelGGL((gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM>), grid, dim3((TN / WN) * (TM / WM) * 64), lds, st, a);
+  hipLaunchKernelGGL((gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2>), grid, dim3((TN / WN) * (TM / WM) * 64), lds,
+                     st, a, top2);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_tiled_top2(const GemmArgs& a0, const GemmPlan& p, float* top2, float* logits, hipStream_t st) {
+  constexpr TileShape T = kTileHiLo;
+  if (!p.tiled || p.S != 1 || p.MT != T.tm || top2 == nullptr || a0.a_cols % kTileK != 0 || a0.a_lo == nullptr)
+    return hipErrorInvalidValue;
+  GemmArgs a = a0;
+  a.chunks_per_split = p.cps;
+  a.part = logits;
+  return launch_tile_lds<2, T.ns, T.tn, T.tm, T.wn, T.wm, true>(a, dim3(p.ntiles, p.mtiles, 1), st, top2);
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p, hipStream_t st) {

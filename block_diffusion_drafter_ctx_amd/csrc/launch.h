@@ -62,6 +62,12 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak);
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide);
 hipError_t launch_gemm_mfma(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, hipStream_t st);
 
+// The LM head on the tiled kernel (plan from plan_gemm(.., A_BF16_HILO, ..) with
+// a single K split; a addresses the hi / lo planes): writes the top-2 of every
+// row within each n-tile to top2 [p.ntiles][M][3] (value, index bits,
+// runner-up) and, when logits != nullptr, the logits [M][N].
+hipError_t launch_gemm_tiled_top2(const GemmArgs& a, const GemmPlan& p, float* top2, float* logits, hipStream_t st);
+
 // Register-K kernel for up to rk_max_rows(tall) activation rows (fp32 split
 // hi/lo, or exact bf16 with ak = A_BF16) against a bf16 weight, 16 rows per
 // workgroup; plan.rk is false when the shape does not qualify.  top2 = true
