@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -292,6 +293,39 @@ DraftWs draft_ws(const dflash_dims* d, int B, int M, int gmax) {
   return w;
 }
 
+// The LM head of M rows (bf16 weights): the register-K kernel with the top-2
+// epilogue (up to 32 rows); else the tiled kernel over hi / lo planes with one
+// K split and the top-2 epilogue (D is a multiple of 64); else split-K
+// partials and a reduce pass.  The single split can cost more whole-K rounds
+// than the tiled planner's choice but writes no partials: on the 151936 x 4096
+// head, 60 rows take 335 us (streaming kernel + reduce: 362 + 53 us) and 124
+// rows 360 us (two splits + reduce: 351 + 30 us).
+struct HeadPlan {
+  bool rk = false, top2 = false;
+  GemmPlan rkp;
+  ActPlan ap;
+};
+
+HeadPlan lm_head_plan(const dflash_dims* d, int M) {
+  HeadPlan h;
+  h.rkp = plan_gemm_rk(M, d->V, d->D, true);
+  if (h.rkp.rk) {
+    h.rk = true;
+    return h;
+  }
+  h.ap = plan_act(M, d->V, d->D, true);
+  const char* knob = getenv("DFLASH_HEAD_TILED");   // 2: the plain GEMM plan (measurement)
+  if (knob == nullptr || atoi(knob) != 2) {
+    GemmPlan t = plan_gemm_tiled(M, d->V, d->D, A_BF16_HILO);
+    t.cps = d->D / 64;                        // one split: every 64-wide k tile
+    t.S = 1;
+    t.part_floats = 0;
+    h.ap = ActPlan{t, A_BF16_HILO};
+  }
+  h.top2 = h.ap.kind == A_BF16_HILO && h.ap.p.S == 1;
+  return h;
+}
+
 // LM head: split-K partials [S][M][V], then per-128-column top-2 [ceil(V/128)][M][3]
 struct ArgmaxWs {
   size_t part, top2, rows, planes, total;
@@ -306,12 +340,12 @@ ArgmaxWs argmax_ws(const dflash_dims* d, int M, bool gathered = false) {
   if (d->dtype == DFLASH_F32) {
     w.part = c.take(static_cast<size_t>(M) * d->V * 4);
   } else {
-    const ActPlan ap = plan_act(M, d->V, d->D, true);
-    size_t pf = ap.p.part_floats;
+    const HeadPlan hp = lm_head_plan(d, M);
+    size_t pf = hp.rk ? 0 : hp.ap.p.part_floats;
     const size_t pf_stream = plan_gemm_mfma(M, d->V, d->D, A_F32_SPLIT, true).part_floats;
     if (pf_stream > pf) pf = pf_stream;
     w.part = c.take(pf * 4);
-    w.planes = c.take(act_planes_bytes(ap, M, d->D));
+    w.planes = c.take(hp.rk ? 0 : act_planes_bytes(hp.ap, M, d->D));
     // top-2 candidates: one row per 512-column reduce tile, 256-column tiled
     // GEMM tile, or register-K workgroup
     size_t t2 = static_cast<size_t>((d->V + 255) / 256);
@@ -914,16 +948,16 @@ static dflash_status lm_head_argmax(const dflash_dims* dims, const dflash_weight
   if (dims->dtype == DFLASH_BF16) {
     g.part = reinterpret_cast<float*>(base + lay.part);
     float* top2 = reinterpret_cast<float*>(base + lay.top2);
-    const GemmPlan rk = plan_gemm_rk(Mr, dims->V, D, true);
-    if (rk.rk) {
+    const HeadPlan hp = lm_head_plan(dims, Mr);
+    if (hp.rk) {
       // one pass over the LM head: logits reduced in-register, top-2 per workgroup
       const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-      DF_HIP(launch_gemm_rk(g, rk, top2, logits_dbg, s));
+      DF_HIP(launch_gemm_rk(g, hp.rkp, top2, logits_dbg, s));
       prof_end(ps, s);
-      DF_HIP(launch_argmax_final(top2, rk.grid, Mr, draft, top2_gap, s));
+      DF_HIP(launch_argmax_final(top2, hp.rkp.grid, Mr, draft, top2_gap, s));
     } else {
-      const ActPlan ap = plan_act(Mr, dims->V, D, true);
-      if (ap.kind == A_BF16_HILO && ap.p.S == 1) {
+      const ActPlan& ap = hp.ap;
+      if (hp.top2) {
         // tiled, one K split: each workgroup reduces its tile to a top-2 per
         // row (no logits round trip unless they are asked for)
         DF_HIP(prepare_act(g, ap, base + lay.planes, s, false));
