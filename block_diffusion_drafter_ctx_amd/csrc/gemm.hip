@@ -1262,14 +1262,20 @@ GemmPlan plan_gemm_rk_short(int M, int N, int K) {
   return p;
 }
 
+// From 33 rows the tiled kernel (one 128-row tile, MFMA-bound) beats the
+// weight-streaming kernels, whose fragment reads from LDS grow with the rows:
+// the 8-layer drafter at 4 x 16 block rows 2358 -> 2235 us; at 32 rows and
+// below it loses (4 x 8 rows 1843 -> 1923 us, 16 rows 880 -> 1000 us a step).
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
+  const int tiled_rows = env_int("DFLASH_TILED_MIN_ROWS", 33);   // (measurement)
+  if (M >= tiled_rows && K % kTileK == 0 && env_int("DFLASH_GEMM_NO_TILED", 0) == 0)
+    return plan_gemm_tiled(M, N, K, ak);
   if ((ak == A_F32_SPLIT || ak == A_BF16) && M <= rk_max_rows(true)) {
     const GemmPlan r = plan_gemm_rk(M, N, K, false);
     if (r.rk && r.S == 1) return r;
     const GemmPlan q = plan_gemm_rk_short(M, N, K);
     if (q.rk) return q;
   }
-  if (M > 64 && K % kTileK == 0 && env_int("DFLASH_GEMM_NO_TILED", 0) == 0) return plan_gemm_tiled(M, N, K, ak);
   return plan_gemm_mfma(M, N, K, ak, wide);
 }
 

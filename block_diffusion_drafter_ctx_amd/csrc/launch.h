@@ -57,8 +57,9 @@ GemmPlan plan_gemm_mfma(int M, int N, int K, GemmAKind ak, bool wide);
 // per tile against 128 (fp32 A split on the fly) or 256 (bf16 A, or pre-split
 // hi/lo planes) weight rows.
 GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak);
-// The plan the library uses for an M x N x K product (tiled for M > 64 when
-// K % 64 == 0, streaming otherwise).
+// The plan the library uses for an M x N x K product (register-K for few rows
+// and suitable shapes, tiled from 33 rows when K % 64 == 0, streaming
+// otherwise).
 GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide);
 hipError_t launch_gemm_mfma(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, hipStream_t st);
 
