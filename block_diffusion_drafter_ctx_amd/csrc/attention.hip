@@ -134,6 +134,19 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
   const int G = a.Hq / a.Hkv;
   const int gb = a.gam[b], Rb = G * gb;       // this sequence's block rows and query rows
   const bool computes = blockIdx.y * kRowsPerGroup + wave * 16 < Rb;   // uniform per wave
+  // The keys this lane's query row sees within [kbeg, kend): all of them,
+  // except in a group of two anchored blocks, where the rows of each block see
+  // only their own context prefix and their own block rows.
+  int klo = kbeg, khi = kend;
+  if (a.blk0[b] >= 0) {
+    const bool second = r % gb >= a.half[b];
+    if (sp == a.nsplit[b] - 1) {
+      klo = kbeg + (second ? a.half[b] : 0);
+      khi = kbeg + (second ? gb : a.half[b]);
+    } else {
+      khi = min(kend, second ? a.ctx2[b] : a.ctx1[b]);
+    }
+  }
 
   uint4 qh[DS], ql[DS];                       // query fragments, loaded after the first key blocks
   const int64_t head = static_cast<int64_t>(a.kvseq[b]) * a.Hkv + j;
@@ -178,7 +191,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  auto compute = [&](const uint4* buf, int k0, int klim) {   // keys >= klim do not count
+  auto compute = [&](const uint4* buf, int k0, int lo, int hi) {   // only keys in [lo, hi) count (per lane)
     // all K fragments of the block first (independent LDS reads, one wait), then
     // the score MFMAs in four independent accumulation chains
     uint4 kf[2][DS][HL];
@@ -214,18 +227,22 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p[kt * 4 + e] = (k0 + kt * 16 + 4 * g4 + e < klim) ? s[kt][e] : -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        const int key = k0 + kt * 16 + 4 * g4 + e;
+        p[kt * 4 + e] = (key >= lo && key < hi) ? s[kt][e] : -INFINITY;
+      }
     float mx = p[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, p[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;   // a row with no key yet: nothing to scale
+    const float alpha = exp2f(m_run - m_use);
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(p[e] - m_new);
+      p[e] = exp2f(p[e] - m_use);
       ps += p[e];
     }
     l_run = l_run * alpha + ps;
@@ -283,7 +300,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
       store(rr[dd], buf, k0);
       load(rr[dd], blk(bi + dd + DEPTH));
       __syncthreads();
-      if (computes) compute(buf, k0, bi + dd < nblk ? kend : k0);
+      const bool live = bi + dd < nblk;
+      if (computes) compute(buf, k0, live ? klo : k0, live ? khi : k0);
     }
   }
 

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -476,7 +477,10 @@ dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t 
   // ragged (the attention bound grows with B and the longest block).
   size_t need = 0;
   auto upd = [&](size_t x) { need = x > need ? x : need; };
-  for (int M = DFLASH_MIN_GAMMA; M <= B * gamma; ++M) upd(draft_ws(dims, B, M, gamma).total);
+  for (int M = DFLASH_MIN_GAMMA; M <= B * gamma; ++M) {
+    upd(draft_ws(dims, B, M, gamma).total);
+    upd(draft_ws(dims, B, M, 2 * gamma).total);   // anchored blocks two to a group
+  }
   for (int M = 1; M <= B * (gamma - 1); ++M) upd(argmax_ws(dims, M, true).total);
   for (int b = 1; b <= B; ++b)
     for (int g = DFLASH_MIN_GAMMA; g <= gamma; ++g) {
@@ -656,10 +660,15 @@ dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w,
 // inference pos0 = nctx = len: the block follows the context.  Anchored blocks
 // (apart) keep their rows in a scratch region past the context, read as a key
 // item of their own.
+// Two anchored blocks of one sequence can share a group (gam = both blocks'
+// rows, the first block's half[b] rows first): their own rows then sit
+// together from pos0[b], the first block sees context rows [0, nctx[b]) and
+// the second [0, nctx2[b]), each only its own block rows.
 struct QueryGroups {
   int n = 0;
   bool apart = false;
   int32_t gam[kMaxSeq], kvseq[kMaxSeq], nctx[kMaxSeq], pos0[kMaxSeq];
+  int32_t half[kMaxSeq], nctx2[kMaxSeq];
 };
 
 static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_weights* w,
@@ -750,7 +759,7 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
 
   int32_t nkeys[kMaxSeq], apart[kMaxSeq];
   for (int b = 0; b < B; ++b) {
-    nkeys[b] = qg.apart ? qg.nctx[b] : qg.nctx[b] + qg.gam[b];
+    nkeys[b] = qg.apart ? std::max(qg.nctx[b], qg.nctx2[b]) : qg.nctx[b] + qg.gam[b];
     apart[b] = qg.apart ? 1 : 0;
   }
   const int R = (Hq / Hkv) * gmax;
@@ -810,6 +819,9 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
       at.qrow0[b] = qrow0[b];
       at.kvseq[b] = qg.kvseq[b];
       at.blk0[b] = qg.apart ? qg.pos0[b] : -1;
+      at.half[b] = qg.half[b];
+      at.ctx1[b] = qg.apart ? qg.nctx[b] : nkeys[b];
+      at.ctx2[b] = qg.apart ? qg.nctx2[b] : nkeys[b];
     }
     at.qrow0[B] = M;
     const int pa = prof_begin(DFLASH_PROF_ATTENTION, s);
@@ -865,8 +877,9 @@ static dflash_status inference_groups(const dflash_dims* dims, const dflash_weig
     DF_REQUIRE(static_cast<int64_t>(cache->len[b]) + gammas[b] <= cache->cap, DFLASH_ERR_CAPACITY,
                "sequence %d: len %d + gamma %d exceeds cap %d", b, cache->len[b], gammas[b], cache->cap);
     qg->gam[b] = gammas[b];
+    qg->half[b] = gammas[b];
     qg->kvseq[b] = b;
-    qg->nctx[b] = qg->pos0[b] = cache->len[b];
+    qg->nctx[b] = qg->nctx2[b] = qg->pos0[b] = cache->len[b];
   }
   return DFLASH_OK;
 }
@@ -907,27 +920,44 @@ dflash_status dflash_draft_forward_blocks(const dflash_dims* dims, const dflash_
   DF_REQUIRE(nblk >= 1 && nblk <= DFLASH_MAX_BATCH, DFLASH_ERR_INVALID_ARG, "nblk=%d outside [1, %d]", nblk,
              DFLASH_MAX_BATCH);
   DF_REQUIRE(block_seq != nullptr && anchors != nullptr, DFLASH_ERR_INVALID_ARG, "block_seq / anchors is NULL");
-  QueryGroups qg;
-  qg.n = nblk;
-  qg.apart = true;
-  const int g32 = (gamma + 31) / 32 * 32;
-  int used[kMaxSeq] = {0};   // scratch slots taken per sequence
   for (int k = 0; k < nblk; ++k) {
     const int sq = block_seq[k];
     DF_REQUIRE(sq >= 0 && sq < cache->B, DFLASH_ERR_INVALID_ARG, "block %d: sequence %d outside [0, %d)", k, sq,
                cache->B);
     DF_REQUIRE(anchors[k] >= 0 && anchors[k] <= cache->len[sq], DFLASH_ERR_INVALID_ARG,
                "block %d: anchor %d outside [0, len %d]", k, anchors[k], cache->len[sq]);
-    // the block's own rows: 32-row slots past the sequence's context
-    const int64_t pos = (static_cast<int64_t>(cache->len[sq]) + 31) / 32 * 32 + static_cast<int64_t>(used[sq]) * g32;
-    DF_REQUIRE(pos + g32 <= cache->cap, DFLASH_ERR_CAPACITY,
+  }
+  // Consecutive blocks of one sequence share a query group (bf16 weights, fp32
+  // cache: the attention kernel that reads each key tile once for both), so
+  // that each context tile is read once for two blocks.  A group's own rows
+  // take one 32-row-aligned slot past the sequence's context: ceil32(rows)
+  // rows, never more than the two blocks' separate slots.
+  const char* knob = getenv("DFLASH_BLOCK_PAIRS");   // 2: one block per group (measurement)
+  const bool pairs = dims->dtype == DFLASH_BF16 && dims->cache_dtype == DFLASH_F32 &&
+                     (knob == nullptr || atoi(knob) != 2);
+  QueryGroups qg;
+  qg.n = 0;
+  qg.apart = true;
+  int64_t next[kMaxSeq];   // next free scratch row per sequence
+  for (int b = 0; b < cache->B; ++b) next[b] = (static_cast<int64_t>(cache->len[b]) + 31) / 32 * 32;
+  for (int k = 0; k < nblk;) {
+    const int sq = block_seq[k];
+    const bool two = pairs && k + 1 < nblk && block_seq[k + 1] == sq;
+    const int rows = two ? 2 * gamma : gamma;
+    const int64_t pos = next[sq];
+    const int64_t slot = (rows + 31) / 32 * 32;
+    DF_REQUIRE(pos + slot <= cache->cap, DFLASH_ERR_CAPACITY,
                "block %d: scratch rows [%lld, %lld) of sequence %d exceed cap %d", k, static_cast<long long>(pos),
-               static_cast<long long>(pos + g32), sq, cache->cap);
-    ++used[sq];
-    qg.gam[k] = gamma;
-    qg.kvseq[k] = sq;
-    qg.nctx[k] = anchors[k];
-    qg.pos0[k] = static_cast<int32_t>(pos);
+               static_cast<long long>(pos + slot), sq, cache->cap);
+    next[sq] = pos + slot;
+    const int g = qg.n++;
+    qg.gam[g] = rows;
+    qg.half[g] = gamma;
+    qg.kvseq[g] = sq;
+    qg.nctx[g] = anchors[k];
+    qg.nctx2[g] = two ? anchors[k + 1] : anchors[k];
+    qg.pos0[g] = static_cast<int32_t>(pos);
+    k += two ? 2 : 1;
   }
   return draft_forward_impl(dims, w, cache, block_tokens, embed_override, qg, h_final, ws, ws_bytes, stream);
 }

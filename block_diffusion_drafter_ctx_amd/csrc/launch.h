@@ -247,6 +247,9 @@ struct AttnArgs {
   int32_t gam[kMaxSeq];       // block rows of sequence b
   int32_t qrow0[kMaxSeq + 1]; // first block row of sequence b in q / o_out (qrow0[B] = M)
   int32_t kvseq[kMaxSeq];     // cache sequence whose K/V block b reads
+  int32_t half[kMaxSeq];      // block rows of group b's first block (gam[b] unless two blocks share the group)
+  int32_t ctx1[kMaxSeq];      // anchored blocks: context keys of the first block's rows
+  int32_t ctx2[kMaxSeq];      // anchored blocks: context keys of the second block's rows
   int32_t blk0[kMaxSeq];      // -1: the block's rows follow the context (keys [0, nkeys[b]));
                               // else its own rows [blk0, blk0 + gam) are a separate key item
                               // after the context keys [0, nkeys[b]) (blk0 % 32 == 0)

@@ -215,10 +215,15 @@ dflash_status dflash_draft_forward_ragged(const dflash_dims* dims, const dflash_
  *   block_tokens        [nblk][gamma] int32 (or embed_override [nblk][gamma][D])
  *   h_final             out [nblk][gamma][D] float32
  * Each block's own K/V rows are written to scratch rows of its sequence past
- * the context: the i-th block of sequence s (in call order) takes rows
- * [L32 + i*G32, L32 + i*G32 + gamma), L32 = len[s] rounded up to a multiple
- * of 32 and G32 = gamma rounded up likewise.  Errors: DFLASH_ERR_CAPACITY if
- * L32 + (blocks of s)*G32 > cap.  Context rows and len are not changed.
+ * the context, in slots that follow one another from L32 = len[s] rounded up
+ * to a multiple of 32, in call order.  With bf16 weights and an fp32 cache two
+ * consecutive blocks of the same sequence form a pair (the attention reads each
+ * context tile once for both): a pair takes a slot of 2*gamma rows rounded up
+ * to a multiple of 32, its first block rows [P, P + gamma) and its second
+ * [P + gamma, P + 2*gamma); any other block takes a slot of gamma rows rounded
+ * up likewise, its rows [P, P + gamma).  Errors: DFLASH_ERR_CAPACITY if a
+ * sequence's slots end past cap (never more rows than L32 + (blocks of s) *
+ * (gamma rounded up to 32)).  Context rows and len are not changed.
  * A workspace sized by dflash_workspace_size(dims, nblk, gamma, ..) suffices. */
 dflash_status dflash_draft_forward_blocks(const dflash_dims* dims, const dflash_weights* w,
                                           const dflash_kv_cache* cache, const int32_t* block_seq,

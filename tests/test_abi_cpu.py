@@ -251,7 +251,7 @@ def test_workspace_covers_ragged_row_counts(lib):
     assert big >= B.workspace_size(d, 3, 16, 1)
 
 
-def test_blocks_checks(lib):
+def test_blocks_checks(lib, monkeypatch):
     w = B.Weights(w_qkv=0x1000, w_o=0x1000, w_gateup=0x1000, w_down=0x1000, g_attn=0x1000, g_ffn=0x1000,
                   g_final=0x1000, embed=0x1000, lm_head=0x1000)
     c = _cache(cap=128, lens=(40, 10))
@@ -259,12 +259,26 @@ def test_blocks_checks(lib):
         with pytest.raises(B.DFlashError) as e:
             B.draft_forward_blocks(_dims(), w, c, seqs, anchors, 16, 0x4000, None, 0x5000, 0x100000, 1 << 30)
         assert e.value.status == B.ERR_INVALID_ARG, (seqs, anchors)
-    # sequence 0: context rounds up to 64, three 32-row slots reach 160 > 128
+    # sequence 0: context rounds up to 64; its blocks 0, 2, 4 are not
+    # consecutive, so three 32-row slots reach 160 > 128
     with pytest.raises(B.DFlashError) as e:
-        B.draft_forward_blocks(_dims(), w, c, [0, 0, 1, 0], [5, 40, 3, 0], 16, 0x4000, None, 0x5000, 0x100000,
-                               1 << 30)
-    assert e.value.status == B.ERR_CAPACITY and "block 3" in B.last_error()
+        B.draft_forward_blocks(_dims(), w, c, [0, 1, 0, 1, 0], [5, 3, 40, 0, 0], 16, 0x4000, None, 0x5000,
+                               0x100000, 1 << 30)
+    assert e.value.status == B.ERR_CAPACITY and "block 4" in B.last_error()
     assert list(c._keep) == [40, 10]
+    # four consecutive blocks of sequence 0 form two pairs (bf16 weights, fp32
+    # cache), one 32-row slot each: rows [64, 128) fit, and the call gets as
+    # far as the device check; one block per group they would need 192 rows
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward_blocks(_dims(), w, c, [0, 0, 0, 0], [5, 40, 3, 0], 16, 0x4000, None, 0x5000, 0x100000,
+                               1 << 30)
+    assert e.value.status == B.ERR_HIP
+    monkeypatch.setenv("DFLASH_BLOCK_PAIRS", "2")
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward_blocks(_dims(), w, c, [0, 0, 0, 0], [5, 40, 3, 0], 16, 0x4000, None, 0x5000, 0x100000,
+                               1 << 30)
+    assert e.value.status == B.ERR_CAPACITY and "block 2" in B.last_error()
+    monkeypatch.delenv("DFLASH_BLOCK_PAIRS")
     with pytest.raises(B.DFlashError) as e:
         B.draft_forward_blocks(_dims(), w, c, [0, 1], [5, 3], 16, 0x4000, None, 0x5000, 0x100000, 16)
     assert e.value.status == B.ERR_WORKSPACE

@@ -2,6 +2,8 @@
 the CPU oracle.  Tolerances as in tests/parity_util.py."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -28,6 +30,25 @@ def small(**kw):
     return shrink(CONFIGS[2], **base)
 
 
+def block_rows(blocks, lens, g, pairs):
+    """(sequence, first scratch row) of each block, by the documented layout:
+    slots from each sequence's context length rounded up to 32, in call order;
+    with pairs, two consecutive blocks of one sequence share a slot of 2g rows
+    rounded up to 32, the second block's rows right after the first's."""
+    nxt = {s: (n + 31) // 32 * 32 for s, n in enumerate(lens)}
+    out, k = [], 0
+    while k < len(blocks):
+        s = blocks[k][0]
+        two = pairs and k + 1 < len(blocks) and blocks[k + 1][0] == s
+        pos = nxt[s]
+        nxt[s] += ((2 * g if two else g) + 31) // 32 * 32
+        out.append((s, pos))
+        if two:
+            out.append((s, pos + g))
+        k += 2 if two else 1
+    return out
+
+
 class Blocks(Workload):
     """A seeded context, then blocks anchored inside it."""
 
@@ -36,6 +57,8 @@ class Blocks(Workload):
         per_seq = max(sum(1 for s, _ in blocks if s == b) for b in range(cfg.B))
         super().__init__(cfg, gamma, 1, override=override, extra_cap=32 + per_seq * g32)
         self.blocks = [(int(s), int(a)) for s, a in blocks]
+        # two consecutive blocks of a sequence share a query group with bf16 weights and an fp32 cache
+        self.pairs = cfg.dtype == "bf16" and cfg.cache_dtype == "f32" and os.environ.get("DFLASH_BLOCK_PAIRS") != "2"
         self.dr.ensure_workspace(max(cfg.B, len(blocks)), gamma, max(cfg.n_ctx_total, 1))
 
     def run_blocks(self, tag="blocks"):
@@ -71,11 +94,7 @@ class Blocks(Workload):
         excl = argmax_agree(draft.cpu().numpy(), d_o, gap_o, f"{tag} drafts",
                             GAP_MIN_BF16_CACHE if self.st == "bf16" else GAP_MIN)
         # each block's own K/V rows sit in its scratch slot past its sequence's context
-        g32 = (g + 31) // 32 * 32
-        used = [0] * cfg.B
-        for k, (s, _) in enumerate(self.blocks):
-            pos = (lens[s] + 31) // 32 * 32 + used[s] * g32
-            used[s] += 1
+        for k, (s, pos) in enumerate(block_rows(self.blocks, lens, g, self.pairs)):
             for l in range(cfg.L):
                 gk = self.cache.k[l, s, :, pos:pos + g].float().cpu().numpy().transpose(1, 0, 2)
                 gv = self.cache.v[l, s, :, :, pos:pos + g].float().cpu().numpy().transpose(2, 0, 1)
