@@ -463,6 +463,13 @@ dflash_status dflash_profile_events(int32_t role, void* const* start, void* cons
 
 const char* dflash_last_error(void) { return g_err.c_str(); }
 
+// Two anchored blocks of gamma rows may share a query group: bf16 weights, an
+// fp32 cache (the attention kernel that masks each row to its own block) and
+// both blocks' query rows within the 128 rows one attention workgroup takes.
+static bool pairs_fit(const dflash_dims* d, int gamma) {
+  return d->dtype == DFLASH_BF16 && d->cache_dtype == DFLASH_F32 && 2 * (d->Hq / d->Hkv) * gamma <= 128;
+}
+
 dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t gamma, int32_t max_rows,
                                     size_t* bytes) {
   dflash_status st = check_dims(dims);
@@ -479,7 +486,7 @@ dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t 
   auto upd = [&](size_t x) { need = x > need ? x : need; };
   for (int M = DFLASH_MIN_GAMMA; M <= B * gamma; ++M) {
     upd(draft_ws(dims, B, M, gamma).total);
-    upd(draft_ws(dims, B, M, 2 * gamma).total);   // anchored blocks two to a group
+    if (pairs_fit(dims, gamma)) upd(draft_ws(dims, B, M, 2 * gamma).total);   // anchored blocks two to a group
   }
   for (int M = 1; M <= B * (gamma - 1); ++M) upd(argmax_ws(dims, M, true).total);
   for (int b = 1; b <= B; ++b)
@@ -933,8 +940,7 @@ dflash_status dflash_draft_forward_blocks(const dflash_dims* dims, const dflash_
   // take one 32-row-aligned slot past the sequence's context: ceil32(rows)
   // rows, never more than the two blocks' separate slots.
   const char* knob = getenv("DFLASH_BLOCK_PAIRS");   // 2: one block per group (measurement)
-  const bool pairs = dims->dtype == DFLASH_BF16 && dims->cache_dtype == DFLASH_F32 &&
-                     (knob == nullptr || atoi(knob) != 2);
+  const bool pairs = pairs_fit(dims, gamma) && (knob == nullptr || atoi(knob) != 2);
   QueryGroups qg;
   qg.n = 0;
   qg.apart = true;

@@ -216,9 +216,10 @@ dflash_status dflash_draft_forward_ragged(const dflash_dims* dims, const dflash_
  *   h_final             out [nblk][gamma][D] float32
  * Each block's own K/V rows are written to scratch rows of its sequence past
  * the context, in slots that follow one another from L32 = len[s] rounded up
- * to a multiple of 32, in call order.  With bf16 weights and an fp32 cache two
- * consecutive blocks of the same sequence form a pair (the attention reads each
- * context tile once for both): a pair takes a slot of 2*gamma rows rounded up
+ * to a multiple of 32, in call order.  With bf16 weights, an fp32 cache and
+ * 2 * (Hq / Hkv) * gamma <= 128, two consecutive blocks of the same sequence
+ * form a pair (the attention reads each context tile once for both): a pair
+ * takes a slot of 2*gamma rows rounded up
  * to a multiple of 32, its first block rows [P, P + gamma) and its second
  * [P + gamma, P + 2*gamma); any other block takes a slot of gamma rows rounded
  * up likewise, its rows [P, P + gamma).  Errors: DFLASH_ERR_CAPACITY if a

@@ -58,7 +58,8 @@ class Blocks(Workload):
         super().__init__(cfg, gamma, 1, override=override, extra_cap=32 + per_seq * g32)
         self.blocks = [(int(s), int(a)) for s, a in blocks]
         # two consecutive blocks of a sequence share a query group with bf16 weights and an fp32 cache
-        self.pairs = cfg.dtype == "bf16" and cfg.cache_dtype == "f32" and os.environ.get("DFLASH_BLOCK_PAIRS") != "2"
+        self.pairs = (cfg.dtype == "bf16" and cfg.cache_dtype == "f32" and 2 * (cfg.Hq // cfg.Hkv) * gamma <= 128
+                      and os.environ.get("DFLASH_BLOCK_PAIRS") != "2")
         self.dr.ensure_workspace(max(cfg.B, len(blocks)), gamma, max(cfg.n_ctx_total, 1))
 
     def run_blocks(self, tag="blocks"):
@@ -116,6 +117,14 @@ def test_blocks_override_bf16_cache_gamma33():
     blocks = [(0, 12), (1, 299), (1, 64), (0, 36)]
     log("anchored blocks, bf16 cache, gamma 33 (two row groups)")
     Blocks(small(cid=131, cache_dtype="bf16"), blocks, 33, override=True).run_blocks()
+
+
+def test_blocks_unpaired_gamma20():
+    # 2 * G * gamma = 160 query rows would not fit one attention workgroup:
+    # consecutive blocks stay one to a group (fp32 cache)
+    blocks = [(0, 30), (0, 7), (1, 200), (1, 250), (0, 37)]
+    log("anchored blocks, gamma 20 (no pairs)")
+    Blocks(small(cid=136), blocks, 20).run_blocks()
 
 
 def test_blocks_head64():
