@@ -1,22 +1,23 @@
-// Weight-streaming GEMMs of the drafter path: C[m][n] = sum_k A[m][k] W[n][k].
-//
-// Every projection on the drafting path is "few activation rows x a large bf16
-// weight matrix" (M = B*gamma <= 256 rows against up to 151936 x 4096 weights),
-// so the kernel is built to stream W from HBM once, at full width, with as many
-// bytes in flight as the chip needs and no barrier in the streaming loop:
-//   * each wave owns one 16-row MFMA strip of W (the A operand of
-//     v_mfma_f32_16x16x32_bf16: lane l loads 16 B of row l%16) and walks the
-//     workgroup's K range with 8 k-steps (8 KB) of loads in flight, double
-//     buffered in registers;
-//   * the activation slice [MT rows x K range] is staged once per workgroup into
-//     LDS in MFMA B-operand order (one conflict-free 16 B read per lane); the K
-//     range is bounded by the LDS slice (split-K across workgroups otherwise);
-//   * fp32 activations are split into bf16 hi + lo and multiplied twice, which
-//     keeps ~16 significant bits against the exact bf16 weights at no cost on an
-//     HBM-bound kernel;
-//   * partial sums go to a [split][M][N] fp32 buffer that the consumer reduces
-//     in split order (deterministic, no float atomics).
-// The fp32 storage path uses a plain LDS-tiled FMA GEMM (tiny workloads only).
+// The GEMMs of the drafter path: C[m][n] = sum_k A[m][k] W[n][k], W bf16
+// [N][K] row-major, A fp32 (split into bf16 hi + lo, two MFMA products, which
+// keeps ~16 significant bits against the exact bf16 weights) or exact bf16.
+// Which kernel runs depends on the activation rows M (plan_gemm):
+//   * register-K (gemm_rk_kernel), M <= 16 per workgroup: a workgroup keeps
+//     its 16 rows' K range in registers and streams whole 16-row weight tiles;
+//     tall weights (LM head, gate/up) take the whole K per workgroup with the
+//     top-2, sampling or SwiGLU epilogue, up to 32 rows in 16-row chunks on
+//     XCD-adjacent workgroups; short weights (QKV, O, down, appends) split K
+//     in 1024-wide ranges;
+//   * streaming (gemm_stream_kernel), 17-32 rows and shapes the others do not
+//     take: each wave streams a 16-row strip of W against an activation slice
+//     staged in LDS, with split-K partials;
+//   * tiled (gemm_tile_lds_kernel), from 33 rows: 256 x 128 (hi / lo planes)
+//     or 256 x 256 (bf16) tiles fed by global-to-LDS loads, launched in
+//     XCD-grouped tile order, with split-K partials or, for the LM head, a
+//     per-tile top-2 epilogue;
+//   * gemm_f32_kernel for fp32 weights (tiny configurations only).
+// Split-K partials go to a [split][M][N] fp32 buffer that the consumer reduces
+// in split order (deterministic, no float atomics).
 #include "common.h"
 #include "launch.h"
 
