@@ -637,7 +637,6 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine_wave_kernel(A
     const int cn = min(64, ns - c0);
     const float* po = a.part_o + (static_cast<int64_t>(it0 + c0) * a.Rpad + r) * a.d + c;
     const int64_t stride = static_cast<int64_t>(a.Rpad) * a.d;   // between consecutive splits
-#pragma unroll 8
     for (int e = 0; e < cn; ++e) {
       const float we = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), e));
       if (two) {

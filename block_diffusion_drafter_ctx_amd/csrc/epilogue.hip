@@ -18,8 +18,6 @@
 namespace dflash {
 namespace {
 
-constexpr int kRowThreads = 256;
-
 // Threads per row kernel: one float4 group per thread where possible.
 int row_threads(int D) {
   int t = D / 4;
