@@ -75,6 +75,7 @@ def main():
     ap.add_argument("--no-ragged", action="store_true", help="skip the per-sequence block-length leg")
     ap.add_argument("--no-blocks", action="store_true", help="skip the anchored-blocks (training-mask) leg")
     ap.add_argument("--no-gamma-sweep", action="store_true", help="skip the block-length sweep on the 8-layer drafter")
+    ap.add_argument("--no-long-context", action="store_true", help="skip the 32768-token context leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the single-GPU path is "
@@ -301,6 +302,8 @@ def main():
         out["ragged"] = ragged_leg(cfg, dr)
     if not args.no_blocks and cfg.dtype == "bf16":
         out["blocks"] = blocks_leg(cfg, dr)
+    if not args.no_long_context and cfg.dtype == "bf16":
+        out["long_context"] = long_context_leg(cfg, dr)
     if not args.no_gamma_sweep and cfg.dtype == "bf16":
         del dr, cache
         torch.cuda.empty_cache()
@@ -316,9 +319,9 @@ def main():
     del src, dst
 
     if not args.no_cpu_baseline:
-        greedy_cpu, sampled_cpu, ragged_cpu, blocks_cpu = cpu_baseline(
+        greedy_cpu, sampled_cpu, ragged_cpu, blocks_cpu, long_cpu = cpu_baseline(
             cfg, inp, args.cpu_seconds, None if args.no_sampling else args.temperature, "ragged" in out,
-            "blocks" in out)
+            "blocks" in out, "long_context" in out)
         out["cpu_baseline"] = greedy_cpu
         if sampled_cpu is not None:
             out["sampling"]["cpu_baseline"] = sampled_cpu
@@ -326,6 +329,8 @@ def main():
             out["ragged"]["cpu_baseline"] = ragged_cpu
         if blocks_cpu is not None:
             out["blocks"]["cpu_baseline"] = blocks_cpu
+        if long_cpu is not None:
+            out["long_context"]["cpu_baseline"] = long_cpu
     print(json.dumps(out), flush=True)
 
 
@@ -560,6 +565,81 @@ def ragged_leg(cfg, dr):
     }
 
 
+LONG_CTX = 32768
+
+
+def long_context_leg(cfg, dr):
+    """The long-context workload (one sequence, a 32768-token context ingested
+    untimed from seeded device-side states, gamma 16): draft forward + LM-head
+    argmax at a fixed cache (median of 20), and the attention launches alone
+    (HIP events the library records around each one on its stream), against
+    the context + block K/V each layer reads."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_drafter_ctx_amd import binding as B
+    from block_diffusion_drafter_ctx_amd import roofline as RF
+
+    dev = "cuda"
+    g, N = 16, LONG_CTX
+    stream = torch.cuda.current_stream()
+    cache = dr.cache(1, (N + g + 31) // 32 * 32)
+    dr.ensure_workspace(1, g, N)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261207)
+    H_t = dr.context_buffer(N)
+    for r0 in range(0, N, 8192):
+        states = [torch.randn(8192, cfg.D, generator=gen, device=dev).to(torch.bfloat16) for _ in range(cfg.n_tgt)]
+        dr.fuse(states, 8192, H_t[r0:r0 + 8192])
+        del states
+    dr.inject(H_t, [N], cache)
+    del H_t
+    tok = torch.full((1, g), cfg.mask_id, dtype=torch.int32, device=dev)
+    hf = torch.empty(1, g, cfg.D, dtype=torch.float32, device=dev)
+    d = torch.empty(1, g - 1, dtype=torch.int32, device=dev)
+
+    def fwd():
+        dr.draft(cache, tok, None, g, hf)
+        dr.argmax_accept(B.ARGMAX, hf, 1, g, d)
+
+    for _ in range(3):
+        fwd()
+    ev = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fwd()
+        b.record(stream)
+        ev.append((a, b))
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cfg.L * 10)]
+    for a, b in pairs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    B.profile_events(B.PROF_ATTENTION, [a.cuda_event for a, _ in pairs], [b.cuda_event for _, b in pairs])
+    for _ in range(10):
+        dr.draft(cache, tok, None, g, hf)
+    torch.cuda.synchronize()
+    B.profile_events(B.PROF_ATTENTION, [], [])
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    att_us = float(np.median([a.elapsed_time(b) for a, b in pairs])) * 1e3
+    es, cs = RF.elem_bytes(cfg.dtype), RF.elem_bytes(cfg.cache_dtype)
+    nbytes = RF.draft_forward_bytes(cfg.D, cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.F, cfg.V, 1, g, [N], es, cs)
+    att_bytes = (N + g) * 2 * cfg.Hkv * cfg.d * cs
+    log(f"long context: {N}-token context, draft fwd + argmax {us:.1f} us, attention {att_us:.1f} us per layer "
+        f"({att_bytes / (att_us * 1e-6) / 1e9:.0f} GB/s)")
+    del cache
+    return {
+        "workload": (f"one sequence, {N}-token context (ingested untimed), gamma {g}, {cfg.L} layers at the bench "
+                     f"drafter's shape, {cfg.cache_dtype} cache; draft forward + LM-head argmax at a fixed cache"),
+        "draft_fwd_us": round(us, 1), "bytes": int(nbytes),
+        "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4),
+        "attention": {"us_per_layer": round(att_us, 2), "bytes_per_layer": int(att_bytes),
+                      "GBps": round(att_bytes / (att_us * 1e-6) / 1e9, 1),
+                      "hbm_frac": round(att_bytes / (att_us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4)},
+    }
+
+
 def gamma_sweep_leg():
     """Draft forward + LM-head argmax of the deep8_b4_n8192 workload (8 layers,
     4 sequences with 8192-token contexts) at blocks of 8, 16 and 32 rows, on one
@@ -694,14 +774,17 @@ def blocks_leg(cfg, dr):
     }
 
 
-def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False, blocks=False):
+def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False, blocks=False, long_ctx=False):
     """The CPU oracle, as it stands, on whole drafting iterations of the same
     workload (draft forward + LM-head argmax + accept + 16-row append), repeated
     for about ``seconds`` with the GPU loop's 8-iteration cache reset; then, when
     ``temperature`` is given, the sampled iteration (draft forward + sampled
     drafts + synthetic target logits + lossless verify + append) for about half
     as long; then, when ``ragged``, one ragged pass over a sample of the ragged
-    leg's batch.  Returns (greedy, sampled or None, ragged or None)."""
+    leg's batch; when ``blocks`` / ``long_ctx``, two of the blocks leg's
+    blocks / one block over the long-context leg's 32768-row context (random
+    context K/V).  Returns (greedy, sampled, ragged, blocks, long context), None
+    for the ones not asked for."""
     import numpy as np
     from oracle import dflash_oracle as O
     from dflash_inputs import build_target_np
@@ -769,8 +852,6 @@ def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False, blocks=False
                         f"+ accept + 16-row append, cache reset every {cfg.iters}), float64 numpy oracle, "
                         f"after an untimed context ingest",
               "seconds": round(dt, 2)}
-    if temperature is None:
-        return greedy, None
     sampled = None
     if temperature is not None:
         done, dt = run(True, seconds / 2)
@@ -798,8 +879,25 @@ def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False, blocks=False
         blk = {"value": round(2 / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
                "sample": f"two anchored blocks (anchors {anchors}) of the blocks leg over random context K/V, "
                          f"float64 numpy oracle", "seconds": round(dt, 2)}
+    lng = None
+    if long_ctx:
+        # one gamma-16 block over a 32768-row context of seeded random K/V
+        rng = np.random.default_rng(20261208)
+        lc = O.OracleCache(cfg.L, 1, cfg.Hkv, cfg.d)
+        for l in range(cfg.L):
+            lc.append(l, 0, rng.normal(0, 1, (LONG_CTX, cfg.Hkv, cfg.d)), rng.normal(0, 1, (LONG_CTX, cfg.Hkv, cfg.d)))
+        toks = [np.array([0] + [cfg.mask_id] * 15)]
+        t0 = time.perf_counter()
+        hf, _ = O.draft_forward_ragged(cfg, layers, gf, lc, [16], embed=E, tokens=toks, storage=cfg.cache_dtype)
+        O.lm_head_argmax_ragged(hf, E)
+        dt = time.perf_counter() - t0
+        del lc
+        log(f"cpu baseline (long context): 1 block in {dt:.1f}s")
+        lng = {"value": round(1 / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"one draft forward + LM-head argmax over a {LONG_CTX}-row context of random K/V, float64 "
+                         f"numpy oracle", "seconds": round(dt, 2)}
     if not ragged:
-        return greedy, sampled, None, blk
+        return greedy, sampled, None, blk, lng
     # the first four sequences of the ragged leg (blocks 4, 8, 16, 32) over
     # seeded random context K/V of their batch16_ragged lengths (stand-ins for
     # an untimed ingest), one ragged pass + argmax
@@ -821,7 +919,7 @@ def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False, blocks=False
            "sample": f"one ragged pass + LM-head argmax over 4 sequences (blocks {gs}, contexts {ctx}, random "
                      f"context K/V), float64 numpy oracle",
            "drafts_per_s": round(sum(g - 1 for g in gs) / dt, 3), "seconds": round(dt, 2)}
-    return greedy, sampled, rag, blk
+    return greedy, sampled, rag, blk, lng
 
 
 if __name__ == "__main__":
