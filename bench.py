@@ -78,8 +78,8 @@ def main():
     ap.add_argument("--no-long-context", action="store_true", help="skip the 32768-token context leg")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the single-GPU path is "
-              "the scope of this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs the drafting "
+              "path on one GPU; sharding it over several is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
