@@ -37,19 +37,19 @@ METRIC = "drafted gamma=16 blocks/sec + draft fwd us at 1 GPU; % HBM BW / % MFMA
 # FETCH_SIZE reads 0.5x the copy's bytes, WRITE_SIZE 1.0x.  Valid only for the
 # default workload and only while the GEMM sources hash to ``src``; otherwise
 # the traffic is reported as null.
-LM_HEAD_COUNTERS = {"src": "f04fee123a8483cc", "config": 2, "cache": "f32",
+LM_HEAD_COUNTERS = {"src": "f04fee123a8483cc", "workload": "qwen3_8b_shape_n2048", "cache": "f32",
                     "fetch_kib": 608755.4, "write_kib": 52.0, "fetch_scale": 1.9998, "write_scale": 1.0}
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/launch.h")
 
 
-def lm_head_traffic(cfg_id, cache):
+def lm_head_traffic(workload, cache):
     import hashlib
     c = LM_HEAD_COUNTERS
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
         with open(os.path.join(ROOT, "block_diffusion_drafter_ctx_amd", f), "rb") as fh:
             h.update(fh.read())
-    if h.hexdigest()[:16] != c["src"] or cfg_id != c["config"] or cache != c["cache"]:
+    if h.hexdigest()[:16] != c["src"] or workload != c["workload"] or cache != c["cache"]:
         return None
     return int(round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024))
 
@@ -63,7 +63,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3_8b_shape_n2048", help="a workload of dflash_inputs.WORKLOADS")
     ap.add_argument("--fwd-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -88,11 +88,11 @@ def main():
     from block_diffusion_drafter_ctx_amd import binding as B
     from block_diffusion_drafter_ctx_amd import roofline as RF
     from block_diffusion_drafter_ctx_amd.runtime import DeviceDrafter, upload
-    from dflash_inputs import CONFIGS, Inputs, shrink
+    from dflash_inputs import WORKLOADS, Inputs, shrink
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.load()
-    cfg = shrink(CONFIGS[args.config], cache_dtype=args.cache)
+    cfg = shrink(WORKLOADS[args.workload], cache_dtype=args.cache)
     gamma = cfg.gamma
     n = gamma - 1
     Bn = cfg.B
@@ -290,7 +290,7 @@ def main():
                       "workgroup), one launch per step, HIP events recorded around that launch on the library "
                       "stream by dflash_profile_events",
             "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": RF.HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(lm_gbs / RF.HBM_PEAK_GBS, 4), "traffic": lm_head_traffic(args.config, cfg.cache_dtype),
+            "frac": round(lm_gbs / RF.HBM_PEAK_GBS, 4), "traffic": lm_head_traffic(args.workload, cfg.cache_dtype),
             "bytes_per_launch": lm_bytes, "us_per_launch": round(lm_us, 2),
         },
     }
@@ -492,10 +492,10 @@ def ragged_leg(cfg, dr):
     import torch
 
     from block_diffusion_drafter_ctx_amd import roofline as RF
-    from dflash_inputs import CONFIGS
+    from dflash_inputs import BATCH16_RAGGED, DEEP8_B4_N8192
 
     dev = "cuda"
-    ctx = list(CONFIGS[4].ctx)
+    ctx = list(BATCH16_RAGGED.ctx)
     gs = RAGGED_GAMMAS
     Bn, gmax, D, V = len(gs), max(gs), cfg.D, cfg.V
     stream = torch.cuda.current_stream()
@@ -651,9 +651,9 @@ def gamma_sweep_leg():
     from block_diffusion_drafter_ctx_amd import binding as B
     from block_diffusion_drafter_ctx_amd import roofline as RF
     from block_diffusion_drafter_ctx_amd.runtime import DeviceDrafter
-    from dflash_inputs import CONFIGS
+    from dflash_inputs import BATCH16_RAGGED, DEEP8_B4_N8192
 
-    cfg = CONFIGS[5]
+    cfg = DEEP8_B4_N8192
     dev = "cuda"
     gammas = list(cfg.gammas)
     gmax, Bn, N = max(gammas), cfg.B, cfg.ctx[0]
@@ -901,10 +901,10 @@ def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False, blocks=False
     # the first four sequences of the ragged leg (blocks 4, 8, 16, 32) over
     # seeded random context K/V of their batch16_ragged lengths (stand-ins for
     # an untimed ingest), one ragged pass + argmax
-    from dflash_inputs import CONFIGS
+    from dflash_inputs import BATCH16_RAGGED, DEEP8_B4_N8192
     rng = np.random.default_rng(20261202)
     gs = RAGGED_GAMMAS[:4]
-    ctx = list(CONFIGS[4].ctx[:4])
+    ctx = list(BATCH16_RAGGED.ctx[:4])
     rc = O.OracleCache(cfg.L, len(gs), cfg.Hkv, cfg.d)
     for l in range(cfg.L):
         for b, n in enumerate(ctx):

@@ -74,22 +74,19 @@ def _ragged_lens(cid: int, B: int, lo: int, hi: int) -> tuple:
 
 _QWEN = dict(D=4096, Hq=32, Hkv=8, d=128, F=12288, V=151936)
 
-CONFIGS = {
-    1: Config(name="tiny_f32", cid=1, dtype="f32", D=256, L=1, Hq=4, Hkv=4, d=64, F=768,
-              V=1024, B=1, ctx=(128,), gammas=(16,)),
-    2: Config(name="qwen3_8b_shape_n2048", cid=2, dtype="bf16", L=5, B=1, ctx=(2048,),
-              gammas=(16,), **_QWEN),
-    3: Config(name="long_ctx_n32768", cid=3, dtype="bf16", L=5, B=1, ctx=(32768,),
-              gammas=(16,), **_QWEN),
-    4: Config(name="batch16_ragged", cid=4, dtype="bf16", L=5, B=16,
-              ctx=_ragged_lens(4, 16, 1024, 4096), gammas=(16,), **_QWEN),
-    5: Config(name="deep8_b4_n8192", cid=5, dtype="bf16", L=8, B=4, ctx=(8192,) * 4,
-              gammas=(8, 16, 32), match="linear", **_QWEN),
-}
+# The five workloads, named by what they are (cid seeds their inputs).
+TINY_F32 = Config(name="tiny_f32", cid=1, dtype="f32", D=256, L=1, Hq=4, Hkv=4, d=64, F=768,
+                  V=1024, B=1, ctx=(128,), gammas=(16,))
+QWEN3_8B_N2048 = Config(name="qwen3_8b_shape_n2048", cid=2, dtype="bf16", L=5, B=1, ctx=(2048,),
+                        gammas=(16,), **_QWEN)
+LONG_CTX_N32768 = Config(name="long_ctx_n32768", cid=3, dtype="bf16", L=5, B=1, ctx=(32768,),
+                         gammas=(16,), **_QWEN)
+BATCH16_RAGGED = Config(name="batch16_ragged", cid=4, dtype="bf16", L=5, B=16,
+                        ctx=_ragged_lens(4, 16, 1024, 4096), gammas=(16,), **_QWEN)
+DEEP8_B4_N8192 = Config(name="deep8_b4_n8192", cid=5, dtype="bf16", L=8, B=4, ctx=(8192,) * 4,
+                        gammas=(8, 16, 32), match="linear", **_QWEN)
 
-
-def get_config(i: int) -> Config:
-    return CONFIGS[i]
+WORKLOADS = {c.name: c for c in (TINY_F32, QWEN3_8B_N2048, LONG_CTX_N32768, BATCH16_RAGGED, DEEP8_B4_N8192)}
 
 
 def shrink(cfg: Config, **kw) -> Config:

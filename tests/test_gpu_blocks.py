@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from block_diffusion_drafter_ctx_amd import binding as B
-from dflash_inputs import CONFIGS, shrink
+from dflash_inputs import BATCH16_RAGGED, DEEP8_B4_N8192, LONG_CTX_N32768, QWEN3_8B_N2048, TINY_F32, shrink
 from oracle import dflash_oracle as O
 from tests.parity_util import GAP_MIN, GAP_MIN_BF16_CACHE, Workload, argmax_agree, close, close_stored, log
 
@@ -27,7 +27,7 @@ def small(**kw):
     base = dict(name="small_bf16_blocks", cid=130, D=512, L=2, Hq=8, Hkv=2, d=128, F=1536, V=1000, B=2,
                 ctx=(37, 300), gammas=(16,), gain_std=0.1, iters=1, append_rows=0)
     base.update(kw)
-    return shrink(CONFIGS[2], **base)
+    return shrink(QWEN3_8B_N2048, **base)
 
 
 def block_rows(blocks, lens, g, pairs):
@@ -136,14 +136,14 @@ def test_blocks_head64():
 def test_blocks_f32():
     blocks = [(0, 100), (0, 3), (0, 128)]
     log("anchored blocks, tiny fp32 drafter")
-    cfg = shrink(CONFIGS[1], cid=133, gain_std=0.1, append_rows=0)
+    cfg = shrink(TINY_F32, cid=133, gain_std=0.1, append_rows=0)
     Blocks(cfg, blocks, 16, override=True).run_blocks()
 
 
 def test_blocks_full_qwen_shape():
     # the Qwen3-8B-shaped drafter at a 2048-token context, 8 blocks anchored in
     # its second half (the response part of a training sequence): 128 block rows
-    cfg = shrink(CONFIGS[2], cid=134, append_rows=0)
+    cfg = shrink(QWEN3_8B_N2048, cid=134, append_rows=0)
     rng = np.random.default_rng(134)
     anchors = sorted(rng.integers(1024, 2049, 8).tolist())
     log(f"anchored blocks, full shape, anchors {anchors}")

@@ -5,7 +5,7 @@ import torch
 
 from block_diffusion_drafter_ctx_amd import binding as B
 from block_diffusion_drafter_ctx_amd.runtime import upload
-from dflash_inputs import CONFIGS, Inputs, shrink
+from dflash_inputs import BATCH16_RAGGED, DEEP8_B4_N8192, LONG_CTX_N32768, QWEN3_8B_N2048, TINY_F32, Inputs, shrink
 from tests.parity_util import Workload, close, log
 
 pytestmark = pytest.mark.gpu
@@ -24,7 +24,7 @@ def small(**kw):
     base = dict(name="small_bf16", cid=101, D=512, L=2, Hq=8, Hkv=2, d=128, F=1536, V=1000, B=3,
                 ctx=(37, 300, 1), gammas=(16,), gain_std=0.1, iters=2)
     base.update(kw)
-    return shrink(CONFIGS[2], **base)
+    return shrink(QWEN3_8B_N2048, **base)
 
 
 def test_small_bf16_tokens():
@@ -125,14 +125,14 @@ def test_tile_order_bit_identical(monkeypatch):
         assert torch.equal(a, b)
 
 
-def test_config1_f32():
-    cfg = CONFIGS[1]
-    log("config 1: tiny fp32 drafter")
+def test_tiny_f32():
+    cfg = TINY_F32
+    log("tiny_f32: tiny fp32 drafter")
     Workload(cfg, cfg.gamma, 3).run()
 
 
-def test_config1_f32_override():
-    cfg = shrink(CONFIGS[1], cid=105, gain_std=0.1)
+def test_tiny_f32_override():
+    cfg = shrink(TINY_F32, cid=105, gain_std=0.1)
     Workload(cfg, cfg.gamma, 1, override=True).run()
 
 
@@ -186,23 +186,23 @@ def test_errors_enqueue_nothing():
 
 
 @pytest.mark.timeout(900)
-def test_config2_full():
-    cfg = CONFIGS[2]
-    log("config 2 full size (Qwen3-8B-shaped, N=2048), 2 iterations")
+def test_qwen3_8b_n2048():
+    cfg = QWEN3_8B_N2048
+    log("qwen3_8b_shape_n2048 full size (N=2048), 2 iterations")
     Workload(cfg, 16, 2).run()
 
 
 @pytest.mark.timeout(900)
-def test_config2_full_override():
-    cfg = shrink(CONFIGS[2], cid=202)
-    log("config 2 full size with distinct block rows (argmax on 15 different rows)")
+def test_qwen3_8b_n2048_override():
+    cfg = shrink(QWEN3_8B_N2048, cid=202)
+    log("qwen3_8b_shape_n2048 full size with distinct block rows (argmax on 15 different rows)")
     Workload(cfg, 16, 1, override=True).run()
 
 
 @pytest.mark.timeout(900)
-def test_config2_full_bf16_cache():
-    cfg = shrink(CONFIGS[2], cid=203, cache_dtype="bf16")
-    log("config 2 full size, bf16 H_t / KV cache, distinct block rows")
+def test_qwen3_8b_n2048_bf16_cache():
+    cfg = shrink(QWEN3_8B_N2048, cid=203, cache_dtype="bf16")
+    log("qwen3_8b_shape_n2048 full size, bf16 H_t / KV cache, distinct block rows")
     Workload(cfg, 16, 1, override=True).run()
 
 
@@ -251,29 +251,29 @@ def test_bf16_storage_rounding_is_rne():
 
 
 @pytest.mark.timeout(1200)
-def test_config3_full():
-    cfg = CONFIGS[3]
-    log("config 3 full size: 32768-row context, 1 iteration + append")
+def test_long_ctx_n32768():
+    cfg = LONG_CTX_N32768
+    log("long_ctx_n32768 full size: 32768-row context, 1 iteration + append")
     Workload(cfg, 16, 1).run()
 
 
 @pytest.mark.timeout(1200)
-def test_config3_full_bf16_cache():
-    cfg = shrink(CONFIGS[3], cid=303, cache_dtype="bf16")
-    log("config 3 full size with a bf16 H_t / KV cache: 32768-row context, 1 iteration + append")
+def test_long_ctx_n32768_bf16_cache():
+    cfg = shrink(LONG_CTX_N32768, cid=303, cache_dtype="bf16")
+    log("long_ctx_n32768 full size with a bf16 H_t / KV cache: 32768-row context, 1 iteration + append")
     Workload(cfg, 16, 1).run()
 
 
 @pytest.mark.timeout(1200)
-def test_config4_full():
-    cfg = CONFIGS[4]
-    log(f"config 4 full size: 16 ragged sequences {list(cfg.ctx)}, 1 iteration + append")
+def test_batch16_ragged():
+    cfg = BATCH16_RAGGED
+    log(f"batch16_ragged full size: 16 ragged sequences {list(cfg.ctx)}, 1 iteration + append")
     Workload(cfg, 16, 1).run()
 
 
 @pytest.mark.timeout(1200)
-def test_config5_full_gamma_sweep():
-    cfg = CONFIGS[5]
-    log("config 5 full size: 8 layers, 4 x 8192 context, gamma 8 / 16 / 32 on one cache")
+def test_deep8_b4_n8192_gamma_sweep():
+    cfg = DEEP8_B4_N8192
+    log("deep8_b4_n8192 full size: 8 layers, 4 x 8192 context, gamma 8 / 16 / 32 on one cache")
     w = Workload(cfg, max(cfg.gammas), 1)
     w.run_gammas(list(cfg.gammas))

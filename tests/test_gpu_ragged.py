@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from block_diffusion_drafter_ctx_amd import binding as B
-from dflash_inputs import CONFIGS, shrink
+from dflash_inputs import BATCH16_RAGGED, DEEP8_B4_N8192, LONG_CTX_N32768, QWEN3_8B_N2048, TINY_F32, shrink
 from oracle import dflash_oracle as O
 from tests.parity_util import (GAP_MIN, GAP_MIN_BF16_CACHE, TOL, Workload, argmax_agree, close, close_stored,
                                log)
@@ -32,7 +32,7 @@ def small(**kw):
     base = dict(name="small_bf16_ragged", cid=120, D=512, L=2, Hq=8, Hkv=2, d=128, F=1536, V=1000, B=4,
                 ctx=(37, 300, 1, 64), gammas=(16,), gain_std=0.1, iters=1)
     base.update(kw)
-    return shrink(CONFIGS[2], **base)
+    return shrink(QWEN3_8B_N2048, **base)
 
 
 class Ragged(Workload):
@@ -135,7 +135,7 @@ def test_ragged_head64():
 
 def test_ragged_f32():
     log("ragged tiny fp32 drafter")
-    cfg = shrink(CONFIGS[1], cid=123, B=3, ctx=(128, 40, 0), gain_std=0.1)
+    cfg = shrink(TINY_F32, cid=123, B=3, ctx=(128, 40, 0), gain_std=0.1)
     Ragged(cfg, [16, 4, 9], override=True).run_ragged()
 
 
@@ -166,7 +166,7 @@ def test_ragged_equal_lengths_match_uniform_bit_for_bit():
 def test_ragged_full_batch16():
     # the batch16_ragged workload (16 sequences, contexts U[1024, 4096]) at the
     # full Qwen3-8B shape, with block lengths 4, 8, 16, 32 cycling over it
-    cfg = CONFIGS[4]
+    cfg = BATCH16_RAGGED
     gammas = [4, 8, 16, 32] * 4
     log(f"ragged full batch16: gammas {gammas}")
     Ragged(cfg, gammas).run_ragged()

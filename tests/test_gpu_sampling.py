@@ -24,7 +24,7 @@ import torch
 
 from block_diffusion_drafter_ctx_amd import binding as B
 from block_diffusion_drafter_ctx_amd.runtime import dims_of, upload
-from dflash_inputs import CONFIGS, Inputs, build_target_logits_np, shrink
+from dflash_inputs import BATCH16_RAGGED, QWEN3_8B_N2048, TINY_F32, Inputs, build_target_logits_np, shrink
 from oracle import dflash_oracle as O
 from tests.parity_util import close, log
 
@@ -120,24 +120,24 @@ def check_accept(tag, tau_g, nxt_g, d, z, t, T, au, ru):
 
 # ------------------------------------------------------------------ drafting
 DRAFT_CASES = [
-    # name, config, overrides, gamma, T
-    ("f32_c1_T1", 1, dict(), 16, 1.0),
-    ("f32_c1_b3_g9_T06", 1, dict(B=3), 9, 0.6),
-    ("bf16_rk_m15", 2, dict(D=2048, V=20000, B=1), 16, 1.0),
-    ("bf16_rk_m16_ragged_v", 2, dict(D=2048, V=20001, B=1), 17, 0.8),
-    ("bf16_rk_m1", 2, dict(D=2048, V=20000, B=1), 2, 1.3),
-    ("bf16_rk_chunks_m30", 2, dict(D=2048, V=20001, B=2), 16, 1.0),
-    ("bf16_stream_m60", 2, dict(D=2048, V=20000, B=4), 16, 1.0),
-    ("bf16_tiled_m75_ragged_v", 2, dict(D=2048, V=20001, B=5), 16, 1.0),
-    ("bf16_small_v", 2, dict(D=256, V=1000, B=2), 16, 0.5),
-    ("bf16_rk_hot_T", 2, dict(D=2048, V=20000, B=1), 16, 25.0),
-    ("bf16_rk_cold_T", 2, dict(D=2048, V=20000, B=1), 16, 0.05),
+    # name, workload, overrides, gamma, T
+    ("f32_tiny_T1", TINY_F32, dict(), 16, 1.0),
+    ("f32_tiny_b3_g9_T06", TINY_F32, dict(B=3), 9, 0.6),
+    ("bf16_rk_m15", QWEN3_8B_N2048, dict(D=2048, V=20000, B=1), 16, 1.0),
+    ("bf16_rk_m16_ragged_v", QWEN3_8B_N2048, dict(D=2048, V=20001, B=1), 17, 0.8),
+    ("bf16_rk_m1", QWEN3_8B_N2048, dict(D=2048, V=20000, B=1), 2, 1.3),
+    ("bf16_rk_chunks_m30", QWEN3_8B_N2048, dict(D=2048, V=20001, B=2), 16, 1.0),
+    ("bf16_stream_m60", QWEN3_8B_N2048, dict(D=2048, V=20000, B=4), 16, 1.0),
+    ("bf16_tiled_m75_ragged_v", QWEN3_8B_N2048, dict(D=2048, V=20001, B=5), 16, 1.0),
+    ("bf16_small_v", QWEN3_8B_N2048, dict(D=256, V=1000, B=2), 16, 0.5),
+    ("bf16_rk_hot_T", QWEN3_8B_N2048, dict(D=2048, V=20000, B=1), 16, 25.0),
+    ("bf16_rk_cold_T", QWEN3_8B_N2048, dict(D=2048, V=20000, B=1), 16, 0.05),
 ]
 
 
-@pytest.mark.parametrize("name,cid,kw,gamma,T", DRAFT_CASES, ids=[c[0] for c in DRAFT_CASES])
-def test_sample_drafts(name, cid, kw, gamma, T):
-    cfg = shrink(CONFIGS[cid], **kw) if kw else CONFIGS[cid]
+@pytest.mark.parametrize("name,base,kw,gamma,T", DRAFT_CASES, ids=[c[0] for c in DRAFT_CASES])
+def test_sample_drafts(name, base, kw, gamma, T):
+    cfg = shrink(base, **kw) if kw else base
     log(f"sample_drafts {name}: B={cfg.B} gamma={gamma} D={cfg.D} V={cfg.V} T={T} {cfg.dtype}")
     head = Head(cfg, gamma)
     h = head.inp.final_states(gamma)
@@ -150,12 +150,11 @@ def test_sample_drafts(name, cid, kw, gamma, T):
     check_drafts(name, cfg, T, d_g, z_g, l_g, d_o, z_o, l_o, gap_o)
 
 
-@pytest.mark.parametrize("cid", [2, 4])
-def test_sample_drafts_full(cid):
+@pytest.mark.parametrize("cfg", [QWEN3_8B_N2048, BATCH16_RAGGED], ids=lambda c: c.name)
+def test_sample_drafts_full(cfg):
     """The full-size LM head (V = 151936, D = 4096): one sequence (the register-K
     kernel with the sampling epilogue, as timed) and 16 sequences (tiled GEMM,
     then the row-statistics pass)."""
-    cfg = CONFIGS[cid]
     gamma, T = 16, 1.0
     log(f"sample_drafts full config {cfg.name}: B={cfg.B}")
     head = Head(cfg, gamma)
@@ -171,7 +170,7 @@ def test_sample_drafts_full(cid):
 
 
 def test_sample_drafts_deterministic():
-    cfg = shrink(CONFIGS[2], D=2048, V=20000, B=1)
+    cfg = shrink(QWEN3_8B_N2048, D=2048, V=20000, B=1)
     head = Head(cfg, 16)
     h = _dev(head.inp.final_states(16))
     u = _dev(head.inp.sample_uniforms(0, 16)[0])
@@ -207,7 +206,7 @@ def _accept_inputs(cfg, gamma, T, it=0):
 
 @pytest.mark.parametrize("name,V,Bn,gamma,T,with_lse", ACCEPT_CASES, ids=[c[0] for c in ACCEPT_CASES])
 def test_sample_accept(name, V, Bn, gamma, T, with_lse):
-    cfg = shrink(CONFIGS[2], V=V, B=Bn)
+    cfg = shrink(QWEN3_8B_N2048, V=V, B=Bn)
     log(f"sample_accept {name}: B={Bn} gamma={gamma} V={V} T={T} lse={'given' if with_lse else 'computed'}")
     z, t, d, au, ru = _accept_inputs(cfg, gamma, T)
     z_d = _dev(z)
@@ -221,7 +220,7 @@ def test_sample_accept(name, V, Bn, gamma, T, with_lse):
 
 def test_sample_accept_edges():
     V, Bn, gamma, T = 4096, 6, 12, 1.0
-    cfg = shrink(CONFIGS[2], V=V, B=Bn)
+    cfg = shrink(QWEN3_8B_N2048, V=V, B=Bn)
     dims = dims_of(cfg)
     z, t, d, au, ru = _accept_inputs(cfg, gamma, T, it=3)
     n = gamma - 1
@@ -262,10 +261,10 @@ def test_sample_accept_edges():
 
 
 # ------------------------------------------------------------------ chained
-def test_sample_chain_config2():
+def test_sample_chain_qwen3_8b_n2048():
     """Draft, then verify, at the full Qwen3-8B-shaped LM head: each side builds
     its target logits from its own draft logits plus the same seeded noise."""
-    cfg = CONFIGS[2]
+    cfg = QWEN3_8B_N2048
     gamma, T = 16, 1.0
     head = Head(cfg, gamma)
     h = head.inp.final_states(gamma)

@@ -1,12 +1,12 @@
 """Seeded input generators: determinism, storage exactness and workload shapes."""
 import numpy as np
 
-from dflash_inputs import CONFIGS, Inputs, bf16_round_f32, build_target_np, shrink
+from dflash_inputs import BATCH16_RAGGED, DEEP8_B4_N8192, LONG_CTX_N32768, QWEN3_8B_N2048, TINY_F32, Inputs, bf16_round_f32, build_target_np, shrink
 from dflash_inputs.gen import CHUNK
 
 
 def test_seeded_and_storage_exact():
-    cfg = shrink(CONFIGS[2], D=256, F=512, V=1000, L=2, ctx=(40,))
+    cfg = shrink(QWEN3_8B_N2048, D=256, F=512, V=1000, L=2, ctx=(40,))
     a, b = Inputs(cfg), Inputs(cfg)
     assert np.array_equal(a.w_qkv(1), b.w_qkv(1))
     assert not np.array_equal(a.w_qkv(0), a.w_qkv(1))
@@ -16,12 +16,12 @@ def test_seeded_and_storage_exact():
     assert abs(w.std() - 0.02) < 0.002
     h = a.ctx_states()
     assert len(h) == 5 and h[0].shape == (40, 256) and abs(h[0].std() - 1) < 0.1
-    f32 = Inputs(CONFIGS[1]).w_c()
+    f32 = Inputs(TINY_F32).w_c()
     assert not np.array_equal(f32, bf16_round_f32(f32.copy()))  # fp32 workload keeps fp32
 
 
 def test_chunked_generation_is_chunk_local():
-    cfg = shrink(CONFIGS[2], D=2048, V=4096, ctx=(8,))
+    cfg = shrink(QWEN3_8B_N2048, D=2048, V=4096, ctx=(8,))
     e = Inputs(cfg).embed()              # 8M elements -> 2 chunks
     assert e.size > CHUNK
     e2 = Inputs(cfg).embed()
@@ -29,17 +29,17 @@ def test_chunked_generation_is_chunk_local():
 
 
 def test_workload_shapes():
-    c4 = CONFIGS[4]
+    c4 = BATCH16_RAGGED
     assert c4.B == 16 and len(c4.ctx) == 16
     assert all(1024 <= n <= 4096 for n in c4.ctx)
-    assert CONFIGS[5].gammas == (8, 16, 32)
-    p = CONFIGS[5].match_probs(16)
+    assert DEEP8_B4_N8192.gammas == (8, 16, 32)
+    p = DEEP8_B4_N8192.match_probs(16)
     assert np.isclose(p[0], 0.9) and np.isclose(p[-1], 0.5)
-    assert np.allclose(CONFIGS[2].match_probs(16), 0.8)
+    assert np.allclose(QWEN3_8B_N2048.match_probs(16), 0.8)
 
 
 def test_block_tokens_and_targets():
-    cfg = CONFIGS[4]
+    cfg = BATCH16_RAGGED
     inp = Inputs(cfg)
     t = inp.block_tokens(16)
     assert t.shape == (16, 16) and np.all(t[:, 1:] == cfg.V - 1)
@@ -53,7 +53,7 @@ def test_block_tokens_and_targets():
 
 
 def test_sampling_uniforms_open_and_exact():
-    cfg = shrink(CONFIGS[2], V=5000, B=2)
+    cfg = shrink(QWEN3_8B_N2048, V=5000, B=2)
     inp = Inputs(cfg)
     g, a, e = inp.sample_uniforms(0, 16)
     assert g.shape == (2, 15, 5000) and a.shape == (2, 15) and e.shape == (2, 5000)
@@ -69,7 +69,7 @@ def test_sampling_uniforms_open_and_exact():
 
 def test_synthetic_target_logits():
     from dflash_inputs import build_target_logits_np
-    cfg = shrink(CONFIGS[2], V=3000, B=2)
+    cfg = shrink(QWEN3_8B_N2048, V=3000, B=2)
     inp = Inputs(cfg)
     z = inp.synthetic_logits(0, 16, 1.28)
     nz = inp.target_noise(0, 16)
