@@ -201,7 +201,10 @@ def main():
     taus = tau.cpu().numpy()
 
     # ---- every other kernel role over one cycle of steps (outside the timed region)
-    es0, cs0 = (2 if cfg.dtype == "bf16" else 4), (2 if cfg.cache_dtype == "bf16" else 4)
+    # algorithmic bytes count the method's own K/V type (bf16 for a bf16 drafter)
+    # whatever the cache holds: an fp32 cache's extra bytes are overhead
+    es0 = 2 if cfg.dtype == "bf16" else 4
+    cs0 = es0
     M = Bn * gamma
     T_app = Bn * cfg.append_rows
     nqkv = (cfg.Hq + 2 * cfg.Hkv) * cfg.d
@@ -244,7 +247,7 @@ def main():
 
     # ---- roofline of the dominant kernel: LM head GEMM + argmax
     es = RF.elem_bytes(cfg.dtype)
-    cs = RF.elem_bytes(cfg.cache_dtype)
+    cs = es                                   # the method's K/V bytes (see above)
     lm_bytes = RF.lm_head_bytes(V, cfg.D, Bn * n, es)
     lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
     step_bytes = (RF.draft_forward_bytes(cfg.D, cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.F, V, Bn, gamma,
@@ -547,7 +550,7 @@ def ragged_leg(cfg, dr):
     rag_us = timeit(ragged)
     pad_us = timeit(padded)
     es = RF.elem_bytes(cfg.dtype)
-    cs = RF.elem_bytes(cfg.cache_dtype)
+    cs = es                                   # the method's K/V bytes
     rb = RF.draft_forward_bytes_ragged(D, cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.F, V, gs, ctx, es, cs)
     log(f"ragged: 16 sequences, blocks {sorted(set(gs))}: {rag_us:.1f} us vs {pad_us:.1f} us padded to {gmax}")
     del cache
@@ -623,7 +626,8 @@ def long_context_leg(cfg, dr):
     B.profile_events(B.PROF_ATTENTION, [], [])
     us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
     att_us = float(np.median([a.elapsed_time(b) for a, b in pairs])) * 1e3
-    es, cs = RF.elem_bytes(cfg.dtype), RF.elem_bytes(cfg.cache_dtype)
+    es = RF.elem_bytes(cfg.dtype)
+    cs = es                                   # the method's K/V bytes
     nbytes = RF.draft_forward_bytes(cfg.D, cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.F, cfg.V, 1, g, [N], es, cs)
     att_bytes = (N + g) * 2 * cfg.Hkv * cfg.d * cs
     log(f"long context: {N}-token context, draft fwd + argmax {us:.1f} us, attention {att_us:.1f} us per layer "
@@ -669,7 +673,8 @@ def gamma_sweep_leg():
     dr.inject(H_t, list(cfg.ctx), cache)
     del states, H_t
     stream = torch.cuda.current_stream()
-    es, cs = RF.elem_bytes(cfg.dtype), RF.elem_bytes(cfg.cache_dtype)
+    es = RF.elem_bytes(cfg.dtype)
+    cs = es                                   # the method's K/V bytes
     res = {}
     for g in gammas:
         tok = torch.full((Bn, g), cfg.mask_id, dtype=torch.int32, device=dev)
@@ -754,7 +759,7 @@ def blocks_leg(cfg, dr):
     M = nb * g
     flops = 2 * M * cfg.L * (RF.layer_weight_elems(cfg.D, cfg.Hq, cfg.Hkv, cfg.d, cfg.F) - 2 * D) + \
         cfg.L * sum(4 * cfg.Hq * g * (a + g) * cfg.d for a in anchors)
-    cs = RF.elem_bytes(cfg.cache_dtype)
+    cs = RF.elem_bytes(cfg.dtype)             # the method's K/V bytes
     nbytes = (cfg.L * RF.layer_weight_elems(cfg.D, cfg.Hq, cfg.Hkv, cfg.d, cfg.F) * RF.elem_bytes(cfg.dtype)
               + cfg.L * sum(a + g for a in anchors) * 2 * cfg.Hkv * cfg.d * cs + M * D * 4 * 2)
     log(f"blocks: {nb} blocks of {g} rows in a {BLOCKS_CTX}-token context: {us:.1f} us")

@@ -40,7 +40,7 @@ class Weights(ctypes.Structure):
 
 class KVCache(ctypes.Structure):
     _fields_ = [("k", c_void_p), ("v", c_void_p), ("B", c_int32), ("cap", c_int32),
-                ("len", POINTER(c_int32))]
+                ("len", POINTER(c_int32)), ("len_dev", c_void_p)]
 
 
 class DFlashError(RuntimeError):

@@ -546,13 +546,8 @@ size_t attn_dma_lds() {
 template <int HD, int NG>
 hipError_t launch_dma(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   const size_t lds = attn_dma_lds<HD, NG>();
-  static bool set = false;   // per instantiation
-  if (!set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_dma_kernel<HD, NG>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    set = true;
-  }
+  const hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(attn_dma_kernel<HD, NG>), static_cast<int>(lds));
+  if (e != hipSuccess) return e;
   const int rows = 16 * 8 / NG;   // query rows per workgroup
   hipLaunchKernelGGL((attn_dma_kernel<HD, NG>), dim3(p.items, (a.R + rows - 1) / rows), dim3(512), lds, st, a);
   return hipGetLastError();
@@ -802,6 +797,7 @@ hipError_t launch_attention(const AttnArgs& a0, const AttnPlan& p, bool bf16_wei
   hipError_t e;
   if (bf16_cache) {
     // the DMA kernel's per-lane byte offsets into one head's K or V are 32-bit
+    // (the entry points reject such caches before any launch)
     if (static_cast<int64_t>(a.cap) * a.d * 2 >= (int64_t{1} << 32)) return hipErrorInvalidValue;
     const bool two = a.R <= 64;
     e = a.d == 128 ? (two ? launch_dma<128, 2>(a, p, st) : launch_dma<128, 1>(a, p, st))

@@ -90,16 +90,23 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void*)p)));
 }
 
+// M0 is declared as an output of the statement (written by its s_mov, read by
+// the load when it issues) rather than as a clobber: the compiler then knows
+// the statement overwrites it.  The load itself writes no register.
+
 // lane l reads src (its own address) into LDS lds_frag + 16 l (lds_frag wave-uniform)
 __device__ __forceinline__ void load_frag_to_lds(const void* src, uint4* lds_frag) {
   const unsigned la = lds_addr(lds_frag);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(la) : "memory", "m0");
+  unsigned m0_set;
+  asm volatile("s_mov_b32 %0, %2\n\tglobal_load_lds_dwordx4 %1, off" : "={m0}"(m0_set) : "v"(src), "s"(la) : "memory");
 }
 
 // lane l reads base + voff (base wave-uniform, in scalar registers; voff a byte
 // offset) into LDS byte address m0 + 16 l
 __device__ __forceinline__ void load_to_lds_sbase(uint32_t voff, const void* base, unsigned m0) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(m0) : "memory", "m0");
+  unsigned m0_set;
+  asm volatile("s_mov_b32 %0, %3\n\tglobal_load_lds_dwordx4 %1, %2" : "={m0}"(m0_set) : "v"(voff), "s"(base), "s"(m0)
+               : "memory");
 }
 
 // s_waitcnt with vmcnt = n (the other counters at their maximum): gfx9 encoding

@@ -102,9 +102,21 @@ dflash_status check_cache(const dflash_kv_cache* c) {
   DF_REQUIRE(aligned16(c->k) && aligned16(c->v), DFLASH_ERR_INVALID_ARG, "cache k/v must be 16-byte aligned");
   DF_REQUIRE(c->cap >= 32 && c->cap % 32 == 0, DFLASH_ERR_INVALID_ARG, "cache->cap=%d must be a positive multiple of 32",
              c->cap);
+  DF_REQUIRE((reinterpret_cast<uintptr_t>(c->len_dev) & 3u) == 0, DFLASH_ERR_INVALID_ARG,
+             "cache->len_dev must be 4-byte aligned");
   for (int b = 0; b < c->B; ++b)
     DF_REQUIRE(c->len[b] >= 0 && c->len[b] <= c->cap, DFLASH_ERR_INVALID_ARG, "cache->len[%d]=%d outside [0, cap]",
                b, c->len[b]);
+  return DFLASH_OK;
+}
+
+// Shape limits of the attention kernels for a cache (checked before any launch).
+dflash_status check_attention_cache(const dflash_dims* d, const dflash_kv_cache* c) {
+  // the bf16-cache kernel addresses one head's K or V with 32-bit byte offsets
+  DF_REQUIRE(d->cache_dtype != DFLASH_BF16 ||
+                 static_cast<int64_t>(c->cap) * d->head_dim * 2 < (int64_t{1} << 32),
+             DFLASH_ERR_UNSUPPORTED, "a bf16 cache needs cap * head_dim * 2 < 2^32 (cap=%d, head_dim=%d)", c->cap,
+             d->head_dim);
   return DFLASH_OK;
 }
 
@@ -654,6 +666,8 @@ dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w,
       (void)hi;
     }
     sa.rows.row_off[cache->B] = M;
+    sa.len_dev = r0 + kRowBlock >= T ? cache->len_dev : nullptr;   // the last pass updates the mirror
+    for (int b = 0; b < cache->B; ++b) sa.len_new[b] = cache->len[b] + rows_per_seq[b];
     DF_HIP(launch_scatter_kv(sa, cbf, s));
   }
   for (int b = 0; b < cache->B; ++b) cache->len[b] += rows_per_seq[b];
@@ -703,6 +717,7 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
   }
   if ((st = check_ptr(h_final, "h_final")) != DFLASH_OK) return st;
   const int B = qg.n;   // query groups (sequences, or anchored blocks)
+  if ((st = check_attention_cache(dims, cache)) != DFLASH_OK) return st;
   const DraftWs lay = draft_ws(dims, B, M, gmax);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != DFLASH_OK) return st;
   if ((st = check_device()) != DFLASH_OK) return st;

@@ -117,6 +117,8 @@ __global__ __launch_bounds__(1024) void ctx_norm_kernel(const float* part, int S
 // threads of a column group write 16 consecutive cache positions.
 template <typename T>
 __global__ __launch_bounds__(256) void scatter_kv_kernel(ScatterArgs a) {
+  if (a.len_dev != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < a.B)
+    a.len_dev[threadIdx.x] = a.len_new[threadIdx.x];
   const int rr = threadIdx.x & 15, cg = threadIdx.x >> 4;
   const int r = blockIdx.y * 16 + rr, n = blockIdx.x * 64 + 4 * cg;
   if (r >= a.M || n >= a.N) return;

@@ -23,6 +23,11 @@
 
 #include <stdlib.h>
 
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace dflash {
 namespace {
 
@@ -943,13 +948,8 @@ hipError_t launch_v(const GemmArgs& a, const GemmPlan& p, hipStream_t st) {
   constexpr int HL = (AK == A_F32_SPLIT) ? 2 : 1;
   const size_t lds = static_cast<size_t>(KR / 32) * (MT / 16) * HL * 64 * sizeof(uint4);
   auto kern = gemm_stream_kernel<MT, AK, WAVES, KR>;
-  static bool attr_set = false;   // one-time opt-in to large dynamic LDS for this instantiation
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(kern), static_cast<int>(lds));
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * WAVES), lds, st, a);
   return hipGetLastError();
 }
@@ -967,18 +967,53 @@ hipError_t launch_mt(const GemmArgs& a, GemmAKind ak, const GemmPlan& p, hipStre
 }
 
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);   // every thread computes the same value
   }
-  return cus[dev];
+  return n;
 }
 
 }  // namespace
+
+namespace {
+std::mutex g_attr_mu;
+std::map<std::pair<int, const void*>, int> g_dyn_lds;    // (device, kernel) -> limit set
+std::map<std::pair<int, const void*>, int> g_lds_room;   // (device, kernel) -> room computed
+}  // namespace
+
+hipError_t ensure_dyn_lds(const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  auto it = g_dyn_lds.find({dev, fn});
+  if (it != g_dyn_lds.end() && it->second >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) g_dyn_lds[{dev, fn}] = bytes;
+  return e;
+}
+
+int dyn_lds_room(const void* fn, int lds_bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  auto it = g_lds_room.find({dev, fn});
+  if (it != g_lds_room.end()) return it->second;
+  int cap = 0;
+  hipFuncAttributes fa{};
+  if (hipFuncGetAttributes(&fa, fn) == hipSuccess && fa.sharedSizeBytes + 1024 < static_cast<size_t>(lds_bytes)) {
+    cap = static_cast<int>(lds_bytes - fa.sharedSizeBytes) / 1024 * 1024;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, cap) != hipSuccess) cap = 0;
+  }
+  g_lds_room[{dev, fn}] = cap;
+  if (cap > 0) g_dyn_lds[{dev, fn}] = cap;
+  return cap;
+}
 
 // Tile = 16 rows per wave x WAVES.  The split-K count S and the wave count are
 // chosen by a small cost model.  The persistent grid (workgroups resident at
@@ -1094,13 +1129,9 @@ hipError_t launch_tile_lds(GemmArgs a, dim3 grid, hipStream_t st, float* top2 = 
     const long T = static_cast<long>(grid.x) * grid.y * grid.z;
     grid = dim3(static_cast<unsigned>((T + 7) / 8 * 8));
   }
-  static bool set = false;   // per instantiation
-  if (!set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    set = true;
-  }
+  const hipError_t e = ensure_dyn_lds(
+      reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2>), static_cast<int>(lds));
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2>), grid, dim3((TN / WN) * (TM / WM) * 64), lds,
                      st, a, top2);
   return hipGetLastError();
@@ -1139,22 +1170,13 @@ hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p,
     const size_t lds = static_cast<size_t>(2) * ((kTileN / 16) * 2 + (kTileM / 16) * 2 * hl) * 64 * sizeof(uint4);
     const dim3 grid(p.ntiles, p.mtiles, p.S);
     if (ak == A_BF16) {
-      static bool set_b = false;
-      if (!set_b) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_kernel<A_BF16>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-        set_b = true;
-      }
+      const hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(gemm_tile_kernel<A_BF16>), static_cast<int>(lds));
+      if (e != hipSuccess) return e;
       hipLaunchKernelGGL(gemm_tile_kernel<A_BF16>, grid, dim3(256), lds, st, a);
     } else {
-      static bool set_f = false;
-      if (!set_f) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_tile_kernel<A_F32_SPLIT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-        set_f = true;
-      }
+      const hipError_t e =
+          ensure_dyn_lds(reinterpret_cast<const void*>(gemm_tile_kernel<A_F32_SPLIT>), static_cast<int>(lds));
+      if (e != hipSuccess) return e;
       hipLaunchKernelGGL(gemm_tile_kernel<A_F32_SPLIT>, grid, dim3(256), lds, st, a);
     }
     return hipGetLastError();
@@ -1286,17 +1308,7 @@ GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
 template <int KS, int EP, int T, int AK = A_F32_SPLIT>
 hipError_t rk_launch(GemmArgs a, const GemmPlan& p, float* top2, float* logits, hipStream_t st) {
   const void* kern = reinterpret_cast<const void*>(&gemm_rk_kernel<KS, EP, T, AK>);
-  static int stage_cap = -1;   // per instantiation: dynamic LDS bytes it may use (0: none)
-  if (stage_cap < 0) {
-    int cap = 0;
-    hipFuncAttributes fa{};
-    if (EP != RK_TOP2 && hipFuncGetAttributes(&fa, kern) == hipSuccess &&
-        fa.sharedSizeBytes + 1024 < static_cast<size_t>(kLdsBytes)) {
-      cap = static_cast<int>(kLdsBytes - fa.sharedSizeBytes) / 1024 * 1024;
-      if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, cap) != hipSuccess) cap = 0;
-    }
-    stage_cap = cap;
-  }
+  const int stage_cap = EP != RK_TOP2 ? dyn_lds_room(kern, kLdsBytes) : 0;   // dynamic LDS bytes it may use
   const size_t tile_bytes = (EP == RK_SWIGLU ? 8 : 16) * 16 * sizeof(float);
   const int slots = (p.S * p.ntiles + p.grid - 1) / p.grid;   // units a workgroup handles
   // the chunk layout: M rows in mr chunks, and unit groups in whole XCD rounds

@@ -12,6 +12,16 @@ namespace dflash {
 constexpr int kMaxSrc = 8;
 constexpr int kMaxSeq = 64;
 
+// ------------------------------------------------------- launch attributes
+// Raise kernel fn's dynamic-LDS limit to at least `bytes` on the current
+// device.  Function attributes are per device; the first launch on each
+// device sets it, later ones find it in a table (thread-safe).
+hipError_t ensure_dyn_lds(const void* fn, int bytes);
+// The dynamic LDS kernel fn may use beside its static LDS (rounded down to
+// KB, 0 if under 1 KB or the limit cannot be raised), set as its limit on the
+// current device the first time it is asked for there (thread-safe).
+int dyn_lds_room(const void* fn, int lds_bytes);
+
 // ------------------------------------------------------------------- GEMMs
 // C[m][n] = sum_k A[m][k] * W[n][k] over a K range, written as split-K partials
 // part[s][m][n] (fp32).
@@ -127,6 +137,8 @@ struct ScatterArgs {
   void* vc;            // cache V base: [L][B][Hkv][d][cap]
   int32_t layer0, B, Hkv, d, cap;
   SeqRows rows;
+  int32_t* len_dev;               // nullable: the cache's device length mirror ...
+  int32_t len_new[kMaxSeq];       // ... set to these values (B of them) by the launch
 };
 
 hipError_t launch_scatter_kv(const ScatterArgs& a, bool bf16_cache, hipStream_t st);

@@ -41,16 +41,19 @@ def upload(arr: np.ndarray, cfg, device="cuda") -> torch.Tensor:
 
 
 class DeviceCache:
-    """KV cache [L][B][Hkv][cap][d] (keys) and [L][B][Hkv][d][cap] (values) plus host lens."""
+    """KV cache [L][B][Hkv][cap][d] (keys) and [L][B][Hkv][d][cap] (values), the
+    host lengths the library plans from, and their device mirror."""
 
     def __init__(self, cfg, B_: int, cap: int, device="cuda"):
         dt = cache_torch_dtype(cfg)
         self.k = torch.zeros(cfg.L, B_, cfg.Hkv, cap, cfg.d, dtype=dt, device=device)
         self.v = torch.zeros(cfg.L, B_, cfg.Hkv, cfg.d, cap, dtype=dt, device=device)
+        self.len_dev = torch.zeros(B_, dtype=torch.int32, device=device)
         self.lens = (ctypes.c_int32 * B_)()
         self.B, self.cap = B_, cap
         self.struct = B.KVCache(k=self.k.data_ptr(), v=self.v.data_ptr(), B=B_, cap=cap,
-                                len=ctypes.cast(self.lens, ctypes.POINTER(ctypes.c_int32)))
+                                len=ctypes.cast(self.lens, ctypes.POINTER(ctypes.c_int32)),
+                                len_dev=self.len_dev.data_ptr())
 
     def len_list(self):
         return [int(self.lens[b]) for b in range(self.B)]
@@ -58,6 +61,23 @@ class DeviceCache:
     def set_lens(self, lens):
         for b, n in enumerate(lens):
             self.lens[b] = int(n)
+        self.len_dev.copy_(torch.tensor(self.len_list(), dtype=torch.int32))
+
+    # ---- reading rows back (tests and measurements; the layout lives here only)
+    def rows(self, b: int, lo: int, hi: int):
+        """Rows [lo, hi) of sequence b in every layer: (K, V) float64 numpy
+        arrays [L][hi - lo][Hkv][d]."""
+        k = self.k[:, b, :, lo:hi].float().cpu().numpy().transpose(0, 2, 1, 3)
+        v = self.v[:, b, :, :, lo:hi].float().cpu().numpy().transpose(0, 3, 1, 2)
+        return k.astype(np.float64), v.astype(np.float64)
+
+    def snapshot(self, b: int, n: int):
+        """A device copy of rows [0, n) of sequence b in every layer."""
+        return self.k[:, b, :, :n].clone(), self.v[:, b, :, :, :n].clone()
+
+    def same_rows(self, snap, b: int, n: int) -> bool:
+        """Rows [0, n) of sequence b are bit-identical to ``snap``."""
+        return torch.equal(self.k[:, b, :, :n], snap[0]) and torch.equal(self.v[:, b, :, :, :n], snap[1])
 
 
 class DeviceDrafter:

@@ -116,14 +116,24 @@ typedef struct {
  *   v: [L][B][Hkv][d][cap]   values stored transposed (key index fastest)
  * len[b] (HOST array, caller-owned) is the number of valid context rows of
  * sequence b.  Rows [0, len[b]) are never written by draft_forward; inject_kv
- * writes rows [len[b], len[b]+T_b) and then adds T_b to len[b]. */
+ * writes rows [len[b], len[b]+T_b) and then adds T_b to len[b].  The host
+ * array is authoritative: every launch shape (key ranges, row tables) is
+ * planned from it on the host, so no kernel reads lengths from the device.
+ * len_dev (nullable, DEVICE [B] int32, caller-owned, 4-byte aligned) is a
+ * device mirror for device-side consumers: when non-NULL, inject_kv writes
+ * the new lengths into it on the stream, with the same kernel that stores the
+ * appended rows, so it holds len[b] once the stream reaches that point.  The
+ * caller initialises it (e.g. with a copy of len) before the first call. */
 typedef struct {
   void* k;
   void* v;
   int32_t B;     /* sequences, 1..DFLASH_MAX_BATCH */
   int32_t cap;   /* rows per (layer, sequence, head); a positive multiple of 32 (the
-                    attention reads keys in aligned 32-row blocks) */
-  int32_t* len;  /* host [B] */
+                    attention reads keys in aligned 32-row blocks).  With a bf16
+                    cache cap * head_dim * 2 must stay below 2^32 (checked;
+                    DFLASH_ERR_UNSUPPORTED otherwise) */
+  int32_t* len;      /* host [B] */
+  int32_t* len_dev;  /* nullable device [B]: mirror of len written by inject_kv */
 } dflash_kv_cache;
 
 /* Version string of the library. */
@@ -159,7 +169,8 @@ dflash_status dflash_fuse_context(const dflash_dims* dims, const dflash_weights*
  *   rows_per_seq  HOST [cache->B] row counts T_b >= 0
  * Errors: DFLASH_ERR_CAPACITY if len[b] + T_b > cap for some b (checked before
  * any work).  On success cache->len[b] += T_b (host), the rows land when the
- * stream reaches the kernels.  Uses weights->w_qkv. */
+ * stream reaches the kernels, and so does the same update of cache->len_dev
+ * when it is given.  Uses weights->w_qkv. */
 dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w, const void* H_t,
                                const int32_t* rows_per_seq, dflash_kv_cache* cache, void* ws,
                                size_t ws_bytes, void* stream);

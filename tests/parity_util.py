@@ -8,14 +8,14 @@ Tolerances (per compared tensor, both must hold):
 Tensors *stored* in bf16 (H_t, cache K/V, block K/V) are compared the same way,
 except that an element may also differ by exactly one bf16 ulp of the oracle's
 value (both sides rounded nearly equal values to neighbouring bf16 numbers; at
-|x| >= 4 one ulp is 0.031 > 2e-2), and at most 0.1% of elements may do so.
-Argmax ids must agree on every row whose oracle top-2 gap is >= 1e-3 when H_t
-and the cache are fp32.  With a bf16 cache, two correctly rounded evaluations
-already differ by up to ~1e-2 in the logits (a 0.1-1% share of cache elements
-round to the neighbouring bf16 number, and the drafter amplifies it), so there
-the exclusion threshold is 3e-2;
-acceptance lengths and next anchors must match bit for bit given the same
-draft and target tokens.
+|x| >= 4 one ulp is 0.031 > 2e-2), and at most 0.1% of elements may do so
+(tests/test_storage_rounding_pin.py measures this between two correct
+evaluations at the Qwen3-8B shape).
+Argmax ids must agree on every row whose oracle top-2 gap is >= 1e-3, for an
+fp32 and a bf16 cache alike (the same pin shows two correct bf16-cache
+evaluations ~2e-3 apart in the logits at most, with no argmax disagreement
+above that gap); acceptance lengths and next anchors must match bit for bit
+given the same draft and target tokens.
 """
 from __future__ import annotations
 
@@ -32,7 +32,6 @@ from oracle import dflash_oracle as O
 
 TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-5)}
 GAP_MIN = 1e-3
-GAP_MIN_BF16_CACHE = 3e-2
 
 
 def log(msg):
@@ -142,18 +141,16 @@ class Workload:
         assert self.cache.len_list() == [a + c for a, c in zip(lens_before, counts)]
         Ht_o = O.fuse_context(states, self.o_wc, self.o_gc, cfg.eps, self.st)
         self.report[f"{tag}/H_t"] = close_stored(H_t.float().cpu().numpy(), Ht_o, self.st, f"{tag} H_t", self.tol)
-        kg = self.cache.k.float().cpu().numpy()
-        vg = self.cache.v.float().cpu().numpy()
         for b, (lo, hi) in enumerate(self.seq_rows(counts)):
             n0 = lens_before[b]
+            gk, gv = self.cache.rows(b, n0, n0 + hi - lo)
             for l in range(cfg.L):
                 k, v = O.inject_kv(Ht_o[lo:hi], self.o_layers[l]["w_qkv"], cfg.Hq, cfg.Hkv, cfg.d, self.st)
                 self.ocache.append(l, b, k, v)
                 if hi > lo:
-                    gk = kg[l, b, :, n0:n0 + hi - lo, :].transpose(1, 0, 2)
-                    gv = vg[l, b, :, :, n0:n0 + hi - lo].transpose(2, 0, 1)
-                    close_stored(gk, k, self.st, f"{tag} K l{l} b{b}", self.tol)
-                    close_stored(gv, v, self.st, f"{tag} V l{l} b{b}", self.tol)
+                    close_stored(gk[l], k, self.st, f"{tag} K l{l} b{b}", self.tol)
+                    close_stored(gv[l], v, self.st, f"{tag} V l{l} b{b}", self.tol)
+        assert self.cache.len_dev.cpu().tolist() == self.cache.len_list(), "device length mirror"
         log(f"{tag}: {T} rows fused + injected, cache matches")
 
     # ------------------------------------------------------------- drafting
@@ -166,8 +163,7 @@ class Workload:
         ov_dev = torch.from_numpy(ov).to(self.dev) if ov is not None else None
         h_final = torch.empty(Bn, g, cfg.D, dtype=torch.float32, device=self.dev)
         lens = self.cache.len_list()
-        k_before = [self.cache.k[:, b, :, :lens[b]].clone() for b in range(Bn)]
-        v_before = [self.cache.v[:, b, :, :, :lens[b]].clone() for b in range(Bn)]
+        before = [self.cache.snapshot(b, lens[b]) for b in range(Bn)]
         self.dr.draft(self.cache, tok_dev, ov_dev, g, h_final)
         draft = torch.empty(Bn, n, dtype=torch.int32, device=self.dev)
         logits = torch.empty(Bn, n, cfg.V, dtype=torch.float32, device=self.dev)
@@ -180,8 +176,8 @@ class Workload:
         assert torch.equal(draft, draft_lean), "argmax differs when logits / gap are not requested"
         assert self.cache.len_list() == lens
         for b in range(Bn):
-            assert torch.equal(self.cache.k[:, b, :, :lens[b]], k_before[b]), "context K rows changed"
-            assert torch.equal(self.cache.v[:, b, :, :, :lens[b]], v_before[b]), "context V rows changed"
+            assert self.cache.same_rows(before[b], b, lens[b]), "context K/V rows changed"
+        del before
         # oracle
         hf_o, block_kv = O.draft_forward(cfg, self.o_layers, self.o_gfinal, self.ocache, g, embed=self.o_embed,
                                          tokens=tokens, override=ov, storage=self.st)
@@ -200,14 +196,12 @@ class Workload:
         self.report[f"{tag}/logits_maxabs"] = float(e_l.max())
         close(lg, logits_o, self.tol, f"{tag} logits")
         # every layer's block K/V rows stay in that layer's cache scratch rows
-        for l, (kb_o, vb_o) in enumerate(block_kv):
-            for b in range(Bn):
-                gk = self.cache.k[l, b, :, lens[b]:lens[b] + g].float().cpu().numpy().transpose(1, 0, 2)
-                gv = self.cache.v[l, b, :, :, lens[b]:lens[b] + g].float().cpu().numpy().transpose(2, 0, 1)
-                close_stored(gk, kb_o[b], self.st, f"{tag} block K l{l} b{b}", self.tol)
-                close_stored(gv, vb_o[b], self.st, f"{tag} block V l{l} b{b}", self.tol)
-        excl = argmax_agree(d_g, d_o, gap_o, f"{tag} drafts",
-                            GAP_MIN_BF16_CACHE if self.st == "bf16" else GAP_MIN)
+        for b in range(Bn):
+            gk, gv = self.cache.rows(b, lens[b], lens[b] + g)
+            for l, (kb_o, vb_o) in enumerate(block_kv):
+                close_stored(gk[l], kb_o[b], self.st, f"{tag} block K l{l} b{b}", self.tol)
+                close_stored(gv[l], vb_o[b], self.st, f"{tag} block V l{l} b{b}", self.tol)
+        excl = argmax_agree(d_g, d_o, gap_o, f"{tag} drafts")
         # the gap is a difference of two logits: compared in absolute terms only
         gmx = TOL[self.tol][0]
         assert np.abs(gg - gap_o).max() <= gmx, f"{tag} top2 gap: max-abs {np.abs(gg - gap_o).max():.3e}"

@@ -61,9 +61,9 @@ def test_bad_gamma(lib, gamma):
     assert e.value.status == B.ERR_INVALID_ARG
 
 
-def _cache(Bn=2, cap=64, lens=(0, 0), k=0x10000, v=0x20000):
+def _cache(Bn=2, cap=64, lens=(0, 0), k=0x10000, v=0x20000, len_dev=0):
     arr = (ctypes.c_int32 * Bn)(*lens)
-    c = B.KVCache(k=k, v=v, B=Bn, cap=cap, len=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+    c = B.KVCache(k=k, v=v, B=Bn, cap=cap, len=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), len_dev=len_dev)
     c._keep = arr
     return c
 
@@ -90,6 +90,38 @@ def test_draft_capacity_and_nulls(lib):
     with pytest.raises(B.DFlashError) as e:
         B.draft_forward(_dims(), w2, _cache(), 0x4000, None, 16, 0x5000, 0x100000, 1 << 30)
     assert e.value.status == B.ERR_INVALID_ARG
+
+
+def test_bf16_cache_shape_limit_checked_before_any_work(lib):
+    # the bf16-cache attention addresses one head's K or V with 32-bit byte
+    # offsets: cap * head_dim * 2 >= 2^32 is refused on the host, before any
+    # launch (and before the device is even looked at)
+    w = B.Weights(w_qkv=0x1000, w_o=0x1000, w_gateup=0x1000, w_down=0x1000, g_attn=0x1000, g_ffn=0x1000,
+                  g_final=0x1000, embed=0x1000, lm_head=0x1000)
+    cap = (1 << 32) // (64 * 2)                 # exactly 2^32 bytes per head at head_dim 64
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward(_dims(cache_dtype=B.BF16), w, _cache(cap=cap), 0x4000, None, 16, 0x5000, 0x100000, 1 << 30)
+    assert e.value.status == B.ERR_UNSUPPORTED
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward_ragged(_dims(cache_dtype=B.BF16), w, _cache(cap=cap), 0x4000, None, [16, 8], 0x5000,
+                               0x100000, 1 << 30)
+    assert e.value.status == B.ERR_UNSUPPORTED
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward_blocks(_dims(cache_dtype=B.BF16), w, _cache(cap=cap), [0], [0], 16, 0x4000, None, 0x5000,
+                               0x100000, 1 << 30)
+    assert e.value.status == B.ERR_UNSUPPORTED
+    # one 32-row step below the limit passes this check (and then fails on the
+    # missing device, not on the shape)
+    with pytest.raises(B.DFlashError) as e:
+        B.draft_forward(_dims(cache_dtype=B.BF16), w, _cache(cap=cap - 32), 0x4000, None, 16, 0x5000, 0x100000,
+                        1 << 30)
+    assert e.value.status != B.ERR_UNSUPPORTED or "gfx950" in B.last_error()
+
+
+def test_len_dev_alignment(lib):
+    with pytest.raises(B.DFlashError) as e:
+        B.inject_kv(_dims(), B.Weights(w_qkv=0x1000), 0x3000, [1, 1], _cache(len_dev=0x3002), 0, 0)
+    assert e.value.status == B.ERR_INVALID_ARG and "len_dev" in B.last_error()
 
 
 def test_workspace_too_small(lib):

@@ -15,7 +15,7 @@ import torch
 from block_diffusion_drafter_ctx_amd import binding as B
 from dflash_inputs import BATCH16_RAGGED, DEEP8_B4_N8192, LONG_CTX_N32768, QWEN3_8B_N2048, TINY_F32, shrink
 from oracle import dflash_oracle as O
-from tests.parity_util import (GAP_MIN, GAP_MIN_BF16_CACHE, TOL, Workload, argmax_agree, close, close_stored,
+from tests.parity_util import (TOL, Workload, argmax_agree, close, close_stored,
                                log)
 
 pytestmark = pytest.mark.gpu
@@ -58,8 +58,7 @@ class Ragged(Workload):
             ov_dev = torch.from_numpy(np.concatenate(ovs)).to(dev)
         h_final = torch.empty(M, D, dtype=torch.float32, device=dev)
         lens = self.cache.len_list()
-        k_before = [self.cache.k[:, b, :, :lens[b]].clone() for b in range(Bn)]
-        v_before = [self.cache.v[:, b, :, :, :lens[b]].clone() for b in range(Bn)]
+        before = [self.cache.snapshot(b, lens[b]) for b in range(Bn)]
         self.dr.draft_ragged(self.cache, tok_dev, ov_dev, gs, h_final)
         nd = M - Bn
         draft = torch.empty(nd, dtype=torch.int32, device=dev)
@@ -72,8 +71,8 @@ class Ragged(Workload):
         assert torch.equal(draft, draft_lean), "argmax differs when logits / gap are not requested"
         assert self.cache.len_list() == lens
         for b in range(Bn):
-            assert torch.equal(self.cache.k[:, b, :, :lens[b]], k_before[b]), "context K rows changed"
-            assert torch.equal(self.cache.v[:, b, :, :, :lens[b]], v_before[b]), "context V rows changed"
+            assert self.cache.same_rows(before[b], b, lens[b]), "context K/V rows changed"
+        del before
         # oracle: each sequence's one-sequence pass over its own block
         hf_o, kv_o = O.draft_forward_ragged(cfg, self.o_layers, self.o_gfinal, self.ocache, gs, embed=self.o_embed,
                                             tokens=toks, override=ovs, storage=self.st)
@@ -82,14 +81,12 @@ class Ragged(Workload):
         e = close(hg, np.concatenate(hf_o), self.tol, f"{tag} h_final")
         close(logits.cpu().numpy(), np.concatenate(z_o), self.tol, f"{tag} logits")
         for b in range(Bn):
+            gk, gv = self.cache.rows(b, lens[b], lens[b] + gs[b])
             for l in range(cfg.L):
-                gk = self.cache.k[l, b, :, lens[b]:lens[b] + gs[b]].float().cpu().numpy().transpose(1, 0, 2)
-                gv = self.cache.v[l, b, :, :, lens[b]:lens[b] + gs[b]].float().cpu().numpy().transpose(2, 0, 1)
-                close_stored(gk, kv_o[b][l][0], self.st, f"{tag} block K l{l} b{b}", self.tol)
-                close_stored(gv, kv_o[b][l][1], self.st, f"{tag} block V l{l} b{b}", self.tol)
+                close_stored(gk[l], kv_o[b][l][0], self.st, f"{tag} block K l{l} b{b}", self.tol)
+                close_stored(gv[l], kv_o[b][l][1], self.st, f"{tag} block V l{l} b{b}", self.tol)
         dcat, gcat = np.concatenate(d_o), np.concatenate(gap_o)
-        excl = argmax_agree(draft.cpu().numpy(), dcat, gcat, f"{tag} drafts",
-                            GAP_MIN_BF16_CACHE if self.st == "bf16" else GAP_MIN)
+        excl = argmax_agree(draft.cpu().numpy(), dcat, gcat, f"{tag} drafts")
         assert np.abs(gap.cpu().numpy() - gcat).max() <= TOL[self.tol][0]
         # acceptance on the oracle's drafts and synthetic targets built from them
         rng = np.random.default_rng([cfg.cid, 77])

@@ -262,25 +262,33 @@ def test_sample_accept_edges():
 
 # ------------------------------------------------------------------ chained
 def test_sample_chain_qwen3_8b_n2048():
-    """Draft, then verify, at the full Qwen3-8B-shaped LM head: each side builds
-    its target logits from its own draft logits plus the same seeded noise."""
+    """Draft, then verify, at the full Qwen3-8B-shaped LM head.  The drafts are
+    compared with the oracle's; the verify then runs on identical inputs on
+    both sides (the oracle's drafts and draft logits, the target logits built
+    from those logits and the seeded noise), so it is always compared.  The
+    GPU's own chain (its drafts, logits and log-normalisers) must also give
+    acceptance lengths in range."""
     cfg = QWEN3_8B_N2048
     gamma, T = 16, 1.0
+    n = gamma - 1
     head = Head(cfg, gamma)
     h = head.inp.final_states(gamma)
     u, au, ru = head.inp.sample_uniforms(1, gamma)
     noise = head.inp.target_noise(1, gamma)
     d_g, z_g, l_g = head.sample(_dev(h), gamma, T, _dev(u))
+    d_o, z_o, l_o, gap_o = O.sample_drafts(h, head.E64, T, u)
+    check_drafts("chain drafts", cfg, T, d_g, z_g, l_g, d_o, z_o, l_o, gap_o)
+    # the GPU's own chain
     t_g = torch.empty(cfg.B, gamma, cfg.V, dtype=torch.float32, device="cuda")
     noise_d = _dev(noise)
-    t_g[:, :gamma - 1] = z_g + 0.5 * noise_d[:, :gamma - 1]
-    t_g[:, gamma - 1] = noise_d[:, gamma - 1]
-    tau, nxt = accept_gpu(head.dims, cfg.B, gamma, T, d_g, z_g, t_g, _dev(au), _dev(ru), l_g)
-    d_o, z_o, l_o, gap_o = O.sample_drafts(h, head.E64, T, u)
-    d_gn = check_drafts("chain drafts", cfg, T, d_g, z_g, l_g, d_o, z_o, l_o, gap_o)
-    t_o = build_target_logits_np(z_o.astype(np.float32), noise)
-    if np.array_equal(d_gn, d_o):
-        check_accept("chain verify", tau, nxt, d_o, z_o, t_o, T, au, ru)
-    else:
-        pytest.skip("a near-tied draft row differs; the verify step is compared in the other tests")
+    t_g[:, :n] = z_g + 0.5 * noise_d[:, :n]
+    t_g[:, n] = noise_d[:, n]
+    tau_g, _ = accept_gpu(head.dims, cfg.B, gamma, T, d_g, z_g, t_g, _dev(au), _dev(ru), l_g)
+    assert np.all((tau_g >= 1) & (tau_g <= gamma))
+    # the verify on identical inputs
+    z32 = np.ascontiguousarray(z_o, dtype=np.float32)
+    t_o = build_target_logits_np(z32, noise)
+    tau, nxt = accept_gpu(head.dims, cfg.B, gamma, T, _dev(d_o.astype(np.int32)), _dev(z32), _dev(t_o), _dev(au),
+                          _dev(ru), None)
+    check_accept("chain verify", tau, nxt, d_o, z32.astype(np.float64), t_o, T, au, ru)
     assert math.isfinite(float(tau.mean()))
