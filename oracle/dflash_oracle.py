@@ -429,3 +429,98 @@ def accept_ragged(drafts, targets):
     return (np.array([int(t[0]) for t, _ in res], dtype=np.int32),
             np.array([int(x[0]) for _, x in res], dtype=np.int32))
 
+
+
+# ---------------------------------------------------------------------------
+# the target side: tapped layers and the parallel verify forward
+# ---------------------------------------------------------------------------
+def tap_layers(L_t: int, n: int = 5):
+    """0-based indices of the n target layers whose hidden states are fused.
+
+    [JP] "실험 설정" (settings table, row on the target hidden features) and
+    [MG] section 3.1: five layers spread uniformly from the target's second
+    layer to its third-from-last.  Index k (k = 0..n-1) is
+    1 + k (L_t - 4) / (n - 1), rounded half up (the pages do not say how a
+    fractional position is rounded).
+    """
+    if n == 1:
+        return [1]
+    first, last = 1, L_t - 3
+    return [first + int(np.floor(k * (last - first) / (n - 1) + 0.5)) for k in range(n)]
+
+
+def attention_causal(q, k, v, n_ctx: int) -> np.ndarray:
+    """Softmax attention of the block rows over [context ; block] with a causal
+    mask inside the block: block row i sees the n_ctx context rows and block
+    rows 0..i (an autoregressive target reads each position's past only).
+    q: [R, Hq, d]; k, v: [n_ctx + R, Hkv, d].  Query head h reads KV head
+    h // (Hq/Hkv), scale 1/sqrt(d).  Returns [R, Hq, d]."""
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    R, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    out = np.empty((R, Hq, d))
+    for h in range(Hq):
+        kv_head = h // G
+        for i in range(R):
+            seen = n_ctx + i + 1
+            sc = (k[:seen, kv_head, :] @ q[i, h, :]) / np.sqrt(d)
+            w = np.exp(sc - np.max(sc))
+            out[i, h, :] = (w / np.sum(w)) @ v[:seen, kv_head, :]
+    return out
+
+
+def target_verify(dims, layers, g_final, embed, lm_head, cache: OracleCache, tokens, taps,
+                  storage: str = "bf16", tap_storage: str = "bf16"):
+    """The target model's parallel verify forward over one block per sequence.
+
+    [JP] "방법론 / 추론 구조", last step: the target checks the whole drafted
+    block in one parallel pass; [GL] "투기적 디코딩에 확산 모델을 끼워 넣다": the
+    target verifies the proposed tokens in parallel and keeps the accepted
+    ones.  The block is the anchor (the last verified token's successor) and
+    the n drafts.  The synthetic target has the drafter's layer form
+    (pre-norm residual layers, no positional encoding, no bias) with causal
+    attention over its own KV cache of the verified context; the row of block
+    position j predicts the token after it, so its argmax is the target's
+    token at draft position j (j < n) and the last row's is the bonus.
+    Alongside, the residual stream after each tapped layer is kept: the hidden
+    states the drafter fuses for the verified tokens ([JP] "추론 구조": hidden
+    states of a fixed set of uniformly chosen layers, read while the target
+    runs).
+
+    tokens [B, gamma] ids; cache: the target's K/V of the context rows;
+    taps: 0-based layer indices.  Returns a dict with "tokens" [B, gamma]
+    (argmax, lowest id on ties), "gap" [B, gamma] (top-2 gap), "logits",
+    "taps" (per tapped layer [B, gamma, D], stored in tap_storage) and
+    "block_kv" (per layer the block's K/V rows, stored in the cache type).
+    """
+    D, Hq, Hkv, d, F, eps = dims.D, dims.Hq, dims.Hkv, dims.d, dims.F, dims.eps
+    tok = np.asarray(tokens)
+    x = np.asarray(embed)[tok].astype(F64)
+    B, gamma = tok.shape
+    kept = {}
+    rows_kv = []
+    for l, w in enumerate(layers):
+        xa = rmsnorm(x, w["g_attn"], eps)
+        proj = xa @ np.asarray(w["w_qkv"], dtype=F64).T
+        qt = proj[..., : Hq * d].reshape(B, gamma, Hq, d)
+        kt = store(proj[..., Hq * d:(Hq + Hkv) * d], storage).reshape(B, gamma, Hkv, d)
+        vt = store(proj[..., (Hq + Hkv) * d:], storage).reshape(B, gamma, Hkv, d)
+        rows_kv.append((kt, vt))
+        att = np.empty((B, gamma, Hq * d))
+        for b in range(B):
+            n_ctx = cache.k[l][b].shape[0]
+            att[b] = attention_causal(qt[b], np.concatenate([cache.k[l][b], kt[b]], axis=0),
+                                      np.concatenate([cache.v[l][b], vt[b]], axis=0), n_ctx).reshape(gamma, Hq * d)
+        x = x + att @ np.asarray(w["w_o"], dtype=F64).T
+        xf = rmsnorm(x, w["g_ffn"], eps)
+        up = xf @ np.asarray(w["w_gateup"], dtype=F64).T
+        x = x + (silu(up[..., :F]) * up[..., F:]) @ np.asarray(w["w_down"], dtype=F64).T
+        if l in taps:
+            kept[l] = store(x, tap_storage)
+    logits = rmsnorm(x, g_final, eps) @ np.asarray(lm_head, dtype=F64).T
+    best = np.argmax(logits, axis=-1).astype(np.int32)
+    two = -np.partition(-logits, 1, axis=-1)[..., :2]
+    return dict(tokens=best, gap=two[..., 0] - two[..., 1], logits=logits, taps=[kept[l] for l in taps],
+                block_kv=rows_kv)

@@ -744,4 +744,171 @@ def pin_sample_accept_cases(o):
     assert tau[0] == 2 and nxt[0] == 3 and info["resid_empty"][0]
 
 
+# ---------------------------------------------------------------------------
+# the target side: tapped layers and the causal verify forward
+# ---------------------------------------------------------------------------
+GOLD_TAPS = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden", "tap_layers.txt")
+
+
+def pin_tap_layers_golden(o):
+    # hand-worked indices for several target depths (tests/golden/tap_layers.txt)
+    for line in open(GOLD_TAPS, encoding="utf-8"):
+        line = line.split("#")[0].split()
+        if line:
+            L_t, want = int(line[0]), [int(x) for x in line[1:]]
+            assert list(o.tap_layers(L_t)) == want, (L_t, o.tap_layers(L_t), want)
+    # the rule's shape at every depth: second layer first, third-from-last
+    # last, strictly increasing, spacings that differ by at most one
+    for L_t in range(8, 101):
+        t = np.asarray(o.tap_layers(L_t))
+        gaps = np.diff(t)
+        assert t[0] == 1 and t[-1] == L_t - 3 and len(t) == 5, (L_t, t)
+        assert gaps.min() >= 1 and gaps.max() - gaps.min() <= 1, (L_t, t)
+
+
+def _torch_target_forward(dm, layers, g_final, ctx_k, ctx_v, h0, taps):
+    """Library-routine composition (float64 CPU) of a causal target forward:
+    SDPA over [context; block] with an explicit boolean mask (block row i sees
+    every context row and block rows 0..i); f32 storage of the block K/V and of
+    the tapped states emulated by float32 round trips.  Returns (normed final
+    states, {layer: residual stream after it})."""
+    D, Hq, Hkv, d, F, eps = dm.D, dm.Hq, dm.Hkv, dm.d, dm.F, dm.eps
+    G = Hq // Hkv
+    h = torch.from_numpy(h0.copy())
+    g_ = h.shape[0]
+    n_ctx = ctx_k[0].shape[0]
+    mask = torch.ones(g_, n_ctx + g_, dtype=torch.bool)
+    mask[:, n_ctx:] = torch.tril(torch.ones(g_, g_, dtype=torch.bool))
+
+    def norm(x, g):
+        m = torch.nn.RMSNorm(D, eps=eps, dtype=torch.float64)
+        with torch.no_grad():
+            m.weight.copy_(torch.from_numpy(np.asarray(g, dtype=F64)))
+            return m(x)
+
+    kept = {}
+    with torch.no_grad():
+        for l, w in enumerate(layers):
+            a = norm(h, w["g_attn"])
+            wq = torch.from_numpy(w["w_qkv"][: Hq * d])
+            wk = torch.from_numpy(w["w_qkv"][Hq * d:(Hq + Hkv) * d])
+            wv = torch.from_numpy(w["w_qkv"][(Hq + Hkv) * d:])
+            q = torch.nn.functional.linear(a, wq).reshape(g_, Hq, d).permute(1, 0, 2)
+            kb = torch.nn.functional.linear(a, wk).float().double().reshape(g_, Hkv, d)
+            vb = torch.nn.functional.linear(a, wv).float().double().reshape(g_, Hkv, d)
+            K = torch.cat([torch.from_numpy(ctx_k[l]), kb], 0).permute(1, 0, 2).repeat_interleave(G, 0)
+            Vv = torch.cat([torch.from_numpy(ctx_v[l]), vb], 0).permute(1, 0, 2).repeat_interleave(G, 0)
+            att = torch.nn.functional.scaled_dot_product_attention(q, K, Vv, attn_mask=mask)
+            att = att.permute(1, 0, 2).reshape(g_, Hq * d)
+            h = h + torch.nn.functional.linear(att, torch.from_numpy(w["w_o"]))
+            f = norm(h, w["g_ffn"])
+            gu = torch.nn.functional.linear(f, torch.from_numpy(w["w_gateup"]))
+            s = torch.nn.functional.silu(gu[:, :F]) * gu[:, F:]
+            h = h + torch.nn.functional.linear(s, torch.from_numpy(w["w_down"]))
+            if l in taps:
+                kept[l] = h.float().double().numpy()
+        return norm(h, g_final).numpy(), kept
+
+
+def _target_setup(seed, L=3, B=2, lens=(6, 0), V=40):
+    rng = _rng(seed)
+    dm = dims()
+    layers = rand_layers(rng, dm, L)
+    gf = 1 + rng.normal(0, 0.2, dm.D)
+    E = rng.normal(0, 1, (V, dm.D))
+    return rng, dm, layers, gf, E
+
+
+def pin_target_torch_composition(o):
+    rng, dm, layers, gf, E = _target_setup(31)
+    lens, gamma, taps = [6, 0], 5, [0, 2]
+    cache = cache_with(o, len(layers), 2, dm.Hkv, dm.d, lens, rng)
+    tok = rng.integers(0, E.shape[0], (2, gamma))
+    res = o.target_verify(dm, layers, gf, E, E, cache, tok, taps, storage="f32", tap_storage="f32")
+    for b in range(2):
+        zf, kept = _torch_target_forward(dm, layers, gf, [cache.k[l][b] for l in range(len(layers))],
+                                         [cache.v[l][b] for l in range(len(layers))], E[tok[b]], taps)
+        ref_logits = zf @ E.T
+        assert np.allclose(res["logits"][b], ref_logits, rtol=1e-9, atol=1e-9), b
+        assert np.array_equal(res["tokens"][b], np.argmax(ref_logits, axis=-1)), b
+        for k, l in enumerate(taps):
+            assert np.allclose(res["taps"][k][b], kept[l], rtol=1e-9, atol=1e-9), (b, l)
+
+
+def pin_target_prefix_consistency(o):
+    # causal attention: a block row depends only on the rows before it, so
+    # verifying the first i+1 tokens alone gives row i's outputs exactly
+    rng, dm, layers, gf, E = _target_setup(32)
+    lens, gamma, taps = [4, 0], 6, [1]
+    cache = cache_with(o, len(layers), 2, dm.Hkv, dm.d, lens, rng)
+    tok = rng.integers(0, E.shape[0], (2, gamma))
+    full = o.target_verify(dm, layers, gf, E, E, cache, tok, taps, storage="f32", tap_storage="f32")
+    for i in range(gamma):
+        part = o.target_verify(dm, layers, gf, E, E, cache, tok[:, :i + 1], taps, storage="f32",
+                               tap_storage="f32")
+        assert np.allclose(part["logits"][:, i], full["logits"][:, i], rtol=1e-10, atol=1e-10), i
+        assert np.allclose(part["taps"][0][:, i], full["taps"][0][:, i], rtol=1e-10, atol=1e-10), i
+    # and a later token never moves an earlier row, while it does move its own
+    tok2 = tok.copy()
+    tok2[:, 3] = (tok2[:, 3] + 1) % E.shape[0]
+    alt = o.target_verify(dm, layers, gf, E, E, cache, tok2, taps, storage="f32", tap_storage="f32")
+    assert np.array_equal(alt["logits"][:, :3], full["logits"][:, :3])
+    assert not np.allclose(alt["logits"][:, 3], full["logits"][:, 3])
+
+
+def pin_target_greedy_lossless(o):
+    # Greedy speculative decoding is lossless: if the drafts are the target's
+    # own greedy continuation, one parallel verify reproduces it and accepts
+    # every draft; a wrong draft at position m stops acceptance there and the
+    # next anchor is the target's own token.  The continuation comes from
+    # autoregressive decoding (one row per call, its K/V appended each time).
+    rng, dm, layers, gf, E = _target_setup(33, B=1, lens=(5,))
+    L, n = len(layers), 6
+    cache = cache_with(o, L, 1, dm.Hkv, dm.d, [5], rng)
+    ar = o.OracleCache(L, 1, dm.Hkv, dm.d)
+    for l in range(L):
+        ar.append(l, 0, cache.k[l][0], cache.v[l][0])
+    seq = [int(rng.integers(0, E.shape[0]))]
+    for _ in range(n + 1):
+        r = o.target_verify(dm, layers, gf, E, E, ar, np.array([[seq[-1]]]), [], storage="f32")
+        for l, (kb, vb) in enumerate(r["block_kv"]):
+            ar.append(l, 0, kb[0], vb[0])
+        seq.append(int(r["tokens"][0, 0]))
+    anchor, cont = seq[0], seq[1:]
+    res = o.target_verify(dm, layers, gf, E, E, cache, np.array([[anchor] + cont[:n]]), [], storage="f32")
+    assert list(res["tokens"][0]) == cont, (list(res["tokens"][0]), cont)
+    tau, nxt = o.accept(np.array([cont[:n]]), res["tokens"])
+    assert tau[0] == n + 1 and nxt[0] == cont[n]
+    for m in (0, 3):
+        dr = list(cont[:n])
+        dr[m] = (dr[m] + 1) % E.shape[0]
+        res = o.target_verify(dm, layers, gf, E, E, cache, np.array([[anchor] + dr]), [], storage="f32")
+        assert list(res["tokens"][0][:m + 1]) == cont[:m + 1]
+        tau, nxt = o.accept(np.array([dr]), res["tokens"])
+        assert tau[0] == m + 1 and nxt[0] == cont[m], (m, tau, nxt)
+
+
+def pin_target_zero_branches(o):
+    # W_O = 0 and W_down = 0: every layer passes the residual stream through,
+    # so every tapped state is the token embedding itself and the logits are
+    # E . RMSNorm(E[token]; g_final), in closed form
+    rng, dm, layers, gf, E = _target_setup(34)
+    for w in layers:
+        w["w_o"] = np.zeros_like(w["w_o"])
+        w["w_down"] = np.zeros_like(w["w_down"])
+    cache = cache_with(o, len(layers), 2, dm.Hkv, dm.d, [3, 2], rng)
+    tok = rng.integers(0, E.shape[0], (2, 4))
+    res = o.target_verify(dm, layers, gf, E, E, cache, tok, [0, 1, 2], storage="f32", tap_storage="f32")
+    for t in res["taps"]:
+        assert np.array_equal(t, E[tok].astype(np.float32).astype(F64))
+    x = E[tok]
+    z = gf * x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + dm.eps)
+    assert np.allclose(res["logits"], z @ E.T, rtol=1e-12, atol=1e-12)
+    # the argmax covers every row, the anchor's included: plant the best token
+    E2 = E.copy()
+    E2[7] = 50.0 * z[0, 0] / np.linalg.norm(z[0, 0])
+    res2 = o.target_verify(dm, layers, gf, E, E2, cache, tok, [], storage="f32")
+    assert res2["tokens"][0, 0] == 7 and res2["gap"][0, 0] > 0
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -93,6 +93,20 @@ MUTANTS = [
      "cache.prefix(0, int(a)), gamma, embed=embed,"),
     ("sample_counts_all_accepts", "while m < n and accepted[b, m]:\n            m += 1",
      "m = int(np.sum(accepted[b]))"),
+    ("taps_from_first_layer", "first, last = 1, L_t - 3", "first, last = 0, L_t - 3"),
+    ("taps_to_second_last", "first, last = 1, L_t - 3", "first, last = 1, L_t - 2"),
+    ("taps_round_down", "(n - 1) + 0.5))", "(n - 1)))"),
+    ("target_not_causal", "seen = n_ctx + i + 1", "seen = k.shape[0]"),
+    ("target_skips_own_row", "seen = n_ctx + i + 1", "seen = max(n_ctx + i, 1)"),
+    ("target_tap_normed", "kept[l] = store(x, tap_storage)",
+     "kept[l] = store(rmsnorm(x, w[\"g_ffn\"], eps), tap_storage)"),
+    ("target_tap_before_ffn", "x = x + (silu(up[..., :F]) * up[..., F:]) @ np.asarray(w[\"w_down\"], dtype=F64).T\n"
+     "        if l in taps:\n            kept[l] = store(x, tap_storage)",
+     "if l in taps:\n            kept[l] = store(x, tap_storage)\n"
+     "        x = x + (silu(up[..., :F]) * up[..., F:]) @ np.asarray(w[\"w_down\"], dtype=F64).T"),
+    ("target_no_final_norm", "logits = rmsnorm(x, g_final, eps) @", "logits = x @"),
+    ("target_context_keys_zeroed", "np.concatenate([cache.k[l][b], kt[b]], axis=0)",
+     "np.concatenate([0 * cache.k[l][b], kt[b]], axis=0)"),
 ]
 
 
