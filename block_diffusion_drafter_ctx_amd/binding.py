@@ -19,7 +19,8 @@ ARGMAX, ACCEPT = 1, 2
 MAX_BATCH, MAX_TGT_LAYERS, MIN_GAMMA, MAX_GAMMA = 64, 8, 2, 33
 
 EXPORTED = ("dflash_version", "dflash_last_error", "dflash_workspace_size", "dflash_fuse_context",
-            "dflash_inject_kv", "dflash_draft_forward", "dflash_draft_forward_ragged",
+            "dflash_inject_kv", "dflash_draft_forward", "dflash_draft_forward_noalloc",
+            "dflash_draft_forward_ragged",
             "dflash_draft_forward_blocks", "dflash_argmax_accept",
             "dflash_argmax_accept_ragged", "dflash_sample_drafts",
             "dflash_sample_accept", "dflash_profile_events")
@@ -76,6 +77,9 @@ def load():
     lib.dflash_draft_forward.restype = c_int32
     lib.dflash_draft_forward.argtypes = [POINTER(Dims), POINTER(Weights), POINTER(KVCache), c_void_p, c_void_p,
                                          c_int32, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dflash_draft_forward_noalloc.restype = c_int32
+    lib.dflash_draft_forward_noalloc.argtypes = [POINTER(Dims), POINTER(Weights), POINTER(KVCache), c_void_p,
+                                                 c_void_p, c_int32, c_void_p, c_void_p]
     lib.dflash_argmax_accept.restype = c_int32
     lib.dflash_argmax_accept.argtypes = [POINTER(Dims), POINTER(Weights), c_uint32, c_void_p, c_int32, c_int32,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -155,6 +159,13 @@ def argmax_accept(dims: Dims, w: Weights, flags: int, h_final, B: int, gamma: in
 
 def _gammas(gammas):
     return (c_int32 * max(1, len(gammas)))(*[int(g) for g in gammas])
+
+
+def draft_forward_noalloc(dims: Dims, w: Weights, cache: KVCache, block_tokens, embed_override, gamma: int,
+                          h_final, stream=0):
+    _check(load().dflash_draft_forward_noalloc(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(cache),
+                                               _p(block_tokens), _p(embed_override), gamma, _p(h_final),
+                                               _p(stream)))
 
 
 def draft_forward_ragged(dims: Dims, w: Weights, cache: KVCache, block_tokens, embed_override, gammas, h_final,

@@ -919,6 +919,57 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
   return draft_forward_impl(dims, w, cache, block_tokens, embed_override, qg, h_final, ws, ws_bytes, stream);
 }
 
+// ---------------------------------------------------- no-allocation variant
+// dflash_draft_forward_noalloc keeps the pass's workspace in this static
+// device array instead of a caller buffer: one copy per GPU, alive until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it only names the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch[64] = {};
+
+// The current device's address of `scratch` (looked up on first use there).
+dflash_status scratch_address(void** out) {
+  int dev = 0;
+  DF_HIP(hipGetDevice(&dev));
+  DF_REQUIRE(dev >= 0 && dev < 64, DFLASH_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    DF_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    DF_REQUIRE(p != nullptr && (reinterpret_cast<uintptr_t>(p) % kAlign) == 0, DFLASH_ERR_HIP,
+               "scratch address %p is not %zu-byte aligned", p, kAlign);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return DFLASH_OK;
+}
+}  // namespace
+
+dflash_status dflash_draft_forward_noalloc(const dflash_dims* dims, const dflash_weights* w,
+                                           const dflash_kv_cache* cache, const int32_t* block_tokens,
+                                           const float* embed_override, int32_t gamma, float* h_final,
+                                           void* stream) {
+  dflash_status st = check_gamma(gamma);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_cache(cache)) != DFLASH_OK) return st;
+  int32_t gammas[kMaxSeq];
+  for (int b = 0; b < cache->B; ++b) gammas[b] = gamma;
+  QueryGroups qg;
+  if ((st = inference_groups(dims, w, cache, gammas, &qg)) != DFLASH_OK) return st;
+  const size_t need = draft_ws(dims, cache->B, cache->B * gamma, gamma).total;
+  DF_REQUIRE(need <= kScratchBytes, DFLASH_ERR_WORKSPACE,
+             "this pass needs %zu bytes of scratch; the no-allocation call holds %zu (use dflash_draft_forward "
+             "with a workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != DFLASH_OK) return st;
+  return draft_forward_impl(dims, w, cache, block_tokens, embed_override, qg, h_final, ws, kScratchBytes, stream);
+}
+
 dflash_status dflash_draft_forward_ragged(const dflash_dims* dims, const dflash_weights* w,
                                           const dflash_kv_cache* cache, const int32_t* block_tokens,
                                           const float* embed_override, const int32_t* gammas, float* h_final,

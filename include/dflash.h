@@ -195,6 +195,24 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
                                    const float* embed_override, int32_t gamma, float* h_final,
                                    void* ws, size_t ws_bytes, void* stream);
 
+/* (c) without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The same pass as dflash_draft_forward, on the same
+ * kernels, with the workspace taken from a static device array of 64 MiB
+ * inside the library (one per GPU, held until the process ends; the call
+ * itself allocates nothing).  Passes whose workspace would exceed it are
+ * refused with DFLASH_ERR_WORKSPACE before anything is enqueued (at the
+ * Qwen3-8B drafter shape, up to four sequences of 16 block rows fit; one
+ * sequence of 33 rows does not).
+ * Nothing in the array needs to start at zero: every byte a kernel reads was
+ * written earlier in the same call.  All calls on one GPU share the array, so
+ * calls that overlap on that GPU (other streams, other threads) race; calls
+ * ordered on one stream do not. */
+dflash_status dflash_draft_forward_noalloc(const dflash_dims* dims, const dflash_weights* w,
+                                           const dflash_kv_cache* cache, const int32_t* block_tokens,
+                                           const float* embed_override, int32_t gamma, float* h_final,
+                                           void* stream);
+
 /* (c) with a block length per sequence ([JP] "Ablation Study": a drafter
  * trained with large blocks keeps its acceptance with smaller inference blocks,
  * which allows choosing the block size per sequence at inference time;

@@ -118,6 +118,23 @@ def test_bf16_cache_shape_limit_checked_before_any_work(lib):
     assert e.value.status != B.ERR_UNSUPPORTED or "gfx950" in B.last_error()
 
 
+def test_noalloc_refuses_passes_beyond_its_scratch(lib):
+    # the size check is host-side and comes before any device call: a pass
+    # that fits goes on to look for the device (absent here), one that does
+    # not is refused with DFLASH_ERR_WORKSPACE
+    qwen = dict(D=4096, L=5, Hq=32, Hkv=8, head_dim=128, F=12288, V=151936, mask_id=151935)
+    w = B.Weights(w_qkv=0x1000, w_o=0x1000, w_gateup=0x1000, w_down=0x1000, g_attn=0x1000, g_ffn=0x1000,
+                  g_final=0x1000, embed=0x1000, lm_head=0x1000)
+    for Bn, g, fits in [(1, 16, True), (4, 16, True), (1, 33, False), (8, 16, False)]:
+        c = _cache(Bn=Bn, cap=4096, lens=[2048] * Bn)
+        with pytest.raises(B.DFlashError) as e:
+            B.draft_forward_noalloc(_dims(**qwen), w, c, 0x4000, None, g, 0x5000)
+        if fits:
+            assert e.value.status != B.ERR_WORKSPACE, B.last_error()
+        else:
+            assert e.value.status == B.ERR_WORKSPACE and "no-allocation" in B.last_error()
+
+
 def test_len_dev_alignment(lib):
     with pytest.raises(B.DFlashError) as e:
         B.inject_kv(_dims(), B.Weights(w_qkv=0x1000), 0x3000, [1, 1], _cache(len_dev=0x3002), 0, 0)
