@@ -22,7 +22,7 @@ EXPORTED = ("dflash_version", "dflash_last_error", "dflash_workspace_size", "dfl
             "dflash_inject_kv", "dflash_draft_forward", "dflash_draft_forward_noalloc",
             "dflash_draft_forward_ragged",
             "dflash_draft_forward_blocks", "dflash_argmax_accept",
-            "dflash_argmax_accept_ragged", "dflash_sample_drafts",
+            "dflash_argmax_accept_ragged", "dflash_target_verify", "dflash_sample_drafts",
             "dflash_sample_accept", "dflash_profile_events")
 (PROF_NONE, PROF_LM_HEAD, PROF_QKV, PROF_O, PROF_GATEUP, PROF_DOWN, PROF_FUSE, PROF_INJECT, PROF_ATTENTION,
  PROF_ROW_STATS, PROF_VERIFY) = range(11)
@@ -80,6 +80,10 @@ def load():
     lib.dflash_draft_forward_noalloc.restype = c_int32
     lib.dflash_draft_forward_noalloc.argtypes = [POINTER(Dims), POINTER(Weights), POINTER(KVCache), c_void_p,
                                                  c_void_p, c_int32, c_void_p, c_void_p]
+    lib.dflash_target_verify.restype = c_int32
+    lib.dflash_target_verify.argtypes = [POINTER(Dims), POINTER(Weights), POINTER(KVCache), c_void_p, c_int32,
+                                         POINTER(c_int32), POINTER(c_void_p), c_void_p, c_void_p, c_void_p,
+                                         c_size_t, c_void_p]
     lib.dflash_argmax_accept.restype = c_int32
     lib.dflash_argmax_accept.argtypes = [POINTER(Dims), POINTER(Weights), c_uint32, c_void_p, c_int32, c_int32,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -166,6 +170,16 @@ def draft_forward_noalloc(dims: Dims, w: Weights, cache: KVCache, block_tokens, 
     _check(load().dflash_draft_forward_noalloc(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(cache),
                                                _p(block_tokens), _p(embed_override), gamma, _p(h_final),
                                                _p(stream)))
+
+
+def target_verify(dims: Dims, w: Weights, cache: KVCache, block_tokens, gamma: int, tap_layers, taps,
+                  target_tokens, top2_gap, ws, ws_bytes: int, stream=0):
+    n = len(tap_layers)
+    tl = (c_int32 * max(n, 1))(*[int(x) for x in tap_layers])
+    tp = (c_void_p * max(n, 1))(*[int(t) if t else None for t in taps])
+    _check(load().dflash_target_verify(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(cache), _p(block_tokens),
+                                       gamma, tl, tp, _p(target_tokens), _p(top2_gap), _p(ws), ws_bytes,
+                                       _p(stream)))
 
 
 def draft_forward_ragged(dims: Dims, w: Weights, cache: KVCache, block_tokens, embed_override, gammas, h_final,

@@ -138,6 +138,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
   // except in a group of two anchored blocks, where the rows of each block see
   // only their own context prefix and their own block rows.
   int klo = kbeg, khi = kend;
+  if (a.causal) khi = min(khi, a.nkeys[b] - gb + r % gb + 1);   // keys up to this row's own
   if (a.blk0[b] >= 0) {
     const bool second = r % gb >= a.half[b];
     if (sp == a.nsplit[b] - 1) {
@@ -358,6 +359,10 @@ __global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
   const int G = a.Hq / a.Hkv;
   const int gb = a.gam[b], Rb = G * gb;         // this sequence's block rows and query rows
   const bool computes = row0 < Rb;              // uniform per wave
+  // causal pass: keys from ctail on are block rows, and this lane's row sees
+  // them up to its own (kcaus = one past it)
+  const int ctail = a.causal ? a.nkeys[b] - gb : INT_MAX;
+  const int kcaus = a.causal ? ctail + r % gb + 1 : INT_MAX;
   const int64_t head = static_cast<int64_t>(a.kvseq[b]) * a.Hkv + j;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.kc) + head * a.cap * HD;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.vc) + head * HD * a.cap;
@@ -422,22 +427,26 @@ __global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[kt * 4 + e] = sc[kt][e];
     const bool partial = k0 + 32 > kend;        // uniform: the last block of the range
-    if (partial) {
+    const bool crows = k0 + 32 > ctail;         // uniform: the block holds block rows of a causal pass
+    if (partial || crows) {
+      const int klim = min(kend, kcaus);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (k0 + 8 * g4 + 4 * kt + e >= kend) p[kt * 4 + e] = -INFINITY;
+          if (k0 + 8 * g4 + 4 * kt + e >= klim) p[kt * 4 + e] = -INFINITY;
     }
     float mx = p[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, p[e]);
-    const float m_new = fmaxf(m_run, max_across16(mx));   // finite: the block holds a valid key
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // finite unless a causal row has seen no key yet (then nothing to scale)
+    const float m_new = fmaxf(m_run, max_across16(mx));
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(p[e] - m_new);
+      p[e] = __builtin_amdgcn_exp2f(p[e] - m_use);
       ps += p[e];
     }
     l_run = l_run * alpha + ps;
@@ -510,7 +519,8 @@ __global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
     if (grp == 1 || !computes) return;
     const float m1 = mml[(wq * 64 + lane) * 2], l1 = mml[(wq * 64 + lane) * 2 + 1];
     const float M = fmaxf(m_run, m1);
-    const float w0 = __builtin_amdgcn_exp2f(m_run - M), w1 = __builtin_amdgcn_exp2f(m1 - M);
+    const float M_use = M == -INFINITY ? 0.f : M;   // neither group saw a key (a causal row): weights 0
+    const float w0 = __builtin_amdgcn_exp2f(m_run - M_use), w1 = __builtin_amdgcn_exp2f(m1 - M_use);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const float4 x = *reinterpret_cast<const float4*>(mo + ((wq * DT + dt) * 64 + lane) * 4);
@@ -668,7 +678,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const float* kb = static_cast<const float*>(a.kc) + head * a.cap * a.d;
   const float* vb = static_cast<const float*>(a.vc) + head * a.d * a.cap;
   float m_run = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  const int nctx = a.nkeys[b], nall = nctx + (a.blk0[b] >= 0 ? a.gam[b] : 0);
+  const int nctx = a.nkeys[b];
+  // a causal pass stops at this row's own key (block rows follow the context)
+  const int nall = a.causal ? nctx - a.gam[b] + (m - a.qrow0[b]) + 1 : nctx + (a.blk0[b] >= 0 ? a.gam[b] : 0);
   for (int tt = 0; tt < nall; ++tt) {
     const int t = tt < nctx ? tt : a.blk0[b] + (tt - nctx);   // the block's own rows when stored apart
     const float* kp = kb + static_cast<int64_t>(t) * a.d;

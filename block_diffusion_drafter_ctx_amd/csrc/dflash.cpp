@@ -420,6 +420,27 @@ AcceptWs sample_accept_ws(const dflash_dims* d, int B, int gamma, bool lse_given
   return w;
 }
 
+// The target's verify pass over B blocks of gamma rows: the drafting pass's
+// workspace, then the final states [M][D] and the LM head's over all M rows.
+struct VerifyWs {
+  size_t hf, head, total;
+  DraftWs draft;
+  ArgmaxWs argmax;
+};
+
+VerifyWs verify_ws(const dflash_dims* d, int B, int gamma) {
+  VerifyWs w{};
+  const int M = B * gamma;
+  w.draft = draft_ws(d, B, M, gamma);
+  w.argmax = argmax_ws(d, M);
+  Carve c;
+  c.take(w.draft.total);
+  w.hf = c.take(static_cast<size_t>(M) * d->D * 4);
+  w.head = c.take(w.argmax.total);
+  w.total = c.off;
+  return w;
+}
+
 dflash_status check_temperature(float T) {
   DF_REQUIRE(std::isfinite(T) && T > 0.f && std::isfinite(1.0f / T), DFLASH_ERR_INVALID_ARG,
              "temperature=%g must be positive and finite (with a finite reciprocal)", static_cast<double>(T));
@@ -501,6 +522,8 @@ dflash_status dflash_workspace_size(const dflash_dims* dims, int32_t B, int32_t 
     if (pairs_fit(dims, gamma)) upd(draft_ws(dims, B, M, 2 * gamma).total);   // anchored blocks two to a group
   }
   for (int M = 1; M <= B * (gamma - 1); ++M) upd(argmax_ws(dims, M, true).total);
+  for (int g = 1; g <= gamma; ++g)
+    for (int b = 1; b <= B; ++b) upd(verify_ws(dims, b, g).total);
   for (int b = 1; b <= B; ++b)
     for (int g = DFLASH_MIN_GAMMA; g <= gamma; ++g) {
       upd(sample_ws(dims, b, g).total);
@@ -692,10 +715,19 @@ struct QueryGroups {
   int32_t half[kMaxSeq], nctx2[kMaxSeq];
 };
 
+// A pass run as the target model's verify forward: causal attention inside
+// the block, and the residual stream after some layers stored (tapped).
+struct TargetPass {
+  int n_taps = 0;
+  int32_t layer[DFLASH_MAX_TGT_LAYERS];
+  void* out[DFLASH_MAX_TGT_LAYERS];   // [M][D] weight type each
+};
+
 static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_weights* w,
                                         const dflash_kv_cache* cache, const int32_t* block_tokens,
                                         const float* embed_override, const QueryGroups& qg, float* h_final,
-                                        void* ws, size_t ws_bytes, void* stream) {
+                                        void* ws, size_t ws_bytes, void* stream,
+                                        const TargetPass* tp = nullptr) {
   dflash_status st = DFLASH_OK;
   int M = 0, gmax = 0;
   int32_t qrow0[kMaxSeq + 1];
@@ -835,6 +867,7 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
     at.cap = cache->cap;
     at.R = R;
     at.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
+    at.causal = tp != nullptr ? 1 : 0;
     for (int b = 0; b < B; ++b) {
       at.nkeys[b] = nkeys[b];
       at.gam[b] = qg.gam[b];
@@ -877,9 +910,12 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
     DF_HIP(gemm(sw, F, wp(w->w_down, static_cast<int64_t>(l) * D * F), D, &S, DFLASH_PROF_DOWN,
                 pl_dn.hi != nullptr && !swiglu_rk.rk));
     const bool last = l + 1 == L;
+    void* tap = nullptr;
+    for (int k = 0; tp != nullptr && k < tp->n_taps; ++k)
+      if (tp->layer[k] == l) tap = tp->out[k];
     DF_HIP(launch_residual_norm(part, S, M, D, h,
                                 last ? w->g_final : wp(w->g_attn, static_cast<int64_t>(l + 1) * D),
-                                dims->rms_eps, last ? h_final : a, bf, s, last ? HiLo{} : pl_qkv));
+                                dims->rms_eps, last ? h_final : a, bf, s, last ? HiLo{} : pl_qkv, tap));
   }
   return ok();
 }
@@ -1186,6 +1222,63 @@ dflash_status dflash_argmax_accept_ragged(const dflash_dims* dims, const dflash_
   }
   if (flags & DFLASH_ACCEPT) DF_HIP(launch_accept_ragged(draft, target, acc, tau, next_anchor, s));
   return ok();
+}
+
+dflash_status dflash_target_verify(const dflash_dims* dims, const dflash_weights* w, const dflash_kv_cache* cache,
+                                   const int32_t* block_tokens, int32_t gamma, const int32_t* tap_layers,
+                                   void* const* taps, int32_t* target_tokens, float* top2_gap, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  dflash_status st = check_dims(dims);
+  if (st != DFLASH_OK) return st;
+  DF_REQUIRE(w != nullptr, DFLASH_ERR_INVALID_ARG, "weights is NULL");
+  if ((st = check_cache(cache)) != DFLASH_OK) return st;
+  DF_REQUIRE(gamma >= 1 && gamma <= DFLASH_MAX_GAMMA, DFLASH_ERR_INVALID_ARG, "gamma=%d outside [1, %d]", gamma,
+             DFLASH_MAX_GAMMA);
+  DF_REQUIRE(block_tokens != nullptr && target_tokens != nullptr, DFLASH_ERR_INVALID_ARG,
+             "block_tokens and target_tokens must be non-NULL");
+  if ((st = check_ptr(w->lm_head, "lm_head")) != DFLASH_OK) return st;
+  if ((st = check_ptr(w->embed, "embed")) != DFLASH_OK) return st;
+  const int nt = dims->n_tgt_layers;
+  DF_REQUIRE(tap_layers != nullptr && taps != nullptr, DFLASH_ERR_INVALID_ARG, "tap_layers and taps must be non-NULL");
+  TargetPass tp;
+  tp.n_taps = nt;
+  for (int k = 0; k < nt; ++k) {
+    DF_REQUIRE(tap_layers[k] >= 0 && tap_layers[k] < dims->L, DFLASH_ERR_INVALID_ARG,
+               "tap_layers[%d]=%d outside [0, L=%d)", k, tap_layers[k], dims->L);
+    DF_REQUIRE(k == 0 || tap_layers[k] > tap_layers[k - 1], DFLASH_ERR_INVALID_ARG,
+               "tap_layers must increase (tap_layers[%d]=%d after %d)", k, tap_layers[k], tap_layers[k - 1]);
+    if ((st = check_ptr(taps[k], "taps[k]")) != DFLASH_OK) return st;
+    tp.layer[k] = tap_layers[k];
+    tp.out[k] = taps[k];
+  }
+  QueryGroups qg;
+  qg.n = cache->B;
+  qg.apart = false;
+  for (int b = 0; b < cache->B; ++b) {
+    DF_REQUIRE(static_cast<int64_t>(cache->len[b]) + gamma <= cache->cap, DFLASH_ERR_CAPACITY,
+               "sequence %d: len %d + gamma %d exceeds cap %d", b, cache->len[b], gamma, cache->cap);
+    qg.gam[b] = qg.half[b] = gamma;
+    qg.kvseq[b] = b;
+    qg.nctx[b] = qg.nctx2[b] = qg.pos0[b] = cache->len[b];
+  }
+  const int B = cache->B, M = B * gamma;
+  const VerifyWs lay = verify_ws(dims, B, gamma);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != DFLASH_OK) return st;
+  char* base = static_cast<char*>(ws);
+  float* hf = reinterpret_cast<float*>(base + lay.hf);
+  // the pass itself checks the remaining weights and the device
+  if ((st = draft_forward_impl(dims, w, cache, block_tokens, nullptr, qg, hf, ws, lay.draft.total, stream, &tp)) !=
+      DFLASH_OK)
+    return st;
+  hipStream_t s = as_stream(stream);
+  GemmArgs g{};
+  for (int k = 0; k < kMaxSrc; ++k) g.a_src[k] = hf;   // every block row, the anchor's included
+  g.a_cols = dims->D;
+  g.a_rg = INT_MAX;
+  g.a_gs = 0;
+  g.a_ld = dims->D;
+  return lm_head_argmax(dims, w, g, M, target_tokens, nullptr, top2_gap, base + lay.head, lay.argmax,
+                        base + lay.head, s);
 }
 
 dflash_status dflash_sample_drafts(const dflash_dims* dims, const dflash_weights* w, const float* h_final,

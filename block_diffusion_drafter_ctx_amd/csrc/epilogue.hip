@@ -152,7 +152,8 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(ScatterArgs a) {
 // ------------------------------------------------------------- residual_norm
 template <typename T>
 __global__ __launch_bounds__(1024) void residual_norm_kernel(const float* part, int S, int M, int D, float* h,
-                                                             const void* g, float eps, float* a_out, HiLo pl) {
+                                                             const void* g, float eps, float* a_out, HiLo pl,
+                                                             void* tap) {
   __shared__ float red[16];
   const int m = blockIdx.x;
   const int64_t stride = static_cast<int64_t>(M) * D;
@@ -166,6 +167,7 @@ __global__ __launch_bounds__(1024) void residual_norm_kernel(const float* part, 
       v[j] = *reinterpret_cast<const float4*>(h + i);
       if (part != nullptr) v[j] = f4add(v[j], sum_parts4(part, S, stride, i));
       *reinterpret_cast<float4*>(h + i) = v[j];
+      if (tap != nullptr) st4<T>(tap, i, v[j]);
       ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
     }
   }
@@ -409,12 +411,14 @@ hipError_t launch_scatter_kv(const ScatterArgs& a, bool bf16_cache, hipStream_t 
 }
 
 hipError_t launch_residual_norm(const float* part, int S, int M, int D, float* h, const void* g, float eps,
-                                float* a_out, bool bf16, hipStream_t st, HiLo pl) {
+                                float* a_out, bool bf16, hipStream_t st, HiLo pl, void* tap) {
   const dim3 block(row_threads(D));
   if ((pl.hi == nullptr) != (pl.lo == nullptr) || (pl.hi != nullptr && !bf16)) return hipErrorInvalidValue;
   if (bf16)
-    hipLaunchKernelGGL(residual_norm_kernel<uint16_t>, dim3(M), block, 0, st, part, S, M, D, h, g, eps, a_out, pl);
-  else hipLaunchKernelGGL(residual_norm_kernel<float>, dim3(M), block, 0, st, part, S, M, D, h, g, eps, a_out, pl);
+    hipLaunchKernelGGL(residual_norm_kernel<uint16_t>, dim3(M), block, 0, st, part, S, M, D, h, g, eps, a_out, pl,
+                       tap);
+  else
+    hipLaunchKernelGGL(residual_norm_kernel<float>, dim3(M), block, 0, st, part, S, M, D, h, g, eps, a_out, pl, tap);
   return hipGetLastError();
 }
 

@@ -1260,9 +1260,9 @@ GemmPlan plan_gemm_rk(int M, int N, int K, bool top2) {
 }
 
 // Register-K for a short weight: 2 k-steps per wave (a K range of 1024 per
-// workgroup, S = K / 1024 splits) and two tiles in flight per wave, so that a
-// workgroup reads only 64 KB of the activation block while its stream of 16 KB
-// weight pieces stays deep.
+// workgroup, S = K / 1024 splits), so that a workgroup reads only 64 KB of the
+// activation block while 256 workgroups keep the stream of 32 KB weight
+// pieces deep.
 GemmPlan plan_gemm_rk_short(int M, int N, int K) {
   GemmPlan p;
   if (M < 1 || M > rk_max_rows(false) || K % (32 * 2 * kRkWaves) != 0 || env_int("DFLASH_GEMM_NO_RK", 0) != 0) return p;
@@ -1342,11 +1342,14 @@ hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, fl
   if (ak == A_BF16) {
     if (p.ks == 8) return rk_launch<8, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
     if (p.ks == 4) return rk_launch<4, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
-    return rk_launch<2, RK_PART, 2, A_BF16>(a, p, nullptr, nullptr, st);
+    return rk_launch<2, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
   }
   if (p.ks == 8) return rk_launch<8, RK_PART, 1>(a, p, nullptr, nullptr, st);
   if (p.ks == 4) return rk_launch<4, RK_PART, 1>(a, p, nullptr, nullptr, st);
-  return rk_launch<2, RK_PART, 2>(a, p, nullptr, nullptr, st);
+  // the short form streams one tile at a time as well: on cold weights (34-100 MB,
+  // rotated past the Infinity Cache) one tile in flight per wave beats two by
+  // 0.5-0.8 us per call and four lose 1-3 us
+  return rk_launch<2, RK_PART, 1>(a, p, nullptr, nullptr, st);
 }
 
 hipError_t launch_gemm_rk_sample(const GemmArgs& a0, const GemmPlan& p, float4* stats, float* logits,

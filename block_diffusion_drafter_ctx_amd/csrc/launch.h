@@ -158,9 +158,11 @@ struct HiLo {
 };
 
 // h[m] += sum_s part[s][m]; a[m] = g * h / sqrt(mean(h^2)+eps)   (part may be null;
-// a as planes when pl.hi is set)
+// a as planes when pl.hi is set).  tap (nullable): the updated h also stored
+// there, [M][D] in the weight type (a tapped hidden state of a target layer).
 hipError_t launch_residual_norm(const float* part, int S, int M, int D, float* h, const void* g,
-                                float eps, float* a_out, bool bf16, hipStream_t st, HiLo pl = HiLo{});
+                                float eps, float* a_out, bool bf16, hipStream_t st, HiLo pl = HiLo{},
+                                void* tap = nullptr);
 
 // s[m][f] = silu(sum_s part[s][m][f]) * sum_s part[s][m][F+f]   (s as planes when pl.hi is set)
 hipError_t launch_swiglu(const float* part, int S, int M, int F, float* s_out, hipStream_t st, HiLo pl = HiLo{});
@@ -265,6 +267,8 @@ struct AttnArgs {
   int32_t blk0[kMaxSeq];      // -1: the block's rows follow the context (keys [0, nkeys[b]));
                               // else its own rows [blk0, blk0 + gam) are a separate key item
                               // after the context keys [0, nkeys[b]) (blk0 % 32 == 0)
+  int32_t causal;        // 1: block row i sees keys [0, nkeys[b] - gam[b] + i] only (blocks that
+                         // follow their context; an autoregressive target's verify pass)
   int32_t split_keys;    // keys per work item (multiple of 32)
   int32_t items;
   float scale_log2;      // log2(e) / sqrt(d)

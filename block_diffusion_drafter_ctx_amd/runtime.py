@@ -24,6 +24,18 @@ def dims_of(cfg) -> B.Dims:
                   cache_dtype=B.BF16 if cfg.cache_dtype == "bf16" else B.F32)
 
 
+def tap_layers(L_t: int, n: int = 5) -> list:
+    """0-based indices of the target layers whose hidden states the drafter
+    fuses: n layers spread evenly from the target's second layer to its
+    third-from-last ("DFlash: Block Diffusion for Flash Speculative Decoding
+    논문 정리", section "실험 설정", settings table; "ICML'26 | DFlash", section
+    3.1), a fractional position rounded half up (integer arithmetic)."""
+    if n < 2:
+        return [1]
+    span = L_t - 4
+    return [1 + (2 * k * span + (n - 1)) // (2 * (n - 1)) for k in range(n)]
+
+
 def torch_dtype(cfg):
     """Weight / target-state type."""
     return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -70,6 +82,16 @@ class DeviceCache:
         k = self.k[:, b, :, lo:hi].float().cpu().numpy().transpose(0, 2, 1, 3)
         v = self.v[:, b, :, :, lo:hi].float().cpu().numpy().transpose(0, 3, 1, 2)
         return k.astype(np.float64), v.astype(np.float64)
+
+    def put_rows(self, b: int, lo: int, k: np.ndarray, v: np.ndarray):
+        """Write rows [lo, lo + n) of sequence b in every layer from (K, V)
+        arrays [L][n][Hkv][d] (values exact in the cache type); lengths are
+        not changed."""
+        n = k.shape[1]
+        kt = torch.from_numpy(np.ascontiguousarray(k.transpose(0, 2, 1, 3), dtype=np.float32))
+        vt = torch.from_numpy(np.ascontiguousarray(v.transpose(0, 2, 3, 1), dtype=np.float32))
+        self.k[:, b, :, lo:lo + n] = kt.to(self.k.device, self.k.dtype)
+        self.v[:, b, :, :, lo:lo + n] = vt.to(self.v.device, self.v.dtype)
 
     def snapshot(self, b: int, n: int):
         """A device copy of rows [0, n) of sequence b in every layer."""
@@ -197,6 +219,12 @@ class DeviceDrafter:
         B.sample_accept(self.dims, B_, gamma, temperature, p(draft), p(draft_logits), p(draft_lse),
                         p(target_logits), p(accept_u), p(resid_u), p(tau), p(nxt), p(self.ws), self.ws_bytes,
                         _stream())
+
+    # ---- the target's verify pass (this object holding a target's weights)
+    def target_verify(self, cache: DeviceCache, tokens, gamma: int, tap_layers, taps, target_tokens, gap=None):
+        p = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+        B.target_verify(self.dims, self.weights, cache.struct, p(tokens), gamma, list(tap_layers),
+                        [t.data_ptr() for t in taps], p(target_tokens), p(gap), p(self.ws), self.ws_bytes, _stream())
 
     # ---- blocks with a length per sequence
     def draft_ragged(self, cache: DeviceCache, tokens, override, gammas, h_final: torch.Tensor):

@@ -14,6 +14,9 @@
  *   dflash_draft_forward_ragged, dflash_argmax_accept_ragged
  * and the drafter over many anchored blocks at once (the training-style mask):
  *   dflash_draft_forward_blocks
+ * the target model's side of an iteration (its causal verify pass over the
+ * block, with the hidden states of the tapped layers):
+ *   dflash_target_verify
  * and, for decoding at a temperature T > 0, the sampled counterpart of (d):
  *   dflash_sample_drafts  draft tokens drawn from softmax(logits / T)
  *   dflash_sample_accept  lossless acceptance of a sampled block against the
@@ -302,6 +305,40 @@ dflash_status dflash_argmax_accept_ragged(const dflash_dims* dims, const dflash_
                                           const int32_t* target, int32_t* tau, int32_t* next_anchor,
                                           float* logits_dbg, float* top2_gap, void* ws, size_t ws_bytes,
                                           void* stream);
+
+/* The target side of a drafting iteration, on a target model of the
+ * drafter's layer form (dims->L target layers; pre-norm residual layers, no
+ * position encoding, no bias) with causal attention.  [JP] "방법론 / 추론
+ * 구조", last step: the target verifies the drafted block in one parallel
+ * pass; [JP] "실험 설정" (settings table) and [MG] section 3.1: the drafter
+ * fuses the hidden states of 5 target layers spread uniformly from the
+ * second to the third-from-last.
+ * For each sequence b the block is block_tokens[b] = (anchor, d_0 .. d_{n-1}),
+ * n = gamma - 1.  Block row i attends to the target's cached context rows
+ * [0, len[b]) and to block rows 0..i; its K/V rows go to the target cache's
+ * scratch rows [len[b], len[b] + i] (len is not changed: after acceptance the
+ * caller keeps the first tau[b] rows by adding tau[b] to len[b]).
+ *   target_tokens[b][i] = argmax of lm_head . RMSNorm(h_i; g_final) (lowest id
+ *   on ties): the target's token at draft position i (i < n), then its bonus
+ *   (i = n) -- the `target` input of dflash_argmax_accept(DFLASH_ACCEPT).
+ *   taps[k] receives the residual stream after layer tap_layers[k] for every
+ *   block row, [B * gamma][D] in the weight type: the rows [b * gamma,
+ *   b * gamma + tau[b]) are the target states of the newly verified tokens,
+ *   the input of dflash_fuse_context (n_tgt_layers = dims->n_tgt_layers).
+ *   dims         the target's shape (n_tgt_layers taps, mask_id unused)
+ *   w            target weights: w_qkv, w_o, w_gateup, w_down, g_attn, g_ffn,
+ *                g_final, embed, lm_head (w_c, g_c unused)
+ *   cache        the target's own KV cache (same layout as the drafter's)
+ *   block_tokens [B][gamma] int32 device, gamma in [1, DFLASH_MAX_GAMMA]
+ *   tap_layers   HOST [n_tgt_layers], increasing, each in [0, L)
+ *   taps         HOST array of n_tgt_layers device pointers
+ *   target_tokens out [B][gamma] int32; top2_gap nullable out [B][gamma] float32
+ * Errors: DFLASH_ERR_CAPACITY if len[b] + gamma > cap.  Workspace:
+ * dflash_workspace_size(dims, B, gamma, ..). */
+dflash_status dflash_target_verify(const dflash_dims* dims, const dflash_weights* w, const dflash_kv_cache* cache,
+                                   const int32_t* block_tokens, int32_t gamma, const int32_t* tap_layers,
+                                   void* const* taps, int32_t* target_tokens, float* top2_gap, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /* Sampled drafting at temperature T ([JP] "주요 결과": DFlash decodes at
  * temperature 1 as well as greedily; [JP] "학습 방법": all block positions after

@@ -44,11 +44,14 @@ def to_bf16(x) -> np.ndarray:
 
 
 def store(x, storage: str) -> np.ndarray:
-    """Value of ``x`` after it is written to a tensor of the storage type."""
+    """Value of ``x`` after it is written to a tensor of the storage type
+    ("f64": kept as computed, for callers that round it themselves)."""
     if storage == "bf16":
         return to_bf16(x)
     if storage == "f32":
         return np.asarray(x, dtype=np.float32).astype(F64)
+    if storage == "f64":
+        return np.asarray(x, dtype=F64)
     raise ValueError(storage)
 
 

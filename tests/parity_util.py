@@ -83,6 +83,38 @@ def close_stored(got, ref, dtype, what, tol=None):
     return float(diff.max(initial=0.0)), rel
 
 
+def close_rounded(got, exact, dtype, what, tol=None, eps=1e-4):
+    """A tensor stored in ``dtype`` against the oracle's unrounded values.  The
+    tolerance class ``tol`` applies to the oracle's stored value r = store(x);
+    beyond it an element may only be r's neighbour in the storage type on the
+    other side of x, when x lies within eps * |x| of the midpoint between the
+    two (a rounding decision the two sides' accumulation errors may take
+    either way).  No share of such elements is capped: each must be a near-tie."""
+    tol = dtype if tol is None else tol
+    x = np.asarray(exact, dtype=np.float64)
+    r = O.store(x, dtype)
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == x.shape, (what, got.shape, x.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    mx, rl = TOL[tol]
+    diff = np.abs(got - r)
+    over = diff > mx
+    if over.any():
+        g, rr, xx = got[over], r[over], x[over]
+        ulp = bf16_ulp(np.minimum(np.abs(g), np.abs(rr))) if dtype == "bf16" else np.spacing(np.abs(rr).astype(np.float32)).astype(np.float64)
+        neighbour = np.abs(g - rr) <= ulp * (1 + 1e-9)
+        bracket = (np.minimum(g, rr) <= xx) & (xx <= np.maximum(g, rr))
+        near_tie = np.abs(xx - 0.5 * (g + rr)) <= eps * np.abs(xx)
+        bad = ~(neighbour & bracket & near_tie)
+        assert not bad.any(), (f"{what}: {int(bad.sum())} of {int(over.sum())} elements beyond max-abs {mx} are not "
+                               f"near-tie neighbours (worst |x - midpoint| / |x| "
+                               f"{float(np.max(np.abs(xx - 0.5 * (g + rr))[bad] / np.abs(xx[bad]))):.2e})")
+    den = float(np.linalg.norm(r))
+    rel = float(np.linalg.norm(got - r) / den) if den > 0 else float(diff.max(initial=0.0))
+    assert rel <= rl, f"{what}: rel {rel:.3e} (tol {rl})"
+    return float(diff.max(initial=0.0)), rel, int(over.sum())
+
+
 def argmax_agree(gpu_ids, ora_ids, ora_gap, what, gap_min=GAP_MIN):
     gpu_ids = np.asarray(gpu_ids).reshape(-1)
     ora_ids = np.asarray(ora_ids).reshape(-1)

@@ -135,6 +135,38 @@ def test_noalloc_refuses_passes_beyond_its_scratch(lib):
             assert e.value.status == B.ERR_WORKSPACE and "no-allocation" in B.last_error()
 
 
+def test_target_verify_checks(lib):
+    w = B.Weights(w_qkv=0x1000, w_o=0x1000, w_gateup=0x1000, w_down=0x1000, g_attn=0x1000, g_ffn=0x1000,
+                  g_final=0x1000, embed=0x1000, lm_head=0x1000)
+    taps = [0x8000] * 5
+    ok_layers = [0, 1, 2, 3, 4]
+
+    def call(**kw):
+        a = dict(dims=_dims(L=8), w=w, cache=_cache(lens=(10, 0)), tok=0x4000, gamma=16, layers=ok_layers, taps=taps,
+                 out=0x5000, ws=0x100000, nbytes=1 << 30)
+        a.update(kw)
+        with pytest.raises(B.DFlashError) as e:
+            B.target_verify(a["dims"], a["w"], a["cache"], a["tok"], a["gamma"], a["layers"], a["taps"], a["out"],
+                            None, a["ws"], a["nbytes"])
+        return e.value.status
+
+    assert call(gamma=0) == B.ERR_INVALID_ARG
+    assert call(gamma=34) == B.ERR_INVALID_ARG
+    assert call(layers=[0, 1, 2, 3, 8]) == B.ERR_INVALID_ARG      # layer outside [0, L)
+    assert call(layers=[0, 2, 1, 3, 4]) == B.ERR_INVALID_ARG      # not increasing
+    assert call(taps=[0x8000] * 4 + [0x8001]) == B.ERR_INVALID_ARG   # misaligned tap buffer
+    assert call(out=0) == B.ERR_INVALID_ARG
+    assert call(cache=_cache(cap=64, lens=(50, 0))) == B.ERR_CAPACITY
+    assert call(nbytes=16) == B.ERR_WORKSPACE
+    # gamma 1 (a plain decoding step) passes the argument checks
+    assert call(gamma=1) not in (B.ERR_INVALID_ARG, B.ERR_CAPACITY, B.ERR_WORKSPACE)
+
+
+def test_workspace_covers_target_verify(lib):
+    qwen = _dims(D=4096, L=36, Hq=32, Hkv=8, head_dim=128, F=12288, V=151936, mask_id=151935)
+    assert B.workspace_size(qwen, 1, 16, 0) > 0
+
+
 def test_len_dev_alignment(lib):
     with pytest.raises(B.DFlashError) as e:
         B.inject_kv(_dims(), B.Weights(w_qkv=0x1000), 0x3000, [1, 1], _cache(len_dev=0x3002), 0, 0)

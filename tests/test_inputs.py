@@ -79,3 +79,14 @@ def test_synthetic_target_logits():
     assert np.array_equal(t[:, 15], nz[:, 15])
     ids = inp.random_ids(0, 16)
     assert ids.shape == (2, 15) and ids.min() >= 0 and ids.max() < 3000
+
+
+def test_runtime_tap_layers_match_the_oracle():
+    # the product side's tap-layer rule (integer arithmetic) against the oracle's
+    from block_diffusion_drafter_ctx_amd.runtime import tap_layers
+    from oracle import dflash_oracle as O
+    for L_t in range(4, 129):
+        for n in (2, 3, 4, 5, 6, 8):
+            if L_t - 3 >= 1:
+                assert tap_layers(L_t, n) == O.tap_layers(L_t, n), (L_t, n)
+    assert tap_layers(36) == [1, 9, 17, 25, 33]
