@@ -1,7 +1,8 @@
 """Benchmark of the DFlash drafter hot path on one MI355X.
 
 One step is one drafting iteration of the whole path on the Qwen3-8B-shaped
-drafter at a 2048-token context (batch 1, block gamma = 16, 5 layers):
+drafter at a 2048-token context (batch 1, block gamma = 16, 5 layers, bf16
+weights, bf16 H_t and KV cache):
   draft forward -> LM-head argmax -> synthetic target tokens (p = 0.8 match)
   -> greedy accept -> append the next 16 target rows (fuse + inject).
 The context (fuse + inject of 2048 rows) is ingested once before timing; every
@@ -9,14 +10,18 @@ The context (fuse + inject of 2048 rows) is ingested once before timing; every
 written), so the timed loop cycles through 8 iteration shapes.
 
 Prints one JSON line.  ``value`` is drafted blocks per second (batch x steps /
-time).  ``roofline`` covers the dominant kernel (the LM-head GEMM with its
-argmax, the largest single weight stream of a step) timed with HIP events on
-the library's stream; ``cpu_baseline`` times the CPU oracle on a bounded sample
-(whole iterations).  ``sampling`` measures the same step decoded at temperature
-1: drafts drawn from softmax(z / T) in the LM head's epilogue, synthetic target
-logits (draft logits + N(0, 0.5^2) noise, the bonus row N(0, 1)), lossless
-verification, append; with its kernels' HBM fractions and its own oracle
-baseline.
+time).  ``roofline`` covers the kernel with the most time in a step (per-launch
+algorithmic bytes over its launches' HIP-event durations on the library's
+stream); ``roofline_lm_head`` the LM head.  ``cpu_baseline`` times the CPU
+oracle on a bounded sample (whole iterations).  Further legs: ``sampling``
+(the same step decoded at temperature 1 with lossless verification),
+``ragged`` (block lengths per sequence), ``blocks`` (anchored blocks, the
+training-style mask), ``long_context`` (32768-token context, both cache
+types), ``gamma_sweep`` (8-layer drafter, blocks of 8/16/32 at a fixed
+cache), ``loops`` (blocks/s of the tiny, long-context, 16-sequence and 8-layer
+workloads over their 8-iteration loops with appends) and ``speculative``
+(greedy speculative decoding with a 36-layer synthetic Qwen3-8B-shaped target
+verifying each block).
 """
 from __future__ import annotations
 
@@ -31,27 +36,70 @@ sys.path.insert(0, ROOT)
 
 METRIC = "drafted gamma=16 blocks/sec + draft fwd us at 1 GPU; % HBM BW / % MFMA peak"
 
-# HBM bytes per LM-head launch from two rocprofv3 counter passes over this
-# script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what
-# the same counter reads for the 256 MiB device copy at the end of main():
-# FETCH_SIZE reads 0.5x the copy's bytes, WRITE_SIZE 1.0x.  Valid only for the
-# default workload and only while the GEMM sources hash to ``src``; otherwise
-# the traffic is reported as null.
-LM_HEAD_COUNTERS = {"src": "f04fee123a8483cc", "workload": "qwen3_8b_shape_n2048", "cache": "f32",
-                    "fetch_kib": 608755.4, "write_kib": 52.0, "fetch_scale": 1.9998, "write_scale": 1.0}
+# HBM bytes per launch of the roofline kernels from two rocprofv3 counter passes
+# over this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled
+# by what the same counter reads for the 256 MiB device copy at the end of
+# main().  Valid only for the recorded workload and cache and only while the
+# GEMM sources hash to ``src``; otherwise the traffic is reported as null.
+KERNEL_COUNTERS = {}
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/launch.h")
 
 
-def lm_head_traffic(workload, cache):
+def gemm_sources_hash():
     import hashlib
-    c = LM_HEAD_COUNTERS
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
         with open(os.path.join(ROOT, "block_diffusion_drafter_ctx_amd", f), "rb") as fh:
             h.update(fh.read())
-    if h.hexdigest()[:16] != c["src"] or workload != c["workload"] or cache != c["cache"]:
+    return h.hexdigest()[:16]
+
+
+def kernel_traffic(which, workload, cache):
+    """HBM bytes per launch of a kernel from the recorded rocprofv3 counters
+    (null unless they were taken on the current GEMM sources, workload and cache)."""
+    c = KERNEL_COUNTERS.get(which)
+    if c is None or gemm_sources_hash() != c["src"] or workload != c["workload"] or cache != c["cache"]:
         return None
     return int(round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024))
+
+
+# Kernel families of one headline step: (name, per-kernel roles it runs, which of
+# them it runs only with an fp32 cache).  The short-weight register-K GEMM takes
+# the Q/K/V, O and down projections and, with an fp32 H_t, the 16-row inject.
+FAMILIES = (
+    ("gemm_rk_kernel<2, RK_PART, 1, A_F32_SPLIT> (short weights: Q/K/V, O and down projections of every layer, "
+     "and the 16-row K/V inject with an fp32 H_t; 16 fp32 activation rows as bf16 hi + lo in registers, split-K "
+     "partials reduced by the next kernel)", ("qkv", "o_proj", "down", "inject_append"), ("inject_append",)),
+    ("gemm_rk_kernel<8, RK_SWIGLU> (FFN gate/up with SwiGLU in the epilogue)", ("gate_up",), ()),
+    ("attention (split over key ranges + log-sum-exp combine)", ("attention",), ()),
+)
+
+
+def dominant_roofline(cfg, per_kernel, lm_bytes, lm_us, workload):
+    """The roofline entry of the kernel with the most time per step: per-launch
+    algorithmic bytes and duration averaged over its launches in a step."""
+    import numpy as np  # noqa: F401
+    from block_diffusion_drafter_ctx_amd import roofline as RF
+    calls = {"qkv": cfg.L, "o_proj": cfg.L, "gate_up": cfg.L, "down": cfg.L, "attention": cfg.L, "inject_append": 1,
+             "fuse_append": 1}
+    cands = [("gemm_rk_kernel<8, RK_TOP2> (LM head with the top-2 epilogue)", lm_bytes, lm_us, 1, "lm_head")]
+    for name, roles, f32_only in FAMILIES:
+        rs = [r for r in roles if r in per_kernel and not (r in f32_only and cfg.cache_dtype != "f32")]
+        n = sum(calls[r] for r in rs)
+        if n == 0:
+            continue
+        tb = sum(per_kernel[r]["bytes"] * calls[r] for r in rs)
+        tu = sum(per_kernel[r]["us"] * calls[r] for r in rs)
+        cands.append((name, tb / n, tu / n, n, "short_rk" if name.startswith("gemm_rk_kernel<2") else None))
+    name, b, us, n, key = max(cands, key=lambda c: c[2] * c[3])
+    gbs = b / (us * 1e-6) / 1e9
+    return {"kernel": name + f"; {n} launch(es) per step, the largest kernel time of a step; HIP events around each "
+                             f"launch on the library stream (dflash_profile_events)",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": RF.HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / RF.HBM_PEAK_GBS, 4),
+            "traffic": kernel_traffic(key, workload, cfg.cache_dtype) if key else None,
+            "bytes_per_launch": int(b), "us_per_launch": round(us, 2), "launches_per_step": n,
+            "us_per_step": round(us * n, 1)}
 
 
 def log(msg):
@@ -68,14 +116,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="run the CPU oracle for about this long (whole iterations)")
-    ap.add_argument("--cache", choices=["f32", "bf16"], default="f32",
-                    help="storage type of H_t and the KV cache")
+    ap.add_argument("--cache", choices=["f32", "bf16"], default="bf16",
+                    help="storage type of H_t and the KV cache (bf16: the method's own; f32: for comparison)")
     ap.add_argument("--temperature", type=float, default=1.0, help="temperature of the sampled-decoding leg")
     ap.add_argument("--no-sampling", action="store_true", help="skip the sampled-decoding leg")
     ap.add_argument("--no-ragged", action="store_true", help="skip the per-sequence block-length leg")
     ap.add_argument("--no-blocks", action="store_true", help="skip the anchored-blocks (training-mask) leg")
     ap.add_argument("--no-gamma-sweep", action="store_true", help="skip the block-length sweep on the 8-layer drafter")
     ap.add_argument("--no-long-context", action="store_true", help="skip the 32768-token context leg")
+    ap.add_argument("--no-speculative", action="store_true",
+                    help="skip the speculative-decoding leg with a 36-layer synthetic target")
+    ap.add_argument("--no-loops", action="store_true",
+                    help="skip the drafting loops of the tiny, long-context, 16-sequence and 8-layer workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs the drafting "
@@ -287,13 +339,15 @@ def main():
         "context_us": round(context_us, 1),
         "context_mfma_frac": round(ctx_flops / (context_us * 1e-6) / 1e12 / RF.MFMA_BF16_TFLOPS, 4),
         "per_kernel": per_kernel,
-        "roofline": {
+        "roofline": dominant_roofline(cfg, per_kernel, lm_bytes, lm_us, args.workload),
+        "roofline_lm_head": {
             "kernel": "gemm_rk_kernel<8, RK_TOP2> (LM head: 151936 x 4096 bf16 streamed once against the 15 "
                       "mask rows held in registers as bf16 hi + lo, logits reduced in-kernel to a top-2 per "
                       "workgroup), one launch per step, HIP events recorded around that launch on the library "
                       "stream by dflash_profile_events",
             "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": RF.HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(lm_gbs / RF.HBM_PEAK_GBS, 4), "traffic": lm_head_traffic(args.workload, cfg.cache_dtype),
+            "frac": round(lm_gbs / RF.HBM_PEAK_GBS, 4), "traffic": kernel_traffic("lm_head", args.workload,
+                                                                                   cfg.cache_dtype),
             "bytes_per_launch": lm_bytes, "us_per_launch": round(lm_us, 2),
         },
     }
@@ -307,10 +361,20 @@ def main():
         out["blocks"] = blocks_leg(cfg, dr)
     if not args.no_long_context and cfg.dtype == "bf16":
         out["long_context"] = long_context_leg(cfg, dr)
+        other = "bf16" if cfg.cache_dtype == "f32" else "f32"
+        out["long_context_" + other + "_cache"] = long_context_leg(shrink(cfg, cache_dtype=other),
+                                                                   dr.with_cache_dtype(other))
     if not args.no_gamma_sweep and cfg.dtype == "bf16":
         del dr, cache
         torch.cuda.empty_cache()
         out["gamma_sweep"] = gamma_sweep_leg()
+    if not args.no_loops:
+        # the other workloads' drafting loops (blocks/s over 8 iterations with appends)
+        out["loops"] = {}
+        for wl in ("tiny_f32", "long_ctx_n32768", "batch16_ragged", "deep8_b4_n8192"):
+            out["loops"][wl] = workload_loop_leg(wl, args.cache)
+    if not args.no_speculative:
+        out["speculative"] = speculative_leg(args.cache)
 
     # A plain device copy of a known size: the reference that scales rocprofv3's
     # FETCH_SIZE / WRITE_SIZE counters into bytes (256 MiB read + 256 MiB written).
@@ -334,6 +398,8 @@ def main():
             out["blocks"]["cpu_baseline"] = blocks_cpu
         if long_cpu is not None:
             out["long_context"]["cpu_baseline"] = long_cpu
+        if "loops" in out:
+            out["loops"]["tiny_f32"]["cpu_baseline"] = cpu_tiny_baseline()
     print(json.dumps(out), flush=True)
 
 
@@ -707,6 +773,264 @@ def gamma_sweep_leg():
             "per_gamma": res, "us_ratio_max_over_min": round(ratio, 3)}
 
 
+def workload_loop_leg(name, cache_dtype, cycles=3, seed=20261210):
+    """The drafting loop of one workload, per block length: ``cycles`` passes
+    over its 8 iterations, each one draft forward -> LM-head argmax ->
+    synthetic target tokens on the device (the workload's match
+    probabilities) -> greedy accept -> append 16 rows per sequence (fuse +
+    inject); the cache length returns to the context length at the start of
+    every pass.  Blocks/s = sequences x iterations / time, with the algorithmic
+    bytes and FLOPs of an iteration (mean over the cycle's cache lengths)
+    against the HBM and bf16 MFMA peaks; plus the draft forward + argmax alone
+    at the context length (median of 20).  Weights are seeded device-side
+    random-init tensors of the workload's shape; context and appended target
+    states are device-side N(0, 1)."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_drafter_ctx_amd import binding as B
+    from block_diffusion_drafter_ctx_amd import roofline as RF
+    from block_diffusion_drafter_ctx_amd.runtime import DeviceDrafter
+    from dflash_inputs import WORKLOADS, shrink
+
+    base = WORKLOADS[name]
+    cfg = shrink(base, cache_dtype=cache_dtype if base.dtype == "bf16" else "f32")
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    Bn, N, A, I = cfg.B, cfg.n_ctx_total, cfg.append_rows, cfg.iters
+    wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    es = RF.elem_bytes(cfg.dtype)
+    dr = DeviceDrafter.random_init(cfg, seed, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 1)
+    rng = np.random.default_rng([seed, cfg.cid])
+    out = {"workload": (f"{cfg.name}: batch {Bn}, contexts {'U[1024, 4096] (sum %d)' % N if Bn > 1 and len(set(cfg.ctx)) > 1 else cfg.ctx[0]}, "
+                        f"{cfg.L} layers, D={cfg.D}, {cfg.Hq}q/{cfg.Hkv}kv x {cfg.d}, FFN {cfg.F}, V={cfg.V}, "
+                        f"{cfg.dtype} weights, {cfg.cache_dtype} cache; {I} iterations of draft forward + argmax + "
+                        f"accept + {A}-row append per sequence"),
+           "per_gamma": {}}
+    for g in cfg.gammas:
+        n = g - 1
+        cap = (max(cfg.ctx) + I * A + g + 31) // 32 * 32
+        cache = dr.cache(Bn, cap)
+        dr.ensure_workspace(Bn, g, max(min(N, 8192), Bn * A))
+        H_t = dr.context_buffer(min(N, 8192))
+        rows = 0
+        lens0 = [0] * Bn
+        # context ingest (untimed) in row blocks of at most 8192, sequence by sequence
+        for b, nb in enumerate(cfg.ctx):
+            for r0 in range(0, nb, 8192):
+                m = min(8192, nb - r0)
+                st = [torch.randn(m, cfg.D, generator=gen, device=dev).to(wdt) for _ in range(cfg.n_tgt)]
+                dr.fuse(st, m, H_t)
+                counts = [0] * Bn
+                counts[b] = m
+                dr.inject(H_t, counts, cache)
+                del st
+        base_lens = cache.len_list()
+        app = []
+        for it in range(I):
+            st = [torch.randn(Bn * A, cfg.D, generator=gen, device=dev).to(wdt) for _ in range(cfg.n_tgt)]
+            match = rng.random((Bn, n)) < cfg.match_probs(g)[None, :]
+            shift = np.where(match, 0, rng.integers(1, cfg.V, (Bn, n))).astype(np.int32)
+            tgt = np.zeros((Bn, g), dtype=np.int32)
+            tgt[:, n] = rng.integers(0, cfg.V, Bn)
+            app.append(dict(states=st, shift=torch.from_numpy(shift).to(dev), target=torch.from_numpy(tgt).to(dev)))
+        H_app = dr.context_buffer(Bn * A)
+        tokens = torch.full((Bn, g), cfg.mask_id, dtype=torch.int32, device=dev)
+        tokens[:, 0] = torch.from_numpy(rng.integers(0, cfg.V - 1, Bn).astype(np.int32)).to(dev)
+        h_final = torch.empty(Bn, g, cfg.D, dtype=torch.float32, device=dev)
+        draft = torch.empty(Bn, n, dtype=torch.int32, device=dev)
+        tau = torch.empty(Bn, dtype=torch.int32, device=dev)
+        nxt = torch.empty(Bn, dtype=torch.int32, device=dev)
+        tmp = torch.empty(Bn, n, dtype=torch.int32, device=dev)
+
+        def step(i):
+            it = i % I
+            if it == 0:
+                cache.set_lens(base_lens)
+            dr.draft(cache, tokens, None, g, h_final)
+            dr.argmax_accept(B.ARGMAX, h_final, Bn, g, draft)
+            d = app[it]
+            torch.add(draft, d["shift"], out=tmp)
+            torch.remainder(tmp, cfg.V, out=d["target"][:, :n])
+            dr.argmax_accept(B.ACCEPT, None, Bn, g, draft, target=d["target"], tau=tau, nxt=nxt)
+            tokens[:, 0].copy_(nxt)
+            dr.fuse(d["states"], Bn * A, H_app)
+            dr.inject(H_app, [A] * Bn, cache)
+
+        for i in range(I):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(cycles * I):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        us_it = max(e0.elapsed_time(e1) * 1e3, wall * 1e6) / (cycles * I)
+        taus = tau.cpu().numpy()
+        # the draft forward + argmax alone at the context length
+        cache.set_lens(base_lens)
+        ev = []
+        for rep in range(23):
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dr.draft(cache, tokens, None, g, h_final)
+            dr.argmax_accept(B.ARGMAX, h_final, Bn, g, draft)
+            b_.record(stream)
+            if rep >= 3:
+                ev.append((a, b_))
+        torch.cuda.synchronize()
+        fwd_us = float(np.median([a.elapsed_time(b_) for a, b_ in ev])) * 1e3
+        # algorithmic work of one iteration, averaged over the cycle's cache lengths
+        nbytes = fl = 0.0
+        for it in range(I):
+            ctx = [c + A * it for c in cfg.ctx]
+            nbytes += (RF.draft_forward_bytes(cfg.D, cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.F, cfg.V, Bn, g, ctx, es, es)
+                       + RF.fuse_bytes(Bn * A, cfg.D, cfg.n_tgt, es, es)
+                       + RF.inject_bytes(Bn * A, cfg.D, cfg.L, cfg.Hkv, cfg.d, es, es)
+                       + RF.accept_bytes(Bn, n)) / I
+            fl += (RF.draft_forward_flops(cfg.D, cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.F, cfg.V, Bn, g, ctx)
+                   + RF.fuse_flops(Bn * A, cfg.D, cfg.n_tgt) + RF.inject_flops(Bn * A, cfg.D, cfg.L, cfg.Hkv, cfg.d)) / I
+        fwd_bytes = RF.draft_forward_bytes(cfg.D, cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.F, cfg.V, Bn, g, list(cfg.ctx),
+                                           es, es)
+        peak_tf = RF.MFMA_BF16_TFLOPS if cfg.dtype == "bf16" else RF.FP32_VECTOR_TFLOPS
+        out["per_gamma"][str(g)] = {
+            "blocks_per_s": round(Bn * 1e6 / us_it, 2), "us_per_iteration": round(us_it, 1),
+            "bytes_per_iteration": int(nbytes), "gflop_per_iteration": round(fl / 1e9, 2),
+            "hbm_frac": round(nbytes / (us_it * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4),
+            "mfma_frac": round(fl / (us_it * 1e-6) / 1e12 / peak_tf, 4),
+            "draft_fwd_us": round(fwd_us, 1),
+            "draft_fwd_hbm_frac": round(fwd_bytes / (fwd_us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4),
+            "last_tau": taus.tolist()[:16]}
+        log(f"loop {cfg.name} gamma {g}: {us_it:.1f} us per iteration ({Bn * 1e6 / us_it:.1f} blocks/s), "
+            f"draft fwd {fwd_us:.1f} us")
+        del cache, app, H_t, H_app
+    if len(cfg.gammas) > 1:
+        us = [v["draft_fwd_us"] for v in out["per_gamma"].values()]
+        out["draft_fwd_us_ratio_max_over_min"] = round(max(us) / min(us), 3)
+    if cfg.dtype != "bf16":
+        out["note"] = "fp32 weights: latency-bound (reported, not graded); mfma_frac is against the fp32 vector peak"
+    del dr
+    torch.cuda.empty_cache()
+    return out
+
+
+def speculative_leg(cache_dtype, steps=24, seed=20261220):
+    """Greedy speculative decoding with the target side in the loop, on a
+    synthetic Qwen3-8B-shaped target (36 layers of the drafter's layer shape,
+    causal attention, seeded device-side random init) and the 5-layer drafter,
+    which shares the target's embedding and LM head.  One step: draft forward
+    + LM-head argmax -> the target's verify pass over (anchor, drafts) with
+    its 5 tapped layers -> greedy accept -> commit (the target keeps tau rows
+    of K/V; the drafter fuses and injects the tau rows' tapped states).  The
+    host reads tau each step (a serving loop must, to emit the tokens).  Both
+    caches start from a 2048-token context (target K/V and drafter context
+    states N(0, 1)) and return to it every 8 steps.  Random weights make the
+    drafter and target disagree (tau ~ 1), so the figures here are the
+    drafting and verify costs of the pages' latency model, (T_draft +
+    T_verify) / tau, not an acceptance rate."""
+    import numpy as np
+    import torch
+
+    from block_diffusion_drafter_ctx_amd import binding as B
+    from block_diffusion_drafter_ctx_amd import roofline as RF
+    from block_diffusion_drafter_ctx_amd.runtime import DeviceDrafter, tap_layers
+    from dflash_inputs import QWEN3_8B_N2048, shrink
+
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    dcfg = shrink(QWEN3_8B_N2048, cache_dtype=cache_dtype)
+    tcfg = shrink(QWEN3_8B_N2048, name="qwen3_8b_shaped_target", L=36, cache_dtype=cache_dtype)
+    g, n, N = 16, 15, dcfg.ctx[0]
+    taps = tap_layers(tcfg.L, tcfg.n_tgt)
+    tgt = DeviceDrafter.random_init(tcfg, seed, dev)
+    drf = DeviceDrafter.random_init(dcfg, seed + 1, dev)
+    drf.embed = tgt.embed
+    drf.weights.embed = drf.weights.lm_head = tgt.embed.data_ptr()
+    cap = (N + 8 * g + g + 31) // 32 * 32
+    tcache, dcache = tgt.cache(1, cap), drf.cache(1, cap)
+    tgt.ensure_workspace(1, g, 1)
+    drf.ensure_workspace(1, g, N)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 2)
+    cdt = tcache.k.dtype
+    tcache.k[:, 0, :, :N].copy_(torch.randn(tcfg.L, tcfg.Hkv, N, tcfg.d, generator=gen, device=dev).to(cdt))
+    tcache.v[:, 0, :, :, :N].copy_(torch.randn(tcfg.L, tcfg.Hkv, tcfg.d, N, generator=gen, device=dev).to(cdt))
+    tcache.set_lens([N])
+    st = [torch.randn(N, dcfg.D, generator=gen, device=dev).to(torch.bfloat16) for _ in range(dcfg.n_tgt)]
+    H = drf.context_buffer(N)
+    drf.fuse(st, N, H)
+    drf.inject(H, [N], dcache)
+    del st, H
+    tap_bufs = [torch.empty(g, tcfg.D, dtype=torch.bfloat16, device=dev) for _ in taps]
+    block = torch.full((1, g), dcfg.mask_id, dtype=torch.int32, device=dev)
+    block[0, 0] = 7
+    tokens = torch.full((1, g), dcfg.mask_id, dtype=torch.int32, device=dev)
+    hf = torch.empty(1, g, dcfg.D, dtype=torch.float32, device=dev)
+    draft = torch.empty(1, n, dtype=torch.int32, device=dev)
+    ttok = torch.empty(1, g, dtype=torch.int32, device=dev)
+    tau = torch.empty(1, dtype=torch.int32, device=dev)
+    nxt = torch.empty(1, dtype=torch.int32, device=dev)
+    H_app = drf.context_buffer(g)
+    ev = {"draft": [], "verify": []}
+
+    def step(i, timed):
+        if i % 8 == 0:
+            tcache.set_lens([N])
+            dcache.set_lens([N])
+        tokens[0, 0] = block[0, 0]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        drf.draft(dcache, tokens, None, g, hf)
+        drf.argmax_accept(B.ARGMAX, hf, 1, g, draft)
+        e[1].record(stream)
+        block[0, 1:].copy_(draft[0])
+        tgt.target_verify(tcache, block, g, taps, tap_bufs, ttok)
+        e[2].record(stream)
+        drf.argmax_accept(B.ACCEPT, None, 1, g, draft, target=ttok, tau=tau, nxt=nxt)
+        t = int(tau.item())                      # the host learns how many tokens were committed
+        tcache.set_lens([tcache.len_list()[0] + t])
+        drf.fuse([b[:t] for b in tap_bufs], t, H_app)
+        drf.inject(H_app, [t], dcache)
+        block[0, 0] = nxt[0]
+        if timed:
+            ev["draft"].append((e[0], e[1]))
+            ev["verify"].append((e[1], e[2]))
+        return t
+
+    for i in range(8):
+        step(i, False)
+    torch.cuda.synchronize()
+    taus = []
+    t0 = time.perf_counter()
+    for i in range(steps):
+        taus.append(step(i, True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    d_us = float(np.median([a.elapsed_time(b) for a, b in ev["draft"]])) * 1e3
+    v_us = float(np.median([a.elapsed_time(b) for a, b in ev["verify"]])) * 1e3
+    step_us = wall / steps * 1e6
+    vbytes = (tcfg.L * RF.layer_weight_elems(tcfg.D, tcfg.Hq, tcfg.Hkv, tcfg.d, tcfg.F) + tcfg.D + tcfg.V * tcfg.D) * 2 \
+        + tcfg.L * (N + 4 * g) * 2 * tcfg.Hkv * tcfg.d * 2
+    log(f"speculative: draft {d_us:.0f} us, verify ({tcfg.L} target layers) {v_us:.0f} us, step {step_us:.0f} us, "
+        f"mean tau {np.mean(taus):.2f}")
+    del tgt, drf, tcache, dcache
+    torch.cuda.empty_cache()
+    return {"workload": (f"greedy speculative decoding, batch 1, 2048-token context: the qwen3_8b_shape_n2048 "
+                         f"drafter and a synthetic Qwen3-8B-shaped target ({tcfg.L} layers, causal, taps {taps}) "
+                         f"sharing the embedding / LM head, random-init weights, {cache_dtype} caches; step = draft "
+                         f"forward + argmax + target verify of 16 rows + accept + commit (host reads tau)"),
+            "t_draft_us": round(d_us, 1), "t_verify_us": round(v_us, 1), "step_us": round(step_us, 1),
+            "verify_over_draft": round(v_us / d_us, 3), "mean_tau": round(float(np.mean(taus)), 3),
+            "tokens_per_s": round(float(np.sum(taus)) / wall, 1),
+            "verify_bytes": int(vbytes),
+            "verify_hbm_frac": round(vbytes / (v_us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4)}
+
+
 BLOCKS_CTX, BLOCKS_N, BLOCKS_GAMMA = 3072, 64, 16
 
 
@@ -777,6 +1101,71 @@ def blocks_leg(cfg, dr):
         "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / RF.HBM_PEAK_GBS, 4),
         "note": "FLOPs are algorithmic (one product per GEMM); the fp32 activations run as two bf16 products",
     }
+
+
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_tiny_baseline(seconds=3.0):
+    """The oracle on whole drafting iterations of the tiny fp32 workload
+    (draft forward + argmax + accept + 16-row append, seeded inputs), on the
+    BLAS threads numpy has and on one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import dflash_oracle as O
+    from dflash_inputs import TINY_F32, Inputs, build_target_np
+
+    cfg = TINY_F32
+    inp = Inputs(cfg)
+    f = lambda a: np.asarray(a, dtype=np.float64)  # noqa: E731
+    layers = [dict(w_qkv=f(inp.w_qkv(l)), w_o=f(inp.w_o(l)), w_gateup=f(inp.w_gateup(l)), w_down=f(inp.w_down(l)),
+                   g_attn=f(inp.g_attn(l)), g_ffn=f(inp.g_ffn(l))) for l in range(cfg.L)]
+    E, gf, wc, gc = f(inp.embed()), f(inp.g_final()), inp.w_c(), inp.g_c()
+    Ht = O.fuse_context(inp.ctx_states(), wc, gc, cfg.eps, cfg.cache_dtype)
+    base = [O.inject_kv(Ht, layers[l]["w_qkv"], cfg.Hq, cfg.Hkv, cfg.d, cfg.cache_dtype) for l in range(cfg.L)]
+    appends = [inp.append_states(it) for it in range(cfg.iters)]
+    draws = [inp.verify_draws(it, cfg.gamma) for it in range(cfg.iters)]
+
+    def run():
+        anchors, done, t0, cache = inp.anchors(), 0, time.perf_counter(), None
+        while done < 4096 and (done == 0 or time.perf_counter() - t0 < seconds):
+            it = done % cfg.iters
+            if it == 0:
+                cache = O.OracleCache(cfg.L, 1, cfg.Hkv, cfg.d)
+                for l in range(cfg.L):
+                    cache.append(l, 0, *base[l])
+            hf, _ = O.draft_forward(cfg, layers, gf, cache, cfg.gamma, embed=E, tokens=inp.block_tokens(cfg.gamma, anchors),
+                                    storage=cfg.cache_dtype)
+            d, _, _ = O.lm_head_argmax(hf, E)
+            m, r, bonus = draws[it]
+            _, anchors = O.accept(d, build_target_np(d, m, r, bonus, cfg.V))
+            Ha = O.fuse_context(appends[it], wc, gc, cfg.eps, cfg.cache_dtype)
+            for l in range(cfg.L):
+                cache.append(l, 0, *O.inject_kv(Ha, layers[l]["w_qkv"], cfg.Hq, cfg.Hkv, cfg.d, cfg.cache_dtype))
+            done += 1
+        return done, time.perf_counter() - t0
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    n_all, t_all = run()
+    with threadpool_limits(limits=1):
+        n_one, t_one = run()
+    log(f"cpu baseline (tiny): {n_all} iterations in {t_all:.1f}s on {threads} threads, {n_one} in {t_one:.1f}s on 1")
+    return {"value": round(n_all / t_all, 2), "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
+            "us_per_iteration": round(t_all / n_all * 1e6, 1),
+            "one_thread": {"value": round(n_one / t_one, 2), "unit": "blocks/s", "cores": 1,
+                           "us_per_iteration": round(t_one / n_one * 1e6, 1)},
+            "cpu_model": cpu_model(),
+            "sample": f"whole drafting iterations of tiny_f32 (draft forward + argmax + accept + 16-row append), "
+                      f"float64 numpy oracle, ~{seconds:.0f} s per thread count"}
 
 
 def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False, blocks=False, long_ctx=False):
@@ -853,6 +1242,7 @@ def cpu_baseline(cfg, inp, seconds, temperature=None, ragged=False, blocks=False
     done, dt = run(False, seconds)
     log(f"cpu baseline: {done} iteration(s) in {dt:.1f}s on {cores} threads")
     greedy = {"value": round(cfg.B * done / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+              "cpu_model": cpu_model(),
               "sample": f"{done} full drafting iterations of the same workload (draft forward + LM-head argmax "
                         f"+ accept + 16-row append, cache reset every {cfg.iters}), float64 numpy oracle, "
                         f"after an untimed context ingest",

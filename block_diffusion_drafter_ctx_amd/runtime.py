@@ -171,6 +171,17 @@ class DeviceDrafter:
         self.ws_bytes = 0
         return self
 
+    def with_cache_dtype(self, cache_dtype: str) -> "DeviceDrafter":
+        """The same device weights with H_t and the KV cache in another type
+        (its own workspace)."""
+        import copy
+        import dataclasses
+        o = copy.copy(self)
+        o.cfg = dataclasses.replace(self.cfg, cache_dtype=cache_dtype)
+        o.dims = dims_of(o.cfg)
+        o.ws, o.ws_bytes = None, 0
+        return o
+
     # ---- memory
     def cache(self, B_: int, cap: int) -> DeviceCache:
         return DeviceCache(self.cfg, B_, cap, self.device)

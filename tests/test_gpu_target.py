@@ -159,11 +159,33 @@ def test_target_verify_qwen3_8b_width():
     Target(cfg, 16).verify(_tokens(cfg, 16, 5), "verify qwen width g16")
 
 
+def greedy_continuation(tgt, anchors, n):
+    """The target's own greedy continuation of each sequence, n tokens, by
+    autoregressive decoding in the oracle (one row per verify, its K/V kept)."""
+    cfg = tgt.cfg
+    out = []
+    for b, a in enumerate(anchors):
+        c = tgt.ocache.prefix(b, tgt.ocache.lens()[b])
+        seq = [int(a)]
+        for _ in range(n):
+            r = O.target_verify(cfg, tgt.o_layers, tgt.gf, tgt.E, tgt.E, c, np.array([[seq[-1]]]), [],
+                                storage=cfg.cache_dtype)
+            for l, (kb, vb) in enumerate(r["block_kv"]):
+                c.append(l, 0, kb[0], vb[0])
+            seq.append(int(r["tokens"][0, 0]))
+        out.append(seq[1:])
+    return np.array(out, dtype=np.int32)
+
+
 def _speculative_loop(dcfg, tcfg, gamma, iters):
     """Drafter and target in a closed greedy loop on both sides: draft ->
     LM-head argmax -> target verify of (anchor, drafts) -> accept -> commit
     (the target keeps tau rows; the drafter fuses and injects the tau rows'
-    tapped states).  The drafter shares the target's embedding and LM head."""
+    tapped states).  The drafter shares the target's embedding and LM head.
+    Random weights make the drafter and the target disagree (tau = 1), so on
+    odd iterations the block carries the target's own greedy continuation
+    instead of the drafts: every draft is then accepted (greedy speculative
+    decoding is lossless) and whole blocks are committed."""
     tgt = Target(tcfg, gamma, extra_rows=iters * gamma)
     w = Workload(dcfg, gamma, iters, extra_cap=iters * gamma)
     # shared embedding / LM head: the target's
@@ -187,6 +209,8 @@ def _speculative_loop(dcfg, tcfg, gamma, iters):
         d_o, gap_o, _ = O.lm_head_argmax(hf_o, w.o_embed)
         close(h.cpu().numpy(), hf_o, dcfg.dtype, f"loop it{it} drafter h_final")
         argmax_agree(d_g.cpu().numpy(), d_o, gap_o, f"loop it{it} drafts")
+        if it % 2 == 1:
+            d_o = greedy_continuation(tgt, anchors, n)
         # the target verifies the oracle's block on both sides
         block = np.concatenate([anchors[:, None], d_o], axis=1).astype(np.int32)
         res, taps, _ = tgt.verify(block, f"loop it{it}")
@@ -198,6 +222,8 @@ def _speculative_loop(dcfg, tcfg, gamma, iters):
         torch.cuda.synchronize()
         tau_o, nxt_o = O.accept(d_o, res["tokens"])
         assert np.array_equal(tau.cpu().numpy(), tau_o) and np.array_equal(nxt.cpu().numpy(), nxt_o)
+        if it % 2 == 1:
+            assert np.all(tau_o == gamma), f"the target's own continuation must be accepted whole: {tau_o}"
         # commit: the target keeps tau rows; the drafter appends their tapped states
         tgt.commit(res, tau_o)
         rows = [slice(b * gamma, b * gamma + int(tau_o[b])) for b in range(Bn)]
@@ -240,10 +266,11 @@ def test_speculative_loop_small():
                   B=2, ctx=(40, 97), gammas=(8,), gain_std=0.1)
     taus = _speculative_loop(dcfg, tcfg, 8, 4)
     assert all(1 <= t <= 8 for row in taus for t in row)
+    assert taus[1] == [8, 8] and taus[3] == [8, 8]
 
 
 def test_speculative_loop_bf16_cache():
     tcfg = target_cfg(cid=412, B=2, ctx=(33, 64), cache_dtype="bf16")
     dcfg = shrink(QWEN3_8B_N2048, name="drafter_small_bf16", cid=413, D=512, L=2, Hq=8, Hkv=2, d=128, F=1536,
                   V=1000, B=2, ctx=(33, 64), gammas=(16,), gain_std=0.1, cache_dtype="bf16")
-    _speculative_loop(dcfg, tcfg, 16, 3)
+    _speculative_loop(dcfg, tcfg, 16, 4)
