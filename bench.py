@@ -93,8 +93,8 @@ def dominant_roofline(cfg, per_kernel, lm_bytes, lm_us, workload):
         cands.append((name, tb / n, tu / n, n, "short_rk" if name.startswith("gemm_rk_kernel<2") else None))
     name, b, us, n, key = max(cands, key=lambda c: c[2] * c[3])
     gbs = b / (us * 1e-6) / 1e9
-    return {"kernel": name + f"; {n} launch(es) per step, the largest kernel time of a step; HIP events around each "
-                             f"launch on the library stream (dflash_profile_events)",
+    return {"kernel": name + f"; {n} launch(es) per step, the largest kernel time of a step; HIP events recorded by each "
+                             f"launch's own dispatch on the library stream (dflash_profile_events)",
             "bound": "hbm", "achieved": round(gbs, 1), "peak": RF.HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / RF.HBM_PEAK_GBS, 4),
             "traffic": kernel_traffic(key, workload, cfg.cache_dtype) if key else None,
@@ -343,7 +343,7 @@ def main():
         "roofline_lm_head": {
             "kernel": "gemm_rk_kernel<8, RK_TOP2> (LM head: 151936 x 4096 bf16 streamed once against the 15 "
                       "mask rows held in registers as bf16 hi + lo, logits reduced in-kernel to a top-2 per "
-                      "workgroup), one launch per step, HIP events recorded around that launch on the library "
+                      "workgroup), one launch per step, HIP events recorded by that launch's dispatch on the library "
                       "stream by dflash_profile_events",
             "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": RF.HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(lm_gbs / RF.HBM_PEAK_GBS, 4), "traffic": kernel_traffic("lm_head", args.workload,

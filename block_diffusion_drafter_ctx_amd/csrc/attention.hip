@@ -559,7 +559,7 @@ hipError_t launch_dma(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   const hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(attn_dma_kernel<HD, NG>), static_cast<int>(lds));
   if (e != hipSuccess) return e;
   const int rows = 16 * 8 / NG;   // query rows per workgroup
-  hipLaunchKernelGGL((attn_dma_kernel<HD, NG>), dim3(p.items, (a.R + rows - 1) / rows), dim3(512), lds, st, a);
+  launch_k(attn_dma_kernel<HD, NG>, dim3(p.items, (a.R + rows - 1) / rows), dim3(512), lds, st, a);
   return hipGetLastError();
 }
 
@@ -794,11 +794,10 @@ size_t attention_part_bound(int B, int Hkv, int R, int d) {
 }
 
 hipError_t launch_attention(const AttnArgs& a0, const AttnPlan& p, bool bf16_weights, bool bf16_cache,
-                            hipStream_t st, void* stop_event) {
+                            hipStream_t st) {
   AttnArgs a = a0;
   if (!bf16_weights) {
-    hipLaunchKernelGGL(attn_f32_kernel, dim3(a.qrow0[a.B] * a.Hq), dim3(64), 0, st, a);
-    if (stop_event != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(stop_event), st);
+    launch_k(attn_f32_kernel, dim3(a.qrow0[a.B] * a.Hq), dim3(64), 0, st, a);
     return hipGetLastError();
   }
   a.split_keys = p.split_keys;
@@ -818,11 +817,10 @@ hipError_t launch_attention(const AttnArgs& a0, const AttnPlan& p, bool bf16_wei
     // LDS: two block buffers of (2 DS + DT) * 64 fragments, hi and lo planes
     const size_t lds = static_cast<size_t>(2) * (a.d / 16 + a.d / 16) * 64 * 2 * sizeof(uint4);
     auto kern = a.d == 128 ? attn_mfma_kernel<128, float> : attn_mfma_kernel<64, float>;
-    hipLaunchKernelGGL(kern, dim3(p.items, p.row_groups), dim3(64 * kAttnWaves), lds, st, a);
+    launch_k(kern, dim3(p.items, p.row_groups), dim3(64 * kAttnWaves), lds, st, a);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  if (stop_event != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(stop_event), st);
   const int pairs = a.qrow0[a.B] * a.Hq;      // (row, head) pairs to merge
   if (pairs >= kCombineWaveMin)
     hipLaunchKernelGGL(attn_combine_wave_kernel, dim3((pairs + kCombineWaves - 1) / kCombineWaves),

@@ -44,6 +44,15 @@ dflash_status ok() {
     if (!(cond)) return fail(st, __VA_ARGS__); \
   } while (0)
 
+// A launch bracketed by the profiling hook: the hook's bookkeeping ends
+// whether or not the launch failed.
+#define DF_HIP_PROF(expr, slot)         \
+  do {                                  \
+    const hipError_t ep_ = (expr);      \
+    prof_end((slot), s);                \
+    DF_HIP(ep_);                        \
+  } while (0)
+
 #define DF_HIP(expr)                                                                   \
   do {                                                                                 \
     hipError_t e_ = (expr);                                                            \
@@ -458,16 +467,35 @@ struct ProfHook {
 };
 thread_local ProfHook g_prof;
 
-// Record the hook's start event if this launch matches; returns the slot used.
+// If this launch matches the hook's role, hand its next event pair to the
+// role's kernel launch (recorded as part of that kernel's dispatch, so the
+// interval is the kernel's own run); returns the slot used.  The verify role
+// brackets two launches and records its events on the stream instead.
 int prof_begin(int role, hipStream_t s) {
   if (g_prof.role != role || g_prof.idx >= g_prof.n) return -1;
   const int i = g_prof.idx++;
-  if (hipEventRecord(static_cast<hipEvent_t>(g_prof.start[i]), s) != hipSuccess) return -1;
+  if (role == DFLASH_PROF_VERIFY) {
+    if (hipEventRecord(static_cast<hipEvent_t>(g_prof.start[i]), s) != hipSuccess) return -1;
+    return i;
+  }
+  pending_events() = PendingEvents{static_cast<hipEvent_t>(g_prof.start[i]), static_cast<hipEvent_t>(g_prof.stop[i])};
   return i;
 }
 
 void prof_end(int slot, hipStream_t s) {
-  if (slot >= 0) (void)hipEventRecord(static_cast<hipEvent_t>(g_prof.stop[slot]), s);
+  if (slot < 0) return;
+  if (g_prof.role == DFLASH_PROF_VERIFY) {
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_prof.stop[slot]), s);
+    return;
+  }
+  // a launch path that did not take the events (none should): record them
+  // back to back so the pair is still complete
+  PendingEvents& pe = pending_events();
+  if (pe.start != nullptr) {
+    (void)hipEventRecord(pe.start, s);
+    (void)hipEventRecord(pe.stop, s);
+    pe = PendingEvents{};
+  }
 }
 
 }  // namespace
@@ -585,8 +613,7 @@ dflash_status dflash_fuse_context(const dflash_dims* dims, const dflash_weights*
       const GemmPlan p = plan_gemm(M, D, K, A_BF16, false);
       S = p.S;
       const int ps = prof_begin(DFLASH_PROF_FUSE, s);
-      DF_HIP(launch_gemm_mfma(g, A_BF16, p, s));
-      prof_end(ps, s);
+      DF_HIP_PROF(launch_gemm_mfma(g, A_BF16, p, s), ps);
     } else {
       DF_HIP(launch_gemm_f32(g, s));
     }
@@ -661,8 +688,7 @@ dflash_status dflash_inject_kv(const dflash_dims* dims, const dflash_weights* w,
         g.a_lo = lo;
       }
       const int ps = prof_begin(DFLASH_PROF_INJECT, s);
-      DF_HIP(launch_gemm_mfma(g, kind, p, s));
-      prof_end(ps, s);
+      DF_HIP_PROF(launch_gemm_mfma(g, kind, p, s), ps);
     } else {
       DF_HIP(launch_gemm_f32(g, s));
     }
@@ -880,7 +906,9 @@ static dflash_status draft_forward_impl(const dflash_dims* dims, const dflash_we
     }
     at.qrow0[B] = M;
     const int pa = prof_begin(DFLASH_PROF_ATTENTION, s);
-    DF_HIP(launch_attention(at, ap, bf, cbf, s, pa >= 0 ? g_prof.stop[pa] : nullptr));
+    const hipError_t ea = launch_attention(at, ap, bf, cbf, s);
+    prof_end(pa, s);
+    DF_HIP(ea);
 
     DF_HIP(gemm(o, hd, wp(w->w_o, static_cast<int64_t>(l) * D * hd), D, &S, DFLASH_PROF_O, pl_o.hi != nullptr));
     DF_HIP(launch_residual_norm(part, S, M, D, h, wp(w->g_ffn, static_cast<int64_t>(l) * D), dims->rms_eps, a, bf, s,
@@ -1090,8 +1118,7 @@ static dflash_status lm_head_argmax(const dflash_dims* dims, const dflash_weight
     if (hp.rk) {
       // one pass over the LM head: logits reduced in-register, top-2 per workgroup
       const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-      DF_HIP(launch_gemm_rk(g, hp.rkp, top2, logits_dbg, s));
-      prof_end(ps, s);
+      DF_HIP_PROF(launch_gemm_rk(g, hp.rkp, top2, logits_dbg, s), ps);
       DF_HIP(launch_argmax_final(top2, hp.rkp.grid, Mr, draft, top2_gap, s));
     } else {
       const ActPlan& ap = hp.ap;
@@ -1100,13 +1127,11 @@ static dflash_status lm_head_argmax(const dflash_dims* dims, const dflash_weight
         // row (no logits round trip unless they are asked for)
         DF_HIP(prepare_act(g, ap, base + lay.planes, s, false));
         const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-        DF_HIP(launch_gemm_tiled_top2(g, ap.p, top2, logits_dbg, s));
-        prof_end(ps, s);
+        DF_HIP_PROF(launch_gemm_tiled_top2(g, ap.p, top2, logits_dbg, s), ps);
         DF_HIP(launch_argmax_final(top2, ap.p.ntiles, Mr, draft, top2_gap, s));
       } else {
         const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-        DF_HIP(launch_act_gemm(g, ap, base + lay.planes, s));
-        prof_end(ps, s);
+        DF_HIP_PROF(launch_act_gemm(g, ap, base + lay.planes, s), ps);
         int nt = 0;
         DF_HIP(launch_reduce_top2(g.part, ap.p.S, Mr, dims->V, logits_dbg, top2, &nt, s));
         DF_HIP(launch_argmax_final(top2, nt, Mr, draft, top2_gap, s));
@@ -1336,16 +1361,14 @@ dflash_status dflash_sample_drafts(const dflash_dims* dims, const dflash_weights
     if (rk.rk) {
       // one pass over the LM head: logits stored, sampling statistics per workgroup
       const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-      DF_HIP(launch_gemm_rk_sample(g, rk, stats, logits, s));
-      prof_end(ps, s);
+      DF_HIP_PROF(launch_gemm_rk_sample(g, rk, stats, logits, s), ps);
       DF_HIP(launch_sample_final(stats, rk.grid, Mr, draft, lse, s));
       return ok();
     }
     const ActPlan ap = plan_act(Mr, V, D, true);
     g.part = reinterpret_cast<float*>(base + lay.part);
     const int ps = prof_begin(DFLASH_PROF_LM_HEAD, s);
-    DF_HIP(launch_act_gemm(g, ap, base + lay.planes, s));
-    prof_end(ps, s);
+    DF_HIP_PROF(launch_act_gemm(g, ap, base + lay.planes, s), ps);
     r.src = g.part;
     r.S = ap.p.S;
     r.split_stride = static_cast<int64_t>(Mr) * V;
@@ -1356,8 +1379,7 @@ dflash_status dflash_sample_drafts(const dflash_dims* dims, const dflash_weights
     r.src = logits;
   }
   const int ps = prof_begin(DFLASH_PROF_ROW_STATS, s);
-  DF_HIP(launch_row_stats(r, s));
-  prof_end(ps, s);
+  DF_HIP_PROF(launch_row_stats(r, s), ps);
   DF_HIP(launch_sample_final(stats, nchunk, Mr, draft, lse, s));
   return ok();
 }
@@ -1396,8 +1418,7 @@ dflash_status dflash_sample_accept(const dflash_dims* dims, int32_t B, int32_t g
   r.inv_t = inv_t;
   r.stats = reinterpret_cast<float4*>(base + lay.stats);
   int ps = prof_begin(DFLASH_PROF_ROW_STATS, s);
-  DF_HIP(launch_row_stats(r, s));
-  prof_end(ps, s);
+  DF_HIP_PROF(launch_row_stats(r, s), ps);
   SpecArgs a{};
   a.draft = draft;
   a.zq = draft_logits;
@@ -1419,8 +1440,7 @@ dflash_status dflash_sample_accept(const dflash_dims* dims, int32_t B, int32_t g
   a.tau = tau;
   a.next_anchor = next_anchor;
   ps = prof_begin(DFLASH_PROF_VERIFY, s);
-  DF_HIP(launch_spec_verify(a, s));
-  prof_end(ps, s);
+  DF_HIP_PROF(launch_spec_verify(a, s), ps);
   return ok();
 }
 

@@ -499,6 +499,10 @@ constexpr int kTileN = 128, kTileM = 128, kTileK = 64;
 // would not leave room for two LDS stages)
 struct TileShape { int tn, tm, wn, wm, ns; };
 constexpr TileShape kTileBf16{256, 256, 64, 128, 2}, kTileHiLo{256, 128, 64, 64, 2};
+// hi / lo planes of at most 64 activation rows: a 64-row tile (eight waves of
+// 64 x 32) does half the MFMA work of the 128-row one and fills 96 KB of LDS
+// per pair of stages instead of 128 KB
+constexpr TileShape kTileHiLo64{256, 64, 64, 32, 2}, kTileHiLo32{256, 32, 64, 16, 2};
 
 template <int AK>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
@@ -950,7 +954,7 @@ hipError_t launch_v(const GemmArgs& a, const GemmPlan& p, hipStream_t st) {
   auto kern = gemm_stream_kernel<MT, AK, WAVES, KR>;
   const hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(kern), static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * WAVES), lds, st, a);
+  launch_k(kern, dim3(p.grid), dim3(64 * WAVES), lds, st, a);
   return hipGetLastError();
 }
 
@@ -979,6 +983,11 @@ int device_cus() {
 }
 
 }  // namespace
+
+PendingEvents& pending_events() {
+  thread_local PendingEvents pe;
+  return pe;
+}
 
 namespace {
 std::mutex g_attr_mu;
@@ -1078,8 +1087,13 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
   GemmPlan p;
   p.tiled = true;
   // register-staged kernel (fp32 A) or LDS-direct kernel
-  const int tn = ak == A_F32_SPLIT ? kTileN : ak == A_BF16 ? kTileBf16.tn : kTileHiLo.tn;
-  const int tm = ak == A_F32_SPLIT ? kTileM : ak == A_BF16 ? kTileBf16.tm : kTileHiLo.tm;
+  // hi / lo planes: the smallest of the 32-, 64- and 128-row tiles that holds M
+  // (DFLASH_TILE64=2: always 128 rows, for measurement)
+  const bool small_tiles = ak == A_BF16_HILO && env_int("DFLASH_TILE64", 1) == 1;
+  const TileShape hl = !small_tiles ? kTileHiLo : M <= kTileHiLo32.tm ? kTileHiLo32
+                                                : M <= kTileHiLo64.tm ? kTileHiLo64 : kTileHiLo;
+  const int tn = ak == A_F32_SPLIT ? kTileN : ak == A_BF16 ? kTileBf16.tn : hl.tn;
+  const int tm = ak == A_F32_SPLIT ? kTileM : ak == A_BF16 ? kTileBf16.tm : hl.tm;
   p.MT = tm;
   p.mtiles = (M + tm - 1) / tm;
   p.ntiles = (N + tn - 1) / tn;
@@ -1132,19 +1146,23 @@ hipError_t launch_tile_lds(GemmArgs a, dim3 grid, hipStream_t st, float* top2 = 
   const hipError_t e = ensure_dyn_lds(
       reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2>), static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2>), grid, dim3((TN / WN) * (TM / WM) * 64), lds,
+  launch_k(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2>, grid, dim3((TN / WN) * (TM / WM) * 64), lds,
                      st, a, top2);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_tiled_top2(const GemmArgs& a0, const GemmPlan& p, float* top2, float* logits, hipStream_t st) {
-  constexpr TileShape T = kTileHiLo;
-  if (!p.tiled || p.S != 1 || p.MT != T.tm || top2 == nullptr || a0.a_cols % kTileK != 0 || a0.a_lo == nullptr)
+  constexpr TileShape T = kTileHiLo, T64 = kTileHiLo64, T32 = kTileHiLo32;
+  if (!p.tiled || p.S != 1 || (p.MT != T.tm && p.MT != T64.tm && p.MT != T32.tm) || top2 == nullptr ||
+      a0.a_cols % kTileK != 0 || a0.a_lo == nullptr)
     return hipErrorInvalidValue;
   GemmArgs a = a0;
   a.chunks_per_split = p.cps;
   a.part = logits;
-  return launch_tile_lds<2, T.ns, T.tn, T.tm, T.wn, T.wm, true>(a, dim3(p.ntiles, p.mtiles, 1), st, top2);
+  const dim3 grid(p.ntiles, p.mtiles, 1);
+  if (p.MT == T32.tm) return launch_tile_lds<2, T32.ns, T32.tn, T32.tm, T32.wn, T32.wm, true>(a, grid, st, top2);
+  if (p.MT == T64.tm) return launch_tile_lds<2, T64.ns, T64.tn, T64.tm, T64.wn, T64.wm, true>(a, grid, st, top2);
+  return launch_tile_lds<2, T.ns, T.tn, T.tm, T.wn, T.wm, true>(a, grid, st, top2);
 }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p, hipStream_t st) {
@@ -1159,7 +1177,9 @@ hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p,
       if (p.MT != T.tm) return hipErrorInvalidValue;
       return launch_tile_lds<1, T.ns, T.tn, T.tm, T.wn, T.wm>(a, grid, st);
     }
-    constexpr TileShape T = kTileHiLo;
+    constexpr TileShape T = kTileHiLo, T64 = kTileHiLo64, T32 = kTileHiLo32;
+    if (p.MT == T32.tm) return launch_tile_lds<2, T32.ns, T32.tn, T32.tm, T32.wn, T32.wm>(a, grid, st);
+    if (p.MT == T64.tm) return launch_tile_lds<2, T64.ns, T64.tn, T64.tm, T64.wn, T64.wm>(a, grid, st);
     if (p.MT != T.tm) return hipErrorInvalidValue;
     return launch_tile_lds<2, T.ns, T.tn, T.tm, T.wn, T.wm>(a, grid, st);
   }
@@ -1172,12 +1192,12 @@ hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p,
     if (ak == A_BF16) {
       const hipError_t e = ensure_dyn_lds(reinterpret_cast<const void*>(gemm_tile_kernel<A_BF16>), static_cast<int>(lds));
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(gemm_tile_kernel<A_BF16>, grid, dim3(256), lds, st, a);
+      launch_k(gemm_tile_kernel<A_BF16>, grid, dim3(256), lds, st, a);
     } else {
       const hipError_t e =
           ensure_dyn_lds(reinterpret_cast<const void*>(gemm_tile_kernel<A_F32_SPLIT>), static_cast<int>(lds));
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(gemm_tile_kernel<A_F32_SPLIT>, grid, dim3(256), lds, st, a);
+      launch_k(gemm_tile_kernel<A_F32_SPLIT>, grid, dim3(256), lds, st, a);
     }
     return hipGetLastError();
   }
@@ -1321,7 +1341,7 @@ hipError_t rk_launch(GemmArgs a, const GemmPlan& p, float* top2, float* logits, 
     a.stage_tiles = slots;
     shm = static_cast<size_t>(slots) * tile_bytes;
   }
-  hipLaunchKernelGGL((gemm_rk_kernel<KS, EP, T, AK>), dim3(p.grid * p.mr), dim3(64 * kRkWaves), shm, st, a, top2,
+  launch_k(gemm_rk_kernel<KS, EP, T, AK>, dim3(p.grid * p.mr), dim3(64 * kRkWaves), shm, st, a, top2,
                      logits);
   return hipGetLastError();
 }
@@ -1402,7 +1422,7 @@ hipError_t launch_split_hilo(const float* x, int64_t ld, int M, int K, uint16_t*
 
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t st) {
   dim3 grid((a.N + kF32Tile - 1) / kF32Tile, (a.M + kF32Tile - 1) / kF32Tile);
-  hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, st, a);
+  launch_k(gemm_f32_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // argument structs are passed to the kernels by value.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -11,6 +12,30 @@ namespace dflash {
 
 constexpr int kMaxSrc = 8;
 constexpr int kMaxSeq = 64;
+
+// ------------------------------------------------------- profiling events
+// A start / stop event pair that the next launch made through launch_k records
+// as part of its own dispatch (hipExtLaunchKernelGGL): the timestamps bracket
+// the kernel itself and add no packets to the stream.  The library's profiling
+// hook sets it right before the launch of a bracketed role; the launch
+// consumes it.  Per thread.
+struct PendingEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+PendingEvents& pending_events();
+
+template <typename K, typename... Args>
+inline void launch_k(K kernel, dim3 grid, dim3 block, size_t shm, hipStream_t st, Args... args) {
+  PendingEvents& pe = pending_events();
+  if (pe.start != nullptr) {
+    const PendingEvents e = pe;
+    pe = PendingEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(shm), st, e.start, e.stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shm, st, args...);
+  }
+}
 
 // ------------------------------------------------------- launch attributes
 // Raise kernel fn's dynamic-LDS limit to at least `bytes` on the current
@@ -288,9 +313,9 @@ struct AttnPlan {
 // from its context (one more key item per (b, kv head))
 AttnPlan plan_attention(int B, const int32_t* nkeys, int Hkv, int R, int d, const int32_t* apart = nullptr);
 size_t attention_part_bound(int B, int Hkv, int R, int d);
-// stop_event (nullable hipEvent_t) is recorded right after the main attention
-// kernel, before its combine step (profiling hook).
+// The main attention kernel is launched through launch_k (pending profiling
+// events bracket it, not its combine step).
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, bool bf16_weights, bool bf16_cache,
-                            hipStream_t st, void* stop_event = nullptr);
+                            hipStream_t st);
 
 }  // namespace dflash

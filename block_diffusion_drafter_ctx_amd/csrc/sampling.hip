@@ -315,7 +315,7 @@ hipError_t launch_row_stats(const RowStatArgs& a0, hipStream_t st) {
   if (a.rows <= 0) return hipSuccess;
   if (a.chunk <= 0 || a.chunk % kStatVec != 0) return hipErrorInvalidValue;
   const int nchunk = (a.N + a.chunk - 1) / a.chunk;
-  hipLaunchKernelGGL(row_stats_kernel, dim3(nchunk, a.rows), dim3(kStatThreads), 0, st, a);
+  launch_k(row_stats_kernel, dim3(nchunk, a.rows), dim3(kStatThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -405,9 +405,12 @@ typedef enum {
 } dflash_prof_role;
 
 /* Profiling hook (measurement only; not needed to run the path).  From now on,
- * on the calling thread, the i-th kernel launch of `role` records start[i]
- * (a hipEvent_t) on its stream right before the launch and stop[i] right after
- * it, for i < n; later launches of the role record nothing.  The caller owns the
+ * on the calling thread, the i-th kernel launch of `role` records start[i] and
+ * stop[i] (hipEvent_t, created with timing enabled) as part of its own dispatch
+ * (hipExtLaunchKernelGGL), so that the interval is that kernel's run, for
+ * i < n; later launches of the role record nothing.  DFLASH_PROF_VERIFY
+ * brackets its two launches with events recorded on the stream before the
+ * first and after the second.  The caller owns the
  * events and must keep the arrays alive until it calls this again.  role ==
  * DFLASH_PROF_NONE (or n == 0) turns the hook off.  Returns the number of
  * launches recorded since the previous call in *recorded (nullable).
