@@ -128,6 +128,8 @@ def main():
                     help="skip the speculative-decoding leg with a 36-layer synthetic target")
     ap.add_argument("--no-loops", action="store_true",
                     help="skip the drafting loops of the tiny, long-context, 16-sequence and 8-layer workloads")
+    ap.add_argument("--loops", default="tiny_f32,long_ctx_n32768,batch16_ragged,deep8_b4_n8192",
+                    help="comma-separated workloads whose drafting loops to run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs the drafting "
@@ -371,7 +373,7 @@ def main():
     if not args.no_loops:
         # the other workloads' drafting loops (blocks/s over 8 iterations with appends)
         out["loops"] = {}
-        for wl in ("tiny_f32", "long_ctx_n32768", "batch16_ragged", "deep8_b4_n8192"):
+        for wl in args.loops.split(","):
             out["loops"][wl] = workload_loop_leg(wl, args.cache)
     if not args.no_speculative:
         out["speculative"] = speculative_leg(args.cache)
@@ -398,7 +400,7 @@ def main():
             out["blocks"]["cpu_baseline"] = blocks_cpu
         if long_cpu is not None:
             out["long_context"]["cpu_baseline"] = long_cpu
-        if "loops" in out:
+        if "tiny_f32" in out.get("loops", {}):
             out["loops"]["tiny_f32"]["cpu_baseline"] = cpu_tiny_baseline()
     print(json.dumps(out), flush=True)
 
@@ -957,9 +959,7 @@ def speculative_leg(cache_dtype, steps=24, seed=20261220):
     drf.ensure_workspace(1, g, N)
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed + 2)
-    cdt = tcache.k.dtype
-    tcache.k[:, 0, :, :N].copy_(torch.randn(tcfg.L, tcfg.Hkv, N, tcfg.d, generator=gen, device=dev).to(cdt))
-    tcache.v[:, 0, :, :, :N].copy_(torch.randn(tcfg.L, tcfg.Hkv, tcfg.d, N, generator=gen, device=dev).to(cdt))
+    tcache.fill_random(0, N, gen)
     tcache.set_lens([N])
     st = [torch.randn(N, dcfg.D, generator=gen, device=dev).to(torch.bfloat16) for _ in range(dcfg.n_tgt)]
     H = drf.context_buffer(N)

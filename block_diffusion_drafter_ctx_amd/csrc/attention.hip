@@ -378,8 +378,8 @@ __global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
       const int kt = f / DS, ds = f % DS;
       const int key = 8 * ((lane & 15) >> 2) + 4 * kt + (lane & 3);
       off[i] = 2u * static_cast<uint32_t>(key * HD + ds * 32 + 8 * g4);
-    } else {
-      off[i] = 2u * static_cast<uint32_t>(((f - KFR) * 16 + (lane & 15)) * a.cap + 8 * g4);
+    } else {                                    // V^T block [d][32]: dimension row, 8 keys
+      off[i] = 2u * static_cast<uint32_t>(((f - KFR) * 16 + (lane & 15)) * 32 + 8 * g4);
     }
   }
   // step u loads blocks NG u .. NG u + NG - 1 into stage st; past the last
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
     for (int i = 0; i < LPW; ++i) {
       const int F = wave + NW * i, f = F % NFR;
       const int k0 = kbeg + min(NG * u + F / NFR, nblk - 1) * 32;
-      const uint16_t* base = f < KFR ? kbase + static_cast<int64_t>(k0) * HD : vbase + k0;
+      const uint16_t* base = f < KFR ? kbase + static_cast<int64_t>(k0) * HD : vbase + static_cast<int64_t>(k0) * HD;
       load_to_lds_sbase(off[i], base, lds0 + static_cast<unsigned>((st * NG * NFR + F) * 1024));
     }
   };
@@ -810,6 +810,12 @@ hipError_t launch_attention(const AttnArgs& a0, const AttnPlan& p, bool bf16_wei
     // the DMA kernel's per-lane byte offsets into one head's K or V are 32-bit
     // (the entry points reject such caches before any launch)
     if (static_cast<int64_t>(a.cap) * a.d * 2 >= (int64_t{1} << 32)) return hipErrorInvalidValue;
+    // V is read in whole blocks of 32 keys ([cap / 32][d][32] per head): every
+    // key range starts on a block (context ranges at multiples of split_keys,
+    // an anchored block's own rows in a 32-aligned slot)
+    if (a.split_keys % 32 != 0 || a.cap % 32 != 0) return hipErrorInvalidValue;
+    for (int b = 0; b < a.B; ++b)
+      if (a.blk0[b] >= 0 && a.blk0[b] % 32 != 0) return hipErrorInvalidValue;
     const bool two = a.R <= 64;
     e = a.d == 128 ? (two ? launch_dma<128, 2>(a, p, st) : launch_dma<128, 1>(a, p, st))
                    : (two ? launch_dma<64, 2>(a, p, st) : launch_dma<64, 1>(a, p, st));

@@ -141,11 +141,17 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(ScatterArgs a) {
     st4<T>(a.kc, ((head0 + j) * a.cap + pos) * a.d + c, v);
   } else {
     const int j = (rem - hd) / a.d, c = (rem - hd) % a.d;
-    T* vp = static_cast<T*>(a.vc) + ((head0 + j) * a.d + c) * a.cap + pos;
+    // fp32 cache: V^T [d][cap] per head; bf16 cache: V^T per block of 32 keys
+    // ([cap / 32][d][32] per head), so dimension c + e of key pos sits e * 32 on
+    const bool blocked = sizeof(T) == 2;
+    T* vp = blocked ? static_cast<T*>(a.vc) + (head0 + j) * a.cap * a.d + static_cast<int64_t>(pos / 32) * (a.d * 32) +
+                          c * 32 + pos % 32
+                    : static_cast<T*>(a.vc) + ((head0 + j) * a.d + c) * a.cap + pos;
+    const int64_t vs = blocked ? 32 : a.cap;
     Store<T>::st(vp, v.x);
-    Store<T>::st(vp + a.cap, v.y);
-    Store<T>::st(vp + 2 * a.cap, v.z);
-    Store<T>::st(vp + 3 * a.cap, v.w);
+    Store<T>::st(vp + vs, v.y);
+    Store<T>::st(vp + 2 * vs, v.z);
+    Store<T>::st(vp + 3 * vs, v.w);
   }
 }
 

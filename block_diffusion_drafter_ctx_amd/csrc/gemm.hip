@@ -42,6 +42,35 @@ __device__ __forceinline__ const T* pick_src(const GemmArgs& g, int s) {
   return static_cast<const T*>(p);
 }
 
+// Kernel arguments are read from memory by scalar loads.  Left alone, the
+// compiler issues each batch where it is first needed, behind branches (and
+// gridDim.x, an implicit argument, with them), and each dependent round is a
+// memory latency before the first weight load goes out.  Naming every field a
+// kernel uses in one empty asm statement before its first branch makes them
+// arrive in one round.
+__device__ __forceinline__ void fetch_args(const GemmArgs& g) {
+  asm volatile("" ::"s"(g.a_src[0]), "s"(g.a_src[1]), "s"(g.a_src[2]), "s"(g.a_src[3]), "s"(g.a_src[4]),
+               "s"(g.a_src[5]), "s"(g.a_src[6]), "s"(g.a_src[7]), "s"(g.a_cols), "s"(g.a_rg), "s"(g.a_ld),
+               "s"(g.a_gs), "s"(g.w), "s"(g.w_ld), "s"(g.w_gs), "s"(g.w_off), "s"(g.w_rg), "s"(g.M), "s"(g.N),
+               "s"(g.K), "s"(g.S), "s"(g.ntiles), "s"(g.part), "s"(g.stage_tiles), "s"(g.rchunks), "s"(gridDim.x));
+}
+
+// A source pointer chosen by a wave-uniform index.  A select among plain
+// argument loads is turned back into one load at a computed offset (a
+// dependent memory round trip); selecting among byte offsets from the first
+// source keeps the values in registers and the pointer in the global space.
+template <typename T>
+__device__ __forceinline__ const T* pick_src_reg(const GemmArgs& g, int s) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(g.a_src[0]);
+  uintptr_t off = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxSrc; ++k) {
+    const uintptr_t d = reinterpret_cast<uintptr_t>(g.a_src[k]) - b;
+    off = s == k ? d : off;
+  }
+  return reinterpret_cast<const T*>(static_cast<const char*>(g.a_src[0]) + off);
+}
+
 __device__ __forceinline__ int64_t a_row_off(const GemmArgs& g, int r) {
   return static_cast<int64_t>(r / g.a_rg) * g.a_gs + static_cast<int64_t>(r % g.a_rg) * g.a_ld;
 }
@@ -241,8 +270,18 @@ constexpr int kRkMinN = 16384;   // weight rows below which the split-K streamin
 
 enum RkEpilogue { RK_PART = 0, RK_TOP2 = 1, RK_SWIGLU = 2, RK_SAMPLE = 3 };
 
+// Source of k index k (uniform): sources are a_cols wide, at most kMaxSrc of
+// them; compares instead of a division.
+__device__ __forceinline__ int src_of(int k, int a_cols) {
+  int s = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxSrc; ++j) s += k >= j * a_cols ? 1 : 0;
+  return s;
+}
+
 template <int KS, int EP, int T, int AK = A_F32_SPLIT>
 __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, float* top2, float* logits) {
+  fetch_args(g);
   constexpr bool TOP2 = EP == RK_TOP2;
   constexpr bool SAMPLE = EP == RK_SAMPLE;
   constexpr int TN = EP == RK_SWIGLU ? 8 : 16;   // outputs per tile
@@ -300,11 +339,14 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
 
   constexpr bool SPLIT = AK == A_F32_SPLIT;    // fp32 activations as bf16 hi + lo; else exact bf16
   uint4 bh[KS], bl[SPLIT ? KS : 1];
+  const int a_m = m0 + (lane & 15) < g.M ? m0 + (lane & 15) : 0;
+  // no division unless the activation rows are grouped
+  const int64_t a_off = g.a_rg >= g.M ? static_cast<int64_t>(a_m) * g.a_ld : a_row_off(g, a_m);
   if constexpr (!SPLIT) {
-    const int s = __builtin_amdgcn_readfirstlane(kwave / g.a_cols);
+    const int s = src_of(kwave, g.a_cols);
     const int m = m0 + (lane & 15);
     const bool ok = m < g.M;
-    const uint16_t* p = pick_src<uint16_t>(g, s) + a_row_off(g, ok ? m : 0) + (kl - s * g.a_cols);
+    const uint16_t* p = pick_src_reg<uint16_t>(g, s) + a_off + (kl - s * g.a_cols);
 #pragma unroll
     for (int x = 0; x < KS; ++x) {
       const uint4 v = *reinterpret_cast<const uint4*>(p + x * 32);
@@ -312,10 +354,10 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
     }
   } else {
     // the host guarantees a_cols % (32 * KS) == 0: a wave's k range lies in one source
-    const int s = __builtin_amdgcn_readfirstlane(kwave / g.a_cols);
+    const int s = src_of(kwave, g.a_cols);
     const int m = m0 + (lane & 15);
     const bool ok = m < g.M;
-    const float* p = pick_src<float>(g, s) + a_row_off(g, ok ? m : 0) + (kl - s * g.a_cols);
+    const float* p = pick_src_reg<float>(g, s) + a_off + (kl - s * g.a_cols);
     float4 av[2 * KS];
 #pragma unroll
     for (int x = 0; x < KS; ++x) {

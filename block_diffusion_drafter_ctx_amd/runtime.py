@@ -53,13 +53,20 @@ def upload(arr: np.ndarray, cfg, device="cuda") -> torch.Tensor:
 
 
 class DeviceCache:
-    """KV cache [L][B][Hkv][cap][d] (keys) and [L][B][Hkv][d][cap] (values), the
-    host lengths the library plans from, and their device mirror."""
+    """KV cache: keys [L][B][Hkv][cap][d]; values transposed, [L][B][Hkv][d][cap]
+    in an fp32 cache and per block of 32 keys, [L][B][Hkv][cap/32][d][32], in a
+    bf16 cache; the host lengths the library plans from, and their device
+    mirror."""
 
     def __init__(self, cfg, B_: int, cap: int, device="cuda"):
         dt = cache_torch_dtype(cfg)
+        self.blocked = cfg.cache_dtype == "bf16"
+        self.L, self.Hkv, self.d = cfg.L, cfg.Hkv, cfg.d
         self.k = torch.zeros(cfg.L, B_, cfg.Hkv, cap, cfg.d, dtype=dt, device=device)
-        self.v = torch.zeros(cfg.L, B_, cfg.Hkv, cfg.d, cap, dtype=dt, device=device)
+        if self.blocked:
+            self.v = torch.zeros(cfg.L, B_, cfg.Hkv, cap // 32, cfg.d, 32, dtype=dt, device=device)
+        else:
+            self.v = torch.zeros(cfg.L, B_, cfg.Hkv, cfg.d, cap, dtype=dt, device=device)
         self.len_dev = torch.zeros(B_, dtype=torch.int32, device=device)
         self.lens = (ctypes.c_int32 * B_)()
         self.B, self.cap = B_, cap
@@ -75,12 +82,33 @@ class DeviceCache:
             self.lens[b] = int(n)
         self.len_dev.copy_(torch.tensor(self.len_list(), dtype=torch.int32))
 
-    # ---- reading rows back (tests and measurements; the layout lives here only)
+    # ---- the layout lives here only (tests and measurements)
+    def _vt(self, b: int, lo: int, hi: int) -> torch.Tensor:
+        """Values of rows [lo, hi) of sequence b as V^T [L][Hkv][d][hi - lo] (a
+        view for an fp32 cache, a copy of the covering blocks for a bf16 one)."""
+        if not self.blocked:
+            return self.v[:, b, :, :, lo:hi]
+        b0, b1 = lo // 32, (hi + 31) // 32
+        blk = self.v[:, b, :, b0:b1]                       # [L][Hkv][nb][d][32]
+        vt = blk.permute(0, 1, 3, 2, 4).reshape(self.L, self.Hkv, self.d, (b1 - b0) * 32)
+        return vt[..., lo - 32 * b0:hi - 32 * b0]
+
+    def _put_vt(self, b: int, lo: int, vt: torch.Tensor):
+        """Write V^T [L][Hkv][d][n] into rows [lo, lo + n) of sequence b."""
+        n = vt.shape[-1]
+        if not self.blocked:
+            self.v[:, b, :, :, lo:lo + n] = vt
+            return
+        b0, b1 = lo // 32, (lo + n + 31) // 32
+        full = self._vt(b, 32 * b0, 32 * b1).clone()
+        full[..., lo - 32 * b0:lo - 32 * b0 + n] = vt
+        self.v[:, b, :, b0:b1] = full.reshape(self.L, self.Hkv, self.d, b1 - b0, 32).permute(0, 1, 3, 2, 4)
+
     def rows(self, b: int, lo: int, hi: int):
         """Rows [lo, hi) of sequence b in every layer: (K, V) float64 numpy
         arrays [L][hi - lo][Hkv][d]."""
         k = self.k[:, b, :, lo:hi].float().cpu().numpy().transpose(0, 2, 1, 3)
-        v = self.v[:, b, :, :, lo:hi].float().cpu().numpy().transpose(0, 3, 1, 2)
+        v = self._vt(b, lo, hi).float().cpu().numpy().transpose(0, 3, 1, 2)
         return k.astype(np.float64), v.astype(np.float64)
 
     def put_rows(self, b: int, lo: int, k: np.ndarray, v: np.ndarray):
@@ -91,15 +119,21 @@ class DeviceCache:
         kt = torch.from_numpy(np.ascontiguousarray(k.transpose(0, 2, 1, 3), dtype=np.float32))
         vt = torch.from_numpy(np.ascontiguousarray(v.transpose(0, 2, 3, 1), dtype=np.float32))
         self.k[:, b, :, lo:lo + n] = kt.to(self.k.device, self.k.dtype)
-        self.v[:, b, :, :, lo:lo + n] = vt.to(self.v.device, self.v.dtype)
+        self._put_vt(b, lo, vt.to(self.v.device, self.v.dtype))
+
+    def fill_random(self, b: int, n: int, gen: torch.Generator):
+        """Rows [0, n) of sequence b in every layer from N(0, 1) draws."""
+        dev, dt = self.k.device, self.k.dtype
+        self.k[:, b, :, :n].copy_(torch.randn(self.L, self.Hkv, n, self.d, generator=gen, device=dev).to(dt))
+        self._put_vt(b, 0, torch.randn(self.L, self.Hkv, self.d, n, generator=gen, device=dev).to(dt))
 
     def snapshot(self, b: int, n: int):
         """A device copy of rows [0, n) of sequence b in every layer."""
-        return self.k[:, b, :, :n].clone(), self.v[:, b, :, :, :n].clone()
+        return self.k[:, b, :, :n].clone(), self._vt(b, 0, n).clone()
 
     def same_rows(self, snap, b: int, n: int) -> bool:
         """Rows [0, n) of sequence b are bit-identical to ``snap``."""
-        return torch.equal(self.k[:, b, :, :n], snap[0]) and torch.equal(self.v[:, b, :, :, :n], snap[1])
+        return torch.equal(self.k[:, b, :, :n], snap[0]) and torch.equal(self._vt(b, 0, n), snap[1])
 
 
 class DeviceDrafter:

@@ -115,8 +115,11 @@ typedef struct {
 /* The drafter's KV cache: injected context rows plus gamma scratch rows per
  * sequence ([JP] "추론 구조", [GL] "KV 주입": injected K/V are cached and reused
  * across drafting iterations).  Layouts, in the cache type:
- *   k: [L][B][Hkv][cap][d]   row-major keys
- *   v: [L][B][Hkv][d][cap]   values stored transposed (key index fastest)
+ *   k: [L][B][Hkv][cap][d]          row-major keys
+ *   v, fp32 cache: [L][B][Hkv][d][cap]           values transposed (key fastest)
+ *   v, bf16 cache: [L][B][Hkv][cap/32][d][32]    values transposed per block of
+ *                  32 keys, each block contiguous (8 KB at d = 128), so the
+ *                  attention streams whole lines
  * len[b] (HOST array, caller-owned) is the number of valid context rows of
  * sequence b.  Rows [0, len[b]) are never written by draft_forward; inject_kv
  * writes rows [len[b], len[b]+T_b) and then adds T_b to len[b].  The host

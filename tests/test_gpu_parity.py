@@ -230,7 +230,7 @@ def test_bf16_storage_rounding_is_rne():
     Ht = torch.from_numpy(H).cuda().to(torch.bfloat16)
     wq = torch.from_numpy(w).cuda().to(torch.bfloat16)
     kc = torch.zeros(L, 1, Hkv, 32, d, dtype=torch.bfloat16, device="cuda")
-    vc = torch.zeros(L, 1, Hkv, d, 32, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(L, 1, Hkv, 1, d, 32, dtype=torch.bfloat16, device="cuda")   # bf16 V: [cap/32][d][32]
     lens = (ctypes.c_int32 * 1)(0)
     cache = B.KVCache(k=kc.data_ptr(), v=vc.data_ptr(), B=1, cap=32, len=ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
     wts = B.Weights(w_qkv=wq.data_ptr())
@@ -242,7 +242,7 @@ def test_bf16_storage_rounding_is_rne():
     exact_k = H.astype(np.float64) @ w[Hq * d:(Hq + Hkv) * d].astype(np.float64).T     # [4, d]
     exact_v = H.astype(np.float64) @ w[(Hq + Hkv) * d:].astype(np.float64).T
     got_k = kc[0, 0, 0, :4].float().cpu().numpy()
-    got_v = vc[0, 0, 0, :, :4].float().cpu().numpy().T
+    got_v = vc[0, 0, 0, 0, :, :4].float().cpu().numpy().T
     assert np.array_equal(got_k, O.to_bf16(exact_k)), (got_k[0, :8], O.to_bf16(exact_k)[0, :8])
     assert np.array_equal(got_v, O.to_bf16(exact_v))
     # the test really exercises ties: some exact values are not bf16 numbers
