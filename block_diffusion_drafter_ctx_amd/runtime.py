@@ -77,10 +77,14 @@ class DeviceCache:
     def len_list(self):
         return [int(self.lens[b]) for b in range(self.B)]
 
-    def set_lens(self, lens):
+    def set_lens(self, lens, mirror: bool = True):
+        """Set the host lengths (what the library plans from) and, unless
+        ``mirror`` is False, copy them to the device mirror (a host-to-device
+        copy on the stream; an inject call rewrites the mirror itself)."""
         for b, n in enumerate(lens):
             self.lens[b] = int(n)
-        self.len_dev.copy_(torch.tensor(self.len_list(), dtype=torch.int32))
+        if mirror:
+            self.len_dev.copy_(torch.tensor(self.len_list(), dtype=torch.int32))
 
     # ---- the layout lives here only (tests and measurements)
     def _vt(self, b: int, lo: int, hi: int) -> torch.Tensor:
