@@ -16,8 +16,9 @@
 //   * online softmax per row with exp2; the MFMA output layout of S^T (4 keys of
 //     one row per lane) is the B-operand layout P^T of the value MFMA, so
 //     probabilities never leave registers;
-//   * O^T = V^T P^T reads values from the transposed V cache ([d][cap], keys
-//     contiguous), P again split hi + lo;
+//   * O^T = V^T P^T reads values from the transposed V cache (keys contiguous:
+//     [d][cap] per head in an fp32 cache, [cap/32][d][32] in a bf16 one), P
+//     again split hi + lo;
 //   * each workgroup writes (max, sum, O) per row; a combine kernel merges the
 //     key ranges in a fixed order (log-sum-exp), so results are deterministic.
 // A bf16 cache streams K/V blocks straight into LDS (attn_dma_kernel); an fp32
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
 // row i -> key 8 (i / 4) + 4 kt + i % 4, so the S^T output leaves lane l (lane
 // group g = l / 16) holding keys 8 g + 4 kt + r of its query column; as the B
 // operand of the value MFMA, k-slot 8 g + e is then key 8 g + e, and the value
-// fragment of lane l is 8 consecutive keys of one row of the transposed V cache
+// fragment of lane l is 8 consecutive keys of one row of the block's V^T
 // (one 16-byte load, like a K fragment).  With G * gamma <= 64 query rows the
 // eight waves form two groups of four that take alternate blocks, each with its
 // own online-softmax state, merged through LDS at the end (two waves per SIMD

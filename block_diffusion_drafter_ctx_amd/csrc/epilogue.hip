@@ -2,7 +2,8 @@
 // row-wise kernels of the drafter path:
 //   ctx_norm       fusion epilogue: sum partials, RMSNorm with g_c, store H_t
 //   scatter_kv     sum partials; query columns -> fp32 Q; key / value columns ->
-//                  the KV cache (keys row-major, values transposed)
+//                  the KV cache (keys row-major, values transposed; per block of
+//                  32 keys in a bf16 cache)
 //   residual_norm  h += sum partials; a = RMSNorm(h; g)
 //   swiglu         s = SiLU(gate) * up
 //   embed_norm     h = embedding rows (or override rows); a = RMSNorm(h; g)

@@ -159,7 +159,7 @@ struct ScatterArgs {
   int32_t nq;          // columns [0, nq) are query columns -> q_out[m][n]
   float* q_out;
   void* kc;            // cache K base of layer `layer0`: [L][B][Hkv][cap][d]
-  void* vc;            // cache V base: [L][B][Hkv][d][cap]
+  void* vc;            // cache V base: [L][B][Hkv][d][cap] (fp32), [L][B][Hkv][cap/32][d][32] (bf16)
   int32_t layer0, B, Hkv, d, cap;
   SeqRows rows;
   int32_t* len_dev;               // nullable: the cache's device length mirror ...
@@ -275,7 +275,7 @@ hipError_t launch_spec_verify(const SpecArgs& a, hipStream_t st);
 struct AttnArgs {
   const float* q;        // [M][Hq*d], M = qrow0[B] block rows (sequence b's at qrow0[b] ..)
   const void* kc;        // layer base [B][Hkv][cap][d]
-  const void* vc;        // layer base [B][Hkv][d][cap]
+  const void* vc;        // layer base [B][Hkv][d][cap] (fp32), [B][Hkv][cap/32][d][32] (bf16)
   float* part_o;         // [items][Rpad][d]
   float* part_ml;        // [items][Rpad][2]
   float* o_out;          // [B*gamma][Hq*d]
