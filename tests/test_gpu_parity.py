@@ -274,16 +274,18 @@ def test_batch16_ragged():
 def test_batch16_ragged_bf16_cache():
     # the bench's batch16 loop runs on a bf16 cache: 16 sequences' block-major
     # V rows, key ranges planned across all of them
+    # (distinct block rows: with mask rows, 15 identical rows of a block round
+    # together, so one near-tie flips 15 elements of the block K/V at once)
     cfg = shrink(BATCH16_RAGGED, cid=304, cache_dtype="bf16")
-    log(f"batch16_ragged full size, bf16 H_t / KV cache {list(cfg.ctx)}, 4 iterations, each appending 16 rows")
-    Workload(cfg, 16, 4).run()
+    log(f"batch16_ragged full size, bf16 H_t / KV cache {list(cfg.ctx)}, distinct block rows, 4 iterations + appends")
+    Workload(cfg, 16, 4, override=True).run()
 
 
 @pytest.mark.timeout(1200)
 def test_deep8_b4_n8192_bf16_cache_gamma_sweep():
     cfg = shrink(DEEP8_B4_N8192, cid=305, cache_dtype="bf16")
-    log("deep8_b4_n8192 full size, bf16 H_t / KV cache: gamma 8 / 16 / 32 on one cache")
-    w = Workload(cfg, max(cfg.gammas), 1)
+    log("deep8_b4_n8192 full size, bf16 H_t / KV cache, distinct block rows: gamma 8 / 16 / 32 on one cache")
+    w = Workload(cfg, max(cfg.gammas), 1, override=True)
     w.run_gammas(list(cfg.gammas))
 
 

@@ -83,14 +83,18 @@ def two_evaluations():
                            g_attn=f(inp.g_attn(l)), g_ffn=f(inp.g_ffn(l))))
     ov = inp.embed_override(16)
     gf = f(inp.g_final())
-    hf64, _ = O.draft_forward(cfg, layers, gf, c64, 16, override=ov, storage="bf16")
-    hf32, _ = O.draft_forward(cfg, layers, gf, c32, 16, override=ov, storage="bf16")
+    hf64, bkv64 = O.draft_forward(cfg, layers, gf, c64, 16, override=ov, storage="bf16")
+    hf32, bkv32 = O.draft_forward(cfg, layers, gf, c32, 16, override=ov, storage="bf16")
+    # the block's own K/V rows of every layer: two forwards of one definition
+    # whose inputs differ only through the bf16 flips of their caches
+    block_flips = [(stored_differences(k64, k32), stored_differences(v64, v32))
+                   for (k64, v64), (k32, v32) in zip(bkv64, bkv32)]
     del layers, c64, c32
     E = f(inp.embed())
     d64, gap64, z64 = O.lm_head_argmax(hf64, E)
     d32, _, z32 = O.lm_head_argmax(hf32, E)
-    return dict(ht_flips=stored_differences(ht64, ht32), kv_flips=kv_flips, d64=d64, d32=d32, gap64=gap64,
-                drift=np.abs(z64 - z32))
+    return dict(ht_flips=stored_differences(ht64, ht32), kv_flips=kv_flips, block_flips=block_flips, d64=d64,
+                d32=d32, gap64=gap64, drift=np.abs(z64 - z32))
 
 
 def test_stored_values_differ_by_one_ulp_at_most(two_evaluations):
@@ -119,3 +123,18 @@ def test_argmax_agrees_above_the_stated_gap(two_evaluations):
     sure = r["gap64"] >= 1e-3
     assert sure.sum() >= 100
     assert np.array_equal(r["d64"][sure], r["d32"][sure])
+
+
+def test_block_kv_flips_grow_with_depth(two_evaluations):
+    """The block's K/V rows are rounded from activations that carry every
+    earlier layer's drift: layer 0's inputs are identical in both evaluations
+    (no flips), deeper layers' differ, and their one-ulp flips beyond 2e-2
+    appear and grow with depth.  (Measured here from the caches' flips alone;
+    an fp32 forward adds its own accumulation drift on top.)"""
+    fl = two_evaluations["block_flips"]
+    print("block K/V flip shares per layer (all, beyond 2e-2):", fl)
+    (k0, _), (v0, _) = fl[0]
+    assert k0 == 0.0 and v0 == 0.0
+    deep = [max(k[0], v[0]) for k, v in fl[1:]]
+    assert all(x > 0.0 for x in deep)
+    assert max(k[1] + v[1] for k, v in fl[2:]) >= max(k[1] + v[1] for k, v in fl[1:2])
