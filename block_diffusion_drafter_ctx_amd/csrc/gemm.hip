@@ -55,6 +55,15 @@ __device__ __forceinline__ void fetch_args(const GemmArgs& g) {
                "s"(g.K), "s"(g.S), "s"(g.ntiles), "s"(g.part), "s"(g.stage_tiles), "s"(g.rchunks), "s"(gridDim.x));
 }
 
+// the tiled kernel's fields, in one statement too
+__device__ __forceinline__ void fetch_args_tile(const GemmArgs& g) {
+  asm volatile("" ::"s"(g.a_src[0]), "s"(g.a_src[1]), "s"(g.a_src[2]), "s"(g.a_src[3]), "s"(g.a_src[4]),
+               "s"(g.a_src[5]), "s"(g.a_src[6]), "s"(g.a_src[7]), "s"(g.a_cols), "s"(g.a_rg), "s"(g.a_ld),
+               "s"(g.a_gs), "s"(g.w), "s"(g.w_ld), "s"(g.w_gs), "s"(g.w_off), "s"(g.w_rg), "s"(g.M), "s"(g.N),
+               "s"(g.K), "s"(g.S), "s"(g.ntiles), "s"(g.mtiles), "s"(g.chunks_per_split), "s"(g.xcd_tiles),
+               "s"(g.part), "s"(g.a_lo));
+}
+
 // A source pointer chosen by a wave-uniform index.  A select among plain
 // argument loads is turned back into one load at a computed offset (a
 // dependent memory round trip); selecting among byte offsets from the first
@@ -542,9 +551,12 @@ constexpr int kTileN = 128, kTileM = 128, kTileK = 64;
 struct TileShape { int tn, tm, wn, wm, ns; };
 constexpr TileShape kTileBf16{256, 256, 64, 128, 2}, kTileHiLo{256, 128, 64, 64, 2};
 // hi / lo planes of at most 64 activation rows: a 64-row tile (eight waves of
-// 64 x 32) does half the MFMA work of the 128-row one and fills 96 KB of LDS
-// per pair of stages instead of 128 KB
-constexpr TileShape kTileHiLo64{256, 64, 64, 32, 2}, kTileHiLo32{256, 32, 64, 16, 2};
+// 64 x 32) does half the MFMA work of the 128-row one, and its 48 KB stage (40
+// KB at 32 rows) leaves room for three stages: two tiles in flight cover the
+// HBM latency of the weight tiles, which one tile in flight does not (the
+// 8-layer drafter at 4 x 16 block rows: 2126 -> 1976 us; bf16 A on 256 x 128
+// tiles with three stages loses to 256 x 256 with two: ingest 585 -> 674 us)
+constexpr TileShape kTileHiLo64{256, 64, 64, 32, 3}, kTileHiLo32{256, 32, 64, 16, 3};
 
 template <int AK>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
@@ -702,8 +714,9 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
 // workgroup writes, for every activation row, the top-2 of its TN weight rows
 // to top2[(n-tile * M + m) * 3] (value, index bits, runner-up; lower index on
 // ties), plus the logits to g.part when that is set.
-template <int HL, int NSTAGE, int TN, int TM, int WN, int WM, bool TOP2 = false>
+template <int HL, int NSTAGE, int TN, int TM, int WN, int WM, bool TOP2 = false, bool EARLY = false>
 __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kernel(GemmArgs g, float* top2) {
+  fetch_args_tile(g);
   constexpr int NW = (TN / WN) * (TM / WM);                 // waves of WN x WM outputs each
   constexpr int FN = WN / 16, FM = WM / 16;                 // 16-row fragments per wave: W, A
   constexpr int WROWS = TN, AROWS = TM * HL;                // LDS rows per stage (A: planes stacked)
@@ -759,7 +772,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kern
     r.kb = (kt_begin + min(t, nk - 1)) * kTileK;
     // a 64-wide k tile never straddles A sources (a_cols % 64 == 0)
     const int s = r.kb / g.a_cols, col = r.kb - s * g.a_cols;
-    r.ahi = pick_src<uint16_t>(g, s) + col;
+    r.ahi = pick_src_reg<uint16_t>(g, s) + col;
     r.alo = HL == 2 ? static_cast<const uint16_t*>(g.a_lo) + col : r.ahi;   // HL == 2: one source
     return r;
   };
@@ -831,19 +844,42 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kern
   bare_barrier();
   Frags fa, fb;
   rd(fa, lds, 0);
-  for (int t = 0; t < nk; ++t) {
-    rd(fb, lds + (t % NSTAGE) * BUF, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mm(fa);                                                   // k-step 0 of tile t
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);                       // lgkmcnt(0): this wave is done reading tile t
-    wait_vmcnt<(NSTAGE - 2) * LPW>();                        // tile t + 1 landed
-    bare_barrier();                                           // ... for every wave; tile t is free
-    const TileSrc src = tile_src(t + NSTAGE);
-    rd(fa, lds + ((t + 1) % NSTAGE) * BUF, 0);                // past the end: a repeated tile, unused
-    __builtin_amdgcn_sched_barrier(0);
-    mm_issue(fb, src, t % NSTAGE);                            // k-step 1 of tile t; tile t + NSTAGE loads
-    __builtin_amdgcn_sched_barrier(0);
+  if constexpr (EARLY) {
+    // Two barriers per tile: the first (every wave has read both k-steps of
+    // tile t) frees its stage, so tile t + NSTAGE's loads go out among the
+    // MFMAs of k-step 0; the second (tile t + 1 landed everywhere) comes half
+    // a tile later.  A load then has NSTAGE - 1/2 tiles of MFMA work to land
+    // in, against NSTAGE - 1 when it waits for the single mid-tile barrier.
+    for (int t = 0; t < nk; ++t) {
+      rd(fb, lds + (t % NSTAGE) * BUF, 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0): this wave is done reading tile t
+      bare_barrier();                                         // ... every wave is: its stage is free
+      const TileSrc src = tile_src(t + NSTAGE);
+      __builtin_amdgcn_sched_barrier(0);
+      mm_issue(fa, src, t % NSTAGE);                          // k-step 0 of tile t; tile t + NSTAGE loads
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<(NSTAGE - 1) * LPW>();                      // tile t + 1 landed (tiles t + 2 .. in flight)
+      bare_barrier();                                         // ... for every wave
+      rd(fa, lds + ((t + 1) % NSTAGE) * BUF, 0);              // past the end: a repeated tile, unused
+      __builtin_amdgcn_sched_barrier(0);
+      mm(fb);                                                 // k-step 1 of tile t
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (int t = 0; t < nk; ++t) {
+      rd(fb, lds + (t % NSTAGE) * BUF, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mm(fa);                                                 // k-step 0 of tile t
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0): this wave is done reading tile t
+      wait_vmcnt<(NSTAGE - 2) * LPW>();                      // tile t + 1 landed
+      bare_barrier();                                         // ... for every wave; tile t is free
+      const TileSrc src = tile_src(t + NSTAGE);
+      rd(fa, lds + ((t + 1) % NSTAGE) * BUF, 0);              // past the end: a repeated tile, unused
+      __builtin_amdgcn_sched_barrier(0);
+      mm_issue(fb, src, t % NSTAGE);                          // k-step 1 of tile t; tile t + NSTAGE loads
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   wait_vmcnt<0>();                                            // the trailing repeated tiles
 
@@ -1185,11 +1221,16 @@ hipError_t launch_tile_lds(GemmArgs a, dim3 grid, hipStream_t st, float* top2 = 
     const long T = static_cast<long>(grid.x) * grid.y * grid.z;
     grid = dim3(static_cast<unsigned>((T + 7) / 8 * 8));
   }
+  // the two-barrier loop that issues a tile's loads half a tile earlier pays
+  // off for the two-stage hi / lo tile (the 8-layer drafter at 4 x 32 block
+  // rows 2575 -> 2521 us); with bf16 A on 256 x 256 tiles (context ingest 579
+  // -> 591 us) and with three stages it does not
+  constexpr bool EARLY = HL == 2 && NS == 2;
   const hipError_t e = ensure_dyn_lds(
-      reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2>), static_cast<int>(lds));
+      reinterpret_cast<const void*>(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2, EARLY>), static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  launch_k(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2>, grid, dim3((TN / WN) * (TM / WM) * 64), lds,
-                     st, a, top2);
+  launch_k(gemm_tile_lds_kernel<HL, NS, TN, TM, WN, WM, TOP2, EARLY>, grid, dim3((TN / WN) * (TM / WM) * 64), lds, st,
+           a, top2);
   return hipGetLastError();
 }
 
