@@ -565,8 +565,9 @@ hipError_t launch_dma(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
 }
 
 // Merge the key ranges of one (row, head): O = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
-// The split weights are computed once per row into LDS; the O loads of all
-// splits are then independent.
+// The split weights are computed once per row into LDS. The O loads of all
+// splits are independent of them and, for up to 32 splits, are in flight
+// together with the (m, l) loads, so the merge waits on one memory round.
 constexpr int kMaxSplitsLds = 1024;
 
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
@@ -579,6 +580,18 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int r = (h - j * G) * a.gam[b] + i;
   const int ns = a.nsplit[b];
   const int it0 = a.item_off[b] + j * ns;
+  // up to kCombRegs splits: each thread's O partials (one column, d <= block) are
+  // requested at entry, beside wave 0's (m, l) loads, instead of after the
+  // barrier; the sums below keep the split order either way
+  constexpr int kCombRegs = 32;
+  const bool in_regs = ns <= kCombRegs && a.d <= static_cast<int>(blockDim.x);  // uniform
+  const int c0 = threadIdx.x;
+  float ov[kCombRegs];
+  if (in_regs && c0 < a.d) {
+#pragma unroll
+    for (int s = 0; s < kCombRegs; ++s)
+      ov[s] = s < ns ? a.part_o[(static_cast<int64_t>(it0 + s) * a.Rpad + r) * a.d + c0] : 0.f;
+  }
   if (threadIdx.x < 64) {
     float M = -INFINITY;
     for (int s = threadIdx.x; s < ns; s += 64) M = fmaxf(M, a.part_ml[(static_cast<int64_t>(it0 + s) * a.Rpad + r) * 2]);
@@ -594,6 +607,18 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
     if (threadIdx.x == 0) inv_l = 1.0f / L;
   }
   __syncthreads();
+  if (in_regs) {
+    if (c0 < a.d) {
+      float O = 0.f;
+#pragma unroll
+      for (int s = 0; s < kCombRegs; ++s)
+        if (s < ns) O += wts[s] * ov[s];
+      const int64_t oi = (static_cast<int64_t>(m) * a.Hq + h) * a.d + c0;
+      if (a.o_hi != nullptr) split1(O * inv_l, a.o_hi[oi], a.o_lo[oi]);
+      else a.o_out[oi] = O * inv_l;
+    }
+    return;
+  }
   for (int c = threadIdx.x; c < a.d; c += blockDim.x) {
     float O = 0.f;
 #pragma unroll 8
