@@ -77,14 +77,16 @@ def kernel_traffic(which, workload, cache):
 
 
 # Kernel families of one headline step: (name, per-kernel roles it runs, which of
-# them it runs only with an fp32 cache).  The short-weight register-K GEMM takes
-# the Q/K/V, O and down projections and, with an fp32 H_t, the 16-row inject.
+# them it runs only with an fp32 cache, the key of its recorded counters).  The
+# short-weight register-K GEMM takes the Q/K/V, O and down projections and, with
+# an fp32 H_t, the 16-row inject.
 FAMILIES = (
-    ("gemm_rk_kernel<2, RK_PART, 1, A_F32_SPLIT> (short weights: Q/K/V, O and down projections of every layer, "
-     "and the 16-row K/V inject with an fp32 H_t; 16 fp32 activation rows as bf16 hi + lo in registers, split-K "
-     "partials reduced by the next kernel)", ("qkv", "o_proj", "down", "inject_append"), ("inject_append",)),
-    ("gemm_rk_kernel<8, RK_SWIGLU> (FFN gate/up with SwiGLU in the epilogue)", ("gate_up",), ()),
-    ("attention (split over key ranges + log-sum-exp combine)", ("attention",), ()),
+    ("gemm_rk_kernel<4, RK_PART, 1, A_F32_SPLIT, 8> (short weights: Q/K/V, O and down projections of every layer, "
+     "and the 16-row K/V inject with an fp32 H_t; 8 waves, 16 fp32 activation rows as bf16 hi + lo in registers, "
+     "split-K partials reduced by the next kernel)", ("qkv", "o_proj", "down", "inject_append"), ("inject_append",),
+     "short_rk"),
+    ("gemm_rk_kernel<8, RK_SWIGLU> (FFN gate/up with SwiGLU in the epilogue)", ("gate_up",), (), None),
+    ("attention (split over key ranges + log-sum-exp combine)", ("attention",), (), None),
 )
 
 
@@ -96,14 +98,14 @@ def dominant_roofline(cfg, per_kernel, lm_bytes, lm_us, workload):
     calls = {"qkv": cfg.L, "o_proj": cfg.L, "gate_up": cfg.L, "down": cfg.L, "attention": cfg.L, "inject_append": 1,
              "fuse_append": 1}
     cands = [("gemm_rk_kernel<8, RK_TOP2> (LM head with the top-2 epilogue)", lm_bytes, lm_us, 1, "lm_head")]
-    for name, roles, f32_only in FAMILIES:
+    for name, roles, f32_only, key in FAMILIES:
         rs = [r for r in roles if r in per_kernel and not (r in f32_only and cfg.cache_dtype != "f32")]
         n = sum(calls[r] for r in rs)
         if n == 0:
             continue
         tb = sum(per_kernel[r]["bytes"] * calls[r] for r in rs)
         tu = sum(per_kernel[r]["us"] * calls[r] for r in rs)
-        cands.append((name, tb / n, tu / n, n, "short_rk" if name.startswith("gemm_rk_kernel<2") else None))
+        cands.append((name, tb / n, tu / n, n, key))
     name, b, us, n, key = max(cands, key=lambda c: c[2] * c[3])
     gbs = b / (us * 1e-6) / 1e9
     return {"kernel": name + f"; {n} launch(es) per step, the largest kernel time of a step; HIP events recorded by each "

@@ -257,13 +257,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(GemmArgs g) {
 // ------------------------------------------------------------- register-K path
 // One block of <= 16 activation rows (a 16-row chunk of a larger block, see
 // rk_max_rows) against a tall weight (the LM head, the
-// FFN gate/up projection).  Sixteen waves split the K range of a workgroup
-// (wave w owns KS k-steps) and keep their activation fragments (hi + lo) in
-// registers for the whole kernel, so a workgroup needs no split-K partner and
-// no LDS slice: every output tile of 16 weight rows is one contiguous
-// 16 x K block of W, streamed by all sixteen waves at once through a ring of
-// KS loads per wave (the next tile's loads are issued as the current tile's
-// MFMAs retire).  The sixteen per-wave partial tiles are summed through LDS
+// FFN gate/up projection; with eight waves, the short split-K form).  NW waves
+// split the K range of a workgroup (wave w owns KS k-steps) and keep their
+// activation fragments (hi + lo) in registers for the whole kernel, so a
+// workgroup needs no split-K partner and no LDS slice: every output tile of
+// 16 weight rows is one contiguous 16 x K block of W, streamed by all NW waves
+// at once through a ring of KS loads per wave (the next tile's loads are
+// issued as the current tile's MFMAs retire).  The NW per-wave partial tiles
+// are summed through LDS
 // in wave order (deterministic).  Epilogues: the [split][M][N] store; the LM
 // head's running top-2 per row (plus the logits when asked for), merged per
 // workgroup into top2[block][m] = (best value, its index, runner-up); the LM
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(GemmArgs g) {
 // the stacked [gate; up] weight, so s = silu(gate) * up leaves the kernel
 // directly (N = F outputs, 8 per tile).
 constexpr int kRkWaves = 16;
+constexpr int kRkShortWaves = 8;   // the short split-K form (see plan_gemm_rk_short)
 constexpr int kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kRkMinN = 16384;   // weight rows below which the split-K streaming kernel wins
 
@@ -288,14 +290,14 @@ __device__ __forceinline__ int src_of(int k, int a_cols) {
   return s;
 }
 
-template <int KS, int EP, int T, int AK = A_F32_SPLIT>
-__global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, float* top2, float* logits) {
+template <int KS, int EP, int T, int AK = A_F32_SPLIT, int NW = kRkWaves>
+__global__ __launch_bounds__(64 * NW) void gemm_rk_kernel(GemmArgs g, float* top2, float* logits) {
   fetch_args(g);
   constexpr bool TOP2 = EP == RK_TOP2;
   constexpr bool SAMPLE = EP == RK_SAMPLE;
   constexpr int TN = EP == RK_SWIGLU ? 8 : 16;   // outputs per tile
   static_assert(EP == RK_PART || T == 1, "fused epilogues stream one tile at a time");
-  __shared__ float red[2][kRkWaves][T][256];
+  __shared__ float red[2][NW][T][256];
   __shared__ float tv1[4][16], tv2[4][16];
   __shared__ int ti1[4][16];
   __shared__ float4 sst[4][16];
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
   const int P = gridDim.x / C;
   if (u0 >= units) return;                    // uniform per workgroup
   const int sp = u0 % S;                      // P % S == 0: the split never changes
-  const int kwave = sp * (32 * KS * kRkWaves) + wave * (32 * KS);
+  const int kwave = sp * (32 * KS * NW) + wave * (32 * KS);
   const int kl = kwave + 8 * (lane >> 4);
   auto wrow = [&](int uu) {
     uu = uu < units ? uu : u0;                // past the last unit: re-read a valid one (result dropped)
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
       if (tid < 128) {
         float vg = 0.f, vu = 0.f;
 #pragma unroll 4
-        for (int w = 0; w < kRkWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
           vg += red[buf][w][0][tid];
           vu += red[buf][w][0][tid + 128];
         }
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
         if (uu < units) {
           float v = 0.f;
 #pragma unroll 4
-          for (int w = 0; w < kRkWaves; ++w) v += red[buf][w][t][tid];
+          for (int w = 0; w < NW; ++w) v += red[buf][w][t][tid];
           const int n = (uu / S) * TN + no;
           if (mg < g.M && n < g.N) {
             if constexpr (TOP2) {
@@ -518,7 +520,7 @@ __global__ __launch_bounds__(64 * kRkWaves) void gemm_rk_kernel(GemmArgs g, floa
     constexpr int PPR = kOutCols / 4;          // float4 pieces per row
     const int nslots = (units - u0 + P - 1) / P;
     float* out = SAMPLE ? logits : g.part + static_cast<int64_t>(sp) * g.M * g.N;
-    for (int i = tid; i < nslots * PPT; i += 64 * kRkWaves) {
+    for (int i = tid; i < nslots * PPT; i += 64 * NW) {
       const int slot = i / PPT, r = (i % PPT) / PPR, c4 = 4 * (i % PPR);
       const int n0 = ((u0 + P * slot) / S) * kOutCols;
       if (m0 + r < g.M) {
@@ -1350,6 +1352,7 @@ GemmPlan plan_gemm_rk(int M, int N, int K, bool top2) {
   if (grid == 0) return p;
   p.rk = true;
   p.ks = ks;
+  p.waves = kRkWaves;
   p.S = S;
   p.MT = 16;
   p.mtiles = 1;
@@ -1362,26 +1365,32 @@ GemmPlan plan_gemm_rk(int M, int N, int K, bool top2) {
   return p;
 }
 
-// Register-K for a short weight: 2 k-steps per wave (a K range of 1024 per
+// Register-K for a short weight: 8 waves of 4 k-steps (a K range of 1024 per
 // workgroup, S = K / 1024 splits), so that a workgroup reads only 64 KB of the
 // activation block while 256 workgroups keep the stream of 32 KB weight
-// pieces deep.
+// pieces deep.  Eight waves rather than sixteen with 2 k-steps: the same bytes
+// in flight per CU with half the waves to launch and to reduce over
+// (0.2 us a call, the step 849 -> 845 us).
 GemmPlan plan_gemm_rk_short(int M, int N, int K) {
   GemmPlan p;
-  if (M < 1 || M > rk_max_rows(false) || K % (32 * 2 * kRkWaves) != 0 || env_int("DFLASH_GEMM_NO_RK", 0) != 0) return p;
-  const int S = K / (32 * 2 * kRkWaves);
+  constexpr int kKsShort = 4;
+  if (M < 1 || M > rk_max_rows(false) || K % (32 * kKsShort * kRkShortWaves) != 0 ||
+      env_int("DFLASH_GEMM_NO_RK", 0) != 0)
+    return p;
+  const int S = K / (32 * kKsShort * kRkShortWaves);
   const int C = (M + 15) / 16;
   const int ntiles = (N + 15) / 16;
   const int grid = rk_unit_groups(S, C, static_cast<long>(S) * ntiles);
   if (grid == 0) return p;
   p.rk = true;
-  p.ks = 2;
+  p.ks = kKsShort;
+  p.waves = kRkShortWaves;
   p.S = S;
   p.MT = 16;
   p.mtiles = 1;
   p.mr = C;
   p.ntiles = ntiles;
-  p.cps = 2 * kRkWaves;
+  p.cps = kKsShort * kRkShortWaves;
   p.nchunks = K / 32;
   p.grid = grid;
   p.part_floats = static_cast<size_t>(p.S) * M * N;
@@ -1408,9 +1417,9 @@ GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
 // Launch one register-K instantiation.  Epilogues that write per tile get
 // their workgroup's output tiles staged in dynamic LDS (written out after the
 // weight stream) whenever they fit beside the kernel's static LDS.
-template <int KS, int EP, int T, int AK = A_F32_SPLIT>
+template <int KS, int EP, int T, int AK = A_F32_SPLIT, int NW = kRkWaves>
 hipError_t rk_launch(GemmArgs a, const GemmPlan& p, float* top2, float* logits, hipStream_t st) {
-  const void* kern = reinterpret_cast<const void*>(&gemm_rk_kernel<KS, EP, T, AK>);
+  const void* kern = reinterpret_cast<const void*>(&gemm_rk_kernel<KS, EP, T, AK, NW>);
   const int stage_cap = EP != RK_TOP2 ? dyn_lds_room(kern, kLdsBytes) : 0;   // dynamic LDS bytes it may use
   const size_t tile_bytes = (EP == RK_SWIGLU ? 8 : 16) * 16 * sizeof(float);
   const int slots = (p.S * p.ntiles + p.grid - 1) / p.grid;   // units a workgroup handles
@@ -1424,7 +1433,8 @@ hipError_t rk_launch(GemmArgs a, const GemmPlan& p, float* top2, float* logits, 
     a.stage_tiles = slots;
     shm = static_cast<size_t>(slots) * tile_bytes;
   }
-  launch_k(gemm_rk_kernel<KS, EP, T, AK>, dim3(p.grid * p.mr), dim3(64 * kRkWaves), shm, st, a, top2,
+  if (p.waves != NW) return hipErrorInvalidValue;
+  launch_k(gemm_rk_kernel<KS, EP, T, AK, NW>, dim3(p.grid * p.mr), dim3(64 * NW), shm, st, a, top2,
                      logits);
   return hipGetLastError();
 }
@@ -1442,17 +1452,18 @@ hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, fl
     if (p.ks == 8) return rk_launch<8, RK_TOP2, 1>(a, p, top2, logits, st);
     return rk_launch<4, RK_TOP2, 1>(a, p, top2, logits, st);
   }
+  // the short form (8 waves) streams one tile at a time as well: on cold weights
+  // (34-100 MB, rotated past the Infinity Cache) one tile in flight per wave
+  // beats two by 0.5-0.8 us per call and four lose 1-3 us
+  const bool short_form = p.waves == kRkShortWaves;
   if (ak == A_BF16) {
+    if (short_form) return rk_launch<4, RK_PART, 1, A_BF16, kRkShortWaves>(a, p, nullptr, nullptr, st);
     if (p.ks == 8) return rk_launch<8, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
-    if (p.ks == 4) return rk_launch<4, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
-    return rk_launch<2, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
+    return rk_launch<4, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
   }
+  if (short_form) return rk_launch<4, RK_PART, 1, A_F32_SPLIT, kRkShortWaves>(a, p, nullptr, nullptr, st);
   if (p.ks == 8) return rk_launch<8, RK_PART, 1>(a, p, nullptr, nullptr, st);
-  if (p.ks == 4) return rk_launch<4, RK_PART, 1>(a, p, nullptr, nullptr, st);
-  // the short form streams one tile at a time as well: on cold weights (34-100 MB,
-  // rotated past the Infinity Cache) one tile in flight per wave beats two by
-  // 0.5-0.8 us per call and four lose 1-3 us
-  return rk_launch<2, RK_PART, 1>(a, p, nullptr, nullptr, st);
+  return rk_launch<4, RK_PART, 1>(a, p, nullptr, nullptr, st);
 }
 
 hipError_t launch_gemm_rk_sample(const GemmArgs& a0, const GemmPlan& p, float4* stats, float* logits,
