@@ -44,10 +44,10 @@ METRIC = "drafted gamma=16 blocks/sec + draft fwd us at 1 GPU; % HBM BW / % MFMA
 KERNEL_COUNTERS = {
     # mean KiB per dispatch over the bench's headline run (the summaries under
     # profiles/ give the commands); scales from the copy above
-    "short_rk": {"src": "18467e3c3006e9ae", "workload": "qwen3_8b_shape_n2048", "cache": "bf16",
-                 "fetch_kib": 30504.0, "write_kib": 1877.3, "fetch_scale": 1.9998, "write_scale": 1.0},
-    "lm_head": {"src": "18467e3c3006e9ae", "workload": "qwen3_8b_shape_n2048", "cache": "bf16",
-                "fetch_kib": 608755.1, "write_kib": 52.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    "short_rk": {"src": "db24cdbdc8d0de21", "workload": "qwen3_8b_shape_n2048", "cache": "bf16",
+                 "fetch_kib": 30506.5, "write_kib": 1877.3, "fetch_scale": 1.9998, "write_scale": 1.0},
+    "lm_head": {"src": "db24cdbdc8d0de21", "workload": "qwen3_8b_shape_n2048", "cache": "bf16",
+                "fetch_kib": 608779.8, "write_kib": 52.0, "fetch_scale": 1.9998, "write_scale": 1.0},
 }
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/launch.h")
 
@@ -97,7 +97,7 @@ def dominant_roofline(cfg, per_kernel, lm_bytes, lm_us, workload):
     from block_diffusion_drafter_ctx_amd import roofline as RF
     calls = {"qkv": cfg.L, "o_proj": cfg.L, "gate_up": cfg.L, "down": cfg.L, "attention": cfg.L, "inject_append": 1,
              "fuse_append": 1}
-    cands = [("gemm_rk_kernel<8, RK_TOP2> (LM head with the top-2 epilogue)", lm_bytes, lm_us, 1, "lm_head")]
+    cands = [("gemm_rk_kernel<16, RK_TOP2, 1, A_F32_SPLIT, 8> (LM head with the top-2 epilogue)", lm_bytes, lm_us, 1, "lm_head")]
     for name, roles, f32_only, key in FAMILIES:
         rs = [r for r in roles if r in per_kernel and not (r in f32_only and cfg.cache_dtype != "f32")]
         n = sum(calls[r] for r in rs)
@@ -363,8 +363,8 @@ def main():
         "per_kernel": per_kernel,
         "roofline": dominant_roofline(cfg, per_kernel, lm_bytes, lm_us, args.workload),
         "roofline_lm_head": {
-            "kernel": "gemm_rk_kernel<8, RK_TOP2> (LM head: 151936 x 4096 bf16 streamed once against the 15 "
-                      "mask rows held in registers as bf16 hi + lo, logits reduced in-kernel to a top-2 per "
+            "kernel": "gemm_rk_kernel<16, RK_TOP2, 1, A_F32_SPLIT, 8> (LM head: 151936 x 4096 bf16 streamed once "
+                      "against the 15 mask rows held in registers of 8 waves as bf16 hi + lo, logits reduced in-kernel to a top-2 per "
                       "workgroup), one launch per step, HIP events recorded by that launch's dispatch on the library "
                       "stream by dflash_profile_events",
             "bound": "hbm", "achieved": round(lm_gbs, 1), "peak": RF.HBM_PEAK_GBS, "unit": "GB/s",

@@ -1433,7 +1433,9 @@ hipError_t rk_launch(GemmArgs a, const GemmPlan& p, float* top2, float* logits, 
     a.stage_tiles = slots;
     shm = static_cast<size_t>(slots) * tile_bytes;
   }
-  if (p.waves != NW) return hipErrorInvalidValue;
+  // the plan fixes the k-steps of a workgroup (its K range); the epilogue picks
+  // how they are spread over waves
+  if (p.cps != KS * NW || a.a_cols % (32 * KS) != 0) return hipErrorInvalidValue;
   launch_k(gemm_rk_kernel<KS, EP, T, AK, NW>, dim3(p.grid * p.mr), dim3(64 * NW), shm, st, a, top2,
                      logits);
   return hipGetLastError();
@@ -1449,6 +1451,11 @@ hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, fl
   a.mtiles = 1;
   a.chunks_per_split = p.cps;
   if (top2 != nullptr) {
+    // the LM head runs its K range on eight waves of twice the k-steps: 205 ->
+    // 200 us at 15 rows x 151936 x 4096 (the gate/up projection, 6 tiles per
+    // workgroup against ~37, gains nothing from it and keeps sixteen)
+    if (p.ks == 8 && a.a_cols % (32 * 16) == 0) return rk_launch<16, RK_TOP2, 1, A_F32_SPLIT, 8>(a, p, top2, logits, st);
+    if (p.ks == 4 && a.a_cols % (32 * 8) == 0) return rk_launch<8, RK_TOP2, 1, A_F32_SPLIT, 8>(a, p, top2, logits, st);
     if (p.ks == 8) return rk_launch<8, RK_TOP2, 1>(a, p, top2, logits, st);
     return rk_launch<4, RK_TOP2, 1>(a, p, top2, logits, st);
   }
@@ -1477,6 +1484,9 @@ hipError_t launch_gemm_rk_sample(const GemmArgs& a0, const GemmPlan& p, float4* 
   a.mtiles = 1;
   a.chunks_per_split = p.cps;
   float* sp = reinterpret_cast<float*>(stats);
+  // eight waves as for the top-2 LM head: 210 -> 208 us at 15 rows x 151936 x 4096
+  if (p.ks == 8 && a.a_cols % (32 * 16) == 0) return rk_launch<16, RK_SAMPLE, 1, A_F32_SPLIT, 8>(a, p, sp, logits, st);
+  if (p.ks == 4 && a.a_cols % (32 * 8) == 0) return rk_launch<8, RK_SAMPLE, 1, A_F32_SPLIT, 8>(a, p, sp, logits, st);
   if (p.ks == 8) return rk_launch<8, RK_SAMPLE, 1>(a, p, sp, logits, st);
   return rk_launch<4, RK_SAMPLE, 1>(a, p, sp, logits, st);
 }
