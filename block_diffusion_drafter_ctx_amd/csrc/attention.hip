@@ -18,7 +18,9 @@
 //     probabilities never leave registers;
 //   * O^T = V^T P^T reads values from the transposed V cache (keys contiguous:
 //     [d][cap] per head in an fp32 cache, [cap/32][d][32] in a bf16 one), P
-//     again split hi + lo;
+//     again split hi + lo; a bf16 cache also stores each 32-key block of K in
+//     the order of the score MFMA's fragments, so every K or V fragment is one
+//     contiguous kilobyte;
 //   * each workgroup writes (max, sum, O) per row; a combine kernel merges the
 //     key ranges in a fixed order (log-sum-exp), so results are deterministic.
 // A bf16 cache streams K/V blocks straight into LDS (attn_dma_kernel); an fp32
@@ -327,7 +329,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attn_mfma_kernel(AttnArgs a) 
 // loads (lane l of a wave-wide 16-byte load lands at LDS base + 16 l): no
 // register staging, no conversion, and the stages in flight cost no
 // registers.  Inside a 32-key block the score tile kt takes keys in the order
-// row i -> key 8 (i / 4) + 4 kt + i % 4, so the S^T output leaves lane l (lane
+// row i -> key 8 (i / 4) + 4 kt + i % 4 (the cache stores the block's K in
+// exactly these fragments, kt-major then 32-dimension slice, lane l's 16 bytes
+// at 16 l, see k_frag_offset), so the S^T output leaves lane l (lane
 // group g = l / 16) holding keys 8 g + 4 kt + r of its query column; as the B
 // operand of the value MFMA, k-slot 8 g + e is then key 8 g + e, and the value
 // fragment of lane l is 8 consecutive keys of one row of the block's V^T
@@ -375,10 +379,8 @@ __global__ __launch_bounds__(512) void attn_dma_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int f = (wave + NW * i) % NFR;
-    if (f < KFR) {
-      const int kt = f / DS, ds = f % DS;
-      const int key = 8 * ((lane & 15) >> 2) + 4 * kt + (lane & 3);
-      off[i] = 2u * static_cast<uint32_t>(key * HD + ds * 32 + 8 * g4);
+    if (f < KFR) {                              // K block in fragment order: one kilobyte per fragment
+      off[i] = 2u * static_cast<uint32_t>(f * 512 + lane * 8);
     } else {                                    // V^T block [d][32]: dimension row, 8 keys
       off[i] = 2u * static_cast<uint32_t>(((f - KFR) * 16 + (lane & 15)) * 32 + 8 * g4);
     }

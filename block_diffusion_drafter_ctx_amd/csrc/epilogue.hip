@@ -2,8 +2,8 @@
 // row-wise kernels of the drafter path:
 //   ctx_norm       fusion epilogue: sum partials, RMSNorm with g_c, store H_t
 //   scatter_kv     sum partials; query columns -> fp32 Q; key / value columns ->
-//                  the KV cache (keys row-major, values transposed; per block of
-//                  32 keys in a bf16 cache)
+//                  the KV cache (keys row-major, values transposed; a bf16
+//                  cache keeps both per block of 32 keys, keys in fragment order)
 //   residual_norm  h += sum partials; a = RMSNorm(h; g)
 //   swiglu         s = SiLU(gate) * up
 //   embed_norm     h = embedding rows (or override rows); a = RMSNorm(h; g)
@@ -139,7 +139,13 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(ScatterArgs a) {
   const int64_t head0 = (static_cast<int64_t>(layer) * a.B + a.rows.seq[b]) * a.Hkv;
   if (rem < hd) {
     const int j = rem / a.d, c = rem % a.d;
-    st4<T>(a.kc, ((head0 + j) * a.cap + pos) * a.d + c, v);
+    // fp32 cache: row-major keys; bf16 cache: each 32-key block in fragment
+    // order (dimensions c .. c + 3 stay adjacent: c % 8 is 0 or 4)
+    const int64_t ki = sizeof(T) == 2
+                           ? (head0 + j) * a.cap * a.d + static_cast<int64_t>(pos / 32) * (32 * a.d) +
+                                 k_frag_offset(pos, c, a.d)
+                           : ((head0 + j) * a.cap + pos) * a.d + c;
+    st4<T>(a.kc, ki, v);
   } else {
     const int j = (rem - hd) / a.d, c = (rem - hd) % a.d;
     // fp32 cache: V^T [d][cap] per head; bf16 cache: V^T per block of 32 keys

@@ -158,7 +158,7 @@ struct ScatterArgs {
   int32_t S, M, N;
   int32_t nq;          // columns [0, nq) are query columns -> q_out[m][n]
   float* q_out;
-  void* kc;            // cache K base of layer `layer0`: [L][B][Hkv][cap][d]
+  void* kc;            // cache K base of layer `layer0`: [L][B][Hkv][cap][d] (fp32), per 32-key block in fragment order (bf16)
   void* vc;            // cache V base: [L][B][Hkv][d][cap] (fp32), [L][B][Hkv][cap/32][d][32] (bf16)
   int32_t layer0, B, Hkv, d, cap;
   SeqRows rows;
@@ -274,7 +274,7 @@ hipError_t launch_spec_verify(const SpecArgs& a, hipStream_t st);
 // ------------------------------------------------------------ attention
 struct AttnArgs {
   const float* q;        // [M][Hq*d], M = qrow0[B] block rows (sequence b's at qrow0[b] ..)
-  const void* kc;        // layer base [B][Hkv][cap][d]
+  const void* kc;        // layer base [B][Hkv][cap][d] (fp32), [B][Hkv][cap/32][32*d] in fragment order (bf16)
   const void* vc;        // layer base [B][Hkv][d][cap] (fp32), [B][Hkv][cap/32][d][32] (bf16)
   float* part_o;         // [items][Rpad][d]
   float* part_ml;        // [items][Rpad][2]

@@ -52,20 +52,35 @@ def upload(arr: np.ndarray, cfg, device="cuda") -> torch.Tensor:
     return t.to(torch_dtype(cfg)) if cfg.dtype == "bf16" else t
 
 
+def k_frag_perm(d: int) -> np.ndarray:
+    """For a bf16 cache's 32-key K block: perm[i * d + c] = position of (key i,
+    dimension c) in the stored block (the attention's score-fragment order:
+    fragment ((i % 8) // 4) * (d // 32) + c // 32 of 512 elements, lane
+    16 ((c % 32) // 8) + 4 (i // 8) + i % 4 of it, 8 dimensions per lane)."""
+    i = np.arange(32)[:, None]
+    c = np.arange(d)[None, :]
+    f = ((i % 8) // 4) * (d // 32) + c // 32
+    lane = 16 * ((c % 32) // 8) + 4 * (i // 8) + i % 4
+    return (f * 512 + lane * 8 + c % 8).reshape(-1)
+
+
 class DeviceCache:
-    """KV cache: keys [L][B][Hkv][cap][d]; values transposed, [L][B][Hkv][d][cap]
-    in an fp32 cache and per block of 32 keys, [L][B][Hkv][cap/32][d][32], in a
-    bf16 cache; the host lengths the library plans from, and their device
-    mirror."""
+    """KV cache.  fp32: keys [L][B][Hkv][cap][d], values transposed
+    [L][B][Hkv][d][cap].  bf16: per block of 32 keys, keys [L][B][Hkv][cap/32][32*d]
+    in the attention's fragment order (k_frag_perm) and values
+    [L][B][Hkv][cap/32][d][32].  Also the host lengths the library plans from,
+    and their device mirror."""
 
     def __init__(self, cfg, B_: int, cap: int, device="cuda"):
         dt = cache_torch_dtype(cfg)
         self.blocked = cfg.cache_dtype == "bf16"
         self.L, self.Hkv, self.d = cfg.L, cfg.Hkv, cfg.d
-        self.k = torch.zeros(cfg.L, B_, cfg.Hkv, cap, cfg.d, dtype=dt, device=device)
         if self.blocked:
+            self.k = torch.zeros(cfg.L, B_, cfg.Hkv, cap // 32, 32 * cfg.d, dtype=dt, device=device)
             self.v = torch.zeros(cfg.L, B_, cfg.Hkv, cap // 32, cfg.d, 32, dtype=dt, device=device)
+            self._perm = torch.from_numpy(k_frag_perm(cfg.d)).to(device)
         else:
+            self.k = torch.zeros(cfg.L, B_, cfg.Hkv, cap, cfg.d, dtype=dt, device=device)
             self.v = torch.zeros(cfg.L, B_, cfg.Hkv, cfg.d, cap, dtype=dt, device=device)
         self.len_dev = torch.zeros(B_, dtype=torch.int32, device=device)
         self.lens = (ctypes.c_int32 * B_)()
@@ -87,6 +102,30 @@ class DeviceCache:
             self.len_dev.copy_(torch.tensor(self.len_list(), dtype=torch.int32))
 
     # ---- the layout lives here only (tests and measurements)
+    def _kt(self, b: int, lo: int, hi: int) -> torch.Tensor:
+        """Keys of rows [lo, hi) of sequence b as [L][Hkv][hi - lo][d] (a view
+        for an fp32 cache, a copy of the covering blocks for a bf16 one)."""
+        if not self.blocked:
+            return self.k[:, b, :, lo:hi]
+        b0, b1 = lo // 32, (hi + 31) // 32
+        blk = self.k[:, b, :, b0:b1]                       # [L][Hkv][nb][32 d] stored order
+        rows = blk[..., self._perm].reshape(self.L, self.Hkv, (b1 - b0) * 32, self.d)
+        return rows[:, :, lo - 32 * b0:hi - 32 * b0]
+
+    def _put_k(self, b: int, lo: int, kt: torch.Tensor):
+        """Write keys [L][Hkv][n][d] into rows [lo, lo + n) of sequence b."""
+        n = kt.shape[2]
+        if not self.blocked:
+            self.k[:, b, :, lo:lo + n] = kt
+            return
+        b0, b1 = lo // 32, (lo + n + 31) // 32
+        full = self._kt(b, 32 * b0, 32 * b1).clone()
+        full[:, :, lo - 32 * b0:lo - 32 * b0 + n] = kt
+        flat = full.reshape(self.L, self.Hkv, b1 - b0, 32 * self.d)
+        stored = torch.empty_like(flat)
+        stored[..., self._perm] = flat
+        self.k[:, b, :, b0:b1] = stored
+
     def _vt(self, b: int, lo: int, hi: int) -> torch.Tensor:
         """Values of rows [lo, hi) of sequence b as V^T [L][Hkv][d][hi - lo] (a
         view for an fp32 cache, a copy of the covering blocks for a bf16 one)."""
@@ -111,7 +150,7 @@ class DeviceCache:
     def rows(self, b: int, lo: int, hi: int):
         """Rows [lo, hi) of sequence b in every layer: (K, V) float64 numpy
         arrays [L][hi - lo][Hkv][d]."""
-        k = self.k[:, b, :, lo:hi].float().cpu().numpy().transpose(0, 2, 1, 3)
+        k = self._kt(b, lo, hi).float().cpu().numpy().transpose(0, 2, 1, 3)
         v = self._vt(b, lo, hi).float().cpu().numpy().transpose(0, 3, 1, 2)
         return k.astype(np.float64), v.astype(np.float64)
 
@@ -122,22 +161,22 @@ class DeviceCache:
         n = k.shape[1]
         kt = torch.from_numpy(np.ascontiguousarray(k.transpose(0, 2, 1, 3), dtype=np.float32))
         vt = torch.from_numpy(np.ascontiguousarray(v.transpose(0, 2, 3, 1), dtype=np.float32))
-        self.k[:, b, :, lo:lo + n] = kt.to(self.k.device, self.k.dtype)
+        self._put_k(b, lo, kt.to(self.k.device, self.k.dtype))
         self._put_vt(b, lo, vt.to(self.v.device, self.v.dtype))
 
     def fill_random(self, b: int, n: int, gen: torch.Generator):
         """Rows [0, n) of sequence b in every layer from N(0, 1) draws."""
         dev, dt = self.k.device, self.k.dtype
-        self.k[:, b, :, :n].copy_(torch.randn(self.L, self.Hkv, n, self.d, generator=gen, device=dev).to(dt))
+        self._put_k(b, 0, torch.randn(self.L, self.Hkv, n, self.d, generator=gen, device=dev).to(dt))
         self._put_vt(b, 0, torch.randn(self.L, self.Hkv, self.d, n, generator=gen, device=dev).to(dt))
 
     def snapshot(self, b: int, n: int):
         """A device copy of rows [0, n) of sequence b in every layer."""
-        return self.k[:, b, :, :n].clone(), self._vt(b, 0, n).clone()
+        return self._kt(b, 0, n).clone(), self._vt(b, 0, n).clone()
 
     def same_rows(self, snap, b: int, n: int) -> bool:
         """Rows [0, n) of sequence b are bit-identical to ``snap``."""
-        return torch.equal(self.k[:, b, :, :n], snap[0]) and torch.equal(self._vt(b, 0, n), snap[1])
+        return torch.equal(self._kt(b, 0, n), snap[0]) and torch.equal(self._vt(b, 0, n), snap[1])
 
 
 class DeviceDrafter:

@@ -115,11 +115,16 @@ typedef struct {
 /* The drafter's KV cache: injected context rows plus gamma scratch rows per
  * sequence ([JP] "추론 구조", [GL] "KV 주입": injected K/V are cached and reused
  * across drafting iterations).  Layouts, in the cache type:
- *   k: [L][B][Hkv][cap][d]          row-major keys
+ *   k, fp32 cache: [L][B][Hkv][cap][d]           row-major keys
+ *   k, bf16 cache: [L][B][Hkv][cap/32][32*d]     per block of 32 keys, the block
+ *                  in the order of the attention's score fragments: key i, dim c
+ *                  of a block at 512*(((i%8)/4)*(d/32) + c/32)
+ *                  + 8*(16*((c%32)/8) + 4*(i/8) + i%4) + c%8 (i = key % 32)
  *   v, fp32 cache: [L][B][Hkv][d][cap]           values transposed (key fastest)
  *   v, bf16 cache: [L][B][Hkv][cap/32][d][32]    values transposed per block of
- *                  32 keys, each block contiguous (8 KB at d = 128), so the
- *                  attention streams whole lines
+ *                  32 keys
+ * In a bf16 cache each block of K or V is contiguous (8 KB at d = 128) and
+ * every kilobyte the attention loads into LDS is one run of whole lines.
  * len[b] (HOST array, caller-owned) is the number of valid context rows of
  * sequence b.  Rows [0, len[b]) are never written by draft_forward; inject_kv
  * writes rows [len[b], len[b]+T_b) and then adds T_b to len[b].  The host

@@ -1,7 +1,8 @@
 """Host-side cache layout helpers (runtime.DeviceCache) on CPU tensors: the
-fp32 cache keeps V transposed per head ([d][cap]), the bf16 cache per block of
-32 keys ([cap/32][d][32]); rows written with put_rows read back unchanged,
-sit where the C ABI's layout puts them, and leave every other row alone."""
+fp32 cache keeps K row-major and V transposed per head ([d][cap]); the bf16
+cache keeps both per block of 32 keys, K in the attention's fragment order and
+V as [d][32]; rows written with put_rows read back unchanged, sit where the C
+ABI's layout puts them, and leave every other row alone."""
 import numpy as np
 import pytest
 import torch
@@ -34,16 +35,26 @@ def test_put_rows_round_trip_and_placement(cache_dtype):
     k2, v2 = c.rows(1, lo, lo + n)
     assert np.array_equal(k2, k) and np.array_equal(v2, v)
     # untouched rows and the other sequence stay zero
-    assert not np.any(c.rows(1, 0, lo)[1]) and not np.any(c.rows(1, lo + n, cap)[1])
-    assert not np.any(c.rows(0, 0, cap)[1])
-    # one value at the address the C ABI's layout gives it
-    l, key, h, dim = 1, lo + 9, 1, 37
-    flat = c.v.reshape(-1)
-    if c.blocked:
-        off = ((((l * 2 + 1) * cfg.Hkv + h) * (cap // 32) + key // 32) * cfg.d + dim) * 32 + key % 32
-    else:
-        off = (((l * 2 + 1) * cfg.Hkv + h) * cfg.d + dim) * cap + key
-    assert float(flat[off]) == v[l, key - lo, h, dim]
+    for part in (0, 1):
+        assert not np.any(c.rows(1, 0, lo)[part]) and not np.any(c.rows(1, lo + n, cap)[part])
+        assert not np.any(c.rows(0, 0, cap)[part])
+    # values at the addresses the C ABI's layout gives them
+    d = cfg.d
+    for l, key, h, dim in [(1, lo + 9, 1, 37), (0, lo, 0, 0), (1, lo + n - 1, 0, d - 1), (0, 40, 1, 13)]:
+        flat = c.v.reshape(-1)
+        if c.blocked:
+            off = ((((l * 2 + 1) * cfg.Hkv + h) * (cap // 32) + key // 32) * d + dim) * 32 + key % 32
+        else:
+            off = (((l * 2 + 1) * cfg.Hkv + h) * d + dim) * cap + key
+        assert float(flat[off]) == v[l, key - lo, h, dim]
+        flat = c.k.reshape(-1)
+        if c.blocked:
+            i = key % 32
+            inblk = 512 * (((i % 8) // 4) * (d // 32) + dim // 32) + 8 * (16 * ((dim % 32) // 8) + 4 * (i // 8) + i % 4) + dim % 8
+            off = (((l * 2 + 1) * cfg.Hkv + h) * (cap // 32) + key // 32) * (32 * d) + inblk
+        else:
+            off = (((l * 2 + 1) * cfg.Hkv + h) * cap + key) * d + dim
+        assert float(flat[off]) == k[l, key - lo, h, dim]
 
 
 @pytest.mark.parametrize("cache_dtype", ["f32", "bf16"])
@@ -61,3 +72,14 @@ def test_fill_random_snapshot_same_rows(cache_dtype):
     c.put_rows(0, 39, np.zeros((cfg.L, 1, cfg.Hkv, cfg.d)), np.ones((cfg.L, 1, cfg.Hkv, cfg.d)))
     assert not c.same_rows(snap, 0, 40)
     assert c.same_rows(c.snapshot(0, 39), 0, 39)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_key_block_order_is_a_permutation(d):
+    """The fragment order of a 32-key block is a bijection onto the block, and
+    lane l of fragment f reads 8 consecutive dimensions of one key."""
+    perm = runtime.k_frag_perm(d)
+    assert sorted(perm.tolist()) == list(range(32 * d))
+    p = perm.reshape(32, d)
+    assert np.all(np.diff(p.reshape(32, d // 8, 8), axis=2) == 1)
+    assert np.all(p.reshape(32, d // 8, 8)[:, :, 0] % 8 == 0)

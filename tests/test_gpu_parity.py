@@ -229,7 +229,7 @@ def test_bf16_storage_rounding_is_rne():
         w[(Hq + Hkv) * d + c, b] = -1.0
     Ht = torch.from_numpy(H).cuda().to(torch.bfloat16)
     wq = torch.from_numpy(w).cuda().to(torch.bfloat16)
-    kc = torch.zeros(L, 1, Hkv, 32, d, dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(L, 1, Hkv, 1, 32 * d, dtype=torch.bfloat16, device="cuda")  # bf16 K: [cap/32][32 d], fragment order
     vc = torch.zeros(L, 1, Hkv, 1, d, 32, dtype=torch.bfloat16, device="cuda")   # bf16 V: [cap/32][d][32]
     lens = (ctypes.c_int32 * 1)(0)
     cache = B.KVCache(k=kc.data_ptr(), v=vc.data_ptr(), B=1, cap=32, len=ctypes.cast(lens, ctypes.POINTER(ctypes.c_int32)))
@@ -241,7 +241,8 @@ def test_bf16_storage_rounding_is_rne():
     assert lens[0] == 4
     exact_k = H.astype(np.float64) @ w[Hq * d:(Hq + Hkv) * d].astype(np.float64).T     # [4, d]
     exact_v = H.astype(np.float64) @ w[(Hq + Hkv) * d:].astype(np.float64).T
-    got_k = kc[0, 0, 0, :4].float().cpu().numpy()
+    from block_diffusion_drafter_ctx_amd.runtime import k_frag_perm
+    got_k = kc[0, 0, 0, 0].float().cpu().numpy()[k_frag_perm(d)].reshape(32, d)[:4]
     got_v = vc[0, 0, 0, 0, :, :4].float().cpu().numpy().T
     assert np.array_equal(got_k, O.to_bf16(exact_k)), (got_k[0, :8], O.to_bf16(exact_k)[0, :8])
     assert np.array_equal(got_v, O.to_bf16(exact_v))
