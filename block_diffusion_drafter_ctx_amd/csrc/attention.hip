@@ -28,6 +28,7 @@
 // hi + lo planes (attn_mfma_kernel, three MFMAs per product).  fp32 weights
 // use a plain one-wave-per-(row, head) online-softmax kernel.
 #include "common.h"
+#include "kv_layout.h"
 #include "launch.h"
 
 #include <stdlib.h>

@@ -86,18 +86,6 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
 // exact counts with wait_vmcnt.
 typedef __attribute__((address_space(3))) void lds_void;
 
-// bf16 KV cache, keys: every block of 32 keys (32 * d elements) is stored in the
-// order of the attention's score fragments, 2 * (d / 32) fragments of 512
-// elements.  Fragment t * (d / 32) + s holds keys 8 q + 4 t + r (q, r < 4) at
-// dimensions [32 s, 32 s + 32); inside it lane l = 16 g + 4 q + r owns the 8
-// dimensions from 32 s + 8 g of key 8 q + 4 t + r.  Element offset of (key i,
-// dimension c) from the start of its block:
-__host__ __device__ __forceinline__ int k_frag_offset(int i, int c, int d) {
-  const int kk = i & 31;
-  const int f = ((kk & 7) >> 2) * (d >> 5) + (c >> 5);
-  const int l = 16 * ((c & 31) >> 3) + 4 * (kk >> 3) + (kk & 3);
-  return f * 512 + l * 8 + (c & 7);
-}
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void*)p)));

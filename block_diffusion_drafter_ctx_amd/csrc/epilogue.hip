@@ -14,6 +14,7 @@
 //   accept_ragged  acceptance with a draft count per sequence
 // Every reduction sums partials in split order: results are bit-reproducible.
 #include "common.h"
+#include "kv_layout.h"
 #include "launch.h"
 
 namespace dflash {
