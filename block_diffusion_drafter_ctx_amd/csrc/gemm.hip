@@ -727,7 +727,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kern
   constexpr int LPW = NLD / NW;                             // loads per wave per stage
   static_assert(NLD % NW == 0 && kTileK == 64, "loads split evenly over the waves");
   extern __shared__ uint4 lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave % (TN / WN), wm = wave / (TN / WN);
   int nt = blockIdx.x, mt = blockIdx.y, split = blockIdx.z;
   if (g.xcd_tiles) {
@@ -753,43 +753,88 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kern
 
   // load q = wave + NW i of a stage covers LDS rows 8q .. 8q + 7 (W rows first,
   // then A: hi plane rows, lo plane rows); lane l fetches chunk
-  // (l % 8) ^ (l / 8) of row 8q + l / 8, the chunk its LDS slot l % 8 holds
+  // (l % 8) ^ (l / 8) of row 8q + l / 8, the chunk its LDS slot l % 8 holds.
+  // voff[i] is that lane's byte offset from the load's scalar base (the W
+  // tile's k column, or the A plane's column); the launcher keeps it below 2^31.
   const int kchunk = 8 * ((lane & 7) ^ (lane >> 3));
-  int64_t roff[LPW];
+  uint32_t voff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int row = 8 * (wave + NW * i) + (lane >> 3);
+    int64_t e;
     if (row < WROWS) {
       const int n = min(n0 + row, g.N - 1);                 // rows past N: results dropped
-      roff[i] = (static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg) * g.w_ld + kchunk;
+      e = (static_cast<int64_t>(n / g.w_rg) * g.w_gs + g.w_off + n % g.w_rg) * g.w_ld + kchunk;
     } else {
       const int m = min(m0 + (row - WROWS) % TM, g.M - 1);       // rows past M: results dropped
-      roff[i] = a_row_off(g, m) + kchunk;
+      e = a_row_off(g, m) + kchunk;
     }
+    voff[i] = static_cast<uint32_t>(e * 2);
   }
   const uint16_t* wbase = static_cast<const uint16_t*>(g.w);
-  struct TileSrc { int kb; const uint16_t *ahi, *alo; };
-  auto tile_src = [&](int t) __attribute__((always_inline)) {   // t: k-tile index within [0, nk)
-    TileSrc r;
-    r.kb = (kt_begin + min(t, nk - 1)) * kTileK;
-    // a 64-wide k tile never straddles A sources (a_cols % 64 == 0)
-    const int s = r.kb / g.a_cols, col = r.kb - s * g.a_cols;
-    r.ahi = pick_src_reg<uint16_t>(g, s) + col;
-    r.alo = HL == 2 ? static_cast<const uint16_t*>(g.a_lo) + col : r.ahi;   // HL == 2: one source
-    return r;
+  const unsigned lds0 = lds_addr(lds);
+  // The tile whose loads go out next: tiles are issued in order, and past the
+  // end of the K range the last one repeats.  Its W, A-hi and A-lo column
+  // pointers advance by additions (a 64-wide k tile never straddles A sources,
+  // a_cols % 64 == 0), so the loop does no division and the load bases stay
+  // in scalar registers.  HL == 2: one source, its hi and lo planes.
+  int c_t = 0;
+  const uint16_t *c_wp, *c_ap, *c_lp;
+  int c_s, c_col;
+  auto uni = [](const uint16_t* p) __attribute__((always_inline)) {   // pin a wave-uniform pointer to SGPRs
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    // readfirstlane returns int: each half goes through uint32_t so that the
+    // low word is not sign-extended into the high one
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+    return reinterpret_cast<const uint16_t*>((static_cast<uint64_t>(hi) << 32) | lo);
   };
-  auto issue_one = [&](int i, const TileSrc& src, int stage) __attribute__((always_inline)) {
+  {
+    const int kb = kt_begin * kTileK;
+    c_s = kb / g.a_cols;
+    c_col = kb - c_s * g.a_cols;
+    c_wp = uni(wbase + kb);
+    c_ap = uni(pick_src_reg<uint16_t>(g, c_s) + c_col);
+    c_lp = HL == 2 ? uni(static_cast<const uint16_t*>(g.a_lo) + c_col) : c_ap;
+  }
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (c_t < nk - 1) {
+      c_wp += kTileK;
+      c_ap += kTileK;
+      if constexpr (HL == 2) c_lp += kTileK;
+      c_col += kTileK;
+      if (c_col == g.a_cols) {                               // the next A source starts
+        c_col = 0;
+        ++c_s;
+        c_ap = uni(pick_src_reg<uint16_t>(g, c_s));
+      }
+    }
+    ++c_t;
+  };
+  // which operand load i of a wave feeds: W rows, then the A hi plane, then
+  // the lo plane; known at compile time when the rows split evenly over the
+  // waves' loads, otherwise a wave-uniform test
+  auto base_of = [&](int i) __attribute__((always_inline)) -> const uint16_t* {
+    constexpr int R8 = 8 * NW;                               // LDS rows one load index covers
+    if constexpr (WROWS % R8 == 0 && (WROWS + TM) % R8 == 0) {
+      if (i < WROWS / R8) return c_wp;
+      if (HL == 2 && i >= (WROWS + TM) / R8) return c_lp;
+      return c_ap;
+    } else {
+      const int row0 = 8 * (wave + NW * i);
+      if (row0 < WROWS) return c_wp;
+      return HL == 2 && row0 - WROWS >= TM ? c_lp : c_ap;
+    }
+  };
+  auto issue_one = [&](int i, int stage) __attribute__((always_inline)) {
     const int q = wave + NW * i;                             // uniform per wave
-    const int row0 = 8 * q;
-    const uint16_t* p;
-    if (row0 < WROWS) p = wbase + roff[i] + src.kb;
-    else p = (row0 - WROWS >= TM ? src.alo : src.ahi) + roff[i];
-    load_frag_to_lds(p, lds + stage * BUF + q * 64);
+    load_to_lds_sbase(voff[i], uni(base_of(i)),
+                      __builtin_amdgcn_readfirstlane(lds0 + static_cast<unsigned>((stage * BUF + q * 64) * 16)));
   };
-  auto issue = [&](int t, int stage) __attribute__((always_inline)) {
-    const TileSrc src = tile_src(t);
+  auto issue = [&](int stage) __attribute__((always_inline)) {   // the cursor's tile into stage; then advance
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) issue_one(i, src, stage);
+    for (int i = 0; i < LPW; ++i) issue_one(i, stage);
+    advance();
   };
 
   f32x4_t acc[FN][FM];
@@ -823,7 +868,7 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kern
   // the same MFMAs with the next tile's loads spread among them, so that the
   // wave keeps the MFMA pipe fed while the load instructions are accepted
   constexpr int NMF = FN * FM * HL, EVERY = (NMF + LPW - 1) / LPW;
-  auto mm_issue = [&](const Frags& f, const TileSrc& src, int stage) __attribute__((always_inline)) {
+  auto mm_issue = [&](const Frags& f, int stage) __attribute__((always_inline)) {
     int q = 0;
 #pragma unroll
     for (int x = 0; x < NMF; ++x) {
@@ -831,21 +876,28 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kern
       acc[i][j] = mfma16x16x32(f.w[i], f.a[j * HL + h], acc[i][j]);
       if (x % EVERY == EVERY - 1 && q < LPW) {
         __builtin_amdgcn_sched_barrier(0);
-        issue_one(q++, src, stage);
+        issue_one(q++, stage);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
     for (int r = 0; r < LPW; ++r)
-      if (r >= q) issue_one(r, src, stage);
+      if (r >= q) issue_one(r, stage);
+    advance();
   };
 
 #pragma unroll
-  for (int st = 0; st < NSTAGE; ++st) issue(st, st);
+  for (int st = 0; st < NSTAGE; ++st) issue(st);
   wait_vmcnt<(NSTAGE - 1) * LPW>();                          // tile 0 landed
   bare_barrier();
   Frags fa, fb;
   rd(fa, lds, 0);
+  // stage of tile t (sc) and of tile t + 1 (sn); tile t + NSTAGE goes to sc
+  int sc = 0, sn = 1 % NSTAGE;
+  auto rotate = [&]() __attribute__((always_inline)) {
+    sc = sn;
+    sn = sn + 1 == NSTAGE ? 0 : sn + 1;
+  };
   if constexpr (EARLY) {
     // Two barriers per tile: the first (every wave has read both k-steps of
     // tile t) frees its stage, so tile t + NSTAGE's loads go out among the
@@ -853,34 +905,34 @@ __global__ __launch_bounds__((TN / WN) * (TM / WM) * 64) void gemm_tile_lds_kern
     // a tile later.  A load then has NSTAGE - 1/2 tiles of MFMA work to land
     // in, against NSTAGE - 1 when it waits for the single mid-tile barrier.
     for (int t = 0; t < nk; ++t) {
-      rd(fb, lds + (t % NSTAGE) * BUF, 1);
+      rd(fb, lds + sc * BUF, 1);
       __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0): this wave is done reading tile t
       bare_barrier();                                         // ... every wave is: its stage is free
-      const TileSrc src = tile_src(t + NSTAGE);
       __builtin_amdgcn_sched_barrier(0);
-      mm_issue(fa, src, t % NSTAGE);                          // k-step 0 of tile t; tile t + NSTAGE loads
+      mm_issue(fa, sc);                                       // k-step 0 of tile t; tile t + NSTAGE loads
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<(NSTAGE - 1) * LPW>();                      // tile t + 1 landed (tiles t + 2 .. in flight)
       bare_barrier();                                         // ... for every wave
-      rd(fa, lds + ((t + 1) % NSTAGE) * BUF, 0);              // past the end: a repeated tile, unused
+      rd(fa, lds + sn * BUF, 0);                              // past the end: a repeated tile, unused
       __builtin_amdgcn_sched_barrier(0);
       mm(fb);                                                 // k-step 1 of tile t
       __builtin_amdgcn_sched_barrier(0);
+      rotate();
     }
   } else {
     for (int t = 0; t < nk; ++t) {
-      rd(fb, lds + (t % NSTAGE) * BUF, 1);
+      rd(fb, lds + sc * BUF, 1);
       __builtin_amdgcn_sched_barrier(0);
       mm(fa);                                                 // k-step 0 of tile t
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0): this wave is done reading tile t
       wait_vmcnt<(NSTAGE - 2) * LPW>();                      // tile t + 1 landed
       bare_barrier();                                         // ... for every wave; tile t is free
-      const TileSrc src = tile_src(t + NSTAGE);
-      rd(fa, lds + ((t + 1) % NSTAGE) * BUF, 0);              // past the end: a repeated tile, unused
+      rd(fa, lds + sn * BUF, 0);                              // past the end: a repeated tile, unused
       __builtin_amdgcn_sched_barrier(0);
-      mm_issue(fb, src, t % NSTAGE);                          // k-step 1 of tile t; tile t + NSTAGE loads
+      mm_issue(fb, sc);                                       // k-step 1 of tile t; tile t + NSTAGE loads
       __builtin_amdgcn_sched_barrier(0);
+      rotate();
     }
   }
   wait_vmcnt<0>();                                            // the trailing repeated tiles
@@ -1215,6 +1267,15 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
 template <int HL, int NS, int TN, int TM, int WN, int WM, bool TOP2 = false>
 hipError_t launch_tile_lds(GemmArgs a, dim3 grid, hipStream_t st, float* top2 = nullptr) {
   const size_t lds = static_cast<size_t>(NS) * (TN + TM * HL) * 8 * sizeof(uint4);
+  // the kernel addresses a tile load as a scalar base (the W tile's k column,
+  // an A plane's column) plus a byte offset per lane, kept below 2^31
+  if (a.N < 1 || a.M < 1 || a.w_rg < 1 || a.a_rg < 1) return hipErrorInvalidValue;
+  const int64_t wrow = static_cast<int64_t>(a.N - 1) / a.w_rg * a.w_gs + a.w_off +
+                       std::min<int64_t>(a.w_rg - 1, a.N - 1);
+  const int64_t arow = static_cast<int64_t>(a.M - 1) / a.a_rg * a.a_gs +
+                       std::min<int64_t>(a.a_rg - 1, a.M - 1) * a.a_ld;
+  if ((wrow * a.w_ld + kTileK) * 2 >= (int64_t{1} << 31) || (arow + kTileK) * 2 >= (int64_t{1} << 31))
+    return hipErrorInvalidValue;
   a.xcd_tiles = env_int("DFLASH_TILE_XCD", 1) == 1 ? 1 : 0;   // 2: grid order (measurement)
   if (a.xcd_tiles) {
     a.ntiles = static_cast<int>(grid.x);
