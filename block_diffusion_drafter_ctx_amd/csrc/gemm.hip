@@ -559,6 +559,14 @@ constexpr TileShape kTileBf16{256, 256, 64, 128, 2}, kTileHiLo{256, 128, 64, 64,
 // 8-layer drafter at 4 x 16 block rows: 2126 -> 1976 us; bf16 A on 256 x 128
 // tiles with three stages loses to 256 x 256 with two: ingest 585 -> 674 us)
 constexpr TileShape kTileHiLo64{256, 64, 64, 32, 3}, kTileHiLo32{256, 32, 64, 16, 3};
+// hi / lo planes of 65-256 activation rows against a drafter-sized weight: 128
+// weight rows x 128 activation rows (eight waves of 64 x 32, three 48 KB
+// stages).  Twice the n-tiles of the 256-row tile, so fewer K splits fill the
+// CUs and fewer fp32 partials go through HBM: 16-sequence ragged pass 2222 ->
+// 2123 us, the 16-sequence loop 2361 -> 2264 us, the 8-layer drafter at 4 x 32
+// block rows 2326 -> 2286 us; with 512 or 1024 rows (anchored blocks) the
+// 256-row tile stays ahead (4745 against 4870 us)
+constexpr TileShape kTileHiLoN128{128, 128, 64, 32, 3};
 
 template <int AK>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
@@ -1219,14 +1227,17 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
   GemmPlan p;
   p.tiled = true;
   // register-staged kernel (fp32 A) or LDS-direct kernel
-  // hi / lo planes: the smallest of the 32-, 64- and 128-row tiles that holds M
-  // (DFLASH_TILE64=2: always 128 rows, for measurement)
+  // hi / lo planes: the smallest of the 32-, 64- and 128-row tiles that holds M,
+  // 128 weight rows wide for 65-256 rows against a weight of <= 32768 rows
+  // (DFLASH_TILE64=2: always 256 x 128 tiles, for measurement)
   const bool small_tiles = ak == A_BF16_HILO && env_int("DFLASH_TILE64", 1) == 1;
-  const TileShape hl = !small_tiles ? kTileHiLo : M <= kTileHiLo32.tm ? kTileHiLo32
-                                                : M <= kTileHiLo64.tm ? kTileHiLo64 : kTileHiLo;
+  TileShape hl = !small_tiles ? kTileHiLo : M <= kTileHiLo32.tm ? kTileHiLo32
+                                          : M <= kTileHiLo64.tm ? kTileHiLo64 : kTileHiLo;
+  if (small_tiles && M > kTileHiLo64.tm && M <= 256 && N <= 32768) hl = kTileHiLoN128;
   const int tn = ak == A_F32_SPLIT ? kTileN : ak == A_BF16 ? kTileBf16.tn : hl.tn;
   const int tm = ak == A_F32_SPLIT ? kTileM : ak == A_BF16 ? kTileBf16.tm : hl.tm;
   p.MT = tm;
+  p.tn = tn;
   p.mtiles = (M + tm - 1) / tm;
   p.ntiles = (N + tn - 1) / tn;
   const int ktiles = K / kTileK;
@@ -1306,6 +1317,10 @@ hipError_t launch_gemm_tiled_top2(const GemmArgs& a0, const GemmPlan& p, float* 
   a.chunks_per_split = p.cps;
   a.part = logits;
   const dim3 grid(p.ntiles, p.mtiles, 1);
+  constexpr TileShape TN1 = kTileHiLoN128;
+  if (p.tn == TN1.tn && p.MT == TN1.tm)
+    return launch_tile_lds<2, TN1.ns, TN1.tn, TN1.tm, TN1.wn, TN1.wm, true>(a, grid, st, top2);
+  if (p.tn != T.tn) return hipErrorInvalidValue;
   if (p.MT == T32.tm) return launch_tile_lds<2, T32.ns, T32.tn, T32.tm, T32.wn, T32.wm, true>(a, grid, st, top2);
   if (p.MT == T64.tm) return launch_tile_lds<2, T64.ns, T64.tn, T64.tm, T64.wn, T64.wm, true>(a, grid, st, top2);
   return launch_tile_lds<2, T.ns, T.tn, T.tm, T.wn, T.wm, true>(a, grid, st, top2);
@@ -1323,7 +1338,8 @@ hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p,
       if (p.MT != T.tm) return hipErrorInvalidValue;
       return launch_tile_lds<1, T.ns, T.tn, T.tm, T.wn, T.wm>(a, grid, st);
     }
-    constexpr TileShape T = kTileHiLo, T64 = kTileHiLo64, T32 = kTileHiLo32;
+    constexpr TileShape T = kTileHiLo, T64 = kTileHiLo64, T32 = kTileHiLo32, TN1 = kTileHiLoN128;
+    if (p.tn == TN1.tn && p.MT == TN1.tm) return launch_tile_lds<2, TN1.ns, TN1.tn, TN1.tm, TN1.wn, TN1.wm>(a, grid, st);
     if (p.MT == T32.tm) return launch_tile_lds<2, T32.ns, T32.tn, T32.tm, T32.wn, T32.wm>(a, grid, st);
     if (p.MT == T64.tm) return launch_tile_lds<2, T64.ns, T64.tn, T64.tm, T64.wn, T64.wm>(a, grid, st);
     if (p.MT != T.tm) return hipErrorInvalidValue;

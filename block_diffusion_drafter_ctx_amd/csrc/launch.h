@@ -82,6 +82,7 @@ struct GemmPlan {
   bool rk = false;      // register-K kernel (16-row chunks, tall weight)
   int ks = 8;           // register-K: k steps per wave
   int mr = 1;           // register-K: 16-row chunks (the launch has mr * grid workgroups)
+  int tn = 0;           // tiled: weight rows per tile (with MT, the tile shape)
   size_t part_floats = 0;
 };
 
