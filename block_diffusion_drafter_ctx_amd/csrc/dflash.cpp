@@ -372,6 +372,7 @@ ArgmaxWs argmax_ws(const dflash_dims* d, int M, bool gathered = false) {
     // GEMM tile, or register-K workgroup
     size_t t2 = static_cast<size_t>((d->V + 255) / 256);
     if (t2 < static_cast<size_t>(kRkMaxGrid)) t2 = kRkMaxGrid;
+    if (!hp.rk && static_cast<size_t>(hp.ap.p.ntiles) > t2) t2 = hp.ap.p.ntiles;   // one per n-tile of the plan
     w.top2 = c.take(t2 * M * 3 * 4);
   }
   w.total = c.off;
@@ -989,7 +990,7 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
 // process ends.  Host code never uses the array's name as an address (on the
 // host it only names the symbol): the device address comes from
 // hipGetSymbolAddress, looked up once per device and kept in g_scratch.
-constexpr size_t kScratchBytes = size_t{64} << 20;
+constexpr size_t kScratchBytes = size_t{96} << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {

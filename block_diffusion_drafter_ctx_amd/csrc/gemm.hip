@@ -567,6 +567,10 @@ constexpr TileShape kTileHiLo64{256, 64, 64, 32, 3}, kTileHiLo32{256, 32, 64, 16
 // block rows 2326 -> 2286 us; with 512 or 1024 rows (anchored blocks) the
 // 256-row tile stays ahead (4745 against 4870 us)
 constexpr TileShape kTileHiLoN128{128, 128, 64, 32, 3};
+// ... and for 33-64 rows 128 x 64 tiles (eight waves of 32 x 32, three 32 KB
+// stages; four measured slightly slower): the 8-layer drafter at 4 x 16 block
+// rows 1766 -> 1715 us a loop iteration
+constexpr TileShape kTileHiLoN128M64{128, 64, 32, 32, 3};
 
 template <int AK>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs g) {
@@ -1228,12 +1232,13 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
   p.tiled = true;
   // register-staged kernel (fp32 A) or LDS-direct kernel
   // hi / lo planes: the smallest of the 32-, 64- and 128-row tiles that holds M,
-  // 128 weight rows wide for 65-256 rows against a weight of <= 32768 rows
+  // 128 weight rows wide for 33-256 rows against a weight of <= 32768 rows
   // (DFLASH_TILE64=2: always 256 x 128 tiles, for measurement)
   const bool small_tiles = ak == A_BF16_HILO && env_int("DFLASH_TILE64", 1) == 1;
   TileShape hl = !small_tiles ? kTileHiLo : M <= kTileHiLo32.tm ? kTileHiLo32
                                           : M <= kTileHiLo64.tm ? kTileHiLo64 : kTileHiLo;
   if (small_tiles && M > kTileHiLo64.tm && M <= 256 && N <= 32768) hl = kTileHiLoN128;
+  if (small_tiles && M > kTileHiLo32.tm && M <= kTileHiLo64.tm && N <= 32768) hl = kTileHiLoN128M64;
   const int tn = ak == A_F32_SPLIT ? kTileN : ak == A_BF16 ? kTileBf16.tn : hl.tn;
   const int tm = ak == A_F32_SPLIT ? kTileM : ak == A_BF16 ? kTileBf16.tm : hl.tm;
   p.MT = tm;
@@ -1317,9 +1322,11 @@ hipError_t launch_gemm_tiled_top2(const GemmArgs& a0, const GemmPlan& p, float* 
   a.chunks_per_split = p.cps;
   a.part = logits;
   const dim3 grid(p.ntiles, p.mtiles, 1);
-  constexpr TileShape TN1 = kTileHiLoN128;
+  constexpr TileShape TN1 = kTileHiLoN128, TN2 = kTileHiLoN128M64;
   if (p.tn == TN1.tn && p.MT == TN1.tm)
     return launch_tile_lds<2, TN1.ns, TN1.tn, TN1.tm, TN1.wn, TN1.wm, true>(a, grid, st, top2);
+  if (p.tn == TN2.tn && p.MT == TN2.tm)
+    return launch_tile_lds<2, TN2.ns, TN2.tn, TN2.tm, TN2.wn, TN2.wm, true>(a, grid, st, top2);
   if (p.tn != T.tn) return hipErrorInvalidValue;
   if (p.MT == T32.tm) return launch_tile_lds<2, T32.ns, T32.tn, T32.tm, T32.wn, T32.wm, true>(a, grid, st, top2);
   if (p.MT == T64.tm) return launch_tile_lds<2, T64.ns, T64.tn, T64.tm, T64.wn, T64.wm, true>(a, grid, st, top2);
@@ -1339,7 +1346,9 @@ hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p,
       return launch_tile_lds<1, T.ns, T.tn, T.tm, T.wn, T.wm>(a, grid, st);
     }
     constexpr TileShape T = kTileHiLo, T64 = kTileHiLo64, T32 = kTileHiLo32, TN1 = kTileHiLoN128;
+    constexpr TileShape TN2 = kTileHiLoN128M64;
     if (p.tn == TN1.tn && p.MT == TN1.tm) return launch_tile_lds<2, TN1.ns, TN1.tn, TN1.tm, TN1.wn, TN1.wm>(a, grid, st);
+    if (p.tn == TN2.tn && p.MT == TN2.tm) return launch_tile_lds<2, TN2.ns, TN2.tn, TN2.tm, TN2.wn, TN2.wm>(a, grid, st);
     if (p.MT == T32.tm) return launch_tile_lds<2, T32.ns, T32.tn, T32.tm, T32.wn, T32.wm>(a, grid, st);
     if (p.MT == T64.tm) return launch_tile_lds<2, T64.ns, T64.tn, T64.tm, T64.wn, T64.wm>(a, grid, st);
     if (p.MT != T.tm) return hipErrorInvalidValue;

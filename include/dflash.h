@@ -209,7 +209,7 @@ dflash_status dflash_draft_forward(const dflash_dims* dims, const dflash_weights
 /* (c) without a workspace argument, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation).  The same pass as dflash_draft_forward, on the same
- * kernels, with the workspace taken from a static device array of 64 MiB
+ * kernels, with the workspace taken from a static device array of 96 MiB
  * inside the library (one per GPU, held until the process ends; the call
  * itself allocates nothing).  Passes whose workspace would exceed it are
  * refused with DFLASH_ERR_WORKSPACE before anything is enqueued (at the
