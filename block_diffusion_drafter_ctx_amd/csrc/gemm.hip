@@ -567,6 +567,11 @@ constexpr TileShape kTileHiLo64{256, 64, 64, 32, 3}, kTileHiLo32{256, 32, 64, 16
 // block rows 2326 -> 2286 us; with 512 or 1024 rows (anchored blocks) the
 // 256-row tile stays ahead (4745 against 4870 us)
 constexpr TileShape kTileHiLoN128{128, 128, 64, 32, 3};
+// bf16 A (the context ingest) on 128 x 256 tiles (eight waves of 64 x 64,
+// three 48 KB stages) rather than 256 x 256 with two: the inject GEMM (2048 x
+// 10240 x 4096) 183 -> 173 us, the fuse unchanged (its 256 tiles then need no
+// K split)
+constexpr TileShape kTileBf16N128{128, 256, 64, 64, 3};
 // ... and for 33-64 rows 128 x 64 tiles (eight waves of 32 x 32, three 32 KB
 // stages; four measured slightly slower): the 8-layer drafter at 4 x 16 block
 // rows 1766 -> 1715 us a loop iteration
@@ -1232,15 +1237,17 @@ GemmPlan plan_gemm_tiled(int M, int N, int K, GemmAKind ak) {
   p.tiled = true;
   // register-staged kernel (fp32 A) or LDS-direct kernel
   // hi / lo planes: the smallest of the 32-, 64- and 128-row tiles that holds M,
-  // 128 weight rows wide for 33-256 rows against a weight of <= 32768 rows
-  // (DFLASH_TILE64=2: always 256 x 128 tiles, for measurement)
+  // 128 weight rows wide for 33-256 rows against a weight of <= 32768 rows;
+  // bf16 A: 128 x 256 tiles (DFLASH_TILE64=2: always 256 x 128 hi / lo and
+  // 256 x 256 bf16 tiles, for measurement)
   const bool small_tiles = ak == A_BF16_HILO && env_int("DFLASH_TILE64", 1) == 1;
   TileShape hl = !small_tiles ? kTileHiLo : M <= kTileHiLo32.tm ? kTileHiLo32
                                           : M <= kTileHiLo64.tm ? kTileHiLo64 : kTileHiLo;
   if (small_tiles && M > kTileHiLo64.tm && M <= 256 && N <= 32768) hl = kTileHiLoN128;
   if (small_tiles && M > kTileHiLo32.tm && M <= kTileHiLo64.tm && N <= 32768) hl = kTileHiLoN128M64;
-  const int tn = ak == A_F32_SPLIT ? kTileN : ak == A_BF16 ? kTileBf16.tn : hl.tn;
-  const int tm = ak == A_F32_SPLIT ? kTileM : ak == A_BF16 ? kTileBf16.tm : hl.tm;
+  const TileShape bf = env_int("DFLASH_TILE64", 1) == 1 ? kTileBf16N128 : kTileBf16;
+  const int tn = ak == A_F32_SPLIT ? kTileN : ak == A_BF16 ? bf.tn : hl.tn;
+  const int tm = ak == A_F32_SPLIT ? kTileM : ak == A_BF16 ? bf.tm : hl.tm;
   p.MT = tm;
   p.tn = tn;
   p.mtiles = (M + tm - 1) / tm;
@@ -1341,7 +1348,8 @@ hipError_t launch_gemm_mfma(const GemmArgs& a0, GemmAKind ak, const GemmPlan& p,
     const dim3 grid(p.ntiles, p.mtiles, p.S);
     if (a.a_cols % kTileK != 0) return hipErrorInvalidValue;
     if (ak == A_BF16) {
-      constexpr TileShape T = kTileBf16;
+      constexpr TileShape T = kTileBf16, T2 = kTileBf16N128;
+      if (p.tn == T2.tn && p.MT == T2.tm) return launch_tile_lds<1, T2.ns, T2.tn, T2.tm, T2.wn, T2.wm>(a, grid, st);
       if (p.MT != T.tm) return hipErrorInvalidValue;
       return launch_tile_lds<1, T.ns, T.tn, T.tm, T.wn, T.wm>(a, grid, st);
     }
