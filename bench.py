@@ -264,6 +264,7 @@ def main():
     for i in range(args.steps):
         step(args.warmup + i)
     s1.record(stream)
+    host_enqueue = time.perf_counter() - t_start   # host time to queue the steps (no wait)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     n_lm = hook(B.PROF_NONE, [])
@@ -332,7 +333,8 @@ def main():
                                        es, cs)
     ctx_flops = RF.fuse_flops(N, cfg.D, cfg.n_tgt) + RF.inject_flops(N, cfg.D, cfg.L, cfg.Hkv, cfg.d)
     log(f"step {ms_per_step * 1e3:.1f} us, draft fwd {draft_fwd_us:.1f} us, LM head {lm_us:.1f} us "
-        f"({lm_gbs:.0f} GB/s), context {context_us:.0f} us, last tau {taus.tolist()}")
+        f"({lm_gbs:.0f} GB/s), context {context_us:.0f} us, last tau {taus.tolist()}, "
+        f"host enqueue {host_enqueue * 1e6 / args.steps:.1f} us per step")
 
     out = {
         "metric": METRIC,
@@ -342,6 +344,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "host_enqueue_us_per_step": round(host_enqueue * 1e6 / args.steps, 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
