@@ -11,8 +11,9 @@
 //   * streaming (gemm_stream_kernel), 17-32 rows and shapes the others do not
 //     take: each wave streams a 16-row strip of W against an activation slice
 //     staged in LDS, with split-K partials;
-//   * tiled (gemm_tile_lds_kernel), from 33 rows: 256 x 128 (hi / lo planes)
-//     or 256 x 256 (bf16) tiles fed by global-to-LDS loads, launched in
+//   * tiled (gemm_tile_lds_kernel), from 33 rows: hi / lo plane tiles of
+//     256 x 128 (128 x 128, 128 x 64, 256 x 64, 256 x 32 for fewer rows) or
+//     128 x 256 bf16 tiles, fed by global-to-LDS loads, launched in
 //     XCD-grouped tile order, with split-K partials or, for the LM head, a
 //     per-tile top-2 epilogue;
 //   * gemm_f32_kernel for fp32 weights (tiny configurations only).
@@ -545,9 +546,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_rk_kernel(GemmArgs g, float* top
 // reads), double-buffered, with the next tile's global loads in flight while
 // the current one is multiplied.  grid = (N / 128, M / 128, splits).
 constexpr int kTileN = 128, kTileM = 128, kTileK = 64;
-// LDS-direct kernel shapes: bf16 A takes 256 x 256 tiles in eight waves of
-// 64 weight rows x 128 activation rows (two waves per SIMD: one issues MFMAs
-// while the other's load instructions are being accepted); hi/lo planes take
+// LDS-direct kernel shapes (weight rows x activation rows): eight waves, two
+// per SIMD, so one issues MFMAs while the other's load instructions are being
+// accepted.  The first bf16 shape was 256 x 256 in waves of 64 x 128 with two
+// 64 KB stages (kTileBf16, still selectable for measurement); hi/lo planes take
 // 256 x 128 tiles in eight waves of 64 x 64 (a 256-row A tile's two planes
 // would not leave room for two LDS stages)
 struct TileShape { int tn, tm, wn, wm, ns; };
