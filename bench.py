@@ -81,10 +81,10 @@ def kernel_traffic(which, workload, cache):
 # short-weight register-K GEMM takes the Q/K/V, O and down projections and, with
 # an fp32 H_t, the 16-row inject.
 FAMILIES = (
-    ("gemm_rk_kernel<4, RK_PART, 1, A_F32_SPLIT, 8> (short weights: Q/K/V, O and down projections of every layer, "
-     "and the 16-row K/V inject with an fp32 H_t; 8 waves, 16 fp32 activation rows as bf16 hi + lo in registers, "
-     "split-K partials reduced by the next kernel)", ("qkv", "o_proj", "down", "inject_append"), ("inject_append",),
-     "short_rk"),
+    ("gemm_rk_kernel<KS, RK_PART, 1, A_F32_SPLIT, 8> (short weights: Q/K/V, O and down projections of every layer, "
+     "and the 16-row K/V inject with an fp32 H_t; 8 waves of KS k-steps, KS = 4 (6 for the down projection), 16 "
+     "fp32 activation rows as bf16 hi + lo in registers, split-K partials reduced by the next kernel)",
+     ("qkv", "o_proj", "down", "inject_append"), ("inject_append",), "short_rk"),
     ("gemm_rk_kernel<8, RK_SWIGLU> (FFN gate/up with SwiGLU in the epilogue)", ("gate_up",), (), None),
     ("attention (split over key ranges + log-sum-exp combine)", ("attention",), (), None),
 )

@@ -1467,17 +1467,31 @@ GemmPlan plan_gemm_rk(int M, int N, int K, bool top2) {
 // pieces deep.  Eight waves rather than sixteen with 2 k-steps: the same bytes
 // in flight per CU with half the waves to launch and to reduce over
 // (0.2 us a call, the step 849 -> 845 us).
-GemmPlan plan_gemm_rk_short(int M, int N, int K) {
+GemmPlan plan_gemm_rk_short(int M, int N, int K, bool ks6) {
   GemmPlan p;
-  constexpr int kKsShort = 4;
-  if (M < 1 || M > rk_max_rows(false) || K % (32 * kKsShort * kRkShortWaves) != 0 ||
-      env_int("DFLASH_GEMM_NO_RK", 0) != 0)
-    return p;
-  const int S = K / (32 * kKsShort * kRkShortWaves);
+  if (M < 1 || M > rk_max_rows(false) || env_int("DFLASH_GEMM_NO_RK", 0) != 0) return p;
   const int C = (M + 15) / 16;
   const int ntiles = (N + 15) / 16;
-  const int grid = rk_unit_groups(S, C, static_cast<long>(S) * ntiles);
-  if (grid == 0) return p;
+  // Four k-steps per wave (a 1024-wide K range) unless six (1536) leave the
+  // workgroups a more even share of units: a workgroup keeps one split, so
+  // the grid is a multiple of the split count and the busiest workgroup sets
+  // the time.  The 4096 x 12288 down projection: 12 splits on 252 workgroups,
+  // 12-13 units of 4 k-steps each, against 8 splits on 256, 8 units of 6.
+  // (Six only for single-source activations: a wave's K range must not
+  // straddle two sources.)
+  int kKsShort = 0, S = 0, grid = 0;
+  long best = -1;
+  for (const int ks : {4, 6}) {
+    if (ks == 6 && !ks6) continue;
+    if (K % (32 * ks * kRkShortWaves) != 0) continue;
+    const int s = K / (32 * ks * kRkShortWaves);
+    const long units = static_cast<long>(s) * ntiles;
+    const int gr = rk_unit_groups(s, C, units);
+    if (gr == 0) continue;
+    const long cost = (units + gr - 1) / gr * ks;
+    if (best < 0 || cost < best) best = cost, kKsShort = ks, S = s, grid = gr;
+  }
+  if (best < 0) return p;
   p.rk = true;
   p.ks = kKsShort;
   p.waves = kRkShortWaves;
@@ -1504,7 +1518,7 @@ GemmPlan plan_gemm(int M, int N, int K, GemmAKind ak, bool wide) {
   if ((ak == A_F32_SPLIT || ak == A_BF16) && M <= rk_max_rows(true)) {
     const GemmPlan r = plan_gemm_rk(M, N, K, false);
     if (r.rk && r.S == 1) return r;
-    const GemmPlan q = plan_gemm_rk_short(M, N, K);
+    const GemmPlan q = plan_gemm_rk_short(M, N, K, ak == A_F32_SPLIT);
     if (q.rk) return q;
   }
   return plan_gemm_mfma(M, N, K, ak, wide);
@@ -1564,6 +1578,7 @@ hipError_t launch_gemm_rk(const GemmArgs& a0, const GemmPlan& p, float* top2, fl
     if (p.ks == 8) return rk_launch<8, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
     return rk_launch<4, RK_PART, 1, A_BF16>(a, p, nullptr, nullptr, st);
   }
+  if (short_form && p.ks == 6) return rk_launch<6, RK_PART, 1, A_F32_SPLIT, kRkShortWaves>(a, p, nullptr, nullptr, st);
   if (short_form) return rk_launch<4, RK_PART, 1, A_F32_SPLIT, kRkShortWaves>(a, p, nullptr, nullptr, st);
   if (p.ks == 8) return rk_launch<8, RK_PART, 1>(a, p, nullptr, nullptr, st);
   return rk_launch<4, RK_PART, 1>(a, p, nullptr, nullptr, st);
