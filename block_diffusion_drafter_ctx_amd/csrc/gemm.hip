@@ -7,7 +7,7 @@
 //     tall weights (LM head, gate/up) take the whole K per workgroup with the
 //     top-2, sampling or SwiGLU epilogue, up to 32 rows in 16-row chunks on
 //     XCD-adjacent workgroups; short weights (QKV, O, down, appends) split K
-//     in 1024-wide ranges;
+//     in 1024-wide ranges (1536 where that evens out the workgroups' share);
 //   * streaming (gemm_stream_kernel), 17-32 rows and shapes the others do not
 //     take: each wave streams a 16-row strip of W against an activation slice
 //     staged in LDS, with split-K partials;
