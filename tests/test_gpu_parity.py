@@ -81,6 +81,15 @@ def test_register_k_shapes():
     # and a 2-sequence batch of 7 (14 rows) through the same kernels
     Workload(shrink(cfg, cid=111, gammas=(5,)), 5, 1, override=True).run()
     Workload(shrink(cfg, cid=112, B=2, ctx=(40, 300), gammas=(7,)), 7, 1, override=True).run()
+    # F = 6144: the down projection (K = 6144) takes six k-steps per wave (4
+    # splits on 256 workgroups rather than 6 on 252), and gate/up (2F = 12288
+    # rows, below the tall form) the split-K form with the separate SwiGLU;
+    # 16, 5 and 14 block rows
+    log("register-K shapes: F=6144 (six k-steps per wave on the down projection)")
+    cfg6 = shrink(cfg, cid=140, F=6144)
+    Workload(cfg6, 16, 1).run()
+    Workload(shrink(cfg6, cid=141, gammas=(5,)), 5, 1, override=True).run()
+    Workload(shrink(cfg6, cid=142, B=2, ctx=(40, 300), gammas=(7,)), 7, 1, override=True).run()
 
 
 def test_register_k_row_chunks(monkeypatch):
